@@ -1,0 +1,120 @@
+"""fp64 CPU oracle of the Kimi Delta Attention recurrence (Python loader).
+
+TEST INFRASTRUCTURE ONLY.  The correctness reference for the GPU path.  Only
+``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (``libkda`` and the
+``gated_delta_rule_67_amd`` binding) never imports it, and it imports nothing
+from the product path.
+
+The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, libm ``exp``): the
+token loop of the gated delta rule as printed in the GLM-5.3-Flash model notes
+(Glm5NextTextLinearAttention snippet), with the output read from the updated
+state, and packed documents reset at their boundaries (NeMo glm5_next.layers,
+``_torch_recurrent_kda``).  This module only marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+
+_lib = None
+
+
+def build(out_path: str = LIB_PATH, src: str = _SRC, extra_flags=()) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared",
+           "-Wall", "-Wextra", *extra_flags, src, "-o", out_path, "-lm"]
+    tmp = out_path + ".tmp"
+    cmd[cmd.index(out_path)] = tmp
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out_path)
+    return out_path
+
+
+def load(path: str = LIB_PATH):
+    """Load a compiled oracle library and declare its signatures."""
+    lib = ctypes.CDLL(path)
+    i64, dp, ip = ctypes.c_int64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)
+    lib.kda_oracle_forward.restype = ctypes.c_int
+    lib.kda_oracle_forward.argtypes = [i64, i64, i64, i64, i64, dp, dp, dp, dp, dp,
+                                       dp, ip, ctypes.c_double, dp, dp, ctypes.c_int]
+    lib.kda_oracle_threads.restype = ctypes.c_int
+    lib.kda_oracle_threads.argtypes = [ctypes.c_int]
+    return lib
+
+
+def _get_lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        _lib = load()
+    return _lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if a is not None else None
+
+
+def threads(n_threads: int = 0) -> int:
+    return _get_lib().kda_oracle_threads(n_threads)
+
+
+def kda_forward(q, k, v, log_g, beta, init_state=None, cu_seqlens=None,
+                scale=None, n_threads: int = 0, lib=None):
+    """Run the token-loop recurrence.
+
+    q, k, log_g: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H].
+    Dense: B independent sequences.  Packed: B == 1 and ``cu_seqlens`` [N+1]
+    splits the row into N documents, each starting from its own initial state.
+    init_state: [N, H, dk, dv] or None (zeros).  scale defaults to dk**-0.5.
+    Returns (out [B, T, H, dv], final_state [N, H, dk, dv]) in float64.
+    """
+    lib = lib or _get_lib()
+    q, k, v, log_g, beta = (_f64(x) for x in (q, k, v, log_g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and log_g.shape == q.shape
+    assert v.shape == (B, T, H, dv) and beta.shape == (B, T, H)
+    if cu_seqlens is not None:
+        assert B == 1, "packed mode takes one row"
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N, L = cu.shape[0] - 1, T
+        cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    else:
+        cu, N, L, cu_p = None, B, T, None
+    if scale is None:
+        scale = dk ** -0.5
+    s0 = _f64(init_state) if init_state is not None else None
+    if s0 is not None:
+        assert s0.shape == (N, H, dk, dv)
+    out = np.zeros((B, T, H, dv), dtype=np.float64)
+    fin = np.zeros((N, H, dk, dv), dtype=np.float64)
+    rc = lib.kda_oracle_forward(N, L, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(log_g),
+                                _ptr(beta), _ptr(s0), cu_p, float(scale), _ptr(out),
+                                _ptr(fin), int(n_threads))
+    if rc != 0:
+        raise ValueError(f"kda_oracle_forward failed with code {rc}")
+    return out, fin
+
+
+def kda_step(q, k, v, log_g, beta, state, scale=None, n_threads: int = 0):
+    """Decode / verify: n_tok rows per sequence applied in order from ``state``.
+
+    Rows are [N, n_tok, H, d]; row t of a sequence is applied after rows < t
+    (metrale glm5next_layer invariants: verify row t uses slot t).  Returns
+    (out [N, n_tok, H, dv], new_state [N, H, dk, dv]); ``state`` is not modified.
+    """
+    return kda_forward(q, k, v, log_g, beta, init_state=state, scale=scale,
+                       n_threads=n_threads)

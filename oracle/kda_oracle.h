@@ -1,0 +1,61 @@
+/*
+ * kda_oracle.h -- fp64 CPU oracle of the Kimi Delta Attention (KDA) recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the correctness reference that the
+ * GPU path is checked against.  Only the test suite, the smoke entry point and
+ * the benchmark's CPU-baseline leg may load or call it.  The product path
+ * (libkda and its Python binding) never links, imports or calls it, and it
+ * shares no code, header or table with the GPU path.
+ *
+ * What it computes (GLM-5.3-Flash model notes, the Glm5NextTextLinearAttention
+ * snippet of the gated delta rule; NeMo glm5_next.layers, `_torch_recurrent_kda`):
+ * for every unit u = (sequence or packed document n, head h), starting from
+ * S = init_state[n,h] (or zeros), and for every token t of n in order
+ *
+ *     S[i,:]  *= exp(log_g[t,h,i])                 decay along the key axis
+ *     kv[j]    = sum_i S[i,j] * k[t,h,i]           read back S^T k
+ *     delta[j] = beta[t,h] * (v[t,h,j] - kv[j])    scaled prediction error
+ *     S[i,j]  += k[t,h,i] * delta[j]               rank-1 delta-rule update
+ *     out[t,h,j] = scale * sum_i S[i,j] * q[t,h,i] output from the updated state
+ *
+ * final_state[n,h] = S after the unit's last token.
+ *
+ * Layouts (row-major, last axis contiguous):
+ *   q, k, log_g : [tokens, H, dk]      v, out : [tokens, H, dv]
+ *   beta        : [tokens, H]          init_state, final_state : [N, H, dk, dv]
+ * Dense mode (cu_seqlens == NULL): N sequences of seq_len tokens each, token
+ * index n*seq_len + t.  Packed mode: cu_seqlens[N+1] (cu[0] = 0, non-decreasing,
+ * cu[N] = total tokens) splits one packed row into N documents; the state is
+ * reset to the document's own initial state at every document start.
+ *
+ * parity pins: every function here is pinned by the CPU tests (closed forms,
+ * exact rational brute force, packed/split/linearity invariants); none is
+ * "parity unpinned".
+ */
+#ifndef KDA_ORACLE_H
+#define KDA_ORACLE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Returns 0 on success, a negative value on invalid arguments
+ * (-1 NULL pointer, -2 bad dimension, -3 malformed cu_seqlens).
+ * n_threads <= 0 uses the OpenMP default. */
+int kda_oracle_forward(int64_t num_seqs, int64_t seq_len, int64_t num_heads,
+                       int64_t dk, int64_t dv,
+                       const double* q, const double* k, const double* v,
+                       const double* log_g, const double* beta,
+                       const double* init_state, const int64_t* cu_seqlens,
+                       double scale, double* out, double* final_state,
+                       int n_threads);
+
+/* Number of OpenMP threads a call with n_threads would use. */
+int kda_oracle_threads(int n_threads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_ORACLE_H */

@@ -1,0 +1,107 @@
+"""Planted mistakes in the oracle must fail its pins (CPU only).
+
+Each mutant is a textual edit of a *copy* of ``oracle/kda_oracle.c`` (a dropped
+term, a wrong sign, a wrong index or axis, a transposed operand, a missing
+reset, a wrong step order), compiled to a temporary library and run against
+``test_oracle_pins.py`` in a subprocess (a mutant may read out of bounds, so it
+never runs in this process).  The committed oracle is never modified.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "kda_oracle.c")
+
+DECAY = ("const double a = exp(gt[i]);\n"
+         "      for (int64_t j = 0; j < dv; ++j) S[i * dv + j] *= a;")
+
+MUTANTS = {
+    "decay_on_value_axis": (DECAY, "for (int64_t j = 0; j < dv; ++j) S[i * dv + j] *= exp(gt[j % dk]);"),
+    "no_decay": (DECAY, "(void)gt;"),
+    "decay_by_log_not_exp": ("const double a = exp(gt[i]);", "const double a = 1.0 + gt[i];"),
+    "decay_exp2": ("const double a = exp(gt[i]);", "const double a = exp2(gt[i]);"),
+    "readback_uses_q": ("kv[j] += S[i * dv + j] * kt[i];", "kv[j] += S[i * dv + j] * qt[i];"),
+    "error_sign": ("delta[j] = bt * (vt[j] - kv[j]);", "delta[j] = bt * (vt[j] + kv[j]);"),
+    "beta_dropped": ("delta[j] = bt * (vt[j] - kv[j]);", "delta[j] = (vt[j] - kv[j]); (void)bt;"),
+    "update_uses_q": ("S[i * dv + j] += kt[i] * delta[j];", "S[i * dv + j] += qt[i] * delta[j];"),
+    "update_dropped": ("S[i * dv + j] += kt[i] * delta[j];", "(void)delta;"),
+    "output_reads_k": ("acc += S[i * dv + j] * qt[i];", "acc += S[i * dv + j] * kt[i];"),
+    "scale_dropped": ("ot[j] = scale * acc;", "ot[j] = acc; (void)scale;"),
+    "transposed_readback": ("kv[j] += S[i * dv + j] * kt[i];",
+                            "kv[j] += S[(j % dk) * dv + (i % dv)] * kt[i];"),
+    "no_reset_between_units": ("memset(S, 0, sizeof(double) * dk * dv);", "(void)0;"),
+    "init_state_ignored": ("if (init_state)\n    memcpy(S,", "if (0)\n    memcpy(S,"),
+    "last_token_skipped": ("t < u->start + u->len; ++t", "t + 1 < u->start + u->len; ++t"),
+    "head_stride_wrong": ("const double* kt = k + (t * H + h) * dk;",
+                          "const double* kt = k + (t * H + (h + 1) % H) * dk;"),
+}
+
+
+def _pre_update_output(src):
+    """Move the output loop before the rank-1 update (output from the pre-update state)."""
+    upd = ("    for (int64_t i = 0; i < dk; ++i)\n"
+           "      for (int64_t j = 0; j < dv; ++j) S[i * dv + j] += kt[i] * delta[j];\n")
+    start = src.index("    /* output from the updated state")
+    end = src.index("  }\n  if (final_state)")
+    out_block = src[start:end]
+    assert upd in src
+    return src.replace(upd, "").replace(out_block, out_block + upd.replace("    ", "    ", 1))
+
+
+def _readback_before_decay(src):
+    """Read back (and update) before decaying: the printed order says decay first."""
+    start = src.index("    /* decay: every key channel")
+    mid = src.index("    /* read back the decayed state")
+    decay_block = src[start:mid]
+    src = src.replace(decay_block, "")
+    anchor = "    /* output from the updated state"
+    return src.replace(anchor, decay_block + anchor)
+
+
+@pytest.fixture(scope="module")
+def workdir(tmp_path_factory):
+    return tmp_path_factory.mktemp("mutants")
+
+
+def _run_pins(lib_path):
+    env = dict(os.environ, KDA_ORACLE_LIB=lib_path)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
+    return r.returncode, r.stdout[-2000:]
+
+
+def _build(workdir, name, src_text):
+    src = os.path.join(workdir, f"{name}.c")
+    with open(src, "w") as f:
+        f.write(src_text)
+    lib = os.path.join(workdir, f"lib_{name}.so")
+    oracle.build(out_path=lib, src=src, extra_flags=["-I", os.path.join(ROOT, "oracle"), "-w"])
+    return lib
+
+
+def test_unmutated_copy_passes(workdir):
+    lib = _build(workdir, "clean", open(SRC).read())
+    rc, out = _run_pins(lib)
+    assert rc == 0, out
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS) + ["pre_update_output", "readback_before_decay"])
+def test_mutant_is_caught(workdir, name):
+    src = open(SRC).read()
+    if name == "pre_update_output":
+        mutated = _pre_update_output(src)
+    elif name == "readback_before_decay":
+        mutated = _readback_before_decay(src)
+    else:
+        old, new = MUTANTS[name]
+        assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
+        mutated = src.replace(old, new)
+    assert mutated != src
+    rc, out = _run_pins(_build(workdir, name, mutated))
+    assert rc != 0, f"mutant {name} survived the pins:\n{out}"
