@@ -1,0 +1,193 @@
+"""Python binding of libkda, the MI355X Kimi Delta Attention (KDA) mixer.
+
+Thin ctypes layer over the C ABI declared in ``include/kda.h``: it checks
+tensor shapes/dtypes/devices, allocates outputs with torch (device memory and
+streams are torch's job), and passes raw device pointers plus torch's current
+HIP stream.  Every step of the computation runs in the HIP kernels of
+``libkda.so``; there is no CPU or PyTorch fallback, and importing this package
+fails if the library has not been built (``python -m gated_delta_rule_67_amd.build``).
+
+    out, final_state = chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None)
+    out = step(q, k, v, log_g, beta, state)        # state updated in place
+
+Argument order follows ``_torch_recurrent_kda(q, k, v, g, beta, cu_seqlens)`` of
+NeMo glm5_next.layers; q/k/v/g are [batch, seq, heads, head_dim], beta is
+[batch, seq, heads].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = ["chunk_fwd", "step", "workspace_bytes", "abi_version", "KdaError", "LIB_PATH",
+           "KDA_F32", "KDA_BF16"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
+KDA_F32, KDA_BF16 = 0, 1
+_STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
+           4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_HIP"}
+
+
+class KdaDesc(ctypes.Structure):
+    """Mirror of ``kda_desc`` in include/kda.h."""
+    _fields_ = [("num_seqs", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
+                ("qkv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def _load(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(f"libkda.so not found at {path}; build it with "
+                          "`python -m gated_delta_rule_67_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    P, D = ctypes.c_void_p, ctypes.POINTER(KdaDesc)
+    lib.kda_abi_version.restype = ctypes.c_int
+    lib.kda_abi_version.argtypes = []
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    lib.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_chunk_workspace_bytes.argtypes = [D]
+    lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+    lib.kda_step.restype = ctypes.c_int
+    lib.kda_step.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    return lib
+
+
+lib = _load()
+
+
+def abi_version() -> int:
+    return lib.kda_abi_version()
+
+
+def _check(status: int):
+    if status != 0:
+        raise KdaError(status, lib.kda_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def _need(t, name, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_desc(num_seqs, seq_len, H, dk, dv, qkv_dtype, scale=None, workspace=None) -> KdaDesc:
+    d = KdaDesc()
+    d.num_seqs, d.seq_len, d.num_heads, d.dk, d.dv = num_seqs, seq_len, H, dk, dv
+    d.qkv_dtype, d.out_dtype = qkv_dtype, KDA_F32
+    d.scale = 0.0 if scale is None else float(scale)
+    if workspace is not None:
+        d.workspace, d.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    return d
+
+
+def workspace_bytes(num_docs: int, H: int, d: int) -> int:
+    desc = make_desc(num_docs, 0, H, d, d, KDA_BF16)
+    return lib.kda_chunk_workspace_bytes(ctypes.byref(desc))
+
+
+def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None,
+              out=None, final_state=None, workspace=None, stream=None):
+    """Chunked prefill.  Returns (out [B,T,H,dv] fp32, final_state [N,H,dk,dv] fp32).
+
+    Dense: B sequences.  Packed: B == 1 and int32 ``cu_seqlens`` [N+1] on the
+    device splits the row into N documents.  ``init_state`` [N,H,dk,dv] or None
+    (zeros).  ``final_state`` may be passed (and may be ``init_state`` itself
+    for an in-place resume); pass ``final_state=False`` to skip it.
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _need(k, "k", (B, T, H, dk), dt, dev)
+    _need(q, "q", (B, T, H, dk), dt, dev)
+    _need(v, "v", (B, T, H, dv), dt, dev)
+    _need(log_g, "log_g", (B, T, H, dk), torch.float32, dev)
+    _need(beta, "beta", (B, T, H), torch.float32, dev)
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed mode takes a single row (B == 1)")
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
+        N, L = cu_seqlens.shape[0] - 1, T
+    else:
+        N, L = B, T
+    if init_state is not None:
+        _need(init_state, "init_state", (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (B, T, H, dv), torch.float32, dev)
+    if final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    else:
+        _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
+    desc = make_desc(N, L, H, dk, dv, code, scale)
+    if cu_seqlens is not None:
+        need = lib.kda_chunk_workspace_bytes(ctypes.byref(desc))
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        desc.workspace, desc.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.kda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
+                             _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
+                             _stream(stream)))
+    return out, final_state
+
+
+def step(q, k, v, log_g, beta, state, scale=None, out=None, stream=None):
+    """Decode (n_tok = 1) or multi-row verify: rows [N, n_tok, H, d] applied in
+    order to ``state`` [N, H, dk, dv] (fp32), which is updated in place.
+    Returns out [N, n_tok, H, dv] fp32."""
+    N, n_tok, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _need(k, "k", (N, n_tok, H, dk), dt, dev)
+    _need(v, "v", (N, n_tok, H, dv), dt, dev)
+    _need(log_g, "log_g", (N, n_tok, H, dk), torch.float32, dev)
+    _need(beta, "beta", (N, n_tok, H), torch.float32, dev)
+    _need(state, "state", (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, n_tok, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (N, n_tok, H, dv), torch.float32, dev)
+    desc = make_desc(N, n_tok, H, dk, dv, code, scale)
+    _check(lib.kda_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
+                        _ptr(state), ctypes.c_int32(n_tok), _ptr(out), _stream(stream)))
+    return out

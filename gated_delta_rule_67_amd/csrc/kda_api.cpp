@@ -1,0 +1,170 @@
+// kda_api.cpp -- the C ABI of libkda: argument validation and kernel dispatch.
+//
+// Every host-visible argument is checked before anything is enqueued and
+// before any HIP runtime call, so a rejected call touches neither the device
+// nor the outputs.  Errors are returned as kda_status with a thread-local
+// detail string; nothing throws across the ABI.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "kda_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kda_status fail(kda_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// Checks shared by both entry points: descriptor fields.
+kda_status check_desc(const kda_desc* d, const char* fn) {
+  if (!d) return fail(KDA_ERR_NULL, "%s: desc is NULL", fn);
+  if (d->num_seqs < 0 || d->num_heads <= 0 || d->dk <= 0 || d->dv <= 0)
+    return fail(KDA_ERR_SHAPE, "%s: need num_seqs >= 0, num_heads > 0, dk > 0, dv > 0 (got %d, %d, %d, %d)",
+                fn, d->num_seqs, d->num_heads, d->dk, d->dv);
+  if (d->qkv_dtype != KDA_F32 && d->qkv_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "%s: unknown qkv_dtype %d", fn, d->qkv_dtype);
+  if (d->out_dtype != KDA_F32 && d->out_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "%s: unknown out_dtype %d", fn, d->out_dtype);
+  if (!std::isfinite(d->scale))
+    return fail(KDA_ERR_SHAPE, "%s: scale must be finite", fn);
+  if (d->dk != d->dv)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: dk != dv (%d vs %d) is not supported", fn, d->dk, d->dv);
+  if (d->dk != 16 && d->dk != 32 && d->dk != 64 && d->dk != 128)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: head dim %d not in {16, 32, 64, 128}", fn, d->dk);
+  if (d->out_dtype != KDA_F32)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: only fp32 out is supported", fn);
+  if (static_cast<int64_t>(d->num_seqs) * d->num_heads > (1 << 26))
+    return fail(KDA_ERR_SHAPE, "%s: num_seqs * num_heads too large", fn);
+  return KDA_OK;
+}
+
+float resolve_scale(const kda_desc* d) {
+  return d->scale != 0.0f ? d->scale : 1.0f / std::sqrt(static_cast<float>(d->dk));
+}
+
+kda_status check_ptr(const void* p, const char* name, const char* fn, bool required) {
+  if (!p) return required ? fail(KDA_ERR_NULL, "%s: %s is NULL", fn, name) : KDA_OK;
+  if (misaligned(p)) return fail(KDA_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, name);
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "required pointer is NULL";
+    case KDA_ERR_SHAPE: return "invalid shape or argument";
+    case KDA_ERR_DTYPE: return "unknown dtype";
+    case KDA_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KDA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+size_t kda_chunk_workspace_bytes(const kda_desc* d) {
+  if (!d) return 0;
+  return kda::chunk_workspace_bytes(d->num_seqs, true);
+}
+
+kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const void* v,
+                         const float* log_g, const float* beta, const float* init_state,
+                         const int32_t* cu_seqlens, void* out, float* final_state, void* stream) {
+  static const char* fn = "kda_chunk_fwd";
+  kda_status st = check_desc(d, fn);
+  if (st != KDA_OK) return st;
+  if (d->seq_len < 0) return fail(KDA_ERR_SHAPE, "%s: seq_len < 0", fn);
+  const bool packed = cu_seqlens != nullptr;
+  const int64_t tokens = packed ? d->seq_len : static_cast<int64_t>(d->num_seqs) * d->seq_len;
+  if (tokens > INT32_MAX / 2) return fail(KDA_ERR_SHAPE, "%s: too many tokens (%lld)", fn, (long long)tokens);
+  if (packed && d->num_seqs == 0 && d->seq_len != 0)
+    return fail(KDA_ERR_SHAPE, "%s: packed problem with tokens but no documents", fn);
+  const bool has_tok = tokens > 0;
+  const bool has_units = d->num_seqs > 0;
+  if ((st = check_ptr(q, "q", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(k, "k", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(v, "v", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(log_g, "log_g", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(beta, "beta", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(out, "out", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(init_state, "init_state", fn, false)) != KDA_OK) return st;
+  if ((st = check_ptr(final_state, "final_state", fn, false)) != KDA_OK) return st;
+  if ((st = check_ptr(cu_seqlens, "cu_seqlens", fn, false)) != KDA_OK) return st;
+  if (out && (out == q || out == k || out == v || out == log_g || out == beta || out == init_state))
+    return fail(KDA_ERR_SHAPE, "%s: out aliases an input", fn);
+  const size_t ws_need = kda::chunk_workspace_bytes(d->num_seqs, packed);
+  if (ws_need > 0) {
+    if (!d->workspace || d->workspace_bytes < ws_need)
+      return fail(KDA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, ws_need,
+                  d->workspace ? d->workspace_bytes : size_t(0));
+    if (misaligned(d->workspace)) return fail(KDA_ERR_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+  }
+  if (!has_units || (!has_tok && !final_state)) return KDA_OK;
+
+  kda::ChunkLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
+  a.init_state = init_state; a.cu_seqlens = cu_seqlens;
+  a.out = out; a.final_state = final_state;
+  a.doc_order = packed ? static_cast<int32_t*>(d->workspace) : nullptr;
+  a.num_seqs = d->num_seqs; a.seq_len = d->seq_len; a.num_heads = d->num_heads;
+  a.d = d->dk; a.bf16 = d->qkv_dtype == KDA_BF16; a.scale = resolve_scale(d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = kda::chunk_mfma_supported(a) ? kda::launch_chunk_mfma(a, s)
+                                                     : kda::launch_chunk_recurrent(a, s);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return KDA_OK;
+}
+
+kda_status kda_step(const kda_desc* d, const void* q, const void* k, const void* v,
+                    const float* log_g, const float* beta, float* state_inout, int32_t n_tok,
+                    void* out, void* stream) {
+  static const char* fn = "kda_step";
+  kda_status st = check_desc(d, fn);
+  if (st != KDA_OK) return st;
+  if (n_tok < 1) return fail(KDA_ERR_SHAPE, "%s: n_tok must be >= 1 (got %d)", fn, n_tok);
+  if (static_cast<int64_t>(d->num_seqs) * n_tok > INT32_MAX / 2)
+    return fail(KDA_ERR_SHAPE, "%s: num_seqs * n_tok too large", fn);
+  const bool any = d->num_seqs > 0;
+  if ((st = check_ptr(q, "q", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(k, "k", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(v, "v", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(log_g, "log_g", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(beta, "beta", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(state_inout, "state_inout", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(out, "out", fn, any)) != KDA_OK) return st;
+  if (out && (out == q || out == k || out == v || out == log_g || out == beta || out == state_inout))
+    return fail(KDA_ERR_SHAPE, "%s: out aliases an input", fn);
+  if (!any) return KDA_OK;
+
+  kda::StepLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
+  a.state = state_inout; a.out = out;
+  a.num_seqs = d->num_seqs; a.n_tok = n_tok; a.num_heads = d->num_heads;
+  a.d = d->dk; a.bf16 = d->qkv_dtype == KDA_BF16; a.scale = resolve_scale(d);
+  const hipError_t e = kda::launch_step(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return KDA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+/*
+ * kda.h -- C ABI of libkda, the MI355X (gfx950) Kimi Delta Attention mixer.
+ *
+ * The operation (GLM-5.3-Flash model notes, Glm5NextTextLinearAttention snippet;
+ * NeMo glm5_next.layers, `_torch_recurrent_kda`): for every unit u = (sequence or
+ * packed document n, head h) a per-head fp32 state S[dk][dv] (row i = key
+ * channel i, column j = value channel j) runs, token by token,
+ *
+ *     S[i,:]   *= exp(log_g[t,h,i])              each key channel decays by its gate
+ *     kv        = S^T k_t                        the state's prediction for k_t
+ *     delta     = beta[t,h] * (v_t - kv)         scaled prediction error
+ *     S        += k_t delta^T                    rank-1 delta-rule update
+ *     out[t,h,:] = scale * S^T q_t               read from the updated state
+ *
+ * Packed documents never share state: each starts from its own initial state
+ * (NeMo glm5_next.layers, `Glm5NextLinearAttention.forward`: KDA runs "without
+ * crossing documents"; `_torch_recurrent_kda`: packed boundaries reset the state).
+ *
+ * Conventions for every entry point
+ *  - Tensors are row-major with the last axis contiguous:
+ *      q, k, log_g : [batch, seq, heads, dk]     v, out : [batch, seq, heads, dv]
+ *      beta        : [batch, seq, heads]         states : [N, heads, dk, dv]
+ *    (the [batch, sequence, heads, head_dim] layout of `_torch_recurrent_kda`).
+ *  - q, k, v have element type desc->qkv_dtype (fp32 or bf16); log_g, beta and
+ *    states are fp32; out has element type desc->out_dtype (fp32 only in v1).
+ *  - Every data pointer is a DEVICE pointer owned by the caller and must be
+ *    16-byte aligned.  The library never allocates, frees or caches device
+ *    memory; scratch comes from desc->workspace.  The descriptor itself is host
+ *    memory and is read only during the call.
+ *  - All work is enqueued on `stream` (a hipStream_t; NULL = the null stream).
+ *    KDA_OK means "validated and enqueued"; faults inside a kernel surface at
+ *    the caller's next synchronisation.  No entry point synchronises.
+ *  - Host-visible arguments are validated before anything is enqueued; a
+ *    non-OK status leaves every output untouched.  kda_last_error() then
+ *    describes the failure (thread-local string).  Nothing throws or aborts
+ *    across the ABI.
+ *  - Preconditions the library does not check (they live in device memory):
+ *    log_g <= 0 (log_g = -inf allowed), cu_seqlens well formed.
+ *  - Supported in v1: dk == dv in {16, 32, 64, 128}; qkv_dtype fp32 or bf16;
+ *    out_dtype fp32.  Anything else returns KDA_ERR_UNSUPPORTED.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  KDA_ERR_SHAPE = 2,       /* a dimension is <= 0, too large, or inconsistent */
+  KDA_ERR_DTYPE = 3,       /* unknown dtype code                              */
+  KDA_ERR_ALIGN = 4,       /* a data pointer is not 16-byte aligned           */
+  KDA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required      */
+  KDA_ERR_UNSUPPORTED = 6, /* valid but not implemented (dk != dv, d, out)    */
+  KDA_ERR_HIP = 7          /* a HIP runtime call or kernel launch failed      */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Problem descriptor (host memory). */
+typedef struct kda_desc {
+  int32_t num_seqs;  /* dense: batch B; packed: number of documents N           */
+  int32_t seq_len;   /* dense: tokens per sequence T; packed: total tokens.
+                        Not read by kda_step (it takes n_tok)                   */
+  int32_t num_heads; /* H, shared by q, k, v                                     */
+  int32_t dk;        /* key / query head dim  (rows of S)                        */
+  int32_t dv;        /* value head dim        (columns of S)                     */
+  int32_t qkv_dtype; /* kda_dtype of q, k, v                                     */
+  int32_t out_dtype; /* kda_dtype of out (KDA_F32)                               */
+  float scale;       /* output scale; 0 selects dk^-0.5                          */
+  void* workspace;   /* device scratch, >= kda_chunk_workspace_bytes(desc)       */
+  size_t workspace_bytes;
+} kda_desc;
+
+/* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
+int kda_abi_version(void);
+
+/* Static description of a status code. Never NULL. */
+const char* kda_status_string(kda_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Device scratch bytes a packed kda_chunk_fwd call (cu_seqlens != NULL) needs
+ * for this descriptor: a few bytes per document for the longest-first document
+ * order.  Dense calls need no workspace (desc->workspace may then be NULL).
+ * Returns 0 for a NULL descriptor. */
+size_t kda_chunk_workspace_bytes(const kda_desc* desc);
+
+/*
+ * Chunked prefill (dense batch or packed varlen).
+ *
+ *   q, k, log_g  [B, T, H, dk];  v [B, T, H, dv];  beta [B, T, H]
+ *   init_state   [N, H, dk, dv] fp32, or NULL for zeros
+ *   cu_seqlens   device int32 [N+1] (cu[0] = 0, non-decreasing, cu[N] = T), or
+ *                NULL for a dense batch of B = num_seqs sequences of T tokens
+ *                (packed: B = 1, T = seq_len total tokens, N = num_seqs docs)
+ *   out          [B, T, H, dv] (out_dtype)
+ *   final_state  [N, H, dk, dv] fp32, or NULL to skip; may alias init_state
+ *                (in-place resume) but nothing else
+ *
+ * Evaluated in chunks of 64 tokens (within a document) with fp32 state and fp32
+ * accumulation; out must not alias any input.  Zero-length documents are
+ * allowed (their final state is their initial state).
+ */
+kda_status kda_chunk_fwd(const kda_desc* desc, const void* q, const void* k,
+                         const void* v, const float* log_g, const float* beta,
+                         const float* init_state, const int32_t* cu_seqlens,
+                         void* out, float* final_state, void* stream);
+
+/*
+ * Decode / multi-row verify, updating the state in place.
+ *
+ *   q, k, log_g [N, n_tok, H, dk];  v [N, n_tok, H, dv];  beta [N, n_tok, H]
+ *   state_inout [N, H, dk, dv] fp32, read once and written once
+ *   out         [N, n_tok, H, dv] (out_dtype): row t's output, read from the
+ *               state after rows 0..t of that sequence
+ *
+ * Rows of one sequence are applied in order t = 0 .. n_tok-1 (metrale
+ * glm5next_layer invariants: verify row t uses slot t; decode is n_tok = 1).
+ * N = desc->num_seqs; desc->seq_len is ignored; no workspace is used.
+ */
+kda_status kda_step(const kda_desc* desc, const void* q, const void* k,
+                    const void* v, const float* log_g, const float* beta,
+                    float* state_inout, int32_t n_tok, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

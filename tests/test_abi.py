@@ -1,0 +1,191 @@
+"""The C ABI of libkda on the CPU: it loads, exports what include/kda.h
+declares, and rejects bad arguments synchronously, before any HIP call.
+
+Calls here never reach a kernel: each one fails validation (or is an empty
+problem) and returns before the runtime is touched.  Non-NULL pointers are
+fake 16-byte-aligned addresses that are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+kda = pytest.importorskip("gated_delta_rule_67_amd")
+lib = kda.lib
+
+FAKE = 0x7f0000000000  # aligned, never dereferenced
+OK, NULL, SHAPE, DTYPE, ALIGN, WORKSPACE, UNSUPPORTED, HIP = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert {"kda_chunk_fwd", "kda_step", "kda_chunk_workspace_bytes", "kda_status_string",
+            "kda_last_error", "kda_abi_version"} <= set(names)
+    raw = ctypes.CDLL(kda.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), f"{n} declared in kda.h but not exported"
+
+
+def test_abi_version_and_status_strings():
+    assert kda.abi_version() == 1
+    seen = set()
+    for code in range(8):
+        s = lib.kda_status_string(code).decode()
+        assert s and s not in seen
+        seen.add(s)
+    assert lib.kda_status_string(99).decode() == "unknown status"
+
+
+def desc(**kw):
+    base = dict(num_seqs=2, seq_len=64, H=4, dk=128, dv=128, qkv_dtype=kda.KDA_BF16)
+    base.update(kw)
+    d = kda.make_desc(base["num_seqs"], base["seq_len"], base["H"], base["dk"], base["dv"],
+                      base["qkv_dtype"], base.get("scale"))
+    for f in ("out_dtype", "workspace", "workspace_bytes"):
+        if f in kw:
+            setattr(d, f, kw[f])
+    return d
+
+
+def P(off=0):
+    return ctypes.c_void_p(FAKE + off)
+
+
+def chunk(d, q=P(0), k=P(1 << 20), v=P(2 << 20), g=P(3 << 20), b=P(4 << 20), s0=None, cu=None,
+          out=P(5 << 20), fin=None):
+    return lib.kda_chunk_fwd(ctypes.byref(d) if d is not None else None, q, k, v, g, b, s0, cu,
+                             out, fin, None)
+
+
+def step(d, n_tok=1, q=P(0), k=P(1 << 20), v=P(2 << 20), g=P(3 << 20), b=P(4 << 20),
+         s=P(6 << 20), out=P(5 << 20)):
+    return lib.kda_step(ctypes.byref(d) if d is not None else None, q, k, v, g, b, s, n_tok, out, None)
+
+
+def last():
+    return lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("call", [chunk, step])
+def test_null_desc(call):
+    assert call(None) == NULL
+    assert "desc" in last()
+
+
+@pytest.mark.parametrize("field,value", [("num_seqs", -1), ("H", 0), ("dk", 0), ("dv", -4)])
+def test_bad_dims(field, value):
+    assert chunk(desc(**{field: value})) == SHAPE
+    assert step(desc(**{field: value})) == SHAPE
+
+
+def test_bad_dtype_codes():
+    assert chunk(desc(qkv_dtype=7)) == DTYPE
+    assert step(desc(qkv_dtype=-1)) == DTYPE
+    assert chunk(desc(out_dtype=5)) == DTYPE
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 64), (48, 48), (256, 256), (8, 8)])
+def test_unsupported_dims(dk, dv):
+    assert chunk(desc(dk=dk, dv=dv)) == UNSUPPORTED
+    assert step(desc(dk=dk, dv=dv)) == UNSUPPORTED
+    assert "kda_" in last()
+
+
+def test_bf16_out_unsupported():
+    assert chunk(desc(out_dtype=kda.KDA_BF16)) == UNSUPPORTED
+
+
+def test_non_finite_scale():
+    assert chunk(desc(scale=float("inf"))) == SHAPE
+    assert step(desc(scale=float("nan"))) == SHAPE
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "g", "b", "out"])
+def test_null_required_pointer(arg):
+    assert chunk(desc(), **{arg: None}) == NULL
+    assert arg.replace("g", "log_g").replace("b", "beta") in last() or arg in last()
+    assert step(desc(), **{arg: None}) == NULL
+
+
+def test_null_state_for_step():
+    assert step(desc(), s=None) == NULL
+    assert "state_inout" in last()
+
+
+@pytest.mark.parametrize("arg", ["q", "k", "v", "g", "b", "out", "s0", "fin"])
+def test_misaligned_pointer(arg):
+    assert chunk(desc(), **{arg: P(8)}) == ALIGN
+
+
+def test_misaligned_step_state():
+    assert step(desc(), s=P(4)) == ALIGN
+
+
+def test_step_needs_rows():
+    assert step(desc(), n_tok=0) == SHAPE
+    assert step(desc(), n_tok=-3) == SHAPE
+
+
+def test_out_must_not_alias():
+    assert chunk(desc(), out=P(0)) == SHAPE
+    assert step(desc(), out=P(6 << 20)) == SHAPE
+
+
+def test_packed_needs_workspace():
+    d = desc(num_seqs=5, seq_len=1000)
+    assert chunk(d, cu=P(7 << 20)) == WORKSPACE
+    need = lib.kda_chunk_workspace_bytes(ctypes.byref(d))
+    assert need >= 5 * 4
+    d.workspace, d.workspace_bytes = FAKE + (8 << 20), need - 1
+    assert chunk(d, cu=P(7 << 20)) == WORKSPACE
+    d.workspace = FAKE + (8 << 20) + 4
+    d.workspace_bytes = need
+    assert chunk(d, cu=P(7 << 20)) == ALIGN
+
+
+def test_packed_tokens_without_documents():
+    d = desc(num_seqs=0, seq_len=10)
+    d.workspace, d.workspace_bytes = FAKE + (8 << 20), 4096
+    assert chunk(d, cu=P(7 << 20)) == SHAPE
+
+
+def test_empty_problems_are_noops():
+    # no sequences: nothing to do, nothing enqueued, NULL tensors accepted
+    assert chunk(desc(num_seqs=0), q=None, k=None, v=None, g=None, b=None, out=None) == OK
+    assert step(desc(num_seqs=0), q=None, k=None, v=None, g=None, b=None, s=None, out=None) == OK
+    # dense sequences of zero tokens and no final state: nothing to write
+    assert chunk(desc(seq_len=0), q=None, k=None, v=None, g=None, b=None, out=None) == OK
+
+
+def test_workspace_bytes_dense_and_null():
+    assert lib.kda_chunk_workspace_bytes(None) == 0
+    assert kda.workspace_bytes(26, 32, 128) >= 26 * 4
+
+
+def test_last_error_is_thread_local():
+    import threading
+    assert chunk(desc(dk=48, dv=48)) == UNSUPPORTED
+    mine = last()
+    other = []
+
+    def worker():
+        other.append(lib.kda_last_error().decode())
+        step(desc(), n_tok=0)
+        other.append(lib.kda_last_error().decode())
+
+    t = threading.Thread(target=worker)
+    t.start()
+    t.join()
+    assert other[0] == ""
+    assert "n_tok" in other[1]
+    assert last() == mine
