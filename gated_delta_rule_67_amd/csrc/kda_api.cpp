@@ -11,6 +11,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 
 #include "kda_launch.h"
 
@@ -24,6 +26,13 @@ kda_status fail(kda_status st, const char* fmt, ...) {
   std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
   return st;
+}
+
+// Prefill path selection: KDA_PREFILL_PATH=recurrent forces the token-recurrent
+// kernel, =chunk (or unset) lets the chunked MFMA kernel take what it supports.
+bool force_recurrent() {
+  const char* e = std::getenv("KDA_PREFILL_PATH");
+  return e && std::strcmp(e, "recurrent") == 0;
 }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -130,8 +139,9 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
   a.num_seqs = d->num_seqs; a.seq_len = d->seq_len; a.num_heads = d->num_heads;
   a.d = d->dk; a.bf16 = d->qkv_dtype == KDA_BF16; a.scale = resolve_scale(d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = kda::chunk_mfma_supported(a) ? kda::launch_chunk_mfma(a, s)
-                                                     : kda::launch_chunk_recurrent(a, s);
+  const hipError_t e = (kda::chunk_mfma_supported(a) && !force_recurrent())
+                           ? kda::launch_chunk_mfma(a, s)
+                           : kda::launch_chunk_recurrent(a, s);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
   return KDA_OK;
 }
