@@ -12,28 +12,38 @@
 //   S_next   = exp(gamma) S + (K exp(gamma - G))^T Delta
 // (the output reads the state after each token's update).
 //
-// One workgroup (4 waves) owns one (unit, 32-column value tile) and walks the
-// unit's chunks in order with its fp32 state tile S[128][32] resident in MFMA
-// accumulator registers.  Value columns are independent, so a unit's 4 tiles
-// run as 4 workgroups (placed on one XCD so they share q/k/log_g in its L2).
+// Work split.  One workgroup owns one (unit, 32-column value tile); a unit's
+// four tiles run as four workgroups placed on one XCD so that they share the
+// unit's q/k/log_g rows in that XCD's L2 (value columns never interact).  Its
+// four waves are software-pipelined over chunks: in each of the three phases
+// per chunk a wave does producer work for chunk k+1 (gate products and
+// decay-scaled operands, the 64x64 products A and Aqk, the inverses of the
+// four 16x16 diagonal blocks of (I + A)) and consumer work for chunk k
+// (everything that needs the state: (K exp G) S and (Q exp G) S, Delta by
+// blocked forward substitution, the outputs and the state update), so VALU
+// gate work overlaps MFMA chains inside one wave.  The fp32 state tile
+// S[128][32] stays in MFMA accumulator registers for the whole unit; global
+// loads of chunk k+2 are issued a full chunk before use; three LDS-only
+// barriers separate the phases.
 //
 // Decay factors without overflow.  The chunk is cut into four 16-token blocks.
-// For block I with reference R_I = G at its first token's predecessor:
+// With R_I = G before block I's first token:
 //   Kl = k exp(G - R_I) <= |k|, Ql = q exp(G - R_I), Kr = k exp(R_{I+1} - G) <= |k|
-// come from prefix / suffix products of exp(log_g) inside the block (thread
-// local).  Off-diagonal tiles (I > J) of A and Aqk use Kl_I * exp(R_I - R_{J+1})
-// against Kr_J: every factor is <= 1 for any gate.  Diagonal tiles use a
-// mid-block reference M_I (after the block's 8th token): Kl_I * exp(R_I - M_I)
-// against Kr_I * exp(M_I - R_{I+1}); these factors are >= 1 and are bounded by
-// exp(HALF_SPAN_MAX).  A chunk whose half-block decay exceeds that bound, or
-// whose inputs could overflow the fp16 MFMA operands, is evaluated token by
-// token (exact fp32) instead, inside this kernel.
+// come from prefix / suffix products of exp(log_g) inside a block (thread
+// local).  Off-diagonal tiles (I > J) pair Kl_I exp(R_I - R_{J+1}) with Kr_J:
+// every factor is <= 1 for any gate.  Diagonal tiles use the block's midpoint
+// M_I as reference: Kl_I exp(R_I - M_I) against Kr_I exp(M_I - R_{I+1}); these
+// factors are >= 1, bounded by exp(HALF_SPAN_MAX).  A chunk whose half-block
+// decay exceeds the bound, whose inputs could overflow an fp16 operand, or
+// whose diagonal blocks of A exceed 1 in magnitude, is evaluated token by
+// token (exact fp32) inside this kernel instead.
 //
 // Arithmetic: fp16 MFMA operands (bf16 q/k/v convert exactly), fp32
-// accumulation, fp32 state and outputs.  (I + A)^-1 is applied by blocked
-// forward substitution: the four 16x16 diagonal blocks are inverted in fp32 on
-// the VALU, then Delta_I = T_II (X_I - sum_{J<I} A_IJ Delta_J) chains 16x16x16
-// MFMAs whose C-layout outputs are directly the next B operands.
+// accumulation, state and outputs.  With L a strictly lower 16x16 diagonal
+// block of A (|L| <= 1, L^16 = 0), (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8)
+// is formed with 16x16x16 MFMAs.  Products whose result feeds another MFMA
+// as its A operand are computed transposed (C = B^T A^T), so the result
+// already sits in the A-operand lane layout and is stored fragment-major.
 #include "kda_common.h"
 #include "kda_launch.h"
 
@@ -45,22 +55,26 @@ typedef f16 f16x2 __attribute__((ext_vector_type(2)));
 typedef f16 f16x4 __attribute__((ext_vector_type(4)));
 typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int C = 64;        // chunk length
 constexpr int D = 128;       // head dim (dk = dv)
 constexpr int DVT = 32;      // value columns per workgroup
 constexpr int NTILE = D / DVT;
-constexpr int NT = 256;      // threads (4 waves)
+constexpr int NT = 256;      // threads: 4 waves, each with a producer and a consumer part
 constexpr int LDK = D + 8;   // fp16 row stride of [64][128] matrices
 constexpr int LDT = C + 8;   // fp16 row stride of [*][64] matrices
-constexpr int LDA = C + 4;   // fp32 row stride of A
-constexpr int LDV = DVT + 4; // fp32 row stride of V
-constexpr float HALF_SPAN_MAX = 6.0f;   // max decay (in e-folds) over half a block
-constexpr float QK_MAX = 64.0f;         // |q|, |k| bound of the fast path
+constexpr int LDV = DVT + 8; // fp16 row stride of the value tile
+constexpr float HALF_SPAN_MAX = 6.0f;   // max decay (e-folds) over half a block
+constexpr unsigned short QK_MAX_BITS = 0x4280;  // bf16 bits of 64.0: |q|, |k| bound
 constexpr float V_MAX = 4096.0f;        // |v| bound of the fast path
 constexpr float S_MAX = 2048.0f;        // |S| bound of the fast path
-constexpr float BETA_MAX = 2.0f;        // |beta| bound of the fast path
+constexpr float BETA_MAX = 1.0f;        // |beta| bound of the fast path
 constexpr int FB_TG = 16;               // tokens staged per pass in the fallback
+
+// fragment slots per chunk buffer: 0-3 diagonal inverses T_II, 4-9 A_IJ
+// (I > J), 10-19 Aqk lower tiles; each slot holds one f16x4 per lane.
+constexpr int SLOT_A = 4, SLOT_Q = 10, NSLOT = 20;
 
 struct ChunkArgs {
   const bf16_t* q;
@@ -79,36 +93,52 @@ struct ChunkArgs {
   float scale;
 };
 
-struct __align__(16) Smem {
-  f16 Kl[C][LDK];       // k exp(G - R_blk)            (also fallback staging)
-  f16 Ql[C][LDK];       // q exp(G - R_blk)
-  f16 Kr[C][LDK];       // k exp(R_blk_end - G)
-  f16 KdT[D][LDT];      // (k exp(gamma - G))^T        [channel][token]
-  f16 ST[DVT][LDK];     // S^T in fp16                 [value col][channel]
-  float A32[C][LDA];    // beta_i * P, strictly lower (fp32, diagonal inverses read it)
-  f16 Ah[C][LDT];       // same in fp16 (off-diagonal blocks feed the substitution)
-  f16 Aqk[C][LDT];      // q k decay products, lower incl. diagonal
-  f16 Td[4][16][20];    // inverses of the four diagonal blocks of (I + A)
-  f16 DT[DVT][LDT];     // Delta^T                     [value col][token]
-  float V[C][LDV];      // value tile of the chunk (fp32)
-  float beta[C];
-  float tot[4][D];      // per-block products of exp(log_g)
-  f16 fR[4][D];         // exp(R_I)
-  f16 fOff[6][D];       // exp(R_I - R_{J+1}), I > J
-  f16 fDl[4][D];        // exp(R_I - M_I)
-  f16 fDr[4][D];        // exp(M_I - R_{I+1})
-  float fGam[D];        // exp(gamma)
-  float red[2][4][DVT][2];  // fallback column reductions
-  float kq[FB_TG];
-};
-
-// Fallback staging aliases the fast-path operand buffers.
 struct FbStage {
   float a[FB_TG][D];
   float k[FB_TG][D];
   float q[FB_TG][D];
+  float v[FB_TG][DVT];
+  float beta[FB_TG];
+  float kq[FB_TG];
+  float red[2][4][DVT][2];
 };
-static_assert(sizeof(FbStage) <= 3 * sizeof(f16) * C * LDK, "fallback staging does not fit");
+
+// Kr and KdT are dead while a chunk is evaluated token by token, so the
+// fallback's staging area overlays them.
+struct KrKd {
+  f16 Kr[C][LDK];          // k exp(R_blk_end - G)   (producer only)
+  f16 KdT[D][LDT];         // (k exp(gamma - G))^T   [channel][token]
+};
+
+struct __align__(16) Smem {
+  f16 Kl[2][C][LDK];       // k exp(G - R_blk), by chunk parity
+  f16 Ql[2][C][LDK];       // q exp(G - R_blk), by chunk parity
+  union {
+    KrKd kk;
+    FbStage fb;
+  } u;
+  f16 V[2][C][LDV];        // value tile (fp16), by chunk parity
+  float beta[2][C];
+  float tot[4][D];         // per-block products of exp(log_g)   (producer only)
+  f16 fDl[4][D];           // exp(R_I - M_I)                     (producer only)
+  f16 fDr[4][D];           // exp(M_I - R_{I+1})                 (producer only)
+  f16 fOff[3][D];          // exp(R_I - R_{J+1}) for (2,0), (3,0), (3,1)
+  f16 fR[2][4][D];         // exp(R_I), by chunk parity
+  float fGam[2][D];        // exp(gamma), by chunk parity
+  f16x4 frag[2][NSLOT][64];
+  f16 ST[DVT][LDK];        // S^T (fp16) for the consumers' products
+  f16 DT[DVT][LDT];        // Delta^T
+  int fbp[2][4];           // producer waves: chunk cannot take the fast path
+  int sbp[4];              // consumer waves: state beyond the fast-path bound
+};
+static_assert(sizeof(FbStage) <= sizeof(KrKd), "fallback staging does not fit");
+
+// Whether the chunk in buffer buf must be evaluated token by token: a
+// producer wave flagged it, or the state left the fast path's range.
+__device__ __forceinline__ bool fast_path_blocked(const Smem& sm, int buf) {
+  return (sm.fbp[buf][0] | sm.fbp[buf][1] | sm.fbp[buf][2] | sm.fbp[buf][3] |
+          sm.sbp[0] | sm.sbp[1] | sm.sbp[2] | sm.sbp[3]) != 0;
+}
 
 __device__ __forceinline__ f32x4 mfma32(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -118,23 +148,26 @@ __device__ __forceinline__ f32x4 mfma16(f16x4 a, f16x4 b, f32x4 c) {
 }
 __device__ __forceinline__ f16x8 ld8(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
 __device__ __forceinline__ f16x4 ld4(const f16* p) { return *reinterpret_cast<const f16x4*>(p); }
-__device__ __forceinline__ f16x4 to_h4(f32x4 x) {
+__device__ __forceinline__ f16x4 h4(f32x4 x) {
   f16x4 r;
   r[0] = (f16)x[0]; r[1] = (f16)x[1]; r[2] = (f16)x[2]; r[3] = (f16)x[3];
   return r;
 }
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// (I, J) of the ten lower 16x16 tiles of a 64x64 matrix, and the index of the
-// off-diagonal pair in fOff.
-__device__ __forceinline__ void tile_ij(int t, int& I, int& J) {
-  // 0:(0,0) 1:(1,0) 2:(1,1) 3:(2,0) 4:(2,1) 5:(2,2) 6:(3,0) 7:(3,1) 8:(3,2) 9:(3,3)
-  I = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
-  J = t - (I * (I + 1)) / 2;
+// Workgroup barrier that orders LDS only: outstanding global loads (the
+// prefetch of the next chunk) and stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
-__device__ __forceinline__ int off_pair(int I, int J) { return (I * (I - 1)) / 2 + J; }  // I > J
 
-__global__ void __launch_bounds__(NT) doc_order_kernel(const int32_t* __restrict__ cu, int n,
-                                                       int32_t* __restrict__ order) {
+__device__ __forceinline__ int tile10(int I, int J) { return (I * (I + 1)) / 2 + J; }  // J <= I
+__device__ __forceinline__ int pair6(int I, int J) { return (I * (I - 1)) / 2 + J; }   // J < I
+
+__global__ void __launch_bounds__(256) doc_order_kernel(const int32_t* __restrict__ cu, int n,
+                                                        int32_t* __restrict__ order) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int li = cu[i + 1] - cu[i];
@@ -146,101 +179,140 @@ __global__ void __launch_bounds__(NT) doc_order_kernel(const int32_t* __restrict
   order[rank] = i;
 }
 
-// Token-by-token evaluation of one chunk (exact fp32), on the state held in
-// MFMA C layout: s[a][b][e] = S[32w + 16a + 4(l/16) + e][16b + (l%16)].
-__device__ void chunk_fallback(Smem& sm, f32x4 (&s)[2][2], const ChunkArgs& p, size_t tok0, int nv,
-                               int h, int col0) {
-  FbStage& st = *reinterpret_cast<FbStage*>(&sm.Kl[0][0]);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lc = lane & 15, lg = lane >> 4;
+// Raw inputs of one chunk as one producer thread loads them (16-byte loads):
+// rows 16*blk + 4*qt + j (j < 4) of channels 8*oct .. 8*oct+7, plus 8 values
+// of the value tile and one beta.
+struct Raw {
+  float4 g[4][2];
+  uint4 k[4];
+  uint4 q[4];
+  uint4 v;
+  float beta;
+};
+
+// What a producer thread carries from stage A to the end of the chunk's products.
+struct Prod {
+  bool bad;
+};
+
+// Token-by-token evaluation of chunk ck, exact fp32, on the state
+// s[a][b][e] = S[32w+16a+4lg+e][col0+16b+lc] (inlined, so the state stays in
+// registers).
+__device__ __forceinline__ void chunk_fallback(Smem& sm, f32x4 (&s)[2][2], const ChunkArgs& p,
+                                            size_t tok_begin, int ntok, int ck, int h, int col0) {
+  const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
+  const int cw = w;
   const int H = p.H;
+
+  FbStage& st = sm.u.fb;
+  const int nv = min(C, ntok - ck * C);
+  const size_t tok0 = tok_begin + static_cast<size_t>(ck) * C;
   for (int t0 = 0; t0 < nv; t0 += FB_TG) {
     const int tg = min(FB_TG, nv - t0);
-    __syncthreads();
+    lds_barrier();
     {
-      constexpr int PER = FB_TG * D / NT;  // elements per thread per pass
+      constexpr int PER = FB_TG * D / NT;
+      static_assert(FB_TG * D % NT == 0 && FB_TG * DVT % NT == 0, "fallback staging split");
       float la[PER], lk[PER], lq[PER];
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int idx = tid + u * NT, r = min(idx / D, tg - 1), c = idx % D;
+      for (int x = 0; x < PER; ++x) {
+        const int idx = tid + x * NT, r = min(idx / D, tg - 1), c = idx % D;
         const size_t row = (tok0 + t0 + r) * H + h;
-        la[u] = p.log_g[row * D + c];
-        lk[u] = to_f32(p.k[row * D + c]);
-        lq[u] = to_f32(p.q[row * D + c]);
+        la[x] = p.log_g[row * D + c];
+        lk[x] = to_f32(p.k[row * D + c]);
+        lq[x] = to_f32(p.q[row * D + c]);
+      }
+      constexpr int PV = FB_TG * DVT / NT;
+      float vv[PV];
+#pragma unroll
+      for (int x = 0; x < PV; ++x) {
+        const int idx = tid + x * NT, vr = idx / DVT, vcol = idx % DVT;
+        vv[x] = to_f32(p.v[((tok0 + t0 + min(vr, tg - 1)) * H + h) * D + col0 + vcol]);
+      }
+      const float bb = p.beta[(tok0 + t0 + min(tid & (FB_TG - 1), tg - 1)) * H + h];
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        const int idx = tid + x * NT, r = idx / D, c = idx % D;
+        st.a[r][c] = exp_fast(la[x]);
+        st.k[r][c] = lk[x];
+        st.q[r][c] = lq[x];
       }
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int idx = tid + u * NT, r = idx / D, c = idx % D;
-        st.a[r][c] = exp_fast(la[u]);
-        st.k[r][c] = lk[u];
-        st.q[r][c] = lq[u];
+      for (int x = 0; x < PV; ++x) {
+        const int idx = tid + x * NT;
+        st.v[idx / DVT][idx % DVT] = vv[x];
       }
+      if (tid < FB_TG) st.beta[tid] = bb;
     }
-    __syncthreads();
+    lds_barrier();
     {  // kq[r] = k_r . q_r : 16 lanes per token, 8 channels each
-      const int r = tid >> 4, c0 = (tid & 15) * 8;
+      const int r = tid >> 4, cc = (tid & 15) * 8;
       float acc = 0.f;
-      if (r < tg) {
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc += st.k[r][c0 + c] * st.q[r][c0 + c];
-      }
+      for (int c = 0; c < 8; ++c) acc += st.k[r][cc + c] * st.q[r][cc + c];
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) acc += __shfl_xor(acc, off);
-      if ((tid & 15) == 0 && r < tg) sm.kq[r] = acc;
+      for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
+      if ((tid & 15) == 0) st.kq[r] = acc;
     }
-    __syncthreads();
+    lds_barrier();
     for (int r = 0; r < tg; ++r) {
       const int par = (t0 + r) & 1;
-      float pa[2] = {0.f, 0.f}, pb[2] = {0.f, 0.f};
+      {
+        float pa[2] = {0.f, 0.f}, pb[2] = {0.f, 0.f};
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int c = 32 * w + 16 * a + 4 * lg + e;
-          const float al = st.a[r][c], kc = st.k[r][c], qc = st.q[r][c];
+          for (int e = 0; e < 4; ++e) {
+            const int c = 32 * cw + 16 * a + 4 * lg + e;
+            const float al = st.a[r][c], kc = st.k[r][c], qc = st.q[r][c];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              s[a][b][e] *= al;
+              pa[b] += s[a][b][e] * kc;
+              pb[b] += s[a][b][e] * qc;
+            }
+          }
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          pa[b] += __shfl_xor(pa[b], 16);
+          pa[b] += __shfl_xor(pa[b], 32);
+          pb[b] += __shfl_xor(pb[b], 16);
+          pb[b] += __shfl_xor(pb[b], 32);
+        }
+        if (lg == 0) {
 #pragma unroll
           for (int b = 0; b < 2; ++b) {
-            s[a][b][e] *= al;
-            pa[b] += s[a][b][e] * kc;
-            pb[b] += s[a][b][e] * qc;
+            st.red[par][cw][16 * b + lc][0] = pa[b];
+            st.red[par][cw][16 * b + lc][1] = pb[b];
           }
         }
       }
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        pa[b] += __shfl_xor(pa[b], 16); pa[b] += __shfl_xor(pa[b], 32);
-        pb[b] += __shfl_xor(pb[b], 16); pb[b] += __shfl_xor(pb[b], 32);
-      }
-      if (lg == 0) {
+      lds_barrier();
+      {
+        const float bt = st.beta[r], kq = st.kq[r];
+        float dl[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-          sm.red[par][w][16 * b + lc][0] = pa[b];
-          sm.red[par][w][16 * b + lc][1] = pb[b];
+          const int n = 16 * b + lc;
+          float A = 0.f, B = 0.f;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            A += st.red[par][x][n][0];
+            B += st.red[par][x][n][1];
+          }
+          dl[b] = bt * (st.v[r][n] - A);
+          if (cw == 0 && lg == 0)
+            p.out[((tok0 + t0 + r) * H + h) * D + col0 + n] = p.scale * (B + dl[b] * kq);
         }
-      }
-      __syncthreads();
-      const float bt = sm.beta[t0 + r], kq = sm.kq[r];
-      float dl[2];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int n = 16 * b + lc;
-        float A = 0.f, B = 0.f;
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-          A += sm.red[par][ww][n][0];
-          B += sm.red[par][ww][n][1];
-        }
-        dl[b] = bt * (sm.V[t0 + r][n] - A);
-        if (w == 0 && lg == 0)
-          p.out[((tok0 + t0 + r) * H + h) * D + col0 + n] = p.scale * (B + dl[b] * kq);
-      }
+          for (int e = 0; e < 4; ++e) {
+            const float kc = st.k[r][32 * cw + 16 * a + 4 * lg + e];
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float kc = st.k[r][32 * w + 16 * a + 4 * lg + e];
-#pragma unroll
-          for (int b = 0; b < 2; ++b) s[a][b][e] += kc * dl[b];
-        }
+            for (int b = 0; b < 2; ++b) s[a][b][e] += kc * dl[b];
+          }
       }
     }
   }
@@ -260,6 +332,7 @@ __global__ void __launch_bounds__(NT, 1) chunk_kernel(ChunkArgs p) {
   const int h = u - rank * p.H;
   const int doc = p.order ? p.order[rank] : rank;
   const int col0 = tile * DVT;
+  const int H = p.H;
   size_t tok_begin;
   int ntok;
   if (p.cu_seqlens) {
@@ -269,324 +342,478 @@ __global__ void __launch_bounds__(NT, 1) chunk_kernel(ChunkArgs p) {
     tok_begin = static_cast<size_t>(doc) * p.T;
     ntok = p.T;
   }
-  const int H = p.H;
+  const int nch = (ntok + C - 1) / C;
   const size_t unit_state = (static_cast<size_t>(doc) * H + h) * D * D;
+  const size_t row_stride = static_cast<size_t>(H) * D;  // elements between tokens
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, lc = lane & 15, lg = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
+  const int pw = w;  // producer role: token block; consumer role: state rows 32w..
+  const int oct = lane & 15;     // producer: channels 8*oct .. 8*oct+7
+  const int qt = lane >> 4;      // producer: rows 4*qt .. 4*qt+3 of block pw
+  const int c8 = 8 * oct;
+  const float lim_lo = __expf(-HALF_SPAN_MAX);
 
-  // Zero the never-written upper parts once: Aqk above the diagonal blocks and
-  // the diagonal-block inverses' upper triangles are read as zeros.
-  for (int idx = tid; idx < C * LDT; idx += NT) {
-    (&sm.Aqk[0][0])[idx] = (f16)0.f;
-    (&sm.Ah[0][0])[idx] = (f16)0.f;
-  }
+  // ---------------- producer helpers
+  auto load_raw = [&](int ck, Raw& r) {
+    const int nv = min(C, ntok - ck * C);
+    const size_t tok0 = tok_begin + static_cast<size_t>(ck) * C;
+    // uniform bases; per-lane 32-bit offsets (64 rows x H x D fits easily)
+    const float* gb = p.log_g + (tok0 * H + h) * D;
+    const bf16_t* kb = p.k + (tok0 * H + h) * D;
+    const bf16_t* qb = p.q + (tok0 * H + h) * D;
+    const int rs = H * D;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const unsigned off = static_cast<unsigned>(min(16 * pw + 4 * qt + j, nv - 1) * rs + c8);
+      r.g[j][0] = *reinterpret_cast<const float4*>(gb + off);
+      r.g[j][1] = *reinterpret_cast<const float4*>(gb + off + 4u);
+      r.k[j] = *reinterpret_cast<const uint4*>(kb + off);
+      r.q[j] = *reinterpret_cast<const uint4*>(qb + off);
+    }
+    const int vr = tid >> 2, vc = (tid & 3) * 8;
+    const bf16_t* vb = p.v + (tok0 * H + h) * D + col0;
+    r.v = *reinterpret_cast<const uint4*>(vb + static_cast<unsigned>(min(vr, nv - 1) * rs + vc));
+    const float* bb = p.beta + tok0 * H + h;
+    r.beta = bb[static_cast<unsigned>(min(tid & (C - 1), nv - 1) * H)];
+  };
 
-  // ---- initial state in C layout: s[a][b][e] = S[32w+16a+4lg+e][col0+16b+lc]
-  f32x4 s[2][2];
+  // stage A of chunk ck into buffer buf: exp(log_g), its products over the
+  // 16-token block (prefix and suffix; the four 4-token quarters of a block
+  // sit in lanes oct, oct+16, oct+32, oct+48), the decay-scaled operands Kl,
+  // Ql, Kr, the block totals and diagonal-tile factors, the value tile and beta.
+  auto stage_a = [&](int ck, int buf, Raw& r, Prod& o) {
+    const int nv = min(C, ntok - ck * C);
+    bool bad = false;
+    u16x2 mk = {0, 0};
+    // padding rows (past the document's end) become identity tokens:
+    // k = q = 0, log_g = 0
+    const int nrow = nv - (16 * pw + 4 * qt);  // rows of this lane's quarter inside the chunk
+    if (nv < C) {  // workgroup-uniform: only a document's last chunk has padding rows
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bool pad = j >= nrow;
+        r.k[j].x = pad ? 0u : r.k[j].x; r.k[j].y = pad ? 0u : r.k[j].y;
+        r.k[j].z = pad ? 0u : r.k[j].z; r.k[j].w = pad ? 0u : r.k[j].w;
+        r.q[j].x = pad ? 0u : r.q[j].x; r.q[j].y = pad ? 0u : r.q[j].y;
+        r.q[j].z = pad ? 0u : r.q[j].z; r.q[j].w = pad ? 0u : r.q[j].w;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) r.g[j][x] = pad ? make_float4(0.f, 0.f, 0.f, 0.f) : r.g[j][x];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t kw[4] = {r.k[j].x, r.k[j].y, r.k[j].z, r.k[j].w};
+      const uint32_t qw[4] = {r.q[j].x, r.q[j].y, r.q[j].z, r.q[j].w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        mk = __builtin_elementwise_max(mk, __builtin_bit_cast(u16x2, kw[x] & 0x7fff7fffu));
+        mk = __builtin_elementwise_max(mk, __builtin_bit_cast(u16x2, qw[x] & 0x7fff7fffu));
+      }
+    }
+    bad |= mk[0] > QK_MAX_BITS || mk[1] > QK_MAX_BITS;
+    // Per channel: P = exp(G - R_blk), S = exp(R_blk_end - G) on this lane's 4
+    // rows, folded straight into the fp16 operand rows.
+    f16x8 hl[4], hq[4], hr[4];
+    float tot8[8];
+    f16x8 fdl8, fdr8;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      float a[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 g4 = r.g[j][c >> 2];
+        const int cc = c & 3;
+        const float gv = cc == 0 ? g4.x : cc == 1 ? g4.y : cc == 2 ? g4.z : g4.w;
+        a[j] = exp_fast(gv);
+      }
+      const float p1 = a[0] * a[1], p2 = p1 * a[2], p3 = p2 * a[3];  // inside the quarter
+      const float s1 = a[2] * a[3], s0 = a[1] * s1;
+      const float t0 = __shfl(p3, oct, 64), t1 = __shfl(p3, oct + 16, 64);
+      const float t2 = __shfl(p3, oct + 32, 64), t3 = __shfl(p3, oct + 48, 64);
+      // exclusive products over the quarters before / after this lane's
+      const float E = (qt >= 1 ? t0 : 1.f) * (qt >= 2 ? t1 : 1.f) * (qt >= 3 ? t2 : 1.f);
+      const float F = (qt <= 2 ? t3 : 1.f) * (qt <= 1 ? t2 : 1.f) * (qt <= 0 ? t1 : 1.f);
+      const float Pv[4] = {E * a[0], E * p1, E * p2, E * p3};
+      const float Sv[4] = {s0 * F, s1 * F, a[3] * F, F};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t kw = c < 2 ? r.k[j].x : c < 4 ? r.k[j].y : c < 6 ? r.k[j].z : r.k[j].w;
+        const uint32_t qw = c < 2 ? r.q[j].x : c < 4 ? r.q[j].y : c < 6 ? r.q[j].z : r.q[j].w;
+        const float kv = (c & 1) ? bf16_hi(kw) : bf16_lo(kw);
+        const float qv = (c & 1) ? bf16_hi(qw) : bf16_lo(qw);
+        hl[j][c] = (f16)(kv * Pv[j]);
+        hq[j][c] = (f16)(qv * Pv[j]);
+        hr[j][c] = (f16)(kv * Sv[j]);
+      }
+      const float dl = t0 * t1, dr = t2 * t3;  // over the first / second half of the block
+      bad |= (dl < lim_lo) | (dr < lim_lo) | (dl != dl) | (dr != dr);
+      tot8[c] = dl * dr;
+      fdl8[c] = (f16)(1.f / fmaxf(dl, lim_lo));
+      fdr8[c] = (f16)(1.f / fmaxf(dr, lim_lo));
+    }
+    // the four quarter lanes of a channel octet write identical values
+    *reinterpret_cast<float4*>(&sm.tot[pw][c8]) = make_float4(tot8[0], tot8[1], tot8[2], tot8[3]);
+    *reinterpret_cast<float4*>(&sm.tot[pw][c8 + 4]) = make_float4(tot8[4], tot8[5], tot8[6], tot8[7]);
+    *reinterpret_cast<f16x8*>(&sm.fDl[pw][c8]) = fdl8;
+    *reinterpret_cast<f16x8*>(&sm.fDr[pw][c8]) = fdr8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * pw + 4 * qt + j;
+      *reinterpret_cast<f16x8*>(&sm.Kl[buf][row][c8]) = hl[j];
+      *reinterpret_cast<f16x8*>(&sm.Ql[buf][row][c8]) = hq[j];
+      *reinterpret_cast<f16x8*>(&sm.u.kk.Kr[row][c8]) = hr[j];
+    }
+    {
+      const int vr = tid >> 2;
+      const uint4 x = r.v;
+      float vv[8] = {bf16_lo(x.x), bf16_hi(x.x), bf16_lo(x.y), bf16_hi(x.y),
+                     bf16_lo(x.z), bf16_hi(x.z), bf16_lo(x.w), bf16_hi(x.w)};
+      f16x8 vh;
+      float vmax = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        vv[j] = vr < nv ? vv[j] : 0.f;
+        vmax = fmaxf(vmax, fabsf(vv[j]));
+        vh[j] = (f16)vv[j];
+      }
+      bad |= !(vmax <= V_MAX);
+      *reinterpret_cast<f16x8*>(&sm.V[buf][vr][(tid & 3) * 8]) = vh;
+      const float bv = (tid & (C - 1)) < nv ? r.beta : 0.f;
+      sm.beta[buf][tid & (C - 1)] = bv;  // the four waves write identical values
+      bad |= !(fabsf(bv) <= BETA_MAX);
+    }
+    o.bad = bad;
+  };
+
+  // factors from the block totals; the KdT values of this chunk into kd[]:
+  // kd[c] holds rows 16*pw+4*qt .. +3 of channel c8+c.
+  auto factors = [&](int buf, f16x4 (&kd)[8]) {
+    float T[4][8];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      const float4 a = *reinterpret_cast<const float4*>(&sm.tot[I][c8]);
+      const float4 b = *reinterpret_cast<const float4*>(&sm.tot[I][c8 + 4]);
+      T[I][0] = a.x; T[I][1] = a.y; T[I][2] = a.z; T[I][3] = a.w;
+      T[I][4] = b.x; T[I][5] = b.y; T[I][6] = b.z; T[I][7] = b.w;
+    }
+    float gd[8], gam[8];
+    f16x8 r1, r2, r3, o20, o30, o31;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      // exp(gamma - R_{pw+1}): product of the totals of the later blocks
+      gd[c] = pw == 0 ? T[1][c] * T[2][c] * T[3][c] : pw == 1 ? T[2][c] * T[3][c] : pw == 2 ? T[3][c] : 1.f;
+      const float e1 = T[0][c], e2 = e1 * T[1][c], e3 = e2 * T[2][c];
+      r1[c] = (f16)e1;  r2[c] = (f16)e2;  r3[c] = (f16)e3;
+      gam[c] = e3 * T[3][c];
+      o20[c] = (f16)T[1][c];
+      o30[c] = (f16)(T[1][c] * T[2][c]);
+      o31[c] = (f16)T[2][c];
+    }
+    // every lane of every wave writes the same values: no branch in this phase
+    const f16 one = (f16)1.f;
+    *reinterpret_cast<f16x8*>(&sm.fR[buf][0][c8]) = f16x8{one, one, one, one, one, one, one, one};
+    *reinterpret_cast<f16x8*>(&sm.fR[buf][1][c8]) = r1;
+    *reinterpret_cast<f16x8*>(&sm.fR[buf][2][c8]) = r2;
+    *reinterpret_cast<f16x8*>(&sm.fR[buf][3][c8]) = r3;
+    *reinterpret_cast<float4*>(&sm.fGam[buf][c8]) = make_float4(gam[0], gam[1], gam[2], gam[3]);
+    *reinterpret_cast<float4*>(&sm.fGam[buf][c8 + 4]) = make_float4(gam[4], gam[5], gam[6], gam[7]);
+    *reinterpret_cast<f16x8*>(&sm.fOff[0][c8]) = o20;  // (2,0)
+    *reinterpret_cast<f16x8*>(&sm.fOff[1][c8]) = o30;  // (3,0)
+    *reinterpret_cast<f16x8*>(&sm.fOff[2][c8]) = o31;  // (3,1)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const f16x8 kr = ld8(&sm.u.kk.Kr[16 * pw + 4 * qt + j][c8]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) kd[c][j] = (f16)((float)kr[c] * gd[c]);
+    }
+  };
+
+  auto write_kdt = [&](const f16x4 (&kd)[8]) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      *reinterpret_cast<f16x4*>(&sm.u.kk.KdT[c8 + c][16 * pw + 4 * qt]) = kd[c];
+  };
+
+  // A, Aqk and the diagonal-block inverses of one chunk into frag[buf].
+  auto products = [&](int buf, bool bad_in) {
+    bool bad = bad_in;
+    // diagonal block I = pw: A-layout (swapped product) and B-layout
+    {
+      const int I = pw;
+      f32x4 accA = zero4(), accB = zero4();
+      f16x8 l[4], r[4], fl[4], fr[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int kc = 32 * ks + 8 * lg;
+        l[ks] = ld8(&sm.Kl[buf][16 * I + lc][kc]);
+        r[ks] = ld8(&sm.u.kk.Kr[16 * I + lc][kc]);
+        fl[ks] = ld8(&sm.fDl[I][kc]);
+        fr[ks] = ld8(&sm.fDr[I][kc]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f16x8 ls = l[ks] * fl[ks], rs = r[ks] * fr[ks];
+        accA = mfma32(rs, ls, accA);  // A layout: rows 16I+lc, cols 16I+4lg+e
+        accB = mfma32(ls, rs, accB);  // B layout: rows 16I+4lg+e, cols 16I+lc
+      }
+      f16x4 a, b;
+      const float bA = sm.beta[buf][16 * I + lc];
+      const float4 bB4 = *reinterpret_cast<const float4*>(&sm.beta[buf][16 * I + 4 * lg]);
+      const float bB[4] = {bB4.x, bB4.y, bB4.z, bB4.w};
+      float lmax = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float la = (4 * lg + e) < lc ? bA * accA[e] : 0.f;
+        const float lb = lc < (4 * lg + e) ? bB[e] * accB[e] : 0.f;
+        lmax = fmaxf(lmax, fabsf(la));
+        a[e] = (f16)la;
+        b[e] = (f16)lb;
+      }
+      bad |= !(lmax <= 1.0f);
+      // (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8), L strictly lower
+      const f16x4 b2 = h4(mfma16(a, b, zero4()));
+      const f16x4 a2 = h4(mfma16(b, a, zero4()));
+      const f16x4 b4 = h4(mfma16(a2, b2, zero4()));
+      const f16x4 a4 = h4(mfma16(b2, a2, zero4()));
+      const f16x4 b8 = h4(mfma16(a4, b4, zero4()));
+      f32x4 t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = (lc == 4 * lg + e ? 1.f : 0.f) - (float)a[e];
+      t = mfma16(b2, h4(t), t);
+      t = mfma16(b4, h4(t), t);
+      t = mfma16(b8, h4(t), t);
+      sm.frag[buf][I][lane] = h4(t);
+    }
+    // four of the sixteen remaining tiles: A_IJ (I > J) and Aqk_IJ (J <= I)
+#pragma unroll 1
+    for (int m = 0; m < 4; ++m) {
+      const int item = pw + 4 * m;
+      const bool isq = item >= 6;
+      int I, J;
+      if (!isq) {
+        // pairs (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+        I = item >= 3 ? 3 : item >= 1 ? 2 : 1;
+        J = item - pair6(I, 0);
+      } else {
+        const int t = item - 6;
+        I = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+        J = t - tile10(I, 0);
+      }
+      const f16(*L)[LDK] = isq ? sm.Ql[buf] : sm.Kl[buf];
+      const int off = (I == 2 && J == 0) ? 0 : (I == 3 && J == 0) ? 1 : (I == 3 && J == 1) ? 2 : -1;
+      f32x4 acc = zero4();
+      f16x8 l[4], r[4], fl[4], fr[4];
+      // factor rows (an all-ones row is never needed: no scaling then)
+      const f16* flp = I == J ? &sm.fDl[I][0] : off >= 0 ? &sm.fOff[off][0] : nullptr;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int kc = 32 * ks + 8 * lg;
+        l[ks] = ld8(&L[16 * I + lc][kc]);
+        r[ks] = ld8(&sm.u.kk.Kr[16 * J + lc][kc]);
+        if (flp) fl[ks] = ld8(flp + kc);
+        if (I == J) fr[ks] = ld8(&sm.fDr[I][kc]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f16x8 ls = flp ? l[ks] * fl[ks] : l[ks];
+        const f16x8 rs = I == J ? r[ks] * fr[ks] : r[ks];
+        acc = mfma32(rs, ls, acc);  // A layout: rows 16I+lc, cols 16J+4lg+e
+      }
+      f16x4 res;
+      if (!isq) {
+        const float bA = sm.beta[buf][16 * I + lc];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[e] = (f16)(bA * acc[e]);
+        sm.frag[buf][SLOT_A + pair6(I, J)][lane] = res;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) res[e] = (f16)((16 * J + 4 * lg + e) <= (16 * I + lc) ? acc[e] : 0.f);
+        sm.frag[buf][SLOT_Q + tile10(I, J)][lane] = res;
+      }
+    }
+    return bad;
+  };
+
+  // ---------------- consumer state: s[a][b][e] = S[32cw+16a+4lg+e][col0+16b+lc]
+  const int cw = pw;
+  const int nb = cw & 1;          // consumer value-column tile (16 columns)
+  const bool is_z = cw >= 2;      // waves 2,3: Z and outputs; waves 0,1: X and Delta
+
+  auto write_st = [&](f32x4 (&s)[2][2]) {
+    bool big = false;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) big |= !(fabsf(s[a][b][e]) <= S_MAX);
+        *reinterpret_cast<f16x4*>(&sm.ST[16 * b + lc][32 * cw + 16 * a + 4 * lg]) = h4(s[a][b]);
+      }
+    const bool any = __builtin_amdgcn_ballot_w64(big) != 0;
+    if (lane == 0) sm.sbp[cw] = any;
+  };
+
+
+  // ---------------- state and prologue
+  f32x4 s[2][2];   // s[a][b][e] = S[32cw+16a+4lg+e][col0+16b+lc]
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        s[a][b][e] = p.init_state
-                         ? p.init_state[unit_state + (32 * w + 16 * a + 4 * lg + e) * D + col0 + 16 * b + lc]
-                         : 0.f;
-  bool s_big = false;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_big |= !(fabsf(s[a][b][e]) <= S_MAX);
-      *reinterpret_cast<f16x4*>(&sm.ST[16 * b + lc][32 * w + 16 * a + 4 * lg]) = to_h4(s[a][b]);
-    }
-
-  const int cp = tid & 63;     // channel pair: channels 2cp, 2cp+1
-  const int c0 = 2 * cp;
-  const int blk = w;           // token block of this thread in stage A
-  const float lim_lo = __expf(-HALF_SPAN_MAX);
-
-  for (int cs = 0; cs < ntok; cs += C) {
-    const int nv = min(C, ntok - cs);  // valid rows of this chunk
-    const size_t tok0 = tok_begin + cs;
-
-    // ---------------- stage A: loads, gate products, base operands
-    float P[16][2], Sf[16][2];
-    uint32_t kk[16], qq[16];
-    bool bad = s_big;
+        s[a][b][e] = p.init_state ? p.init_state[unit_state + (32 * cw + 16 * a + 4 * lg + e) * D + col0 + 16 * b + lc]
+                                  : 0.f;
+  write_st(s);
+  Raw raw;
+  Prod pr;
+  f16x4 kd[8];
+  if (nch > 0) {
+    load_raw(0, raw);
+    stage_a(0, 0, raw, pr);
+    if (nch > 1) load_raw(1, raw);
+    lds_barrier();
+    factors(0, kd);
+    lds_barrier();
     {
-      // Loads are issued unconditionally (rows past the end of the document
-      // re-read its last row) so that all of them are in flight at once; the
-      // padding rows are then replaced by identity tokens (k = q = v = 0,
-      // log_g = 0, beta = 0).
-      float2 lgv[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = min(16 * blk + i, nv - 1);
-        const size_t row = (tok0 + r) * H + h;
-        lgv[i] = *reinterpret_cast<const float2*>(p.log_g + row * D + c0);
-        kk[i] = *reinterpret_cast<const uint32_t*>(p.k + row * D + c0);
-        qq[i] = *reinterpret_cast<const uint32_t*>(p.q + row * D + c0);
-      }
-      const int vr = tid >> 2, vc = (tid & 3) * 8;  // V: 64 rows x 4 threads x 8 columns
-      const uint4 vraw =
-          *reinterpret_cast<const uint4*>(p.v + ((tok0 + min(vr, nv - 1)) * H + h) * D + col0 + vc);
-      const float braw = p.beta[(tok0 + min(tid & (C - 1), nv - 1)) * H + h];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (16 * blk + i >= nv) {
-          lgv[i] = make_float2(0.f, 0.f);
-          kk[i] = 0u;
-          qq[i] = 0u;
-        }
-      }
-      if (tid < C) {
-        const float bv = tid < nv ? braw : 0.f;
-        sm.beta[tid] = bv;
-        bad |= !(fabsf(bv) <= BETA_MAX);
-      }
-      {
-        float vv[8] = {bf16_lo(vraw.x), bf16_hi(vraw.x), bf16_lo(vraw.y), bf16_hi(vraw.y),
-                       bf16_lo(vraw.z), bf16_hi(vraw.z), bf16_lo(vraw.w), bf16_hi(vraw.w)};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (vr >= nv) vv[j] = 0.f;
-          sm.V[vr][vc + j] = vv[j];
-          bad |= !(fabsf(vv[j]) <= V_MAX);
-        }
-      }
-      float al[16][2];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        al[i][0] = exp_fast(lgv[i].x);
-        al[i][1] = exp_fast(lgv[i].y);
-      }
-#pragma unroll
-      for (int ch = 0; ch < 2; ++ch) {
-        float pr = 1.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) { pr *= al[i][ch]; P[i][ch] = pr; }
-        float sf = 1.f;
-#pragma unroll
-        for (int i = 15; i >= 0; --i) { Sf[i][ch] = sf; sf *= al[i][ch]; }
-        sm.tot[blk][c0 + ch] = P[15][ch];
-        // diagonal-tile factors around the mid-block reference
-        const float dl = P[7][ch], dr = Sf[7][ch];
-        bad |= !(dl >= lim_lo) || !(dr >= lim_lo);
-        sm.fDl[blk][c0 + ch] = (f16)(1.f / fmaxf(dl, lim_lo));
-        sm.fDr[blk][c0 + ch] = (f16)(1.f / fmaxf(dr, lim_lo));
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int r = 16 * blk + i;
-        const float k0 = bf16_lo(kk[i]), k1 = bf16_hi(kk[i]);
-        const float q0 = bf16_lo(qq[i]), q1 = bf16_hi(qq[i]);
-        bad |= !(fabsf(k0) <= QK_MAX) || !(fabsf(k1) <= QK_MAX) || !(fabsf(q0) <= QK_MAX) ||
-               !(fabsf(q1) <= QK_MAX);
-        f16x2 hk, hq, hr;
-        hk[0] = (f16)(k0 * P[i][0]); hk[1] = (f16)(k1 * P[i][1]);
-        hq[0] = (f16)(q0 * P[i][0]); hq[1] = (f16)(q1 * P[i][1]);
-        hr[0] = (f16)(k0 * Sf[i][0]); hr[1] = (f16)(k1 * Sf[i][1]);
-        *reinterpret_cast<f16x2*>(&sm.Kl[r][c0]) = hk;
-        *reinterpret_cast<f16x2*>(&sm.Ql[r][c0]) = hq;
-        *reinterpret_cast<f16x2*>(&sm.Kr[r][c0]) = hr;
-      }
+      const bool bad = products(0, pr.bad);
+      const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
+      if (lane == 0) sm.fbp[0][pw] = any;
     }
-    const bool fallback = __syncthreads_or(bad);  // also publishes tot/fDl/fDr/V/beta
+    lds_barrier();
+  }
 
-    if (fallback) {
-      chunk_fallback(sm, s, p, tok0, nv, h, col0);
+  // ---------------- one chunk: consumer work on chunk k, producer work on
+  // chunk k+1 (when `produce`).  The consumer part runs the fast path's
+  // products for every chunk; for a chunk flagged for token-by-token
+  // evaluation it skips the state update, and the fallback then recomputes
+  // the chunk's outputs over the ones written here.
+  auto chunk_step = [&](int k, bool produce) {
+    const int buf = k & 1, nbuf = buf ^ 1;
+    const bool fbk = fast_path_blocked(sm, buf);
+    const size_t tok0 = tok_begin + static_cast<size_t>(k) * C;
+    const int nv = min(C, ntok - k * C);
+    f32x4 yz[4];
+
+    // ---- phase 1: producer stage A of chunk k+1; consumer Y / Z of chunk k
+    if (produce) {
+      write_kdt(kd);
+      stage_a(k + 1, nbuf, raw, pr);
     } else {
-      // ---------------- factors from the block totals; Kd^T
-      {
-        float Qt[4][2];
+      write_kdt(kd);
+    }
+    {
+      // Y = (Kl exp R_I) S (waves 0,1) or Z = (Ql exp R_I) S (waves 2,3)
+      const f16(*L)[LDK] = is_z ? sm.Ql[buf] : sm.Kl[buf];
+      f16x8 sf[4];
 #pragma unroll
-        for (int I = 0; I < 4; ++I) { Qt[I][0] = sm.tot[I][c0]; Qt[I][1] = sm.tot[I][c0 + 1]; }
+      for (int ks = 0; ks < 4; ++ks) sf[ks] = ld8(&sm.ST[16 * nb + lc][32 * ks + 8 * lg]);
 #pragma unroll
-        for (int ch = 0; ch < 2; ++ch) {
-          const int c = c0 + ch;
-          // e^{gamma - R_{blk+1}}: product of the totals of the later blocks
-          float gd = 1.f;
-#pragma unroll
-          for (int I = 3; I > 0; --I)
-            if (I > blk) gd *= Qt[I][ch];
-          f16 col[16];
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float kv = ch == 0 ? bf16_lo(kk[i]) : bf16_hi(kk[i]);
-            col[i] = (f16)(kv * Sf[i][ch] * gd);
-          }
-          *reinterpret_cast<f16x8*>(&sm.KdT[c][16 * blk]) =
-              f16x8{col[0], col[1], col[2], col[3], col[4], col[5], col[6], col[7]};
-          *reinterpret_cast<f16x8*>(&sm.KdT[c][16 * blk + 8]) =
-              f16x8{col[8], col[9], col[10], col[11], col[12], col[13], col[14], col[15]};
-          if (blk == 0) {
-            float r = 1.f;
-#pragma unroll
-            for (int I = 0; I < 4; ++I) { sm.fR[I][c] = (f16)r; r *= Qt[I][ch]; }
-            sm.fGam[c] = r;
-            sm.fOff[off_pair(1, 0)][c] = (f16)1.f;
-            sm.fOff[off_pair(2, 0)][c] = (f16)Qt[1][ch];
-            sm.fOff[off_pair(2, 1)][c] = (f16)1.f;
-            sm.fOff[off_pair(3, 0)][c] = (f16)(Qt[1][ch] * Qt[2][ch]);
-            sm.fOff[off_pair(3, 1)][c] = (f16)Qt[2][ch];
-            sm.fOff[off_pair(3, 2)][c] = (f16)1.f;
-          }
-        }
-      }
-      __syncthreads();
-
-      // ---------------- (a)/(b): A = Kl Kr^T and Aqk = Ql Kr^T, lower tiles
-      for (int t = w; t < 20; t += 4) {
-        int I, J;
-        tile_ij(t % 10, I, J);
-        const bool isq = t >= 10;
-        const f16(*L)[LDK] = isq ? sm.Ql : sm.Kl;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int I = 0; I < 4; ++I) {
+        f16x8 a[4], f[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
           const int kc = 32 * ks + 8 * lg;
-          f16x8 af = ld8(&L[16 * I + lc][kc]);
-          f16x8 bf = ld8(&sm.Kr[16 * J + lc][kc]);
-          if (I == J) {
-            af = af * ld8(&sm.fDl[I][kc]);
-            bf = bf * ld8(&sm.fDr[I][kc]);
-          } else if (I > J + 1) {
-            af = af * ld8(&sm.fOff[off_pair(I, J)][kc]);
-          }
-          acc = mfma32(af, bf, acc);
+          a[ks] = ld8(&L[16 * I + lc][kc]);
+          f[ks] = ld8(&sm.fR[buf][I][kc]);
         }
-        const int j = 16 * J + lc;
+        f32x4 acc = zero4();
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 16 * I + 4 * lg + e;
-          if (isq) {
-            sm.Aqk[i][j] = (f16)(j <= i ? acc[e] : 0.f);
-          } else {
-            const float a = j < i ? sm.beta[i] * acc[e] : 0.f;
-            sm.A32[i][j] = a;
-            sm.Ah[i][j] = (f16)a;
-          }
-        }
+        for (int ks = 0; ks < 4; ++ks) acc = mfma32(a[ks] * f[ks], sf[ks], acc);
+        yz[I] = acc;
       }
-
-      // ---------------- (c)/(d): Y = Kg S (waves 0,1) and Z = Qg S (waves 2,3)
-      // Kg = Kl exp(R_I) row block by row block; B operand S^T from LDS.
-      const int nb = w & 1;           // value-column tile of 16 handled by this wave
-      const bool is_z = w >= 2;
-      f32x4 yz[4];
-      {
-        const f16(*L)[LDK] = is_z ? sm.Ql : sm.Kl;
+      if (!is_z) {  // X = beta (V - Y)
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) {
-            const int kc = 32 * ks + 8 * lg;
-            const f16x8 af = ld8(&L[16 * I + lc][kc]) * ld8(&sm.fR[I][kc]);
-            const f16x8 bf = ld8(&sm.ST[16 * nb + lc][kc]);
-            acc = mfma32(af, bf, acc);
-          }
-          yz[I] = acc;
-        }
-      }
-      // X = beta (V - Y) on waves 0,1 (C layout rows 16I+4lg+e, column 16nb+lc)
-      if (!is_z) {
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
+          const float4 b4 = *reinterpret_cast<const float4*>(&sm.beta[buf][16 * I + 4 * lg]);
+          const float bt[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * lg + e;
-            yz[I][e] = sm.beta[i] * (sm.V[i][16 * nb + lc] - yz[I][e]);
+            yz[I][e] = bt[e] * ((float)sm.V[buf][i][16 * nb + lc] - yz[I][e]);
           }
-      }
-      __syncthreads();  // A32 / Ah / Aqk complete
-
-      // ---------------- inverses of the diagonal blocks of (I + A), fp32 VALU
-      {
-        const int I = w;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[i] = (i == lc) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-#pragma unroll
-          for (int i = j + 1; i < 16; ++i) x[i] -= sm.A32[16 * I + i][16 * I + j] * x[j];
-        }
-        if (lg == 0) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) sm.Td[I][i][lc] = (f16)x[i];
-        }
-      }
-      __syncthreads();
-
-      // ---------------- Delta by blocked forward substitution (waves 0,1)
-      if (!is_z) {
-        f16x4 dh[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          f32x4 r = yz[I];
-#pragma unroll
-          for (int J = 0; J < I; ++J) {
-            const f16x4 a = -ld4(&sm.Ah[16 * I + lc][16 * J + 4 * lg]);
-            r = mfma16(a, dh[J], r);
-          }
-          f32x4 z = {0.f, 0.f, 0.f, 0.f};
-          const f32x4 d = mfma16(ld4(&sm.Td[I][lc][4 * lg]), to_h4(r), z);
-          dh[I] = to_h4(d);
-          *reinterpret_cast<f16x4*>(&sm.DT[16 * nb + lc][16 * I + 4 * lg]) = dh[I];
-        }
-      }
-      __syncthreads();
-
-      // ---------------- O = scale (Z + Aqk Delta) (waves 2,3)
-      if (is_z) {
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          f32x4 o = yz[I];
-#pragma unroll
-          for (int J = 0; J <= I; ++J)
-            o = mfma16(ld4(&sm.Aqk[16 * I + lc][16 * J + 4 * lg]), ld4(&sm.DT[16 * nb + lc][16 * J + 4 * lg]), o);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 16 * I + 4 * lg + e;
-            if (i < nv) p.out[((tok0 + i) * H + h) * D + col0 + 16 * nb + lc] = p.scale * o[e];
-          }
-        }
-      }
-
-      // ---------------- S = exp(gamma) S + Kd^T Delta (all waves)
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float g = sm.fGam[32 * w + 16 * a + 4 * lg + e];
-          s[a][0][e] *= g;
-          s[a][1][e] *= g;
-        }
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-#pragma unroll
-          for (int J = 0; J < 4; ++J)
-            s[a][b] = mfma16(ld4(&sm.KdT[32 * w + 16 * a + lc][16 * J + 4 * lg]),
-                             ld4(&sm.DT[16 * b + lc][16 * J + 4 * lg]), s[a][b]);
         }
       }
     }
+    lds_barrier();
 
-    // ---------------- S^T (fp16) for the next chunk; magnitude guard
-    __syncthreads();  // everyone is done reading ST / DT / staging of this chunk
-    s_big = false;
+    // ---- phase 2: producer factors of chunk k+1 and loads of chunk k+2;
+    // consumer Delta_I = T_II (X_I - sum_{J<I} A_IJ Delta_J)  (waves 0,1)
+    if (produce) {
+      factors(nbuf, kd);
+      load_raw(min(k + 2, nch - 1), raw);
+    }
+    if (!is_z) {
+      f16x4 dh[4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+      for (int I = 0; I < 4; ++I) {
+        f32x4 r = yz[I];
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s_big |= !(fabsf(s[a][b][e]) <= S_MAX);
-        *reinterpret_cast<f16x4*>(&sm.ST[16 * b + lc][32 * w + 16 * a + 4 * lg]) = to_h4(s[a][b]);
+        for (int J = 0; J < I; ++J) r = mfma16(-sm.frag[buf][SLOT_A + pair6(I, J)][lane], dh[J], r);
+        dh[I] = h4(mfma16(sm.frag[buf][I][lane], h4(r), zero4()));
+        *reinterpret_cast<f16x4*>(&sm.DT[16 * nb + lc][16 * I + 4 * lg]) = dh[I];
       }
-  }
+    }
+    lds_barrier();
+
+    // ---- phase 3: producer products of chunk k+1; consumer O = scale (Z + Aqk Delta)
+    // (waves 2,3) and S = exp(gamma) S + Kd^T Delta (all waves)
+    if (produce) {
+      const bool bad = products(nbuf, pr.bad);
+      const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
+      if (lane == 0) sm.fbp[nbuf][pw] = any;
+    }
+    if (is_z) {
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        f32x4 o = yz[I];
+#pragma unroll
+        for (int J = 0; J <= I; ++J)
+          o = mfma16(sm.frag[buf][SLOT_Q + tile10(I, J)][lane], ld4(&sm.DT[16 * nb + lc][16 * J + 4 * lg]), o);
+        float* ob = p.out + (tok0 * H + h) * D + col0 + 16 * nb + lc;
+        if (nv == C) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ob[static_cast<unsigned>((16 * I + 4 * lg + e) * H * D)] = p.scale * o[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * lg + e;
+            if (i < nv) ob[static_cast<unsigned>(i * H * D)] = p.scale * o[e];
+          }
+        }
+      }
+    }
+    if (!fbk) {  // workgroup-uniform; a chunk taken token by token keeps its entry state
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const float4 g4 = *reinterpret_cast<const float4*>(&sm.fGam[buf][32 * cw + 16 * a + 4 * lg]);
+      const float gg[4] = {g4.x, g4.y, g4.z, g4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[a][0][e] *= gg[e];
+        s[a][1][e] *= gg[e];
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int J = 0; J < 4; ++J)
+          s[a][b] = mfma16(ld4(&sm.u.kk.KdT[32 * cw + 16 * a + lc][16 * J + 4 * lg]),
+                           ld4(&sm.DT[16 * b + lc][16 * J + 4 * lg]), s[a][b]);
+    }
+    write_st(s);
+    }
+    lds_barrier();
+
+    if (fbk) {  // workgroup-uniform
+      chunk_fallback(sm, s, p, tok_begin, ntok, k, h, col0);
+      write_st(s);
+      lds_barrier();
+    }
+  };
+
+  for (int k = 0; k + 1 < nch; ++k) chunk_step(k, true);
+  if (nch > 0) chunk_step(nch - 1, false);
 
   if (p.final_state) {
 #pragma unroll
@@ -595,7 +822,7 @@ __global__ void __launch_bounds__(NT, 1) chunk_kernel(ChunkArgs p) {
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          p.final_state[unit_state + (32 * w + 16 * a + 4 * lg + e) * D + col0 + 16 * b + lc] = s[a][b][e];
+          p.final_state[unit_state + (32 * cw + 16 * a + 4 * lg + e) * D + col0 + 16 * b + lc] = s[a][b][e];
   }
 }
 
@@ -634,7 +861,7 @@ hipError_t launch_chunk_mfma(const ChunkLaunch& a, hipStream_t stream) {
   p.scale = a.scale;
   if (a.cu_seqlens && a.num_seqs > 1 && a.num_seqs <= 4096 && a.doc_order) {
     const int n = a.num_seqs;
-    hipLaunchKernelGGL(doc_order_kernel, dim3((n + NT - 1) / NT), dim3(NT), 0, stream, a.cu_seqlens, n,
+    hipLaunchKernelGGL(doc_order_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a.cu_seqlens, n,
                        a.doc_order);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
