@@ -58,7 +58,7 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
     lib.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
-    lib.kda_chunk_workspace_bytes.argtypes = [D]
+    lib.kda_chunk_workspace_bytes.argtypes = [D, ctypes.c_int]
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.kda_step.restype = ctypes.c_int
@@ -116,9 +116,11 @@ def make_desc(num_seqs, seq_len, H, dk, dv, qkv_dtype, scale=None, workspace=Non
     return d
 
 
-def workspace_bytes(num_docs: int, H: int, d: int) -> int:
-    desc = make_desc(num_docs, 0, H, d, d, KDA_BF16)
-    return lib.kda_chunk_workspace_bytes(ctypes.byref(desc))
+def workspace_bytes(num_seqs: int, seq_len: int, H: int, d: int, packed: bool,
+                    qkv_dtype: int = KDA_BF16) -> int:
+    """Device scratch bytes of a chunk_fwd call (see kda_chunk_workspace_bytes)."""
+    desc = make_desc(num_seqs, seq_len, H, d, d, qkv_dtype)
+    return lib.kda_chunk_workspace_bytes(ctypes.byref(desc), int(packed))
 
 
 def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None,
@@ -129,6 +131,7 @@ def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None
     device splits the row into N documents.  ``init_state`` [N,H,dk,dv] or None
     (zeros).  ``final_state`` may be passed (and may be ``init_state`` itself
     for an in-place resume); pass ``final_state=False`` to skip it.
+    ``workspace`` (uint8 device tensor) is allocated when absent or too small.
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -159,10 +162,10 @@ def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None
     else:
         _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
     desc = make_desc(N, L, H, dk, dv, code, scale)
-    if cu_seqlens is not None:
-        need = lib.kda_chunk_workspace_bytes(ctypes.byref(desc))
+    need = lib.kda_chunk_workspace_bytes(ctypes.byref(desc), int(cu_seqlens is not None))
+    if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         desc.workspace, desc.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     _check(lib.kda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
                              _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),

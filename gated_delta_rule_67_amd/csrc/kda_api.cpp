@@ -28,11 +28,42 @@ kda_status fail(kda_status st, const char* fmt, ...) {
   return st;
 }
 
-// Prefill path selection: KDA_PREFILL_PATH=recurrent forces the token-recurrent
-// kernel, =chunk (or unset) lets the chunked MFMA kernel take what it supports.
-bool force_recurrent() {
+// Prefill path.  bf16 q/k/v with d = 128 run chunked on MFMA: by default in
+// two passes (parallel per-chunk preparation, then the serial state scan);
+// KDA_PREFILL_PATH=fused selects the single-pass fused kernel instead,
+// KDA_PREFILL_PATH=recurrent forces the token-recurrent kernel (any dtype / d),
+// and unset or =twopass keeps the default.
+enum class Path { Recurrent, Fused, TwoPass };
+
+Path prefill_path(const kda::ChunkLaunch& a) {
   const char* e = std::getenv("KDA_PREFILL_PATH");
-  return e && std::strcmp(e, "recurrent") == 0;
+  if (e && std::strcmp(e, "recurrent") == 0) return Path::Recurrent;
+  if (e && std::strcmp(e, "fused") == 0 && kda::chunk_mfma_supported(a)) return Path::Fused;
+  if (kda::twopass_supported(a)) return Path::TwoPass;
+  if (kda::chunk_mfma_supported(a)) return Path::Fused;
+  return Path::Recurrent;
+}
+
+size_t workspace_need(Path path, const kda::ChunkLaunch& a) {
+  const bool packed = a.cu_seqlens != nullptr;
+  switch (path) {
+    case Path::TwoPass: return kda::twopass_workspace_bytes(a.num_seqs, a.seq_len, a.num_heads, packed);
+    case Path::Fused: return kda::chunk_workspace_bytes(a.num_seqs, packed);
+    default: return 0;
+  }
+}
+
+// The launch record of a descriptor (pointers left empty; cu_seqlens only
+// marks a packed problem).
+kda::ChunkLaunch launch_of(const kda_desc* d, bool packed) {
+  kda::ChunkLaunch a{};
+  a.cu_seqlens = packed ? reinterpret_cast<const int32_t*>(uintptr_t(16)) : nullptr;
+  a.num_seqs = d->num_seqs;
+  a.seq_len = d->seq_len;
+  a.num_heads = d->num_heads;
+  a.d = d->dk;
+  a.bf16 = d->qkv_dtype == KDA_BF16;
+  return a;
 }
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
@@ -92,9 +123,11 @@ const char* kda_status_string(kda_status s) {
 
 const char* kda_last_error(void) { return g_last_error; }
 
-size_t kda_chunk_workspace_bytes(const kda_desc* d) {
-  if (!d) return 0;
-  return kda::chunk_workspace_bytes(d->num_seqs, true);
+size_t kda_chunk_workspace_bytes(const kda_desc* d, int packed) {
+  if (!d || d->num_seqs < 0 || d->seq_len < 0 || d->num_heads <= 0) return 0;
+  if (d->dk != d->dv) return 0;
+  const kda::ChunkLaunch a = launch_of(d, packed != 0);
+  return workspace_need(prefill_path(a), a);
 }
 
 kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const void* v,
@@ -122,7 +155,9 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
   if ((st = check_ptr(cu_seqlens, "cu_seqlens", fn, false)) != KDA_OK) return st;
   if (out && (out == q || out == k || out == v || out == log_g || out == beta || out == init_state))
     return fail(KDA_ERR_SHAPE, "%s: out aliases an input", fn);
-  const size_t ws_need = kda::chunk_workspace_bytes(d->num_seqs, packed);
+  kda::ChunkLaunch a = launch_of(d, packed);
+  const Path path = prefill_path(a);
+  const size_t ws_need = workspace_need(path, a);
   if (ws_need > 0) {
     if (!d->workspace || d->workspace_bytes < ws_need)
       return fail(KDA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, ws_need,
@@ -131,17 +166,15 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
   }
   if (!has_units || (!has_tok && !final_state)) return KDA_OK;
 
-  kda::ChunkLaunch a{};
   a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
   a.init_state = init_state; a.cu_seqlens = cu_seqlens;
   a.out = out; a.final_state = final_state;
-  a.doc_order = packed ? static_cast<int32_t*>(d->workspace) : nullptr;
-  a.num_seqs = d->num_seqs; a.seq_len = d->seq_len; a.num_heads = d->num_heads;
-  a.d = d->dk; a.bf16 = d->qkv_dtype == KDA_BF16; a.scale = resolve_scale(d);
+  a.workspace = ws_need > 0 ? d->workspace : nullptr;
+  a.scale = resolve_scale(d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = (kda::chunk_mfma_supported(a) && !force_recurrent())
-                           ? kda::launch_chunk_mfma(a, s)
-                           : kda::launch_chunk_recurrent(a, s);
+  const hipError_t e = path == Path::TwoPass ? kda::launch_chunk_twopass(a, s)
+                       : path == Path::Fused ? kda::launch_chunk_mfma(a, s)
+                                             : kda::launch_chunk_recurrent(a, s);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
   return KDA_OK;
 }

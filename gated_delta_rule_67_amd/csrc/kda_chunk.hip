@@ -45,17 +45,11 @@
 // as its A operand are computed transposed (C = B^T A^T), so the result
 // already sits in the A-operand lane layout and is stored fragment-major.
 #include "kda_common.h"
+#include "kda_fallback.h"
 #include "kda_launch.h"
 
 namespace kda {
 namespace {
-
-typedef _Float16 f16;
-typedef f16 f16x2 __attribute__((ext_vector_type(2)));
-typedef f16 f16x4 __attribute__((ext_vector_type(4)));
-typedef f16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int C = 64;        // chunk length
 constexpr int D = 128;       // head dim (dk = dv)
@@ -70,7 +64,6 @@ constexpr unsigned short QK_MAX_BITS = 0x4280;  // bf16 bits of 64.0: |q|, |k| b
 constexpr float V_MAX = 4096.0f;        // |v| bound of the fast path
 constexpr float S_MAX = 2048.0f;        // |S| bound of the fast path
 constexpr float BETA_MAX = 1.0f;        // |beta| bound of the fast path
-constexpr int FB_TG = 16;               // tokens staged per pass in the fallback
 
 // fragment slots per chunk buffer: 0-3 diagonal inverses T_II, 4-9 A_IJ
 // (I > J), 10-19 Aqk lower tiles; each slot holds one f16x4 per lane.
@@ -93,15 +86,6 @@ struct ChunkArgs {
   float scale;
 };
 
-struct FbStage {
-  float a[FB_TG][D];
-  float k[FB_TG][D];
-  float q[FB_TG][D];
-  float v[FB_TG][DVT];
-  float beta[FB_TG];
-  float kq[FB_TG];
-  float red[2][4][DVT][2];
-};
 
 // Kr and KdT are dead while a chunk is evaluated token by token, so the
 // fallback's staging area overlays them.
@@ -115,7 +99,7 @@ struct __align__(16) Smem {
   f16 Ql[2][C][LDK];       // q exp(G - R_blk), by chunk parity
   union {
     KrKd kk;
-    FbStage fb;
+    fb::Stage fb;
   } u;
   f16 V[2][C][LDV];        // value tile (fp16), by chunk parity
   float beta[2][C];
@@ -131,7 +115,7 @@ struct __align__(16) Smem {
   int fbp[2][4];           // producer waves: chunk cannot take the fast path
   int sbp[4];              // consumer waves: state beyond the fast-path bound
 };
-static_assert(sizeof(FbStage) <= sizeof(KrKd), "fallback staging does not fit");
+static_assert(sizeof(fb::Stage) <= sizeof(KrKd), "fallback staging does not fit");
 
 // Whether the chunk in buffer buf must be evaluated token by token: a
 // producer wave flagged it, or the state left the fast path's range.
@@ -140,44 +124,9 @@ __device__ __forceinline__ bool fast_path_blocked(const Smem& sm, int buf) {
           sm.sbp[0] | sm.sbp[1] | sm.sbp[2] | sm.sbp[3]) != 0;
 }
 
-__device__ __forceinline__ f32x4 mfma32(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma16(f16x4 a, f16x4 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f16x8 ld8(const f16* p) { return *reinterpret_cast<const f16x8*>(p); }
-__device__ __forceinline__ f16x4 ld4(const f16* p) { return *reinterpret_cast<const f16x4*>(p); }
-__device__ __forceinline__ f16x4 h4(f32x4 x) {
-  f16x4 r;
-  r[0] = (f16)x[0]; r[1] = (f16)x[1]; r[2] = (f16)x[2]; r[3] = (f16)x[3];
-  return r;
-}
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// Workgroup barrier that orders LDS only: outstanding global loads (the
-// prefetch of the next chunk) and stores stay in flight across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 __device__ __forceinline__ int tile10(int I, int J) { return (I * (I + 1)) / 2 + J; }  // J <= I
 __device__ __forceinline__ int pair6(int I, int J) { return (I * (I - 1)) / 2 + J; }   // J < I
 
-__global__ void __launch_bounds__(256) doc_order_kernel(const int32_t* __restrict__ cu, int n,
-                                                        int32_t* __restrict__ order) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int li = cu[i + 1] - cu[i];
-  int rank = 0;
-  for (int j = 0; j < n; ++j) {
-    const int lj = cu[j + 1] - cu[j];
-    rank += (lj > li) || (lj == li && j < i);
-  }
-  order[rank] = i;
-}
 
 // Raw inputs of one chunk as one producer thread loads them (16-byte loads):
 // rows 16*blk + 4*qt + j (j < 4) of channels 8*oct .. 8*oct+7, plus 8 values
@@ -194,129 +143,6 @@ struct Raw {
 struct Prod {
   bool bad;
 };
-
-// Token-by-token evaluation of chunk ck, exact fp32, on the state
-// s[a][b][e] = S[32w+16a+4lg+e][col0+16b+lc] (inlined, so the state stays in
-// registers).
-__device__ __forceinline__ void chunk_fallback(Smem& sm, f32x4 (&s)[2][2], const ChunkArgs& p,
-                                            size_t tok_begin, int ntok, int ck, int h, int col0) {
-  const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
-  const int cw = w;
-  const int H = p.H;
-
-  FbStage& st = sm.u.fb;
-  const int nv = min(C, ntok - ck * C);
-  const size_t tok0 = tok_begin + static_cast<size_t>(ck) * C;
-  for (int t0 = 0; t0 < nv; t0 += FB_TG) {
-    const int tg = min(FB_TG, nv - t0);
-    lds_barrier();
-    {
-      constexpr int PER = FB_TG * D / NT;
-      static_assert(FB_TG * D % NT == 0 && FB_TG * DVT % NT == 0, "fallback staging split");
-      float la[PER], lk[PER], lq[PER];
-#pragma unroll
-      for (int x = 0; x < PER; ++x) {
-        const int idx = tid + x * NT, r = min(idx / D, tg - 1), c = idx % D;
-        const size_t row = (tok0 + t0 + r) * H + h;
-        la[x] = p.log_g[row * D + c];
-        lk[x] = to_f32(p.k[row * D + c]);
-        lq[x] = to_f32(p.q[row * D + c]);
-      }
-      constexpr int PV = FB_TG * DVT / NT;
-      float vv[PV];
-#pragma unroll
-      for (int x = 0; x < PV; ++x) {
-        const int idx = tid + x * NT, vr = idx / DVT, vcol = idx % DVT;
-        vv[x] = to_f32(p.v[((tok0 + t0 + min(vr, tg - 1)) * H + h) * D + col0 + vcol]);
-      }
-      const float bb = p.beta[(tok0 + t0 + min(tid & (FB_TG - 1), tg - 1)) * H + h];
-#pragma unroll
-      for (int x = 0; x < PER; ++x) {
-        const int idx = tid + x * NT, r = idx / D, c = idx % D;
-        st.a[r][c] = exp_fast(la[x]);
-        st.k[r][c] = lk[x];
-        st.q[r][c] = lq[x];
-      }
-#pragma unroll
-      for (int x = 0; x < PV; ++x) {
-        const int idx = tid + x * NT;
-        st.v[idx / DVT][idx % DVT] = vv[x];
-      }
-      if (tid < FB_TG) st.beta[tid] = bb;
-    }
-    lds_barrier();
-    {  // kq[r] = k_r . q_r : 16 lanes per token, 8 channels each
-      const int r = tid >> 4, cc = (tid & 15) * 8;
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) acc += st.k[r][cc + c] * st.q[r][cc + c];
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
-      if ((tid & 15) == 0) st.kq[r] = acc;
-    }
-    lds_barrier();
-    for (int r = 0; r < tg; ++r) {
-      const int par = (t0 + r) & 1;
-      {
-        float pa[2] = {0.f, 0.f}, pb[2] = {0.f, 0.f};
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int c = 32 * cw + 16 * a + 4 * lg + e;
-            const float al = st.a[r][c], kc = st.k[r][c], qc = st.q[r][c];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              s[a][b][e] *= al;
-              pa[b] += s[a][b][e] * kc;
-              pb[b] += s[a][b][e] * qc;
-            }
-          }
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          pa[b] += __shfl_xor(pa[b], 16);
-          pa[b] += __shfl_xor(pa[b], 32);
-          pb[b] += __shfl_xor(pb[b], 16);
-          pb[b] += __shfl_xor(pb[b], 32);
-        }
-        if (lg == 0) {
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            st.red[par][cw][16 * b + lc][0] = pa[b];
-            st.red[par][cw][16 * b + lc][1] = pb[b];
-          }
-        }
-      }
-      lds_barrier();
-      {
-        const float bt = st.beta[r], kq = st.kq[r];
-        float dl[2];
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int n = 16 * b + lc;
-          float A = 0.f, B = 0.f;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            A += st.red[par][x][n][0];
-            B += st.red[par][x][n][1];
-          }
-          dl[b] = bt * (st.v[r][n] - A);
-          if (cw == 0 && lg == 0)
-            p.out[((tok0 + t0 + r) * H + h) * D + col0 + n] = p.scale * (B + dl[b] * kq);
-        }
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float kc = st.k[r][32 * cw + 16 * a + 4 * lg + e];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) s[a][b][e] += kc * dl[b];
-          }
-      }
-    }
-  }
-}
 
 __global__ void __launch_bounds__(NT, 1) chunk_kernel(ChunkArgs p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -806,7 +632,8 @@ __global__ void __launch_bounds__(NT, 1) chunk_kernel(ChunkArgs p) {
     lds_barrier();
 
     if (fbk) {  // workgroup-uniform
-      chunk_fallback(sm, s, p, tok_begin, ntok, k, h, col0);
+      const fb::Args fa{p.q, p.k, p.v, p.log_g, p.beta, p.out, p.H, p.scale};
+      fb::eval_chunk(sm.u.fb, s, fa, tok_begin, ntok, k, h, col0);
       write_st(s);
       lds_barrier();
     }
@@ -859,13 +686,11 @@ hipError_t launch_chunk_mfma(const ChunkLaunch& a, hipStream_t stream) {
   p.T = a.seq_len;
   p.H = a.num_heads;
   p.scale = a.scale;
-  if (a.cu_seqlens && a.num_seqs > 1 && a.num_seqs <= 4096 && a.doc_order) {
-    const int n = a.num_seqs;
-    hipLaunchKernelGGL(doc_order_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, a.cu_seqlens, n,
-                       a.doc_order);
-    const hipError_t e = hipGetLastError();
+  if (a.cu_seqlens && a.num_seqs > 1 && a.num_seqs <= 4096 && a.workspace) {
+    int32_t* order = static_cast<int32_t*>(a.workspace);
+    const hipError_t e = launch_doc_order(a.cu_seqlens, a.num_seqs, order, stream);
     if (e != hipSuccess) return e;
-    p.order = a.doc_order;
+    p.order = order;
   }
   const unsigned units = static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads);
   const unsigned blocks = ((units + 7) / 8) * 8 * NTILE;

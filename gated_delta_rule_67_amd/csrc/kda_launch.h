@@ -34,7 +34,7 @@ struct ChunkLaunch {
   const int32_t* cu_seqlens;  // may be null (dense)
   void* out;
   float* final_state;         // may be null
-  int32_t* doc_order;         // workspace: longest-first document order (packed only)
+  void* workspace;            // caller scratch (already checked to be large enough)
   int num_seqs;               // dense B or packed N
   int seq_len;                // dense T or packed total
   int num_heads;
@@ -44,14 +44,22 @@ struct ChunkLaunch {
 };
 
 hipError_t launch_step(const StepLaunch& a, hipStream_t stream);
-// Prefill through the token-recurrent kernel (any dtype / d).
+// Prefill through the token-recurrent kernel (any dtype / d).  No workspace.
 hipError_t launch_chunk_recurrent(const ChunkLaunch& a, hipStream_t stream);
-// Prefill through the chunked MFMA kernel (bf16 q/k/v, d = 128).
-hipError_t launch_chunk_mfma(const ChunkLaunch& a, hipStream_t stream);
-// Whether the chunked MFMA kernel takes this problem.
-bool chunk_mfma_supported(const ChunkLaunch& a);
 
-// Workspace bytes of the chunked prefill for a packed problem with n_docs documents.
+// Prefill through the fused single-pass chunked MFMA kernel (bf16 q/k/v, d = 128).
+hipError_t launch_chunk_mfma(const ChunkLaunch& a, hipStream_t stream);
+bool chunk_mfma_supported(const ChunkLaunch& a);
+// Its workspace: the longest-first document order of a packed problem.
 size_t chunk_workspace_bytes(int n_docs, bool packed);
+
+// Prefill in two passes: per-chunk preparation over all chunks at once, then
+// the serial state scan (bf16 q/k/v, d = 128).
+hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream);
+bool twopass_supported(const ChunkLaunch& a);
+size_t twopass_workspace_bytes(int num_seqs, int seq_len, int num_heads, bool packed);
+
+// Longest-first order of the documents of a packed problem (n <= 4096).
+hipError_t launch_doc_order(const int32_t* cu_seqlens, int n, int32_t* order, hipStream_t stream);
 
 }  // namespace kda

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum {
   KDA_OK = 0,
@@ -75,7 +75,8 @@ typedef struct kda_desc {
   int32_t qkv_dtype; /* kda_dtype of q, k, v                                     */
   int32_t out_dtype; /* kda_dtype of out (KDA_F32)                               */
   float scale;       /* output scale; 0 selects dk^-0.5                          */
-  void* workspace;   /* device scratch, >= kda_chunk_workspace_bytes(desc)       */
+  void* workspace;   /* device scratch of kda_chunk_fwd, at least
+                        kda_chunk_workspace_bytes(desc, packed) bytes          */
   size_t workspace_bytes;
 } kda_desc;
 
@@ -88,11 +89,16 @@ const char* kda_status_string(kda_status status);
 /* Detail of the last non-OK status returned on the calling thread ("" if none). */
 const char* kda_last_error(void);
 
-/* Device scratch bytes a packed kda_chunk_fwd call (cu_seqlens != NULL) needs
- * for this descriptor: a few bytes per document for the longest-first document
- * order.  Dense calls need no workspace (desc->workspace may then be NULL).
- * Returns 0 for a NULL descriptor. */
-size_t kda_chunk_workspace_bytes(const kda_desc* desc);
+/* Device scratch bytes kda_chunk_fwd needs for this descriptor; packed != 0
+ * for a call with cu_seqlens (desc->seq_len = total tokens, num_seqs =
+ * documents), 0 for a dense batch.  For bf16 q/k/v with d = 128 the chunked
+ * prefill stages fp16 per-chunk operands there: about 81 KiB per 64-token
+ * chunk and head (dense: B * ceil(T/64) chunks; packed: ceil(T/64) + N, an
+ * upper bound), plus a few bytes per document when packed.  Other
+ * configurations need none (0; desc->workspace may then be NULL).  The
+ * workspace is scratch: its contents on entry do not matter and are
+ * clobbered.  Returns 0 for a NULL or invalid descriptor. */
+size_t kda_chunk_workspace_bytes(const kda_desc* desc, int packed);
 
 /*
  * Chunked prefill (dense batch or packed varlen).

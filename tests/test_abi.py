@@ -37,7 +37,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert kda.abi_version() == 1
+    assert kda.abi_version() == 2
     seen = set()
     for code in range(8):
         s = lib.kda_status_string(code).decode()
@@ -144,7 +144,7 @@ def test_out_must_not_alias():
 def test_packed_needs_workspace():
     d = desc(num_seqs=5, seq_len=1000)
     assert chunk(d, cu=P(7 << 20)) == WORKSPACE
-    need = lib.kda_chunk_workspace_bytes(ctypes.byref(d))
+    need = lib.kda_chunk_workspace_bytes(ctypes.byref(d), 1)
     assert need >= 5 * 4
     d.workspace, d.workspace_bytes = FAKE + (8 << 20), need - 1
     assert chunk(d, cu=P(7 << 20)) == WORKSPACE
@@ -167,9 +167,31 @@ def test_empty_problems_are_noops():
     assert chunk(desc(seq_len=0), q=None, k=None, v=None, g=None, b=None, out=None) == OK
 
 
+SLOT = 82944  # workspace bytes per (64-token chunk, head) of the bf16 d = 128 prefill
+
+
 def test_workspace_bytes_dense_and_null():
-    assert lib.kda_chunk_workspace_bytes(None) == 0
-    assert kda.workspace_bytes(26, 32, 128) >= 26 * 4
+    assert lib.kda_chunk_workspace_bytes(None, 0) == 0
+    # dense: one slot per chunk and head
+    assert kda.workspace_bytes(4, 4096, 16, 128, packed=False) == 4 * 64 * 16 * SLOT
+    assert kda.workspace_bytes(3, 65, 2, 128, packed=False) == 3 * 2 * 2 * SLOT
+    # packed: ceil(T/64) + N slots per head, plus the document map
+    assert kda.workspace_bytes(26, 65536, 32, 128, packed=True) >= (1024 + 26) * 32 * SLOT
+    assert kda.workspace_bytes(26, 65536, 32, 128, packed=True) < (1024 + 26) * 32 * SLOT + 8192
+    # paths without a chunked kernel need nothing
+    assert kda.workspace_bytes(4, 4096, 16, 128, packed=False, qkv_dtype=kda.KDA_F32) == 0
+    assert kda.workspace_bytes(4, 4096, 16, 64, packed=True) == 0
+    assert kda.workspace_bytes(-1, 64, 4, 128, packed=False) == 0
+
+
+def test_dense_bf16_needs_workspace():
+    d = desc()
+    assert chunk(d) == WORKSPACE
+    assert "workspace" in last()
+    need = lib.kda_chunk_workspace_bytes(ctypes.byref(d), 0)
+    assert need == 2 * 1 * 4 * SLOT
+    d.workspace, d.workspace_bytes = FAKE + (8 << 20) + 8, need
+    assert chunk(d) == ALIGN
 
 
 def test_last_error_is_thread_local():

@@ -21,6 +21,17 @@ if not torch.cuda.is_available():  # collected on CPU, skipped there
 
 import gated_delta_rule_67_amd as kda  # noqa: E402
 
+# bf16 d = 128 prefill has two chunked MFMA implementations: the default
+# two-pass one (parallel per-chunk preparation, then the state scan) and the
+# fused single-pass kernel.  Every test runs under both.
+PATHS = ["twopass", "fused"]
+
+
+@pytest.fixture(params=PATHS, autouse=True)
+def prefill_path(request, monkeypatch):
+    monkeypatch.setenv("KDA_PREFILL_PATH", request.param)
+    return request.param
+
 
 def run_chunk(inp, **kw):
     d = to_dev(inp)
@@ -219,13 +230,13 @@ def test_mixed_fast_and_fallback_chunks():
     check_full(inp, "mixed fast/fallback chunks")
 
 
-def test_mfma_path_matches_recurrent_path(monkeypatch):
-    """The two prefill kernels agree with each other (and with the oracle)."""
+def test_mfma_path_matches_recurrent_path(monkeypatch, prefill_path):
+    """The chunked kernel agrees with the token-recurrent one (and with the oracle)."""
     inp = kda_inputs.make_inputs(B=2, T=333, H=4, dk=128, dv=128, dtype="bf16", seed=91)
     out_c, fin_c = run_chunk(inp)
     monkeypatch.setenv("KDA_PREFILL_PATH", "recurrent")
     out_r, fin_r = run_chunk(inp)
-    monkeypatch.delenv("KDA_PREFILL_PATH")
+    monkeypatch.setenv("KDA_PREFILL_PATH", prefill_path)
     ref_o, ref_f = oracle_full(inp)
     e_c = err(out_c.cpu().numpy(), ref_o)
     e_r = err(out_r.cpu().numpy(), ref_o)
@@ -234,3 +245,34 @@ def test_mfma_path_matches_recurrent_path(monkeypatch):
     assert e_c <= TOL["bf16"]
     assert err(out_c.cpu().numpy(), out_r.cpu().numpy()) <= TOL["bf16"]
     assert err(fin_c.cpu().numpy(), fin_r.cpu().numpy()) <= TOL["bf16"]
+
+
+def test_workspace_reused_and_contents_ignored():
+    """A caller workspace serves calls of different shapes, and whatever it
+    holds on entry (here NaN bytes) does not leak into the results."""
+    big = kda_inputs.make_inputs(B=1, T=700, H=3, dk=128, dv=128, dtype="bf16", seed=92,
+                                 lengths=[300, 0, 64, 336], init="normal", init_std=0.05)
+    small = kda_inputs.make_inputs(B=2, T=129, H=3, dk=128, dv=128, dtype="bf16", seed=93)
+    need = max(kda.workspace_bytes(4, 700, 3, 128, packed=True), kda.workspace_bytes(2, 129, 3, 128, packed=False))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    for inp, tag in ((big, "ws packed"), (small, "ws dense"), (big, "ws packed again")):
+        out, fin = run_chunk(inp, workspace=ws)
+        ref_o, ref_f = oracle_full(inp)
+        e_o, e_f = err(out.cpu().numpy(), ref_o), err(fin.cpu().numpy(), ref_f)
+        print(f"[{tag}] err_out={e_o:.3e} err_final={e_f:.3e}", flush=True)
+        assert e_o <= TOL["bf16"] and e_f <= TOL["bf16"]
+
+
+def test_twopass_matches_fused(monkeypatch):
+    """The two chunked implementations agree with each other on a packed batch."""
+    inp = kda_inputs.make_inputs(B=1, T=1500, H=4, dk=128, dv=128, dtype="bf16", seed=94,
+                                 lengths=[1, 700, 63, 0, 736], init="normal", init_std=0.05)
+    res = {}
+    for path in PATHS:
+        monkeypatch.setenv("KDA_PREFILL_PATH", path)
+        res[path] = run_chunk(inp)
+    (o1, f1), (o2, f2) = res["twopass"], res["fused"]
+    e_o = err(o1.cpu().numpy(), o2.cpu().numpy())
+    e_f = err(f1.cpu().numpy(), f2.cpu().numpy())
+    print(f"[twopass vs fused] out={e_o:.3e} final={e_f:.3e}", flush=True)
+    assert e_o <= TOL["bf16"] and e_f <= TOL["bf16"]
