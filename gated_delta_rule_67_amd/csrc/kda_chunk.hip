@@ -99,7 +99,7 @@ struct __align__(16) Smem {
   f16 Ql[2][C][LDK];       // q exp(G - R_blk), by chunk parity
   union {
     KrKd kk;
-    fb::Stage fb;
+    fb::Stage<4> fb;
   } u;
   f16 V[2][C][LDV];        // value tile (fp16), by chunk parity
   float beta[2][C];
@@ -115,7 +115,7 @@ struct __align__(16) Smem {
   int fbp[2][4];           // producer waves: chunk cannot take the fast path
   int sbp[4];              // consumer waves: state beyond the fast-path bound
 };
-static_assert(sizeof(fb::Stage) <= sizeof(KrKd), "fallback staging does not fit");
+static_assert(sizeof(fb::Stage<4>) <= sizeof(KrKd), "fallback staging does not fit");
 
 // Whether the chunk in buffer buf must be evaluated token by token: a
 // producer wave flagged it, or the state left the fast path's range.
@@ -633,7 +633,7 @@ __global__ void __launch_bounds__(NT, 1) chunk_kernel(ChunkArgs p) {
 
     if (fbk) {  // workgroup-uniform
       const fb::Args fa{p.q, p.k, p.v, p.log_g, p.beta, p.out, p.H, p.scale};
-      fb::eval_chunk(sm.u.fb, s, fa, tok_begin, ntok, k, h, col0);
+      fb::eval_chunk<4>(sm.u.fb, s, fa, tok_begin, ntok, k, h, col0);
       write_st(s);
       lds_barrier();
     }

@@ -58,4 +58,16 @@ __device__ __forceinline__ f16x4 h4(f32x4 x) {
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Raw buffer resource over [base, base + bytes) (CDNA buffer descriptor, no
+// swizzle, stride 0): a lane whose access falls outside the range has its
+// store dropped by the hardware, so partial tiles need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void buffer_store16(f32x4 x, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, static_cast<int>(byte_off), 0, 0);
+}
+
 }  // namespace kda

@@ -1,9 +1,10 @@
 // kda_fallback.h -- exact fp32 token-by-token evaluation of one 64-token chunk
 // on a 32-column state tile, for the chunks the MFMA fast path cannot take.
 //
-// The tile lives in MFMA accumulator layout across the four waves of a
-// 256-thread workgroup: s[a][b][e] = S[32w + 16a + 4lg + e][col0 + 16b + lc]
-// (w = wave, lane = 16lg + lc).  Per token (GLM-5.3-Flash model notes,
+// The tile lives in MFMA accumulator layout across the NWAVE waves of the
+// workgroup, each owning NA = 8 / NWAVE blocks of 16 key rows:
+// s[a][b][e] = S[16 NA w + 16a + 4lg + e][col0 + 16b + lc] (w = wave,
+// lane = 16lg + lc).  Per token (GLM-5.3-Flash model notes,
 // Glm5NextTextLinearAttention snippet): decay the key rows, read back S^T k,
 // form delta = beta (v - S^T k), add k delta^T; the output is read from the
 // updated state through S_new^T q = S_decayed^T q + delta (k . q).
@@ -17,9 +18,9 @@ namespace fb {
 constexpr int C = 64;     // chunk length
 constexpr int D = 128;    // head dim
 constexpr int DVT = 32;   // state columns per workgroup
-constexpr int NT = 256;   // threads per workgroup
 constexpr int TG = 16;    // tokens staged per pass
 
+template <int NWAVE>
 struct Stage {
   float a[TG][D];
   float k[TG][D];
@@ -27,7 +28,7 @@ struct Stage {
   float v[TG][DVT];
   float beta[TG];
   float kq[TG];
-  float red[2][4][DVT][2];
+  float red[2][NWAVE][DVT][2];
 };
 
 struct Args {
@@ -44,8 +45,11 @@ struct Args {
 // Chunk ck of the document whose tokens start at tok_begin (ntok tokens), head
 // h, state columns col0 .. col0+31.  Writes the chunk's outputs and advances s.
 // Every thread of the workgroup must call it (it synchronises internally).
-__device__ __forceinline__ void eval_chunk(Stage& st, f32x4 (&s)[2][2], const Args& p, size_t tok_begin,
-                                           int ntok, int ck, int h, int col0) {
+template <int NWAVE>
+__device__ __forceinline__ void eval_chunk(Stage<NWAVE>& st, f32x4 (&s)[8 / NWAVE][2], const Args& p,
+                                           size_t tok_begin, int ntok, int ck, int h, int col0) {
+  constexpr int NT = 64 * NWAVE;
+  constexpr int NA = 8 / NWAVE;
   const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
   const int cw = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
   const int H = p.H;
@@ -90,13 +94,15 @@ __device__ __forceinline__ void eval_chunk(Stage& st, f32x4 (&s)[2][2], const Ar
     }
     lds_barrier();
     {  // kq[r] = k_r . q_r : 16 lanes per token, 8 channels each
-      const int r = tid >> 4, cc = (tid & 15) * 8;
-      float acc = 0.f;
+      if (tid < 16 * TG) {
+        const int r = tid >> 4, cc = (tid & 15) * 8;
+        float acc = 0.f;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc += st.k[r][cc + c] * st.q[r][cc + c];
+        for (int c = 0; c < 8; ++c) acc += st.k[r][cc + c] * st.q[r][cc + c];
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
-      if ((tid & 15) == 0) st.kq[r] = acc;
+        for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
+        if ((tid & 15) == 0) st.kq[r] = acc;
+      }
     }
     lds_barrier();
     for (int r = 0; r < tg; ++r) {
@@ -104,10 +110,10 @@ __device__ __forceinline__ void eval_chunk(Stage& st, f32x4 (&s)[2][2], const Ar
       {
         float pa[2] = {0.f, 0.f}, pb[2] = {0.f, 0.f};
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < NA; ++a)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int c = 32 * cw + 16 * a + 4 * lg + e;
+            const int c = 16 * NA * cw + 16 * a + 4 * lg + e;
             const float al = st.a[r][c], kc = st.k[r][c], qc = st.q[r][c];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
@@ -140,7 +146,7 @@ __device__ __forceinline__ void eval_chunk(Stage& st, f32x4 (&s)[2][2], const Ar
           const int n = 16 * b + lc;
           float A = 0.f, B = 0.f;
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
+          for (int x = 0; x < NWAVE; ++x) {
             A += st.red[par][x][n][0];
             B += st.red[par][x][n][1];
           }
@@ -149,10 +155,10 @@ __device__ __forceinline__ void eval_chunk(Stage& st, f32x4 (&s)[2][2], const Ar
             p.out[((tok0 + t0 + r) * H + h) * D + col0 + n] = p.scale * (B + dl[b] * kq);
         }
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < NA; ++a)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float kc = st.k[r][32 * cw + 16 * a + 4 * lg + e];
+            const float kc = st.k[r][16 * NA * cw + 16 * a + 4 * lg + e];
 #pragma unroll
             for (int b = 0; b < 2; ++b) s[a][b][e] += kc * dl[b];
           }

@@ -20,7 +20,9 @@
 // value tile) it walks the unit's chunks with the fp32 state in MFMA
 // accumulators, three 64x128x32-class products per chunk (W S and Q' S share
 // the state operand; K^T Delta updates the state), with the slot operands
-// prefetched two chunks ahead.
+// of the next two chunks in flight while one chunk is processed.  Its eight waves split the roles: four form
+// Delta (the serial chain), four form the outputs, all eight update 16 state
+// rows each.
 //
 // Decay factors without overflow (pass 1).  The chunk is cut into four
 // 16-token blocks.  With R_I = G before block I's first token:
@@ -74,8 +76,8 @@ constexpr float F16_SAFE = 16384.0f;            // bound of every fp16 intermedi
 constexpr size_t OFF_NW = 0;        // -W          [64 tok][128 dk]  fp16
 constexpr size_t OFF_QP = 16384;    // Q'          [64 tok][128 dk]  fp16
 constexpr size_t OFF_KDT = 32768;   // (K exp(gamma - G))^T [128 dk][64 tok] fp16
-constexpr size_t OFF_UT = 49152;    // U^T         [128 dv][64 tok]  fp16
-constexpr size_t OFF_OU = 65536;    // Ou          [64 tok][128 dv]  fp16
+constexpr size_t OFF_UP = 49152;    // U  by scan lane: [I][tile][lane][b][e] = U[16I+lc][32tile+16b+4lg+e]
+constexpr size_t OFF_OP = 65536;    // Ou by scan lane: [I][tile][lane][b][e] = Ou[16I+lc][32tile+16b+4lg+e]
 constexpr size_t OFF_GAM = 81920;   // exp(gamma)  [128] fp32
 constexpr size_t OFF_FLAG = 82432;  // per-wave "not on the fast path" [4] int32
 constexpr size_t SLOT_BYTES = 82944;
@@ -511,8 +513,8 @@ __global__ void __launch_bounds__(NT, 2) prep_kernel(PrepArgs p) {
   {
     f16* nw = reinterpret_cast<f16*>(slot + OFF_NW);
     f16* qp = reinterpret_cast<f16*>(slot + OFF_QP);
-    f16* ut = reinterpret_cast<f16*>(slot + OFF_UT);
-    f16* ou = reinterpret_cast<f16*>(slot + OFF_OU);
+    f16* up = reinterpret_cast<f16*>(slot + OFF_UP);
+    f16* op = reinterpret_cast<f16*>(slot + OFF_OP);
     float omax = 0.f;
 #pragma unroll
     for (int nn = 0; nn < 2; ++nn) {
@@ -544,7 +546,7 @@ __global__ void __launch_bounds__(NT, 2) prep_kernel(PrepArgs p) {
           const f16x4 tf = I == J ? sm.frag[S_TD + I][lane] : sm.frag[S_TO + pair6(I, J)][lane];
           const f16x4 bf = sm.frag[S_BS + tile10(I, J)][lane];
           aW = mfma16(xk[J], tf, aW);   // W^T     [col 4lg+e][tok lc]
-          aU = mfma16(tf, xvv[J], aU);  // U       [tok 4lg+e][col lc]
+          aU = mfma16(xvv[J], tf, aU);  // U^T     [col 4lg+e][tok lc]
           aQ = mfma16(xk[J], bf, aQ);   // Q'^T    [col 4lg+e][tok lc]
           aO = mfma16(xvv[J], bf, aO);  // -Ou^T   [col 4lg+e][tok lc]
         }
@@ -557,8 +559,10 @@ __global__ void __launch_bounds__(NT, 2) prep_kernel(PrepArgs p) {
         const int rowoff = (16 * I + lc) * D + 16 * n + 4 * lg;
         *reinterpret_cast<f16x4*>(nw + rowoff) = h4(aW);
         *reinterpret_cast<f16x4*>(qp + rowoff) = h4(aQ);
-        *reinterpret_cast<f16x4*>(ou + rowoff) = h4(aO);
-        *reinterpret_cast<f16x4*>(ut + (16 * n + lc) * C + 16 * I + 4 * lg) = h4(aU);
+        // U and Ou in the order one scan lane consumes them (same lane here)
+        const int laneoff = ((I * NTILE + (n >> 1)) * 64 + lane) * 8 + 4 * (n & 1);
+        *reinterpret_cast<f16x4*>(up + laneoff) = h4(aU);
+        *reinterpret_cast<f16x4*>(op + laneoff) = h4(aO);
       }
     }
     bad |= !(omax <= F16_SAFE);
@@ -591,26 +595,44 @@ struct ScanArgs {
   float scale;
 };
 
+constexpr int NTS = 512;  // scan threads: 8 waves
+
 struct __align__(16) ScanSmem {
   f16 ST[DVT][LDK];   // S^T (fp16) [value col][key row]
   f16 DT[DVT][LDT];   // Delta^T    [value col][token]
-  fb::Stage fb;
-  int sbp[4];         // per wave: state beyond the fast-path bound
-  int dbp[4];         // per wave: Delta beyond the fp16 bound
+  f16 DTX[DVT][LDT];  // where the output waves' copy of that store lands (never read)
+  fb::Stage<8> fb;
+  int sbp[8];         // per wave: state beyond the fast-path bound
+  int dbp[8];         // per wave: Delta beyond the fp16 bound (output waves: unused)
 };
 
-// Slot operands of one chunk as one scan thread uses them.
+// Slot operands of one chunk as one scan thread uses them.  Waves 0-3 form
+// Delta rows 16w.. (m = -W rows, uo = U); waves 4-7 form output rows
+// 16(w-4).. (m = Q' rows, uo = Ou); every wave updates key rows 16w.. .
+// Both kinds run the same instruction stream (transposed products
+// [col][token]); only their operands and the targets of their stores differ.
 struct Pre {
-  f16x8 nw[4];      // -W  rows 16cw+lc, key cols 32ks+8lg ..
-  f16x8 qp[4];      // Q'  rows 16cw+lc, key cols 32ks+8lg ..
-  f16x8 kd[2][2];   // Kd^T rows 32cw+16a+lc, tokens 32ks+8lg ..
-  f16x4 ut[2];      // U   rows 16cw+4lg .., value col col0+16b+lc
-  f16x4 ou[2];      // Ou  row 16cw+lc, value cols col0+16b+4lg ..
-  float4 gam[2];    // exp(gamma) of key rows 32cw+16a+4lg ..
+  f16x8 m[4];       // -W or Q' row 16I+lc, key cols 32ks+8lg ..
+  f16x8 kd[2];      // Kd^T row 16w+lc, tokens 32ks+8lg ..
+  f16x8 uo;         // U / Ou of this lane, [b][e]
+  float4 gam;       // exp(gamma) of key rows 16w+4lg ..
   int4 flag;
 };
 
-__global__ void __launch_bounds__(NT, 1) scan_kernel(ScanArgs p) {
+struct State2 {
+  f32x4 s0, s1;
+};
+
+// The token-by-token evaluation of one chunk, out of line: its scattered
+// loads and waits stay out of the scan loop's wait-count bookkeeping.
+__device__ __noinline__ State2 scan_fallback(fb::Stage<8>& st, State2 in, const fb::Args fa, size_t tok_begin,
+                                             int ntok, int k, int h, int col0) {
+  f32x4 s[1][2] = {{in.s0, in.s1}};
+  fb::eval_chunk<8>(st, s, fa, tok_begin, ntok, k, h, col0);
+  return State2{s[0][0], s[0][1]};
+}
+
+__global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   ScanSmem& sm = *reinterpret_cast<ScanSmem*>(smem_raw);
 
@@ -643,106 +665,115 @@ __global__ void __launch_bounds__(NT, 1) scan_kernel(ScanArgs p) {
   const size_t slot_stride = static_cast<size_t>(H) * SLOT_BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
-  const int cw = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
+  const bool is_o = w >= 4;     // output wave (else Delta wave)
+  const int I = w & 3;          // token block of the Delta / output rows
 
+  // Loads of chunk k's operands, in three groups: the flag (used first), the
+  // Delta / output operands (phase A) and the state-update operands (phase B).
+  auto slot_of = [&](int k) { return slot0 + static_cast<size_t>(k) * slot_stride; };
+  auto load_flag = [&](int k, Pre& r) { r.flag = *reinterpret_cast<const int4*>(slot_of(k) + OFF_FLAG); };
+  auto load_a = [&](int k, Pre& r) {
+    const unsigned char* sl = slot_of(k);
+    const f16* mp = reinterpret_cast<const f16*>(sl + (is_o ? OFF_QP : OFF_NW)) + (16 * I + lc) * D + 8 * lg;
+    const f16* uo = reinterpret_cast<const f16*>(sl + (is_o ? OFF_OP : OFF_UP)) + ((I * NTILE + tile) * 64 + lane) * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) r.m[ks] = ld8(mp + 32 * ks);
+    r.uo = ld8(uo);
+  };
+  auto load_b = [&](int k, Pre& r) {
+    const unsigned char* sl = slot_of(k);
+    const f16* kd = reinterpret_cast<const f16*>(sl + OFF_KDT) + (16 * w + lc) * C + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) r.kd[ks] = ld8(kd + 32 * ks);
+    r.gam = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl + OFF_GAM) + 16 * w + 4 * lg);
+  };
   auto load = [&](int k, Pre& r) {
-    const unsigned char* sl = slot0 + static_cast<size_t>(k) * slot_stride;
-    const f16* nw = reinterpret_cast<const f16*>(sl + OFF_NW);
-    const f16* qp = reinterpret_cast<const f16*>(sl + OFF_QP);
-    const f16* kd = reinterpret_cast<const f16*>(sl + OFF_KDT);
-    const f16* ut = reinterpret_cast<const f16*>(sl + OFF_UT);
-    const f16* ou = reinterpret_cast<const f16*>(sl + OFF_OU);
-    const float* gm = reinterpret_cast<const float*>(sl + OFF_GAM);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      r.nw[ks] = ld8(nw + (16 * cw + lc) * D + 32 * ks + 8 * lg);
-      r.qp[ks] = ld8(qp + (16 * cw + lc) * D + 32 * ks + 8 * lg);
-    }
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) r.kd[a][ks] = ld8(kd + (32 * cw + 16 * a + lc) * C + 32 * ks + 8 * lg);
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      r.ut[b] = ld4(ut + (col0 + 16 * b + lc) * C + 16 * cw + 4 * lg);
-      r.ou[b] = ld4(ou + (16 * cw + lc) * D + col0 + 16 * b + 4 * lg);
-    }
-#pragma unroll
-    for (int a = 0; a < 2; ++a) r.gam[a] = *reinterpret_cast<const float4*>(gm + 32 * cw + 16 * a + 4 * lg);
-    r.flag = *reinterpret_cast<const int4*>(sl + OFF_FLAG);
+    load_flag(k, r);
+    load_a(k, r);
+    load_b(k, r);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // s[a][b][e] = S[32cw+16a+4lg+e][col0+16b+lc]
-  auto write_st = [&](f32x4 (&s)[2][2]) {
+  // s[0][b][e] = S[16w+4lg+e][col0+16b+lc]
+  auto write_st = [&](f32x4 (&s)[1][2]) {
     bool big = false;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 2; ++b) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) big |= !(fabsf(s[a][b][e]) <= S_MAX);
-        *reinterpret_cast<f16x4*>(&sm.ST[16 * b + lc][32 * cw + 16 * a + 4 * lg]) = h4(s[a][b]);
-      }
+      for (int e = 0; e < 4; ++e) big |= !(fabsf(s[0][b][e]) <= S_MAX);
+      *reinterpret_cast<f16x4*>(&sm.ST[16 * b + lc][16 * w + 4 * lg]) = h4(s[0][b]);
+    }
     const bool any = __builtin_amdgcn_ballot_w64(big) != 0;
-    if (lane == 0) sm.sbp[cw] = any;
+    if (lane == 0) sm.sbp[w] = any;
   };
 
-  f32x4 s[2][2];
+  f32x4 s[1][2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        s[a][b][e] = p.init_state ? p.init_state[unit_state + (32 * cw + 16 * a + 4 * lg + e) * D + col0 + 16 * b + lc]
-                                  : 0.f;
+    for (int e = 0; e < 4; ++e)
+      s[0][b][e] = p.init_state ? p.init_state[unit_state + (16 * w + 4 * lg + e) * D + col0 + 16 * b + lc] : 0.f;
   write_st(s);
   const fb::Args fa{p.q, p.k, p.v, p.log_g, p.beta, p.out, H, p.scale};
 
-  // One chunk: consume cur (chunk k), prefetch chunk k+2 into nxt.
-  auto step = [&](int k, Pre& cur, Pre& nxt) {
-    if (k + 2 < nch) load(k + 2, nxt);
+  // One chunk: consume cur (chunk k); each group of cur's registers is
+  // refilled with chunk k+2 right after its last use (clamped to the last
+  // chunk, so every step issues the same loads), which gives each load
+  // almost two steps to arrive without a third register buffer.
+  auto step = [&](int k, Pre& cur) {
+    const int kn = min(k + 2, nch - 1);
     const size_t tok0 = tok_begin + static_cast<size_t>(k) * C;
     const int nv = min(C, ntok - k * C);
     lds_barrier();  // ST of the entry state is complete
     const int pflag = __builtin_amdgcn_readfirstlane(cur.flag.x | cur.flag.y | cur.flag.z | cur.flag.w);
-    const bool sbig = (sm.sbp[0] | sm.sbp[1] | sm.sbp[2] | sm.sbp[3]) != 0;
+    // the load groups stay in program order (flag, phase A, phase B operands,
+    // chunk after chunk), so the wait before each use counts exactly the
+    // loads issued after it
+    __builtin_amdgcn_sched_barrier(0);
+    load_flag(kn, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool sbig = (sm.sbp[0] | sm.sbp[1] | sm.sbp[2] | sm.sbp[3] | sm.sbp[4] | sm.sbp[5] | sm.sbp[6] |
+                       sm.sbp[7]) != 0;
 
-    // ---- phase A: Delta = U - W S (into DT), O = Q' S + Ou
+    // ---- phase A: Delta^T = U^T + S^T (-W)^T (waves 0-3, into DT) and
+    // O^T = Ou^T + S^T Q'^T (waves 4-7, to out), one instruction stream
     f16x8 sf[4][2];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int b = 0; b < 2; ++b) sf[ks][b] = ld8(&sm.ST[16 * b + lc][32 * ks + 8 * lg]);
+    // output rows past the document's end fall outside the resource; the
+    // Delta waves' copy of the store gets an empty resource (dropped)
+    const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(
+        p.out + (tok0 * H + h) * D + col0, is_o ? static_cast<uint32_t>(((nv - 1) * H * D + DVT) * 4) : 0u);
+    const uint32_t ooff = static_cast<uint32_t>(((16 * I + lc) * H * D + 4 * lg) * 4);
+    f16* dt = is_o ? &sm.DTX[0][0] : &sm.DT[0][0];
     bool dbig = false;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       f32x4 acc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = (float)cur.ut[b][e];
+      for (int e = 0; e < 4; ++e) acc[e] = (float)cur.uo[4 * b + e];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma32(cur.nw[ks], sf[ks][b], acc);  // [tok 4lg+e][col lc]
+      for (int ks = 0; ks < 4; ++ks) acc = mfma32(sf[ks][b], cur.m[ks], acc);  // [col 4lg+e][tok lc]
+      buffer_store16(acc, orsrc, ooff + 64 * b);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dbig |= !(fabsf(acc[e]) <= F16_SAFE);
-      *reinterpret_cast<f16x4*>(&sm.DT[16 * b + lc][16 * cw + 4 * lg]) = h4(acc);
+      for (int e = 0; e < 4; ++e) {
+        dbig |= !(fabsf(acc[e]) <= F16_SAFE);
+        dt[(16 * b + 4 * lg + e) * LDT + 16 * I + lc] = (f16)acc[e];
+      }
     }
     {
       const bool any = __builtin_amdgcn_ballot_w64(dbig) != 0;
-      if (lane == 0) sm.dbp[cw] = any;
+      if (lane == 0) sm.dbp[w] = any;
     }
-    float* orow = p.out + ((tok0 + 16 * cw + lc) * H + h) * D + col0 + 4 * lg;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      f32x4 o;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = (float)cur.ou[b][e];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) o = mfma32(sf[ks][b], cur.qp[ks], o);  // [col 4lg+e][tok lc]
-      if (16 * cw + lc < nv) *reinterpret_cast<float4*>(orow + 16 * b) = make_float4(o[0], o[1], o[2], o[3]);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(kn, cur);
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
 
-    // ---- phase B: S = exp(gamma) S + Kd^T Delta
+    // ---- phase B: S = exp(gamma) S + Kd^T Delta (all waves, key rows 16w..)
     const bool fbk = pflag != 0 || sbig || (sm.dbp[0] | sm.dbp[1] | sm.dbp[2] | sm.dbp[3]) != 0;
     if (!fbk) {  // workgroup-uniform
       f16x8 dB[2][2];
@@ -750,44 +781,52 @@ __global__ void __launch_bounds__(NT, 1) scan_kernel(ScanArgs p) {
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
         for (int b = 0; b < 2; ++b) dB[ks][b] = ld8(&sm.DT[16 * b + lc][32 * ks + 8 * lg]);
+      const float gg[4] = {cur.gam.x, cur.gam.y, cur.gam.z, cur.gam.w};
 #pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const float gg[4] = {cur.gam[a].x, cur.gam[a].y, cur.gam[a].z, cur.gam[a].w};
+      for (int b = 0; b < 2; ++b) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int e = 0; e < 4; ++e) s[0][b][e] *= gg[e];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[a][b][e] *= gg[e];
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) s[a][b] = mfma32(cur.kd[a][ks], dB[ks][b], s[a][b]);
-        }
+        for (int ks = 0; ks < 2; ++ks) s[0][b] = mfma32(cur.kd[ks], dB[ks][b], s[0][b]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      load_b(kn, cur);
+      __builtin_amdgcn_sched_barrier(0);
       write_st(s);
     } else {
       // token by token from the entry state; rewrites this chunk's outputs
       __syncthreads();
-      fb::eval_chunk(sm.fb, s, fa, tok_begin, ntok, k, h, col0);
+      const State2 r = scan_fallback(sm.fb, State2{s[0][0], s[0][1]}, fa, tok_begin, ntok, k, h, col0);
+      s[0][0] = r.s0;
+      s[0][1] = r.s1;
       __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      load_b(kn, cur);
+      __builtin_amdgcn_sched_barrier(0);
       write_st(s);
     }
   };
 
-  Pre b0, b1, b2;
-  if (nch > 0) load(0, b0);
-  if (nch > 1) load(1, b1);
-  for (int k = 0; k < nch; k += 3) {
-    step(k, b0, b2);
-    if (k + 1 < nch) step(k + 1, b1, b0);
-    if (k + 2 < nch) step(k + 2, b2, b1);
+  // two operand buffers, even and odd chunks; the main loop body has no
+  // branch around a step
+  if (nch > 0) {  // workgroup-uniform
+    Pre b0, b1;
+    load(0, b0);
+    load(min(1, nch - 1), b1);
+    int k = 0;
+    for (; k + 2 <= nch; k += 2) {
+      step(k, b0);
+      step(k + 1, b1);
+    }
+    if (k < nch) step(k, b0);
   }
 
   if (p.final_state) {
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          p.final_state[unit_state + (32 * cw + 16 * a + 4 * lg + e) * D + col0 + 16 * b + lc] = s[a][b][e];
+      for (int e = 0; e < 4; ++e)
+        p.final_state[unit_state + (16 * w + 4 * lg + e) * D + col0 + 16 * b + lc] = s[0][b][e];
   }
 }
 
@@ -963,7 +1002,7 @@ hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream) {
   sp.scale = a.scale;
   const unsigned units = static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads);
   const unsigned blocks = ((units + 7) / 8) * 8 * NTILE;
-  hipLaunchKernelGGL(scan_kernel, dim3(blocks), dim3(NT), sizeof(ScanSmem), stream, sp);
+  hipLaunchKernelGGL(scan_kernel, dim3(blocks), dim3(NTS), sizeof(ScanSmem), stream, sp);
   return hipGetLastError();
 }
 
