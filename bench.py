@@ -1,6 +1,8 @@
 """Benchmark of libkda on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py --only {prefill,step,copy}      (profiling runs)
+    python bench.py --traffic-from FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
 
 A step is one kda_chunk_fwd call (chunked prefill) over the dense workload
 B=4 x T=4096 tokens, H=16 heads, dk=dv=128, bf16 q/k/v, fp32 gates/beta/state,
@@ -15,10 +17,20 @@ fp32 out, with inputs resident in HBM.  ``value`` is prefill tokens/s
   cpu_baseline  the fp64 oracle timed on the host on a bounded sample of the
                 same prefill workload
 Only one GPU is used; --gpus above 1 exits with a message.
+
+roofline.traffic is the HBM bytes of one prefill call measured with rocprofv3
+counters (FETCH_SIZE, WRITE_SIZE; one pass each), scaled by what the same
+counters read for a plain copy of known size (--only copy).  --traffic-from
+turns those four runs' CSV output into profiles/traffic_prefill_dense.txt,
+stamped with a hash of the kernel sources; the figure is reported only while
+the sources still hash the same (else null).
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -35,6 +47,72 @@ import kda_inputs  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2516.6      # MI355X dense fp16/bf16 MFMA, TFLOP/s
 CHUNK = 64
+COPY_BYTES = 512 << 20         # calibration copy: bytes read (= bytes written)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_dense.txt")
+KERNEL_SOURCES = ["kda_twopass.hip", "kda_common.h", "kda_fallback.h", "kda_api.cpp", "kda_launch.h"]
+
+
+def sources_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_67_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per prefill call from the committed counter summary, or None
+    when it is missing or was taken on other kernel sources."""
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("sources_sha256") != sources_hash():
+            return None
+        return int(kv["traffic_bytes_per_call"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def _counter_sums(run_dir: str, counter: str):
+    """{kernel name: mean per-dispatch value} of one rocprofv3 --pmc csv run."""
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {run_dir}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") != counter:
+                continue
+            key = (r["Kernel_Name"], r["Dispatch_Id"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in per.items():
+        out.setdefault(name, []).append(v)
+    return {k: sum(v) / len(v) for k, v in out.items()}
+
+
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+    fe, wr = _counter_sums(fetch_dir, "FETCH_SIZE"), _counter_sums(write_dir, "WRITE_SIZE")
+    cf, cw = _counter_sums(copy_fetch_dir, "FETCH_SIZE"), _counter_sums(copy_write_dir, "WRITE_SIZE")
+    pick = lambda d, pat: sum(v for k, v in d.items() if pat in k)
+    copy_f = max(cf.values())   # the copy is the largest dispatch of its run
+    copy_w = max(cw.values())
+    k_fetch = COPY_BYTES / (copy_f * 1024.0)
+    k_write = COPY_BYTES / (copy_w * 1024.0)
+    lines = [f"sources_sha256: {sources_hash()}",
+             f"copy_fetch_kib: {copy_f:.1f}", f"copy_write_kib: {copy_w:.1f}",
+             f"fetch_scale: {k_fetch:.4f}", f"write_scale: {k_write:.4f}"]
+    total = 0.0
+    for pat in ("prep_kernel", "scan_kernel"):
+        f, w = pick(fe, pat), pick(wr, pat)
+        b = f * 1024 * k_fetch + w * 1024 * k_write
+        total += b
+        lines += [f"{pat}_fetch_kib: {f:.1f}", f"{pat}_write_kib: {w:.1f}", f"{pat}_bytes: {b:.0f}"]
+    lines.append(f"traffic_bytes_per_call: {total:.0f}")
+    return lines
 
 
 def prefill_bytes(tokens: int, H: int, d: int, n_states: int, qkv_bytes=2) -> int:
@@ -117,34 +195,36 @@ def bench_step(kda, name, steps, warmup):
 
 
 def cpu_baseline(inp, target_s=10.0):
-    """Time the fp64 oracle on a bounded sample of the prefill workload: whole
-    sequences, a subset of heads, sized from a pilot run to ~target_s."""
+    """Time the fp64 oracle on a bounded sample of the prefill workload: the
+    whole workload (all sequences and heads, OpenMP over the units), repeated
+    until about target_s of wall time has passed."""
     import oracle
     from kda_inputs import to_f64
     threads = max(1, min(16, os.cpu_count() or 1))
     B, T, H, D = inp["q"].shape
-
-    def run(nb, nh):
-        sl = lambda t: to_f64(t[:nb, :, :nh])
-        s0 = to_f64(inp["init_state"][:nb, :nh])
-        args = (sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), sl(inp["log_g"]),
-                to_f64(inp["beta"][:nb, :, :nh]))
+    args = (to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]), to_f64(inp["log_g"]), to_f64(inp["beta"]))
+    s0 = to_f64(inp["init_state"])
+    reps, elapsed = 0, 0.0
+    while elapsed < target_s:
         t0 = time.perf_counter()
         oracle.kda_forward(*args, init_state=s0, scale=inp["scale"], n_threads=threads)
-        return time.perf_counter() - t0
-
-    # pilot: one sequence, up to `threads` heads, one unit per thread
-    t_pilot = run(1, min(H, threads))
-    waves = max(1, int(target_s / max(t_pilot, 1e-3)))
-    units = min(B * H, waves * threads)
-    nh = H if units >= H else units
-    nb = max(1, min(B, units // H))
-    elapsed = run(nb, nh)
-    token_heads = nb * T * nh
-    return {"value": round(token_heads / elapsed / H, 1), "unit": "tokens/s", "cores": threads,
+        elapsed += time.perf_counter() - t0
+        reps += 1
+    token_heads = reps * B * T * H
+    return {"value": round(reps * B * T / elapsed, 1), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{nb} x {T} tokens x {nh} of {H} heads ({token_heads} token-heads, fp64 token loop, "
-                      f"{elapsed:.1f} s); tokens/s of the {H}-head mixer"}
+            "sample": f"the whole workload ({B} x {T} tokens x {H} heads, fp64 token loop) run {reps} times "
+                      f"back to back, {token_heads} token-heads in {elapsed:.1f} s on {threads} threads"}
+
+
+def bench_copy(steps, warmup):
+    """A plain device copy of COPY_BYTES (the counter calibration kernel)."""
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    wall, ms = timed_calls(lambda: dst.copy_(src), steps, warmup)
+    avg = float(np.mean(ms))
+    print(f"copy: {COPY_BYTES >> 20} MiB in {avg * 1e3:.1f} us = {2 * COPY_BYTES / (avg * 1e-3) / 1e9:.0f} GB/s",
+          file=sys.stderr, flush=True)
 
 
 def main():
@@ -153,9 +233,26 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "step"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "step", "copy"], default="all",
                     help="restrict the run (profiling); the JSON line needs 'all'")
+    ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
+                    help="rocprofv3 csv dirs: prefill FETCH_SIZE, prefill WRITE_SIZE, copy FETCH_SIZE, "
+                         "copy WRITE_SIZE; writes " + os.path.relpath(TRAFFIC_FILE, ROOT))
     args = ap.parse_args()
+    if args.traffic_from:
+        lines = write_traffic(*args.traffic_from)
+        with open(TRAFFIC_FILE, "w") as fh:
+            fh.write("# HBM traffic of one kda_chunk_fwd call, dense 4 x 4096 tokens, 16 heads, d = 128, bf16\n")
+            fh.write("# made by: python bench.py --traffic-from " + " ".join(args.traffic_from) + "\n")
+            fh.write("# from four counter runs (cd /tmp && export TMPDIR=/tmp first), one pass each:\n")
+            for ctr, what, d in (("FETCH_SIZE", "prefill", args.traffic_from[0]), ("WRITE_SIZE", "prefill", args.traffic_from[1]),
+                                 ("FETCH_SIZE", "copy", args.traffic_from[2]), ("WRITE_SIZE", "copy", args.traffic_from[3])):
+                steps = "--steps 3 --warmup 1"
+                fh.write(f"#   rocprofv3 --pmc {ctr} -f csv -d {d} -o run -- python3 bench.py --only {what} {steps}\n")
+            fh.write("# values are KiB per dispatch (mean over the run's dispatches); scale = copy bytes / counter bytes\n")
+            fh.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build runs on a single MI355X)", file=sys.stderr)
@@ -165,6 +262,9 @@ def main():
         sys.exit(2)
     import gated_delta_rule_67_amd as kda
 
+    if args.only == "copy":
+        bench_copy(args.steps, args.warmup)
+        return
     res = {}
     if args.only in ("all", "prefill"):
         res["prefill"] = bench_prefill(kda, args.steps, args.warmup)
@@ -194,13 +294,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": os.environ.get("KDA_BENCH_DTYPE_LABEL", "bf16 in, f32 state"),
+        "dtype": "f16 MFMA operands, f32 accumulation and state (bf16 inputs)",
         "data": "synthetic (seeded; q,v~N(0,1), k L2-normalised, log_g=-softplus(N)*0.05, beta=sigmoid(N))",
         "config": {"workload": "chunked prefill, dense B=4 x T=4096, H=16, dk=dv=128, bf16 q/k/v, "
                                "fp32 log_g/beta/state, fp32 out, chunk 64",
                    "global_batch": 4, "seq_len": 4096, "heads": 16, "head_dim": 128},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
+                     "kernel": "kda_chunk_fwd = prep_kernel + scan_kernel back to back (one call)"},
         "prefill_kernel_us": round(k_ms * 1e3, 2),
         "algorithmic_bytes_per_launch": p["bytes"],
         "mfma": {"achieved_TFLOPs": round(tflops, 2), "peak_TFLOPs": MFMA_PEAK_TFLOPS,
