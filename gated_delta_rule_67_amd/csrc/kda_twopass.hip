@@ -73,9 +73,13 @@ constexpr float S_MAX = 2048.0f;                // |S| bound of the fast path
 constexpr float F16_SAFE = 16384.0f;            // bound of every fp16 intermediate
 
 // Workspace slot of one (chunk, head), bytes.
-constexpr size_t OFF_NW = 0;        // -W          [64 tok][128 dk]  fp16
-constexpr size_t OFF_QP = 16384;    // Q'          [64 tok][128 dk]  fp16
-constexpr size_t OFF_KDT = 32768;   // (K exp(gamma - G))^T [128 dk][64 tok] fp16
+// -W, Q' and (K exp(gamma - G))^T are stored in the order the scan's lanes
+// read them, so every scan load instruction covers 1 KiB of whole lines:
+//   NW, QP: [I 4][ks 4][lane 64][j 8] = X[16I+lc][32ks+8lg+j]
+//   KDT:    [r 8][ks 2][lane 64][j 8] = Kd^T[16r+lc][32ks+8lg+j]
+constexpr size_t OFF_NW = 0;        // -W          64 x 128  fp16
+constexpr size_t OFF_QP = 16384;    // Q'          64 x 128  fp16
+constexpr size_t OFF_KDT = 32768;   // Kd^T        128 x 64  fp16
 constexpr size_t OFF_UP = 49152;    // U  by scan lane: [I][tile][lane][b][e] = U[16I+lc][32tile+16b+4lg+e]
 constexpr size_t OFF_OP = 65536;    // Ou by scan lane: [I][tile][lane][b][e] = Ou[16I+lc][32tile+16b+4lg+e]
 constexpr size_t OFF_GAM = 81920;   // exp(gamma)  [128] fp32
@@ -366,7 +370,11 @@ __global__ void __launch_bounds__(NT, 2) prep_kernel(PrepArgs p) {
       f16x4 kd;
 #pragma unroll
       for (int j = 0; j < 4; ++j) kd[j] = (f16)((float)hr[j][c] * gd[c]);
-      *reinterpret_cast<f16x4*>(kdt + (c8 + c) * C + 16 * w + 4 * qt) = kd;
+      // Kd^T[dk 8oct+c][tok 16w+4qt+j]: row block dk/16, k-step tok/32,
+      // lane (lg = tok%32/8, lc = dk%16), position 4(qt&1)+j
+      const int dk = c8 + c;
+      const int sl = 16 * (2 * (w & 1) + (qt >> 1)) + (dk & 15);
+      *reinterpret_cast<f16x4*>(kdt + (((dk >> 4) * 2 + (w >> 1)) * 64 + sl) * 8 + 4 * (qt & 1)) = kd;
     }
     // Xk = beta k exp(G) = beta Kl exp(R_w), kept in registers until the
     // products have released Kl / Kr
@@ -556,7 +564,9 @@ __global__ void __launch_bounds__(NT, 2) prep_kernel(PrepArgs p) {
           aW[e] = -aW[e];
           aO[e] = -aO[e];
         }
-        const int rowoff = (16 * I + lc) * D + 16 * n + 4 * lg;
+        // X[tok 16I+lc][col 16n+4lg+e]: block I, k-step n/2, lane
+        // (lg' = 2(n&1) + lg/2, lc), position 4(lg&1)+e
+        const int rowoff = ((I * 4 + (n >> 1)) * 64 + 16 * (2 * (n & 1) + (lg >> 1)) + lc) * 8 + 4 * (lg & 1);
         *reinterpret_cast<f16x4*>(nw + rowoff) = h4(aW);
         *reinterpret_cast<f16x4*>(qp + rowoff) = h4(aQ);
         // U and Ou in the order one scan lane consumes them (same lane here)
@@ -675,17 +685,17 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
   auto load_flag = [&](int k, Pre& r) { r.flag = *reinterpret_cast<const int4*>(slot_of(k) + OFF_FLAG); };
   auto load_a = [&](int k, Pre& r) {
     const unsigned char* sl = slot_of(k);
-    const f16* mp = reinterpret_cast<const f16*>(sl + (is_o ? OFF_QP : OFF_NW)) + (16 * I + lc) * D + 8 * lg;
+    const f16* mp = reinterpret_cast<const f16*>(sl + (is_o ? OFF_QP : OFF_NW)) + (I * 4 * 64 + lane) * 8;
     const f16* uo = reinterpret_cast<const f16*>(sl + (is_o ? OFF_OP : OFF_UP)) + ((I * NTILE + tile) * 64 + lane) * 8;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) r.m[ks] = ld8(mp + 32 * ks);
+    for (int ks = 0; ks < 4; ++ks) r.m[ks] = ld8(mp + ks * 64 * 8);
     r.uo = ld8(uo);
   };
   auto load_b = [&](int k, Pre& r) {
     const unsigned char* sl = slot_of(k);
-    const f16* kd = reinterpret_cast<const f16*>(sl + OFF_KDT) + (16 * w + lc) * C + 8 * lg;
+    const f16* kd = reinterpret_cast<const f16*>(sl + OFF_KDT) + (w * 2 * 64 + lane) * 8;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) r.kd[ks] = ld8(kd + 32 * ks);
+    for (int ks = 0; ks < 2; ++ks) r.kd[ks] = ld8(kd + ks * 64 * 8);
     r.gam = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl + OFF_GAM) + 16 * w + 4 * lg);
   };
   auto load = [&](int k, Pre& r) {
