@@ -28,6 +28,16 @@ __device__ __forceinline__ float exp_fast(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
+// 16-byte fp32 load / store with the nontemporal hint (data read or written
+// once: keep it from displacing reused lines in the caches).
+__device__ __forceinline__ float4 load4_stream(const float* p) {
+  const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+  return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void store4_stream(float* p, float4 v) {
+  __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(p));
+}
+
 // Load 4 consecutive elements (16-byte aligned for fp32, 8-byte for bf16) as floats.
 __device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ float4 load4(const bf16_t* p) {

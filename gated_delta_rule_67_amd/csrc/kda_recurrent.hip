@@ -28,7 +28,8 @@ namespace {
 
 template <int D, int DVT>
 struct RecCfg {
-  static constexpr int NT = (D * DVT / 4) >= 1024 ? 256 : 64;  // threads per workgroup
+  // threads per workgroup: a whole 64 KiB state streams best with 512 threads
+  static constexpr int NT = (D * DVT / 4) >= 4096 ? 512 : (D * DVT / 4) >= 1024 ? 256 : 64;
   static constexpr int CL = DVT / 4;                            // column lanes
   static constexpr int RG = NT / CL;                            // row groups
   static constexpr int RP = D / RG;                             // rows per thread
@@ -102,11 +103,12 @@ __global__ void __launch_bounds__((RecCfg<D, DVT>::NT)) recurrent_kernel(RecArgs
   const In* v = static_cast<const In*>(a.v);
   const int H = a.H;
 
+  // the state streams through once: nontemporal loads and stores
   float4 s[RP];
   if (a.init_state) {
     const float* S0 = a.init_state + static_cast<size_t>(unit) * D * D;
 #pragma unroll
-    for (int p = 0; p < RP; ++p) s[p] = load4(S0 + (g * RP + p) * D + col);
+    for (int p = 0; p < RP; ++p) s[p] = load4_stream(S0 + (g * RP + p) * D + col);
   } else {
 #pragma unroll
     for (int p = 0; p < RP; ++p) s[p] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -186,7 +188,7 @@ __global__ void __launch_bounds__((RecCfg<D, DVT>::NT)) recurrent_kernel(RecArgs
   if (a.final_state) {
     float* S1 = a.final_state + static_cast<size_t>(unit) * D * D;
 #pragma unroll
-    for (int p = 0; p < RP; ++p) *reinterpret_cast<float4*>(S1 + (g * RP + p) * D + col) = s[p];
+    for (int p = 0; p < RP; ++p) store4_stream(S1 + (g * RP + p) * D + col, s[p]);
   }
 }
 
@@ -199,18 +201,21 @@ hipError_t launch_rec(const RecArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Pick the value-column tile: split a unit only when there are too few units
-// to give every CU several workgroups.
+// Pick the value-column tile: split a unit when there are too few units to
+// give every CU several workgroups, or when each unit carries several tokens
+// (per-token reductions then dominate, and half-width tiles halve them).  A
+// single-token unit (decode) keeps whole 64 KiB tiles, which stream best.
 template <typename In>
 hipError_t launch_rec_d(int d, const RecArgs& a, hipStream_t stream) {
   const bool few = a.num_units < 1024;
+  const bool multi = a.cu_seqlens != nullptr || a.T > 1;
   switch (d) {
     case 16: return launch_rec<16, 16, In>(a, stream);
     case 32: return launch_rec<32, 32, In>(a, stream);
     case 64: return few ? launch_rec<64, 32, In>(a, stream) : launch_rec<64, 64, In>(a, stream);
     case 128:
       if (a.num_units < 256) return launch_rec<128, 32, In>(a, stream);
-      return few ? launch_rec<128, 64, In>(a, stream) : launch_rec<128, 128, In>(a, stream);
+      return (few || multi) ? launch_rec<128, 64, In>(a, stream) : launch_rec<128, 128, In>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
