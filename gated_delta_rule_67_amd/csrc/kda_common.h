@@ -79,5 +79,13 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void buffer_store16(f32x4 x, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, static_cast<int>(byte_off), 0, 0);
 }
+// Range-checked loads through the same descriptor: a lane whose access falls
+// outside the range reads zeros.
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(byte_off), 0, 0));
+}
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(byte_off), 0, 0));
+}
 
 }  // namespace kda

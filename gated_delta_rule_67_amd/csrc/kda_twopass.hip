@@ -61,7 +61,7 @@ constexpr int C = 64;        // chunk length
 constexpr int D = 128;       // head dim (dk = dv)
 constexpr int DVT = 32;      // value columns per scan workgroup
 constexpr int NTILE = D / DVT;
-constexpr int NT = 256;      // threads per workgroup (both passes)
+constexpr int NTP = 512;     // threads per prep workgroup: eight waves, two workgroups per CU
 constexpr int LDK = D + 8;   // fp16 row stride of [64][128] LDS arrays
 constexpr int LDX = C + 4;   // fp16 row stride of [128][64] LDS arrays
 constexpr int LDT = C + 8;   // fp16 row stride of the Delta^T tile
@@ -83,7 +83,7 @@ constexpr size_t OFF_KDT = 32768;   // Kd^T        128 x 64  fp16
 constexpr size_t OFF_UP = 49152;    // U  by scan lane: [I][tile][lane][b][e] = U[16I+lc][32tile+16b+4lg+e]
 constexpr size_t OFF_OP = 65536;    // Ou by scan lane: [I][tile][lane][b][e] = Ou[16I+lc][32tile+16b+4lg+e]
 constexpr size_t OFF_GAM = 81920;   // exp(gamma)  [128] fp32
-constexpr size_t OFF_FLAG = 82432;  // per-wave "not on the fast path" [4] int32
+constexpr size_t OFF_FLAG = 82432;  // per prep wave "not on the fast path" [8] bytes, then 8 zero bytes
 constexpr size_t SLOT_BYTES = 82944;
 
 // LDS fragment slots of pass 1 (one f16x4 per lane each).
@@ -193,7 +193,7 @@ __device__ __forceinline__ bool t_column(PrepSmem& sm, f16x4 tbJ, float nscale, 
   return bad;
 }
 
-__global__ void __launch_bounds__(NT, 2) prep_kernel(PrepArgs p) {
+__global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) prep_kernel(PrepArgs p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
 
@@ -219,57 +219,49 @@ __global__ void __launch_bounds__(NT, 2) prep_kernel(PrepArgs p) {
   unsigned char* slot = p.ws + (static_cast<size_t>(cs) * H + h) * SLOT_BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
-  const int oct = lane & 15;  // stage A: channels 8*oct .. 8*oct+7
-  const int qt = lane >> 4;   // stage A: rows 16w + 4qt .. +3
-  const int c8 = 8 * oct;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index 0..7, uniform (SGPR)
+  // stage A: wave w covers block IA = w/2 (rows 16IA .. 16IA+15) and channel
+  // half w%2; lane (oct, qt) = (lane%8, lane/8) owns rows r0 = 16IA+2qt, r0+1
+  // and channels c8 .. c8+7.  The eight lanes of one channel octet sit 8 apart.
+  const int IA = w >> 1;
+  const int oct = lane & 7;
+  const int qt = lane >> 3;
+  const int c8 = 64 * (w & 1) + 8 * oct;
+  const int r0 = 16 * IA + 2 * qt;
   const float lim_lo = __expf(-HALF_SPAN_MAX);
   bool bad = false;
 
-  // ---------------- phase 1: loads and stage A (this thread: 4 rows x 8 channels)
-  float4 g[4][2];
-  uint4 kr[4], qr[4], vr[4];
-  float bt[4];
+  // ---------------- phase 1: loads and stage A (this thread: 2 rows x 8 channels)
+  float4 g[2][2];
+  uint4 kr[2], qr[2], vr[2];
+  float bt[2];
   {
-    const unsigned rs = static_cast<unsigned>(H * D);
+    // range-checked loads over the chunk's nv valid rows: rows past a
+    // document's end read zeros, i.e. identity tokens (k = 0, beta = 0, log_g = 0)
+    const uint32_t rs = static_cast<uint32_t>(H * D);  // row stride, elements
     const size_t base = (tok0 * H + h) * D;
-    const float* gb = p.log_g + base;
-    const bf16_t* kb = p.k + base;
-    const bf16_t* qb = p.q + base;
-    const bf16_t* vb = p.v + base;
-    const float* bb = p.beta + tok0 * H + h;
+    const uint32_t nrow = static_cast<uint32_t>(nv);
+    const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(p.log_g + base, nrow * rs * 4u);
+    const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k + base, nrow * rs * 2u);
+    const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(p.q + base, nrow * rs * 2u);
+    const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v + base, nrow * rs * 2u);
+    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(p.beta + tok0 * H + h, nrow * static_cast<uint32_t>(H) * 4u);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const unsigned row = static_cast<unsigned>(min(16 * w + 4 * qt + j, nv - 1));
-      const unsigned off = row * rs + c8;
-      g[j][0] = *reinterpret_cast<const float4*>(gb + off);
-      g[j][1] = *reinterpret_cast<const float4*>(gb + off + 4u);
-      kr[j] = *reinterpret_cast<const uint4*>(kb + off);
-      qr[j] = *reinterpret_cast<const uint4*>(qb + off);
-      vr[j] = *reinterpret_cast<const uint4*>(vb + off);
-      bt[j] = bb[row * static_cast<unsigned>(H)];
-    }
-  }
-  if (nv < C) {  // workgroup-uniform: rows past the document's end become identity tokens
-    const int nrow = nv - (16 * w + 4 * qt);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool pad = j >= nrow;
-      kr[j].x = pad ? 0u : kr[j].x; kr[j].y = pad ? 0u : kr[j].y;
-      kr[j].z = pad ? 0u : kr[j].z; kr[j].w = pad ? 0u : kr[j].w;
-      qr[j].x = pad ? 0u : qr[j].x; qr[j].y = pad ? 0u : qr[j].y;
-      qr[j].z = pad ? 0u : qr[j].z; qr[j].w = pad ? 0u : qr[j].w;
-      vr[j].x = pad ? 0u : vr[j].x; vr[j].y = pad ? 0u : vr[j].y;
-      vr[j].z = pad ? 0u : vr[j].z; vr[j].w = pad ? 0u : vr[j].w;
-#pragma unroll
-      for (int x = 0; x < 2; ++x) g[j][x] = pad ? make_float4(0.f, 0.f, 0.f, 0.f) : g[j][x];
-      bt[j] = pad ? 0.f : bt[j];
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t row = static_cast<uint32_t>(r0 + j);
+      const uint32_t off = row * rs + static_cast<uint32_t>(c8);
+      g[j][0] = __builtin_bit_cast(float4, buffer_load16(rg, off * 4u));
+      g[j][1] = __builtin_bit_cast(float4, buffer_load16(rg, off * 4u + 16u));
+      kr[j] = buffer_load16(rk, off * 2u);
+      qr[j] = buffer_load16(rq, off * 2u);
+      vr[j] = buffer_load16(rv, off * 2u);
+      bt[j] = buffer_load_f32(rb, row * static_cast<uint32_t>(H) * 4u);
     }
   }
   {
     u16x2 mk = {0, 0}, mv = {0, 0};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
       const uint32_t kw[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
       const uint32_t qw[4] = {qr[j].x, qr[j].y, qr[j].z, qr[j].w};
       const uint32_t vw[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
@@ -283,123 +275,127 @@ __global__ void __launch_bounds__(NT, 2) prep_kernel(PrepArgs p) {
     }
     bad |= mk[0] > QK_MAX_BITS || mk[1] > QK_MAX_BITS || mv[0] > V_MAX_BITS || mv[1] > V_MAX_BITS;
   }
-  f16x8 hl[4], hq[4], hr[4], xv[4];
+  f16x8 hl[2], hr[2], xv[2];  // k exp(G - R), k exp(R' - G), beta v of rows r0, r0+1
   {
-    float tot8[8];
-    f16x8 fdl8, fdr8;
+    const int ldn8 = (lane - 8) & 63, ldn16 = (lane - 16) & 63, ldn32 = (lane - 32) & 63;
+    const int lup8 = (lane + 8) & 63, lup16 = (lane + 16) & 63, lup32 = (lane + 32) & 63;
+    // two passes of four channels keep the live registers down
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      float a[4];
+    for (int hc = 0; hc < 2; ++hc) {
+      float tot4[4];
+      f16x4 fdl4, fdr4, hq4[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 g4 = g[j][c >> 2];
-        const int cc = c & 3;
-        a[j] = exp_fast(cc == 0 ? g4.x : cc == 1 ? g4.y : cc == 2 ? g4.z : g4.w);
+      for (int cc = 0; cc < 4; ++cc) {
+        const int c = 4 * hc + cc;
+        const float4 ga = g[0][hc], gb4 = g[1][hc];
+        const float a0 = exp_fast(cc == 0 ? ga.x : cc == 1 ? ga.y : cc == 2 ? ga.z : ga.w);
+        const float a1 = exp_fast(cc == 0 ? gb4.x : cc == 1 ? gb4.y : cc == 2 ? gb4.z : gb4.w);
+        const float pr = a0 * a1;
+        // inclusive prefix (x) and suffix (y) products over the block's eight row pairs
+        float x = pr, y = pr, t;
+        t = __shfl(x, ldn8, 64);  x = qt >= 1 ? x * t : x;
+        t = __shfl(x, ldn16, 64); x = qt >= 2 ? x * t : x;
+        t = __shfl(x, ldn32, 64); x = qt >= 4 ? x * t : x;
+        t = __shfl(y, lup8, 64);  y = qt <= 6 ? y * t : y;
+        t = __shfl(y, lup16, 64); y = qt <= 5 ? y * t : y;
+        t = __shfl(y, lup32, 64); y = qt <= 3 ? y * t : y;
+        const float xe = __shfl(x, ldn8, 64), ye = __shfl(y, lup8, 64);
+        const float E = qt >= 1 ? xe : 1.f;  // over the row pairs before this lane's
+        const float F = qt <= 6 ? ye : 1.f;  // over the row pairs after it
+        const float dl = __shfl(x, oct + 24, 64);  // over the first half of the block
+        const float dr = __shfl(y, oct + 32, 64);  // over the second half
+        const float Pv[2] = {E * a0, E * pr};
+        const float Sv[2] = {a1 * F, F};
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint32_t kw = c < 2 ? kr[j].x : c < 4 ? kr[j].y : c < 6 ? kr[j].z : kr[j].w;
+          const uint32_t qw = c < 2 ? qr[j].x : c < 4 ? qr[j].y : c < 6 ? qr[j].z : qr[j].w;
+          const uint32_t vw = c < 2 ? vr[j].x : c < 4 ? vr[j].y : c < 6 ? vr[j].z : vr[j].w;
+          const float kv = (c & 1) ? bf16_hi(kw) : bf16_lo(kw);
+          const float qv = (c & 1) ? bf16_hi(qw) : bf16_lo(qw);
+          const float vv = (c & 1) ? bf16_hi(vw) : bf16_lo(vw);
+          hl[j][c] = (f16)(kv * Pv[j]);
+          hq4[j][cc] = (f16)(qv * Pv[j]);
+          hr[j][c] = (f16)(kv * Sv[j]);
+          xv[j][c] = (f16)(bt[j] * vv);
+        }
+        bad |= (dl < lim_lo) | (dr < lim_lo) | (dl != dl) | (dr != dr);
+        tot4[cc] = dl * dr;
+        // the reciprocals only feed fp16 factors: the hardware estimate is enough
+        fdl4[cc] = (f16)__builtin_amdgcn_rcpf(fmaxf(dl, lim_lo));
+        fdr4[cc] = (f16)__builtin_amdgcn_rcpf(fmaxf(dr, lim_lo));
       }
-      const float p1 = a[0] * a[1], p2 = p1 * a[2], p3 = p2 * a[3];  // inside the quarter
-      const float s1 = a[2] * a[3], s0 = a[1] * s1;
-      const float t0 = __shfl(p3, oct, 64), t1 = __shfl(p3, oct + 16, 64);
-      const float t2 = __shfl(p3, oct + 32, 64), t3 = __shfl(p3, oct + 48, 64);
-      // exclusive products over the quarters before / after this lane's
-      const float E = (qt >= 1 ? t0 : 1.f) * (qt >= 2 ? t1 : 1.f) * (qt >= 3 ? t2 : 1.f);
-      const float F = (qt <= 2 ? t3 : 1.f) * (qt <= 1 ? t2 : 1.f) * (qt <= 0 ? t1 : 1.f);
-      const float Pv[4] = {E * a[0], E * p1, E * p2, E * p3};
-      const float Sv[4] = {s0 * F, s1 * F, a[3] * F, F};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t kw = c < 2 ? kr[j].x : c < 4 ? kr[j].y : c < 6 ? kr[j].z : kr[j].w;
-        const uint32_t qw = c < 2 ? qr[j].x : c < 4 ? qr[j].y : c < 6 ? qr[j].z : qr[j].w;
-        const uint32_t vw = c < 2 ? vr[j].x : c < 4 ? vr[j].y : c < 6 ? vr[j].z : vr[j].w;
-        const float kv = (c & 1) ? bf16_hi(kw) : bf16_lo(kw);
-        const float qv = (c & 1) ? bf16_hi(qw) : bf16_lo(qw);
-        const float vv = (c & 1) ? bf16_hi(vw) : bf16_lo(vw);
-        hl[j][c] = (f16)(kv * Pv[j]);
-        hq[j][c] = (f16)(qv * Pv[j]);
-        hr[j][c] = (f16)(kv * Sv[j]);
-        xv[j][c] = (f16)(bt[j] * vv);
+      const int cb = c8 + 4 * hc;
+      if (qt == 0) {
+        *reinterpret_cast<float4*>(&sm.tot[IA][cb]) = make_float4(tot4[0], tot4[1], tot4[2], tot4[3]);
+        *reinterpret_cast<f16x4*>(&sm.fDl[IA][cb]) = fdl4;
+        *reinterpret_cast<f16x4*>(&sm.fDr[IA][cb]) = fdr4;
       }
-      const float dl = t0 * t1, dr = t2 * t3;  // over the first / second half of the block
-      bad |= (dl < lim_lo) | (dr < lim_lo) | (dl != dl) | (dr != dr);
-      tot8[c] = dl * dr;
-      fdl8[c] = (f16)(1.f / fmaxf(dl, lim_lo));
-      fdr8[c] = (f16)(1.f / fmaxf(dr, lim_lo));
-    }
-    // the four quarter lanes of a channel octet write identical values
-    *reinterpret_cast<float4*>(&sm.tot[w][c8]) = make_float4(tot8[0], tot8[1], tot8[2], tot8[3]);
-    *reinterpret_cast<float4*>(&sm.tot[w][c8 + 4]) = make_float4(tot8[4], tot8[5], tot8[6], tot8[7]);
-    *reinterpret_cast<f16x8*>(&sm.fDl[w][c8]) = fdl8;
-    *reinterpret_cast<f16x8*>(&sm.fDr[w][c8]) = fdr8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 16 * w + 4 * qt + j;
-      *reinterpret_cast<f16x8*>(&sm.u.a.Kl[row][c8]) = hl[j];
-      *reinterpret_cast<f16x8*>(&sm.Ql[row][c8]) = hq[j];
-      *reinterpret_cast<f16x8*>(&sm.u.a.Kr[row][c8]) = hr[j];
+      for (int j = 0; j < 2; ++j) *reinterpret_cast<f16x4*>(&sm.Ql[r0 + j][cb]) = hq4[j];
     }
-    if (oct == 0) *reinterpret_cast<float4*>(&sm.beta[16 * w + 4 * qt]) = make_float4(bt[0], bt[1], bt[2], bt[3]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      *reinterpret_cast<f16x8*>(&sm.u.a.Kl[r0 + j][c8]) = hl[j];
+      *reinterpret_cast<f16x8*>(&sm.u.a.Kr[r0 + j][c8]) = hr[j];
+    }
+    if ((w & 1) == 0 && oct == 0) *reinterpret_cast<float2*>(&sm.beta[r0]) = make_float2(bt[0], bt[1]);
   }
   lds_barrier();
 
-  // ---------------- phase 2: decay factors, K exp(gamma - G) out, products
+  // ---------------- phase 2: K exp(gamma - G) out, Xk, products
   {
-    float T[4][8];
-#pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      const float4 a = *reinterpret_cast<const float4*>(&sm.tot[I][c8]);
-      const float4 b = *reinterpret_cast<const float4*>(&sm.tot[I][c8 + 4]);
-      T[I][0] = a.x; T[I][1] = a.y; T[I][2] = a.z; T[I][3] = a.w;
-      T[I][4] = b.x; T[I][5] = b.y; T[I][6] = b.z; T[I][7] = b.w;
-    }
-    float fr[8], gd[8], gam[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float e1 = T[0][c], e2 = e1 * T[1][c], e3 = e2 * T[2][c];
-      fr[c] = w == 0 ? 1.f : w == 1 ? e1 : w == 2 ? e2 : e3;                       // exp(R_w)
-      gd[c] = w == 0 ? T[1][c] * T[2][c] * T[3][c] : w == 1 ? T[2][c] * T[3][c]  // exp(gamma - R_{w+1})
-            : w == 2 ? T[3][c] : 1.f;
-      gam[c] = e3 * T[3][c];
-    }
-    if (w == 0 && qt == 0) {
-      float* gp = reinterpret_cast<float*>(slot + OFF_GAM) + c8;
-      *reinterpret_cast<float4*>(gp) = make_float4(gam[0], gam[1], gam[2], gam[3]);
-      *reinterpret_cast<float4*>(gp + 4) = make_float4(gam[4], gam[5], gam[6], gam[7]);
-    }
     f16* kdt = reinterpret_cast<f16*>(slot + OFF_KDT);
+    // Kd^T[dk][tok] for dk = c8+c, tok = r0, r0+1: row block dk/16, k-step
+    // tok/32 = IA/2, lane (lg = tok%32/8, lc = dk%16), positions tok%8 .. +1
+    const int lgk = 2 * (IA & 1) + (qt >> 2);
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      f16x4 kd;
+    for (int hc = 0; hc < 2; ++hc) {
+      const int cb = c8 + 4 * hc;
+      float4 T[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kd[j] = (f16)((float)hr[j][c] * gd[c]);
-      // Kd^T[dk 8oct+c][tok 16w+4qt+j]: row block dk/16, k-step tok/32,
-      // lane (lg = tok%32/8, lc = dk%16), position 4(qt&1)+j
-      const int dk = c8 + c;
-      const int sl = 16 * (2 * (w & 1) + (qt >> 1)) + (dk & 15);
-      *reinterpret_cast<f16x4*>(kdt + (((dk >> 4) * 2 + (w >> 1)) * 64 + sl) * 8 + 4 * (qt & 1)) = kd;
+      for (int I = 0; I < 4; ++I) T[I] = *reinterpret_cast<const float4*>(&sm.tot[I][cb]);
+      float gam[4];
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int c = 4 * hc + cc;
+        const float t0 = cc == 0 ? T[0].x : cc == 1 ? T[0].y : cc == 2 ? T[0].z : T[0].w;
+        const float t1 = cc == 0 ? T[1].x : cc == 1 ? T[1].y : cc == 2 ? T[1].z : T[1].w;
+        const float t2 = cc == 0 ? T[2].x : cc == 1 ? T[2].y : cc == 2 ? T[2].z : T[2].w;
+        const float t3 = cc == 0 ? T[3].x : cc == 1 ? T[3].y : cc == 2 ? T[3].z : T[3].w;
+        const float e1 = t0, e2 = e1 * t1, e3 = e2 * t2;
+        const float fr = IA == 0 ? 1.f : IA == 1 ? e1 : IA == 2 ? e2 : e3;      // exp(R_IA)
+        const float gd = IA == 0 ? t1 * t2 * t3 : IA == 1 ? t2 * t3             // exp(gamma - R_{IA+1})
+                       : IA == 2 ? t3 : 1.f;
+        gam[cc] = e3 * t3;
+        const int dk = c8 + c;
+        f16x2 kd;
+        kd[0] = (f16)((float)hr[0][c] * gd);
+        kd[1] = (f16)((float)hr[1][c] * gd);
+        *reinterpret_cast<f16x2*>(kdt + (((dk >> 4) * 2 + (IA >> 1)) * 64 + 16 * lgk + (dk & 15)) * 8 + 2 * (qt & 3)) = kd;
+        // Xk = beta k exp(G) = beta Kl exp(R_IA), kept in registers until the
+        // products have released Kl / Kr
+#pragma unroll
+        for (int j = 0; j < 2; ++j) hl[j][c] = (f16)((float)hl[j][c] * bt[j] * fr);
+      }
+      if (IA == 0 && qt == 0)
+        *reinterpret_cast<float4*>(reinterpret_cast<float*>(slot + OFF_GAM) + cb) = make_float4(gam[0], gam[1], gam[2], gam[3]);
     }
-    // Xk = beta k exp(G) = beta Kl exp(R_w), kept in registers until the
-    // products have released Kl / Kr
+    // materialise Xk here: sunk below the products, its factors would stay live there
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) hl[j][c] = (f16)((float)hl[j][c] * bt[j] * fr[c]);
+    for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(hl[j]));
   }
-  f16x4 tbd;  // fragB(T_ww)
-  {
+  f16x4 tbd;  // fragB(T_ww), waves 0-3
+  int item0 = 0, nitem = 0;
+  if (w < 4) {
     // diagonal block I = w of A in both layouts, and its inverse
     const int I = w;
     f32x4 accA = zero4(), accB = zero4();
-    f16x8 l[4], r[4], fl[4], frr[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kc = 32 * ks + 8 * lg;
-      l[ks] = ld8(&sm.u.a.Kl[16 * I + lc][kc]);
-      r[ks] = ld8(&sm.u.a.Kr[16 * I + lc][kc]);
-      fl[ks] = ld8(&sm.fDl[I][kc]);
-      frr[ks] = ld8(&sm.fDr[I][kc]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const f16x8 ls = l[ks] * fl[ks], rs = r[ks] * frr[ks];
+      const f16x8 ls = ld8(&sm.u.a.Kl[16 * I + lc][kc]) * ld8(&sm.fDl[I][kc]);
+      const f16x8 rs = ld8(&sm.u.a.Kr[16 * I + lc][kc]) * ld8(&sm.fDr[I][kc]);
       accA = mfma32(rs, ls, accA);  // fragA: rows 16I+lc, cols 16I+4lg+e
       accB = mfma32(ls, rs, accB);  // fragB: rows 16I+4lg+e, cols 16I+lc
     }
@@ -443,11 +439,16 @@ __global__ void __launch_bounds__(NT, 2) prep_kernel(PrepArgs p) {
     bad |= !(tmax <= F16_SAFE);
     sm.frag[S_TD + I][lane] = h4(ta);
     tbd = h4(tb);
+    item0 = 12 + w;  // one of the last four tiles (Aqk row block 3)
+    nitem = 1;
+  } else {
+    item0 = 3 * (w - 4);  // three of the first twelve tiles
+    nitem = 3;
   }
-  // four of the sixteen remaining tiles: A_IJ (I > J) and Aqk_IJ (J <= I)
+  // the sixteen remaining tiles: A_IJ (I > J) and Aqk_IJ (J <= I)
 #pragma unroll 1
-  for (int m = 0; m < 4; ++m) {
-    const int item = w + 4 * m;
+  for (int m = 0; m < nitem; ++m) {
+    const int item = item0 + m;
     const bool isq = item >= 6;
     int I, J;
     if (!isq) {  // pairs (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
@@ -494,17 +495,14 @@ __global__ void __launch_bounds__(NT, 2) prep_kernel(PrepArgs p) {
   }
   lds_barrier();
 
-  // ---------------- phase 3: Xk^T, Xv^T into LDS; column w of T and of -scale B
+  // ---------------- phase 3: Xk^T, Xv^T into LDS; waves 0-3: column w of T and of -scale B
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    f16x4 xk4, xv4;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      xk4[j] = hl[j][c];
-      xv4[j] = xv[j][c];
-    }
-    *reinterpret_cast<f16x4*>(&sm.u.x.XkT[c8 + c][16 * w + 4 * qt]) = xk4;
-    *reinterpret_cast<f16x4*>(&sm.u.x.XvT[c8 + c][16 * w + 4 * qt]) = xv4;
+    f16x2 xk2, xv2;
+    xk2[0] = hl[0][c]; xk2[1] = hl[1][c];
+    xv2[0] = xv[0][c]; xv2[1] = xv[1][c];
+    *reinterpret_cast<f16x2*>(&sm.u.x.XkT[c8 + c][r0]) = xk2;
+    *reinterpret_cast<f16x2*>(&sm.u.x.XvT[c8 + c][r0]) = xv2;
   }
   {
     const float nscale = -p.scale;
@@ -512,73 +510,73 @@ __global__ void __launch_bounds__(NT, 2) prep_kernel(PrepArgs p) {
       case 0: bad |= t_column<0>(sm, tbd, nscale, lane); break;
       case 1: bad |= t_column<1>(sm, tbd, nscale, lane); break;
       case 2: bad |= t_column<2>(sm, tbd, nscale, lane); break;
-      default: bad |= t_column<3>(sm, tbd, nscale, lane); break;
+      case 3: bad |= t_column<3>(sm, tbd, nscale, lane); break;
+      default: break;
     }
   }
   lds_barrier();
 
-  // ---------------- phase 4: W, U, Q', Ou for value / key columns 32w .. 32w+31
+  // ---------------- phase 4: W, U, Q', Ou for value / key columns 16w .. 16w+15
   {
     f16* nw = reinterpret_cast<f16*>(slot + OFF_NW);
     f16* qp = reinterpret_cast<f16*>(slot + OFF_QP);
     f16* up = reinterpret_cast<f16*>(slot + OFF_UP);
     f16* op = reinterpret_cast<f16*>(slot + OFF_OP);
     float omax = 0.f;
+    const int n = w;
+    f16x4 xk[4], xvv[4];
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn) {
-      const int n = 2 * w + nn;
-      f16x4 xk[4], xvv[4];
+    for (int J = 0; J < 4; ++J) {
+      xk[J] = ld4(&sm.u.x.XkT[16 * n + lc][16 * J + 4 * lg]);
+      xvv[J] = ld4(&sm.u.x.XvT[16 * n + lc][16 * J + 4 * lg]);
+    }
+    // exp(R_I) of columns 16n+4lg .. +3
+    const float4 e0 = *reinterpret_cast<const float4*>(&sm.tot[0][16 * n + 4 * lg]);
+    const float4 e1 = *reinterpret_cast<const float4*>(&sm.tot[1][16 * n + 4 * lg]);
+    const float4 e2 = *reinterpret_cast<const float4*>(&sm.tot[2][16 * n + 4 * lg]);
+    const float R1[4] = {e0.x, e0.y, e0.z, e0.w};
+    const float R2[4] = {R1[0] * e1.x, R1[1] * e1.y, R1[2] * e1.z, R1[3] * e1.w};
+    const float R3[4] = {R2[0] * e2.x, R2[1] * e2.y, R2[2] * e2.z, R2[3] * e2.w};
 #pragma unroll
-      for (int J = 0; J < 4; ++J) {
-        xk[J] = ld4(&sm.u.x.XkT[16 * n + lc][16 * J + 4 * lg]);
-        xvv[J] = ld4(&sm.u.x.XvT[16 * n + lc][16 * J + 4 * lg]);
+    for (int I = 0; I < 4; ++I) {
+      f32x4 aW = zero4(), aU = zero4(), aQ, aO = zero4();
+      const f16x4 ql = ld4(&sm.Ql[16 * I + lc][16 * n + 4 * lg]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float rI = I == 0 ? 1.f : I == 1 ? R1[e] : I == 2 ? R2[e] : R3[e];
+        aQ[e] = p.scale * (float)ql[e] * rI;
       }
-      // exp(R_I) of columns 16n+4lg .. +3
-      const float4 e0 = *reinterpret_cast<const float4*>(&sm.tot[0][16 * n + 4 * lg]);
-      const float4 e1 = *reinterpret_cast<const float4*>(&sm.tot[1][16 * n + 4 * lg]);
-      const float4 e2 = *reinterpret_cast<const float4*>(&sm.tot[2][16 * n + 4 * lg]);
-      const float R1[4] = {e0.x, e0.y, e0.z, e0.w};
-      const float R2[4] = {R1[0] * e1.x, R1[1] * e1.y, R1[2] * e1.z, R1[3] * e1.w};
-      const float R3[4] = {R2[0] * e2.x, R2[1] * e2.y, R2[2] * e2.z, R2[3] * e2.w};
 #pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        f32x4 aW = zero4(), aU = zero4(), aQ, aO = zero4();
-        const f16x4 ql = ld4(&sm.Ql[16 * I + lc][16 * n + 4 * lg]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float rI = I == 0 ? 1.f : I == 1 ? R1[e] : I == 2 ? R2[e] : R3[e];
-          aQ[e] = p.scale * (float)ql[e] * rI;
-        }
-#pragma unroll
-        for (int J = 0; J <= I; ++J) {
-          const f16x4 tf = I == J ? sm.frag[S_TD + I][lane] : sm.frag[S_TO + pair6(I, J)][lane];
-          const f16x4 bf = sm.frag[S_BS + tile10(I, J)][lane];
-          aW = mfma16(xk[J], tf, aW);   // W^T     [col 4lg+e][tok lc]
-          aU = mfma16(xvv[J], tf, aU);  // U^T     [col 4lg+e][tok lc]
-          aQ = mfma16(xk[J], bf, aQ);   // Q'^T    [col 4lg+e][tok lc]
-          aO = mfma16(xvv[J], bf, aO);  // -Ou^T   [col 4lg+e][tok lc]
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          omax = fmaxf(omax, fmaxf(fmaxf(fabsf(aW[e]), fabsf(aU[e])), fmaxf(fabsf(aQ[e]), fabsf(aO[e]))));
-          aW[e] = -aW[e];
-          aO[e] = -aO[e];
-        }
-        // X[tok 16I+lc][col 16n+4lg+e]: block I, k-step n/2, lane
-        // (lg' = 2(n&1) + lg/2, lc), position 4(lg&1)+e
-        const int rowoff = ((I * 4 + (n >> 1)) * 64 + 16 * (2 * (n & 1) + (lg >> 1)) + lc) * 8 + 4 * (lg & 1);
-        *reinterpret_cast<f16x4*>(nw + rowoff) = h4(aW);
-        *reinterpret_cast<f16x4*>(qp + rowoff) = h4(aQ);
-        // U and Ou in the order one scan lane consumes them (same lane here)
-        const int laneoff = ((I * NTILE + (n >> 1)) * 64 + lane) * 8 + 4 * (n & 1);
-        *reinterpret_cast<f16x4*>(up + laneoff) = h4(aU);
-        *reinterpret_cast<f16x4*>(op + laneoff) = h4(aO);
+      for (int J = 0; J <= I; ++J) {
+        const f16x4 tf = I == J ? sm.frag[S_TD + I][lane] : sm.frag[S_TO + pair6(I, J)][lane];
+        const f16x4 bf = sm.frag[S_BS + tile10(I, J)][lane];
+        aW = mfma16(xk[J], tf, aW);   // W^T     [col 4lg+e][tok lc]
+        aU = mfma16(xvv[J], tf, aU);  // U^T     [col 4lg+e][tok lc]
+        aQ = mfma16(xk[J], bf, aQ);   // Q'^T    [col 4lg+e][tok lc]
+        aO = mfma16(xvv[J], bf, aO);  // -Ou^T   [col 4lg+e][tok lc]
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        omax = fmaxf(omax, fmaxf(fmaxf(fabsf(aW[e]), fabsf(aU[e])), fmaxf(fabsf(aQ[e]), fabsf(aO[e]))));
+        aW[e] = -aW[e];
+        aO[e] = -aO[e];
+      }
+      // X[tok 16I+lc][col 16n+4lg+e]: block I, k-step n/2, lane
+      // (lg' = 2(n&1) + lg/2, lc), position 4(lg&1)+e
+      const int rowoff = ((I * 4 + (n >> 1)) * 64 + 16 * (2 * (n & 1) + (lg >> 1)) + lc) * 8 + 4 * (lg & 1);
+      *reinterpret_cast<f16x4*>(nw + rowoff) = h4(aW);
+      *reinterpret_cast<f16x4*>(qp + rowoff) = h4(aQ);
+      // U and Ou in the order one scan lane consumes them (same lane here)
+      const int laneoff = ((I * NTILE + (n >> 1)) * 64 + lane) * 8 + 4 * (n & 1);
+      *reinterpret_cast<f16x4*>(up + laneoff) = h4(aU);
+      *reinterpret_cast<f16x4*>(op + laneoff) = h4(aO);
     }
     bad |= !(omax <= F16_SAFE);
   }
+  // one "not on the fast path" byte per wave; bytes 8..15 of the flag word are zero
   const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
-  if (lane == 0) reinterpret_cast<int*>(slot + OFF_FLAG)[w] = any ? 1 : 0;
+  if (lane == 0) slot[OFF_FLAG + w] = any ? 1 : 0;
+  if (w == 0 && lane == 1) *reinterpret_cast<uint2*>(slot + OFF_FLAG + 8) = make_uint2(0u, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -945,17 +943,31 @@ bool twopass_supported(const ChunkLaunch& a) {
   return a.bf16 && a.d == D && blocks < (int64_t(1) << 31);
 }
 
+// The kernels' LDS limits are raised once per device (the attribute is per
+// device).
+static hipError_t prepare_device() {
+  constexpr int MAX_DEV = 64;
+  static bool ready[MAX_DEV] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+  if (!ready[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(sizeof(PrepSmem)));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(sizeof(ScanSmem)));
+    if (e != hipSuccess) return e;
+    ready[dev] = true;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(sizeof(PrepSmem)));
+  {
+    const hipError_t e = prepare_device();
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sizeof(ScanSmem)));
-    if (e != hipSuccess) return e;
-    attr_set = true;
   }
   const bool packed = a.cu_seqlens != nullptr;
   const WsLayout l = ws_layout(a.workspace, a.num_seqs, a.seq_len, a.num_heads, packed);
@@ -986,7 +998,7 @@ hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream) {
     pp.H = a.num_heads;
     pp.nchd = nchd;
     pp.scale = a.scale;
-    hipLaunchKernelGGL(prep_kernel, dim3(static_cast<unsigned>(ns * a.num_heads)), dim3(NT), sizeof(PrepSmem),
+    hipLaunchKernelGGL(prep_kernel, dim3(static_cast<unsigned>(ns * a.num_heads)), dim3(NTP), sizeof(PrepSmem),
                        stream, pp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
