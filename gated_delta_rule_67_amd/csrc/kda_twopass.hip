@@ -83,7 +83,7 @@ constexpr size_t OFF_KDT = 32768;   // Kd^T        128 x 64  fp16
 constexpr size_t OFF_UP = 49152;    // U  by scan lane: [I][tile][lane][b][e] = U[16I+lc][32tile+16b+4lg+e]
 constexpr size_t OFF_OP = 65536;    // Ou by scan lane: [I][tile][lane][b][e] = Ou[16I+lc][32tile+16b+4lg+e]
 constexpr size_t OFF_GAM = 81920;   // exp(gamma)  [128] fp32
-constexpr size_t OFF_FLAG = 82432;  // per prep wave "not on the fast path" [8] bytes, then 8 zero bytes
+constexpr size_t OFF_FLAG = 82432;  // per prep wave "not on the fast path" [8] bytes
 constexpr size_t SLOT_BYTES = 82944;
 
 // LDS fragment slots of pass 1 (one f16x4 per lane each).
@@ -573,10 +573,9 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
     }
     bad |= !(omax <= F16_SAFE);
   }
-  // one "not on the fast path" byte per wave; bytes 8..15 of the flag word are zero
+  // one "not on the fast path" byte per wave
   const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
   if (lane == 0) slot[OFF_FLAG + w] = any ? 1 : 0;
-  if (w == 0 && lane == 1) *reinterpret_cast<uint2*>(slot + OFF_FLAG + 8) = make_uint2(0u, 0u);
 }
 
 // ---------------------------------------------------------------------------
@@ -624,7 +623,7 @@ struct Pre {
   f16x8 kd[2];      // Kd^T row 16w+lc, tokens 32ks+8lg ..
   f16x8 uo;         // U / Ou of this lane, [b][e]
   float4 gam;       // exp(gamma) of key rows 16w+4lg ..
-  int4 flag;
+  int2 flag;        // the eight per-wave bytes of the prep kernel
 };
 
 struct State2 {
@@ -680,7 +679,7 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
   // Loads of chunk k's operands, in three groups: the flag (used first), the
   // Delta / output operands (phase A) and the state-update operands (phase B).
   auto slot_of = [&](int k) { return slot0 + static_cast<size_t>(k) * slot_stride; };
-  auto load_flag = [&](int k, Pre& r) { r.flag = *reinterpret_cast<const int4*>(slot_of(k) + OFF_FLAG); };
+  auto load_flag = [&](int k, Pre& r) { r.flag = *reinterpret_cast<const int2*>(slot_of(k) + OFF_FLAG); };
   auto load_a = [&](int k, Pre& r) {
     const unsigned char* sl = slot_of(k);
     const f16* mp = reinterpret_cast<const f16*>(sl + (is_o ? OFF_QP : OFF_NW)) + (I * 4 * 64 + lane) * 8;
@@ -734,7 +733,7 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
     const size_t tok0 = tok_begin + static_cast<size_t>(k) * C;
     const int nv = min(C, ntok - k * C);
     lds_barrier();  // ST of the entry state is complete
-    const int pflag = __builtin_amdgcn_readfirstlane(cur.flag.x | cur.flag.y | cur.flag.z | cur.flag.w);
+    const int pflag = __builtin_amdgcn_readfirstlane(cur.flag.x | cur.flag.y);
     // the load groups stay in program order (flag, phase A, phase B operands,
     // chunk after chunk), so the wait before each use counts exactly the
     // loads issued after it
