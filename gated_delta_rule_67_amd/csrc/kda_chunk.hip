@@ -38,7 +38,8 @@
 // whose diagonal blocks of A exceed 1 in magnitude, is evaluated token by
 // token (exact fp32) inside this kernel instead.
 //
-// Arithmetic: fp16 MFMA operands (bf16 q/k/v convert exactly), fp32
+// Arithmetic: fp16 MFMA operands (formed in fp32 from the bf16 inputs,
+// rounded once, kept inside fp16's range by the guard), fp32
 // accumulation, state and outputs.  With L a strictly lower 16x16 diagonal
 // block of A (|L| <= 1, L^16 = 0), (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8)
 // is formed with 16x16x16 MFMAs.  Products whose result feeds another MFMA

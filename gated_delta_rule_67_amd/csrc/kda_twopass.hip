@@ -19,10 +19,10 @@
 // slot.  Pass 2 (scan_kernel) is the only serial part: per (unit, 32-column
 // value tile) it walks the unit's chunks with the fp32 state in MFMA
 // accumulators, three 64x128x32-class products per chunk (W S and Q' S share
-// the state operand; K^T Delta updates the state), with the slot operands
-// of the next two chunks in flight while one chunk is processed.  Its eight waves split the roles: four form
-// Delta (the serial chain), four form the outputs, all eight update 16 state
-// rows each.
+// the state operand; K^T Delta updates the state), with the slot operands of
+// the next two chunks in flight while one chunk is processed.  Its eight
+// waves split the roles: four form Delta (the serial chain), four form the
+// outputs, all eight update 16 state rows each.
 //
 // Decay factors without overflow (pass 1).  The chunk is cut into four
 // 16-token blocks.  With R_I = G before block I's first token:
@@ -40,7 +40,8 @@
 // magnitude, any fp16 intermediate (T, B, W, U, Q', Ou, Delta) would exceed
 // F16_SAFE, or the entry state exceeds S_MAX.
 //
-// Arithmetic: fp16 MFMA operands (bf16 q/k/v convert exactly), fp32
+// Arithmetic: fp16 MFMA operands (formed in fp32 from the bf16 inputs and
+// rounded once; the guard keeps them inside fp16's range), fp32
 // accumulation, state and outputs.  With L a strictly lower 16x16 diagonal
 // block of A (L^16 = 0), (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8); the
 // off-diagonal blocks of T follow by block forward substitution,
