@@ -1,0 +1,83 @@
+"""Host-side checks of bench.py's contract (no GPU needed).
+
+The algorithmic byte and FLOP counts are the fixed per-unit figures of the
+measurement plan: 1796 B per token-head for prefill (q, k, v bf16, log_g and
+out fp32, beta), plus the initial and final state once per unit; two state
+passes per unit plus 1796 B per row for kda_step; 5*2*C*d + 3*2*d*d FLOP per
+token-head for the chunked form.
+"""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_prefill_bytes_and_flops_of_the_dense_workload():
+    tokens, H, d = 4 * 4096, 16, 128
+    # 16384 tokens x 16 heads x 1796 B + 2 x 4 sequences x 16 heads x 64 KiB
+    assert bench.prefill_bytes(tokens, H, d, n_states=4) == 16384 * 16 * 1796 + 2 * 4 * 16 * 65536
+    assert bench.prefill_bytes(tokens, H, d, n_states=4) == 479_199_232
+    assert bench.prefill_flops(tokens, H, d) == 16384 * 16 * 180_224 == 47_244_640_256
+
+
+def test_step_bytes_of_decode_and_verify():
+    # 2 x 64 KiB of state per unit plus one 1796-byte row per token-head
+    assert bench.step_bytes(256, 1, 32, 128) == 256 * 32 * (2 * 65536 + 1796) == 1_088_454_656
+    assert bench.step_bytes(64, 4, 32, 128) == 64 * 32 * (2 * 65536 + 4 * 1796) == 283_148_288
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in r.stderr
+    assert r.stdout.strip() == ""  # no JSON line
+
+
+def _write_counter_csv(dirname, counter, rows):
+    os.makedirs(dirname, exist_ok=True)
+    with open(os.path.join(dirname, "run_counter_collection.csv"), "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Dispatch_Id", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for name, disp, val in rows:
+            w.writerow({"Kernel_Name": name, "Dispatch_Id": disp, "Counter_Name": counter, "Counter_Value": val})
+
+
+def test_traffic_is_scaled_by_the_copy_calibration(tmp_path):
+    kib = bench.COPY_BYTES / 1024.0
+    # the copy's FETCH_SIZE reads half its bytes, WRITE_SIZE all of them
+    _write_counter_csv(tmp_path / "cf", "FETCH_SIZE", [("copy_kernel", 1, kib / 2), ("tiny", 2, 1.0)])
+    _write_counter_csv(tmp_path / "cw", "WRITE_SIZE", [("copy_kernel", 1, kib)])
+    # two dispatches of each prefill kernel: the mean per dispatch is used
+    _write_counter_csv(tmp_path / "pf", "FETCH_SIZE", [("prep_kernel(x)", 1, 100.0), ("prep_kernel(x)", 3, 300.0),
+                                                       ("scan_kernel(y)", 2, 50.0), ("scan_kernel(y)", 4, 50.0)])
+    _write_counter_csv(tmp_path / "pw", "WRITE_SIZE", [("prep_kernel(x)", 1, 10.0), ("prep_kernel(x)", 3, 10.0),
+                                                       ("scan_kernel(y)", 2, 20.0), ("scan_kernel(y)", 4, 20.0)])
+    lines = bench.write_traffic(str(tmp_path / "pf"), str(tmp_path / "pw"), str(tmp_path / "cf"), str(tmp_path / "cw"))
+    kv = dict(l.split(": ", 1) for l in lines)
+    assert float(kv["fetch_scale"]) == pytest.approx(2.0, rel=1e-4)
+    assert float(kv["write_scale"]) == pytest.approx(1.0, rel=1e-4)
+    prep = (200.0 * 2.0 + 10.0) * 1024
+    scan = (50.0 * 2.0 + 20.0) * 1024
+    assert int(kv["prep_kernel_bytes"]) == round(prep)
+    assert int(kv["scan_kernel_bytes"]) == round(scan)
+    assert int(kv["traffic_bytes_per_call"]) == round(prep + scan)
+    assert kv["sources_sha256"] == bench.sources_hash()
+
+
+def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.txt"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    f.write_text(f"# comment\nsources_sha256: {bench.sources_hash()}\ntraffic_bytes_per_call: 123456\n")
+    assert bench.read_traffic() == 123456
+    f.write_text("sources_sha256: 0000000000000000\ntraffic_bytes_per_call: 123456\n")
+    assert bench.read_traffic() is None
+    f.unlink()
+    assert bench.read_traffic() is None
