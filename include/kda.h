@@ -95,8 +95,10 @@ const char* kda_last_error(void);
  * prefill stages fp16 per-chunk operands there: about 81 KiB per 64-token
  * chunk and head (dense: B * ceil(T/64) chunks; packed: ceil(T/64) + N, an
  * upper bound), plus a few bytes per document when packed.  Other
- * configurations need none (0; desc->workspace may then be NULL).  The
- * workspace is scratch: its contents on entry do not matter and are
+ * configurations need at most a few bytes per document (0 for a dense
+ * batch; desc->workspace may then be NULL).  The figure is for the
+ * evaluation path in force when it is queried (see KDA_PREFILL_PATH below).
+ * The workspace is scratch: its contents on entry do not matter and are
  * clobbered.  Returns 0 for a NULL or invalid descriptor. */
 size_t kda_chunk_workspace_bytes(const kda_desc* desc, int packed);
 
@@ -115,6 +117,14 @@ size_t kda_chunk_workspace_bytes(const kda_desc* desc, int packed);
  * Evaluated in chunks of 64 tokens (within a document) with fp32 state and fp32
  * accumulation; out must not alias any input.  Zero-length documents are
  * allowed (their final state is their initial state).
+ *
+ * Evaluation path: bf16 q/k/v with d = 128 take the two-pass chunked kernels
+ * (per-chunk operands staged in the workspace); other inputs take the
+ * token-recurrent kernel.  The environment variable KDA_PREFILL_PATH, read at
+ * every call, overrides this for testing: "fused" selects the single-pass
+ * chunked kernel (bf16, d = 128; a few workspace bytes per document), and
+ * "recurrent" the token-recurrent kernel.  A workspace smaller than the
+ * selected path needs returns KDA_ERR_WORKSPACE before anything is enqueued.
  */
 kda_status kda_chunk_fwd(const kda_desc* desc, const void* q, const void* k,
                          const void* v, const float* log_g, const float* beta,
