@@ -940,7 +940,10 @@ size_t twopass_workspace_bytes(int num_seqs, int seq_len, int num_heads, bool pa
 
 bool twopass_supported(const ChunkLaunch& a) {
   const int64_t blocks = n_slots_of(a.num_seqs, a.seq_len, a.cu_seqlens != nullptr) * a.num_heads;
-  return a.bf16 && a.d == D && blocks < (int64_t(1) << 31);
+  // the prep kernel's range-checked loads span one chunk's rows of log_g in
+  // 32-bit byte offsets: C * H * D * 4 bytes
+  const bool offsets_fit = int64_t(C) * a.num_heads * D * 4 <= int64_t(UINT32_MAX);
+  return a.bf16 && a.d == D && blocks < (int64_t(1) << 31) && offsets_fit;
 }
 
 // The kernels' LDS limits are raised once per device (the attribute is per
