@@ -120,6 +120,26 @@ def test_packed_edge_lengths(dtype):
     assert torch.equal(fin_dev[0].cpu(), s0[0]) and torch.equal(fin_dev[5].cpu(), s0[5])
 
 
+def test_long_single_document():
+    """One document of 257 chunks with a ragged tail: the scan's long serial walk."""
+    lens = [256 * 64 + 37]
+    inp = kda_inputs.make_inputs(B=1, T=sum(lens), H=2, dk=128, dv=128, dtype="bf16", seed=22,
+                                 lengths=lens, init="normal", init_std=0.05)
+    check_full(inp, "packed one long document")
+
+
+def test_more_documents_than_the_ordering_covers():
+    """5000 short documents (0 to 40 tokens): packed problems past 4096 documents are
+    scanned in their given order, and the chunk map walks the documents in
+    several blocks of 1024."""
+    rng = np.random.default_rng(23)
+    lens = [int(x) for x in rng.integers(0, 41, size=5000)]
+    lens[0], lens[1] = 0, 1
+    inp = kda_inputs.make_inputs(B=1, T=sum(lens), H=2, dk=128, dv=128, dtype="bf16", seed=24,
+                                 lengths=lens, init="normal", init_std=0.05)
+    check_full(inp, "packed 5000 short documents")
+
+
 def test_packed_zero_initial_state():
     lens = [100, 28, 256, 1]
     inp = kda_inputs.make_inputs(B=1, T=sum(lens), H=2, dk=128, dv=128, dtype="bf16", seed=21,
