@@ -12,6 +12,8 @@ fp32 out, with inputs resident in HBM.  ``value`` is prefill tokens/s
                 (HIP events on the launch stream) against 8 TB/s HBM
   mfma          algorithmic prefill FLOP/s against the 2516.6 TFLOP/s dense
                 16-bit MFMA peak
+  varlen        the packed 65536-token, 32-head prefill: tokens/s and its own
+                HBM roofline (beside the headline, not part of it)
   decode/verify kda_step GB/s on 256 x 1 and 64 x 4 rows, H=32, d=128, each
                 with its own roofline (state read + write + row traffic)
   cpu_baseline  the fp64 oracle timed on the host on a bounded sample of the
@@ -173,6 +175,34 @@ def bench_prefill(kda, steps, warmup):
                 bytes=prefill_bytes(tokens, H, D, n_states=B), flops=prefill_flops(tokens, H, D))
 
 
+def bench_varlen(kda, steps, warmup):
+    """The packed workload: 65536 tokens split into documents of log-uniform
+    length, H=32, d=128, bf16, zero initial states; timed like the dense
+    prefill (back-to-back calls, HIP events per call).  Reported beside the
+    headline, not as it."""
+    inp = kda_inputs.config("varlen")
+    d = to_dev(inp)
+    B, T, H, D = inp["q"].shape
+    N = d["cu_seqlens"].numel() - 1
+    out = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
+    fin = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+
+    def call():
+        kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_g"], d["beta"], cu_seqlens=d["cu_seqlens"],
+                      out=out, final_state=fin)
+
+    wall, ms = timed_calls(call, steps, warmup)
+    avg = float(np.mean(ms))
+    nbytes = prefill_bytes(T, H, D, n_states=0) + N * H * D * D * 4  # final states only (zero initial)
+    gbs = nbytes / (avg * 1e-3) / 1e9
+    return {"workload": f"packed varlen prefill, 1 x {T} tokens in {N} documents (log-uniform 64..16384), "
+                        f"H={H}, dk=dv={D}, bf16 q/k/v, zero initial states",
+            "tokens_per_s": round(T / (wall / steps), 1), "us_per_call": round(avg * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+            "algorithmic_bytes": nbytes}
+
+
 def bench_step(kda, name, steps, warmup):
     """kda_step timed per call with HIP events; before every call a 1 GiB
     buffer is read (clean lines, nothing to write back) so the state (128 MiB
@@ -251,7 +281,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "step", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "varlen", "step", "copy"], default="all",
                     help="restrict the run (profiling); the JSON line needs 'all'")
     ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
                     help="rocprofv3 csv dirs: prefill FETCH_SIZE, prefill WRITE_SIZE, copy FETCH_SIZE, "
@@ -287,6 +317,9 @@ def main():
     if args.only in ("all", "prefill"):
         res["prefill"] = bench_prefill(kda, args.steps, args.warmup)
         print(f"prefill: mean {np.mean(res['prefill']['ms']) * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+    if args.only in ("all", "varlen"):
+        res["varlen"] = bench_varlen(kda, args.steps, args.warmup)
+        print(f"varlen prefill: {res['varlen']['us_per_call']} us/call", file=sys.stderr, flush=True)
     if args.only in ("all", "step"):
         res["decode"] = bench_step(kda, "decode", args.steps, args.warmup)
         res["verify"] = bench_step(kda, "verify", args.steps, args.warmup)
@@ -324,6 +357,7 @@ def main():
         "algorithmic_bytes_per_launch": p["bytes"],
         "mfma": {"achieved_TFLOPs": round(tflops, 2), "peak_TFLOPs": MFMA_PEAK_TFLOPS,
                  "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "algorithmic_flop_per_launch": p["flops"]},
+        "varlen": res["varlen"],
         "decode": res["decode"],
         "verify": res["verify"],
     }
