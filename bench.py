@@ -18,6 +18,9 @@ fp32 out, with inputs resident in HBM.  ``value`` is prefill tokens/s
                 with its own roofline (state read + write + row traffic)
   cpu_baseline  the fp64 oracle timed on the host on a bounded sample of the
                 same prefill workload
+Every timed region follows SETTLE_S seconds of the same workload run back to
+back (untimed), then the W warm-up steps: the GPU's clocks need some 30 ms
+of sustained load to reach their steady state.
 Only one GPU is used; --gpus above 1 exits with a message.
 
 roofline.traffic is the HBM bytes of one prefill call measured with rocprofv3
@@ -135,9 +138,27 @@ def step_bytes(N: int, n_tok: int, H: int, d: int, qkv_bytes=2) -> int:
     return N * H * 2 * d * d * 4 + N * n_tok * H * per_token_head
 
 
+SETTLE_S = 0.2  # untimed sustained load before the warm-up steps
+
+
+def settle(fn, seconds: float = SETTLE_S):
+    """Run fn back to back for about ``seconds`` (untimed).  Under sustained
+    load the GPU's clocks take some 30 ms to reach their steady state (the
+    dense prefill runs at about 310 us per call for its first 20 calls and
+    270 us from the 100th on; one idle second undoes it), so every timed
+    region starts from that steady state."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def timed_calls(fn, steps: int, warmup: int):
-    """Run fn warmup times, then steps times bracketed by synchronisation.
-    Returns (wall seconds of the timed region, per-call event milliseconds)."""
+    """Settle, run fn warmup times, then steps times bracketed by
+    synchronisation.  Returns (wall seconds of the timed region, per-call
+    event milliseconds)."""
+    settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -219,6 +240,11 @@ def bench_step(kda, name, steps, warmup):
     def call():
         kda.step(d["q"], d["k"], d["v"], d["log_g"], d["beta"], state, out=out)
 
+    def flushed_call():
+        torch.sum(flush, dim=0, out=sink)
+        call()
+
+    settle(flushed_call)
     for _ in range(warmup):
         call()
     stream = torch.cuda.current_stream()
