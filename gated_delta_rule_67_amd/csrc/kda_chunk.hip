@@ -664,13 +664,19 @@ size_t chunk_workspace_bytes(int n_docs, bool packed) {
 bool chunk_mfma_supported(const ChunkLaunch& a) { return a.bf16 && a.d == D; }
 
 hipError_t launch_chunk_mfma(const ChunkLaunch& a, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_kernel),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(sizeof(Smem)));
+  {  // the kernel's LDS limit is raised once per device (the attribute is per device)
+    constexpr int MAX_DEV = 64;
+    static bool ready[MAX_DEV] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
+    if (!ready[dev]) {
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(chunk_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(sizeof(Smem)));
+      if (e != hipSuccess) return e;
+      ready[dev] = true;
+    }
   }
   ChunkArgs p{};
   p.q = static_cast<const bf16_t*>(a.q);
