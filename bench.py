@@ -285,10 +285,37 @@ def cpu_baseline(inp, target_s=10.0):
         elapsed += time.perf_counter() - t0
         reps += 1
     token_heads = reps * B * T * H
-    return {"value": round(reps * B * T / elapsed, 1), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"the whole workload ({B} x {T} tokens x {H} heads, fp64 token loop) run {reps} times "
-                      f"back to back, {token_heads} token-heads in {elapsed:.1f} s on {threads} threads"}
+    res = {"value": round(reps * B * T / elapsed, 1), "unit": "tokens/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"the whole workload ({B} x {T} tokens x {H} heads, fp64 token loop) run {reps} times "
+                     f"back to back, {token_heads} token-heads in {elapsed:.1f} s on {threads} threads",
+           "host_cpu": host_cpu_model()}
+    # single-thread oracle on the small workloads (the whole of each, once)
+    single = {}
+    for name in ("tiny", "decode", "verify"):
+        wi = kda_inputs.config(name)
+        Nw, n_tok, Hw, Dw = wi["q"].shape
+        st = to_f64(wi["init_state"]) if wi["init_state"] is not None else None
+        t0 = time.perf_counter()
+        oracle.kda_forward(to_f64(wi["q"]), to_f64(wi["k"]), to_f64(wi["v"]), to_f64(wi["log_g"]),
+                           to_f64(wi["beta"]), init_state=st, scale=wi["scale"], n_threads=1)
+        dt = time.perf_counter() - t0
+        if name == "tiny":
+            single[name] = {"tokens_per_s": round(Nw * n_tok / dt, 1)}
+        else:
+            single[name] = {"GB_per_s": round(step_bytes(Nw, n_tok, Hw, Dw) / dt / 1e9, 3)}
+    res["single_thread"] = single
+    return res
+
+
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def bench_copy(steps, warmup):
