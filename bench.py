@@ -14,6 +14,8 @@ fp32 out, with inputs resident in HBM.  ``value`` is prefill tokens/s
                 16-bit MFMA peak
   varlen        the packed 65536-token, 32-head prefill: tokens/s and its own
                 HBM roofline (beside the headline, not part of it)
+  verify_rollback  the 64 x 4-row verify split into kda_step_rows (state read
+                only) and kda_step_commit, each with its own HBM roofline
   decode/verify kda_step GB/s on 256 x 1 and 64 x 4 rows, H=32, d=128, each
                 with its own roofline (state read + write + row traffic)
   cpu_baseline  the fp64 oracle timed on the host on a bounded sample of the
@@ -268,6 +270,70 @@ def bench_step(kda, name, steps, warmup):
             "algorithmic_bytes": nbytes}
 
 
+def rows_bytes(N: int, n_tok: int, H: int, d: int, qkv_bytes=2) -> int:
+    """kda_step_rows: the state read once (not written), each row in, its
+    output and delta out."""
+    per_row_head = 3 * d * qkv_bytes + d * 4 + 4 + d * 4 + d * 4
+    return N * H * d * d * 4 + N * n_tok * H * per_row_head
+
+
+def commit_bytes(N: int, n_tok: int, H: int, d: int, qkv_bytes=2) -> int:
+    """kda_step_commit of every row: the state read and written, each row's
+    k, log_g and delta read, the accept counts."""
+    return N * H * 2 * d * d * 4 + N * n_tok * H * (d * qkv_bytes + d * 4 + d * 4) + N * 4
+
+
+def bench_verify_commit(kda, steps, warmup):
+    """Speculative verify on the verify workload: kda_step_rows (state read
+    only) then kda_step_commit of all rows, each timed with HIP events after a
+    1 GiB read, like bench_step."""
+    inp = kda_inputs.config("verify")
+    d = to_dev(inp)
+    N, n_tok, H, D = inp["q"].shape
+    state = d["init_state"].clone()
+    out = torch.empty((N, n_tok, H, D), dtype=torch.float32, device="cuda")
+    deltas = torch.empty((N, n_tok, H, D), dtype=torch.float32, device="cuda")
+    accept = torch.full((N,), n_tok, dtype=torch.int32, device="cuda")
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def rows():
+        kda.step_rows(d["q"], d["k"], d["v"], d["log_g"], d["beta"], state, out=out, deltas=deltas)
+
+    def commit():
+        kda.step_commit(d["k"], d["log_g"], deltas, state, accept)
+
+    def both():
+        torch.sum(flush, dim=0, out=sink)
+        rows()
+        torch.sum(flush, dim=0, out=sink)
+        commit()
+
+    settle(both)
+    for _ in range(warmup):
+        both()
+    stream = torch.cuda.current_stream()
+    t_rows, t_commit = [], []
+    for _ in range(steps):
+        for fn, acc in ((rows, t_rows), (commit, t_commit)):
+            torch.sum(flush, dim=0, out=sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            acc.append(a.elapsed_time(b))
+    r_us, c_us = float(np.mean(t_rows)) * 1e3, float(np.mean(t_commit)) * 1e3
+    rb, cb = rows_bytes(N, n_tok, H, D), commit_bytes(N, n_tok, H, D)
+    r_gbs, c_gbs = rb / (r_us * 1e-6) / 1e9, cb / (c_us * 1e-6) / 1e9
+    roof = lambda g: {"bound": "hbm", "achieved": round(g, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(g / HBM_PEAK_GBS, 4), "traffic": None}
+    return {"workload": f"{N} sequences x {n_tok} draft rows, H={H}, dk=dv={D}, bf16 q/k/v: rows scored with the "
+                        "state read only, then every row committed (caches flushed before each call)",
+            "rows": {"us_per_call": round(r_us, 2), "algorithmic_bytes": rb, "roofline": roof(r_gbs)},
+            "commit": {"us_per_call": round(c_us, 2), "algorithmic_bytes": cb, "roofline": roof(c_gbs)}}
+
+
 def cpu_baseline(inp, target_s=10.0):
     """Time the fp64 oracle on a bounded sample of the prefill workload: the
     whole workload (all sequences and heads, OpenMP over the units), repeated
@@ -376,7 +442,10 @@ def main():
     if args.only in ("all", "step"):
         res["decode"] = bench_step(kda, "decode", args.steps, args.warmup)
         res["verify"] = bench_step(kda, "verify", args.steps, args.warmup)
-        print(f"decode {res['decode']['us_per_call']} us, verify {res['verify']['us_per_call']} us",
+        res["verify_rollback"] = bench_verify_commit(kda, args.steps, args.warmup)
+        vr = res["verify_rollback"]
+        print(f"decode {res['decode']['us_per_call']} us, verify {res['verify']['us_per_call']} us, "
+              f"verify rows {vr['rows']['us_per_call']} us + commit {vr['commit']['us_per_call']} us",
               file=sys.stderr, flush=True)
     if args.only != "all":
         return
@@ -413,6 +482,7 @@ def main():
         "varlen": res["varlen"],
         "decode": res["decode"],
         "verify": res["verify"],
+        "verify_rollback": res["verify_rollback"],
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p["inp"])

@@ -21,7 +21,7 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "step", "workspace_bytes", "abi_version", "KdaError", "LIB_PATH",
+__all__ = ["chunk_fwd", "step", "step_rows", "step_commit", "workspace_bytes", "abi_version", "KdaError", "LIB_PATH",
            "KDA_F32", "KDA_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -63,6 +63,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.kda_step.restype = ctypes.c_int
     lib.kda_step.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P]
+    lib.kda_step_rows.restype = ctypes.c_int
+    lib.kda_step_rows.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P, P]
+    lib.kda_step_commit.restype = ctypes.c_int
+    lib.kda_step_commit.argtypes = [D, P, P, P, P, P, ctypes.c_int32, P]
     return lib
 
 
@@ -194,3 +198,47 @@ def step(q, k, v, log_g, beta, state, scale=None, out=None, stream=None):
     _check(lib.kda_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
                         _ptr(state), ctypes.c_int32(n_tok), _ptr(out), _stream(stream)))
     return out
+
+
+def step_rows(q, k, v, log_g, beta, state, scale=None, out=None, deltas=None, stream=None):
+    """Speculative verify, first half: the outputs of rows [N, n_tok, H, d] as
+    ``step`` would give them, with ``state`` left unchanged.  Returns (out,
+    deltas), both [N, n_tok, H, dv] fp32; ``deltas`` feeds ``step_commit``."""
+    N, n_tok, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _need(k, "k", (N, n_tok, H, dk), dt, dev)
+    _need(v, "v", (N, n_tok, H, dv), dt, dev)
+    _need(log_g, "log_g", (N, n_tok, H, dk), torch.float32, dev)
+    _need(beta, "beta", (N, n_tok, H), torch.float32, dev)
+    _need(state, "state", (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, n_tok, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (N, n_tok, H, dv), torch.float32, dev)
+    if deltas is None:
+        deltas = torch.empty((N, n_tok, H, dv), dtype=torch.float32, device=dev)
+    else:
+        _need(deltas, "deltas", (N, n_tok, H, dv), torch.float32, dev)
+    desc = make_desc(N, n_tok, H, dk, dv, code, scale)
+    _check(lib.kda_step_rows(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
+                             _ptr(state), ctypes.c_int32(n_tok), _ptr(out), _ptr(deltas), _stream(stream)))
+    return out, deltas
+
+
+def step_commit(k, log_g, deltas, state, accept, stream=None):
+    """Speculative verify, second half: advance each sequence n of ``state``
+    (in place) by its first ``accept[n]`` rows (int32 [N] on the device), from
+    the ``deltas`` that ``step_rows`` returned for the same rows and state."""
+    N, n_tok, H, dk = k.shape
+    dv = deltas.shape[-1]
+    dev = k.device
+    code = _dtype_code(k)
+    _need(log_g, "log_g", (N, n_tok, H, dk), torch.float32, dev)
+    _need(deltas, "deltas", (N, n_tok, H, dv), torch.float32, dev)
+    _need(state, "state", (N, H, dk, dv), torch.float32, dev)
+    _need(accept, "accept", (N,), torch.int32, dev)
+    desc = make_desc(N, n_tok, H, dk, dv, code, None)
+    _check(lib.kda_step_commit(ctypes.byref(desc), _ptr(k), _ptr(log_g), _ptr(deltas), _ptr(accept),
+                               _ptr(state), ctypes.c_int32(n_tok), _stream(stream)))

@@ -101,6 +101,28 @@ kda_status check_ptr(const void* p, const char* name, const char* fn, bool requi
   return KDA_OK;
 }
 
+// The decode / verify checks shared by kda_step and kda_step_rows.
+kda_status check_rows(const kda_desc* d, const void* q, const void* k, const void* v, const float* log_g,
+                      const float* beta, const float* state, const char* state_name, int32_t n_tok,
+                      const void* out, const char* fn) {
+  kda_status st = check_desc(d, fn);
+  if (st != KDA_OK) return st;
+  if (n_tok < 1) return fail(KDA_ERR_SHAPE, "%s: n_tok must be >= 1 (got %d)", fn, n_tok);
+  if (static_cast<int64_t>(d->num_seqs) * n_tok > INT32_MAX / 2)
+    return fail(KDA_ERR_SHAPE, "%s: num_seqs * n_tok too large", fn);
+  const bool any = d->num_seqs > 0;
+  if ((st = check_ptr(q, "q", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(k, "k", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(v, "v", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(log_g, "log_g", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(beta, "beta", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(state, state_name, fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(out, "out", fn, any)) != KDA_OK) return st;
+  if (out && (out == q || out == k || out == v || out == log_g || out == beta || out == state))
+    return fail(KDA_ERR_SHAPE, "%s: out aliases an input", fn);
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,26 +201,65 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
   return KDA_OK;
 }
 
-kda_status kda_step(const kda_desc* d, const void* q, const void* k, const void* v,
-                    const float* log_g, const float* beta, float* state_inout, int32_t n_tok,
-                    void* out, void* stream) {
-  static const char* fn = "kda_step";
+kda_status kda_step_rows(const kda_desc* d, const void* q, const void* k, const void* v,
+                         const float* log_g, const float* beta, const float* state, int32_t n_tok,
+                         void* out, float* deltas, void* stream) {
+  static const char* fn = "kda_step_rows";
+  kda_status st = check_rows(d, q, k, v, log_g, beta, state, "state", n_tok, out, fn);
+  if (st != KDA_OK) return st;
+  const bool any = d->num_seqs > 0;
+  if ((st = check_ptr(deltas, "deltas", fn, any)) != KDA_OK) return st;
+  if (deltas && (deltas == out || deltas == q || deltas == k || deltas == v || deltas == log_g ||
+                 deltas == beta || deltas == state))
+    return fail(KDA_ERR_SHAPE, "%s: deltas aliases another argument", fn);
+  if (!any) return KDA_OK;
+
+  kda::StepLaunch a{};
+  a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
+  a.state = const_cast<float*>(state);  // read only: keep_state
+  a.keep_state = true;
+  a.out = out; a.deltas = deltas;
+  a.num_seqs = d->num_seqs; a.n_tok = n_tok; a.num_heads = d->num_heads;
+  a.d = d->dk; a.bf16 = d->qkv_dtype == KDA_BF16; a.scale = resolve_scale(d);
+  const hipError_t e = kda::launch_step(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return KDA_OK;
+}
+
+kda_status kda_step_commit(const kda_desc* d, const void* k, const float* log_g, const float* deltas,
+                           const int32_t* accept, float* state_inout, int32_t n_tok, void* stream) {
+  static const char* fn = "kda_step_commit";
   kda_status st = check_desc(d, fn);
   if (st != KDA_OK) return st;
   if (n_tok < 1) return fail(KDA_ERR_SHAPE, "%s: n_tok must be >= 1 (got %d)", fn, n_tok);
   if (static_cast<int64_t>(d->num_seqs) * n_tok > INT32_MAX / 2)
     return fail(KDA_ERR_SHAPE, "%s: num_seqs * n_tok too large", fn);
   const bool any = d->num_seqs > 0;
-  if ((st = check_ptr(q, "q", fn, any)) != KDA_OK) return st;
   if ((st = check_ptr(k, "k", fn, any)) != KDA_OK) return st;
-  if ((st = check_ptr(v, "v", fn, any)) != KDA_OK) return st;
   if ((st = check_ptr(log_g, "log_g", fn, any)) != KDA_OK) return st;
-  if ((st = check_ptr(beta, "beta", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(deltas, "deltas", fn, any)) != KDA_OK) return st;
+  if (any && !accept) return fail(KDA_ERR_NULL, "%s: accept is NULL", fn);
   if ((st = check_ptr(state_inout, "state_inout", fn, any)) != KDA_OK) return st;
-  if ((st = check_ptr(out, "out", fn, any)) != KDA_OK) return st;
-  if (out && (out == q || out == k || out == v || out == log_g || out == beta || out == state_inout))
-    return fail(KDA_ERR_SHAPE, "%s: out aliases an input", fn);
+  if (state_inout && (static_cast<const void*>(state_inout) == k || state_inout == log_g || state_inout == deltas))
+    return fail(KDA_ERR_SHAPE, "%s: state_inout aliases an input", fn);
   if (!any) return KDA_OK;
+
+  kda::CommitLaunch a{};
+  a.k = k; a.log_g = log_g; a.deltas = deltas; a.accept = accept; a.state = state_inout;
+  a.num_seqs = d->num_seqs; a.n_tok = n_tok; a.num_heads = d->num_heads;
+  a.d = d->dk; a.bf16 = d->qkv_dtype == KDA_BF16;
+  const hipError_t e = kda::launch_commit(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return KDA_OK;
+}
+
+kda_status kda_step(const kda_desc* d, const void* q, const void* k, const void* v,
+                    const float* log_g, const float* beta, float* state_inout, int32_t n_tok,
+                    void* out, void* stream) {
+  static const char* fn = "kda_step";
+  const kda_status st = check_rows(d, q, k, v, log_g, beta, state_inout, "state_inout", n_tok, out, fn);
+  if (st != KDA_OK) return st;
+  if (d->num_seqs == 0) return KDA_OK;
 
   kda::StepLaunch a{};
   a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;

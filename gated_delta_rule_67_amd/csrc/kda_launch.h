@@ -13,14 +13,30 @@ struct StepLaunch {
   const void* v;
   const float* log_g;
   const float* beta;
-  float* state;
+  float* state;        // read, and written back unless keep_state
   void* out;
+  float* deltas;       // per-row delta [N, n_tok, H, dv], or null
+  bool keep_state;     // true: the state is only read (speculative rows)
   int num_seqs;
   int n_tok;
   int num_heads;
   int d;        // dk == dv
   bool bf16;    // q/k/v element type
   float scale;
+};
+
+// Arguments of one commit of accepted rows; shapes already validated.
+struct CommitLaunch {
+  const void* k;
+  const float* log_g;
+  const float* deltas;
+  const int32_t* accept;  // device [N]
+  float* state;
+  int num_seqs;
+  int n_tok;
+  int num_heads;
+  int d;
+  bool bf16;
 };
 
 // Arguments of one chunked prefill launch; shapes already validated.
@@ -44,6 +60,7 @@ struct ChunkLaunch {
 };
 
 hipError_t launch_step(const StepLaunch& a, hipStream_t stream);
+hipError_t launch_commit(const CommitLaunch& a, hipStream_t stream);
 // Prefill through the token-recurrent kernel (any dtype / d).  No workspace.
 hipError_t launch_chunk_recurrent(const ChunkLaunch& a, hipStream_t stream);
 

@@ -49,6 +49,7 @@ struct RecArgs {
   float* final_state;         // [N, H, D, D] or null; may equal init_state
   const int32_t* cu_seqlens;  // [N+1] or null (dense)
   float* out;
+  float* deltas;              // per-token delta [.., H, dv] or null
   int num_units;              // N * H
   int T;                      // dense: tokens per sequence
   int H;
@@ -175,8 +176,10 @@ __global__ void __launch_bounds__((RecCfg<D, DVT>::NT)) recurrent_kernel(RecArgs
         dl[c] = bt * (vj[c] - A[c]);
         o[c] = a.scale * (B[c] + dl[c] * KQ);
       }
-      if (g == 0)
+      if (g == 0) {
         *reinterpret_cast<float4*>(a.out + row * D + col) = make_float4(o[0], o[1], o[2], o[3]);
+        if (a.deltas) *reinterpret_cast<float4*>(a.deltas + row * D + col) = make_float4(dl[0], dl[1], dl[2], dl[3]);
+      }
 #pragma unroll
       for (int p = 0; p < RP; ++p) {
         const float kr = s_k[tt][g * RP + p];
@@ -190,6 +193,91 @@ __global__ void __launch_bounds__((RecCfg<D, DVT>::NT)) recurrent_kernel(RecArgs
 #pragma unroll
     for (int p = 0; p < RP; ++p) store4_stream(S1 + (g * RP + p) * D + col, s[p]);
   }
+}
+
+
+// Commit of accepted rows: sequence n's state advances by its first accept[n]
+// rows with the delta of each row already known (saved by the rows pass), so
+// each row is only the state update of the recurrence above,
+// S' = Diag(exp(log_g_t)) S + k_t delta_t^T, in the same order of operations.
+// Nothing is reduced; the tile streams in and out once.
+struct CommitArgs {
+  const void* k;
+  const float* log_g;
+  const float* deltas;
+  const int32_t* accept;
+  float* state;
+  int num_units;  // N * H
+  int n_tok;
+  int H;
+};
+
+template <int D, int DVT, typename In>
+__global__ void __launch_bounds__((RecCfg<D, DVT>::NT)) commit_kernel(CommitArgs a) {
+  using C = RecCfg<D, DVT>;
+  constexpr int CL = C::CL, RP = C::RP, NT = C::NT, TG = C::TG, NTILE = C::NTILE;
+  __shared__ float s_k[TG][D];
+  __shared__ float s_a[TG][D];
+
+  int unit, tile;
+  if (NTILE == 1) {
+    unit = blockIdx.x;
+    tile = 0;
+  } else {
+    const int grp = blockIdx.x / (8 * NTILE);
+    const int rem = blockIdx.x - grp * 8 * NTILE;
+    tile = rem / 8;
+    unit = grp * 8 + (rem & 7);
+  }
+  if (unit >= a.num_units) return;
+  const int n = unit / a.H;
+  const int h = unit - n * a.H;
+  const int m = min(max(a.accept[n], 0), a.n_tok);
+  if (m == 0) return;  // nothing accepted: the state stays as it is
+
+  const int tid = threadIdx.x;
+  const int cl = tid % CL;
+  const int g = tid / CL;
+  const int col = tile * DVT + 4 * cl;
+  const int H = a.H;
+  const In* k = static_cast<const In*>(a.k);
+  float* S = a.state + static_cast<size_t>(unit) * D * D;
+
+  float4 s[RP];
+#pragma unroll
+  for (int p = 0; p < RP; ++p) s[p] = load4_stream(S + (g * RP + p) * D + col);
+
+  for (int t0 = 0; t0 < m; t0 += TG) {
+    const int tg = min(TG, m - t0);
+    __syncthreads();  // the previous pass is done with the staging buffers
+    for (int idx = tid; idx < tg * D; idx += NT) {
+      const int tt = idx / D, i = idx - tt * D;
+      const size_t row = (static_cast<size_t>(n) * a.n_tok + t0 + tt) * H + h;
+      s_k[tt][i] = to_f32(k[row * D + i]);
+      s_a[tt][i] = exp_fast(a.log_g[row * D + i]);
+    }
+    __syncthreads();
+    for (int tt = 0; tt < tg; ++tt) {
+      const size_t row = (static_cast<size_t>(n) * a.n_tok + t0 + tt) * H + h;
+      const float4 dl = load4(a.deltas + row * D + col);
+#pragma unroll
+      for (int p = 0; p < RP; ++p) {
+        const int r = g * RP + p;
+        const float al = s_a[tt][r], kr = s_k[tt][r];
+        s[p].x *= al; s[p].y *= al; s[p].z *= al; s[p].w *= al;
+        s[p].x += kr * dl.x; s[p].y += kr * dl.y; s[p].z += kr * dl.z; s[p].w += kr * dl.w;
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < RP; ++p) store4_stream(S + (g * RP + p) * D + col, s[p]);
+}
+
+template <int D, typename In>
+hipError_t launch_commit_d(const CommitArgs& a, hipStream_t stream) {
+  using C = RecCfg<D, D>;  // whole states: nothing is reduced, the tile only streams
+  hipLaunchKernelGGL((commit_kernel<D, D, In>), dim3(static_cast<unsigned>(a.num_units)), dim3(C::NT), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int D, int DVT, typename In>
@@ -232,14 +320,33 @@ hipError_t launch_step(const StepLaunch& s, hipStream_t stream) {
   RecArgs a{};
   a.q = s.q; a.k = s.k; a.v = s.v; a.log_g = s.log_g; a.beta = s.beta;
   a.init_state = s.state;
-  a.final_state = s.state;  // in place: every workgroup reads its tile before writing it
+  // in place: every workgroup reads its tile before writing it; speculative
+  // rows leave the state as it was
+  a.final_state = s.keep_state ? nullptr : s.state;
   a.cu_seqlens = nullptr;
   a.out = static_cast<float*>(s.out);
+  a.deltas = s.deltas;
   a.num_units = s.num_seqs * s.num_heads;
   a.T = s.n_tok;
   a.H = s.num_heads;
   a.scale = s.scale;
   return launch_recurrent(a, s.d, s.bf16, stream);
+}
+
+hipError_t launch_commit(const CommitLaunch& c, hipStream_t stream) {
+  if (c.num_seqs == 0) return hipSuccess;
+  CommitArgs a{};
+  a.k = c.k; a.log_g = c.log_g; a.deltas = c.deltas; a.accept = c.accept; a.state = c.state;
+  a.num_units = c.num_seqs * c.num_heads;
+  a.n_tok = c.n_tok;
+  a.H = c.num_heads;
+  switch (c.d) {
+    case 16: return c.bf16 ? launch_commit_d<16, bf16_t>(a, stream) : launch_commit_d<16, float>(a, stream);
+    case 32: return c.bf16 ? launch_commit_d<32, bf16_t>(a, stream) : launch_commit_d<32, float>(a, stream);
+    case 64: return c.bf16 ? launch_commit_d<64, bf16_t>(a, stream) : launch_commit_d<64, float>(a, stream);
+    case 128: return c.bf16 ? launch_commit_d<128, bf16_t>(a, stream) : launch_commit_d<128, float>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_chunk_recurrent(const ChunkLaunch& c, hipStream_t stream) {

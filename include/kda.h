@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum {
   KDA_OK = 0,
@@ -146,6 +146,41 @@ kda_status kda_chunk_fwd(const kda_desc* desc, const void* q, const void* k,
 kda_status kda_step(const kda_desc* desc, const void* q, const void* k,
                     const void* v, const float* log_g, const float* beta,
                     float* state_inout, int32_t n_tok, void* out, void* stream);
+
+/*
+ * Speculative verify in two calls: score n_tok draft rows per sequence, then
+ * keep only each sequence's accepted prefix (verify row t uses slot t:
+ * metrale glm5next_layer invariants; rows past the accepted prefix must
+ * leave no trace in the state).
+ *
+ * kda_step_rows: the outputs of rows 0 .. n_tok-1, exactly as kda_step would
+ * produce them, WITHOUT changing the state; each row's
+ * delta_t = beta_t (v_t - kv_t) is written so any prefix can be committed.
+ *   q, k, log_g [N, n_tok, H, dk];  v [N, n_tok, H, dv];  beta [N, n_tok, H]
+ *   state       [N, H, dk, dv] fp32, read only
+ *   out         [N, n_tok, H, dv] (out_dtype)
+ *   deltas      [N, n_tok, H, dv] fp32
+ *
+ * kda_step_commit: advance sequence n's state by its first accept[n] rows,
+ * S <- Diag(exp(log_g_t)) S + k_t delta_t^T for t = 0 .. accept[n]-1 (the
+ * state update of kda_step with the read-back already done), from the same
+ * state kda_step_rows read.  With accept[n] = n_tok the result is kda_step's
+ * final state; with accept[n] = 0 the state is left as it was.
+ *   k, log_g    [N, n_tok, H, dk]: the rows given to kda_step_rows
+ *   deltas      [N, n_tok, H, dv]: its output
+ *   accept      device int32 [N]; values outside [0, n_tok] are clamped
+ *   state_inout [N, H, dk, dv] fp32, updated in place
+ * Neither call uses a workspace; out and deltas must not alias any input.
+ */
+kda_status kda_step_rows(const kda_desc* desc, const void* q, const void* k,
+                         const void* v, const float* log_g, const float* beta,
+                         const float* state, int32_t n_tok, void* out,
+                         float* deltas, void* stream);
+
+kda_status kda_step_commit(const kda_desc* desc, const void* k,
+                           const float* log_g, const float* deltas,
+                           const int32_t* accept, float* state_inout,
+                           int32_t n_tok, void* stream);
 
 #ifdef __cplusplus
 }

@@ -29,15 +29,15 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert {"kda_chunk_fwd", "kda_step", "kda_chunk_workspace_bytes", "kda_status_string",
-            "kda_last_error", "kda_abi_version"} <= set(names)
+    assert {"kda_chunk_fwd", "kda_step", "kda_step_rows", "kda_step_commit", "kda_chunk_workspace_bytes",
+            "kda_status_string", "kda_last_error", "kda_abi_version"} <= set(names)
     raw = ctypes.CDLL(kda.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in kda.h but not exported"
 
 
 def test_abi_version_and_status_strings():
-    assert kda.abi_version() == 2
+    assert kda.abi_version() == 3
     seen = set()
     for code in range(8):
         s = lib.kda_status_string(code).decode()
@@ -211,3 +211,32 @@ def test_last_error_is_thread_local():
     assert other[0] == ""
     assert "n_tok" in other[1]
     assert last() == mine
+
+
+def rows(d, n_tok=2, q=P(0), k=P(1 << 20), v=P(2 << 20), g=P(3 << 20), b=P(4 << 20),
+         s=P(6 << 20), out=P(5 << 20), dl=P(7 << 20)):
+    return lib.kda_step_rows(ctypes.byref(d) if d is not None else None, q, k, v, g, b, s, n_tok, out, dl, None)
+
+
+def commit(d, n_tok=2, k=P(1 << 20), g=P(3 << 20), dl=P(7 << 20), acc=P(8 << 20), s=P(6 << 20)):
+    return lib.kda_step_commit(ctypes.byref(d) if d is not None else None, k, g, dl, acc, s, n_tok, None)
+
+
+def test_rows_and_commit_validate_like_step():
+    assert rows(None) == NULL and commit(None) == NULL
+    assert rows(desc(), n_tok=0) == SHAPE and commit(desc(), n_tok=0) == SHAPE
+    assert rows(desc(dk=64, dv=128)) == UNSUPPORTED and commit(desc(dk=64, dv=128)) == UNSUPPORTED
+    assert rows(desc(), s=None) == NULL and "state" in last()
+    assert rows(desc(), dl=None) == NULL and "deltas" in last()
+    assert rows(desc(), dl=P(8)) == ALIGN
+    assert rows(desc(), dl=P(5 << 20)) == SHAPE  # deltas over out
+    assert rows(desc(), out=P(6 << 20)) == SHAPE  # out over the state
+    assert commit(desc(), acc=None) == NULL and "accept" in last()
+    assert commit(desc(), dl=None) == NULL and "deltas" in last()
+    assert commit(desc(), s=P(4)) == ALIGN
+    assert commit(desc(), s=P(7 << 20)) == SHAPE  # state over deltas
+
+
+def test_rows_and_commit_of_no_sequences_are_noops():
+    assert rows(desc(num_seqs=0), q=None, k=None, v=None, g=None, b=None, s=None, out=None, dl=None) == OK
+    assert commit(desc(num_seqs=0), k=None, g=None, dl=None, acc=None, s=None) == OK

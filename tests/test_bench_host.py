@@ -33,6 +33,15 @@ def test_step_bytes_of_decode_and_verify():
     assert bench.step_bytes(64, 4, 32, 128) == 64 * 32 * (2 * 65536 + 4 * 1796) == 283_148_288
 
 
+def test_rows_and_commit_bytes_of_the_verify_workload():
+    # rows: the state read once, each row's q, k, v (bf16), log_g, beta, out and delta
+    per_row = 3 * 256 + 512 + 4 + 512 + 512
+    assert bench.rows_bytes(64, 4, 32, 128) == 64 * 32 * (65536 + 4 * per_row) == 153_124_864
+    # commit: the state read and written, each row's k (bf16), log_g and delta, the accept counts
+    assert bench.commit_bytes(64, 4, 32, 128) == 64 * 32 * (2 * 65536 + 4 * (256 + 512 + 512)) + 64 * 4
+    assert bench.commit_bytes(64, 4, 32, 128) == 278_921_472
+
+
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=300)
