@@ -105,3 +105,37 @@ def test_verify_workload_with_random_acceptance():
         worst = max(worst, err(got[seqs].numpy(), ref_f[seqs]))
     print(f"[verify workload, random acceptance] worst state err {worst:.2e}", flush=True)
     assert worst <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype,rows", [("bf16", 8), ("f32", 5)])
+def test_prompt_tail_through_multi_row_steps(dtype, rows):
+    """A 205-token prompt: its three whole 64-token chunks through
+    kda_chunk_fwd, the 13-token tail through kda_step calls of `rows` rows
+    (the batched sub-chunk walk); and the whole prompt through that walk
+    alone.  Both equal the oracle on the whole prompt."""
+    T, done = 205, 192
+    inp = kda_inputs.make_inputs(B=3, T=T, H=4, dk=128, dv=128, dtype=dtype, seed=90 + rows,
+                                 init="normal", init_std=0.05)
+    dv = to_dev(inp)
+    sl = lambda x, a, b: x[:, a:b].contiguous()
+
+    def walk(state, start):
+        outs = []
+        for a in range(start, T, rows):
+            b = min(a + rows, T)
+            outs.append(kda.step(sl(dv["q"], a, b), sl(dv["k"], a, b), sl(dv["v"], a, b), sl(dv["log_g"], a, b),
+                                 sl(dv["beta"], a, b), state, scale=inp["scale"]))
+        return outs
+
+    o_head, state = kda.chunk_fwd(sl(dv["q"], 0, done), sl(dv["k"], 0, done), sl(dv["v"], 0, done),
+                                  sl(dv["log_g"], 0, done), sl(dv["beta"], 0, done), init_state=dv["init_state"],
+                                  scale=inp["scale"])
+    o_mixed = torch.cat([o_head] + walk(state, done), 1)
+    s_walk = dv["init_state"].clone()
+    o_walk = torch.cat(walk(s_walk, 0), 1)
+    torch.cuda.synchronize()
+    ref_o, ref_f = oracle_prefix(inp, T)
+    for name, o, f in (("chunks + tail", o_mixed, state), ("sub-chunk walk", o_walk, s_walk)):
+        eo, ef = err(o.cpu().numpy(), ref_o), err(f.cpu().numpy(), ref_f)
+        print(f"[prompt {dtype} rows={rows} {name}] out {eo:.2e} state {ef:.2e}", flush=True)
+        assert eo <= TOL[dtype] and ef <= TOL[dtype]
