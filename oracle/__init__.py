@@ -10,7 +10,9 @@ The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, libm ``exp``): the
 token loop of the gated delta rule as printed in the GLM-5.3-Flash model notes
 (Glm5NextTextLinearAttention snippet), with the output read from the updated
 state, and packed documents reset at their boundaries (NeMo glm5_next.layers,
-``_torch_recurrent_kda``).  This module only marshals numpy arrays.
+``_torch_recurrent_kda``); and its reverse mode, the same loop differentiated
+token by token (that page documents the recurrence as differentiable).  This
+module only marshals numpy arrays.
 """
 from __future__ import annotations
 
@@ -45,6 +47,9 @@ def load(path: str = LIB_PATH):
     lib.kda_oracle_forward.restype = ctypes.c_int
     lib.kda_oracle_forward.argtypes = [i64, i64, i64, i64, i64, dp, dp, dp, dp, dp,
                                        dp, ip, ctypes.c_double, dp, dp, ctypes.c_int]
+    lib.kda_oracle_backward.restype = ctypes.c_int
+    lib.kda_oracle_backward.argtypes = [i64, i64, i64, i64, i64, dp, dp, dp, dp, dp, dp, ip,
+                                        ctypes.c_double, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
     lib.kda_oracle_threads.restype = ctypes.c_int
     lib.kda_oracle_threads.argtypes = [ctypes.c_int]
     return lib
@@ -118,3 +123,47 @@ def kda_step(q, k, v, log_g, beta, state, scale=None, n_threads: int = 0):
     """
     return kda_forward(q, k, v, log_g, beta, init_state=state, scale=scale,
                        n_threads=n_threads)
+
+
+def kda_backward(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None,
+                 d_out=None, d_final=None, n_threads: int = 0, lib=None):
+    """Gradients of L = sum(d_out * out) + sum(d_final * final_state).
+
+    Inputs as for :func:`kda_forward`; ``d_out`` [B, T, H, dv] and ``d_final``
+    [N, H, dk, dv] may be None (zeros).  Returns a dict of float64 arrays
+    ``dq, dk, dv, dlog_g, dbeta, d_init_state`` shaped like q, k, v, log_g,
+    beta and the initial state.
+    """
+    lib = lib or _get_lib()
+    q, k, v, log_g, beta = (_f64(x) for x in (q, k, v, log_g, beta))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    assert k.shape == q.shape and log_g.shape == q.shape
+    assert v.shape == (B, T, H, dv) and beta.shape == (B, T, H)
+    if cu_seqlens is not None:
+        assert B == 1, "packed mode takes one row"
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N, L = cu.shape[0] - 1, T
+        cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    else:
+        cu, N, L, cu_p = None, B, T, None
+    if scale is None:
+        scale = dk ** -0.5
+    s0 = _f64(init_state) if init_state is not None else None
+    if s0 is not None:
+        assert s0.shape == (N, H, dk, dv)
+    do = _f64(d_out) if d_out is not None else None
+    if do is not None:
+        assert do.shape == (B, T, H, dv)
+    dfin = _f64(d_final) if d_final is not None else None
+    if dfin is not None:
+        assert dfin.shape == (N, H, dk, dv)
+    g = {"dq": np.zeros(q.shape), "dk": np.zeros(q.shape), "dv": np.zeros(v.shape),
+         "dlog_g": np.zeros(q.shape), "dbeta": np.zeros(beta.shape), "d_init_state": np.zeros((N, H, dk, dv))}
+    rc = lib.kda_oracle_backward(N, L, H, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
+                                 _ptr(s0), cu_p, float(scale), _ptr(do), _ptr(dfin), _ptr(g["dq"]),
+                                 _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_g"]), _ptr(g["dbeta"]),
+                                 _ptr(g["d_init_state"]), int(n_threads))
+    if rc != 0:
+        raise ValueError(f"kda_oracle_backward failed with code {rc}")
+    return g

@@ -86,6 +86,198 @@ static void run_unit(const unit_t* u, int64_t H, int64_t dk, int64_t dv,
     memcpy(final_state + (n * H + h) * dk * dv, S, sizeof(double) * dk * dv);
 }
 
+/* One unit in reverse mode.  Forward: the same token loop as run_unit, with
+ * the state before every token kept in hist.  Backward: for t = last .. first,
+ * dS holds dL/dS_t (the state after token t); each line below is the chain
+ * rule through one line of the forward step, taken in reverse order:
+ *
+ *   forward step t                      reverse
+ *   P = Diag(a) S_{t-1}, a = exp(g_t)    dS_{t-1} = Diag(a) dP,  dg_t[i] = a[i] sum_j dP[i,j] S_{t-1}[i,j]
+ *   kv = P^T k_t                          dP += k_t dkv^T,  dk_t += P dkv
+ *   delta = beta_t (v_t - kv)             dv_t = beta_t ddelta,  dkv = -beta_t ddelta,
+ *                                         dbeta_t = ddelta . (v_t - kv)
+ *   S_t = P + k_t delta^T                 dP = dS,  dk_t = dS delta,  ddelta = dS^T k_t
+ *   o_t = scale S_t^T q_t                 dq_t = scale S_t do_t,  dS += scale q_t do_t^T
+ */
+static int run_unit_bwd(const unit_t* u, int64_t H, int64_t dk, int64_t dv,
+                        const double* q, const double* k, const double* v,
+                        const double* log_g, const double* beta,
+                        const double* init_state, double scale,
+                        const double* d_out, const double* d_final,
+                        double* dq, double* dk_out, double* dv_out,
+                        double* dlog_g, double* dbeta, double* d_init) {
+  const int64_t n = u->n, h = u->h, len = u->len, sz = dk * dv;
+  /* hist: len states; then S, P, dS, dP (dk x dv each), kv, delta, ddelta, dkv (dv), a (dk) */
+  double* hist = (double*)malloc(sizeof(double) * ((len + 4) * sz + 4 * dv + dk));
+  if (!hist) return -4;
+  double* S = hist + len * sz;
+  double* P = S + sz;
+  double* dS = P + sz;
+  double* dP = dS + sz;
+  double* kv = dP + sz;
+  double* delta = kv + dv;
+  double* ddelta = delta + dv;
+  double* dkv = ddelta + dv;
+  double* a = dkv + dv;
+
+  if (init_state)
+    memcpy(S, init_state + (n * H + h) * sz, sizeof(double) * sz);
+  else
+    memset(S, 0, sizeof(double) * sz);
+
+  /* forward, keeping the state before every token */
+  for (int64_t s = 0; s < len; ++s) {
+    const int64_t t = u->start + s;
+    const double* kt = k + (t * H + h) * dk;
+    const double* gt = log_g + (t * H + h) * dk;
+    const double* vt = v + (t * H + h) * dv;
+    const double bt = beta[t * H + h];
+    memcpy(hist + s * sz, S, sizeof(double) * sz);
+    for (int64_t i = 0; i < dk; ++i) {
+      const double ai = exp(gt[i]);
+      for (int64_t j = 0; j < dv; ++j) S[i * dv + j] *= ai;
+    }
+    for (int64_t j = 0; j < dv; ++j) kv[j] = 0.0;
+    for (int64_t i = 0; i < dk; ++i)
+      for (int64_t j = 0; j < dv; ++j) kv[j] += S[i * dv + j] * kt[i];
+    for (int64_t j = 0; j < dv; ++j) delta[j] = bt * (vt[j] - kv[j]);
+    for (int64_t i = 0; i < dk; ++i)
+      for (int64_t j = 0; j < dv; ++j) S[i * dv + j] += kt[i] * delta[j];
+  }
+
+  /* dL/dS after the last token */
+  if (d_final)
+    memcpy(dS, d_final + (n * H + h) * sz, sizeof(double) * sz);
+  else
+    memset(dS, 0, sizeof(double) * sz);
+
+  for (int64_t s = len - 1; s >= 0; --s) {
+    const int64_t t = u->start + s;
+    const double* qt = q + (t * H + h) * dk;
+    const double* kt = k + (t * H + h) * dk;
+    const double* gt = log_g + (t * H + h) * dk;
+    const double* vt = v + (t * H + h) * dv;
+    const double bt = beta[t * H + h];
+    const double* Sprev = hist + s * sz;
+    double* dqt = dq + (t * H + h) * dk;
+    double* dkt = dk_out + (t * H + h) * dk;
+    double* dgt = dlog_g + (t * H + h) * dk;
+    double* dvt = dv_out + (t * H + h) * dv;
+
+    /* recompute this token's forward quantities from the state before it */
+    for (int64_t i = 0; i < dk; ++i) {
+      a[i] = exp(gt[i]);
+      for (int64_t j = 0; j < dv; ++j) P[i * dv + j] = a[i] * Sprev[i * dv + j];
+    }
+    for (int64_t j = 0; j < dv; ++j) kv[j] = 0.0;
+    for (int64_t i = 0; i < dk; ++i)
+      for (int64_t j = 0; j < dv; ++j) kv[j] += P[i * dv + j] * kt[i];
+    for (int64_t j = 0; j < dv; ++j) delta[j] = bt * (vt[j] - kv[j]);
+    for (int64_t i = 0; i < dk; ++i)
+      for (int64_t j = 0; j < dv; ++j) S[i * dv + j] = P[i * dv + j] + kt[i] * delta[j];
+
+    /* output o_t = scale S_t^T q_t */
+    if (d_out) {
+      const double* dot = d_out + (t * H + h) * dv;
+      for (int64_t i = 0; i < dk; ++i) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < dv; ++j) acc += S[i * dv + j] * dot[j];
+        dqt[i] = scale * acc;
+      }
+      for (int64_t i = 0; i < dk; ++i)
+        for (int64_t j = 0; j < dv; ++j) dS[i * dv + j] += scale * qt[i] * dot[j];
+    } else {
+      for (int64_t i = 0; i < dk; ++i) dqt[i] = 0.0;
+    }
+    /* rank-1 update S_t = P + k_t delta^T */
+    for (int64_t i = 0; i < dk; ++i) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < dv; ++j) acc += dS[i * dv + j] * delta[j];
+      dkt[i] = acc;
+    }
+    for (int64_t j = 0; j < dv; ++j) ddelta[j] = 0.0;
+    for (int64_t i = 0; i < dk; ++i)
+      for (int64_t j = 0; j < dv; ++j) ddelta[j] += dS[i * dv + j] * kt[i];
+    /* scaled error delta = beta_t (v_t - kv) */
+    {
+      double acc = 0.0;
+      for (int64_t j = 0; j < dv; ++j) acc += ddelta[j] * (vt[j] - kv[j]);
+      dbeta[t * H + h] = acc;
+    }
+    for (int64_t j = 0; j < dv; ++j) {
+      dvt[j] = bt * ddelta[j];
+      dkv[j] = -bt * ddelta[j];
+    }
+    /* read-back kv = P^T k_t */
+    for (int64_t i = 0; i < dk; ++i) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < dv; ++j) {
+        dP[i * dv + j] = dS[i * dv + j] + kt[i] * dkv[j];
+        acc += P[i * dv + j] * dkv[j];
+      }
+      dkt[i] += acc;
+    }
+    /* decay P = Diag(exp(g_t)) S_{t-1} */
+    for (int64_t i = 0; i < dk; ++i) {
+      double acc = 0.0;
+      for (int64_t j = 0; j < dv; ++j) acc += dP[i * dv + j] * Sprev[i * dv + j];
+      dgt[i] = a[i] * acc;
+      for (int64_t j = 0; j < dv; ++j) dS[i * dv + j] = a[i] * dP[i * dv + j];
+    }
+  }
+  if (d_init) memcpy(d_init + (n * H + h) * sz, dS, sizeof(double) * sz);
+  free(hist);
+  return 0;
+}
+
+int kda_oracle_backward(int64_t num_seqs, int64_t seq_len, int64_t num_heads,
+                        int64_t dk, int64_t dv, const double* q, const double* k,
+                        const double* v, const double* log_g, const double* beta,
+                        const double* init_state, const int64_t* cu_seqlens,
+                        double scale, const double* d_out, const double* d_final,
+                        double* dq, double* dk_out, double* dv_out,
+                        double* dlog_g, double* dbeta, double* d_init,
+                        int n_threads) {
+  if (!q || !k || !v || !log_g || !beta || !dq || !dk_out || !dv_out || !dlog_g || !dbeta)
+    return -1;
+  if (num_seqs < 0 || seq_len < 0 || num_heads <= 0 || dk <= 0 || dv <= 0)
+    return -2;
+  if (cu_seqlens) {
+    if (cu_seqlens[0] != 0 || cu_seqlens[num_seqs] != seq_len) return -3;
+    for (int64_t n = 0; n < num_seqs; ++n)
+      if (cu_seqlens[n + 1] < cu_seqlens[n]) return -3;
+  }
+  const int64_t n_units = num_seqs * num_heads;
+  unit_t* units = (unit_t*)malloc(sizeof(unit_t) * (n_units > 0 ? n_units : 1));
+  if (!units) return -4;
+  for (int64_t n = 0; n < num_seqs; ++n)
+    for (int64_t h = 0; h < num_heads; ++h) {
+      unit_t* u = &units[n * num_heads + h];
+      u->n = n;
+      u->h = h;
+      u->start = cu_seqlens ? cu_seqlens[n] : n * seq_len;
+      u->len = cu_seqlens ? cu_seqlens[n + 1] - cu_seqlens[n] : seq_len;
+    }
+  qsort(units, (size_t)n_units, sizeof(unit_t), by_len_desc);
+
+  int failed = 0;
+#ifdef _OPENMP
+  const int nt = kda_oracle_threads(n_threads);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 1)
+#endif
+  for (int64_t u = 0; u < n_units; ++u) {
+    if (run_unit_bwd(&units[u], num_heads, dk, dv, q, k, v, log_g, beta, init_state, scale,
+                     d_out, d_final, dq, dk_out, dv_out, dlog_g, dbeta, d_init) != 0) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      failed = 1;
+    }
+  }
+  free(units);
+  return failed ? -4 : 0;
+}
+
 int kda_oracle_threads(int n_threads) {
 #ifdef _OPENMP
   return n_threads > 0 ? n_threads : omp_get_max_threads();

@@ -29,8 +29,9 @@
  * reset to the document's own initial state at every document start.
  *
  * parity pins: every function here is pinned by the CPU tests (closed forms,
- * exact rational brute force, packed/split/linearity invariants); none is
- * "parity unpinned".
+ * exact rational brute force, packed/split/linearity invariants; the backward
+ * by central finite differences of the forward, a closed form and structural
+ * invariants); none is "parity unpinned".
  */
 #ifndef KDA_ORACLE_H
 #define KDA_ORACLE_H
@@ -51,6 +52,27 @@ int kda_oracle_forward(int64_t num_seqs, int64_t seq_len, int64_t num_heads,
                        const double* init_state, const int64_t* cu_seqlens,
                        double scale, double* out, double* final_state,
                        int n_threads);
+
+/* Reverse mode of kda_oracle_forward (NeMo glm5_next.layers: the reference
+ * recurrence `_torch_recurrent_kda` is documented as differentiable, and the
+ * KDA parameters are trained under FSDP).
+ *
+ * For the scalar loss L = sum(d_out * out) + sum(d_final * final_state),
+ * returns dL/dq, dL/dk, dL/dv, dL/dlog_g, dL/dbeta and dL/dinit_state.  Same
+ * shapes and layouts as the forward's inputs; d_out [tokens, H, dv] and
+ * d_final [N, H, dk, dv] may be NULL (zeros); d_init may be NULL (not
+ * written).  The forward is rerun per unit with the state before every token
+ * kept (len * dk * dv doubles per unit in flight), then every token's step is
+ * differentiated in reverse order.  Same return codes as the forward. */
+int kda_oracle_backward(int64_t num_seqs, int64_t seq_len, int64_t num_heads,
+                        int64_t dk, int64_t dv,
+                        const double* q, const double* k, const double* v,
+                        const double* log_g, const double* beta,
+                        const double* init_state, const int64_t* cu_seqlens,
+                        double scale, const double* d_out, const double* d_final,
+                        double* dq, double* dk_out, double* dv_out,
+                        double* dlog_g, double* dbeta, double* d_init,
+                        int n_threads);
 
 /* Number of OpenMP threads a call with n_threads would use. */
 int kda_oracle_threads(int n_threads);

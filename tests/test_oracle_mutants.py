@@ -3,7 +3,8 @@
 Each mutant is a textual edit of a *copy* of ``oracle/kda_oracle.c`` (a dropped
 term, a wrong sign, a wrong index or axis, a transposed operand, a missing
 reset, a wrong step order), compiled to a temporary library and run against
-``test_oracle_pins.py`` in a subprocess (a mutant may read out of bounds, so it
+``test_oracle_pins.py`` (forward mutants) or ``test_oracle_bwd_pins.py``
+(reverse-mode mutants) in a subprocess (a mutant may read out of bounds, so it
 never runs in this process).  The committed oracle is never modified.
 """
 import os
@@ -42,6 +43,36 @@ MUTANTS = {
 }
 
 
+# planted mistakes in the reverse mode, each a plausible slip in one chain-rule line
+BWD_MUTANTS = {
+    "bwd_dq_from_pre_update_state": ("acc += S[i * dv + j] * dot[j];", "acc += P[i * dv + j] * dot[j];"),
+    "bwd_output_term_dropped": ("dS[i * dv + j] += scale * qt[i] * dot[j];", "(void)0;"),
+    "bwd_dq_scale_dropped": ("dqt[i] = scale * acc;", "dqt[i] = acc;"),
+    "bwd_dbeta_sign": ("acc += ddelta[j] * (vt[j] - kv[j]);", "acc += ddelta[j] * (vt[j] + kv[j]);"),
+    "bwd_dkv_sign": ("dkv[j] = -bt * ddelta[j];", "dkv[j] = bt * ddelta[j];"),
+    "bwd_dv_beta_dropped": ("dvt[j] = bt * ddelta[j];", "dvt[j] = ddelta[j];"),
+    "bwd_ddelta_uses_q": ("ddelta[j] += dS[i * dv + j] * kt[i];", "ddelta[j] += dS[i * dv + j] * qt[i];"),
+    "bwd_readback_dk_dropped": ("dkt[i] += acc;", "(void)acc;"),
+    "bwd_readback_dP_dropped": ("dP[i * dv + j] = dS[i * dv + j] + kt[i] * dkv[j];",
+                                "dP[i * dv + j] = dS[i * dv + j];"),
+    "bwd_dlog_g_missing_exp": ("dgt[i] = a[i] * acc;", "dgt[i] = acc;"),
+    "bwd_dS_not_decayed": ("dS[i * dv + j] = a[i] * dP[i * dv + j];", "dS[i * dv + j] = dP[i * dv + j];"),
+    "bwd_dlog_g_uses_post_state": ("acc += dP[i * dv + j] * Sprev[i * dv + j];",
+                                   "acc += dP[i * dv + j] * S[i * dv + j];"),
+    "bwd_d_final_ignored": ("if (d_final)\n    memcpy(dS,", "if (0)\n    memcpy(dS,"),
+    "bwd_history_after_decay": ("    memcpy(hist + s * sz, S, sizeof(double) * sz);\n"
+                                "    for (int64_t i = 0; i < dk; ++i) {\n"
+                                "      const double ai = exp(gt[i]);\n"
+                                "      for (int64_t j = 0; j < dv; ++j) S[i * dv + j] *= ai;\n"
+                                "    }\n",
+                                "    for (int64_t i = 0; i < dk; ++i) {\n"
+                                "      const double ai = exp(gt[i]);\n"
+                                "      for (int64_t j = 0; j < dv; ++j) S[i * dv + j] *= ai;\n"
+                                "    }\n"
+                                "    memcpy(hist + s * sz, S, sizeof(double) * sz);\n"),
+}
+
+
 def _pre_update_output(src):
     """Move the output loop before the rank-1 update (output from the pre-update state)."""
     upd = ("    for (int64_t i = 0; i < dk; ++i)\n"
@@ -68,10 +99,10 @@ def workdir(tmp_path_factory):
     return tmp_path_factory.mktemp("mutants")
 
 
-def _run_pins(lib_path):
+def _run_pins(lib_path, pins="test_oracle_pins.py"):
     env = dict(os.environ, KDA_ORACLE_LIB=lib_path)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                        os.path.join(ROOT, "tests", pins)],
                        env=env, cwd=ROOT, capture_output=True, text=True, timeout=600)
     return r.returncode, r.stdout[-2000:]
 
@@ -87,8 +118,9 @@ def _build(workdir, name, src_text):
 
 def test_unmutated_copy_passes(workdir):
     lib = _build(workdir, "clean", open(SRC).read())
-    rc, out = _run_pins(lib)
-    assert rc == 0, out
+    for pins in ("test_oracle_pins.py", "test_oracle_bwd_pins.py"):
+        rc, out = _run_pins(lib, pins)
+        assert rc == 0, out
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS) + ["pre_update_output", "readback_before_decay"])
@@ -105,3 +137,13 @@ def test_mutant_is_caught(workdir, name):
     assert mutated != src
     rc, out = _run_pins(_build(workdir, name, mutated))
     assert rc != 0, f"mutant {name} survived the pins:\n{out}"
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_backward_mutant_is_caught(workdir, name):
+    src = open(SRC).read()
+    old, new = BWD_MUTANTS[name]
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
+    mutated = src.replace(old, new)
+    rc, out = _run_pins(_build(workdir, name, mutated), "test_oracle_bwd_pins.py")
+    assert rc != 0, f"mutant {name} survived the backward pins:\n{out}"
