@@ -73,6 +73,17 @@ BWD_MUTANTS = {
 }
 
 
+def _mutate_in(src, func, old, new, name):
+    """Replace `old` by `new` inside the body of the C function starting with
+    `func` (up to the next top-level closing brace); `old` must occur exactly
+    once there."""
+    a = src.index(func)
+    e = src.index("\n}\n", a) + 3
+    body = src[a:e]
+    assert body.count(old) == 1, f"mutation anchor for {name} not unique/found in {func}"
+    return src[:a] + body.replace(old, new) + src[e:]
+
+
 def _pre_update_output(src):
     """Move the output loop before the rank-1 update (output from the pre-update state)."""
     upd = ("    for (int64_t i = 0; i < dk; ++i)\n"
@@ -126,14 +137,14 @@ def test_unmutated_copy_passes(workdir):
 @pytest.mark.parametrize("name", sorted(MUTANTS) + ["pre_update_output", "readback_before_decay"])
 def test_mutant_is_caught(workdir, name):
     src = open(SRC).read()
-    if name == "pre_update_output":
-        mutated = _pre_update_output(src)
-    elif name == "readback_before_decay":
-        mutated = _readback_before_decay(src)
+    if name in ("pre_update_output", "readback_before_decay"):
+        a = src.index("static void run_unit(")
+        e = src.index("\n}\n", a) + 3
+        edit = _pre_update_output if name == "pre_update_output" else _readback_before_decay
+        mutated = src[:a] + edit(src[a:e]) + src[e:]
     else:
         old, new = MUTANTS[name]
-        assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
-        mutated = src.replace(old, new)
+        mutated = _mutate_in(src, "static void run_unit(", old, new, name)
     assert mutated != src
     rc, out = _run_pins(_build(workdir, name, mutated))
     assert rc != 0, f"mutant {name} survived the pins:\n{out}"
@@ -143,7 +154,6 @@ def test_mutant_is_caught(workdir, name):
 def test_backward_mutant_is_caught(workdir, name):
     src = open(SRC).read()
     old, new = BWD_MUTANTS[name]
-    assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
-    mutated = src.replace(old, new)
+    mutated = _mutate_in(src, "static int run_unit_bwd(", old, new, name)
     rc, out = _run_pins(_build(workdir, name, mutated), "test_oracle_bwd_pins.py")
     assert rc != 0, f"mutant {name} survived the backward pins:\n{out}"
