@@ -9,6 +9,7 @@ fails if the library has not been built (``python -m gated_delta_rule_67_amd.bui
 
     out, final_state = chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None)
     out = step(q, k, v, log_g, beta, state)        # state updated in place
+    grads = chunk_bwd(q, k, v, log_g, beta, d_out, init_state=None, cu_seqlens=None, d_final=None)
 
 Argument order follows ``_torch_recurrent_kda(q, k, v, g, beta, cu_seqlens)`` of
 NeMo glm5_next.layers; q/k/v/g are [batch, seq, heads, head_dim], beta is
@@ -21,8 +22,8 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "step", "step_rows", "step_commit", "workspace_bytes", "abi_version", "KdaError", "LIB_PATH",
-           "KDA_F32", "KDA_BF16"]
+__all__ = ["chunk_fwd", "chunk_bwd", "step", "step_rows", "step_commit", "workspace_bytes", "bwd_workspace_bytes",
+           "abi_version", "KdaError", "LIB_PATH", "KDA_F32", "KDA_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 KDA_F32, KDA_BF16 = 0, 1
@@ -61,6 +62,10 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_workspace_bytes.argtypes = [D, ctypes.c_int]
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+    lib.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_chunk_bwd_workspace_bytes.argtypes = [D, ctypes.c_int]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
+    lib.kda_chunk_bwd.argtypes = [D] + [P] * 15 + [P]
     lib.kda_step.restype = ctypes.c_int
     lib.kda_step.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P]
     lib.kda_step_rows.restype = ctypes.c_int
@@ -175,6 +180,67 @@ def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None
                              _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
                              _stream(stream)))
     return out, final_state
+
+
+def bwd_workspace_bytes(num_seqs: int, seq_len: int, H: int, d: int, packed: bool) -> int:
+    """Device scratch bytes of a chunk_bwd call (see kda_chunk_bwd_workspace_bytes)."""
+    desc = make_desc(num_seqs, seq_len, H, d, d, KDA_BF16)
+    return lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(desc), int(packed))
+
+
+def chunk_bwd(q, k, v, log_g, beta, d_out, init_state=None, cu_seqlens=None, d_final=None, scale=None,
+              grads=None, d_init_state=True, workspace=None, stream=None):
+    """Reverse mode of ``chunk_fwd``: gradients of sum(d_out * out) +
+    sum(d_final * final_state) for the same inputs.
+
+    Returns a dict of fp32 tensors ``dq, dk, dv, dlog_g, dbeta`` shaped like
+    q, k, v, log_g, beta, and ``d_init_state`` [N, H, dk, dv] (None when
+    ``d_init_state=False``).  ``grads`` may hold preallocated output tensors
+    under the same keys.  ``workspace`` (uint8 device tensor) is allocated when
+    absent or too small.
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _need(k, "k", (B, T, H, dk), dt, dev)
+    _need(v, "v", (B, T, H, dv), dt, dev)
+    _need(log_g, "log_g", (B, T, H, dk), torch.float32, dev)
+    _need(beta, "beta", (B, T, H), torch.float32, dev)
+    _need(d_out, "d_out", (B, T, H, dv), torch.float32, dev)
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed mode takes a single row (B == 1)")
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
+        N, L = cu_seqlens.shape[0] - 1, T
+    else:
+        N, L = B, T
+    if init_state is not None:
+        _need(init_state, "init_state", (N, H, dk, dv), torch.float32, dev)
+    if d_final is not None:
+        _need(d_final, "d_final", (N, H, dk, dv), torch.float32, dev)
+    shapes = {"dq": (B, T, H, dk), "dk": (B, T, H, dk), "dv": (B, T, H, dv), "dlog_g": (B, T, H, dk),
+              "dbeta": (B, T, H), "d_init_state": (N, H, dk, dv)}
+    g = dict(grads or {})
+    for name, shp in shapes.items():
+        if name == "d_init_state" and d_init_state is False:
+            g[name] = None
+            continue
+        if g.get(name) is None:
+            g[name] = torch.empty(shp, dtype=torch.float32, device=dev)
+        else:
+            _need(g[name], name, shp, torch.float32, dev)
+    desc = make_desc(N, L, H, dk, dv, code, scale)
+    need = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(desc), int(cu_seqlens is not None))
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        desc.workspace, desc.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(lib.kda_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
+                             _ptr(init_state), _ptr(cu_seqlens), _ptr(d_out), _ptr(d_final), _ptr(g["dq"]),
+                             _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_g"]), _ptr(g["dbeta"]),
+                             _ptr(g["d_init_state"]), _stream(stream)))
+    return g
 
 
 def step(q, k, v, log_g, beta, state, scale=None, out=None, stream=None):

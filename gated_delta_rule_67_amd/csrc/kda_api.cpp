@@ -271,4 +271,74 @@ kda_status kda_step(const kda_desc* d, const void* q, const void* k, const void*
   return KDA_OK;
 }
 
+size_t kda_chunk_bwd_workspace_bytes(const kda_desc* d, int packed) {
+  if (!d || d->num_seqs < 0 || d->seq_len < 0 || d->num_heads <= 0) return 0;
+  if (d->dk != d->dv || (d->dk != 16 && d->dk != 32 && d->dk != 64 && d->dk != 128)) return 0;
+  return kda::bwd_workspace_bytes(d->num_seqs, d->seq_len, d->num_heads, d->dk, packed != 0);
+}
+
+kda_status kda_chunk_bwd(const kda_desc* d, const void* q, const void* k, const void* v,
+                         const float* log_g, const float* beta, const float* init_state,
+                         const int32_t* cu_seqlens, const float* d_out, const float* d_final_state,
+                         float* dq, float* dk, float* dv, float* dlog_g, float* dbeta,
+                         float* d_init_state, void* stream) {
+  static const char* fn = "kda_chunk_bwd";
+  kda_status st = check_desc(d, fn);
+  if (st != KDA_OK) return st;
+  if (d->seq_len < 0) return fail(KDA_ERR_SHAPE, "%s: seq_len < 0", fn);
+  const bool packed = cu_seqlens != nullptr;
+  const int64_t tokens = packed ? d->seq_len : static_cast<int64_t>(d->num_seqs) * d->seq_len;
+  if (tokens > INT32_MAX / 2) return fail(KDA_ERR_SHAPE, "%s: too many tokens (%lld)", fn, (long long)tokens);
+  if (packed && d->num_seqs == 0 && d->seq_len != 0)
+    return fail(KDA_ERR_SHAPE, "%s: packed problem with tokens but no documents", fn);
+  const bool has_tok = tokens > 0;
+  const char* in_names[] = {"q", "k", "v", "log_g", "beta", "d_out"};
+  const void* ins[] = {q, k, v, log_g, beta, d_out};
+  for (int i = 0; i < 6; ++i)
+    if ((st = check_ptr(ins[i], in_names[i], fn, has_tok)) != KDA_OK) return st;
+  const char* out_names[] = {"dq", "dk", "dv", "dlog_g", "dbeta"};
+  float* outs[] = {dq, dk, dv, dlog_g, dbeta};
+  for (int i = 0; i < 5; ++i)
+    if ((st = check_ptr(outs[i], out_names[i], fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(init_state, "init_state", fn, false)) != KDA_OK) return st;
+  if ((st = check_ptr(d_final_state, "d_final_state", fn, false)) != KDA_OK) return st;
+  if ((st = check_ptr(d_init_state, "d_init_state", fn, false)) != KDA_OK) return st;
+  if ((st = check_ptr(cu_seqlens, "cu_seqlens", fn, false)) != KDA_OK) return st;
+  // outputs alias neither an input nor each other
+  const void* all_in[] = {q, k, v, log_g, beta, init_state, cu_seqlens, d_out, d_final_state};
+  float* all_out[] = {dq, dk, dv, dlog_g, dbeta, d_init_state};
+  for (int i = 0; i < 6; ++i) {
+    if (!all_out[i]) continue;
+    for (const void* p : all_in)
+      if (p && p == all_out[i]) return fail(KDA_ERR_SHAPE, "%s: a gradient output aliases an input", fn);
+    for (int j = 0; j < i; ++j)
+      if (all_out[j] == all_out[i]) return fail(KDA_ERR_SHAPE, "%s: two gradient outputs alias", fn);
+  }
+  kda::BwdLaunch a{};
+  a.num_seqs = d->num_seqs;
+  a.seq_len = d->seq_len;
+  a.num_heads = d->num_heads;
+  a.d = d->dk;
+  a.bf16 = d->qkv_dtype == KDA_BF16;
+  a.cu_seqlens = cu_seqlens;
+  if (!kda::bwd_supported(a)) return fail(KDA_ERR_SHAPE, "%s: problem too large", fn);
+  const size_t ws_need = kda::bwd_workspace_bytes(d->num_seqs, d->seq_len, d->num_heads, d->dk, packed);
+  const bool use_ws = has_tok || (packed && d->num_seqs > 0);  // packed: the chunk map lives there
+  if (use_ws) {
+    if (!d->workspace || d->workspace_bytes < ws_need)
+      return fail(KDA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, ws_need,
+                  d->workspace ? d->workspace_bytes : size_t(0));
+    if (misaligned(d->workspace)) return fail(KDA_ERR_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+  }
+  if (d->num_seqs == 0 || (!has_tok && !d_init_state)) return KDA_OK;
+  a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta; a.init_state = init_state;
+  a.d_out = d_out; a.d_final = d_final_state;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_g = dlog_g; a.dbeta = dbeta; a.d_init = d_init_state;
+  a.workspace = use_ws ? d->workspace : nullptr;
+  a.scale = resolve_scale(d);
+  const hipError_t e = kda::launch_chunk_bwd(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return KDA_OK;
+}
+
 }  // extern "C"

@@ -76,6 +76,37 @@ hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream);
 bool twopass_supported(const ChunkLaunch& a);
 size_t twopass_workspace_bytes(int num_seqs, int seq_len, int num_heads, bool packed);
 
+// Arguments of one reverse-mode launch of the chunked prefill; shapes
+// already validated.  Gradients are fp32 and laid out like their inputs.
+struct BwdLaunch {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* log_g;
+  const float* beta;
+  const float* init_state;    // may be null (zeros)
+  const int32_t* cu_seqlens;  // may be null (dense)
+  const float* d_out;
+  const float* d_final;       // may be null (zeros)
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dlog_g;
+  float* dbeta;
+  float* d_init;              // may be null (not written)
+  void* workspace;            // caller scratch (already checked to be large enough)
+  int num_seqs;
+  int seq_len;
+  int num_heads;
+  int d;
+  bool bf16;
+  float scale;
+};
+
+hipError_t launch_chunk_bwd(const BwdLaunch& a, hipStream_t stream);
+bool bwd_supported(const BwdLaunch& a);
+size_t bwd_workspace_bytes(int num_seqs, int seq_len, int num_heads, int d, bool packed);
+
 // Longest-first order of the documents of a packed problem (n <= 4096).
 hipError_t launch_doc_order(const int32_t* cu_seqlens, int n, int32_t* order, hipStream_t stream);
 

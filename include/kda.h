@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum {
   KDA_OK = 0,
@@ -181,6 +181,43 @@ kda_status kda_step_commit(const kda_desc* desc, const void* k,
                            const float* log_g, const float* deltas,
                            const int32_t* accept, float* state_inout,
                            int32_t n_tok, void* stream);
+
+/*
+ * Reverse mode of kda_chunk_fwd (training): gradients of the scalar loss
+ *
+ *     L = sum(d_out * out) + sum(d_final_state * final_state)
+ *
+ * with respect to q, k, v, log_g, beta and init_state, for the same problem
+ * (NeMo glm5_next.layers: `_torch_recurrent_kda` is documented as the
+ * differentiable reference of this recurrence, and the layer is trained with
+ * FSDP).  Inputs are exactly those of kda_chunk_fwd (same shapes, dtypes,
+ * dense or packed, init_state NULL = zeros), plus
+ *
+ *   d_out          [B, T, H, dv] fp32, required when there are tokens
+ *   d_final_state  [N, H, dk, dv] fp32, or NULL (the final state does not
+ *                  enter the loss)
+ *
+ * Outputs, all fp32 whatever qkv_dtype is, laid out like their inputs:
+ *   dq, dk, dlog_g [B, T, H, dk];  dv [B, T, H, dv];  dbeta [B, T, H]
+ *   d_init_state   [N, H, dk, dv], or NULL to skip (zero-length documents
+ *                  pass d_final_state through unchanged)
+ * No output may alias an input or another output.  Everything is computed
+ * in fp32 (fp32 matrix-core products, fp32 state); the forward is recomputed
+ * inside the call, so out and final_state are not inputs.
+ *
+ * desc->workspace must hold kda_chunk_bwd_workspace_bytes(desc, packed)
+ * bytes whenever there are tokens or the problem is packed: about 400 KiB
+ * per 64-token chunk and head at d = 128 (chunk entry states and their
+ * gradients, per-chunk operands).  Its contents on entry do not matter.
+ * Same status codes and preconditions as kda_chunk_fwd.
+ */
+size_t kda_chunk_bwd_workspace_bytes(const kda_desc* desc, int packed);
+kda_status kda_chunk_bwd(const kda_desc* desc, const void* q, const void* k,
+                         const void* v, const float* log_g, const float* beta,
+                         const float* init_state, const int32_t* cu_seqlens,
+                         const float* d_out, const float* d_final_state,
+                         float* dq, float* dk, float* dv, float* dlog_g,
+                         float* dbeta, float* d_init_state, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,8 @@ gate normal, the beta normal, the initial-state normal.
     reaches the total; the last one is truncated.
 Layouts: q, k, log_g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H];
 init_state [N, H, dk, dv]; cu_seqlens int32 [N+1].
+Upstream gradients of the backward (their own stream, ``upstream_grads``):
+d_out ~ N(0, 1) like out, d_final ~ N(0, 1) like the state.
 """
 from __future__ import annotations
 
@@ -114,6 +116,20 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
         cu_seqlens=torch.from_numpy(cu.astype(np.int32)) if cu is not None else None,
         scale=dk ** -0.5, dtype=dtype, N=N,
     )
+
+
+def upstream_grads(inp: dict, seed: int, final: bool = True, final_std: float = 1.0) -> dict:
+    """Seeded upstream gradients for a workload drawn by ``make_inputs``:
+    d_out ~ N(0, 1) shaped like out [B, T, H, dv] and, when ``final``,
+    d_final ~ N(0, final_std^2) shaped like the state [N, H, dk, dv] (fp32)."""
+    rng = np.random.default_rng(seed)
+    B, T, H, dk = inp["q"].shape
+    dv = inp["v"].shape[-1]
+    d_out = rng.standard_normal((B, T, H, dv), dtype=np.float32)
+    d_final = None
+    if final:
+        d_final = rng.standard_normal((inp["N"], H, dk, dv), dtype=np.float32) * np.float32(final_std)
+    return dict(d_out=torch.from_numpy(d_out), d_final=torch.from_numpy(d_final) if final else None)
 
 
 def config(name: str, **overrides) -> dict:

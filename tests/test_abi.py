@@ -29,15 +29,16 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert {"kda_chunk_fwd", "kda_step", "kda_step_rows", "kda_step_commit", "kda_chunk_workspace_bytes",
-            "kda_status_string", "kda_last_error", "kda_abi_version"} <= set(names)
+    assert {"kda_chunk_fwd", "kda_chunk_bwd", "kda_chunk_bwd_workspace_bytes", "kda_step", "kda_step_rows",
+            "kda_step_commit", "kda_chunk_workspace_bytes", "kda_status_string", "kda_last_error",
+            "kda_abi_version"} <= set(names)
     raw = ctypes.CDLL(kda.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), f"{n} declared in kda.h but not exported"
 
 
 def test_abi_version_and_status_strings():
-    assert kda.abi_version() == 3
+    assert kda.abi_version() == 4
     seen = set()
     for code in range(8):
         s = lib.kda_status_string(code).decode()
@@ -240,3 +241,63 @@ def test_rows_and_commit_validate_like_step():
 def test_rows_and_commit_of_no_sequences_are_noops():
     assert rows(desc(num_seqs=0), q=None, k=None, v=None, g=None, b=None, s=None, out=None, dl=None) == OK
     assert commit(desc(num_seqs=0), k=None, g=None, dl=None, acc=None, s=None) == OK
+
+
+# --------------------------------------------------------------------------- kda_chunk_bwd
+BWD_IN = ["q", "k", "v", "log_g", "beta", "s0", "cu", "d_out", "d_final"]
+BWD_OUT = ["dq", "dk", "dv", "dlog_g", "dbeta", "d_init"]
+
+
+def bwd(d, **kw):
+    ptrs = {n: P(i << 20) for i, n in enumerate(["q", "k", "v", "log_g", "beta", "d_out"])}
+    ptrs.update({n: P((10 + i) << 20) for i, n in enumerate(BWD_OUT)})
+    ptrs.update({"s0": None, "cu": None, "d_final": None})
+    ptrs.update(kw)
+    return lib.kda_chunk_bwd(ctypes.byref(d) if d is not None else None,
+                             *[ptrs[n] for n in BWD_IN + BWD_OUT], None)
+
+
+def bwd_desc(**kw):
+    d = desc(**kw)
+    need = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(d), int(kw.get("packed", 0)))
+    d.workspace, d.workspace_bytes = FAKE + (40 << 20), need
+    return d
+
+
+def test_bwd_workspace_size():
+    # dense 2 x 64 tokens, 4 heads, d = 128: 2 chunk slots x 4 heads, each
+    # 2 d*d + 6 C*d + 5 C*C + d floats
+    per = 2 * 128 * 128 + 6 * 64 * 128 + 5 * 64 * 64 + 128
+    d = desc()
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(d), 0) == 8 * per * 4
+    assert kda.bwd_workspace_bytes(2, 64, 4, 128, packed=False) == 8 * per * 4
+    assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(desc(dk=96, dv=96)), 0) == 0
+    assert lib.kda_chunk_bwd_workspace_bytes(None, 0) == 0
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "log_g", "beta", "d_out"] + BWD_OUT[:5])
+def test_bwd_required_pointers(name):
+    assert bwd(bwd_desc(), **{name: None}) == NULL
+    assert name in last()
+
+
+def test_bwd_rejects_aliasing_misalignment_and_missing_workspace():
+    d = bwd_desc()
+    assert bwd(d, dq=P(0)) == SHAPE and "alias" in last()          # dq aliases q
+    assert bwd(d, dv=P(10 << 20)) == SHAPE and "alias" in last()    # dv aliases dq
+    assert bwd(d, d_init=P(3)) == ALIGN
+    d.workspace_bytes -= 16
+    assert bwd(d) == WORKSPACE
+    d.workspace = None
+    assert bwd(d) == WORKSPACE
+    assert bwd(bwd_desc(dk=96, dv=96)) == UNSUPPORTED
+    assert bwd(None) == NULL
+
+
+def test_bwd_of_nothing_is_a_noop():
+    d = bwd_desc(num_seqs=0, seq_len=0)
+    nulls = {n: None for n in ["q", "k", "v", "log_g", "beta", "d_out"] + BWD_OUT}
+    assert bwd(d, **nulls) == OK
+    # dense sequences of no tokens, no d_init requested: nothing to do
+    d = bwd_desc(seq_len=0)
+    assert bwd(d, **nulls) == OK

@@ -1,0 +1,121 @@
+"""GPU parity of kda_chunk_bwd against the oracle's reverse mode.
+
+Every gradient (dq, dk, dv, dlog_g, dbeta, d_init_state) is compared element
+by element with the fp64 oracle on the same seeded inputs and upstream
+gradients, with the tolerance of the forward parity tests: max |gpu - oracle|
+/ rms(oracle) per tensor <= 1e-4 for fp32 q/k/v and 2e-2 for bf16 q/k/v (the
+backward computes in fp32 either way).  Cases span several 64-token chunks and
+a ragged tail, every supported head dim, packed documents with edge lengths,
+gates down to -inf, and sampled units of the dense 4 x 4096-token, 16-head
+workload at full size.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import oracle
+from gpu_helpers import TOL, err, oracle_threads, to_dev
+from kda_inputs import to_f64
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU, skipped there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import gated_delta_rule_67_amd as kda  # noqa: E402
+
+NAMES = ("dq", "dk", "dv", "dlog_g", "dbeta", "d_init_state")
+
+
+def oracle_bwd(inp, up, init=True):
+    cu = inp["cu_seqlens"].numpy().astype(np.int64) if inp["cu_seqlens"] is not None else None
+    return oracle.kda_backward(to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]), to_f64(inp["log_g"]),
+                               to_f64(inp["beta"]), init_state=to_f64(inp["init_state"]) if init else None,
+                               cu_seqlens=cu, scale=inp["scale"], d_out=to_f64(up["d_out"]),
+                               d_final=to_f64(up["d_final"]), n_threads=oracle_threads())
+
+
+def gpu_bwd(inp, up, init=True):
+    d = to_dev(inp)
+    g = kda.chunk_bwd(d["q"], d["k"], d["v"], d["log_g"], d["beta"], up["d_out"].cuda(),
+                      init_state=d["init_state"] if init else None, cu_seqlens=d["cu_seqlens"],
+                      d_final=up["d_final"].cuda() if up["d_final"] is not None else None, scale=inp["scale"])
+    torch.cuda.synchronize()
+    return {n: g[n].cpu().numpy() for n in NAMES}
+
+
+def check(tag, got, ref, tol):
+    worst = 0.0
+    for n in NAMES:
+        e = err(got[n], ref[n])
+        worst = max(worst, e)
+        print(f"[{tag}] {n} {e:.2e}", flush=True)
+        assert e <= tol, (tag, n, e)
+    return worst
+
+
+@pytest.mark.parametrize("dtype,d,B,T,H", [("f32", 32, 2, 150, 2), ("bf16", 128, 2, 200, 2),
+                                            ("f32", 16, 1, 64, 3), ("f32", 64, 1, 129, 2),
+                                            ("f32", 128, 1, 70, 1)])
+def test_dense_ragged(dtype, d, B, T, H):
+    inp = kda_inputs.make_inputs(B=B, T=T, H=H, dk=d, dv=d, dtype=dtype, seed=100 + d + T,
+                                 init="normal", init_std=0.05)
+    up = kda_inputs.upstream_grads(inp, seed=200 + d)
+    check(f"dense {dtype} d={d} B={B} T={T}", gpu_bwd(inp, up), oracle_bwd(inp, up), TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_packed_edge_lengths(dtype):
+    lens = [0, 1, 63, 64, 65, 0, 130, 7]
+    inp = kda_inputs.make_inputs(B=1, T=sum(lens), H=2, dk=64, dv=64, dtype=dtype, seed=110, lengths=lens,
+                                 init="normal", init_std=0.05)
+    up = kda_inputs.upstream_grads(inp, seed=210)
+    got, ref = gpu_bwd(inp, up), oracle_bwd(inp, up)
+    check(f"packed {dtype}", got, ref, TOL[dtype])
+    # empty documents pass d_final straight through
+    for n in (0, 5):
+        np.testing.assert_array_equal(got["d_init_state"][n], up["d_final"][n].numpy())
+
+
+def test_no_initial_state_and_no_final_gradient():
+    inp = kda_inputs.make_inputs(B=2, T=100, H=2, dk=32, dv=32, dtype="f32", seed=120, init="zeros")
+    up = kda_inputs.upstream_grads(inp, seed=220, final=False)
+    check("zeros", gpu_bwd(inp, up, init=False), oracle_bwd(inp, up, init=False), TOL["f32"])
+
+
+@pytest.mark.parametrize("mode", ["uniform", "erase"])
+def test_extreme_gates(mode):
+    """Gates uniform in [-20, 0], and every fifth token erasing the state
+    (log_g = -inf): no factor of the chunk form may overflow or lose the
+    gradient of the tokens it separates."""
+    inp = kda_inputs.make_inputs(B=1, T=160, H=2, dk=32, dv=32, dtype="f32", seed=130, init="normal",
+                                 init_std=0.1)
+    rng = np.random.default_rng(131)
+    g = rng.uniform(-20.0, 0.0, inp["log_g"].shape).astype(np.float32)
+    if mode == "erase":
+        g = inp["log_g"].numpy().copy()
+        g[:, ::5] = -np.inf
+    inp["log_g"] = torch.from_numpy(g)
+    up = kda_inputs.upstream_grads(inp, seed=230)
+    got, ref = gpu_bwd(inp, up), oracle_bwd(inp, up)
+    check(f"gates {mode}", got, ref, TOL["f32"])
+
+
+def test_full_size_dense_workload_sampled_units():
+    """The dense 4 x 4096-token, 16-head, d = 128 workload (bf16) at full size,
+    in the launch configuration the benchmark times; the oracle checks every
+    gradient of three sampled (sequence, head) units."""
+    inp = kda_inputs.config("prefill")
+    up = kda_inputs.upstream_grads(inp, seed=240)
+    got = gpu_bwd(inp, up)
+    for n, h in [(0, 0), (2, 7), (3, 15)]:
+        sl = lambda t: t[n:n + 1, :, h:h + 1]
+        unit = dict(q=sl(inp["q"]), k=sl(inp["k"]), v=sl(inp["v"]), log_g=sl(inp["log_g"]),
+                    beta=inp["beta"][n:n + 1, :, h:h + 1], init_state=inp["init_state"][n:n + 1, h:h + 1],
+                    cu_seqlens=None, scale=inp["scale"])
+        uup = dict(d_out=sl(up["d_out"]), d_final=up["d_final"][n:n + 1, h:h + 1])
+        ref = oracle_bwd(unit, uup)
+        mine = {nm: (got[nm][n:n + 1, h:h + 1] if nm == "d_init_state" else
+                     got[nm][n:n + 1, :, h:h + 1]) for nm in NAMES}
+        check(f"full-size unit ({n},{h})", mine, ref, TOL["bf16"])
