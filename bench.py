@@ -1,7 +1,7 @@
 """Benchmark of libkda on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --only {prefill,step,copy}      (profiling runs)
+    python bench.py --only {prefill,varlen,step,backward,copy}      (profiling runs)
     python bench.py --traffic-from FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
 
 A step is one kda_chunk_fwd call (chunked prefill) over the dense workload
@@ -14,6 +14,8 @@ fp32 out, with inputs resident in HBM.  ``value`` is prefill tokens/s
                 16-bit MFMA peak
   varlen        the packed 65536-token, 32-head prefill: tokens/s and its own
                 HBM roofline (beside the headline, not part of it)
+  backward      kda_chunk_bwd on the dense workload: tokens/s and its roofline
+                against the 157.3 TFLOP/s fp32 peak (it computes in fp32)
   verify_rollback  the 64 x 4-row verify split into kda_step_rows (state read
                 only) and kda_step_commit, each with its own HBM roofline
   decode/verify kda_step GB/s on 256 x 1 and 64 x 4 rows, H=32, d=128, each
@@ -53,6 +55,7 @@ import kda_inputs  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_PEAK_TFLOPS = 2516.6      # MI355X dense fp16/bf16 MFMA, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (matrix and vector), TFLOP/s
 CHUNK = 64
 COPY_BYTES = 512 << 20         # calibration copy: bytes read (= bytes written)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_dense.txt")
@@ -140,6 +143,25 @@ def step_bytes(N: int, n_tok: int, H: int, d: int, qkv_bytes=2) -> int:
     return N * H * 2 * d * d * 4 + N * n_tok * H * per_token_head
 
 
+def backward_bytes(tokens: int, H: int, d: int, n_states: int, qkv_bytes=2) -> int:
+    """Algorithmic HBM bytes of one kda_chunk_bwd call: q, k, v, log_g, beta
+    and d_out in; dq, dk, dv, dlog_g (fp32) and dbeta out; per unit the
+    initial state and d_final in, d_init_state out."""
+    per_token_head = 3 * d * qkv_bytes + d * 4 + 4 + d * 4 + 4 * d * 4 + 4
+    return tokens * H * per_token_head + 3 * n_states * H * d * d * 4
+
+
+def backward_flops(tokens: int, H: int, d: int) -> int:
+    """Algorithmic FLOP of the chunk-form reverse mode per token-head, 2 x the
+    multiply-adds per 64-token chunk divided by 64: C^3/6 (the triangular
+    inverse) + 6 C^2 d (pair matrices, W and U, the triangular products of the
+    two scans and of the gradients) + 8 C d^2 (the C x d x d products: two in
+    the forward scan, three in the reverse scan, three in the gradients)."""
+    C = CHUNK
+    macs_per_chunk = C ** 3 // 6 + 6 * C * C * d + 8 * C * d * d
+    return tokens * H * 2 * macs_per_chunk // C
+
+
 SETTLE_S = 0.2  # untimed sustained load before the warm-up steps
 
 
@@ -224,6 +246,39 @@ def bench_varlen(kda, steps, warmup):
             "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
             "algorithmic_bytes": nbytes}
+
+
+def bench_backward(kda, steps, warmup):
+    """kda_chunk_bwd on the dense prefill workload (4 x 4096 tokens, H = 16,
+    d = 128, bf16 q/k/v) with seeded upstream gradients, timed like the
+    prefill (back-to-back calls, HIP events per call).  The backward computes
+    in fp32 on the matrix cores, so its roofline is the fp32 peak."""
+    inp = kda_inputs.config("prefill")
+    up = kda_inputs.upstream_grads(inp, seed=240)
+    d = to_dev(inp)
+    B, T, H, D = inp["q"].shape
+    do, dfin = up["d_out"].cuda(), up["d_final"].cuda()
+    ws = torch.empty(kda.bwd_workspace_bytes(B, T, H, D, False), dtype=torch.uint8, device="cuda")
+    grads = kda.chunk_bwd(d["q"], d["k"], d["v"], d["log_g"], d["beta"], do, init_state=d["init_state"],
+                          d_final=dfin, workspace=ws)
+
+    def call():
+        kda.chunk_bwd(d["q"], d["k"], d["v"], d["log_g"], d["beta"], do, init_state=d["init_state"], d_final=dfin,
+                      grads=grads, workspace=ws)
+
+    wall, ms = timed_calls(call, steps, warmup)
+    avg = float(np.mean(ms))
+    tokens = B * T
+    fl, nb = backward_flops(tokens, H, D), backward_bytes(tokens, H, D, n_states=B)
+    tf = fl / (avg * 1e-3) / 1e12
+    return {"workload": f"dense backward, {B} x {T} tokens, H={H}, dk=dv={D}, bf16 q/k/v, fp32 gradients, "
+                        "seeded d_out and d_final",
+            "tokens_per_s": round(tokens / (wall / steps), 1), "us_per_call": round(avg * 1e3, 2),
+            "algorithmic_flops": fl, "algorithmic_bytes": nb,
+            "hbm_gbs": round(nb / (avg * 1e-3) / 1e9, 1),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tf / FP32_PEAK_TFLOPS, 4), "traffic": None},
+            "workspace_bytes": int(ws.numel())}
 
 
 def bench_step(kda, name, steps, warmup):
@@ -400,7 +455,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "varlen", "step", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "varlen", "step", "backward", "copy"], default="all",
                     help="restrict the run (profiling); the JSON line needs 'all'")
     ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
                     help="rocprofv3 csv dirs: prefill FETCH_SIZE, prefill WRITE_SIZE, copy FETCH_SIZE, "
@@ -439,6 +494,9 @@ def main():
     if args.only in ("all", "varlen"):
         res["varlen"] = bench_varlen(kda, args.steps, args.warmup)
         print(f"varlen prefill: {res['varlen']['us_per_call']} us/call", file=sys.stderr, flush=True)
+    if args.only in ("all", "backward"):
+        res["backward"] = bench_backward(kda, args.steps, args.warmup)
+        print(f"backward {res['backward']['us_per_call']} us per call", file=sys.stderr, flush=True)
     if args.only in ("all", "step"):
         res["decode"] = bench_step(kda, "decode", args.steps, args.warmup)
         res["verify"] = bench_step(kda, "verify", args.steps, args.warmup)
@@ -483,6 +541,7 @@ def main():
         "decode": res["decode"],
         "verify": res["verify"],
         "verify_rollback": res["verify_rollback"],
+        "backward": res["backward"],
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p["inp"])

@@ -134,34 +134,56 @@ __device__ __forceinline__ void unit_chunks(const BwdArgs& a, int n, int& first,
 }
 
 // C rows of a [tokens, H, D] tensor into LDS (row stride LD), rows >= count zero.
+// (The staging helpers run a compile-time number of iterations so that all of
+// a thread's loads are in flight before its LDS stores.)
 template <int D, int LD, typename In, int NTH = NT>
 __device__ __forceinline__ void load_rows(float* dst, const In* src, int64_t tok0, int count, int H, int h) {
-  constexpr int G = D / 4;
-  for (int idx = threadIdx.x; idx < C * G; idx += NTH) {
-    const int t = idx / G, g4 = idx - t * G;
-    float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < count) x = load4(src + ((tok0 + t) * H + h) * D + 4 * g4);
-    *reinterpret_cast<float4*>(dst + t * LD + 4 * g4) = x;
+  constexpr int G = D / 4, N = C * G, IT = (N + NTH - 1) / NTH;
+  float4 x[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
+    x[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (idx < N && t < count) x[it] = load4(src + ((tok0 + t) * H + h) * D + 4 * g4);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
+    if (idx < N) *reinterpret_cast<float4*>(dst + t * LD + 4 * g4) = x[it];
   }
 }
 
 // A dense rows x cols fp32 matrix (contiguous) into LDS with row stride LD.
 template <int ROWS, int COLS, int LD, int NTH = NT>
 __device__ __forceinline__ void load_mat(float* dst, const float* src) {
-  constexpr int G = COLS / 4;
-  for (int idx = threadIdx.x; idx < ROWS * G; idx += NTH) {
-    const int t = idx / G, g4 = idx - t * G;
-    *reinterpret_cast<float4*>(dst + t * LD + 4 * g4) = load4(src + t * COLS + 4 * g4);
+  constexpr int G = COLS / 4, N = ROWS * G, IT = (N + NTH - 1) / NTH;
+  float4 x[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTH + threadIdx.x;
+    if (idx < N) x[it] = load4(src + idx * 4);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
+    if (idx < N) *reinterpret_cast<float4*>(dst + t * LD + 4 * g4) = x[it];
   }
 }
 
 // Columns [c0, c0 + COLS) of a dense rows x LDG matrix into LDS (stride LD).
 template <int ROWS, int COLS, int LD>
 __device__ __forceinline__ void load_cols(float* dst, const float* src, int ldg, int c0) {
-  constexpr int G = COLS / 4;
-  for (int idx = threadIdx.x; idx < ROWS * G; idx += NT) {
-    const int t = idx / G, g4 = idx - t * G;
-    *reinterpret_cast<float4*>(dst + t * LD + 4 * g4) = load4(src + static_cast<int64_t>(t) * ldg + c0 + 4 * g4);
+  constexpr int G = COLS / 4, N = ROWS * G, IT = (N + NT - 1) / NT;
+  float4 x[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NT + threadIdx.x, t = idx / G, g4 = idx - t * G;
+    if (idx < N) x[it] = load4(src + static_cast<int64_t>(t) * ldg + c0 + 4 * g4);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NT + threadIdx.x, t = idx / G, g4 = idx - t * G;
+    if (idx < N) *reinterpret_cast<float4*>(dst + t * LD + 4 * g4) = x[it];
   }
 }
 
@@ -669,19 +691,21 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
   }
   load_mat<C, C, LM>(sT, a.Tm + sh * C * C);
   load_mat<C, D, LD>(sX, a.dDl + sh * C * D);
+  load_rows<D, LD>(sR, a.log_g, L.tok0, L.count, H, h);  // log_g rows (0 past the end)
+  __syncthreads();
   // per channel: b_t into sR, r(C-1, t) into sS (staging), b_C into sEg
   for (int i = tid; i < D; i += NT) {
-    float b = 1.f;
-    for (int t = 0; t < C; ++t) {
-      b *= t < L.count ? exp_fast(a.log_g[row(t) * D + i]) : 1.f;
-      sR[t * LD + i] = b;
-    }
-    sEg[i] = b;
     float rr = 1.f;
     for (int t = C - 1; t >= 0; --t) {
       sS[t * LD + i] = rr;
-      rr *= t < L.count ? exp_fast(a.log_g[row(t) * D + i]) : 1.f;
+      rr *= exp_fast(sR[t * LD + i]);
     }
+    float b = 1.f;
+    for (int t = 0; t < C; ++t) {
+      b *= exp_fast(sR[t * LD + i]);
+      sR[t * LD + i] = b;
+    }
+    sEg[i] = b;
   }
   __syncthreads();
   float bb[NCT][4], rc[NCT][4], kv[NCT][4];
@@ -770,15 +794,24 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
       dg_[ct][j] += dqb * qv * bb[ct][j];
     }
   }
-  // b_C sum_j dS'[i, j] S[i, j]
-  for (int i = tid; i < D; i += NT) {
-    const float* g = a.dSo + sh * D * D + static_cast<size_t>(i) * D;
-    float acc = 0.f;
-    for (int jj = 0; jj < D; jj += 4) {
-      const float4 x = load4(g + jj);
-      acc += x.x * sS[i * LD + jj] + x.y * sS[i * LD + jj + 1] + x.z * sS[i * LD + jj + 2] + x.w * sS[i * LD + jj + 3];
+  // b_C sum_j dS'[i, j] S[i, j]: D / 4 consecutive threads per row, coalesced
+  {
+    constexpr int G = D / 4, N = D * G, IT = (N + NT - 1) / NT;
+    static_assert(G <= 64 && NT % G == 0 && (N >= NT || N % 64 == 0), "row groups must stay inside a wave");
+    float4 x[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it)
+      if (it * NT + tid < N) x[it] = load4(a.dSo + sh * D * D + static_cast<size_t>(it * NT + tid) * 4);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NT + tid, i = idx / G, jj = 4 * (idx - i * G);
+      if (idx >= N) continue;  // whole waves
+      const float* sr = sS + i * LD + jj;
+      float acc = x[it].x * sr[0] + x[it].y * sr[1] + x[it].z * sr[2] + x[it].w * sr[3];
+#pragma unroll
+      for (int o = 1; o < G; o <<= 1) acc += __shfl_xor(acc, o, 64);
+      if ((tid & (G - 1)) == 0) sGam[i] = sEg[i] * acc;
     }
-    sGam[i] = sEg[i] * acc;
   }
   __syncthreads();  // done with S
   load_mat<C, D, LD>(sS, a.Dl + sh * C * D);  // Delta, rows

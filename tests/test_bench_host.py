@@ -90,3 +90,14 @@ def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path, monk
     assert bench.read_traffic() is None
     f.unlink()
     assert bench.read_traffic() is None
+
+
+def test_backward_bytes_and_flops_of_the_dense_workload():
+    tokens, H, d = 4 * 4096, 16, 128
+    # q, k, v bf16, log_g, beta, d_out in; dq, dk, dv, dlog_g fp32 and dbeta out: 3848 B per
+    # token-head; init_state and d_final in, d_init_state out per unit
+    assert bench.backward_bytes(tokens, H, d, n_states=4) == tokens * H * 3848 + 3 * 4 * 16 * 65536
+    # per 64-token chunk: 64^3/6 + 6 * 64^2 * 128 + 8 * 64 * 128^2 multiply-adds
+    macs = 64 ** 3 // 6 + 6 * 64 * 64 * 128 + 8 * 64 * 128 * 128
+    assert macs == 11_578_026
+    assert bench.backward_flops(tokens, H, d) == tokens * H * 2 * macs // 64 == 94_847_188_992
