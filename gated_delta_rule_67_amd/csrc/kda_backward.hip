@@ -80,15 +80,17 @@ struct BwdArgs {
   float* Wm;    // C x D
   float* Um;    // C x D
   float* Kd;    // C x D
-  float* Qs;    // C x D   scale * q_t * b_t
+  float* QsT;   // D x C   (scale * q_t * b_t)^T
   float* Dl;    // C x D   Delta
   float* dDl;   // C x D   dDelta
-  float* As;    // C x C   scale * Aqk
+  float* AsT;   // C x C   (scale * Aqk)^T
   float* Tm;    // C x C
   float* Ab;    // C x C   Akk (strictly lower, beta not applied)
   float* dAq;   // C x C   dL/dAqk
   float* dAb;   // C x C   dL/dAkk
   float* eg;    // D       b_C
+  float* WT;    // D x C   W^T
+  float* KdT;   // D x C   Kd^T
   int N;
   int T;
   int H;
@@ -150,6 +152,30 @@ __device__ __forceinline__ void load_rows(float* dst, const In* src, int64_t tok
   for (int it = 0; it < IT; ++it) {
     const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
     if (idx < N) *reinterpret_cast<float4*>(dst + t * LD + 4 * g4) = x[it];
+  }
+}
+
+// C rows of a [tokens, H, D] tensor transposed into LDS: dst[i * LDT + t],
+// rows >= count zero.
+template <int D, int LDT, typename In, int NTH = NT>
+__device__ __forceinline__ void load_rows_t(float* dst, const In* src, int64_t tok0, int count, int H, int h) {
+  constexpr int G = D / 4, N = C * G, IT = (N + NTH - 1) / NTH;
+  float4 x[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
+    x[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (idx < N && t < count) x[it] = load4(src + ((tok0 + t) * H + h) * D + 4 * g4);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTH + threadIdx.x, t = idx / G, c = 4 * (idx - t * G);
+    if (idx < N) {
+      dst[(c + 0) * LDT + t] = x[it].x;
+      dst[(c + 1) * LDT + t] = x[it].y;
+      dst[(c + 2) * LDT + t] = x[it].z;
+      dst[(c + 3) * LDT + t] = x[it].w;
+    }
   }
 }
 
@@ -248,10 +274,10 @@ __device__ __forceinline__ f32x4 zero4f() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 template <int D>
 struct PrepL {
   static constexpr int LD = D + 4, LM = C + 4;
-  static constexpr int CD = C * LD, CM = C * LM;
-  static constexpr int R0 = 0;                          // K, later V
-  static constexpr int R1 = R0 + CD;                    // Q, later K*b
-  static constexpr int R2 = R1 + CD;                    // F, later Akk | Aqk
+  static constexpr int CD = C * LD, CM = C * LM, XT = (CD > D * LM ? CD : D * LM);
+  static constexpr int R0 = 0;                          // K rows, later V^T
+  static constexpr int R1 = R0 + XT;                    // Q rows, later (K*b)^T
+  static constexpr int R2 = R1 + XT;                    // F, later Akk | Aqk
   static constexpr int R3 = R2 + (CD > 2 * CM ? CD : 2 * CM);  // T
   static constexpr int R4 = R3 + CM;                    // 4 x 16 x 17 wave scratch
   static constexpr int RB = R4 + 4 * 16 * 17;           // beta [C]
@@ -293,16 +319,24 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
   if (chan) load_alpha<D>(al, a.log_g, L.tok0, L.count, a.H, h, ci, 32 * ph);
 
   f32x4 ab_d = zero4f(), aq_d = zero4f(), ab_0 = zero4f(), aq_0 = zero4f(), ab_1 = zero4f(), aq_1 = zero4f();
-  // product of one 16 x 16 tile (I, J) with factors
+  // product of one 16 x 16 tile (I, J) with factors; channels read as float4
+  // (k = k0 + 4 kq + m for the m-th MFMA, the same order on both sides)
   auto pair_tile = [&](int I, int J, f32x4& accK, f32x4& accQ) {
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const int kk = k0 + kq;
-      const int ts = (16 * J + r) * LD + kk, tt = (16 * I + r) * LD + kk;
-      const float ys = sK[ts] * sF[ts];
-      const float ft = sF[tt];
-      accK = mma(sK[tt] * ft, ys, accK);
-      accQ = mma(sQ[tt] * ft, ys, accQ);
+    const int tt = (16 * I + r) * LD + 4 * kq, ts = (16 * J + r) * LD + 4 * kq;
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const float4 ft = *reinterpret_cast<const float4*>(sF + tt + k0);
+      const float4 kt = *reinterpret_cast<const float4*>(sK + tt + k0);
+      const float4 qt = *reinterpret_cast<const float4*>(sQ + tt + k0);
+      const float4 fs = *reinterpret_cast<const float4*>(sF + ts + k0);
+      const float4 ks = *reinterpret_cast<const float4*>(sK + ts + k0);
+      accK = mma(kt.x * ft.x, ks.x * fs.x, accK);
+      accQ = mma(qt.x * ft.x, ks.x * fs.x, accQ);
+      accK = mma(kt.y * ft.y, ks.y * fs.y, accK);
+      accQ = mma(qt.y * ft.y, ks.y * fs.y, accQ);
+      accK = mma(kt.z * ft.z, ks.z * fs.z, accK);
+      accQ = mma(qt.z * ft.z, ks.z * fs.z, accQ);
+      accK = mma(kt.w * ft.w, ks.w * fs.w, accK);
+      accQ = mma(qt.w * ft.w, ks.w * fs.w, accQ);
     }
   };
 #pragma unroll
@@ -337,10 +371,14 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
   // diagonal of Aqk: r(t, t) = 1
   {
     f32x4 tq = zero4f();
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const int kk = k0 + kq;
-      tq = mma(sQ[(16 * w + r) * LD + kk], sK[(16 * w + r) * LD + kk], tq);
+    const int tt = (16 * w + r) * LD + 4 * kq;
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const float4 qt = *reinterpret_cast<const float4*>(sQ + tt + k0);
+      const float4 kt = *reinterpret_cast<const float4*>(sK + tt + k0);
+      tq = mma(qt.x, kt.x, tq);
+      tq = mma(qt.y, kt.y, tq);
+      tq = mma(qt.z, kt.z, tq);
+      tq = mma(qt.w, kt.w, tq);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) aq_d[j] += (4 * kq + j == r) ? tq[j] : 0.f;
@@ -368,13 +406,14 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
     sTot[ph * D + ci] = p;
   }
   __syncthreads();
-  // Akk and scale * Aqk to the workspace
+  // Akk and (scale * Aqk)^T to the workspace
   for (int idx = tid; idx < C * C; idx += NT) {
     const int t = idx / C, s = idx - t * C;
     a.Ab[sh * C * C + idx] = sAb[t * LM + s];
-    a.As[sh * C * C + idx] = a.scale * sAq[t * LM + s];
+    a.AsT[sh * C * C + idx] = a.scale * sAq[s * LM + t];
   }
-  // per channel: b_t (prefix), Qs = scale q b, K*b (in place of Q), Kd = k r(C-1, t), b_C
+  // per channel: b_t (prefix), Qs = scale q b, K*b (kept), Kd = k r(C-1, t), b_C
+  float kb[32];
   if (chan) {
     float b = ph == 1 ? sTot[ci] : 1.f;
 #pragma unroll
@@ -382,21 +421,30 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
       const int t = 32 * ph + u;
       b *= al[u];
       const float qv = sQ[t * LD + ci];
-      a.Qs[(sh * C + t) * D + ci] = a.scale * qv * b;
-      sQ[t * LD + ci] = sK[t * LD + ci] * b;
+      a.QsT[(sh * D + ci) * C + t] = a.scale * qv * b;
+      kb[u] = sK[t * LD + ci] * b;
     }
     if (ph == 1) a.eg[sh * D + ci] = b;
     float rr = ph == 0 ? sTot[D + ci] : 1.f;
 #pragma unroll
     for (int u = 31; u >= 0; --u) {
       const int t = 32 * ph + u;
-      a.Kd[(sh * C + t) * D + ci] = sK[t * LD + ci] * rr;
+      const float kd = sK[t * LD + ci] * rr;
+      a.Kd[(sh * C + t) * D + ci] = kd;
+      a.KdT[(sh * D + ci) * C + t] = kd;
       rr *= al[u];
     }
   }
   for (int idx = tid; idx < P::CM; idx += NT) sT[idx] = 0.f;
-  __syncthreads();  // K no longer needed; T zeroed
-  load_rows<D, LD>(sK, v, L.tok0, L.count, a.H, h);  // V
+  __syncthreads();  // K and Q no longer needed; T zeroed
+  float* sKbT = sQ;  // (K*b)^T [i][t]
+  float* sVT = sK;   // V^T [i][t]
+  if (chan) {
+#pragma unroll
+    for (int u = 0; u < 32; u += 4)
+      *reinterpret_cast<float4*>(sKbT + ci * LM + 32 * ph + u) = make_float4(kb[u], kb[u + 1], kb[u + 2], kb[u + 3]);
+  }
+  load_rows_t<D, LM>(sVT, v, L.tok0, L.count, a.H, h);
   // T = (I + diag(beta) Akk)^-1: diagonal 16 x 16 blocks by forward substitution
   if (tid < 64) {
     const int I = tid >> 4, c = tid & 15;
@@ -447,51 +495,165 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
     const int t = idx / C, s = idx - t * C;
     a.Tm[sh * C * C + idx] = sT[t * LM + s];
   }
-  // W = T diag(beta) (K*b), U = T diag(beta) V; T is lower triangular
+  // W = T diag(beta) (K*b), U = T diag(beta) V; T is lower triangular, so
+  // rows [16w, 16w + 16) contract over s < 16 (w + 1)
+  constexpr int NCT = D / 16, NB = NCT < 4 ? NCT : 4;
   const int kend = 16 * (w + 1);
-  for (int ct = 0; ct < D / 16; ++ct) {
-    f32x4 accW = zero4f(), accU = zero4f();
-    for (int k0 = 0; k0 < kend; k0 += 4) {
-      const int s = k0 + kq;
-      const float tv = sT[(16 * w + r) * LM + s];
-      const float bs = sBeta[s];
-      accW = mma(tv, bs * sQ[s * LD + 16 * ct + r], accW);
-      accU = mma(tv, bs * sK[s * LD + 16 * ct + r], accU);
+#pragma unroll
+  for (int c0 = 0; c0 < NCT; c0 += NB) {
+    f32x4 accW[NB], accU[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) accW[n] = accU[n] = zero4f();
+    for (int k0 = 0; k0 < kend; k0 += 16) {
+      const float4 tv = *reinterpret_cast<const float4*>(sT + (16 * w + r) * LM + k0 + 4 * kq);
+      const float4 bs = *reinterpret_cast<const float4*>(sBeta + k0 + 4 * kq);
+      const float4 av = make_float4(tv.x * bs.x, tv.y * bs.y, tv.z * bs.z, tv.w * bs.w);
+      float4 bw[NB], bu[NB];
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        bw[n] = *reinterpret_cast<const float4*>(sKbT + (16 * (c0 + n) + r) * LM + k0 + 4 * kq);
+        bu[n] = *reinterpret_cast<const float4*>(sVT + (16 * (c0 + n) + r) * LM + k0 + 4 * kq);
+      }
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        accW[n] = mma(av.x, bw[n].x, accW[n]);
+        accU[n] = mma(av.x, bu[n].x, accU[n]);
+      }
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        accW[n] = mma(av.y, bw[n].y, accW[n]);
+        accU[n] = mma(av.y, bu[n].y, accU[n]);
+      }
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        accW[n] = mma(av.z, bw[n].z, accW[n]);
+        accU[n] = mma(av.z, bu[n].z, accU[n]);
+      }
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        accW[n] = mma(av.w, bw[n].w, accW[n]);
+        accU[n] = mma(av.w, bu[n].w, accU[n]);
+      }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 16 * w + 4 * kq + j;
-      a.Wm[(sh * C + t) * D + 16 * ct + r] = accW[j];
-      a.Um[(sh * C + t) * D + 16 * ct + r] = accU[j];
+    for (int n = 0; n < NB; ++n) {
+      const int i = 16 * (c0 + n) + r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * w + 4 * kq + j;
+        a.Wm[(sh * C + t) * D + i] = accW[n][j];
+        a.Um[(sh * C + t) * D + i] = accU[n][j];
+      }
+      *reinterpret_cast<float4*>(a.WT + (sh * D + i) * C + 16 * w + 4 * kq) =
+          make_float4(accW[n][0], accW[n][1], accW[n][2], accW[n][3]);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// bwd_fscan: per (unit, value-column tile), serially over the unit's chunks.
+// Scans: per (unit, 32-column value tile), serially over the unit's chunks.
+// The state (or state-gradient) tile lives in LDS transposed, [column][i], so
+// that every product reads both operands along the contraction index; the
+// next chunk's operands are loaded into registers while the current chunk is
+// computed.
 template <int D>
 struct ScanL {
   static constexpr int DVT = D < 32 ? D : 32;
   static constexpr int NTILE = D / DVT;
-  static constexpr int LD = D + 4, LV = DVT + 4, LM = C + 4;
-  // forward: state tile, W, Kd, U tile, Delta tile, b_C
-  static constexpr int FS = 0, FW = FS + D * LV, FK = FW + C * LD, FU = FK + C * LD, FX = FU + C * LV,
-                       FG = FX + C * LV, F_FLOATS = FG + D;
-  // reverse: dS tile, Kd, Qs, W, dO tile, dDelta tile, b_C, As
-  static constexpr int RS = 0, RK = RS + D * LV, RQ = RK + C * LD, RW = RQ + C * LD, RO = RW + C * LD,
-                       RX = RO + C * LV, RG = RX + C * LV, RM = RG + D, R_FLOATS = RM + C * LM;
+  static constexpr int NBC = DVT / 16;  // 16-column blocks per tile
+  static constexpr int LD = D + 4, LM = C + 4, LV = DVT + 4;
+  // forward: S^T tile, W rows, Kd^T rows, U tile, Delta^T tile, b_C
+  static constexpr int FS = 0, FW = FS + DVT * LD, FK = FW + C * LD, FU = FK + D * LM, FX = FU + C * LV,
+                       FG = FX + DVT * LM, F_FLOATS = FG + D;
+  // reverse: dS^T tile, As^T rows, Kd rows, Qs^T rows, W^T rows, dO^T tile, dDelta^T tile, b_C
+  static constexpr int RS = 0, RA = RS + DVT * LD, RK = RA + C * LM, RQ = RK + C * LD, RW = RQ + D * LM,
+                       RO = RW + D * LM, RX = RO + DVT * LM, RG = RX + DVT * LM, R_FLOATS = RG + D;
 };
 
+// Registers holding one ROWS x COLS block of a row-major global matrix
+// (leading dimension ldg, first column c0) on its way to LDS.
+template <int ROWS, int COLS>
+struct Staged {
+  static constexpr int G = COLS / 4, N = ROWS * G, IT = (N + NT - 1) / NT;
+  float4 x[IT];
+  __device__ __forceinline__ void load(const float* src, int ldg, int c0, int valid_rows = ROWS) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NT + threadIdx.x, t = idx / G, g4 = idx - t * G;
+      x[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (idx < N && t < valid_rows) x[it] = load4(src + static_cast<int64_t>(t) * ldg + c0 + 4 * g4);
+    }
+  }
+  // rows of tokens of a [tokens, H, D] tensor (rows >= valid_rows zero)
+  __device__ __forceinline__ void load_tokens(const float* src, int64_t tok0, int H, int h, int D, int c0,
+                                              int valid_rows) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NT + threadIdx.x, t = idx / G, g4 = idx - t * G;
+      x[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (idx < N && t < valid_rows) x[it] = load4(src + ((tok0 + t) * H + h) * D + c0 + 4 * g4);
+    }
+  }
+  __device__ __forceinline__ void store(float* dst, int ld) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NT + threadIdx.x, t = idx / G, g4 = idx - t * G;
+      if (idx < N) *reinterpret_cast<float4*>(dst + t * ld + 4 * g4) = x[it];
+    }
+  }
+  __device__ __forceinline__ void store_t(float* dst, int ldt) const {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NT + threadIdx.x, t = idx / G, c = 4 * (idx - t * G);
+      if (idx < N) {
+        dst[(c + 0) * ldt + t] = x[it].x;
+        dst[(c + 1) * ldt + t] = x[it].y;
+        dst[(c + 2) * ldt + t] = x[it].z;
+        dst[(c + 3) * ldt + t] = x[it].w;
+      }
+    }
+  }
+};
+
+// A D x DVT tile kept transposed in LDS (tT[col * LD + i]) to or from the
+// row-major D x D global matrix g at columns [c0, c0 + DVT).
+template <int D, int DVT, int LD>
+__device__ __forceinline__ void tile_to_global(float* g, int c0, const float* tT) {
+  constexpr int G = DVT / 4;
+  for (int idx = threadIdx.x; idx < D * G; idx += NT) {
+    const int i = idx / G, c = 4 * (idx - i * G);
+    *reinterpret_cast<float4*>(g + static_cast<size_t>(i) * D + c0 + c) =
+        make_float4(tT[c * LD + i], tT[(c + 1) * LD + i], tT[(c + 2) * LD + i], tT[(c + 3) * LD + i]);
+  }
+}
+template <int D, int DVT, int LD>
+__device__ __forceinline__ void tile_from_global(float* tT, const float* g, int c0) {
+  constexpr int G = DVT / 4;
+  for (int idx = threadIdx.x; idx < D * G; idx += NT) {
+    const int i = idx / G, c = 4 * (idx - i * G);
+    const float4 x = g ? load4(g + static_cast<size_t>(i) * D + c0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    tT[c * LD + i] = x.x;
+    tT[(c + 1) * LD + i] = x.y;
+    tT[(c + 2) * LD + i] = x.z;
+    tT[(c + 3) * LD + i] = x.w;
+  }
+}
+
+template <int NB>
+__device__ __forceinline__ void mm_kc(f32x4 (&acc)[NB], const float* A, int lda, const float* Bt, int ldb, int k_lo,
+                                      int k_hi);
+
+// bwd_fscan: entry state of every chunk, and Delta = U - W S.
 template <int D>
 __global__ void __launch_bounds__(NT) bwd_fscan(BwdArgs a) {
   using P = ScanL<D>;
-  constexpr int DVT = P::DVT, LD = P::LD, LV = P::LV;
+  constexpr int DVT = P::DVT, NBC = P::NBC, LD = P::LD, LM = P::LM, LV = P::LV;
   extern __shared__ __align__(16) float sm[];
-  float* sS = sm + P::FS;
+  float* sST = sm + P::FS;
   float* sW = sm + P::FW;
-  float* sKd = sm + P::FK;
+  float* sKT = sm + P::FK;
   float* sU = sm + P::FU;
-  float* sX = sm + P::FX;
+  float* sXT = sm + P::FX;
   float* sG = sm + P::FG;
 
   const int unit = blockIdx.x / P::NTILE, tile = blockIdx.x - unit * P::NTILE;
@@ -501,70 +663,79 @@ __global__ void __launch_bounds__(NT) bwd_fscan(BwdArgs a) {
   int first, nch;
   unit_chunks(a, n, first, nch);
 
-  // entry state of the first chunk
-  for (int idx = tid; idx < D * DVT; idx += NT) {
-    const int i = idx / DVT, j = idx - i * DVT;
-    sS[i * LV + j] = a.init_state ? a.init_state[(static_cast<size_t>(n) * a.H + h) * D * D + i * D + c0 + j] : 0.f;
-  }
+  tile_from_global<D, DVT, LD>(sST, a.init_state ? a.init_state + (static_cast<size_t>(n) * a.H + h) * D * D : nullptr,
+                               c0);
+  Staged<C, D> pW;
+  Staged<D, C> pK;
+  Staged<C, DVT> pU;
+  Staged<1, D> pG;
+  auto fetch = [&](int c) {
+    const size_t sh = static_cast<size_t>(first + c) * a.H + h;
+    pW.load(a.Wm + sh * C * D, D, 0);
+    pK.load(a.KdT + sh * D * C, C, 0);
+    pU.load(a.Um + sh * C * D, D, c0);
+    pG.load(a.eg + sh * D, D, 0);
+  };
+  if (nch > 0) fetch(0);
   for (int c = 0; c < nch; ++c) {
     const size_t sh = static_cast<size_t>(first + c) * a.H + h;
-    __syncthreads();  // previous chunk done with every buffer
-    load_mat<C, D, LD>(sW, a.Wm + sh * C * D);
-    load_mat<C, D, LD>(sKd, a.Kd + sh * C * D);
-    load_cols<C, DVT, LV>(sU, a.Um + sh * C * D, D, c0);
-    for (int i = tid; i < D; i += NT) sG[i] = a.eg[sh * D + i];
-    store_cols<D, DVT, LV>(a.S_in + sh * D * D, D, c0, sS);
+    __syncthreads();  // the previous chunk is done with every buffer
+    pW.store(sW, LD);
+    pK.store(sKT, LM);
+    pU.store(sU, LV);
+    pG.store(sG, D);
+    if (c + 1 < nch) fetch(c + 1);
+    tile_to_global<D, DVT, LD>(a.S_in + sh * D * D, c0, sST);
     __syncthreads();
-    // Delta = U - W S
-    for (int tq = w; tq < 4 * (DVT / 16); tq += 4) {
-      const int tb = tq % 4, cb = tq / 4;
-      f32x4 acc = zero4f();
-#pragma unroll 4
-      for (int k0 = 0; k0 < D; k0 += 4) {
-        const int kk = k0 + kq;
-        acc = mma(sW[(16 * tb + r) * LD + kk], sS[kk * LV + 16 * cb + r], acc);
-      }
+    // Delta = U - W S: wave w, rows [16w, 16w + 16)
+    {
+      f32x4 acc[NBC];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 16 * tb + 4 * kq + j, col = 16 * cb + r;
-        const float dl = sU[t * LV + col] - acc[j];
-        sX[t * LV + col] = dl;
-        a.Dl[(sh * C + t) * D + c0 + col] = dl;
-      }
+      for (int nb = 0; nb < NBC; ++nb) acc[nb] = zero4f();
+      mm_kc<NBC>(acc, sW + 16 * w * LD, LD, sST, LD, 0, D);
+#pragma unroll
+      for (int nb = 0; nb < NBC; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * w + 4 * kq + j, col = 16 * nb + r;
+          const float dl = sU[t * LV + col] - acc[nb][j];
+          sXT[col * LM + t] = dl;
+          a.Dl[(sh * C + t) * D + c0 + col] = dl;
+        }
     }
     __syncthreads();
     // S = b_C S + Kd^T Delta
-    for (int tq = w; tq < (D / 16) * (DVT / 16); tq += 4) {
-      const int ib = tq % (D / 16), cb = tq / (D / 16);
-      f32x4 acc = zero4f();
-#pragma unroll 4
-      for (int k0 = 0; k0 < C; k0 += 4) {
-        const int s = k0 + kq;
-        acc = mma(sKd[s * LD + 16 * ib + r], sX[s * LV + 16 * cb + r], acc);
-      }
+    for (int ib = w; ib < D / 16; ib += 4) {
+      f32x4 acc[NBC];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 16 * ib + 4 * kq + j, col = 16 * cb + r;
-        sS[i * LV + col] = sG[i] * sS[i * LV + col] + acc[j];
-      }
+      for (int nb = 0; nb < NBC; ++nb) acc[nb] = zero4f();
+      mm_kc<NBC>(acc, sKT + 16 * ib * LM, LM, sXT, LM, 0, C);
+#pragma unroll
+      for (int nb = 0; nb < NBC; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 16 * ib + 4 * kq + j, col = 16 * nb + r;
+          sST[col * LD + i] = sG[i] * sST[col * LD + i] + acc[nb][j];
+        }
     }
   }
 }
 
-// bwd_rscan: per (unit, value-column tile), backwards over the unit's chunks.
+// bwd_rscan: backwards over the unit's chunks; dDelta and the exit-state
+// gradient of every chunk, and the gradient of the initial state.
 template <int D>
 __global__ void __launch_bounds__(NT) bwd_rscan(BwdArgs a) {
   using P = ScanL<D>;
-  constexpr int DVT = P::DVT, LD = P::LD, LV = P::LV, LM = P::LM;
+  constexpr int DVT = P::DVT, NBC = P::NBC, LD = P::LD, LM = P::LM;
   extern __shared__ __align__(16) float sm[];
-  float* sS = sm + P::RS;  // dS tile
+  float* sST = sm + P::RS;  // dS^T tile
+  float* sAT = sm + P::RA;
   float* sKd = sm + P::RK;
-  float* sQs = sm + P::RQ;
-  float* sW = sm + P::RW;
-  float* sO = sm + P::RO;  // dO tile
-  float* sX = sm + P::RX;  // dDelta tile
+  float* sQT = sm + P::RQ;
+  float* sWT = sm + P::RW;
+  float* sOT = sm + P::RO;  // dO^T tile
+  float* sXT = sm + P::RX;  // dDelta^T tile
   float* sG = sm + P::RG;
-  float* sAs = sm + P::RM;
 
   const int unit = blockIdx.x / P::NTILE, tile = blockIdx.x - unit * P::NTILE;
   const int n = unit / a.H, h = unit - n * a.H;
@@ -574,70 +745,123 @@ __global__ void __launch_bounds__(NT) bwd_rscan(BwdArgs a) {
   unit_chunks(a, n, first, nch);
   const size_t uo = (static_cast<size_t>(n) * a.H + h) * D * D;
 
-  for (int idx = tid; idx < D * DVT; idx += NT) {
-    const int i = idx / DVT, j = idx - i * DVT;
-    sS[i * LV + j] = a.d_final ? a.d_final[uo + i * D + c0 + j] : 0.f;
-  }
-  for (int c = nch - 1; c >= 0; --c) {
+  tile_from_global<D, DVT, LD>(sST, a.d_final ? a.d_final + uo : nullptr, c0);
+  Staged<C, C> pA;
+  Staged<C, D> pK;
+  Staged<D, C> pQ;
+  Staged<D, C> pW;
+  Staged<C, DVT> pO;
+  Staged<1, D> pG;
+  auto fetch = [&](int c) {
     const int slot = first + c;
     const size_t sh = static_cast<size_t>(slot) * a.H + h;
     Loc L;
     locate(a, slot, L);
+    pA.load(a.AsT + sh * C * C, C, 0);
+    pK.load(a.Kd + sh * C * D, D, 0);
+    pQ.load(a.QsT + sh * D * C, C, 0);
+    pW.load(a.WT + sh * D * C, C, 0);
+    pO.load_tokens(a.d_out, L.tok0, a.H, h, D, c0, L.count);
+    pG.load(a.eg + sh * D, D, 0);
+  };
+  if (nch > 0) fetch(nch - 1);
+  for (int c = nch - 1; c >= 0; --c) {
+    const size_t sh = static_cast<size_t>(first + c) * a.H + h;
     __syncthreads();
-    load_mat<C, C, LM>(sAs, a.As + sh * C * C);
-    load_mat<C, D, LD>(sKd, a.Kd + sh * C * D);
-    load_mat<C, D, LD>(sQs, a.Qs + sh * C * D);
-    load_mat<C, D, LD>(sW, a.Wm + sh * C * D);
-    for (int idx = tid; idx < C * (DVT / 4); idx += NT) {
-      const int t = idx / (DVT / 4), g4 = idx - t * (DVT / 4);
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < L.count) x = load4(a.d_out + ((L.tok0 + t) * a.H + h) * D + c0 + 4 * g4);
-      *reinterpret_cast<float4*>(sO + t * LV + 4 * g4) = x;
-    }
-    for (int i = tid; i < D; i += NT) sG[i] = a.eg[sh * D + i];
-    store_cols<D, DVT, LV>(a.dSo + sh * D * D, D, c0, sS);
+    pA.store(sAT, LM);
+    pK.store(sKd, LD);
+    pQ.store(sQT, LM);
+    pW.store(sWT, LM);
+    pO.store_t(sOT, LM);
+    pG.store(sG, D);
+    if (c > 0) fetch(c - 1);
+    tile_to_global<D, DVT, LD>(a.dSo + sh * D * D, c0, sST);
     __syncthreads();
     // dDelta = As^T dO + Kd dS
-    for (int tq = w; tq < 4 * (DVT / 16); tq += 4) {
-      const int tb = tq % 4, cb = tq / 4;
-      f32x4 acc = zero4f();
-#pragma unroll 4
-      for (int k0 = 0; k0 < C; k0 += 4) {
-        const int s = k0 + kq;
-        acc = mma(sAs[s * LM + 16 * tb + r], sO[s * LV + 16 * cb + r], acc);
-      }
-#pragma unroll 4
-      for (int k0 = 0; k0 < D; k0 += 4) {
-        const int kk = k0 + kq;
-        acc = mma(sKd[(16 * tb + r) * LD + kk], sS[kk * LV + 16 * cb + r], acc);
-      }
+    {
+      f32x4 acc[NBC];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 16 * tb + 4 * kq + j, col = 16 * cb + r;
-        sX[t * LV + col] = acc[j];
-        a.dDl[(sh * C + t) * D + c0 + col] = acc[j];
-      }
+      for (int nb = 0; nb < NBC; ++nb) acc[nb] = zero4f();
+      mm_kc<NBC>(acc, sAT + 16 * w * LM, LM, sOT, LM, 0, C);
+      mm_kc<NBC>(acc, sKd + 16 * w * LD, LD, sST, LD, 0, D);
+#pragma unroll
+      for (int nb = 0; nb < NBC; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * w + 4 * kq + j, col = 16 * nb + r;
+          sXT[col * LM + t] = acc[nb][j];
+          a.dDl[(sh * C + t) * D + c0 + col] = acc[nb][j];
+        }
     }
     __syncthreads();
     // dS = b_C dS + Qs^T dO - W^T dDelta
-    for (int tq = w; tq < (D / 16) * (DVT / 16); tq += 4) {
-      const int ib = tq % (D / 16), cb = tq / (D / 16);
-      f32x4 acc = zero4f();
-#pragma unroll 4
-      for (int k0 = 0; k0 < C; k0 += 4) {
-        const int t = k0 + kq;
-        acc = mma(sQs[t * LD + 16 * ib + r], sO[t * LV + 16 * cb + r], acc);
-        acc = mma(-sW[t * LD + 16 * ib + r], sX[t * LV + 16 * cb + r], acc);
-      }
+    for (int ib = w; ib < D / 16; ib += 4) {
+      f32x4 acc[NBC], neg[NBC];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 16 * ib + 4 * kq + j, col = 16 * cb + r;
-        sS[i * LV + col] = sG[i] * sS[i * LV + col] + acc[j];
-      }
+      for (int nb = 0; nb < NBC; ++nb) acc[nb] = neg[nb] = zero4f();
+      mm_kc<NBC>(acc, sQT + 16 * ib * LM, LM, sOT, LM, 0, C);
+      mm_kc<NBC>(neg, sWT + 16 * ib * LM, LM, sXT, LM, 0, C);
+#pragma unroll
+      for (int nb = 0; nb < NBC; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 16 * ib + 4 * kq + j, col = 16 * nb + r;
+          sST[col * LD + i] = sG[i] * sST[col * LD + i] + acc[nb][j] - neg[nb][j];
+        }
     }
   }
   __syncthreads();
-  if (a.d_init) store_cols<D, DVT, LV>(a.d_init + uo, D, c0, sS);
+  if (a.d_init) tile_to_global<D, DVT, LD>(a.d_init + uo, c0, sST);
+}
+
+// ---------------------------------------------------------------------------
+// Tile products with both operands contiguous along the contraction index k
+// (rows of A, rows of Bt): lane (r, kq) reads one float4 per 16-wide k block
+// and feeds it to four MFMAs, k = k0 + 4 kq + m for the m-th.  The order of k
+// inside a block is the same permutation for A and B, so the sum is unchanged.
+// acc[n] += A[16 rows from A][k] * Bt[16 rows from Bt + 16 n ldb][k], k in [k_lo, k_hi).
+template <int NB>
+__device__ __forceinline__ void mm_kc(f32x4 (&acc)[NB], const float* A, int lda, const float* Bt, int ldb, int k_lo,
+                                      int k_hi) {
+  const int lane = threadIdx.x & 63, r = lane & 15, kq = lane >> 4;
+  const float* ar = A + r * lda + 4 * kq;
+  const float* br = Bt + r * ldb + 4 * kq;
+  for (int k0 = k_lo; k0 < k_hi; k0 += 16) {
+    const float4 a = *reinterpret_cast<const float4*>(ar + k0);
+    float4 b[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) b[n] = *reinterpret_cast<const float4*>(br + 16 * n * ldb + k0);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = mma(a.x, b[n].x, acc[n]);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = mma(a.y, b[n].y, acc[n]);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = mma(a.z, b[n].z, acc[n]);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = mma(a.w, b[n].w, acc[n]);
+  }
+}
+
+// A dense rows x cols fp32 matrix, transposed into LDS: dst[c * LDT + r] = src[r][c].
+template <int ROWS, int COLS, int LDT, int NTH = NT>
+__device__ __forceinline__ void load_mat_t(float* dst, const float* src) {
+  constexpr int G = COLS / 4, N = ROWS * G, IT = (N + NTH - 1) / NTH;
+  float4 x[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTH + threadIdx.x;
+    if (idx < N) x[it] = load4(src + idx * 4);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTH + threadIdx.x, rr = idx / G, c = 4 * (idx - rr * G);
+    if (idx < N) {
+      dst[(c + 0) * LDT + rr] = x[it].x;
+      dst[(c + 1) * LDT + rr] = x[it].y;
+      dst[(c + 2) * LDT + rr] = x[it].z;
+      dst[(c + 3) * LDT + rr] = x[it].w;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -646,10 +870,12 @@ __global__ void __launch_bounds__(NT) bwd_rscan(BwdArgs a) {
 template <int D>
 struct GsL {
   static constexpr int LD = D + 4, LM = C + 4;
+  static constexpr int BIG = (D > C ? D : C) * LD;
+  static constexpr int MID = (C * LD > D * LM ? C * LD : D * LM);
   static constexpr int RS = 0;                 // r(C-1, t) (staging), S, Delta (rows), dS'
-  static constexpr int RX = RS + (D > C ? D : C) * LD;  // dDelta, Kb, dO
-  static constexpr int RR = RX + C * LD;       // b (staging), dR, Delta
-  static constexpr int RT = RR + C * LD;       // T
+  static constexpr int RX = RS + BIG;          // dDelta^T (D x LM), dO
+  static constexpr int RR = RX + MID;          // log_g, b (staging), dR, Delta
+  static constexpr int RT = RR + C * LD;       // T^T
   static constexpr int RB = RT + C * LM;       // beta [C]
   static constexpr int RE = RB + C;            // b_C [D]
   static constexpr int RY = RE + D;            // dgamma [D]
@@ -662,7 +888,7 @@ struct GsL {
 template <int D, typename In>
 __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
   using P = GsL<D>;
-  constexpr int LD = P::LD, LM = P::LM, NCT = D / 16;
+  constexpr int LD = P::LD, LM = P::LM, NCT = D / 16, NB = NCT < 4 ? NCT : 4;
   extern __shared__ __align__(16) float sm[];
   float* sS = sm + P::RS;
   float* sX = sm + P::RX;
@@ -689,8 +915,8 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
     sBeta[tid] = tid < L.count ? a.beta[row(tid)] : 0.f;
     sDb[tid] = 0.f;
   }
-  load_mat<C, C, LM>(sT, a.Tm + sh * C * C);
-  load_mat<C, D, LD>(sX, a.dDl + sh * C * D);
+  load_mat_t<C, C, LM>(sT, a.Tm + sh * C * C);   // T^T
+  load_mat_t<C, D, LM>(sX, a.dDl + sh * C * D);  // dDelta^T
   load_rows<D, LD>(sR, a.log_g, L.tok0, L.count, H, h);  // log_g rows (0 past the end)
   __syncthreads();
   // per channel: b_t into sR, r(C-1, t) into sS (staging), b_C into sEg
@@ -719,80 +945,66 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
       kv[ct][j] = t < L.count ? to_f32(k[row(t) * D + i]) : 0.f;
     }
   __syncthreads();
-  // dR = T^T dDelta -> sR;  dv = beta dR
-  for (int ct = 0; ct < NCT; ++ct) {
-    f32x4 acc = zero4f();
-    for (int k0 = 16 * w; k0 < C; k0 += 4) {
-      const int s = k0 + kq;
-      acc = mma(sT[s * LM + 16 * w + r], sX[s * LD + 16 * ct + r], acc);
-    }
+  // dR = T^T dDelta -> sR;  dv = beta dR.  (T^T)[t][s] = 0 for s < t.
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 16 * w + 4 * kq + j, i = 16 * ct + r;
-      sR[t * LD + i] = acc[j];
-      if (t < L.count) a.dv[row(t) * D + i] = sBeta[t] * acc[j];
-    }
+  for (int c0 = 0; c0 < NCT; c0 += NB) {
+    f32x4 acc[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = zero4f();
+    mm_kc<NB>(acc, sT + 16 * w * LM, LM, sX + 16 * c0 * LM, LM, 16 * w, C);
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * w + 4 * kq + j, i = 16 * (c0 + n) + r;
+        sR[t * LD + i] = acc[n][j];
+        if (t < L.count) a.dv[row(t) * D + i] = sBeta[t] * acc[n][j];
+      }
   }
-  __syncthreads();
-  // S into sS; K*b into sX
   load_mat<D, D, LD>(sS, a.S_in + sh * D * D);
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sX[(16 * w + 4 * kq + j) * LD + 16 * ct + r] = kv[ct][j] * bb[ct][j];
-  __syncthreads();
+  __syncthreads();  // dR and S in place; dDelta^T no longer needed
+  load_rows<D, LD>(sX, a.d_out, L.tok0, L.count, H, h);  // dO
   float dq_[NCT][4], dk_[NCT][4], dg_[NCT][4];
   float dbr[4] = {0.f, 0.f, 0.f, 0.f};
-  // V - (K*b) S against dR: the R part of dbeta
-  for (int ct = 0; ct < NCT; ++ct) {
-    f32x4 acc = zero4f();
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const int kk = k0 + kq;
-      acc = mma(sX[(16 * w + r) * LD + kk], sS[kk * LD + 16 * ct + r], acc);
-    }
+  // X = dR S^T: d(K*b) = -beta X, and the R part of dbeta,
+  // dR_t . (v_t - (K*b)_t S) = dR_t . v_t - (K*b)_t . X_t
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 16 * w + 4 * kq + j, jj = 16 * ct + r;
-      const float vv = t < L.count ? to_f32(v[row(t) * D + jj]) : 0.f;
-      dbr[j] += sR[t * LD + jj] * (vv - acc[j]);
-    }
+  for (int c0 = 0; c0 < NCT; c0 += NB) {
+    f32x4 acc[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = zero4f();
+    mm_kc<NB>(acc, sR + 16 * w * LD, LD, sS + 16 * c0 * LD, LD, 0, D);
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ct = c0 + n, t = 16 * w + 4 * kq + j, i = 16 * ct + r;
+        const float kb = kv[ct][j] * bb[ct][j];
+        const float vv = t < L.count ? to_f32(v[row(t) * D + i]) : 0.f;
+        dbr[j] += sR[t * LD + i] * vv - kb * acc[n][j];
+        const float dkb = -sBeta[t] * acc[n][j];
+        dk_[ct][j] = dkb * bb[ct][j];
+        dg_[ct][j] = dkb * kb;
+      }
   }
-  // d(K*b) = -beta dR S^T
-  for (int ct = 0; ct < NCT; ++ct) {
-    f32x4 acc = zero4f();
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const int jj = k0 + kq;
-      acc = mma(sR[(16 * w + r) * LD + jj], sS[(16 * ct + r) * LD + jj], acc);
-    }
+  __syncthreads();  // dO in place
+  // Y = dO S^T: d(Q*b) = scale Y
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 16 * w + 4 * kq + j;
-      const float dkb = -sBeta[t] * acc[j];
-      dk_[ct][j] = dkb * bb[ct][j];
-      dg_[ct][j] = dkb * kv[ct][j] * bb[ct][j];
-    }
-  }
-  __syncthreads();  // done with K*b
-  load_rows<D, LD>(sX, a.d_out, L.tok0, L.count, H, h);
-  __syncthreads();
-  // d(Q*b) = scale dO S^T
-  for (int ct = 0; ct < NCT; ++ct) {
-    f32x4 acc = zero4f();
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const int jj = k0 + kq;
-      acc = mma(sX[(16 * w + r) * LD + jj], sS[(16 * ct + r) * LD + jj], acc);
-    }
+  for (int c0 = 0; c0 < NCT; c0 += NB) {
+    f32x4 acc[NB];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 16 * w + 4 * kq + j, i = 16 * ct + r;
-      const float dqb = a.scale * acc[j];
-      const float qv = t < L.count ? to_f32(q[row(t) * D + i]) : 0.f;
-      dq_[ct][j] = dqb * bb[ct][j];
-      dg_[ct][j] += dqb * qv * bb[ct][j];
-    }
+    for (int n = 0; n < NB; ++n) acc[n] = zero4f();
+    mm_kc<NB>(acc, sX + 16 * w * LD, LD, sS + 16 * c0 * LD, LD, 0, D);
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int ct = c0 + n, t = 16 * w + 4 * kq + j, i = 16 * ct + r;
+        const float dqb = a.scale * acc[n][j];
+        const float qv = t < L.count ? to_f32(q[row(t) * D + i]) : 0.f;
+        dq_[ct][j] = dqb * bb[ct][j];
+        dg_[ct][j] += dqb * qv * bb[ct][j];
+      }
   }
   // b_C sum_j dS'[i, j] S[i, j]: D / 4 consecutive threads per row, coalesced
   {
@@ -816,27 +1028,24 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
   __syncthreads();  // done with S
   load_mat<C, D, LD>(sS, a.Dl + sh * C * D);  // Delta, rows
   __syncthreads();
-  // dAqk = scale tril(dO Delta^T), dA = -tril(dR Delta^T, -1)
-  for (int sb = 0; sb < 4; ++sb) {
-    f32x4 aq = zero4f(), aa = zero4f();
-    if (sb <= w) {
-#pragma unroll 4
-      for (int k0 = 0; k0 < D; k0 += 4) {
-        const int jj = k0 + kq;
-        const float dl = sS[(16 * sb + r) * LD + jj];
-        aq = mma(sX[(16 * w + r) * LD + jj], dl, aq);
-        aa = mma(sR[(16 * w + r) * LD + jj], dl, aa);
-      }
-    }
+  // dAqk = scale tril(dO Delta^T), dA = -tril(dR Delta^T, -1); s blocks 0..3
+  {
+    f32x4 aq[4], aa[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 16 * w + 4 * kq + j, s = 16 * sb + r;
-      const float gq = s <= t ? a.scale * aq[j] : 0.f;
-      const float ga = s < t ? -aa[j] : 0.f;
-      dbr[j] += ga * a.Ab[sh * C * C + t * C + s];
-      a.dAq[sh * C * C + t * C + s] = gq;
-      a.dAb[sh * C * C + t * C + s] = sBeta[t] * ga;
-    }
+    for (int n = 0; n < 4; ++n) aq[n] = aa[n] = zero4f();
+    mm_kc<4>(aq, sX + 16 * w * LD, LD, sS, LD, 0, D);
+    mm_kc<4>(aa, sR + 16 * w * LD, LD, sS, LD, 0, D);
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * w + 4 * kq + j, s = 16 * sb + r;
+        const float gq = s <= t ? a.scale * aq[sb][j] : 0.f;
+        const float ga = s < t ? -aa[sb][j] : 0.f;
+        dbr[j] += ga * a.Ab[sh * C * C + t * C + s];
+        a.dAq[sh * C * C + t * C + s] = gq;
+        a.dAb[sh * C * C + t * C + s] = sBeta[t] * ga;
+      }
   }
   // rows of dbeta: reduce over the 16 lanes sharing kq
 #pragma unroll
@@ -852,26 +1061,29 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
   load_mat<C, D, LD>(sR, a.Dl + sh * C * D);   // Delta
   load_mat<D, D, LD>(sS, a.dSo + sh * D * D);  // dS'
   __syncthreads();
-  // dKd = Delta dS'^T
+  // Z = Delta dS'^T: dKd = Z
   float colp[NCT];
-  for (int ct = 0; ct < NCT; ++ct) {
-    f32x4 acc = zero4f();
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 4) {
-      const int jj = k0 + kq;
-      acc = mma(sR[(16 * w + r) * LD + jj], sS[(16 * ct + r) * LD + jj], acc);
-    }
-    float cs = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float kd = kv[ct][j] * rc[ct][j];
-      dk_[ct][j] += acc[j] * rc[ct][j];
-      dg_[ct][j] -= acc[j] * kd;
-      cs += acc[j] * kd;
+  for (int c0 = 0; c0 < NCT; c0 += NB) {
+    f32x4 acc[NB];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) acc[n] = zero4f();
+    mm_kc<NB>(acc, sR + 16 * w * LD, LD, sS + 16 * c0 * LD, LD, 0, D);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int ct = c0 + n;
+      float cs = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float kd = kv[ct][j] * rc[ct][j];
+        dk_[ct][j] += acc[n][j] * rc[ct][j];
+        dg_[ct][j] -= acc[n][j] * kd;
+        cs += acc[n][j] * kd;
+      }
+      cs += __shfl_xor(cs, 16, 64);
+      cs += __shfl_xor(cs, 32, 64);
+      colp[ct] = cs;
     }
-    cs += __shfl_xor(cs, 16, 64);
-    cs += __shfl_xor(cs, 32, 64);
-    colp[ct] = cs;
   }
   if (kq == 0)
 #pragma unroll
@@ -895,30 +1107,61 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 // bwd_gpairs: per (chunk, head): pair terms of Aqk and Akk, then dlog_g.
+// Q, K and the level factors are kept transposed ([channel][token]) so that
+// the pair products read them along the contracted token index.
 template <int D>
 struct GpL {
-  static constexpr int LD = D + 4, LM = C + 4;
-  static constexpr int RQ = 0;
-  static constexpr int RK = RQ + C * LD;
-  static constexpr int RF = RK + C * LD;  // F, later dG
-  static constexpr int RA = RF + C * LD;  // dAqk
-  static constexpr int RB = RA + C * LM;  // dAkk
+  static constexpr int LM = C + 4;
+  static constexpr int RQ = 0;                // Q^T
+  static constexpr int RK = RQ + D * LM;      // K^T
+  static constexpr int RF = RK + D * LM;      // F^T, later dG^T
+  static constexpr int RA = RF + D * LM;      // dAqk
+  static constexpr int RB = RA + C * LM;      // dAkk
   static constexpr int FLOATS = RB + C * LM;
   static constexpr size_t BYTES = sizeof(float) * FLOATS;
 };
+
+// level_factors, written transposed: sFT[i * LM + t].
+template <int L, int LM>
+__device__ __forceinline__ void level_factors_t(const float (&al)[32], int base, int i, float* sFT) {
+  constexpr int HH = 32 >> L;
+  float f[32];
+#pragma unroll
+  for (int b0 = 0; b0 < 32; b0 += HH) {
+    const bool upper = ((base + b0) & HH) != 0;
+    if (upper) {
+      float p = 1.f;
+#pragma unroll
+      for (int u = 0; u < HH; ++u) {
+        p *= al[b0 + u];
+        f[b0 + u] = p;
+      }
+    } else {
+      float p = 1.f;
+#pragma unroll
+      for (int u = HH - 1; u >= 0; --u) {
+        f[b0 + u] = p;
+        p *= al[b0 + u];
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 32; u += 4)
+    *reinterpret_cast<float4*>(sFT + i * LM + base + u) = make_float4(f[u], f[u + 1], f[u + 2], f[u + 3]);
+}
 
 constexpr int NTG = 512;  // bwd_gpairs: 8 waves, two per token block
 
 template <int D, typename In>
 __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
   using P = GpL<D>;
-  constexpr int LD = P::LD, LM = P::LM, NCT = D / 16;
-  // wave wv: token block w = wv & 3, channel tiles [ch * NCTW, ch * NCTW + NCTW)
+  constexpr int LM = P::LM, NCT = D / 16;
+  // wave wv: token block w = wv & 3, channel tiles [ctb, ctb + NCTW)
   constexpr int NCTW = NCT >= 2 ? NCT / 2 : 1;
   extern __shared__ __align__(16) float sm[];
-  float* sQ = sm + P::RQ;
-  float* sK = sm + P::RK;
-  float* sF = sm + P::RF;
+  float* sQT = sm + P::RQ;
+  float* sKT = sm + P::RK;
+  float* sFT = sm + P::RF;
   float* sdAq = sm + P::RA;
   float* sdAb = sm + P::RB;
 
@@ -932,8 +1175,8 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
   const int H = a.H;
   auto row = [&](int t) { return (L.tok0 + t) * H + h; };
 
-  load_rows<D, LD, In, NTG>(sQ, static_cast<const In*>(a.q), L.tok0, L.count, H, h);
-  load_rows<D, LD, In, NTG>(sK, static_cast<const In*>(a.k), L.tok0, L.count, H, h);
+  load_rows_t<D, LM, In, NTG>(sQT, static_cast<const In*>(a.q), L.tok0, L.count, H, h);
+  load_rows_t<D, LM, In, NTG>(sKT, static_cast<const In*>(a.k), L.tok0, L.count, H, h);
   load_mat<C, C, LM, NTG>(sdAq, a.dAq + sh * C * C);
   load_mat<C, C, LM, NTG>(sdAb, a.dAb + sh * C * C);
   const int ci = tid % D, ph = tid / D;
@@ -947,45 +1190,74 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) dq_[ct][j] = dk_[ct][j] = dg_[ct][j] = 0.f;
 
-  // rows of block w against the partner range [p0, p0 + plen) at level l:
-  // dX (w in the upper half) or dY (w in the lower half)
+  // rows of block w against the partner tokens [p0, p0 + plen) at level l:
+  // dX (block w in the upper half) or dY (block w in the lower half)
   auto level_terms = [&](int l, bool upper_rows, int p0, int plen) {
 #pragma unroll
     for (int ct = 0; ct < NCTW; ++ct) {
       const int i0 = 16 * (ctb + ct);
+      const float* bk = sKT + (i0 + r) * LM + 4 * kq;
+      const float* bq = sQT + (i0 + r) * LM + 4 * kq;
+      const float* bf = sFT + (i0 + r) * LM + 4 * kq;
       if (upper_rows) {
+        const int t = 16 * w + r;
         f32x4 xq = zero4f(), xk = zero4f();
-        for (int k0 = 0; k0 < plen; k0 += 4) {
-          const int s = p0 + k0 + kq, t = 16 * w + r;
-          const bool ok = at_level(l, t, s);
-          const float ys = sK[s * LD + i0 + r] * sF[s * LD + i0 + r];
-          xq = mma(ok ? sdAq[t * LM + s] : 0.f, ys, xq);
-          xk = mma(ok ? sdAb[t * LM + s] : 0.f, ys, xk);
+        for (int k0 = p0; k0 < p0 + plen; k0 += 16) {
+          const int s0 = k0 + 4 * kq;
+          const float4 aq = *reinterpret_cast<const float4*>(sdAq + t * LM + s0);
+          const float4 ab = *reinterpret_cast<const float4*>(sdAb + t * LM + s0);
+          const float4 kk = *reinterpret_cast<const float4*>(bk + k0);
+          const float4 ff = *reinterpret_cast<const float4*>(bf + k0);
+          const bool m0 = at_level(l, t, s0), m1 = at_level(l, t, s0 + 1), m2 = at_level(l, t, s0 + 2),
+                     m3 = at_level(l, t, s0 + 3);
+          xq = mma(m0 ? aq.x : 0.f, kk.x * ff.x, xq);
+          xk = mma(m0 ? ab.x : 0.f, kk.x * ff.x, xk);
+          xq = mma(m1 ? aq.y : 0.f, kk.y * ff.y, xq);
+          xk = mma(m1 ? ab.y : 0.f, kk.y * ff.y, xk);
+          xq = mma(m2 ? aq.z : 0.f, kk.z * ff.z, xq);
+          xk = mma(m2 ? ab.z : 0.f, kk.z * ff.z, xk);
+          xq = mma(m3 ? aq.w : 0.f, kk.w * ff.w, xq);
+          xk = mma(m3 ? ab.w : 0.f, kk.w * ff.w, xk);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int t = 16 * w + 4 * kq + j, i = i0 + r;
-          const float ft = sF[t * LD + i];
+          const int to = 16 * w + 4 * kq + j, i = i0 + r;
+          const float ft = sFT[i * LM + to];
           const float gq = ft * xq[j], gk = ft * xk[j];
           dq_[ct][j] += gq;
           dk_[ct][j] += gk;
-          dg_[ct][j] += sQ[t * LD + i] * gq + sK[t * LD + i] * gk;
+          dg_[ct][j] += sQT[i * LM + to] * gq + sKT[i * LM + to] * gk;
         }
       } else {
-        f32x4 y = zero4f();
-        for (int k0 = 0; k0 < plen; k0 += 4) {
-          const int t = p0 + k0 + kq, s = 16 * w + r;
-          const bool ok = at_level(l, t, s);
-          const float ft = sF[t * LD + i0 + r];
-          y = mma(ok ? sdAq[t * LM + s] : 0.f, sQ[t * LD + i0 + r] * ft, y);
-          y = mma(ok ? sdAb[t * LM + s] : 0.f, sK[t * LD + i0 + r] * ft, y);
+        const int s = 16 * w + r;
+        f32x4 y1 = zero4f(), y2 = zero4f();
+        for (int k0 = p0; k0 < p0 + plen; k0 += 16) {
+          const int t0 = k0 + 4 * kq;
+          const float4 qq = *reinterpret_cast<const float4*>(bq + k0);
+          const float4 kk = *reinterpret_cast<const float4*>(bk + k0);
+          const float4 ff = *reinterpret_cast<const float4*>(bf + k0);
+          float aq[4], ab[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const bool ok = at_level(l, t0 + m, s);
+            aq[m] = ok ? sdAq[(t0 + m) * LM + s] : 0.f;
+            ab[m] = ok ? sdAb[(t0 + m) * LM + s] : 0.f;
+          }
+          y1 = mma(aq[0], qq.x * ff.x, y1);
+          y2 = mma(ab[0], kk.x * ff.x, y2);
+          y1 = mma(aq[1], qq.y * ff.y, y1);
+          y2 = mma(ab[1], kk.y * ff.y, y2);
+          y1 = mma(aq[2], qq.z * ff.z, y1);
+          y2 = mma(ab[2], kk.z * ff.z, y2);
+          y1 = mma(aq[3], qq.w * ff.w, y1);
+          y2 = mma(ab[3], kk.w * ff.w, y2);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int s = 16 * w + 4 * kq + j, i = i0 + r;
-          const float gy = sF[s * LD + i] * y[j];
+          const int so = 16 * w + 4 * kq + j, i = i0 + r;
+          const float gy = sFT[i * LM + so] * (y1[j] + y2[j]);
           dk_[ct][j] += gy;
-          dg_[ct][j] -= sK[s * LD + i] * gy;
+          dg_[ct][j] -= sKT[i * LM + so] * gy;
         }
       }
     }
@@ -995,12 +1267,12 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
     __syncthreads();
     if (chan) {
       switch (l) {
-        case 0: level_factors<0, LD>(al, 32 * ph, ci, sF); break;
-        case 1: level_factors<1, LD>(al, 32 * ph, ci, sF); break;
-        case 2: level_factors<2, LD>(al, 32 * ph, ci, sF); break;
-        case 3: level_factors<3, LD>(al, 32 * ph, ci, sF); break;
-        case 4: level_factors<4, LD>(al, 32 * ph, ci, sF); break;
-        default: level_factors<5, LD>(al, 32 * ph, ci, sF); break;
+        case 0: level_factors_t<0, LM>(al, 32 * ph, ci, sFT); break;
+        case 1: level_factors_t<1, LM>(al, 32 * ph, ci, sFT); break;
+        case 2: level_factors_t<2, LM>(al, 32 * ph, ci, sFT); break;
+        case 3: level_factors_t<3, LM>(al, 32 * ph, ci, sFT); break;
+        case 4: level_factors_t<4, LM>(al, 32 * ph, ci, sFT); break;
+        default: level_factors_t<5, LM>(al, 32 * ph, ci, sFT); break;
       }
     }
     __syncthreads();
@@ -1023,31 +1295,32 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
     for (int j = 0; j < 4; ++j) {
       const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + ct) + r;
       const float d = sdAq[t * LM + t];
-      dq_[ct][j] += d * sK[t * LD + i];
-      dk_[ct][j] += d * sQ[t * LD + i];
+      dq_[ct][j] += d * sKT[i * LM + t];
+      dk_[ct][j] += d * sQT[i * LM + t];
     }
-  __syncthreads();  // done with F
-  // add the state-side parts staged by bwd_gstate; dG into sF for the cumsum
+  __syncthreads();  // done with F^T
+  // add the state-side parts staged by bwd_gstate; dG^T into sFT for the cumsum
+  if (active) {
 #pragma unroll
-  for (int ct = 0; ct < NCTW; ++ct)
+    for (int ct = 0; ct < NCTW; ++ct)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + ct) + r;
-      if (!active) continue;
-      float g = 0.f;
-      if (t < L.count) {
-        const int64_t o = row(t) * D + i;
-        a.dq[o] += dq_[ct][j];
-        a.dk[o] += dk_[ct][j];
-        g = a.dlog_g[o] + dg_[ct][j];
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + ct) + r;
+        float g = 0.f;
+        if (t < L.count) {
+          const int64_t o = row(t) * D + i;
+          a.dq[o] += dq_[ct][j];
+          a.dk[o] += dk_[ct][j];
+          g = a.dlog_g[o] + dg_[ct][j];
+        }
+        sFT[i * LM + t] = g;
       }
-      sF[t * LD + i] = g;
-    }
+  }
   __syncthreads();
   for (int i = tid; i < D; i += NTG) {
     float acc = 0.f;
     for (int t = C - 1; t >= 0; --t) {
-      acc += sF[t * LD + i];
+      acc += sFT[i * LM + t];
       if (t < L.count) a.dlog_g[row(t) * D + i] = acc;
     }
   }
@@ -1100,7 +1373,7 @@ int64_t bwd_slots(int num_seqs, int seq_len, bool packed) {
 struct BwdWs {
   int32_t* cstart;
   int32_t* table;
-  float* f[14];
+  float* f[16];
   size_t bytes;
 };
 
@@ -1117,10 +1390,10 @@ BwdWs bwd_ws(void* base, int num_seqs, int seq_len, int H, int D, bool packed) {
     off += al256(static_cast<size_t>(ns) * 4);
   }
   const size_t sh = static_cast<size_t>(ns) * H;
-  const size_t per[14] = {size_t(D) * D, size_t(D) * D, size_t(C) * D, size_t(C) * D, size_t(C) * D,
+  const size_t per[16] = {size_t(D) * D, size_t(D) * D, size_t(C) * D, size_t(C) * D, size_t(C) * D,
                           size_t(C) * D, size_t(C) * D, size_t(C) * D, size_t(C) * C, size_t(C) * C,
-                          size_t(C) * C, size_t(C) * C, size_t(C) * C, size_t(D)};
-  for (int i = 0; i < 14; ++i) {
+                          size_t(C) * C, size_t(C) * C, size_t(C) * C, size_t(D), size_t(C) * D, size_t(C) * D};
+  for (int i = 0; i < 16; ++i) {
     l.f[i] = reinterpret_cast<float*>(b + off);
     off += al256(sh * per[i] * 4);
   }
@@ -1219,9 +1492,9 @@ hipError_t launch_chunk_bwd(const BwdLaunch& s, hipStream_t stream) {
   a.table = packed ? l.table : nullptr;
   a.d_out = s.d_out; a.d_final = s.d_final;
   a.dq = s.dq; a.dk = s.dk; a.dv = s.dv; a.dlog_g = s.dlog_g; a.dbeta = s.dbeta; a.d_init = s.d_init;
-  a.S_in = l.f[0]; a.dSo = l.f[1]; a.Wm = l.f[2]; a.Um = l.f[3]; a.Kd = l.f[4]; a.Qs = l.f[5];
-  a.Dl = l.f[6]; a.dDl = l.f[7]; a.As = l.f[8]; a.Tm = l.f[9]; a.Ab = l.f[10]; a.dAq = l.f[11];
-  a.dAb = l.f[12]; a.eg = l.f[13];
+  a.S_in = l.f[0]; a.dSo = l.f[1]; a.Wm = l.f[2]; a.Um = l.f[3]; a.Kd = l.f[4]; a.QsT = l.f[5];
+  a.Dl = l.f[6]; a.dDl = l.f[7]; a.AsT = l.f[8]; a.Tm = l.f[9]; a.Ab = l.f[10]; a.dAq = l.f[11];
+  a.dAb = l.f[12]; a.eg = l.f[13]; a.WT = l.f[14]; a.KdT = l.f[15];
   a.N = s.num_seqs; a.T = s.seq_len; a.H = s.num_heads;
   a.cps = packed ? 0 : static_cast<int>((static_cast<int64_t>(s.seq_len) + C - 1) / C);
   a.scale = s.scale;

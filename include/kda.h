@@ -206,7 +206,7 @@ kda_status kda_step_commit(const kda_desc* desc, const void* k,
  * inside the call, so out and final_state are not inputs.
  *
  * desc->workspace must hold kda_chunk_bwd_workspace_bytes(desc, packed)
- * bytes whenever there are tokens or the problem is packed: about 400 KiB
+ * bytes whenever there are tokens or the problem is packed: about 465 KiB
  * per 64-token chunk and head at d = 128 (chunk entry states and their
  * gradients, per-chunk operands).  Its contents on entry do not matter.
  * Same status codes and preconditions as kda_chunk_fwd.

@@ -266,8 +266,8 @@ def bwd_desc(**kw):
 
 def test_bwd_workspace_size():
     # dense 2 x 64 tokens, 4 heads, d = 128: 2 chunk slots x 4 heads, each
-    # 2 d*d + 6 C*d + 5 C*C + d floats
-    per = 2 * 128 * 128 + 6 * 64 * 128 + 5 * 64 * 64 + 128
+    # 2 d*d + 8 C*d + 5 C*C + d floats
+    per = 2 * 128 * 128 + 8 * 64 * 128 + 5 * 64 * 64 + 128
     d = desc()
     assert lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(d), 0) == 8 * per * 4
     assert kda.bwd_workspace_bytes(2, 64, 4, 128, packed=False) == 8 * per * 4
