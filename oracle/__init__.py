@@ -10,9 +10,10 @@ The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, libm ``exp``): the
 token loop of the gated delta rule as printed in the GLM-5.3-Flash model notes
 (Glm5NextTextLinearAttention snippet), with the output read from the updated
 state, and packed documents reset at their boundaries (NeMo glm5_next.layers,
-``_torch_recurrent_kda``); and its reverse mode, the same loop differentiated
-token by token (that page documents the recurrence as differentiable).  This
-module only marshals numpy arrays.
+``_torch_recurrent_kda``); its reverse mode, the same loop differentiated
+token by token (that page documents the recurrence as differentiable); and the
+short causal depthwise convolution that feeds q, k and v
+(``_TorchShortConvolution``).  This module only marshals numpy arrays.
 """
 from __future__ import annotations
 
@@ -50,6 +51,8 @@ def load(path: str = LIB_PATH):
     lib.kda_oracle_backward.restype = ctypes.c_int
     lib.kda_oracle_backward.argtypes = [i64, i64, i64, i64, i64, dp, dp, dp, dp, dp, dp, ip,
                                         ctypes.c_double, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
+    lib.kda_oracle_short_conv.restype = ctypes.c_int
+    lib.kda_oracle_short_conv.argtypes = [i64, i64, i64, i64, dp, dp, ip, dp, ctypes.c_int, dp, dp, ctypes.c_int]
     lib.kda_oracle_threads.restype = ctypes.c_int
     lib.kda_oracle_threads.argtypes = [ctypes.c_int]
     return lib
@@ -167,3 +170,35 @@ def kda_backward(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=N
     if rc != 0:
         raise ValueError(f"kda_oracle_backward failed with code {rc}")
     return g
+
+
+def short_conv(x, w, cu_seqlens=None, init_cache=None, act: int = 0, n_threads: int = 0, lib=None):
+    """Short causal depthwise convolution.
+
+    x: [B, T, channels] (dense: B sequences; packed: B == 1 with ``cu_seqlens``
+    [N+1]); w: [channels, K]; init_cache: [N, channels, K-1] or None (zeros);
+    act 0 = identity, 1 = SiLU.  Returns (y [B, T, channels],
+    final_cache [N, channels, K-1]) in float64.
+    """
+    lib = lib or _get_lib()
+    x, w = _f64(x), _f64(w)
+    B, T, Cn = x.shape
+    K = w.shape[1]
+    assert w.shape == (Cn, K)
+    if cu_seqlens is not None:
+        assert B == 1, "packed mode takes one row"
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        N, L = cu.shape[0] - 1, T
+        cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    else:
+        cu, N, L, cu_p = None, B, T, None
+    c0 = _f64(init_cache) if init_cache is not None else None
+    if c0 is not None:
+        assert c0.shape == (N, Cn, K - 1)
+    y = np.zeros((B, T, Cn))
+    fin = np.zeros((N, Cn, K - 1))
+    rc = lib.kda_oracle_short_conv(N, L, Cn, K, _ptr(x), _ptr(w), cu_p, _ptr(c0), int(act), _ptr(y), _ptr(fin),
+                                   int(n_threads))
+    if rc != 0:
+        raise ValueError(f"kda_oracle_short_conv failed with code {rc}")
+    return y, fin

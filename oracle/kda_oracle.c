@@ -278,6 +278,56 @@ int kda_oracle_backward(int64_t num_seqs, int64_t seq_len, int64_t num_heads,
   return failed ? -4 : 0;
 }
 
+/* The short causal depthwise convolution, one (document, channel) at a time:
+ * the extended sequence (cache, then the document's inputs) is walked token by
+ * token and each output is the K-tap dot product ending at that token. */
+int kda_oracle_short_conv(int64_t num_seqs, int64_t seq_len, int64_t channels,
+                          int64_t K, const double* x, const double* w,
+                          const int64_t* cu_seqlens, const double* init_cache,
+                          int act, double* y, double* final_cache, int n_threads) {
+  if (!x || !w || !y) return -1;
+  if (num_seqs < 0 || seq_len < 0 || channels <= 0 || K < 1 || (act != 0 && act != 1)) return -2;
+  if (cu_seqlens) {
+    if (cu_seqlens[0] != 0 || cu_seqlens[num_seqs] != seq_len) return -3;
+    for (int64_t n = 0; n < num_seqs; ++n)
+      if (cu_seqlens[n + 1] < cu_seqlens[n]) return -3;
+  }
+  const int64_t M = K - 1; /* cached inputs per (document, channel) */
+  int failed = 0;
+#ifdef _OPENMP
+  const int nt = kda_oracle_threads(n_threads);
+#pragma omp parallel for num_threads(nt) schedule(dynamic, 16)
+#endif
+  for (int64_t nc = 0; nc < num_seqs * channels; ++nc) {
+    const int64_t n = nc / channels, c = nc % channels;
+    const int64_t start = cu_seqlens ? cu_seqlens[n] : n * seq_len;
+    const int64_t len = cu_seqlens ? cu_seqlens[n + 1] - cu_seqlens[n] : seq_len;
+    /* extended sequence: M cached inputs, then the document's len inputs */
+    double* xe = (double*)malloc(sizeof(double) * (size_t)(M + len + 1));
+    if (!xe) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      failed = 1;
+      continue;
+    }
+    for (int64_t m = 0; m < M; ++m)
+      xe[m] = init_cache ? init_cache[(n * channels + c) * M + m] : 0.0;
+    for (int64_t t = 0; t < len; ++t) xe[M + t] = x[(start + t) * channels + c];
+    for (int64_t t = 0; t < len; ++t) {
+      /* window xe[t .. t + M] (in extended indices) ends at the document's token t */
+      double acc = 0.0;
+      for (int64_t j = 0; j < K; ++j) acc += w[c * K + j] * xe[t + j];
+      if (act == 1) acc = acc / (1.0 + exp(-acc));
+      y[(start + t) * channels + c] = acc;
+    }
+    if (final_cache)
+      for (int64_t m = 0; m < M; ++m) final_cache[(n * channels + c) * M + m] = xe[len + m];
+    free(xe);
+  }
+  return failed ? -4 : 0;
+}
+
 int kda_oracle_threads(int n_threads) {
 #ifdef _OPENMP
   return n_threads > 0 ? n_threads : omp_get_max_threads();

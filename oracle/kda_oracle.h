@@ -74,6 +74,27 @@ int kda_oracle_backward(int64_t num_seqs, int64_t seq_len, int64_t num_heads,
                         double* dlog_g, double* dbeta, double* d_init,
                         int n_threads);
 
+/* Short causal depthwise convolution that feeds q, k and v (NeMo
+ * glm5_next.layers, `_TorchShortConvolution`: a depthwise causal Conv1d over
+ * [batch, sequence, channels] that resets at packed boundaries; its width is
+ * the config's linear_conv_kernel_dim).  For every sequence or document n,
+ * channel c and token t of n (t counted from the document start),
+ *
+ *     y[t, c] = act( sum_{j=0}^{K-1} w[c, j] * xe[t - (K-1) + j, c] )
+ *
+ * where xe is the document's inputs preceded by its K-1 cached inputs
+ * init_cache[n, c, 0..K-2] (oldest first; zeros when init_cache is NULL), so
+ * the window never reaches into another document.  act = identity (0) or
+ * SiLU, y / (1 + exp(-y)) (1).  final_cache[n, c, m] = xe[len - (K-1) + m, c]
+ * (the last K-1 entries of the extended sequence), if not NULL.
+ * Layouts: x, y [tokens, channels] (dense: token n*seq_len + t); w
+ * [channels, K]; caches [N, channels, K-1].  Same return codes as the forward
+ * (-2 also for K < 1 or an unknown act). */
+int kda_oracle_short_conv(int64_t num_seqs, int64_t seq_len, int64_t channels,
+                          int64_t K, const double* x, const double* w,
+                          const int64_t* cu_seqlens, const double* init_cache,
+                          int act, double* y, double* final_cache, int n_threads);
+
 /* Number of OpenMP threads a call with n_threads would use. */
 int kda_oracle_threads(int n_threads);
 

@@ -3,8 +3,9 @@
 Each mutant is a textual edit of a *copy* of ``oracle/kda_oracle.c`` (a dropped
 term, a wrong sign, a wrong index or axis, a transposed operand, a missing
 reset, a wrong step order), compiled to a temporary library and run against
-``test_oracle_pins.py`` (forward mutants) or ``test_oracle_bwd_pins.py``
-(reverse-mode mutants) in a subprocess (a mutant may read out of bounds, so it
+``test_oracle_pins.py`` (forward mutants), ``test_oracle_bwd_pins.py``
+(reverse-mode mutants) or ``test_oracle_conv_pins.py`` (convolution mutants)
+in a subprocess (a mutant may read out of bounds, so it
 never runs in this process).  The committed oracle is never modified.
 """
 import os
@@ -73,6 +74,20 @@ BWD_MUTANTS = {
 }
 
 
+# planted mistakes in the short convolution
+CONV_MUTANTS = {
+    "conv_taps_reversed": ("acc += w[c * K + j] * xe[t + j];", "acc += w[c * K + (K - 1 - j)] * xe[t + j];"),
+    "conv_window_one_late": ("acc += w[c * K + j] * xe[t + j];",
+                             "acc += w[c * K + j] * (t + j + 1 < M + len ? xe[t + j + 1] : 0.0);"),
+    "conv_cache_ignored": ("xe[m] = init_cache ? init_cache[(n * channels + c) * M + m] : 0.0;", "xe[m] = 0.0;"),
+    "conv_no_reset_between_documents": ("xe[m] = init_cache ? init_cache[(n * channels + c) * M + m] : 0.0;",
+                                        "xe[m] = start - M + m >= 0 ? x[(start - M + m) * channels + c] : 0.0;"),
+    "conv_silu_before_sum": ("if (act == 1) acc = acc / (1.0 + exp(-acc));", "(void)0;"),
+    "conv_final_cache_shifted": ("final_cache[(n * channels + c) * M + m] = xe[len + m];",
+                                 "final_cache[(n * channels + c) * M + m] = xe[len + m - (m > 0)];"),
+}
+
+
 def _mutate_in(src, func, old, new, name):
     """Replace `old` by `new` inside the body of the C function starting with
     `func` (up to the next top-level closing brace); `old` must occur exactly
@@ -129,7 +144,7 @@ def _build(workdir, name, src_text):
 
 def test_unmutated_copy_passes(workdir):
     lib = _build(workdir, "clean", open(SRC).read())
-    for pins in ("test_oracle_pins.py", "test_oracle_bwd_pins.py"):
+    for pins in ("test_oracle_pins.py", "test_oracle_bwd_pins.py", "test_oracle_conv_pins.py"):
         rc, out = _run_pins(lib, pins)
         assert rc == 0, out
 
@@ -157,3 +172,12 @@ def test_backward_mutant_is_caught(workdir, name):
     mutated = _mutate_in(src, "static int run_unit_bwd(", old, new, name)
     rc, out = _run_pins(_build(workdir, name, mutated), "test_oracle_bwd_pins.py")
     assert rc != 0, f"mutant {name} survived the backward pins:\n{out}"
+
+
+@pytest.mark.parametrize("name", sorted(CONV_MUTANTS))
+def test_conv_mutant_is_caught(workdir, name):
+    src = open(SRC).read()
+    old, new = CONV_MUTANTS[name]
+    mutated = _mutate_in(src, "int kda_oracle_short_conv(", old, new, name)
+    rc, out = _run_pins(_build(workdir, name, mutated), "test_oracle_conv_pins.py")
+    assert rc != 0, f"mutant {name} survived the convolution pins:\n{out}"
