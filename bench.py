@@ -1,7 +1,7 @@
 """Benchmark of libkda on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --only {prefill,varlen,step,backward,copy}      (profiling runs)
+    python bench.py --only {prefill,varlen,step,backward,conv,copy}      (profiling runs)
     python bench.py --traffic-from FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
 
 A step is one kda_chunk_fwd call (chunked prefill) over the dense workload
@@ -14,6 +14,8 @@ fp32 out, with inputs resident in HBM.  ``value`` is prefill tokens/s
                 16-bit MFMA peak
   varlen        the packed 65536-token, 32-head prefill: tokens/s and its own
                 HBM roofline (beside the headline, not part of it)
+  short_conv    kda_short_conv over q, k, v of the dense workload (6144
+                channels, width 4, bf16): its own HBM roofline
   backward      kda_chunk_bwd on the dense workload: tokens/s and its roofline
                 against the 157.3 TFLOP/s fp32 peak (it computes in fp32)
   verify_rollback  the 64 x 4-row verify split into kda_step_rows (state read
@@ -281,6 +283,39 @@ def bench_backward(kda, steps, warmup):
             "workspace_bytes": int(ws.numel())}
 
 
+def conv_bytes(tokens: int, channels: int, K: int, n_seqs: int, x_bytes=2) -> int:
+    """Algorithmic HBM bytes of one kda_short_conv call: x read and out
+    written once, the fp32 weights, the final cache written (zero initial
+    cache)."""
+    return tokens * channels * 2 * x_bytes + channels * K * 4 + n_seqs * channels * (K - 1) * 4
+
+
+def bench_conv(kda, steps, warmup):
+    """kda_short_conv over q, k and v of the dense workload side by side
+    (4 x 4096 tokens, 3 x 16 heads x 128 = 6144 channels, bf16), width 4,
+    identity activation, zero caches, final cache written; timed like the
+    prefill."""
+    B, T, Cn, K = 4, 4096, 6144, 4
+    inp = kda_inputs.conv_inputs(B=B, T=T, channels=Cn, K=K, dtype="bf16", seed=330, cache=False)
+    x, w = inp["x"].cuda(), inp["weight"].cuda()
+    out = torch.empty_like(x)
+    fin = torch.empty((B, Cn, K - 1), dtype=torch.float32, device="cuda")
+
+    def call():
+        kda.short_conv(x, w, out=out, final_cache=fin)
+
+    wall, ms = timed_calls(call, steps, warmup)
+    avg = float(np.mean(ms))
+    nb = conv_bytes(B * T, Cn, K, B)
+    gbs = nb / (avg * 1e-3) / 1e9
+    return {"workload": f"short causal depthwise conv, {B} x {T} tokens, {Cn} channels (q, k, v of 16 heads x 128), "
+                        f"width {K}, bf16 in and out, zero caches",
+            "tokens_per_s": round(B * T / (wall / steps), 1), "us_per_call": round(avg * 1e3, 2),
+            "algorithmic_bytes": nb,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+
+
 def bench_step(kda, name, steps, warmup):
     """kda_step timed per call with HIP events; before every call a 1 GiB
     buffer is read (clean lines, nothing to write back) so the state (128 MiB
@@ -455,7 +490,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "varlen", "step", "backward", "copy"], default="all",
+    ap.add_argument("--only", choices=["all", "prefill", "varlen", "step", "backward", "conv", "copy"],
+                    default="all",
                     help="restrict the run (profiling); the JSON line needs 'all'")
     ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
                     help="rocprofv3 csv dirs: prefill FETCH_SIZE, prefill WRITE_SIZE, copy FETCH_SIZE, "
@@ -497,6 +533,9 @@ def main():
     if args.only in ("all", "backward"):
         res["backward"] = bench_backward(kda, args.steps, args.warmup)
         print(f"backward {res['backward']['us_per_call']} us per call", file=sys.stderr, flush=True)
+    if args.only in ("all", "conv"):
+        res["short_conv"] = bench_conv(kda, args.steps, args.warmup)
+        print(f"short conv {res['short_conv']['us_per_call']} us per call", file=sys.stderr, flush=True)
     if args.only in ("all", "step"):
         res["decode"] = bench_step(kda, "decode", args.steps, args.warmup)
         res["verify"] = bench_step(kda, "verify", args.steps, args.warmup)
@@ -542,6 +581,7 @@ def main():
         "verify": res["verify"],
         "verify_rollback": res["verify_rollback"],
         "backward": res["backward"],
+        "short_conv": res["short_conv"],
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p["inp"])

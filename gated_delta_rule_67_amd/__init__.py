@@ -22,7 +22,8 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "step", "step_rows", "step_commit", "workspace_bytes", "bwd_workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_bwd", "step", "step_rows", "step_commit", "short_conv", "workspace_bytes",
+           "bwd_workspace_bytes",
            "abi_version", "KdaError", "LIB_PATH", "KDA_F32", "KDA_BF16"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
@@ -66,6 +67,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [D, ctypes.c_int]
     lib.kda_chunk_bwd.restype = ctypes.c_int
     lib.kda_chunk_bwd.argtypes = [D] + [P] * 15 + [P]
+    lib.kda_short_conv.restype = ctypes.c_int
+    lib.kda_short_conv.argtypes = [D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, P]
     lib.kda_step.restype = ctypes.c_int
     lib.kda_step.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P]
     lib.kda_step_rows.restype = ctypes.c_int
@@ -241,6 +244,47 @@ def chunk_bwd(q, k, v, log_g, beta, d_out, init_state=None, cu_seqlens=None, d_f
                              _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_g"]), _ptr(g["dbeta"]),
                              _ptr(g["d_init_state"]), _stream(stream)))
     return g
+
+
+def short_conv(x, weight, cu_seqlens=None, init_cache=None, activation=0, out=None, final_cache=None,
+               stream=None):
+    """Short causal depthwise convolution of x [B, T, channels] (fp32 or bf16)
+    with ``weight`` [channels, K] (fp32), resetting at the documents of
+    ``cu_seqlens`` (packed, B == 1).  ``init_cache`` [N, channels, K-1] holds
+    the K-1 inputs before each sequence (None: zeros).  ``activation`` 0 is the
+    identity, 1 SiLU.  Returns (out like x, final_cache [N, channels, K-1]
+    fp32); pass ``final_cache=False`` to skip it, or a tensor (it may be
+    ``init_cache`` itself for dense sequences of 1, 2, 4, 8, 16 or 32 tokens)."""
+    B, T, Cn = x.shape
+    K = weight.shape[1]
+    dev = x.device
+    code = _dtype_code(x)
+    _need(weight, "weight", (Cn, K), torch.float32, dev)
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed mode takes a single row (B == 1)")
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
+        N, L = cu_seqlens.shape[0] - 1, T
+    else:
+        N, L = B, T
+    if init_cache is not None:
+        _need(init_cache, "init_cache", (N, Cn, K - 1), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _need(out, "out", (B, T, Cn), x.dtype, dev)
+    if final_cache is None:
+        final_cache = torch.empty((N, Cn, K - 1), dtype=torch.float32, device=dev)
+    elif final_cache is False:
+        final_cache = None
+    else:
+        _need(final_cache, "final_cache", (N, Cn, K - 1), torch.float32, dev)
+    desc = make_desc(N, L, 1, 16, 16, code)
+    fc = final_cache if (final_cache is not None and final_cache.numel() > 0) else None
+    ic = init_cache if (init_cache is not None and init_cache.numel() > 0) else None
+    _check(lib.kda_short_conv(ctypes.byref(desc), Cn, K, int(activation), _ptr(x), _ptr(weight), _ptr(cu_seqlens),
+                              _ptr(ic), _ptr(out), _ptr(fc), _stream(stream)))
+    return out, final_cache
 
 
 def step(q, k, v, log_g, beta, state, scale=None, out=None, stream=None):

@@ -341,4 +341,51 @@ kda_status kda_chunk_bwd(const kda_desc* d, const void* q, const void* k, const 
   return KDA_OK;
 }
 
+kda_status kda_short_conv(const kda_desc* d, int32_t channels, int32_t kernel_size, int32_t activation,
+                          const void* x, const float* weight, const int32_t* cu_seqlens, const float* init_cache,
+                          void* out, float* final_cache, void* stream) {
+  static const char* fn = "kda_short_conv";
+  if (!d) return fail(KDA_ERR_NULL, "%s: desc is NULL", fn);
+  if (d->num_seqs < 0 || d->seq_len < 0)
+    return fail(KDA_ERR_SHAPE, "%s: need num_seqs >= 0 and seq_len >= 0 (got %d, %d)", fn, d->num_seqs, d->seq_len);
+  if (d->qkv_dtype != KDA_F32 && d->qkv_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "%s: unknown qkv_dtype %d", fn, d->qkv_dtype);
+  if (channels <= 0 || channels % 8 != 0)
+    return fail(KDA_ERR_SHAPE, "%s: channels must be a positive multiple of 8 (got %d)", fn, channels);
+  if (kernel_size < 1 || kernel_size > 8)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: kernel_size %d not in [1, 8]", fn, kernel_size);
+  if (activation != 0 && activation != 1)
+    return fail(KDA_ERR_SHAPE, "%s: activation must be 0 (identity) or 1 (SiLU), got %d", fn, activation);
+  const bool packed = cu_seqlens != nullptr;
+  const int64_t tokens = packed ? d->seq_len : static_cast<int64_t>(d->num_seqs) * d->seq_len;
+  if (tokens * channels > (int64_t(1) << 40)) return fail(KDA_ERR_SHAPE, "%s: problem too large", fn);
+  if (tokens / 32 >= (int64_t(1) << 31)) return fail(KDA_ERR_SHAPE, "%s: too many tokens", fn);
+  if (packed && d->num_seqs == 0 && d->seq_len != 0)
+    return fail(KDA_ERR_SHAPE, "%s: packed problem with tokens but no documents", fn);
+  const bool has_tok = tokens > 0;
+  kda_status st;
+  if ((st = check_ptr(x, "x", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(out, "out", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(weight, "weight", fn, has_tok || (final_cache && d->num_seqs > 0))) != KDA_OK) return st;
+  if ((st = check_ptr(cu_seqlens, "cu_seqlens", fn, false)) != KDA_OK) return st;
+  if ((st = check_ptr(init_cache, "init_cache", fn, false)) != KDA_OK) return st;
+  if ((st = check_ptr(final_cache, "final_cache", fn, false)) != KDA_OK) return st;
+  if (out && (out == x || out == static_cast<const void*>(weight) || out == init_cache || out == final_cache))
+    return fail(KDA_ERR_SHAPE, "%s: out aliases another argument", fn);
+  // In place (final_cache == init_cache) only where every document is read and
+  // written by one thread: dense sequences whose length divides the kernel's
+  // 32-token run, so that no sequence straddles two runs.
+  if (init_cache && final_cache == init_cache && (packed || d->seq_len == 0 || 32 % d->seq_len != 0))
+    return fail(KDA_ERR_SHAPE, "%s: final_cache may alias init_cache only for dense sequences of 1, 2, 4, 8, 16 "
+                "or 32 tokens", fn);
+  if (d->num_seqs == 0 || (!has_tok && !final_cache)) return KDA_OK;
+  kda::ConvLaunch a{};
+  a.x = x; a.weight = weight; a.cu_seqlens = cu_seqlens; a.init_cache = init_cache; a.final_cache = final_cache;
+  a.out = out; a.num_seqs = d->num_seqs; a.seq_len = d->seq_len; a.channels = channels;
+  a.kernel_size = kernel_size; a.activation = activation; a.bf16 = d->qkv_dtype == KDA_BF16;
+  const hipError_t e = kda::launch_short_conv(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return KDA_OK;
+}
+
 }  // extern "C"

@@ -107,6 +107,24 @@ hipError_t launch_chunk_bwd(const BwdLaunch& a, hipStream_t stream);
 bool bwd_supported(const BwdLaunch& a);
 size_t bwd_workspace_bytes(int num_seqs, int seq_len, int num_heads, int d, bool packed);
 
+// Arguments of one short causal depthwise convolution; shapes already validated.
+struct ConvLaunch {
+  const void* x;
+  const float* weight;        // [channels, kernel_size]
+  const int32_t* cu_seqlens;  // may be null (dense)
+  const float* init_cache;    // may be null (zeros)
+  float* final_cache;         // may be null
+  void* out;
+  int num_seqs;
+  int seq_len;
+  int channels;
+  int kernel_size;            // 1..8
+  int activation;             // 0 identity, 1 SiLU
+  bool bf16;                  // x and out element type
+};
+
+hipError_t launch_short_conv(const ConvLaunch& a, hipStream_t stream);
+
 // Longest-first order of the documents of a packed problem (n <= 4096).
 hipError_t launch_doc_order(const int32_t* cu_seqlens, int n, int32_t* order, hipStream_t stream);
 

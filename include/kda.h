@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum {
   KDA_OK = 0,
@@ -218,6 +218,43 @@ kda_status kda_chunk_bwd(const kda_desc* desc, const void* q, const void* k,
                          const float* d_out, const float* d_final_state,
                          float* dq, float* dk, float* dv, float* dlog_g,
                          float* dbeta, float* d_init_state, void* stream);
+
+/*
+ * Short causal depthwise convolution that feeds q, k and v (NeMo
+ * glm5_next.layers, `_TorchShortConvolution`: a depthwise causal Conv1d over
+ * [batch, sequence, channels] that resets at packed boundaries; its width is
+ * the config's linear_conv_kernel_dim).  For every sequence or document n,
+ * channel c and token t of n (counted from the document start):
+ *
+ *     out[t, c] = act( sum_{j < K} weight[c, j] * xe[t - (K-1) + j, c] )
+ *
+ * where xe is the document's inputs preceded by its K-1 cached inputs
+ * init_cache[n, c, 0..K-2] (oldest first; zeros when init_cache is NULL): the
+ * window never reaches into another document.  Accumulation is fp32; out has
+ * the element type of x.
+ *
+ *   desc         num_seqs (dense B / packed N), seq_len (dense T / packed total
+ *                tokens) and qkv_dtype (element type of x and out) are read;
+ *                the other fields are ignored
+ *   channels     multiple of 8;  kernel_size K in [1, 8]
+ *   activation   0 identity (the convolution as the pages name it), 1 SiLU
+ *                applied to the sum (y / (1 + exp(-y)))
+ *   x, out       [B, T, channels] (dense) or [1, T, channels] (packed);
+ *                out must not alias x
+ *   weight       [channels, K] fp32 (a depthwise Conv1d weight without its
+ *                middle axis)
+ *   cu_seqlens   device int32 [N+1] or NULL (dense), as for kda_chunk_fwd
+ *   init_cache   [N, channels, K-1] fp32 or NULL
+ *   final_cache  [N, channels, K-1] fp32 or NULL: the last K-1 entries of xe
+ *                (the state a decode step continues from).  It may alias
+ *                init_cache only for dense sequences of 1, 2, 4, 8, 16 or 32
+ *                tokens (decode and verify); otherwise it must not.
+ * No workspace.  Returns KDA_ERR_UNSUPPORTED for K outside [1, 8].
+ */
+kda_status kda_short_conv(const kda_desc* desc, int32_t channels, int32_t kernel_size,
+                          int32_t activation, const void* x, const float* weight,
+                          const int32_t* cu_seqlens, const float* init_cache, void* out,
+                          float* final_cache, void* stream);
 
 #ifdef __cplusplus
 }

@@ -19,6 +19,8 @@ Layouts: q, k, log_g [B, T, H, dk]; v [B, T, H, dv]; beta [B, T, H];
 init_state [N, H, dk, dv]; cu_seqlens int32 [N+1].
 Upstream gradients of the backward (their own stream, ``upstream_grads``):
 d_out ~ N(0, 1) like out, d_final ~ N(0, 1) like the state.
+Short convolution (``conv_inputs``, its own stream): x ~ N(0, 1), weight
+~ N(0, 1/K), cache ~ N(0, 1).
 """
 from __future__ import annotations
 
@@ -130,6 +132,26 @@ def upstream_grads(inp: dict, seed: int, final: bool = True, final_std: float = 
     if final:
         d_final = rng.standard_normal((inp["N"], H, dk, dv), dtype=np.float32) * np.float32(final_std)
     return dict(d_out=torch.from_numpy(d_out), d_final=torch.from_numpy(d_final) if final else None)
+
+
+def conv_inputs(B: int, T: int, channels: int, K: int, dtype: str = "bf16", seed: int = 0, lengths=None,
+                cache: bool = True) -> dict:
+    """Seeded inputs of the short convolution: x ~ N(0, 1) [B, T, channels]
+    cast to ``dtype``; weight ~ N(0, 1/K) [channels, K] (fp32); init_cache ~
+    N(0, 1) [N, channels, K-1] (fp32) when ``cache``; packed when ``lengths``
+    (B == 1) is given."""
+    rng = np.random.default_rng(seed)
+    cu = None
+    if lengths is not None:
+        assert B == 1 and sum(lengths) == T
+        cu = cu_from_lengths(lengths)
+    N = len(cu) - 1 if cu is not None else B
+    x = rng.standard_normal((B, T, channels), dtype=np.float32)
+    w = rng.standard_normal((channels, K), dtype=np.float32) / np.float32(np.sqrt(K))
+    c0 = rng.standard_normal((N, channels, K - 1), dtype=np.float32) if cache else None
+    return dict(x=_cast(x, dtype), weight=torch.from_numpy(w),
+                init_cache=torch.from_numpy(c0) if c0 is not None else None,
+                cu_seqlens=torch.from_numpy(cu.astype(np.int32)) if cu is not None else None, N=N)
 
 
 def config(name: str, **overrides) -> dict:

@@ -38,7 +38,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert kda.abi_version() == 4
+    assert kda.abi_version() == 5
     seen = set()
     for code in range(8):
         s = lib.kda_status_string(code).decode()
@@ -301,3 +301,32 @@ def test_bwd_of_nothing_is_a_noop():
     # dense sequences of no tokens, no d_init requested: nothing to do
     d = bwd_desc(seq_len=0)
     assert bwd(d, **nulls) == OK
+
+
+# --------------------------------------------------------------------------- kda_short_conv
+def conv(d, channels=2048, K=4, act=0, x=P(0), w=P(1 << 20), cu=None, c0=None, out=P(2 << 20), fin=None):
+    return lib.kda_short_conv(ctypes.byref(d) if d is not None else None, channels, K, act, x, w, cu, c0, out, fin,
+                              None)
+
+
+def test_conv_validation():
+    d = desc()
+    assert conv(None) == NULL
+    assert conv(d, channels=12) == SHAPE and "multiple of 8" in last()
+    assert conv(d, K=0) == UNSUPPORTED and conv(d, K=9) == UNSUPPORTED
+    assert conv(d, act=2) == SHAPE
+    assert conv(d, x=None) == NULL and conv(d, out=None) == NULL and conv(d, w=None) == NULL
+    assert conv(d, out=P(0)) == SHAPE and "alias" in last()
+    assert conv(d, x=P(8)) == ALIGN
+    # in-place cache only for dense sequences whose length divides 32
+    assert conv(desc(seq_len=64), c0=P(3 << 20), fin=P(3 << 20)) == SHAPE
+    assert conv(desc(seq_len=5), c0=P(3 << 20), fin=P(3 << 20)) == SHAPE
+    assert conv(desc(seq_len=64), c0=P(3 << 20), fin=P(3 << 20), cu=P(4 << 20)) == SHAPE
+    bad = desc()
+    bad.qkv_dtype = 7
+    assert conv(bad) == DTYPE
+
+
+def test_conv_of_nothing_is_a_noop():
+    assert conv(desc(num_seqs=0, seq_len=0), x=None, w=None, out=None) == OK
+    assert conv(desc(seq_len=0), x=None, w=None, out=None) == OK

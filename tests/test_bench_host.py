@@ -101,3 +101,8 @@ def test_backward_bytes_and_flops_of_the_dense_workload():
     macs = 64 ** 3 // 6 + 6 * 64 * 64 * 128 + 8 * 64 * 128 * 128
     assert macs == 11_578_026
     assert bench.backward_flops(tokens, H, d) == tokens * H * 2 * macs // 64 == 94_847_188_992
+
+
+def test_conv_bytes_of_the_qkv_workload():
+    # 4 x 4096 tokens x 6144 channels of bf16 read and written, weights, final caches
+    assert bench.conv_bytes(4 * 4096, 6144, 4, 4) == 16384 * 6144 * 4 + 6144 * 4 * 4 + 4 * 6144 * 3 * 4

@@ -1,0 +1,102 @@
+"""GPU parity of kda_short_conv against the oracle's short convolution.
+
+Output and final cache are compared element by element with the fp64 oracle
+on the same seeded inputs.  fp32 x: max |gpu - oracle| / rms(oracle) <= 1e-4.
+bf16 x: the output is, by definition, the fp32 result rounded once to bf16,
+so each element must lie within one bf16 rounding of the exact value plus the
+fp32 accumulation error: |gpu - oracle| <= 2^-8 |oracle| + 1e-5 rms(oracle)
+(a relative-to-RMS bar would mistake correct rounding of large outputs, such
+as SiLU's tail, for an error).  Cases: widths 1..8,
+SiLU, ragged lengths and partial channel blocks, packed documents of edge
+lengths with caches, a decode chain that updates the cache in place, and the
+full 4 x 4096-token, 6144-channel workload.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs
+import oracle
+from gpu_helpers import TOL, err, oracle_threads
+from kda_inputs import to_f64
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # collected on CPU, skipped there
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import gated_delta_rule_67_amd as kda  # noqa: E402
+
+
+def ref(inp, act):
+    cu = inp["cu_seqlens"].numpy().astype(np.int64) if inp["cu_seqlens"] is not None else None
+    return oracle.short_conv(to_f64(inp["x"]), to_f64(inp["weight"]), cu_seqlens=cu,
+                             init_cache=to_f64(inp["init_cache"]), act=act, n_threads=oracle_threads())
+
+
+def gpu(inp, act):
+    dev = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    y, fin = kda.short_conv(dev["x"], dev["weight"], cu_seqlens=dev["cu_seqlens"], init_cache=dev["init_cache"],
+                            activation=act)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy(), fin.cpu().numpy()
+
+
+def check(tag, got, want, dtype, K):
+    ec = err(got[1], want[1]) if K > 1 else 0.0
+    if dtype == "bf16":
+        y, yr = np.asarray(got[0], dtype=np.float64), want[0]
+        assert np.all(np.isfinite(y))
+        bound = 2.0 ** -8 * np.abs(yr) + 1e-5 * np.sqrt(np.mean(yr ** 2))
+        worst = float(np.max(np.abs(y - yr) / bound))
+        print(f"[conv {tag}] out within {worst:.2f} of the bf16 bound, rms err {err(y, yr):.2e}, "
+              f"cache {ec:.2e}", flush=True)
+        assert worst <= 1.0
+    else:
+        ey = err(got[0], want[0])
+        print(f"[conv {tag}] out {ey:.2e} cache {ec:.2e}", flush=True)
+        assert ey <= TOL[dtype]
+    assert ec <= 1e-6   # the cache holds inputs: exact
+
+
+@pytest.mark.parametrize("dtype,K,act,T", [("f32", 4, 0, 37), ("bf16", 4, 1, 100), ("f32", 1, 0, 16),
+                                           ("bf16", 8, 0, 65), ("f32", 2, 1, 33), ("bf16", 3, 0, 64)])
+def test_dense(dtype, K, act, T):
+    inp = kda_inputs.conv_inputs(B=2, T=T, channels=1032, K=K, dtype=dtype, seed=300 + K + T)
+    check(f"dense {dtype} K={K} act={act} T={T}", gpu(inp, act), ref(inp, act), dtype, K)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_packed_edge_lengths(dtype):
+    lens = [0, 1, 2, 3, 31, 32, 33, 0, 64, 65, 5]
+    inp = kda_inputs.conv_inputs(B=1, T=sum(lens), channels=512, K=4, dtype=dtype, seed=310, lengths=lens)
+    got, want = gpu(inp, 0), ref(inp, 0)
+    check(f"packed {dtype}", got, want, dtype, 4)
+    for n in (0, 7):                       # empty documents keep their cache
+        np.testing.assert_array_equal(got[1][n], inp["init_cache"][n].numpy())
+
+
+def test_decode_chain_updates_the_cache_in_place():
+    """37 one-token calls, the cache updated in place, equal the one call over
+    the whole sequences (and the oracle)."""
+    B, T, Cn, K = 3, 37, 256, 4
+    inp = kda_inputs.conv_inputs(B=B, T=T, channels=Cn, K=K, dtype="f32", seed=320)
+    x, w = inp["x"].cuda(), inp["weight"].cuda()
+    cache = inp["init_cache"].cuda().clone()
+    outs = []
+    for t in range(T):
+        y, _ = kda.short_conv(x[:, t:t + 1].contiguous(), w, init_cache=cache, final_cache=cache, activation=1)
+        outs.append(y)
+    y_chain = torch.cat(outs, 1)
+    y_full, fin_full = kda.short_conv(x, w, init_cache=inp["init_cache"].cuda(), activation=1)
+    torch.cuda.synchronize()
+    assert torch.equal(y_chain, y_full)
+    assert torch.equal(cache, fin_full)
+    check("decode chain", (y_chain.cpu().numpy(), cache.cpu().numpy()), ref(inp, 1), "f32", K)
+
+
+def test_full_size_workload():
+    """4 x 4096 tokens, 6144 channels (q, k and v of 16 heads x 128 side by
+    side), K = 4, bf16, zero caches: every element against the oracle."""
+    inp = kda_inputs.conv_inputs(B=4, T=4096, channels=6144, K=4, dtype="bf16", seed=330, cache=False)
+    check("full size", gpu(inp, 0), ref(inp, 0), "bf16", 4)
