@@ -13,7 +13,8 @@ state, and packed documents reset at their boundaries (NeMo glm5_next.layers,
 ``_torch_recurrent_kda``); its reverse mode, the same loop differentiated
 token by token (that page documents the recurrence as differentiable); and the
 short causal depthwise convolution that feeds q, k and v
-(``_TorchShortConvolution``).  This module only marshals numpy arrays.
+(``_TorchShortConvolution``); and the gated per-head RMSNorm on the output
+(``_TorchRMSNormGated``).  This module only marshals numpy arrays.
 """
 from __future__ import annotations
 
@@ -53,6 +54,8 @@ def load(path: str = LIB_PATH):
                                         ctypes.c_double, dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_int]
     lib.kda_oracle_short_conv.restype = ctypes.c_int
     lib.kda_oracle_short_conv.argtypes = [i64, i64, i64, i64, dp, dp, ip, dp, ctypes.c_int, dp, dp, ctypes.c_int]
+    lib.kda_oracle_gated_rmsnorm.restype = ctypes.c_int
+    lib.kda_oracle_gated_rmsnorm.argtypes = [i64, i64, dp, dp, dp, ctypes.c_double, dp]
     lib.kda_oracle_threads.restype = ctypes.c_int
     lib.kda_oracle_threads.argtypes = [ctypes.c_int]
     return lib
@@ -202,3 +205,18 @@ def short_conv(x, w, cu_seqlens=None, init_cache=None, act: int = 0, n_threads: 
     if rc != 0:
         raise ValueError(f"kda_oracle_short_conv failed with code {rc}")
     return y, fin
+
+
+def gated_rmsnorm(o, g, w, eps: float, lib=None):
+    """Gated per-head RMSNorm over the last axis: o, g [..., D]; w [D].
+    Returns y shaped like o (float64)."""
+    lib = lib or _get_lib()
+    o, g, w = _f64(o), _f64(g), _f64(w)
+    assert g.shape == o.shape and w.shape == (o.shape[-1],)
+    D = o.shape[-1]
+    rows = o.size // D
+    y = np.zeros(o.shape)
+    rc = lib.kda_oracle_gated_rmsnorm(rows, D, _ptr(o), _ptr(g), _ptr(w), float(eps), _ptr(y))
+    if rc != 0:
+        raise ValueError(f"kda_oracle_gated_rmsnorm failed with code {rc}")
+    return y

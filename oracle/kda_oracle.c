@@ -328,6 +328,26 @@ int kda_oracle_short_conv(int64_t num_seqs, int64_t seq_len, int64_t channels,
   return failed ? -4 : 0;
 }
 
+/* Gated per-head RMSNorm, one row at a time: the mean square over the head
+ * dim, the normalised row times the weight, then the sigmoid gate. */
+int kda_oracle_gated_rmsnorm(int64_t rows, int64_t D, const double* o, const double* g,
+                             const double* w, double eps, double* y) {
+  if (!o || !g || !w || !y) return -1;
+  if (rows < 0 || D <= 0 || !(eps >= 0.0)) return -2;
+  for (int64_t r = 0; r < rows; ++r) {
+    const double* orow = o + r * D;
+    double ms = 0.0;
+    for (int64_t i = 0; i < D; ++i) ms += orow[i] * orow[i];
+    ms /= (double)D;
+    const double inv = 1.0 / sqrt(ms + eps);
+    for (int64_t i = 0; i < D; ++i) {
+      const double gate = 1.0 / (1.0 + exp(-g[r * D + i]));
+      y[r * D + i] = orow[i] * inv * w[i] * gate;
+    }
+  }
+  return 0;
+}
+
 int kda_oracle_threads(int n_threads) {
 #ifdef _OPENMP
   return n_threads > 0 ? n_threads : omp_get_max_threads();

@@ -95,6 +95,18 @@ int kda_oracle_short_conv(int64_t num_seqs, int64_t seq_len, int64_t channels,
                           const int64_t* cu_seqlens, const double* init_cache,
                           int act, double* y, double* final_cache, int n_threads);
 
+/* Gated per-head RMSNorm on the mixer output (NeMo glm5_next.layers,
+ * `_TorchRMSNormGated`: normalise [batch, sequence, heads, head_dim], then
+ * gate with a sigmoid; its base RMSNorm accumulates the variance in fp32, and
+ * the metrale glm5next_layer invariants fix every norm as x * w / rms, never
+ * x * (1 + w) / rms).  For every row r (a token and head) of head_dim D:
+ *
+ *     y[r, i] = o[r, i] / sqrt(mean_i(o[r, :]^2) + eps) * w[i] * sigmoid(g[r, i])
+ *
+ * o, g, y: [rows, D]; w: [D].  Returns 0, or -1 NULL pointer / -2 bad size. */
+int kda_oracle_gated_rmsnorm(int64_t rows, int64_t D, const double* o, const double* g,
+                             const double* w, double eps, double* y);
+
 /* Number of OpenMP threads a call with n_threads would use. */
 int kda_oracle_threads(int n_threads);
 

@@ -4,8 +4,8 @@ Each mutant is a textual edit of a *copy* of ``oracle/kda_oracle.c`` (a dropped
 term, a wrong sign, a wrong index or axis, a transposed operand, a missing
 reset, a wrong step order), compiled to a temporary library and run against
 ``test_oracle_pins.py`` (forward mutants), ``test_oracle_bwd_pins.py``
-(reverse-mode mutants) or ``test_oracle_conv_pins.py`` (convolution mutants)
-in a subprocess (a mutant may read out of bounds, so it
+(reverse-mode mutants), ``test_oracle_conv_pins.py`` (convolution mutants) or
+``test_oracle_norm_pins.py`` (norm mutants) in a subprocess (a mutant may read out of bounds, so it
 never runs in this process).  The committed oracle is never modified.
 """
 import os
@@ -88,6 +88,20 @@ CONV_MUTANTS = {
 }
 
 
+# planted mistakes in the gated RMSNorm
+NORM_MUTANTS = {
+    "norm_one_plus_weight": ("y[r * D + i] = orow[i] * inv * w[i] * gate;",
+                             "y[r * D + i] = orow[i] * inv * (1.0 + w[i]) * gate;"),
+    "norm_eps_outside_sqrt": ("const double inv = 1.0 / sqrt(ms + eps);", "const double inv = 1.0 / (sqrt(ms) + eps);"),
+    "norm_sum_not_mean": ("ms /= (double)D;", "(void)0;"),
+    "norm_silu_gate": ("const double gate = 1.0 / (1.0 + exp(-g[r * D + i]));",
+                       "const double gate = g[r * D + i] / (1.0 + exp(-g[r * D + i]));"),
+    "norm_gate_inside_rms": ("    for (int64_t i = 0; i < D; ++i) ms += orow[i] * orow[i];",
+                             "    for (int64_t i = 0; i < D; ++i) ms += orow[i] * orow[i] / (1.0 + exp(-g[r * D + i]));"),
+    "norm_no_sqrt": ("const double inv = 1.0 / sqrt(ms + eps);", "const double inv = 1.0 / (ms + eps);"),
+}
+
+
 def _mutate_in(src, func, old, new, name):
     """Replace `old` by `new` inside the body of the C function starting with
     `func` (up to the next top-level closing brace); `old` must occur exactly
@@ -144,7 +158,8 @@ def _build(workdir, name, src_text):
 
 def test_unmutated_copy_passes(workdir):
     lib = _build(workdir, "clean", open(SRC).read())
-    for pins in ("test_oracle_pins.py", "test_oracle_bwd_pins.py", "test_oracle_conv_pins.py"):
+    for pins in ("test_oracle_pins.py", "test_oracle_bwd_pins.py", "test_oracle_conv_pins.py",
+                 "test_oracle_norm_pins.py"):
         rc, out = _run_pins(lib, pins)
         assert rc == 0, out
 
@@ -181,3 +196,12 @@ def test_conv_mutant_is_caught(workdir, name):
     mutated = _mutate_in(src, "int kda_oracle_short_conv(", old, new, name)
     rc, out = _run_pins(_build(workdir, name, mutated), "test_oracle_conv_pins.py")
     assert rc != 0, f"mutant {name} survived the convolution pins:\n{out}"
+
+
+@pytest.mark.parametrize("name", sorted(NORM_MUTANTS))
+def test_norm_mutant_is_caught(workdir, name):
+    src = open(SRC).read()
+    old, new = NORM_MUTANTS[name]
+    mutated = _mutate_in(src, "int kda_oracle_gated_rmsnorm(", old, new, name)
+    rc, out = _run_pins(_build(workdir, name, mutated), "test_oracle_norm_pins.py")
+    assert rc != 0, f"mutant {name} survived the norm pins:\n{out}"
