@@ -1,7 +1,7 @@
 """Benchmark of libkda on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --only {prefill,varlen,step,backward,conv,copy}      (profiling runs)
+    python bench.py --only {prefill,varlen,step,backward,conv,norm,copy}      (profiling runs)
     python bench.py --traffic-from FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
 
 A step is one kda_chunk_fwd call (chunked prefill) over the dense workload
@@ -14,6 +14,8 @@ fp32 out, with inputs resident in HBM.  ``value`` is prefill tokens/s
                 16-bit MFMA peak
   varlen        the packed 65536-token, 32-head prefill: tokens/s and its own
                 HBM roofline (beside the headline, not part of it)
+  gated_rmsnorm kda_gated_rmsnorm on the dense workload's output (fp32 o,
+                bf16 gate and out): its own HBM roofline
   short_conv    kda_short_conv over q, k, v of the dense workload (6144
                 channels, width 4, bf16): its own HBM roofline
   backward      kda_chunk_bwd on the dense workload: tokens/s and its roofline
@@ -316,6 +318,37 @@ def bench_conv(kda, steps, warmup):
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
 
 
+def norm_bytes(rows: int, d: int, o_bytes=4, gate_bytes=2, out_bytes=2) -> int:
+    """Algorithmic HBM bytes of one kda_gated_rmsnorm call: o and the gate read,
+    out written once, the weight."""
+    return rows * d * (o_bytes + gate_bytes + out_bytes) + d * 4
+
+
+def bench_norm(kda, steps, warmup):
+    """kda_gated_rmsnorm on the mixer output of the dense workload (4 x 4096
+    tokens x 16 heads x 128: fp32 o, bf16 gate, bf16 out), timed like the
+    prefill."""
+    B, T, H, D = 4, 4096, 16, 128
+    rng = np.random.default_rng(420)
+    o = torch.from_numpy(rng.standard_normal((B, T, H, D), dtype=np.float32)).cuda()
+    g = torch.from_numpy(rng.standard_normal((B, T, H, D), dtype=np.float32)).to(torch.bfloat16).cuda()
+    w = torch.from_numpy(rng.standard_normal(D).astype(np.float32)).cuda()
+    out = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        kda.gated_rmsnorm(o, g, w, 1e-6, out=out)
+
+    wall, ms = timed_calls(call, steps, warmup)
+    avg = float(np.mean(ms))
+    nb = norm_bytes(B * T * H, D)
+    gbs = nb / (avg * 1e-3) / 1e9
+    return {"workload": f"gated per-head RMSNorm, {B} x {T} tokens x {H} heads x {D}, fp32 o, bf16 gate, bf16 out",
+            "tokens_per_s": round(B * T / (wall / steps), 1), "us_per_call": round(avg * 1e3, 2),
+            "algorithmic_bytes": nb,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+
+
 def bench_step(kda, name, steps, warmup):
     """kda_step timed per call with HIP events; before every call a 1 GiB
     buffer is read (clean lines, nothing to write back) so the state (128 MiB
@@ -490,7 +523,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "varlen", "step", "backward", "conv", "copy"],
+    ap.add_argument("--only", choices=["all", "prefill", "varlen", "step", "backward", "conv", "norm", "copy"],
                     default="all",
                     help="restrict the run (profiling); the JSON line needs 'all'")
     ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
@@ -536,6 +569,9 @@ def main():
     if args.only in ("all", "conv"):
         res["short_conv"] = bench_conv(kda, args.steps, args.warmup)
         print(f"short conv {res['short_conv']['us_per_call']} us per call", file=sys.stderr, flush=True)
+    if args.only in ("all", "norm"):
+        res["gated_rmsnorm"] = bench_norm(kda, args.steps, args.warmup)
+        print(f"gated rmsnorm {res['gated_rmsnorm']['us_per_call']} us per call", file=sys.stderr, flush=True)
     if args.only in ("all", "step"):
         res["decode"] = bench_step(kda, "decode", args.steps, args.warmup)
         res["verify"] = bench_step(kda, "verify", args.steps, args.warmup)
@@ -582,6 +618,7 @@ def main():
         "verify_rollback": res["verify_rollback"],
         "backward": res["backward"],
         "short_conv": res["short_conv"],
+        "gated_rmsnorm": res["gated_rmsnorm"],
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p["inp"])

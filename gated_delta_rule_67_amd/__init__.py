@@ -22,7 +22,8 @@ import os
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "step", "step_rows", "step_commit", "short_conv", "workspace_bytes",
+__all__ = ["chunk_fwd", "chunk_bwd", "step", "step_rows", "step_commit", "short_conv", "gated_rmsnorm",
+           "workspace_bytes",
            "bwd_workspace_bytes",
            "abi_version", "KdaError", "LIB_PATH", "KDA_F32", "KDA_BF16"]
 
@@ -69,6 +70,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_bwd.argtypes = [D] + [P] * 15 + [P]
     lib.kda_short_conv.restype = ctypes.c_int
     lib.kda_short_conv.argtypes = [D, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P, P, P, P]
+    lib.kda_gated_rmsnorm.restype = ctypes.c_int
+    lib.kda_gated_rmsnorm.argtypes = [D, P, P, P, ctypes.c_float, P, P]
     lib.kda_step.restype = ctypes.c_int
     lib.kda_step.argtypes = [D, P, P, P, P, P, P, ctypes.c_int32, P, P]
     lib.kda_step_rows.restype = ctypes.c_int
@@ -285,6 +288,29 @@ def short_conv(x, weight, cu_seqlens=None, init_cache=None, activation=0, out=No
     _check(lib.kda_short_conv(ctypes.byref(desc), Cn, K, int(activation), _ptr(x), _ptr(weight), _ptr(cu_seqlens),
                               _ptr(ic), _ptr(out), _ptr(fc), _stream(stream)))
     return out, final_cache
+
+
+def gated_rmsnorm(o, gate, weight, eps, out=None, out_dtype=torch.bfloat16, stream=None):
+    """Gated per-head RMSNorm of the mixer output o [B, T, H, D] (fp32) with
+    ``gate`` like o (fp32 or bf16) and ``weight`` [D] (fp32):
+    o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate) per (token, head).
+    Returns out [B, T, H, D] in ``out_dtype`` (bf16 or fp32; ``out`` may be o
+    itself when fp32)."""
+    B, T, H, D = o.shape
+    dev = o.device
+    _need(o, "o", (B, T, H, D), torch.float32, dev)
+    _need(gate, "gate", (B, T, H, D), gate.dtype, dev)
+    g_code = _dtype_code(gate)
+    _need(weight, "weight", (D,), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, D), dtype=out_dtype, device=dev)
+    else:
+        _need(out, "out", (B, T, H, D), out.dtype, dev)
+    desc = make_desc(B, T, H, D, D, g_code)
+    desc.out_dtype = _dtype_code(out)
+    _check(lib.kda_gated_rmsnorm(ctypes.byref(desc), _ptr(o), _ptr(gate), _ptr(weight), ctypes.c_float(eps),
+                                 _ptr(out), _stream(stream)))
+    return out
 
 
 def step(q, k, v, log_g, beta, state, scale=None, out=None, stream=None):

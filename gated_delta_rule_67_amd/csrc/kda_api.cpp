@@ -388,4 +388,36 @@ kda_status kda_short_conv(const kda_desc* d, int32_t channels, int32_t kernel_si
   return KDA_OK;
 }
 
+kda_status kda_gated_rmsnorm(const kda_desc* d, const float* o, const void* gate, const float* weight, float eps,
+                             void* out, void* stream) {
+  static const char* fn = "kda_gated_rmsnorm";
+  if (!d) return fail(KDA_ERR_NULL, "%s: desc is NULL", fn);
+  if (d->num_seqs < 0 || d->seq_len < 0 || d->num_heads <= 0)
+    return fail(KDA_ERR_SHAPE, "%s: need num_seqs >= 0, seq_len >= 0, num_heads > 0", fn);
+  if (d->qkv_dtype != KDA_F32 && d->qkv_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "%s: unknown qkv_dtype %d", fn, d->qkv_dtype);
+  if (d->out_dtype != KDA_F32 && d->out_dtype != KDA_BF16)
+    return fail(KDA_ERR_DTYPE, "%s: unknown out_dtype %d", fn, d->out_dtype);
+  if (d->dv != 16 && d->dv != 32 && d->dv != 64 && d->dv != 128)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: head dim %d not in {16, 32, 64, 128}", fn, d->dv);
+  if (!std::isfinite(eps) || eps < 0.f) return fail(KDA_ERR_SHAPE, "%s: eps must be finite and >= 0", fn);
+  const int64_t rows = static_cast<int64_t>(d->num_seqs) * d->seq_len * d->num_heads;
+  if (rows > (int64_t(1) << 34)) return fail(KDA_ERR_SHAPE, "%s: too many rows", fn);
+  const bool any = rows > 0;
+  kda_status st;
+  if ((st = check_ptr(o, "o", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(gate, "gate", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(weight, "weight", fn, any)) != KDA_OK) return st;
+  if ((st = check_ptr(out, "out", fn, any)) != KDA_OK) return st;
+  // in place over o is fine with fp32 out (each lane reads its channels before writing them)
+  if (out && (out == gate || out == static_cast<const void*>(weight) ||
+              (out == static_cast<const void*>(o) && d->out_dtype != KDA_F32)))
+    return fail(KDA_ERR_SHAPE, "%s: out aliases gate or weight, or o with a bf16 out", fn);
+  if (!any) return KDA_OK;
+  kda::NormLaunch a{o, gate, weight, out, rows, d->dv, eps, d->qkv_dtype == KDA_BF16, d->out_dtype == KDA_BF16};
+  const hipError_t e = kda::launch_gated_rmsnorm(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  return KDA_OK;
+}
+
 }  // extern "C"

@@ -125,6 +125,21 @@ struct ConvLaunch {
 
 hipError_t launch_short_conv(const ConvLaunch& a, hipStream_t stream);
 
+// Arguments of one gated per-head RMSNorm; shapes already validated.
+struct NormLaunch {
+  const float* o;       // [rows, d]
+  const void* gate;     // [rows, d]
+  const float* weight;  // [d]
+  void* out;            // [rows, d]
+  int64_t rows;
+  int d;
+  float eps;
+  bool gate_bf16;
+  bool out_bf16;
+};
+
+hipError_t launch_gated_rmsnorm(const NormLaunch& a, hipStream_t stream);
+
 // Longest-first order of the documents of a packed problem (n <= 4096).
 hipError_t launch_doc_order(const int32_t* cu_seqlens, int n, int32_t* order, hipStream_t stream);
 

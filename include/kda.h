@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum {
   KDA_OK = 0,
@@ -255,6 +255,29 @@ kda_status kda_short_conv(const kda_desc* desc, int32_t channels, int32_t kernel
                           int32_t activation, const void* x, const float* weight,
                           const int32_t* cu_seqlens, const float* init_cache, void* out,
                           float* final_cache, void* stream);
+
+/*
+ * Gated per-head RMSNorm on the mixer output (NeMo glm5_next.layers,
+ * `_TorchRMSNormGated`: normalise [batch, sequence, heads, head_dim], then gate
+ * with a sigmoid; the base RMSNorm accumulates the variance in fp32, and every
+ * norm is x * w / rms, never x * (1 + w) / rms, per the metrale
+ * glm5next_layer invariants).  For every token and head (a row of D = desc->dv
+ * channels):
+ *
+ *     out[i] = o[i] / sqrt(mean(o^2) + eps) * weight[i] * sigmoid(gate[i])
+ *
+ *   desc    rows = num_seqs * seq_len * num_heads (a packed row: num_seqs = 1,
+ *           seq_len = tokens); dv in {16, 32, 64, 128}; qkv_dtype is the
+ *           element type of gate, out_dtype that of out (fp32 or bf16);
+ *           dk, scale and the workspace are ignored
+ *   o       [rows, D] fp32 (the output of kda_chunk_fwd or kda_step)
+ *   gate    [rows, D];  weight [D] fp32 (shared by the heads);  eps >= 0
+ *   out     [rows, D]; may be o itself when out_dtype is fp32, must not alias
+ *           gate or weight
+ * bf16 out is rounded to nearest even once, from the fp32 result.
+ */
+kda_status kda_gated_rmsnorm(const kda_desc* desc, const float* o, const void* gate,
+                             const float* weight, float eps, void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -38,7 +38,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert kda.abi_version() == 5
+    assert kda.abi_version() == 6
     seen = set()
     for code in range(8):
         s = lib.kda_status_string(code).decode()
@@ -330,3 +330,22 @@ def test_conv_validation():
 def test_conv_of_nothing_is_a_noop():
     assert conv(desc(num_seqs=0, seq_len=0), x=None, w=None, out=None) == OK
     assert conv(desc(seq_len=0), x=None, w=None, out=None) == OK
+
+
+# --------------------------------------------------------------------------- kda_gated_rmsnorm
+def rmsnorm(d, o=P(0), g=P(1 << 20), w=P(2 << 20), eps=1e-6, out=P(3 << 20)):
+    return lib.kda_gated_rmsnorm(ctypes.byref(d) if d is not None else None, o, g, w, ctypes.c_float(eps), out, None)
+
+
+def test_rmsnorm_validation():
+    d = desc()
+    assert rmsnorm(None) == NULL
+    assert rmsnorm(d, o=None) == NULL and rmsnorm(d, g=None) == NULL and rmsnorm(d, w=None) == NULL
+    assert rmsnorm(d, out=None) == NULL
+    assert rmsnorm(d, eps=-1.0) == SHAPE and rmsnorm(d, eps=float("inf")) == SHAPE
+    assert rmsnorm(desc(dk=96, dv=96)) == UNSUPPORTED
+    assert rmsnorm(d, out=P(1 << 20)) == SHAPE                  # out aliases gate
+    d.out_dtype = kda.KDA_BF16
+    assert rmsnorm(d, out=P(0)) == SHAPE                        # bf16 out over fp32 o
+    assert rmsnorm(d, g=P(4)) == ALIGN
+    assert rmsnorm(desc(num_seqs=0), o=None, g=None, w=None, out=None) == OK

@@ -106,3 +106,8 @@ def test_backward_bytes_and_flops_of_the_dense_workload():
 def test_conv_bytes_of_the_qkv_workload():
     # 4 x 4096 tokens x 6144 channels of bf16 read and written, weights, final caches
     assert bench.conv_bytes(4 * 4096, 6144, 4, 4) == 16384 * 6144 * 4 + 6144 * 4 * 4 + 4 * 6144 * 3 * 4
+
+
+def test_norm_bytes_of_the_output_workload():
+    # 262144 rows of 128: fp32 o and bf16 gate read, bf16 out written; the weight
+    assert bench.norm_bytes(4 * 4096 * 16, 128) == 262144 * 128 * 8 + 512
