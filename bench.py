@@ -63,7 +63,8 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (matrix and vector), TFLOP/s
 CHUNK = 64
 COPY_BYTES = 512 << 20         # calibration copy: bytes read (= bytes written)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_dense.txt")
-KERNEL_SOURCES = ["kda_twopass.hip", "kda_common.h", "kda_fallback.h", "kda_api.cpp", "kda_launch.h"]
+# the files that define the two prefill kernels (their code, not the ABI around them)
+KERNEL_SOURCES = ["kda_twopass.hip", "kda_common.h", "kda_fallback.h"]
 
 
 def sources_hash() -> str:
