@@ -880,15 +880,19 @@ struct GsL {
   static constexpr int RE = RB + C;            // b_C [D]
   static constexpr int RY = RE + D;            // dgamma [D]
   static constexpr int RW = RY + D;            // per-wave column sums [4][D]
-  static constexpr int RQ = RW + 4 * D;        // dbeta rows [C]
-  static constexpr int FLOATS = RQ + C;
+  static constexpr int RQ = RW + 4 * D;        // dbeta rows, two halves [2][C]
+  static constexpr int FLOATS = RQ + 2 * C;
   static constexpr size_t BYTES = sizeof(float) * FLOATS;
 };
 
+constexpr int NTS = 512;  // bwd_gstate: 8 waves, two per token block
+
 template <int D, typename In>
-__global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
+__global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
   using P = GsL<D>;
-  constexpr int LD = P::LD, LM = P::LM, NCT = D / 16, NB = NCT < 4 ? NCT : 4;
+  constexpr int LD = P::LD, LM = P::LM, NCT = D / 16;
+  // wave wv: token block w = wv & 3, channel tiles [ctb, ctb + NCTH)
+  constexpr int NCTH = NCT >= 2 ? NCT / 2 : 1, NB = NCTH < 4 ? NCTH : 4;
   extern __shared__ __align__(16) float sm[];
   float* sS = sm + P::RS;
   float* sX = sm + P::RX;
@@ -898,12 +902,15 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
   float* sEg = sm + P::RE;
   float* sGam = sm + P::RY;
   float* sCol = sm + P::RW;
-  float* sDb = sm + P::RQ;
+  float* sDb = sm + P::RQ;  // [2][C]: the two halves of each row's dbeta
 
   const int slot = blockIdx.x / a.H, h = blockIdx.x - slot * a.H;
   Loc L;
   if (!locate(a, slot, L)) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, w = wv & 3, half = wv >> 2;
+  const int r = lane & 15, kq = lane >> 4;
+  const int ctb = half * NCTH;
+  const bool active = ctb < NCT;
   const size_t sh = static_cast<size_t>(slot) * a.H + h;
   const In* q = static_cast<const In*>(a.q);
   const In* k = static_cast<const In*>(a.k);
@@ -911,16 +918,14 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
   const int H = a.H;
   auto row = [&](int t) { return (L.tok0 + t) * H + h; };
 
-  if (tid < C) {
-    sBeta[tid] = tid < L.count ? a.beta[row(tid)] : 0.f;
-    sDb[tid] = 0.f;
-  }
-  load_mat_t<C, C, LM>(sT, a.Tm + sh * C * C);   // T^T
-  load_mat_t<C, D, LM>(sX, a.dDl + sh * C * D);  // dDelta^T
-  load_rows<D, LD>(sR, a.log_g, L.tok0, L.count, H, h);  // log_g rows (0 past the end)
+  if (tid < C) sBeta[tid] = tid < L.count ? a.beta[row(tid)] : 0.f;
+  if (tid < 2 * C) sDb[tid] = 0.f;
+  load_mat_t<C, C, LM, NTS>(sT, a.Tm + sh * C * C);   // T^T
+  load_mat_t<C, D, LM, NTS>(sX, a.dDl + sh * C * D);  // dDelta^T
+  load_rows<D, LD, float, NTS>(sR, a.log_g, L.tok0, L.count, H, h);  // log_g rows (0 past the end)
   __syncthreads();
   // per channel: b_t into sR, r(C-1, t) into sS (staging), b_C into sEg
-  for (int i = tid; i < D; i += NT) {
+  for (int i = tid; i < D; i += NTS) {
     float rr = 1.f;
     for (int t = C - 1; t >= 0; --t) {
       sS[t * LD + i] = rr;
@@ -934,89 +939,95 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
     sEg[i] = b;
   }
   __syncthreads();
-  float bb[NCT][4], rc[NCT][4], kv[NCT][4];
+  float bb[NCTH][4], rc[NCTH][4], kv[NCTH][4];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
+  for (int c = 0; c < NCTH; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int t = 16 * w + 4 * kq + j, i = 16 * ct + r;
-      bb[ct][j] = sR[t * LD + i];
-      rc[ct][j] = sS[t * LD + i];
-      kv[ct][j] = t < L.count ? to_f32(k[row(t) * D + i]) : 0.f;
+      const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + c) + r;
+      bb[c][j] = active ? sR[t * LD + i] : 0.f;
+      rc[c][j] = active ? sS[t * LD + i] : 0.f;
+      kv[c][j] = active && t < L.count ? to_f32(k[row(t) * D + i]) : 0.f;
     }
   __syncthreads();
   // dR = T^T dDelta -> sR;  dv = beta dR.  (T^T)[t][s] = 0 for s < t.
+  if (active) {
 #pragma unroll
-  for (int c0 = 0; c0 < NCT; c0 += NB) {
-    f32x4 acc[NB];
+    for (int c0 = 0; c0 < NCTH; c0 += NB) {
+      f32x4 acc[NB];
 #pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] = zero4f();
-    mm_kc<NB>(acc, sT + 16 * w * LM, LM, sX + 16 * c0 * LM, LM, 16 * w, C);
+      for (int n = 0; n < NB; ++n) acc[n] = zero4f();
+      mm_kc<NB>(acc, sT + 16 * w * LM, LM, sX + 16 * (ctb + c0) * LM, LM, 16 * w, C);
 #pragma unroll
-    for (int n = 0; n < NB; ++n)
+      for (int n = 0; n < NB; ++n)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = 16 * w + 4 * kq + j, i = 16 * (c0 + n) + r;
-        sR[t * LD + i] = acc[n][j];
-        if (t < L.count) a.dv[row(t) * D + i] = sBeta[t] * acc[n][j];
-      }
+        for (int j = 0; j < 4; ++j) {
+          const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + c0 + n) + r;
+          sR[t * LD + i] = acc[n][j];
+          if (t < L.count) a.dv[row(t) * D + i] = sBeta[t] * acc[n][j];
+        }
+    }
   }
-  load_mat<D, D, LD>(sS, a.S_in + sh * D * D);
+  load_mat<D, D, LD, NTS>(sS, a.S_in + sh * D * D);
   __syncthreads();  // dR and S in place; dDelta^T no longer needed
-  load_rows<D, LD>(sX, a.d_out, L.tok0, L.count, H, h);  // dO
-  float dq_[NCT][4], dk_[NCT][4], dg_[NCT][4];
+  load_rows<D, LD, float, NTS>(sX, a.d_out, L.tok0, L.count, H, h);  // dO
+  float dq_[NCTH][4], dk_[NCTH][4], dg_[NCTH][4];
   float dbr[4] = {0.f, 0.f, 0.f, 0.f};
   // X = dR S^T: d(K*b) = -beta X, and the R part of dbeta,
   // dR_t . (v_t - (K*b)_t S) = dR_t . v_t - (K*b)_t . X_t
+  if (active) {
 #pragma unroll
-  for (int c0 = 0; c0 < NCT; c0 += NB) {
-    f32x4 acc[NB];
+    for (int c0 = 0; c0 < NCTH; c0 += NB) {
+      f32x4 acc[NB];
 #pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] = zero4f();
-    mm_kc<NB>(acc, sR + 16 * w * LD, LD, sS + 16 * c0 * LD, LD, 0, D);
+      for (int n = 0; n < NB; ++n) acc[n] = zero4f();
+      mm_kc<NB>(acc, sR + 16 * w * LD, LD, sS + 16 * (ctb + c0) * LD, LD, 0, D);
 #pragma unroll
-    for (int n = 0; n < NB; ++n)
+      for (int n = 0; n < NB; ++n)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ct = c0 + n, t = 16 * w + 4 * kq + j, i = 16 * ct + r;
-        const float kb = kv[ct][j] * bb[ct][j];
-        const float vv = t < L.count ? to_f32(v[row(t) * D + i]) : 0.f;
-        dbr[j] += sR[t * LD + i] * vv - kb * acc[n][j];
-        const float dkb = -sBeta[t] * acc[n][j];
-        dk_[ct][j] = dkb * bb[ct][j];
-        dg_[ct][j] = dkb * kb;
-      }
+        for (int j = 0; j < 4; ++j) {
+          const int c = c0 + n, t = 16 * w + 4 * kq + j, i = 16 * (ctb + c) + r;
+          const float kb = kv[c][j] * bb[c][j];
+          const float vv = t < L.count ? to_f32(v[row(t) * D + i]) : 0.f;
+          dbr[j] += sR[t * LD + i] * vv - kb * acc[n][j];
+          const float dkb = -sBeta[t] * acc[n][j];
+          dk_[c][j] = dkb * bb[c][j];
+          dg_[c][j] = dkb * kb;
+        }
+    }
   }
   __syncthreads();  // dO in place
   // Y = dO S^T: d(Q*b) = scale Y
+  if (active) {
 #pragma unroll
-  for (int c0 = 0; c0 < NCT; c0 += NB) {
-    f32x4 acc[NB];
+    for (int c0 = 0; c0 < NCTH; c0 += NB) {
+      f32x4 acc[NB];
 #pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] = zero4f();
-    mm_kc<NB>(acc, sX + 16 * w * LD, LD, sS + 16 * c0 * LD, LD, 0, D);
+      for (int n = 0; n < NB; ++n) acc[n] = zero4f();
+      mm_kc<NB>(acc, sX + 16 * w * LD, LD, sS + 16 * (ctb + c0) * LD, LD, 0, D);
 #pragma unroll
-    for (int n = 0; n < NB; ++n)
+      for (int n = 0; n < NB; ++n)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ct = c0 + n, t = 16 * w + 4 * kq + j, i = 16 * ct + r;
-        const float dqb = a.scale * acc[n][j];
-        const float qv = t < L.count ? to_f32(q[row(t) * D + i]) : 0.f;
-        dq_[ct][j] = dqb * bb[ct][j];
-        dg_[ct][j] += dqb * qv * bb[ct][j];
-      }
+        for (int j = 0; j < 4; ++j) {
+          const int c = c0 + n, t = 16 * w + 4 * kq + j, i = 16 * (ctb + c) + r;
+          const float dqb = a.scale * acc[n][j];
+          const float qv = t < L.count ? to_f32(q[row(t) * D + i]) : 0.f;
+          dq_[c][j] = dqb * bb[c][j];
+          dg_[c][j] += dqb * qv * bb[c][j];
+        }
+    }
   }
   // b_C sum_j dS'[i, j] S[i, j]: D / 4 consecutive threads per row, coalesced
   {
-    constexpr int G = D / 4, N = D * G, IT = (N + NT - 1) / NT;
-    static_assert(G <= 64 && NT % G == 0 && (N >= NT || N % 64 == 0), "row groups must stay inside a wave");
+    constexpr int G = D / 4, N = D * G, IT = (N + NTS - 1) / NTS;
+    static_assert(G <= 64 && NTS % G == 0 && (N >= NTS || N % 64 == 0), "row groups must stay inside a wave");
     float4 x[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it)
-      if (it * NT + tid < N) x[it] = load4(a.dSo + sh * D * D + static_cast<size_t>(it * NT + tid) * 4);
+      if (it * NTS + tid < N) x[it] = load4(a.dSo + sh * D * D + static_cast<size_t>(it * NTS + tid) * 4);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int idx = it * NT + tid, i = idx / G, jj = 4 * (idx - i * G);
+      const int idx = it * NTS + tid, i = idx / G, jj = 4 * (idx - i * G);
       if (idx >= N) continue;  // whole waves
       const float* sr = sS + i * LD + jj;
       float acc = x[it].x * sr[0] + x[it].y * sr[1] + x[it].z * sr[2] + x[it].w * sr[3];
@@ -1026,28 +1037,29 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
     }
   }
   __syncthreads();  // done with S
-  load_mat<C, D, LD>(sS, a.Dl + sh * C * D);  // Delta, rows
+  load_mat<C, D, LD, NTS>(sS, a.Dl + sh * C * D);  // Delta, rows
   __syncthreads();
-  // dAqk = scale tril(dO Delta^T), dA = -tril(dR Delta^T, -1); s blocks 0..3
+  // dAqk = scale tril(dO Delta^T), dA = -tril(dR Delta^T, -1); this wave's
+  // two s blocks [2 half, 2 half + 2)
   {
-    f32x4 aq[4], aa[4];
+    f32x4 aq[2], aa[2];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) aq[n] = aa[n] = zero4f();
-    mm_kc<4>(aq, sX + 16 * w * LD, LD, sS, LD, 0, D);
-    mm_kc<4>(aa, sR + 16 * w * LD, LD, sS, LD, 0, D);
+    for (int n = 0; n < 2; ++n) aq[n] = aa[n] = zero4f();
+    mm_kc<2>(aq, sX + 16 * w * LD, LD, sS + 32 * half * LD, LD, 0, D);
+    mm_kc<2>(aa, sR + 16 * w * LD, LD, sS + 32 * half * LD, LD, 0, D);
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int t = 16 * w + 4 * kq + j, s = 16 * sb + r;
-        const float gq = s <= t ? a.scale * aq[sb][j] : 0.f;
-        const float ga = s < t ? -aa[sb][j] : 0.f;
+        const int t = 16 * w + 4 * kq + j, s = 16 * (2 * half + n) + r;
+        const float gq = s <= t ? a.scale * aq[n][j] : 0.f;
+        const float ga = s < t ? -aa[n][j] : 0.f;
         dbr[j] += ga * a.Ab[sh * C * C + t * C + s];
         a.dAq[sh * C * C + t * C + s] = gq;
         a.dAb[sh * C * C + t * C + s] = sBeta[t] * ga;
       }
   }
-  // rows of dbeta: reduce over the 16 lanes sharing kq
+  // rows of dbeta: reduce over the 16 lanes sharing kq; one half per wave pair
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float x = dbr[j];
@@ -1055,54 +1067,58 @@ __global__ void __launch_bounds__(NT) bwd_gstate(BwdArgs a) {
     x += __shfl_xor(x, 2, 64);
     x += __shfl_xor(x, 4, 64);
     x += __shfl_xor(x, 8, 64);
-    if (r == 0) sDb[16 * w + 4 * kq + j] = x;
+    if (r == 0) sDb[half * C + 16 * w + 4 * kq + j] = x;
   }
   __syncthreads();  // done with Delta rows (sS) and dR (sR)
-  load_mat<C, D, LD>(sR, a.Dl + sh * C * D);   // Delta
-  load_mat<D, D, LD>(sS, a.dSo + sh * D * D);  // dS'
+  load_mat<C, D, LD, NTS>(sR, a.Dl + sh * C * D);   // Delta
+  load_mat<D, D, LD, NTS>(sS, a.dSo + sh * D * D);  // dS'
   __syncthreads();
   // Z = Delta dS'^T: dKd = Z
-  float colp[NCT];
+  float colp[NCTH];
+  if (active) {
 #pragma unroll
-  for (int c0 = 0; c0 < NCT; c0 += NB) {
-    f32x4 acc[NB];
+    for (int c0 = 0; c0 < NCTH; c0 += NB) {
+      f32x4 acc[NB];
 #pragma unroll
-    for (int n = 0; n < NB; ++n) acc[n] = zero4f();
-    mm_kc<NB>(acc, sR + 16 * w * LD, LD, sS + 16 * c0 * LD, LD, 0, D);
+      for (int n = 0; n < NB; ++n) acc[n] = zero4f();
+      mm_kc<NB>(acc, sR + 16 * w * LD, LD, sS + 16 * (ctb + c0) * LD, LD, 0, D);
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const int ct = c0 + n;
-      float cs = 0.f;
+      for (int n = 0; n < NB; ++n) {
+        const int c = c0 + n;
+        float cs = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float kd = kv[ct][j] * rc[ct][j];
-        dk_[ct][j] += acc[n][j] * rc[ct][j];
-        dg_[ct][j] -= acc[n][j] * kd;
-        cs += acc[n][j] * kd;
+        for (int j = 0; j < 4; ++j) {
+          const float kd = kv[c][j] * rc[c][j];
+          dk_[c][j] += acc[n][j] * rc[c][j];
+          dg_[c][j] -= acc[n][j] * kd;
+          cs += acc[n][j] * kd;
+        }
+        cs += __shfl_xor(cs, 16, 64);
+        cs += __shfl_xor(cs, 32, 64);
+        colp[c] = cs;
       }
-      cs += __shfl_xor(cs, 16, 64);
-      cs += __shfl_xor(cs, 32, 64);
-      colp[ct] = cs;
     }
-  }
-  if (kq == 0)
+    if (kq == 0)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) sCol[w * D + 16 * ct + r] = colp[ct];
+      for (int c = 0; c < NCTH; ++c) sCol[w * D + 16 * (ctb + c) + r] = colp[c];
+  }
   __syncthreads();
   // dgamma joins dG at the chunk's last token; write the staged parts
+  if (active) {
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
+    for (int c = 0; c < NCTH; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int t = 16 * w + 4 * kq + j, i = 16 * ct + r;
-      if (t >= L.count) continue;
-      float g = dg_[ct][j];
-      if (t == L.count - 1) g += sGam[i] + sCol[i] + sCol[D + i] + sCol[2 * D + i] + sCol[3 * D + i];
-      a.dq[row(t) * D + i] = dq_[ct][j];
-      a.dk[row(t) * D + i] = dk_[ct][j];
-      a.dlog_g[row(t) * D + i] = g;
-    }
-  if (tid < L.count) a.dbeta[row(tid)] = sDb[tid];
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + c) + r;
+        if (t >= L.count) continue;
+        float g = dg_[c][j];
+        if (t == L.count - 1) g += sGam[i] + sCol[i] + sCol[D + i] + sCol[2 * D + i] + sCol[3 * D + i];
+        a.dq[row(t) * D + i] = dq_[c][j];
+        a.dk[row(t) * D + i] = dk_[c][j];
+        a.dlog_g[row(t) * D + i] = g;
+      }
+  }
+  if (tid < L.count) a.dbeta[row(tid)] = sDb[tid] + sDb[C + tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -1458,7 +1474,7 @@ hipError_t run_bwd(const BwdArgs& a, int64_t ns, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (chunk_blocks > 0) {
-    hipLaunchKernelGGL((bwd_gstate<D, In>), dim3(chunk_blocks), dim3(NT), GsL<D>::BYTES, stream, a);
+    hipLaunchKernelGGL((bwd_gstate<D, In>), dim3(chunk_blocks), dim3(NTS), GsL<D>::BYTES, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_gpairs<D, In>), dim3(chunk_blocks), dim3(NTG), GpL<D>::BYTES, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
