@@ -119,3 +119,27 @@ def test_full_size_dense_workload_sampled_units():
         mine = {nm: (got[nm][n:n + 1, h:h + 1] if nm == "d_init_state" else
                      got[nm][n:n + 1, :, h:h + 1]) for nm in NAMES}
         check(f"full-size unit ({n},{h})", mine, ref, TOL["bf16"])
+
+
+def test_full_size_packed_workload_sampled_units():
+    """The packed 65536-token, 32-head workload (26 documents, log-uniform
+    lengths 64..16384, zero initial states) at full size; the oracle checks
+    every gradient of sampled (document, head) units: the two shortest
+    documents, a mid-length one, and the first document at another head."""
+    inp = kda_inputs.config("varlen")
+    up = kda_inputs.upstream_grads(inp, seed=250)
+    got = gpu_bwd(inp, up)
+    cu = inp["cu_seqlens"].numpy().astype(np.int64)
+    lens = np.diff(cu)
+    order = np.argsort(lens)
+    docs = [int(order[0]), int(order[1]), int(order[len(order) // 2])]
+    for n, h in [(docs[0], 0), (docs[1], 17), (docs[2], 31), (0, 5)]:
+        a, e = int(cu[n]), int(cu[n + 1])
+        sl = lambda t: t[:, a:e, h:h + 1]
+        unit = dict(q=sl(inp["q"]), k=sl(inp["k"]), v=sl(inp["v"]), log_g=sl(inp["log_g"]),
+                    beta=inp["beta"][:, a:e, h:h + 1], init_state=None, cu_seqlens=None, scale=inp["scale"])
+        uup = dict(d_out=sl(up["d_out"]), d_final=up["d_final"][n:n + 1, h:h + 1])
+        ref = oracle_bwd(unit, uup, init=False)
+        mine = {nm: (got[nm][n:n + 1, h:h + 1] if nm == "d_init_state" else got[nm][:, a:e, h:h + 1])
+                for nm in NAMES}
+        check(f"packed full-size doc {n} (len {e - a}) head {h}", mine, ref, TOL["bf16"])
