@@ -21,6 +21,7 @@
 
 #include "kda_common.h"
 #include "kda_launch.h"
+#include "kda_vec8.h"
 
 namespace kda {
 namespace {
@@ -42,34 +43,6 @@ struct ConvArgs {
   int Cn;
   int act;                   // 0 identity, 1 SiLU
 };
-
-// 8 consecutive channels as floats; bf16 is one 16-byte access
-__device__ __forceinline__ void load8(const float* p, float (&o)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-  o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w; o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
-}
-__device__ __forceinline__ void load8(const bf16_t* p, float (&o)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x); o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
-  o[4] = bf16_lo(u.z); o[5] = bf16_hi(u.z); o[6] = bf16_lo(u.w); o[7] = bf16_hi(u.w);
-}
-__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
-  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-}
-// fp32 -> bf16, round to nearest even (inputs here are finite)
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ void store8(bf16_t* p, const float (&v)[8]) {
-  uint4 u;
-  u.x = bf16_bits(v[0]) | (bf16_bits(v[1]) << 16);
-  u.y = bf16_bits(v[2]) | (bf16_bits(v[3]) << 16);
-  u.z = bf16_bits(v[4]) | (bf16_bits(v[5]) << 16);
-  u.w = bf16_bits(v[6]) | (bf16_bits(v[7]) << 16);
-  *reinterpret_cast<uint4*>(p) = u;
-}
 
 // document containing token t: [ds, de)
 __device__ __forceinline__ void doc_of(const ConvArgs& a, int64_t t, int& n, int64_t& ds, int64_t& de) {
@@ -123,7 +96,7 @@ __global__ void __launch_bounds__(NTC) conv_kernel(ConvArgs a) {
     for (int m = 0; m < M; ++m) {
       const int64_t tau = t - M + m;
       if (tau >= ds) {
-        load8(x + tau * Cn + c, win[m]);
+        load8f(x + tau * Cn + c, win[m]);
       } else if (a.init_cache) {
         const int p = static_cast<int>(tau - ds) + M;
         const float* cc = a.init_cache + (static_cast<size_t>(n) * Cn + c) * M + p;
@@ -146,7 +119,7 @@ __global__ void __launch_bounds__(NTC) conv_kernel(ConvArgs a) {
       float xv[UNR][CH];
 #pragma unroll
       for (int u = 0; u < UNR; ++u)
-        if (tb + u < te) load8(x + (tb + u) * Cn + c, xv[u]);
+        if (tb + u < te) load8f(x + (tb + u) * Cn + c, xv[u]);
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         if (tb + u >= te) break;
@@ -159,7 +132,7 @@ __global__ void __launch_bounds__(NTC) conv_kernel(ConvArgs a) {
           if (a.act == 1) acc = acc / (1.f + exp_fast(-acc));
           o[ch] = acc;
         }
-        store8(y + (tb + u) * Cn + c, o);
+        store8f(y + (tb + u) * Cn + c, o);
 #pragma unroll
         for (int m = 0; m + 1 < M; ++m)
 #pragma unroll

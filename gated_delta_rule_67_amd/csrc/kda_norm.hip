@@ -12,6 +12,7 @@
 // inside the group.
 #include "kda_common.h"
 #include "kda_launch.h"
+#include "kda_vec8.h"
 
 namespace kda {
 namespace {
@@ -27,33 +28,6 @@ struct NormArgs {
   float eps;
 };
 
-__device__ __forceinline__ void ld8(const float* p, float (&v)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p), b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-__device__ __forceinline__ void ld8(const bf16_t* p, float (&v)[8]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
-  v[0] = bf16_lo(u.x); v[1] = bf16_hi(u.x); v[2] = bf16_lo(u.y); v[3] = bf16_hi(u.y);
-  v[4] = bf16_lo(u.z); v[5] = bf16_hi(u.z); v[6] = bf16_lo(u.w); v[7] = bf16_hi(u.w);
-}
-__device__ __forceinline__ void st8(float* p, const float (&v)[8]) {
-  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
-}
-// fp32 -> bf16, round to nearest even (finite inputs)
-__device__ __forceinline__ uint32_t to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-__device__ __forceinline__ void st8(bf16_t* p, const float (&v)[8]) {
-  uint4 u;
-  u.x = to_bf16_bits(v[0]) | (to_bf16_bits(v[1]) << 16);
-  u.y = to_bf16_bits(v[2]) | (to_bf16_bits(v[3]) << 16);
-  u.z = to_bf16_bits(v[4]) | (to_bf16_bits(v[5]) << 16);
-  u.w = to_bf16_bits(v[6]) | (to_bf16_bits(v[7]) << 16);
-  *reinterpret_cast<uint4*>(p) = u;
-}
-
 template <int D, typename G, typename O>
 __global__ void __launch_bounds__(NTN) gated_rmsnorm_kernel(NormArgs a) {
   constexpr int L = D / 8;  // lanes per row (divides 64)
@@ -63,9 +37,9 @@ __global__ void __launch_bounds__(NTN) gated_rmsnorm_kernel(NormArgs a) {
   if (row >= a.rows) return;  // the lanes of one row leave together
   const int64_t off = row * D + 8 * part;
   float o[8], g[8], w[8];
-  ld8(a.o + off, o);
-  ld8(static_cast<const G*>(a.g) + off, g);
-  ld8(a.w + 8 * part, w);
+  load8f(a.o + off, o);
+  load8f(static_cast<const G*>(a.g) + off, g);
+  load8f(a.w + 8 * part, w);
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ss += o[i] * o[i];
@@ -75,7 +49,7 @@ __global__ void __launch_bounds__(NTN) gated_rmsnorm_kernel(NormArgs a) {
   float y[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) y[i] = o[i] * inv * w[i] / (1.f + exp_fast(-g[i]));
-  st8(static_cast<O*>(a.out) + off, y);
+  store8f(static_cast<O*>(a.out) + off, y);
 }
 
 template <int D>
