@@ -143,3 +143,14 @@ def test_full_size_packed_workload_sampled_units():
         mine = {nm: (got[nm][n:n + 1, h:h + 1] if nm == "d_init_state" else got[nm][:, a:e, h:h + 1])
                 for nm in NAMES}
         check(f"packed full-size doc {n} (len {e - a}) head {h}", mine, ref, TOL["bf16"])
+
+
+def test_many_short_documents():
+    """5000 documents of 0 to 3 tokens (more than one pass of the chunk-map
+    kernel's 1024 threads), 2 heads, d = 16: every gradient of every document."""
+    rng = np.random.default_rng(140)
+    lens = [int(x) for x in rng.integers(0, 4, 5000)]
+    inp = kda_inputs.make_inputs(B=1, T=sum(lens), H=2, dk=16, dv=16, dtype="f32", seed=141, lengths=lens,
+                                 init="normal", init_std=0.1)
+    up = kda_inputs.upstream_grads(inp, seed=142)
+    check("5000 short documents", gpu_bwd(inp, up), oracle_bwd(inp, up), TOL["f32"])

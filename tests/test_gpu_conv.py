@@ -100,3 +100,12 @@ def test_full_size_workload():
     side), K = 4, bf16, zero caches: every element against the oracle."""
     inp = kda_inputs.conv_inputs(B=4, T=4096, channels=6144, K=4, dtype="bf16", seed=330, cache=False)
     check("full size", gpu(inp, 0), ref(inp, 0), "bf16", 4)
+
+
+def test_many_short_documents():
+    """5000 documents of 0 to 3 tokens with caches, width 4: every document
+    starts from its own cache (empty ones pass it through)."""
+    rng = np.random.default_rng(340)
+    lens = [int(x) for x in rng.integers(0, 4, 5000)]
+    inp = kda_inputs.conv_inputs(B=1, T=sum(lens), channels=64, K=4, dtype="f32", seed=341, lengths=lens)
+    check("5000 short documents", gpu(inp, 0), ref(inp, 0), "f32", 4)
