@@ -94,7 +94,8 @@ struct BwdArgs {
   int N;
   int T;
   int H;
-  int cps;  // dense: chunks per sequence
+  int cps;      // dense: chunks per sequence
+  int n_slots;  // chunk slots per head
   float scale;
 };
 
@@ -1122,68 +1123,148 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// bwd_gpairs: per (chunk, head): pair terms of Aqk and Akk, then dlog_g.
-// Q, K and the level factors are kept transposed ([channel][token]) so that
-// the pair products read them along the contracted token index.
-template <int D>
+// bwd_gpairs: per (chunk, head, group of up to 64 channels): pair terms of Aqk
+// and Akk, then dlog_g.  Every term is per channel, so a chunk's channels split
+// over NSPL workgroups; that keeps a workgroup's LDS under half of a CU's and
+// lets two of them share a CU, one streaming while the other computes.  Q, K
+// and the level factors are kept transposed ([channel][token]) so that the
+// pair products read them along the contracted token index; bf16 inputs stay
+// bf16 in LDS.
+template <int D, typename In>
 struct GpL {
+  static constexpr int CW = D < 64 ? D : 64;  // channels per workgroup
+  static constexpr int NSPL = D / CW;         // workgroups per (chunk, head)
   static constexpr int LM = C + 4;
-  static constexpr int RQ = 0;                // Q^T
-  static constexpr int RK = RQ + D * LM;      // K^T
-  static constexpr int RF = RK + D * LM;      // F^T, later dG^T
-  static constexpr int RA = RF + D * LM;      // dAqk
-  static constexpr int RB = RA + C * LM;      // dAkk
-  static constexpr int FLOATS = RB + C * LM;
-  static constexpr size_t BYTES = sizeof(float) * FLOATS;
+  static constexpr size_t QKB = sizeof(In) * CW * LM;
+  static constexpr size_t OQ = 0;                                 // Q^T  [CW][LM] In
+  static constexpr size_t OK = OQ + QKB;                          // K^T  [CW][LM] In
+  static constexpr size_t OF = OK + QKB;                          // F^T, later dG^T [CW][LM]
+  static constexpr size_t OA = OF + sizeof(float) * CW * LM;      // dAqk [C][LM]
+  static constexpr size_t OB = OA + sizeof(float) * C * LM;       // dAkk [C][LM]
+  static constexpr size_t OS = OB + sizeof(float) * C * LM;       // per-segment totals [8][CW]
+  static constexpr size_t BYTES = OS + sizeof(float) * 8 * CW;
 };
-
-// level_factors, written transposed: sFT[i * LM + t].
-template <int L, int LM>
-__device__ __forceinline__ void level_factors_t(const float (&al)[32], int base, int i, float* sFT) {
-  constexpr int HH = 32 >> L;
-  float f[32];
-#pragma unroll
-  for (int b0 = 0; b0 < 32; b0 += HH) {
-    const bool upper = ((base + b0) & HH) != 0;
-    if (upper) {
-      float p = 1.f;
-#pragma unroll
-      for (int u = 0; u < HH; ++u) {
-        p *= al[b0 + u];
-        f[b0 + u] = p;
-      }
-    } else {
-      float p = 1.f;
-#pragma unroll
-      for (int u = HH - 1; u >= 0; --u) {
-        f[b0 + u] = p;
-        p *= al[b0 + u];
-      }
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < 32; u += 4)
-    *reinterpret_cast<float4*>(sFT + i * LM + base + u) = make_float4(f[u], f[u + 1], f[u + 2], f[u + 3]);
-}
 
 constexpr int NTG = 512;  // bwd_gpairs: 8 waves, two per token block
 
+// Channels [c0, c0 + CW) of C rows of a [tokens, H, D] tensor, transposed into
+// LDS as the input type: dst[c * LDT + t], rows >= count zero.
+template <int D, int CW, int LDT, typename In>
+__device__ __forceinline__ void load_cols_t(In* dst, const In* src, int64_t tok0, int count, int H, int h, int c0) {
+  constexpr int G = CW / 4, N = C * G, IT = (N + NTG - 1) / NTG;
+  uint2 xb[IT];   // bf16: 4 raw values
+  float4 xf[IT];  // fp32
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTG + threadIdx.x, t = idx / G, g4 = idx - t * G;
+    const In* p = src + ((tok0 + t) * H + h) * D + c0 + 4 * g4;
+    if constexpr (sizeof(In) == 2) {
+      xb[it] = make_uint2(0u, 0u);
+      if (idx < N && t < count) xb[it] = *reinterpret_cast<const uint2*>(p);
+    } else {
+      xf[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (idx < N && t < count) xf[it] = *reinterpret_cast<const float4*>(p);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTG + threadIdx.x, t = idx / G, c = 4 * (idx - t * G);
+    if (idx >= N) continue;
+    if constexpr (sizeof(In) == 2) {
+      uint16_t* d = reinterpret_cast<uint16_t*>(dst);
+      d[(c + 0) * LDT + t] = static_cast<uint16_t>(xb[it].x);
+      d[(c + 1) * LDT + t] = static_cast<uint16_t>(xb[it].x >> 16);
+      d[(c + 2) * LDT + t] = static_cast<uint16_t>(xb[it].y);
+      d[(c + 3) * LDT + t] = static_cast<uint16_t>(xb[it].y >> 16);
+    } else {
+      dst[(c + 0) * LDT + t] = xf[it].x;
+      dst[(c + 1) * LDT + t] = xf[it].y;
+      dst[(c + 2) * LDT + t] = xf[it].z;
+      dst[(c + 3) * LDT + t] = xf[it].w;
+    }
+  }
+}
+
+__device__ __forceinline__ float ld1f(const float* p) { return *p; }
+__device__ __forceinline__ float ld1f(const bf16_t* p) { return to_f32(*p); }
+
+// Level-l factors of one channel for the 8 tokens [8 seg, 8 seg + 8): al are
+// their gates, segtot[s] the product of the gates of segment s (LDS, this
+// channel, stride CW).  A half of 8 or more tokens spans whole segments: its
+// factors are a product inside the segment times the totals of the segments
+// before it (upper half) or after it (lower half) within the half.
+template <int L, int CW>
+__device__ __forceinline__ void level_factors8(const float (&al)[8], int seg, const float* segtot, float (&f)[8]) {
+  constexpr int HH = 32 >> L;
+  if constexpr (HH >= 8) {
+    constexpr int NS = HH / 8;            // segments per half
+    const int s0 = seg & ~(NS - 1);       // first segment of the half
+    const bool upper = ((8 * seg) & HH) != 0;
+    if (upper) {
+      float p = 1.f;
+      for (int s = s0; s < seg; ++s) p *= segtot[s * CW];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        p *= al[u];
+        f[u] = p;
+      }
+    } else {
+      float p = 1.f;
+      for (int s = seg + 1; s < s0 + NS; ++s) p *= segtot[s * CW];
+#pragma unroll
+      for (int u = 7; u >= 0; --u) {
+        f[u] = p;
+        p *= al[u];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int b0 = 0; b0 < 8; b0 += HH) {
+      const bool upper = ((b0 & HH) != 0);  // 8 seg is a multiple of 2 HH
+      if (upper) {
+        float p = 1.f;
+#pragma unroll
+        for (int u = 0; u < HH; ++u) {
+          p *= al[b0 + u];
+          f[b0 + u] = p;
+        }
+      } else {
+        float p = 1.f;
+#pragma unroll
+        for (int u = HH - 1; u >= 0; --u) {
+          f[b0 + u] = p;
+          p *= al[b0 + u];
+        }
+      }
+    }
+  }
+}
+
 template <int D, typename In>
-__global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
-  using P = GpL<D>;
-  constexpr int LM = P::LM, NCT = D / 16;
+__global__ void __launch_bounds__(NTG, 2) bwd_gpairs(BwdArgs a) {
+  using P = GpL<D, In>;
+  constexpr int CW = P::CW, NSPL = P::NSPL, LM = P::LM, NCT = CW / 16;
   // wave wv: token block w = wv & 3, channel tiles [ctb, ctb + NCTW)
   constexpr int NCTW = NCT >= 2 ? NCT / 2 : 1;
-  extern __shared__ __align__(16) float sm[];
-  float* sQT = sm + P::RQ;
-  float* sKT = sm + P::RK;
-  float* sFT = sm + P::RF;
-  float* sdAq = sm + P::RA;
-  float* sdAb = sm + P::RB;
+  extern __shared__ __align__(16) unsigned char gsm[];
+  In* sQT = reinterpret_cast<In*>(gsm + P::OQ);
+  In* sKT = reinterpret_cast<In*>(gsm + P::OK);
+  float* sFT = reinterpret_cast<float*>(gsm + P::OF);
+  float* sdAq = reinterpret_cast<float*>(gsm + P::OA);
+  float* sdAb = reinterpret_cast<float*>(gsm + P::OB);
+  float* sSeg = reinterpret_cast<float*>(gsm + P::OS);
 
-  const int slot = blockIdx.x / a.H, h = blockIdx.x - slot * a.H;
+  // the NSPL channel groups of a (chunk, head) are 8 blocks apart (one XCD,
+  // one L2 for the shared dA tiles)
+  const int b = blockIdx.x;
+  const int grp = b / (8 * NSPL), rem = b - grp * 8 * NSPL;
+  const int part = rem / 8;
+  const int sh_idx = grp * 8 + (rem & 7);
+  const int slot = sh_idx / a.H, h = sh_idx - slot * a.H;
+  if (slot >= a.n_slots) return;
   Loc L;
   if (!locate(a, slot, L)) return;
+  const int c0 = part * CW;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, w = wv & 3, r = lane & 15, kq = lane >> 4;
   const int ctb = (wv >> 2) * NCTW;
   const bool active = ctb < NCT;
@@ -1191,14 +1272,25 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
   const int H = a.H;
   auto row = [&](int t) { return (L.tok0 + t) * H + h; };
 
-  load_rows_t<D, LM, In, NTG>(sQT, static_cast<const In*>(a.q), L.tok0, L.count, H, h);
-  load_rows_t<D, LM, In, NTG>(sKT, static_cast<const In*>(a.k), L.tok0, L.count, H, h);
+  load_cols_t<D, CW, LM, In>(sQT, static_cast<const In*>(a.q), L.tok0, L.count, H, h, c0);
+  load_cols_t<D, CW, LM, In>(sKT, static_cast<const In*>(a.k), L.tok0, L.count, H, h, c0);
   load_mat<C, C, LM, NTG>(sdAq, a.dAq + sh * C * C);
   load_mat<C, C, LM, NTG>(sdAb, a.dAb + sh * C * C);
-  const int ci = tid % D, ph = tid / D;
-  const bool chan = ph < 2;
-  float al[32];
-  if (chan) load_alpha<D>(al, a.log_g, L.tok0, L.count, H, h, ci, 32 * ph);
+  // factor threads: channel fi, tokens [8 seg, 8 seg + 8)
+  const int fi = tid % CW, seg = tid / CW;
+  const bool fthr = seg < 8;
+  float al[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int t = 8 * seg + u;
+    al[u] = (fthr && t < L.count) ? exp_fast(a.log_g[row(t) * D + c0 + fi]) : 1.f;
+  }
+  if (fthr) {
+    float p = 1.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) p *= al[u];
+    sSeg[seg * CW + fi] = p;
+  }
 
   float dq_[NCTW][4], dk_[NCTW][4], dg_[NCTW][4];
 #pragma unroll
@@ -1212,8 +1304,8 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
 #pragma unroll
     for (int ct = 0; ct < NCTW; ++ct) {
       const int i0 = 16 * (ctb + ct);
-      const float* bk = sKT + (i0 + r) * LM + 4 * kq;
-      const float* bq = sQT + (i0 + r) * LM + 4 * kq;
+      const In* bk = sKT + (i0 + r) * LM + 4 * kq;
+      const In* bq = sQT + (i0 + r) * LM + 4 * kq;
       const float* bf = sFT + (i0 + r) * LM + 4 * kq;
       if (upper_rows) {
         const int t = 16 * w + r;
@@ -1222,7 +1314,7 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
           const int s0 = k0 + 4 * kq;
           const float4 aq = *reinterpret_cast<const float4*>(sdAq + t * LM + s0);
           const float4 ab = *reinterpret_cast<const float4*>(sdAb + t * LM + s0);
-          const float4 kk = *reinterpret_cast<const float4*>(bk + k0);
+          const float4 kk = load4(bk + k0);
           const float4 ff = *reinterpret_cast<const float4*>(bf + k0);
           const bool m0 = at_level(l, t, s0), m1 = at_level(l, t, s0 + 1), m2 = at_level(l, t, s0 + 2),
                      m3 = at_level(l, t, s0 + 3);
@@ -1242,15 +1334,15 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
           const float gq = ft * xq[j], gk = ft * xk[j];
           dq_[ct][j] += gq;
           dk_[ct][j] += gk;
-          dg_[ct][j] += sQT[i * LM + to] * gq + sKT[i * LM + to] * gk;
+          dg_[ct][j] += ld1f(sQT + i * LM + to) * gq + ld1f(sKT + i * LM + to) * gk;
         }
       } else {
         const int s = 16 * w + r;
         f32x4 y1 = zero4f(), y2 = zero4f();
         for (int k0 = p0; k0 < p0 + plen; k0 += 16) {
           const int t0 = k0 + 4 * kq;
-          const float4 qq = *reinterpret_cast<const float4*>(bq + k0);
-          const float4 kk = *reinterpret_cast<const float4*>(bk + k0);
+          const float4 qq = load4(bq + k0);
+          const float4 kk = load4(bk + k0);
           const float4 ff = *reinterpret_cast<const float4*>(bf + k0);
           float aq[4], ab[4];
 #pragma unroll
@@ -1273,23 +1365,27 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
           const int so = 16 * w + 4 * kq + j, i = i0 + r;
           const float gy = sFT[i * LM + so] * (y1[j] + y2[j]);
           dk_[ct][j] += gy;
-          dg_[ct][j] -= sKT[i * LM + so] * gy;
+          dg_[ct][j] -= ld1f(sKT + i * LM + so) * gy;
         }
       }
     }
   };
 #pragma unroll
   for (int l = 0; l < 6; ++l) {
-    __syncthreads();
-    if (chan) {
+    __syncthreads();  // segment totals written; previous level's factors read
+    if (fthr) {
+      float f[8];
       switch (l) {
-        case 0: level_factors_t<0, LM>(al, 32 * ph, ci, sFT); break;
-        case 1: level_factors_t<1, LM>(al, 32 * ph, ci, sFT); break;
-        case 2: level_factors_t<2, LM>(al, 32 * ph, ci, sFT); break;
-        case 3: level_factors_t<3, LM>(al, 32 * ph, ci, sFT); break;
-        case 4: level_factors_t<4, LM>(al, 32 * ph, ci, sFT); break;
-        default: level_factors_t<5, LM>(al, 32 * ph, ci, sFT); break;
+        case 0: level_factors8<0, CW>(al, seg, sSeg + fi, f); break;
+        case 1: level_factors8<1, CW>(al, seg, sSeg + fi, f); break;
+        case 2: level_factors8<2, CW>(al, seg, sSeg + fi, f); break;
+        case 3: level_factors8<3, CW>(al, seg, sSeg + fi, f); break;
+        case 4: level_factors8<4, CW>(al, seg, sSeg + fi, f); break;
+        default: level_factors8<5, CW>(al, seg, sSeg + fi, f); break;
       }
+      float* dst = sFT + fi * LM + 8 * seg;
+      *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<float4*>(dst + 4) = make_float4(f[4], f[5], f[6], f[7]);
     }
     __syncthreads();
     if (!active) continue;
@@ -1311,8 +1407,8 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
     for (int j = 0; j < 4; ++j) {
       const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + ct) + r;
       const float d = sdAq[t * LM + t];
-      dq_[ct][j] += d * sKT[i * LM + t];
-      dk_[ct][j] += d * sQT[i * LM + t];
+      dq_[ct][j] += d * ld1f(sKT + i * LM + t);
+      dk_[ct][j] += d * ld1f(sQT + i * LM + t);
     }
   __syncthreads();  // done with F^T
   // add the state-side parts staged by bwd_gstate; dG^T into sFT for the cumsum
@@ -1324,7 +1420,7 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
         const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + ct) + r;
         float g = 0.f;
         if (t < L.count) {
-          const int64_t o = row(t) * D + i;
+          const int64_t o = row(t) * D + c0 + i;
           a.dq[o] += dq_[ct][j];
           a.dk[o] += dk_[ct][j];
           g = a.dlog_g[o] + dg_[ct][j];
@@ -1333,11 +1429,25 @@ __global__ void __launch_bounds__(NTG) bwd_gpairs(BwdArgs a) {
       }
   }
   __syncthreads();
-  for (int i = tid; i < D; i += NTG) {
-    float acc = 0.f;
-    for (int t = C - 1; t >= 0; --t) {
-      acc += sFT[i * LM + t];
-      if (t < L.count) a.dlog_g[row(t) * D + i] = acc;
+  // dlog_g = reverse cumulative sum of dG over the chunk: each factor thread
+  // sums its 8 tokens, then adds the totals of the segments after its own
+  float g[8];
+  if (fthr) {
+    const float* src = sFT + fi * LM + 8 * seg;
+    const float4 x0 = *reinterpret_cast<const float4*>(src), x1 = *reinterpret_cast<const float4*>(src + 4);
+    g[0] = x0.x; g[1] = x0.y; g[2] = x0.z; g[3] = x0.w; g[4] = x1.x; g[5] = x1.y; g[6] = x1.z; g[7] = x1.w;
+#pragma unroll
+    for (int u = 6; u >= 0; --u) g[u] += g[u + 1];
+    sSeg[seg * CW + fi] = g[0];
+  }
+  __syncthreads();
+  if (fthr) {
+    float off = 0.f;
+    for (int s = seg + 1; s < 8; ++s) off += sSeg[s * CW + fi];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = 8 * seg + u;
+      if (t < L.count) a.dlog_g[row(t) * D + c0 + fi] = g[u] + off;
     }
   }
 }
@@ -1427,7 +1537,7 @@ hipError_t set_lds_d() {
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(GsL<D>::BYTES));
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_gpairs<D, In>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(GpL<D>::BYTES));
+                          hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(GpL<D, In>::BYTES));
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_fscan<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(sizeof(float) * ScanL<D>::F_FLOATS));
@@ -1476,7 +1586,9 @@ hipError_t run_bwd(const BwdArgs& a, int64_t ns, hipStream_t stream) {
   if (chunk_blocks > 0) {
     hipLaunchKernelGGL((bwd_gstate<D, In>), dim3(chunk_blocks), dim3(NTS), GsL<D>::BYTES, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_gpairs<D, In>), dim3(chunk_blocks), dim3(NTG), GpL<D>::BYTES, stream, a);
+    using P = GpL<D, In>;
+    const unsigned pair_blocks = (chunk_blocks + 7) / 8 * 8 * P::NSPL;
+    hipLaunchKernelGGL((bwd_gpairs<D, In>), dim3(pair_blocks), dim3(NTG), P::BYTES, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1491,7 +1603,8 @@ size_t bwd_workspace_bytes(int num_seqs, int seq_len, int num_heads, int d, bool
 bool bwd_supported(const BwdLaunch& a) {
   const bool packed = a.cu_seqlens != nullptr;
   const int64_t blocks = bwd_slots(a.num_seqs, a.seq_len, packed) * a.num_heads;
-  return (a.d == 16 || a.d == 32 || a.d == 64 || a.d == 128) && blocks < (int64_t(1) << 31) &&
+  // bwd_gpairs runs up to two workgroups per (slot, head), rounded up to 16
+  return (a.d == 16 || a.d == 32 || a.d == 64 || a.d == 128) && (blocks + 16) * 2 < (int64_t(1) << 31) &&
          int64_t(a.num_seqs) * a.num_heads * 4 < (int64_t(1) << 31);
 }
 
@@ -1513,6 +1626,7 @@ hipError_t launch_chunk_bwd(const BwdLaunch& s, hipStream_t stream) {
   a.dAb = l.f[12]; a.eg = l.f[13]; a.WT = l.f[14]; a.KdT = l.f[15];
   a.N = s.num_seqs; a.T = s.seq_len; a.H = s.num_heads;
   a.cps = packed ? 0 : static_cast<int>((static_cast<int64_t>(s.seq_len) + C - 1) / C);
+  a.n_slots = static_cast<int>(ns);
   a.scale = s.scale;
   if (packed) {
     hipLaunchKernelGGL(bwd_chunk_map, dim3(1), dim3(1024), 0, stream, s.cu_seqlens, s.num_seqs,
