@@ -138,7 +138,10 @@ __device__ __forceinline__ void unit_chunks(const BwdArgs& a, int n, int& first,
 
 // C rows of a [tokens, H, D] tensor into LDS (row stride LD), rows >= count zero.
 // (The staging helpers run a compile-time number of iterations so that all of
-// a thread's loads are in flight before its LDS stores.)
+// a thread's loads are in flight before its LDS stores.  Their loads are
+// unconditional, from an index clamped into range, and out-of-range values
+// are replaced afterwards: a load under a branch waits for its data before
+// the next one issues.  count >= 1.)
 template <int D, int LD, typename In, int NTH = NT>
 __device__ __forceinline__ void load_rows(float* dst, const In* src, int64_t tok0, int count, int H, int h) {
   constexpr int G = D / 4, N = C * G, IT = (N + NTH - 1) / NTH;
@@ -146,8 +149,8 @@ __device__ __forceinline__ void load_rows(float* dst, const In* src, int64_t tok
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
-    x[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (idx < N && t < count) x[it] = load4(src + ((tok0 + t) * H + h) * D + 4 * g4);
+    const float4 y = load4(src + ((tok0 + min(t, count - 1)) * H + h) * D + 4 * g4);
+    x[it] = t < count ? y : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -165,8 +168,8 @@ __device__ __forceinline__ void load_rows_t(float* dst, const In* src, int64_t t
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
-    x[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (idx < N && t < count) x[it] = load4(src + ((tok0 + t) * H + h) * D + 4 * g4);
+    const float4 y = load4(src + ((tok0 + min(t, count - 1)) * H + h) * D + 4 * g4);
+    x[it] = t < count ? y : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -188,7 +191,7 @@ __device__ __forceinline__ void load_mat(float* dst, const float* src) {
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int idx = it * NTH + threadIdx.x;
-    if (idx < N) x[it] = load4(src + idx * 4);
+    x[it] = load4(src + min(idx, N - 1) * 4);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -205,7 +208,7 @@ __device__ __forceinline__ void load_cols(float* dst, const float* src, int ldg,
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int idx = it * NT + threadIdx.x, t = idx / G, g4 = idx - t * G;
-    if (idx < N) x[it] = load4(src + static_cast<int64_t>(t) * ldg + c0 + 4 * g4);
+    x[it] = load4(src + static_cast<int64_t>(min(t, ROWS - 1)) * ldg + c0 + 4 * g4);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -229,11 +232,12 @@ __device__ __forceinline__ void store_cols(float* dst, int ldg, int c0, const fl
 template <int D>
 __device__ __forceinline__ void load_alpha(float (&al)[32], const float* log_g, int64_t tok0, int count, int H, int h,
                                            int i, int base) {
+  float lg[32];
 #pragma unroll
-  for (int u = 0; u < 32; ++u) {
-    const int t = base + u;
-    al[u] = t < count ? exp_fast(log_g[((tok0 + t) * H + h) * D + i]) : 1.f;
-  }
+  for (int u = 0; u < 32; ++u) lg[u] = log_g[((tok0 + min(base + u, count - 1)) * H + h) * D + i];
+  __builtin_amdgcn_sched_barrier(0);  // all 32 loads in flight before the first use
+#pragma unroll
+  for (int u = 0; u < 32; ++u) al[u] = base + u < count ? exp_fast(lg[u]) : 1.f;
 }
 
 // Level-l factors F_l(t) of one channel for tokens [base, base + 32), written
@@ -312,7 +316,10 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
 
   load_rows<D, LD>(sK, k, L.tok0, L.count, a.H, h);
   load_rows<D, LD>(sQ, q, L.tok0, L.count, a.H, h);
-  if (tid < C) sBeta[tid] = tid < L.count ? a.beta[(L.tok0 + tid) * a.H + h] : 0.f;
+  if (tid < C) {
+    const float bv = a.beta[(L.tok0 + min(tid, L.count - 1)) * a.H + h];
+    sBeta[tid] = tid < L.count ? bv : 0.f;
+  }
   // gates of channel ci over half ph of the chunk
   const int ci = tid % D, ph = tid / D;
   const bool chan = ph < 2;
@@ -851,7 +858,7 @@ __device__ __forceinline__ void load_mat_t(float* dst, const float* src) {
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int idx = it * NTH + threadIdx.x;
-    if (idx < N) x[it] = load4(src + idx * 4);
+    x[it] = load4(src + min(idx, N - 1) * 4);
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -919,7 +926,10 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
   const int H = a.H;
   auto row = [&](int t) { return (L.tok0 + t) * H + h; };
 
-  if (tid < C) sBeta[tid] = tid < L.count ? a.beta[row(tid)] : 0.f;
+  if (tid < C) {
+    const float bv = a.beta[row(min(tid, L.count - 1))];
+    sBeta[tid] = tid < L.count ? bv : 0.f;
+  }
   if (tid < 2 * C) sDb[tid] = 0.f;
   load_mat_t<C, C, LM, NTS>(sT, a.Tm + sh * C * C);   // T^T
   load_mat_t<C, D, LM, NTS>(sX, a.dDl + sh * C * D);  // dDelta^T
@@ -948,7 +958,8 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
       const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + c) + r;
       bb[c][j] = active ? sR[t * LD + i] : 0.f;
       rc[c][j] = active ? sS[t * LD + i] : 0.f;
-      kv[c][j] = active && t < L.count ? to_f32(k[row(t) * D + i]) : 0.f;
+      const float kx = to_f32(k[row(min(t, L.count - 1)) * D + min(i, D - 1)]);
+      kv[c][j] = active && t < L.count ? kx : 0.f;
     }
   __syncthreads();
   // dR = T^T dDelta -> sR;  dv = beta dR.  (T^T)[t][s] = 0 for s < t.
@@ -989,7 +1000,8 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
         for (int j = 0; j < 4; ++j) {
           const int c = c0 + n, t = 16 * w + 4 * kq + j, i = 16 * (ctb + c) + r;
           const float kb = kv[c][j] * bb[c][j];
-          const float vv = t < L.count ? to_f32(v[row(t) * D + i]) : 0.f;
+          const float vx = to_f32(v[row(min(t, L.count - 1)) * D + i]);
+          const float vv = t < L.count ? vx : 0.f;
           dbr[j] += sR[t * LD + i] * vv - kb * acc[n][j];
           const float dkb = -sBeta[t] * acc[n][j];
           dk_[c][j] = dkb * bb[c][j];
@@ -1012,7 +1024,8 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
         for (int j = 0; j < 4; ++j) {
           const int c = c0 + n, t = 16 * w + 4 * kq + j, i = 16 * (ctb + c) + r;
           const float dqb = a.scale * acc[n][j];
-          const float qv = t < L.count ? to_f32(q[row(t) * D + i]) : 0.f;
+          const float qx = to_f32(q[row(min(t, L.count - 1)) * D + i]);
+          const float qv = t < L.count ? qx : 0.f;
           dq_[c][j] = dqb * bb[c][j];
           dg_[c][j] += dqb * qv * bb[c][j];
         }
@@ -1025,7 +1038,7 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
     float4 x[IT];
 #pragma unroll
     for (int it = 0; it < IT; ++it)
-      if (it * NTS + tid < N) x[it] = load4(a.dSo + sh * D * D + static_cast<size_t>(it * NTS + tid) * 4);
+      x[it] = load4(a.dSo + sh * D * D + static_cast<size_t>(min(it * NTS + tid, N - 1)) * 4);
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int idx = it * NTS + tid, i = idx / G, jj = 4 * (idx - i * G);
@@ -1157,13 +1170,13 @@ __device__ __forceinline__ void load_cols_t(In* dst, const In* src, int64_t tok0
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int idx = it * NTG + threadIdx.x, t = idx / G, g4 = idx - t * G;
-    const In* p = src + ((tok0 + t) * H + h) * D + c0 + 4 * g4;
+    const In* p = src + ((tok0 + min(t, count - 1)) * H + h) * D + c0 + 4 * g4;
     if constexpr (sizeof(In) == 2) {
-      xb[it] = make_uint2(0u, 0u);
-      if (idx < N && t < count) xb[it] = *reinterpret_cast<const uint2*>(p);
+      const uint2 y = *reinterpret_cast<const uint2*>(p);
+      xb[it] = t < count ? y : make_uint2(0u, 0u);
     } else {
-      xf[it] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (idx < N && t < count) xf[it] = *reinterpret_cast<const float4*>(p);
+      const float4 y = *reinterpret_cast<const float4*>(p);
+      xf[it] = t < count ? y : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
 #pragma unroll
@@ -1279,12 +1292,12 @@ __global__ void __launch_bounds__(NTG, 2) bwd_gpairs(BwdArgs a) {
   // factor threads: channel fi, tokens [8 seg, 8 seg + 8)
   const int fi = tid % CW, seg = tid / CW;
   const bool fthr = seg < 8;
-  float al[8];
+  float al[8], lg[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int t = 8 * seg + u;
-    al[u] = (fthr && t < L.count) ? exp_fast(a.log_g[row(t) * D + c0 + fi]) : 1.f;
-  }
+  for (int u = 0; u < 8; ++u) lg[u] = a.log_g[row(min(8 * seg + u, L.count - 1)) * D + c0 + fi];
+  __builtin_amdgcn_sched_barrier(0);  // all 8 loads in flight before the first use
+#pragma unroll
+  for (int u = 0; u < 8; ++u) al[u] = (fthr && 8 * seg + u < L.count) ? exp_fast(lg[u]) : 1.f;
   if (fthr) {
     float p = 1.f;
 #pragma unroll
@@ -1418,12 +1431,13 @@ __global__ void __launch_bounds__(NTG, 2) bwd_gpairs(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + ct) + r;
+        const int64_t o = row(min(t, L.count - 1)) * D + c0 + i;
+        const float xq = a.dq[o], xk = a.dk[o], xg = a.dlog_g[o];
         float g = 0.f;
         if (t < L.count) {
-          const int64_t o = row(t) * D + c0 + i;
-          a.dq[o] += dq_[ct][j];
-          a.dk[o] += dk_[ct][j];
-          g = a.dlog_g[o] + dg_[ct][j];
+          a.dq[o] = xq + dq_[ct][j];
+          a.dk[o] = xk + dk_[ct][j];
+          g = xg + dg_[ct][j];
         }
         sFT[i * LM + t] = g;
       }
