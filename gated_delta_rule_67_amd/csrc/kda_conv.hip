@@ -116,10 +116,11 @@ __global__ void __launch_bounds__(NTC) conv_kernel(ConvArgs a) {
   while (true) {
     const int64_t te = min(t1, de);
     for (int64_t tb = t; tb < te; tb += UNR) {
+      // unconditional loads (past te they repeat token te-1 and go unused):
+      // a load under a branch would wait for its data before the next issues
       float xv[UNR][CH];
 #pragma unroll
-      for (int u = 0; u < UNR; ++u)
-        if (tb + u < te) load8f(x + (tb + u) * Cn + c, xv[u]);
+      for (int u = 0; u < UNR; ++u) load8f(x + min(tb + u, te - 1) * Cn + c, xv[u]);
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         if (tb + u >= te) break;
