@@ -421,25 +421,32 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
     a.AsT[sh * C * C + idx] = a.scale * sAq[s * LM + t];
   }
   // per channel: b_t (prefix), Qs = scale q b, K*b (kept), Kd = k r(C-1, t), b_C
+  // (the transposed rows QsT and KdT of channel ci are 32 consecutive floats
+  // of this thread: written as float4)
   float kb[32];
   if (chan) {
     float b = ph == 1 ? sTot[ci] : 1.f;
+    float* qst = a.QsT + (sh * D + ci) * C + 32 * ph;
+    float x4[4];
 #pragma unroll
     for (int u = 0; u < 32; ++u) {
       const int t = 32 * ph + u;
       b *= al[u];
       const float qv = sQ[t * LD + ci];
-      a.QsT[(sh * D + ci) * C + t] = a.scale * qv * b;
+      x4[u & 3] = a.scale * qv * b;
+      if ((u & 3) == 3) *reinterpret_cast<float4*>(qst + u - 3) = make_float4(x4[0], x4[1], x4[2], x4[3]);
       kb[u] = sK[t * LD + ci] * b;
     }
     if (ph == 1) a.eg[sh * D + ci] = b;
     float rr = ph == 0 ? sTot[D + ci] : 1.f;
+    float* kdt = a.KdT + (sh * D + ci) * C + 32 * ph;
 #pragma unroll
     for (int u = 31; u >= 0; --u) {
       const int t = 32 * ph + u;
       const float kd = sK[t * LD + ci] * rr;
       a.Kd[(sh * C + t) * D + ci] = kd;
-      a.KdT[(sh * D + ci) * C + t] = kd;
+      x4[u & 3] = kd;
+      if ((u & 3) == 0) *reinterpret_cast<float4*>(kdt + u) = make_float4(x4[0], x4[1], x4[2], x4[3]);
       rr *= al[u];
     }
   }
