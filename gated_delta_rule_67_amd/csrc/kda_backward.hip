@@ -586,15 +586,18 @@ struct ScanL {
 };
 
 // Registers holding one ROWS x COLS block of a row-major global matrix
-// (leading dimension ldg, first column c0) on its way to LDS.
-template <int ROWS, int COLS>
+// (leading dimension ldg, first column c0) on its way to LDS: the loads are
+// issued early and the block is written to LDS after the work they overlap.
+template <int ROWS, int COLS, int NTH = NT>
 struct Staged {
-  static constexpr int G = COLS / 4, N = ROWS * G, IT = (N + NT - 1) / NT;
+  static constexpr int G = COLS / 4, N = ROWS * G, IT = (N + NTH - 1) / NTH;
   float4 x[IT];
+  // (the scans' next-chunk prefetch; these branches do not hold the scan
+  // loop, whose loads have a whole step to arrive)
   __device__ __forceinline__ void load(const float* src, int ldg, int c0, int valid_rows = ROWS) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int idx = it * NT + threadIdx.x, t = idx / G, g4 = idx - t * G;
+      const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
       x[it] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (idx < N && t < valid_rows) x[it] = load4(src + static_cast<int64_t>(t) * ldg + c0 + 4 * g4);
     }
@@ -604,22 +607,40 @@ struct Staged {
                                               int valid_rows) {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int idx = it * NT + threadIdx.x, t = idx / G, g4 = idx - t * G;
+      const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
       x[it] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (idx < N && t < valid_rows) x[it] = load4(src + ((tok0 + t) * H + h) * D + c0 + 4 * g4);
+    }
+  }
+  // The same without branches: unconditional loads from a row clamped into
+  // range (valid_rows >= 1), rows >= valid_rows replaced by zeros afterwards.
+  __device__ __forceinline__ void load_all(const float* src, int ldg, int c0) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
+      x[it] = load4(src + static_cast<int64_t>(min(t, ROWS - 1)) * ldg + c0 + 4 * g4);
+    }
+  }
+  __device__ __forceinline__ void load_tokens_all(const float* src, int64_t tok0, int H, int h, int D, int c0,
+                                                  int valid_rows) {
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
+      const float4 y = load4(src + ((tok0 + min(t, valid_rows - 1)) * H + h) * D + c0 + 4 * g4);
+      x[it] = t < valid_rows ? y : make_float4(0.f, 0.f, 0.f, 0.f);
     }
   }
   __device__ __forceinline__ void store(float* dst, int ld) const {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int idx = it * NT + threadIdx.x, t = idx / G, g4 = idx - t * G;
+      const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
       if (idx < N) *reinterpret_cast<float4*>(dst + t * ld + 4 * g4) = x[it];
     }
   }
   __device__ __forceinline__ void store_t(float* dst, int ldt) const {
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const int idx = it * NT + threadIdx.x, t = idx / G, c = 4 * (idx - t * G);
+      const int idx = it * NTH + threadIdx.x, t = idx / G, c = 4 * (idx - t * G);
       if (idx < N) {
         dst[(c + 0) * ldt + t] = x[it].x;
         dst[(c + 1) * ldt + t] = x[it].y;
@@ -887,9 +908,9 @@ struct GsL {
   static constexpr int LD = D + 4, LM = C + 4;
   static constexpr int BIG = (D > C ? D : C) * LD;
   static constexpr int MID = (C * LD > D * LM ? C * LD : D * LM);
-  static constexpr int RS = 0;                 // r(C-1, t) (staging), S, Delta (rows), dS'
-  static constexpr int RX = RS + BIG;          // dDelta^T (D x LM), dO
-  static constexpr int RR = RX + MID;          // log_g, b (staging), dR, Delta
+  static constexpr int RS = 0;                 // r(C-1, t) (staging), S, Delta (rows)
+  static constexpr int RX = RS + BIG;          // dDelta^T (D x LM), dO; then dS' over RX and RR
+  static constexpr int RR = RX + MID;          // log_g, b (staging), dR
   static constexpr int RT = RR + C * LD;       // T^T
   static constexpr int RB = RT + C * LM;       // beta [C]
   static constexpr int RE = RB + C;            // b_C [D]
@@ -942,6 +963,11 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
   load_mat_t<C, D, LM, NTS>(sX, a.dDl + sh * C * D);  // dDelta^T
   load_rows<D, LD, float, NTS>(sR, a.log_g, L.tok0, L.count, H, h);  // log_g rows (0 past the end)
   __syncthreads();
+  // the entry state and dO are loaded now and written to LDS after dR
+  Staged<D, D, NTS> stS;
+  stS.load_all(a.S_in + sh * D * D, D, 0);
+  Staged<C, D, NTS> stO;
+  stO.load_tokens_all(a.d_out, L.tok0, H, h, D, 0, L.count);
   // per channel: b_t into sR, r(C-1, t) into sS (staging), b_C into sEg
   for (int i = tid; i < D; i += NTS) {
     float rr = 1.f;
@@ -987,9 +1013,11 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
         }
     }
   }
-  load_mat<D, D, LD, NTS>(sS, a.S_in + sh * D * D);
+  stS.store(sS, LD);
   __syncthreads();  // dR and S in place; dDelta^T no longer needed
-  load_rows<D, LD, float, NTS>(sX, a.d_out, L.tok0, L.count, H, h);  // dO
+  stO.store(sX, LD);  // dO
+  Staged<D, D, NTS> stD;  // dS', for the row sums against S
+  stD.load_all(a.dSo + sh * D * D, D, 0);
   float dq_[NCTH][4], dk_[NCTH][4], dg_[NCTH][4];
   float dbr[4] = {0.f, 0.f, 0.f, 0.f};
   // X = dR S^T: d(K*b) = -beta X, and the R part of dbeta,
@@ -1017,6 +1045,8 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
     }
   }
   __syncthreads();  // dO in place
+  Staged<C, D, NTS> stL;  // Delta rows
+  stL.load_all(a.Dl + sh * C * D, D, 0);
   // Y = dO S^T: d(Q*b) = scale Y
   if (active) {
 #pragma unroll
@@ -1042,28 +1072,32 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
   {
     constexpr int G = D / 4, N = D * G, IT = (N + NTS - 1) / NTS;
     static_assert(G <= 64 && NTS % G == 0 && (N >= NTS || N % 64 == 0), "row groups must stay inside a wave");
-    float4 x[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it)
-      x[it] = load4(a.dSo + sh * D * D + static_cast<size_t>(min(it * NTS + tid, N - 1)) * 4);
+    static_assert(decltype(stD)::IT == IT, "same thread mapping as the staged dS'");
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
       const int idx = it * NTS + tid, i = idx / G, jj = 4 * (idx - i * G);
       if (idx >= N) continue;  // whole waves
       const float* sr = sS + i * LD + jj;
-      float acc = x[it].x * sr[0] + x[it].y * sr[1] + x[it].z * sr[2] + x[it].w * sr[3];
+      const float4 xd = stD.x[it];
+      float acc = xd.x * sr[0] + xd.y * sr[1] + xd.z * sr[2] + xd.w * sr[3];
 #pragma unroll
       for (int o = 1; o < G; o <<= 1) acc += __shfl_xor(acc, o, 64);
       if ((tid & (G - 1)) == 0) sGam[i] = sEg[i] * acc;
     }
   }
   __syncthreads();  // done with S
-  load_mat<C, D, LD, NTS>(sS, a.Dl + sh * C * D);  // Delta, rows
+  stL.store(sS, LD);  // Delta, rows
   __syncthreads();
+  stD.load_all(a.dSo + sh * D * D, D, 0);  // dS' again (L2), for Z
   // dAqk = scale tril(dO Delta^T), dA = -tril(dR Delta^T, -1); this wave's
   // two s blocks [2 half, 2 half + 2)
   {
     f32x4 aq[2], aa[2];
+    float akk[2][4];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) akk[n][j] = a.Ab[sh * C * C + (16 * w + 4 * kq + j) * C + 16 * (2 * half + n) + r];
 #pragma unroll
     for (int n = 0; n < 2; ++n) aq[n] = aa[n] = zero4f();
     mm_kc<2>(aq, sX + 16 * w * LD, LD, sS + 32 * half * LD, LD, 0, D);
@@ -1075,7 +1109,7 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
         const int t = 16 * w + 4 * kq + j, s = 16 * (2 * half + n) + r;
         const float gq = s <= t ? a.scale * aq[n][j] : 0.f;
         const float ga = s < t ? -aa[n][j] : 0.f;
-        dbr[j] += ga * a.Ab[sh * C * C + t * C + s];
+        dbr[j] += ga * akk[n][j];
         a.dAq[sh * C * C + t * C + s] = gq;
         a.dAb[sh * C * C + t * C + s] = sBeta[t] * ga;
       }
@@ -1090,9 +1124,9 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
     x += __shfl_xor(x, 8, 64);
     if (r == 0) sDb[half * C + 16 * w + 4 * kq + j] = x;
   }
-  __syncthreads();  // done with Delta rows (sS) and dR (sR)
-  load_mat<C, D, LD, NTS>(sR, a.Dl + sh * C * D);   // Delta
-  load_mat<D, D, LD, NTS>(sS, a.dSo + sh * D * D);  // dS'
+  __syncthreads();  // done with dO (sX) and dR (sR); Delta rows stay in sS
+  static_assert(D * LD <= P::MID + C * LD, "dS' fits over the dO and dR regions");
+  stD.store(sX, LD);  // dS'
   __syncthreads();
   // Z = Delta dS'^T: dKd = Z
   float colp[NCTH];
@@ -1102,7 +1136,7 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
       f32x4 acc[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n) acc[n] = zero4f();
-      mm_kc<NB>(acc, sR + 16 * w * LD, LD, sS + 16 * (ctb + c0) * LD, LD, 0, D);
+      mm_kc<NB>(acc, sS + 16 * w * LD, LD, sX + 16 * (ctb + c0) * LD, LD, 0, D);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         const int c = c0 + n;
