@@ -679,6 +679,15 @@ template <int NB>
 __device__ __forceinline__ void mm_kc(f32x4 (&acc)[NB], const float* A, int lda, const float* Bt, int ldb, int k_lo,
                                       int k_hi);
 
+// Block -> (unit, value tile): the NTILE tiles of a unit are 8 blocks apart,
+// so they run on one XCD and the chunk operands they all read (W, Kd, ...)
+// come from HBM once into that XCD's L2.
+__device__ __forceinline__ void scan_block(int& unit, int& tile, int ntile) {
+  const int b = blockIdx.x, grp = b / (8 * ntile), rem = b - grp * 8 * ntile;
+  tile = rem / 8;
+  unit = grp * 8 + (rem & 7);
+}
+
 // bwd_fscan: entry state of every chunk, and Delta = U - W S.
 template <int D>
 __global__ void __launch_bounds__(NT) bwd_fscan(BwdArgs a) {
@@ -692,7 +701,9 @@ __global__ void __launch_bounds__(NT) bwd_fscan(BwdArgs a) {
   float* sXT = sm + P::FX;
   float* sG = sm + P::FG;
 
-  const int unit = blockIdx.x / P::NTILE, tile = blockIdx.x - unit * P::NTILE;
+  int unit, tile;
+  scan_block(unit, tile, P::NTILE);
+  if (unit >= a.N * a.H) return;
   const int n = unit / a.H, h = unit - n * a.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kq = lane >> 4;
   const int c0 = tile * DVT;
@@ -773,7 +784,9 @@ __global__ void __launch_bounds__(NT) bwd_rscan(BwdArgs a) {
   float* sXT = sm + P::RX;  // dDelta^T tile
   float* sG = sm + P::RG;
 
-  const int unit = blockIdx.x / P::NTILE, tile = blockIdx.x - unit * P::NTILE;
+  int unit, tile;
+  scan_block(unit, tile, P::NTILE);
+  if (unit >= a.N * a.H) return;
   const int n = unit / a.H, h = unit - n * a.H;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kq = lane >> 4;
   const int c0 = tile * DVT;
@@ -1626,7 +1639,7 @@ hipError_t bwd_prepare_device() {
 template <int D, typename In>
 hipError_t run_bwd(const BwdArgs& a, int64_t ns, hipStream_t stream) {
   const unsigned chunk_blocks = static_cast<unsigned>(ns * a.H);
-  const unsigned unit_blocks = static_cast<unsigned>(a.N) * a.H * ScanL<D>::NTILE;
+  const unsigned unit_blocks = static_cast<unsigned>((static_cast<int64_t>(a.N) * a.H + 7) / 8 * 8) * ScanL<D>::NTILE;
   hipError_t e;
   if (chunk_blocks > 0) {
     hipLaunchKernelGGL((bwd_prep<D, In>), dim3(chunk_blocks), dim3(NT), PrepL<D>::BYTES, stream, a);
@@ -1660,7 +1673,7 @@ bool bwd_supported(const BwdLaunch& a) {
   const int64_t blocks = bwd_slots(a.num_seqs, a.seq_len, packed) * a.num_heads;
   // bwd_gpairs runs up to two workgroups per (slot, head), rounded up to 16
   return (a.d == 16 || a.d == 32 || a.d == 64 || a.d == 128) && (blocks + 16) * 2 < (int64_t(1) << 31) &&
-         int64_t(a.num_seqs) * a.num_heads * 4 < (int64_t(1) << 31);
+         (int64_t(a.num_seqs) * a.num_heads + 8) * 4 < (int64_t(1) << 31);
 }
 
 hipError_t launch_chunk_bwd(const BwdLaunch& s, hipStream_t stream) {
