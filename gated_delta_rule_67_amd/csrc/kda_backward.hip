@@ -653,19 +653,19 @@ struct Staged {
 
 // A D x DVT tile kept transposed in LDS (tT[col * LD + i]) to or from the
 // row-major D x D global matrix g at columns [c0, c0 + DVT).
-template <int D, int DVT, int LD>
+template <int D, int DVT, int LD, int NTH = NT>
 __device__ __forceinline__ void tile_to_global(float* g, int c0, const float* tT) {
   constexpr int G = DVT / 4;
-  for (int idx = threadIdx.x; idx < D * G; idx += NT) {
+  for (int idx = threadIdx.x; idx < D * G; idx += NTH) {
     const int i = idx / G, c = 4 * (idx - i * G);
     *reinterpret_cast<float4*>(g + static_cast<size_t>(i) * D + c0 + c) =
         make_float4(tT[c * LD + i], tT[(c + 1) * LD + i], tT[(c + 2) * LD + i], tT[(c + 3) * LD + i]);
   }
 }
-template <int D, int DVT, int LD>
+template <int D, int DVT, int LD, int NTH = NT>
 __device__ __forceinline__ void tile_from_global(float* tT, const float* g, int c0) {
   constexpr int G = DVT / 4;
-  for (int idx = threadIdx.x; idx < D * G; idx += NT) {
+  for (int idx = threadIdx.x; idx < D * G; idx += NTH) {
     const int i = idx / G, c = 4 * (idx - i * G);
     const float4 x = g ? load4(g + static_cast<size_t>(i) * D + c0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
     tT[c * LD + i] = x.x;
@@ -688,9 +688,11 @@ __device__ __forceinline__ void scan_block(int& unit, int& tile, int ntile) {
   unit = grp * 8 + (rem & 7);
 }
 
+constexpr int NSC = 512;  // scan threads: 8 waves
+
 // bwd_fscan: entry state of every chunk, and Delta = U - W S.
 template <int D>
-__global__ void __launch_bounds__(NT) bwd_fscan(BwdArgs a) {
+__global__ void __launch_bounds__(NSC) bwd_fscan(BwdArgs a) {
   using P = ScanL<D>;
   constexpr int DVT = P::DVT, NBC = P::NBC, LD = P::LD, LM = P::LM, LV = P::LV;
   extern __shared__ __align__(16) float sm[];
@@ -710,12 +712,12 @@ __global__ void __launch_bounds__(NT) bwd_fscan(BwdArgs a) {
   int first, nch;
   unit_chunks(a, n, first, nch);
 
-  tile_from_global<D, DVT, LD>(sST, a.init_state ? a.init_state + (static_cast<size_t>(n) * a.H + h) * D * D : nullptr,
-                               c0);
-  Staged<C, D> pW;
-  Staged<D, C> pK;
-  Staged<C, DVT> pU;
-  Staged<1, D> pG;
+  tile_from_global<D, DVT, LD, NSC>(
+      sST, a.init_state ? a.init_state + (static_cast<size_t>(n) * a.H + h) * D * D : nullptr, c0);
+  Staged<C, D, NSC> pW;
+  Staged<D, C, NSC> pK;
+  Staged<C, DVT, NSC> pU;
+  Staged<1, D, NSC> pG;
   auto fetch = [&](int c) {
     const size_t sh = static_cast<size_t>(first + c) * a.H + h;
     pW.load(a.Wm + sh * C * D, D, 0);
@@ -732,27 +734,24 @@ __global__ void __launch_bounds__(NT) bwd_fscan(BwdArgs a) {
     pU.store(sU, LV);
     pG.store(sG, D);
     if (c + 1 < nch) fetch(c + 1);
-    tile_to_global<D, DVT, LD>(a.S_in + sh * D * D, c0, sST);
+    tile_to_global<D, DVT, LD, NSC>(a.S_in + sh * D * D, c0, sST);
     __syncthreads();
-    // Delta = U - W S: wave w, rows [16w, 16w + 16)
-    {
-      f32x4 acc[NBC];
+    // Delta = U - W S: wave w, rows [16 (w & 3), +16), columns [16 (w >> 2), +16)
+    if (w < 4 * NBC) {
+      const int I = w & 3, nb = w >> 2;
+      f32x4 acc[1] = {zero4f()};
+      mm_kc<1>(acc, sW + 16 * I * LD, LD, sST + 16 * nb * LD, LD, 0, D);
 #pragma unroll
-      for (int nb = 0; nb < NBC; ++nb) acc[nb] = zero4f();
-      mm_kc<NBC>(acc, sW + 16 * w * LD, LD, sST, LD, 0, D);
-#pragma unroll
-      for (int nb = 0; nb < NBC; ++nb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = 16 * w + 4 * kq + j, col = 16 * nb + r;
-          const float dl = sU[t * LV + col] - acc[nb][j];
-          sXT[col * LM + t] = dl;
-          a.Dl[(sh * C + t) * D + c0 + col] = dl;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * I + 4 * kq + j, col = 16 * nb + r;
+        const float dl = sU[t * LV + col] - acc[0][j];
+        sXT[col * LM + t] = dl;
+        a.Dl[(sh * C + t) * D + c0 + col] = dl;
+      }
     }
     __syncthreads();
     // S = b_C S + Kd^T Delta
-    for (int ib = w; ib < D / 16; ib += 4) {
+    for (int ib = w; ib < D / 16; ib += 8) {
       f32x4 acc[NBC];
 #pragma unroll
       for (int nb = 0; nb < NBC; ++nb) acc[nb] = zero4f();
@@ -771,7 +770,7 @@ __global__ void __launch_bounds__(NT) bwd_fscan(BwdArgs a) {
 // bwd_rscan: backwards over the unit's chunks; dDelta and the exit-state
 // gradient of every chunk, and the gradient of the initial state.
 template <int D>
-__global__ void __launch_bounds__(NT) bwd_rscan(BwdArgs a) {
+__global__ void __launch_bounds__(NSC) bwd_rscan(BwdArgs a) {
   using P = ScanL<D>;
   constexpr int DVT = P::DVT, NBC = P::NBC, LD = P::LD, LM = P::LM;
   extern __shared__ __align__(16) float sm[];
@@ -794,13 +793,13 @@ __global__ void __launch_bounds__(NT) bwd_rscan(BwdArgs a) {
   unit_chunks(a, n, first, nch);
   const size_t uo = (static_cast<size_t>(n) * a.H + h) * D * D;
 
-  tile_from_global<D, DVT, LD>(sST, a.d_final ? a.d_final + uo : nullptr, c0);
-  Staged<C, C> pA;
-  Staged<C, D> pK;
-  Staged<D, C> pQ;
-  Staged<D, C> pW;
-  Staged<C, DVT> pO;
-  Staged<1, D> pG;
+  tile_from_global<D, DVT, LD, NSC>(sST, a.d_final ? a.d_final + uo : nullptr, c0);
+  Staged<C, C, NSC> pA;
+  Staged<C, D, NSC> pK;
+  Staged<D, C, NSC> pQ;
+  Staged<D, C, NSC> pW;
+  Staged<C, DVT, NSC> pO;
+  Staged<1, D, NSC> pG;
   auto fetch = [&](int c) {
     const int slot = first + c;
     const size_t sh = static_cast<size_t>(slot) * a.H + h;
@@ -824,27 +823,24 @@ __global__ void __launch_bounds__(NT) bwd_rscan(BwdArgs a) {
     pO.store_t(sOT, LM);
     pG.store(sG, D);
     if (c > 0) fetch(c - 1);
-    tile_to_global<D, DVT, LD>(a.dSo + sh * D * D, c0, sST);
+    tile_to_global<D, DVT, LD, NSC>(a.dSo + sh * D * D, c0, sST);
     __syncthreads();
-    // dDelta = As^T dO + Kd dS
-    {
-      f32x4 acc[NBC];
+    // dDelta = As^T dO + Kd dS: wave w, rows [16 (w & 3), +16), columns [16 (w >> 2), +16)
+    if (w < 4 * NBC) {
+      const int I = w & 3, nb = w >> 2;
+      f32x4 acc[1] = {zero4f()};
+      mm_kc<1>(acc, sAT + 16 * I * LM, LM, sOT + 16 * nb * LM, LM, 0, C);
+      mm_kc<1>(acc, sKd + 16 * I * LD, LD, sST + 16 * nb * LD, LD, 0, D);
 #pragma unroll
-      for (int nb = 0; nb < NBC; ++nb) acc[nb] = zero4f();
-      mm_kc<NBC>(acc, sAT + 16 * w * LM, LM, sOT, LM, 0, C);
-      mm_kc<NBC>(acc, sKd + 16 * w * LD, LD, sST, LD, 0, D);
-#pragma unroll
-      for (int nb = 0; nb < NBC; ++nb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int t = 16 * w + 4 * kq + j, col = 16 * nb + r;
-          sXT[col * LM + t] = acc[nb][j];
-          a.dDl[(sh * C + t) * D + c0 + col] = acc[nb][j];
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * I + 4 * kq + j, col = 16 * nb + r;
+        sXT[col * LM + t] = acc[0][j];
+        a.dDl[(sh * C + t) * D + c0 + col] = acc[0][j];
+      }
     }
     __syncthreads();
     // dS = b_C dS + Qs^T dO - W^T dDelta
-    for (int ib = w; ib < D / 16; ib += 4) {
+    for (int ib = w; ib < D / 16; ib += 8) {
       f32x4 acc[NBC], neg[NBC];
 #pragma unroll
       for (int nb = 0; nb < NBC; ++nb) acc[nb] = neg[nb] = zero4f();
@@ -860,7 +856,7 @@ __global__ void __launch_bounds__(NT) bwd_rscan(BwdArgs a) {
     }
   }
   __syncthreads();
-  if (a.d_init) tile_to_global<D, DVT, LD>(a.d_init + uo, c0, sST);
+  if (a.d_init) tile_to_global<D, DVT, LD, NSC>(a.d_init + uo, c0, sST);
 }
 
 // ---------------------------------------------------------------------------
@@ -1646,9 +1642,9 @@ hipError_t run_bwd(const BwdArgs& a, int64_t ns, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (unit_blocks > 0) {
-    hipLaunchKernelGGL((bwd_fscan<D>), dim3(unit_blocks), dim3(NT), sizeof(float) * ScanL<D>::F_FLOATS, stream, a);
+    hipLaunchKernelGGL((bwd_fscan<D>), dim3(unit_blocks), dim3(NSC), sizeof(float) * ScanL<D>::F_FLOATS, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_rscan<D>), dim3(unit_blocks), dim3(NT), sizeof(float) * ScanL<D>::R_FLOATS, stream, a);
+    hipLaunchKernelGGL((bwd_rscan<D>), dim3(unit_blocks), dim3(NSC), sizeof(float) * ScanL<D>::R_FLOATS, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (chunk_blocks > 0) {
