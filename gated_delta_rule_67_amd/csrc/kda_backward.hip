@@ -291,8 +291,10 @@ struct PrepL {
   static constexpr size_t BYTES = sizeof(float) * FLOATS;
 };
 
+constexpr int NTP = 512;  // bwd_prep threads: 8 waves, two per 16-token block
+
 template <int D, typename In>
-__global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
+__global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
   using P = PrepL<D>;
   constexpr int LD = P::LD, LM = P::LM;
   extern __shared__ __align__(16) float sm[];
@@ -308,14 +310,18 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
   const int slot = blockIdx.x / a.H, h = blockIdx.x - slot * a.H;
   Loc L;
   if (!locate(a, slot, L)) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kq = lane >> 4;
+  // wave wv: 16-token block w, and half hf of the channels (pair tiles) or of
+  // the column tiles (W, U)
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, w = wv & 3, hf = wv >> 2, r = lane & 15, kq = lane >> 4;
+  constexpr int KH = D >= 32 ? D / 2 : D;  // channels per half
+  const bool khalf = hf * KH < D;
   const size_t sh = static_cast<size_t>(slot) * a.H + h;
   const In* q = static_cast<const In*>(a.q);
   const In* k = static_cast<const In*>(a.k);
   const In* v = static_cast<const In*>(a.v);
 
-  load_rows<D, LD>(sK, k, L.tok0, L.count, a.H, h);
-  load_rows<D, LD>(sQ, q, L.tok0, L.count, a.H, h);
+  load_rows<D, LD, In, NTP>(sK, k, L.tok0, L.count, a.H, h);
+  load_rows<D, LD, In, NTP>(sQ, q, L.tok0, L.count, a.H, h);
   if (tid < C) {
     const float bv = a.beta[(L.tok0 + min(tid, L.count - 1)) * a.H + h];
     sBeta[tid] = tid < L.count ? bv : 0.f;
@@ -331,7 +337,7 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
   // (k = k0 + 4 kq + m for the m-th MFMA, the same order on both sides)
   auto pair_tile = [&](int I, int J, f32x4& accK, f32x4& accQ) {
     const int tt = (16 * I + r) * LD + 4 * kq, ts = (16 * J + r) * LD + 4 * kq;
-    for (int k0 = 0; k0 < D; k0 += 16) {
+    for (int k0 = hf * KH; k0 < hf * KH + KH; k0 += 16) {
       const float4 ft = *reinterpret_cast<const float4*>(sF + tt + k0);
       const float4 kt = *reinterpret_cast<const float4*>(sK + tt + k0);
       const float4 qt = *reinterpret_cast<const float4*>(sQ + tt + k0);
@@ -361,6 +367,7 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
       }
     }
     __syncthreads();
+    if (!khalf) continue;
     if (l == 0) {
       pair_tile(2 + (w >> 1), w & 1, ab_0, aq_0);
     } else if (l == 1) {
@@ -377,10 +384,10 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
     }
   }
   // diagonal of Aqk: r(t, t) = 1
-  {
+  if (khalf) {
     f32x4 tq = zero4f();
     const int tt = (16 * w + r) * LD + 4 * kq;
-    for (int k0 = 0; k0 < D; k0 += 16) {
+    for (int k0 = hf * KH; k0 < hf * KH + KH; k0 += 16) {
       const float4 qt = *reinterpret_cast<const float4*>(sQ + tt + k0);
       const float4 kt = *reinterpret_cast<const float4*>(sK + tt + k0);
       tq = mma(qt.x, kt.x, tq);
@@ -392,19 +399,25 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
     for (int j = 0; j < 4; ++j) aq_d[j] += (4 * kq + j == r) ? tq[j] : 0.f;
   }
   __syncthreads();  // everyone done with sF
-  for (int idx = tid; idx < 2 * P::CM; idx += NT) sAb[idx] = 0.f;
+  for (int idx = tid; idx < 2 * P::CM; idx += NTP) sAb[idx] = 0.f;
   __syncthreads();
+  // the two channel halves of every tile: the first half's waves store, the
+  // second half's add
   auto put = [&](float* M, int I, int J, const f32x4& x) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) M[(16 * I + 4 * kq + j) * LM + 16 * J + r] = x[j];
+    for (int j = 0; j < 4; ++j) M[(16 * I + 4 * kq + j) * LM + 16 * J + r] += x[j];
   };
-  put(sAb, w, w, ab_d);
-  put(sAq, w, w, aq_d);
-  put(sAb, 2 + (w >> 1), w & 1, ab_0);
-  put(sAq, 2 + (w >> 1), w & 1, aq_0);
-  if (w < 2) {
-    put(sAb, w == 0 ? 1 : 3, w == 0 ? 0 : 2, ab_1);
-    put(sAq, w == 0 ? 1 : 3, w == 0 ? 0 : 2, aq_1);
+  for (int pass = 0; pass < 2; ++pass) {
+    if (pass == 1) __syncthreads();
+    if (hf != pass || !khalf) continue;
+    put(sAb, w, w, ab_d);
+    put(sAq, w, w, aq_d);
+    put(sAb, 2 + (w >> 1), w & 1, ab_0);
+    put(sAq, 2 + (w >> 1), w & 1, aq_0);
+    if (w < 2) {
+      put(sAb, w == 0 ? 1 : 3, w == 0 ? 0 : 2, ab_1);
+      put(sAq, w == 0 ? 1 : 3, w == 0 ? 0 : 2, aq_1);
+    }
   }
   // block totals of the two halves for the cumulative decays
   if (chan) {
@@ -415,7 +428,7 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
   }
   __syncthreads();
   // Akk and (scale * Aqk)^T to the workspace
-  for (int idx = tid; idx < C * C; idx += NT) {
+  for (int idx = tid; idx < C * C; idx += NTP) {
     const int t = idx / C, s = idx - t * C;
     a.Ab[sh * C * C + idx] = sAb[t * LM + s];
     a.AsT[sh * C * C + idx] = a.scale * sAq[s * LM + t];
@@ -450,7 +463,7 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
       rr *= al[u];
     }
   }
-  for (int idx = tid; idx < P::CM; idx += NT) sT[idx] = 0.f;
+  for (int idx = tid; idx < P::CM; idx += NTP) sT[idx] = 0.f;
   __syncthreads();  // K and Q no longer needed; T zeroed
   float* sKbT = sQ;  // (K*b)^T [i][t]
   float* sVT = sK;   // V^T [i][t]
@@ -459,7 +472,7 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
     for (int u = 0; u < 32; u += 4)
       *reinterpret_cast<float4*>(sKbT + ci * LM + 32 * ph + u) = make_float4(kb[u], kb[u + 1], kb[u + 2], kb[u + 3]);
   }
-  load_rows_t<D, LM>(sVT, v, L.tok0, L.count, a.H, h);
+  load_rows_t<D, LM, In, NTP>(sVT, v, L.tok0, L.count, a.H, h);
   // T = (I + diag(beta) Akk)^-1: diagonal 16 x 16 blocks by forward substitution
   if (tid < 64) {
     const int I = tid >> 4, c = tid & 15;
@@ -475,10 +488,10 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
     }
   }
   // off-diagonal blocks: T_IJ = -T_II sum_{J <= K < I} A_IK T_KJ
-  float* scr = sm + P::R4 + w * 16 * 17;
+  float* scr = sm + P::R4 + w * 16 * 17;  // (waves wv < 4 only)
   for (int I = 1; I < 4; ++I) {
     __syncthreads();
-    if (w < I) {
+    if (wv < I) {
       const int J = w;
       f32x4 x = zero4f();
       const float bI = sBeta[16 * I + r];
@@ -493,7 +506,7 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
       for (int j = 0; j < 4; ++j) scr[(4 * kq + j) * 17 + r] = x[j];
     }
     __syncthreads();
-    if (w < I) {
+    if (wv < I) {
       const int J = w;
       f32x4 y = zero4f();
 #pragma unroll
@@ -506,16 +519,16 @@ __global__ void __launch_bounds__(NT) bwd_prep(BwdArgs a) {
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < C * C; idx += NT) {
+  for (int idx = tid; idx < C * C; idx += NTP) {
     const int t = idx / C, s = idx - t * C;
     a.Tm[sh * C * C + idx] = sT[t * LM + s];
   }
   // W = T diag(beta) (K*b), U = T diag(beta) V; T is lower triangular, so
   // rows [16w, 16w + 16) contract over s < 16 (w + 1)
-  constexpr int NCT = D / 16, NB = NCT < 4 ? NCT : 4;
+  constexpr int NCT = D / 16, NCTP = NCT >= 2 ? NCT / 2 : NCT, NB = NCTP < 4 ? NCTP : 4;
   const int kend = 16 * (w + 1);
 #pragma unroll
-  for (int c0 = 0; c0 < NCT; c0 += NB) {
+  for (int c0 = hf * NCTP; c0 < hf * NCTP + NCTP && c0 < NCT; c0 += NB) {
     f32x4 accW[NB], accU[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) accW[n] = accU[n] = zero4f();
@@ -1638,7 +1651,7 @@ hipError_t run_bwd(const BwdArgs& a, int64_t ns, hipStream_t stream) {
   const unsigned unit_blocks = static_cast<unsigned>((static_cast<int64_t>(a.N) * a.H + 7) / 8 * 8) * ScanL<D>::NTILE;
   hipError_t e;
   if (chunk_blocks > 0) {
-    hipLaunchKernelGGL((bwd_prep<D, In>), dim3(chunk_blocks), dim3(NT), PrepL<D>::BYTES, stream, a);
+    hipLaunchKernelGGL((bwd_prep<D, In>), dim3(chunk_blocks), dim3(NTP), PrepL<D>::BYTES, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (unit_blocks > 0) {
