@@ -1446,18 +1446,17 @@ __global__ void __launch_bounds__(NTG, 2) bwd_gpairs(BwdArgs a) {
       }
     }
   };
+  // levels 0-2 (pairs across 32-, 16- and 8-token halves) as MFMA tile
+  // products; levels 3-5 (pairs inside an aligned 8-token group) below
 #pragma unroll
-  for (int l = 0; l < 6; ++l) {
+  for (int l = 0; l < 3; ++l) {
     __syncthreads();  // segment totals written; previous level's factors read
     if (fthr) {
       float f[8];
       switch (l) {
         case 0: level_factors8<0, CW>(al, seg, sSeg + fi, f); break;
         case 1: level_factors8<1, CW>(al, seg, sSeg + fi, f); break;
-        case 2: level_factors8<2, CW>(al, seg, sSeg + fi, f); break;
-        case 3: level_factors8<3, CW>(al, seg, sSeg + fi, f); break;
-        case 4: level_factors8<4, CW>(al, seg, sSeg + fi, f); break;
-        default: level_factors8<5, CW>(al, seg, sSeg + fi, f); break;
+        default: level_factors8<2, CW>(al, seg, sSeg + fi, f); break;
       }
       float* dst = sFT + fi * LM + 8 * seg;
       *reinterpret_cast<float4*>(dst) = make_float4(f[0], f[1], f[2], f[3]);
@@ -1472,8 +1471,43 @@ __global__ void __launch_bounds__(NTG, 2) bwd_gpairs(BwdArgs a) {
       if (w & 1) level_terms(1, true, 16 * (w - 1), 16);
       else level_terms(1, false, 16 * (w + 1), 16);
     } else {
-      level_terms(l, true, 16 * w, 16);
-      level_terms(l, false, 16 * w, 16);
+      level_terms(2, true, 16 * w, 16);
+      level_terms(2, false, 16 * w, 16);
+    }
+  }
+  // Pairs t > s inside the 8-token group [8 seg, 8 seg + 8), per channel fi:
+  // r(t, s) is a running product of the gates, so each pair costs a few
+  // fused multiply-adds on the vector units instead of a masked MFMA level.
+  //   a = dAqk r, b = dAkk r:  dq_t += a k_s, dk_t += b k_s,
+  //   c = a q_t + b k_t: dk_s += c,  u = k_s c: dG_t += u, dG_s -= u
+  float pq[8], pk[8], pg[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) pq[u] = pk[u] = pg[u] = 0.f;
+  if (fthr) {
+    float kx[8], qx[8];
+    {
+      const float4 k0 = load4(sKT + fi * LM + 8 * seg), k1 = load4(sKT + fi * LM + 8 * seg + 4);
+      const float4 q0 = load4(sQT + fi * LM + 8 * seg), q1 = load4(sQT + fi * LM + 8 * seg + 4);
+      kx[0] = k0.x; kx[1] = k0.y; kx[2] = k0.z; kx[3] = k0.w; kx[4] = k1.x; kx[5] = k1.y; kx[6] = k1.z; kx[7] = k1.w;
+      qx[0] = q0.x; qx[1] = q0.y; qx[2] = q0.z; qx[3] = q0.w; qx[4] = q1.x; qx[5] = q1.y; qx[6] = q1.z; qx[7] = q1.w;
+    }
+    const float* aq = sdAq + 8 * seg * LM + 8 * seg;  // aq[t * LM + s]: dAqk of the group's pair (t, s)
+    const float* ab = sdAb + 8 * seg * LM + 8 * seg;
+#pragma unroll
+    for (int s0 = 0; s0 < 7; ++s0) {
+      float rr = 1.f;
+#pragma unroll
+      for (int t0 = s0 + 1; t0 < 8; ++t0) {
+        rr *= al[t0];
+        const float av = aq[t0 * LM + s0] * rr, bv = ab[t0 * LM + s0] * rr;
+        pq[t0] += av * kx[s0];
+        pk[t0] += bv * kx[s0];
+        const float cv = av * qx[t0] + bv * kx[t0];
+        pk[s0] += cv;
+        const float uv = kx[s0] * cv;
+        pg[t0] += uv;
+        pg[s0] -= uv;
+      }
     }
   }
   // pairs t = s (r = 1): Aqk only
@@ -1486,7 +1520,20 @@ __global__ void __launch_bounds__(NTG, 2) bwd_gpairs(BwdArgs a) {
       dq_[ct][j] += d * ld1f(sKT + i * LM + t);
       dk_[ct][j] += d * ld1f(sQT + i * LM + t);
     }
-  __syncthreads();  // done with F^T
+  __syncthreads();  // done with F^T and the dA tiles
+  // the in-group terms, by channel row, over the dA tiles (dq, dk) and F^T (dG)
+  if (fthr) {
+    float* dq8 = sdAq + fi * LM + 8 * seg;
+    float* dk8 = sdAb + fi * LM + 8 * seg;
+    float* dg8 = sFT + fi * LM + 8 * seg;
+    *reinterpret_cast<float4*>(dq8) = make_float4(pq[0], pq[1], pq[2], pq[3]);
+    *reinterpret_cast<float4*>(dq8 + 4) = make_float4(pq[4], pq[5], pq[6], pq[7]);
+    *reinterpret_cast<float4*>(dk8) = make_float4(pk[0], pk[1], pk[2], pk[3]);
+    *reinterpret_cast<float4*>(dk8 + 4) = make_float4(pk[4], pk[5], pk[6], pk[7]);
+    *reinterpret_cast<float4*>(dg8) = make_float4(pg[0], pg[1], pg[2], pg[3]);
+    *reinterpret_cast<float4*>(dg8 + 4) = make_float4(pg[4], pg[5], pg[6], pg[7]);
+  }
+  __syncthreads();
   // add the state-side parts staged by bwd_gstate; dG^T into sFT for the cumsum
   if (active) {
 #pragma unroll
@@ -1497,10 +1544,11 @@ __global__ void __launch_bounds__(NTG, 2) bwd_gpairs(BwdArgs a) {
         const int64_t o = row(min(t, L.count - 1)) * D + c0 + i;
         const float xq = a.dq[o], xk = a.dk[o], xg = a.dlog_g[o];
         float g = 0.f;
+        const float gin = sFT[i * LM + t];
         if (t < L.count) {
-          a.dq[o] = xq + dq_[ct][j];
-          a.dk[o] = xk + dk_[ct][j];
-          g = xg + dg_[ct][j];
+          a.dq[o] = xq + dq_[ct][j] + sdAq[i * LM + t];
+          a.dk[o] = xk + dk_[ct][j] + sdAb[i * LM + t];
+          g = xg + dg_[ct][j] + gin;
         }
         sFT[i * LM + t] = g;
       }
