@@ -3,7 +3,10 @@
 // The loss L = sum(d_out * out) + sum(d_final * final_state) is differentiated
 // through the gated delta rule (NeMo glm5_next.layers: `_torch_recurrent_kda`
 // is the differentiable reference; the KDA parameters are trained under FSDP).
-// Everything is fp32: operands, MFMA (v_mfma_f32_16x16x4_f32) and state.
+// Arithmetic: fp32 operands, MFMA (v_mfma_f32_16x16x4_f32) and state; for bf16
+// inputs the two scans form their products from split-bf16 operands (three
+// bf16 MFMAs per product, about 16 bits of precision per term) with the state
+// kept in fp32.
 //
 // Chunk form (64 tokens, one unit = (sequence or document, head)).  Inside a
 // chunk with entry state S, b_t = prod_{u<=t} alpha_u (alpha = exp(log_g), per
@@ -37,7 +40,9 @@
 // or per (unit, value-column tile)):
 //   bwd_prep      per chunk: Akk, Aqk, T, W, U, Kd, scale*(Q*b), b_C
 //   bwd_fscan     per unit, serially over its chunks: entry states S, Delta
+//                 (bwd_fscan3 with split-bf16 products)
 //   bwd_rscan     per unit, backwards: exit-state gradients dS', dDelta, dS0
+//                 (bwd_rscan3 with split-bf16 products)
 //   bwd_gstate    per chunk: dv, dbeta, dAqk, dA and the state-side parts of
 //                 dq, dk and dG (staged in the dq, dk, dlog_g outputs)
 //   bwd_gpairs    per chunk: the pair terms, then dlog_g = reverse cumsum(dG)
@@ -274,6 +279,48 @@ __device__ __forceinline__ bool at_level(int l, int t, int s) {
 
 __device__ __forceinline__ f32x4 zero4f() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Split-bf16 operands (bf16 inputs).  An fp32 value x is held as hi + lo, two
+// bf16 values (round to nearest even twice: |x - hi - lo| <= 2^-16 |x|), and a
+// product as three bf16 MFMAs, hi*hi + hi*lo + lo*hi.
+// bf16 inputs (2e-2 bar) run the scans on split-bf16 products; fp32 inputs
+// keep fp32 products.  The split kernels contract in 32-wide blocks.
+template <int D, typename In>
+constexpr bool split_scans() {
+  return sizeof(In) == 2 && D % 32 == 0;
+}
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f32x4 mfma_bf(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ uint32_t rne_bf16(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+// hi and lo halves of x, as bf16 bits
+__device__ __forceinline__ void split2(float x, uint32_t& hi, uint32_t& lo) {
+  hi = rne_bf16(x);
+  lo = rne_bf16(x - __uint_as_float(hi << 16));
+}
+__device__ __forceinline__ void put_split(uint16_t* hi, uint16_t* lo, float x) {
+  uint32_t h, l;
+  split2(x, h, l);
+  *hi = static_cast<uint16_t>(h);
+  *lo = static_cast<uint16_t>(l);
+}
+// four consecutive values
+__device__ __forceinline__ void put_split4(uint16_t* hi, uint16_t* lo, float4 x) {
+  uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+  split2(x.x, h0, l0);
+  split2(x.y, h1, l1);
+  split2(x.z, h2, l2);
+  split2(x.w, h3, l3);
+  *reinterpret_cast<uint2*>(hi) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+  *reinterpret_cast<uint2*>(lo) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+}
+
+
 // ---------------------------------------------------------------------------
 // bwd_prep: per (chunk, head).
 template <int D>
@@ -457,8 +504,8 @@ __global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
     for (int u = 31; u >= 0; --u) {
       const int t = 32 * ph + u;
       const float kd = sK[t * LD + ci] * rr;
-      a.Kd[(sh * C + t) * D + ci] = kd;
       x4[u & 3] = kd;
+      a.Kd[(sh * C + t) * D + ci] = kd;
       if ((u & 3) == 0) *reinterpret_cast<float4*>(kdt + u) = make_float4(x4[0], x4[1], x4[2], x4[3]);
       rr *= al[u];
     }
@@ -528,7 +575,9 @@ __global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
   constexpr int NCT = D / 16, NCTP = NCT >= 2 ? NCT / 2 : NCT, NB = NCTP < 4 ? NCTP : 4;
   const int kend = 16 * (w + 1);
 #pragma unroll
-  for (int c0 = hf * NCTP; c0 < hf * NCTP + NCTP && c0 < NCT; c0 += NB) {
+  for (int cc = 0; cc < NCTP; cc += NB) {
+    const int c0 = hf * NCTP + cc;
+    if (c0 >= NCT) break;  // (D = 16: one column tile, first half only)
     f32x4 accW[NB], accU[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) accW[n] = accU[n] = zero4f();
@@ -777,6 +826,322 @@ __global__ void __launch_bounds__(NSC) bwd_fscan(BwdArgs a) {
           sST[col * LD + i] = sG[i] * sST[col * LD + i] + acc[nb][j];
         }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scans with split-bf16 products (bf16 inputs): about 16 bits of precision per
+// product term at 16 times the matrix rate of fp32.  The state itself stays
+// fp32; its split copy is refreshed after each update.
+// acc[n] += A[16 rows][k] * Bt[16 rows + 16 n][k] over k in [k_lo, k_hi), both
+// operands split (hi, lo arrays of bf16 bits, row strides lda, ldb in
+// elements); lane (r, g) feeds k = k0 + 8 g + j of each 32-wide block.
+template <int NB>
+__device__ __forceinline__ void mm3(f32x4 (&acc)[NB], const uint16_t* Ah, const uint16_t* Al, int lda,
+                                    const uint16_t* Bh, const uint16_t* Bl, int ldb, int k_lo, int k_hi) {
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const int ao = r * lda + 8 * g, bo = r * ldb + 8 * g;
+  f32x4 cross[NB];
+#pragma unroll
+  for (int n = 0; n < NB; ++n) cross[n] = zero4f();
+  for (int k0 = k_lo; k0 < k_hi; k0 += 32) {
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(Ah + ao + k0);
+    const bf16x8 al = *reinterpret_cast<const bf16x8*>(Al + ao + k0);
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(Bh + 16 * n * ldb + bo + k0);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(Bl + 16 * n * ldb + bo + k0);
+      acc[n] = mfma_bf(ah, bh, acc[n]);
+      cross[n] = mfma_bf(ah, bl, cross[n]);
+      cross[n] = mfma_bf(al, bh, cross[n]);
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < NB; ++n) acc[n] += cross[n];
+}
+
+// Split layout of the forward scan (bytes): S^T fp32 and split, W rows split,
+// Kd^T rows split, U tile fp32, Delta^T split, b_C.
+template <int D>
+struct ScanLS {
+  using B = ScanL<D>;
+  static constexpr int DVT = B::DVT, LD = B::LD, LV = B::LV;
+  static constexpr int LDH = D + 8, LMH = C + 8;  // bf16 row strides
+  static constexpr size_t SST = 0;
+  static constexpr size_t SSH = SST + sizeof(float) * DVT * LD;
+  static constexpr size_t SSL = SSH + 2 * DVT * LDH;
+  static constexpr size_t SWH = SSL + 2 * DVT * LDH;
+  static constexpr size_t SWL = SWH + 2 * C * LDH;
+  static constexpr size_t SKH = SWL + 2 * C * LDH;
+  static constexpr size_t SKL = SKH + 2 * D * LMH;
+  static constexpr size_t SU = SKL + 2 * D * LMH;
+  static constexpr size_t SXH = SU + sizeof(float) * C * LV;
+  static constexpr size_t SXL = SXH + 2 * DVT * LMH;
+  static constexpr size_t SG = SXL + 2 * DVT * LMH;
+  static constexpr size_t BYTES = SG + sizeof(float) * D;
+};
+
+// Registers of a staged block written split (rows of ld elements).
+template <int ROWS, int COLS, int NTH>
+__device__ __forceinline__ void store_split(const Staged<ROWS, COLS, NTH>& s, uint16_t* hi, uint16_t* lo, int ld) {
+  constexpr int G = COLS / 4;
+#pragma unroll
+  for (int it = 0; it < Staged<ROWS, COLS, NTH>::IT; ++it) {
+    const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
+    if (idx < Staged<ROWS, COLS, NTH>::N) put_split4(hi + t * ld + 4 * g4, lo + t * ld + 4 * g4, s.x[it]);
+  }
+}
+
+// bwd_fscan with split-bf16 products: entry state of every chunk, Delta = U - W S.
+template <int D>
+__global__ void __launch_bounds__(NSC) bwd_fscan3(BwdArgs a) {
+  using P = ScanLS<D>;
+  constexpr int DVT = P::DVT, NBC = DVT / 16, LD = P::LD, LV = P::LV, LDH = P::LDH, LMH = P::LMH;
+  constexpr int LM = ScanL<D>::LM;
+  extern __shared__ __align__(16) unsigned char smb[];
+  float* sST = reinterpret_cast<float*>(smb + P::SST);
+  uint16_t* sSh = reinterpret_cast<uint16_t*>(smb + P::SSH);
+  uint16_t* sSl = reinterpret_cast<uint16_t*>(smb + P::SSL);
+  uint16_t* sWh = reinterpret_cast<uint16_t*>(smb + P::SWH);
+  uint16_t* sWl = reinterpret_cast<uint16_t*>(smb + P::SWL);
+  uint16_t* sKh = reinterpret_cast<uint16_t*>(smb + P::SKH);
+  uint16_t* sKl = reinterpret_cast<uint16_t*>(smb + P::SKL);
+  float* sU = reinterpret_cast<float*>(smb + P::SU);
+  uint16_t* sXh = reinterpret_cast<uint16_t*>(smb + P::SXH);
+  uint16_t* sXl = reinterpret_cast<uint16_t*>(smb + P::SXL);
+  float* sG = reinterpret_cast<float*>(smb + P::SG);
+
+  int unit, tile;
+  scan_block(unit, tile, ScanL<D>::NTILE);
+  if (unit >= a.N * a.H) return;
+  const int n = unit / a.H, h = unit - n * a.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kq = lane >> 4;
+  const int c0 = tile * DVT;
+  int first, nch;
+  unit_chunks(a, n, first, nch);
+
+  tile_from_global<D, DVT, LD, NSC>(
+      sST, a.init_state ? a.init_state + (static_cast<size_t>(n) * a.H + h) * D * D : nullptr, c0);
+  __syncthreads();
+  for (int idx = tid; idx < DVT * D; idx += NSC) {
+    const int col = idx / D, i = idx - col * D;
+    put_split(sSh + col * LDH + i, sSl + col * LDH + i, sST[col * LD + i]);
+  }
+  // W and Kd^T arrive fp32 and are split as they are staged
+  Staged<C, D, NSC> pW;
+  Staged<D, C, NSC> pK;
+  Staged<C, DVT, NSC> pU;
+  Staged<1, D, NSC> pG;
+  auto fetch = [&](int c) {
+    const size_t sh = static_cast<size_t>(first + c) * a.H + h;
+    pW.load(a.Wm + sh * C * D, D, 0);
+    pK.load(a.KdT + sh * D * C, C, 0);
+    pU.load(a.Um + sh * C * D, D, c0);
+    pG.load(a.eg + sh * D, D, 0);
+  };
+  if (nch > 0) fetch(0);
+  for (int c = 0; c < nch; ++c) {
+    const size_t sh = static_cast<size_t>(first + c) * a.H + h;
+    __syncthreads();  // the previous chunk is done with every buffer
+    store_split(pW, sWh, sWl, LDH);
+    store_split(pK, sKh, sKl, LMH);
+    pU.store(sU, LV);
+    pG.store(sG, D);
+    if (c + 1 < nch) fetch(c + 1);
+    tile_to_global<D, DVT, LD, NSC>(a.S_in + sh * D * D, c0, sST);
+    __syncthreads();
+    // Delta = U - W S: wave w, rows [16 (w & 3), +16), columns [16 (w >> 2), +16)
+    if (w < 4 * NBC) {
+      const int I = w & 3, nb = w >> 2;
+      f32x4 acc[1] = {zero4f()};
+      mm3<1>(acc, sWh + 16 * I * LDH, sWl + 16 * I * LDH, LDH, sSh + 16 * nb * LDH, sSl + 16 * nb * LDH, LDH, 0, D);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * I + 4 * kq + j, col = 16 * nb + r;
+        const float dl = sU[t * LV + col] - acc[0][j];
+        put_split(sXh + col * LMH + t, sXl + col * LMH + t, dl);
+        a.Dl[(sh * C + t) * D + c0 + col] = dl;
+      }
+    }
+    __syncthreads();
+    // S = b_C S + Kd^T Delta (fp32 state; its split copy refreshed)
+    for (int ib = w; ib < D / 16; ib += 8) {
+      f32x4 acc[NBC];
+#pragma unroll
+      for (int nb = 0; nb < NBC; ++nb) acc[nb] = zero4f();
+      mm3<NBC>(acc, sKh + 16 * ib * LMH, sKl + 16 * ib * LMH, LMH, sXh, sXl, LMH, 0, C);
+#pragma unroll
+      for (int nb = 0; nb < NBC; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 16 * ib + 4 * kq + j, col = 16 * nb + r;
+          const float v = sG[i] * sST[col * LD + i] + acc[nb][j];
+          sST[col * LD + i] = v;
+          put_split(sSh + col * LDH + i, sSl + col * LDH + i, v);
+        }
+    }
+  }
+  (void)LM;
+}
+
+// Split layout of the reverse scan (bytes): dS^T split (the fp32 dS tile is
+// held in registers), As^T rows, Kd rows, Qs^T rows, W^T rows, dO^T and
+// dDelta^T tiles, all split; b_C.
+template <int D>
+struct ScanLR {
+  static constexpr int DVT = ScanL<D>::DVT;
+  static constexpr int LDH = D + 8, LMH = C + 8;  // bf16 row strides
+  static constexpr size_t SSH = 0;
+  static constexpr size_t SSL = SSH + 2 * DVT * LDH;
+  static constexpr size_t SAH = SSL + 2 * DVT * LDH;
+  static constexpr size_t SAL = SAH + 2 * C * LMH;
+  static constexpr size_t SKH = SAL + 2 * C * LMH;
+  static constexpr size_t SKL = SKH + 2 * C * LDH;
+  static constexpr size_t SQH = SKL + 2 * C * LDH;
+  static constexpr size_t SQL = SQH + 2 * D * LMH;
+  static constexpr size_t SWH = SQL + 2 * D * LMH;
+  static constexpr size_t SWL = SWH + 2 * D * LMH;
+  static constexpr size_t SOH = SWL + 2 * D * LMH;
+  static constexpr size_t SOL = SOH + 2 * DVT * LMH;
+  static constexpr size_t SXH = SOL + 2 * DVT * LMH;
+  static constexpr size_t SXL = SXH + 2 * DVT * LMH;
+  static constexpr size_t SG = SXL + 2 * DVT * LMH;
+  static constexpr size_t BYTES = SG + sizeof(float) * D;
+  static_assert(BYTES <= 160 * 1024, "fits one CU's LDS");
+};
+
+// bwd_rscan with split-bf16 products: backwards over the unit's chunks,
+// dDelta and the exit-state gradient of every chunk, and dS0.  Wave w owns
+// the dS elements (16 w + 4 kq + j, 16 nb + r) of the tile in registers.
+template <int D>
+__global__ void __launch_bounds__(NSC) bwd_rscan3(BwdArgs a) {
+  using P = ScanLR<D>;
+  constexpr int DVT = P::DVT, NBC = DVT / 16, LDH = P::LDH, LMH = P::LMH;
+  extern __shared__ __align__(16) unsigned char smb[];
+  uint16_t* sSh = reinterpret_cast<uint16_t*>(smb + P::SSH);
+  uint16_t* sSl = reinterpret_cast<uint16_t*>(smb + P::SSL);
+  uint16_t* sAh = reinterpret_cast<uint16_t*>(smb + P::SAH);
+  uint16_t* sAl = reinterpret_cast<uint16_t*>(smb + P::SAL);
+  uint16_t* sKh = reinterpret_cast<uint16_t*>(smb + P::SKH);
+  uint16_t* sKl = reinterpret_cast<uint16_t*>(smb + P::SKL);
+  uint16_t* sQh = reinterpret_cast<uint16_t*>(smb + P::SQH);
+  uint16_t* sQl = reinterpret_cast<uint16_t*>(smb + P::SQL);
+  uint16_t* sWh = reinterpret_cast<uint16_t*>(smb + P::SWH);
+  uint16_t* sWl = reinterpret_cast<uint16_t*>(smb + P::SWL);
+  uint16_t* sOh = reinterpret_cast<uint16_t*>(smb + P::SOH);
+  uint16_t* sOl = reinterpret_cast<uint16_t*>(smb + P::SOL);
+  uint16_t* sXh = reinterpret_cast<uint16_t*>(smb + P::SXH);
+  uint16_t* sXl = reinterpret_cast<uint16_t*>(smb + P::SXL);
+  float* sG = reinterpret_cast<float*>(smb + P::SG);
+
+  int unit, tile;
+  scan_block(unit, tile, ScanL<D>::NTILE);
+  if (unit >= a.N * a.H) return;
+  const int n = unit / a.H, h = unit - n * a.H;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, kq = lane >> 4;
+  const int c0 = tile * DVT;
+  int first, nch;
+  unit_chunks(a, n, first, nch);
+  const size_t uo = (static_cast<size_t>(n) * a.H + h) * D * D;
+  const bool owner = w < D / 16;  // this wave holds rows [16 w, 16 w + 16) of dS
+
+  // dS tile in registers: ds[nb][j] = dS[16 w + 4 kq + j][c0 + 16 nb + r]
+  float ds[NBC][4];
+#pragma unroll
+  for (int nb = 0; nb < NBC; ++nb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = 16 * w + 4 * kq + j, col = 16 * nb + r;
+      ds[nb][j] = (owner && a.d_final) ? a.d_final[uo + static_cast<size_t>(i) * D + c0 + col] : 0.f;
+      if (owner) put_split(sSh + col * LDH + i, sSl + col * LDH + i, ds[nb][j]);
+    }
+  // the operands arrive fp32 and are split as they are staged
+  Staged<C, C, NSC> pA;
+  Staged<C, D, NSC> pK;
+  Staged<D, C, NSC> pQ;
+  Staged<D, C, NSC> pW;
+  Staged<C, DVT, NSC> pO;
+  Staged<1, D, NSC> pG;
+  auto fetch = [&](int c) {
+    const int slot = first + c;
+    const size_t sh = static_cast<size_t>(slot) * a.H + h;
+    Loc L;
+    locate(a, slot, L);
+    pA.load(a.AsT + sh * C * C, C, 0);
+    pK.load(a.Kd + sh * C * D, D, 0);
+    pQ.load(a.QsT + sh * D * C, C, 0);
+    pW.load(a.WT + sh * D * C, C, 0);
+    pO.load_tokens(a.d_out, L.tok0, a.H, h, D, c0, L.count);
+    pG.load(a.eg + sh * D, D, 0);
+  };
+  if (nch > 0) fetch(nch - 1);
+  for (int c = nch - 1; c >= 0; --c) {
+    const size_t sh = static_cast<size_t>(first + c) * a.H + h;
+    __syncthreads();
+    store_split(pA, sAh, sAl, LMH);
+    store_split(pK, sKh, sKl, LDH);
+    store_split(pQ, sQh, sQl, LMH);
+    store_split(pW, sWh, sWl, LMH);
+    {  // dO^T tile, split
+      constexpr int G = DVT / 4;
+#pragma unroll
+      for (int it = 0; it < decltype(pO)::IT; ++it) {
+        const int idx = it * NSC + tid, t = idx / G, cc = 4 * (idx - t * G);
+        if (idx >= decltype(pO)::N) continue;
+        put_split(sOh + (cc + 0) * LMH + t, sOl + (cc + 0) * LMH + t, pO.x[it].x);
+        put_split(sOh + (cc + 1) * LMH + t, sOl + (cc + 1) * LMH + t, pO.x[it].y);
+        put_split(sOh + (cc + 2) * LMH + t, sOl + (cc + 2) * LMH + t, pO.x[it].z);
+        put_split(sOh + (cc + 3) * LMH + t, sOl + (cc + 3) * LMH + t, pO.x[it].w);
+      }
+    }
+    pG.store(sG, D);
+    if (c > 0) fetch(c - 1);
+    // the exit-state gradient of chunk c
+    if (owner) {
+#pragma unroll
+      for (int nb = 0; nb < NBC; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          a.dSo[sh * D * D + static_cast<size_t>(16 * w + 4 * kq + j) * D + c0 + 16 * nb + r] = ds[nb][j];
+    }
+    __syncthreads();
+    // dDelta = As^T dO + Kd dS: wave w, rows [16 (w & 3), +16), columns [16 (w >> 2), +16)
+    if (w < 4 * NBC) {
+      const int I = w & 3, nb = w >> 2;
+      f32x4 acc[1] = {zero4f()};
+      mm3<1>(acc, sAh + 16 * I * LMH, sAl + 16 * I * LMH, LMH, sOh + 16 * nb * LMH, sOl + 16 * nb * LMH, LMH, 0, C);
+      mm3<1>(acc, sKh + 16 * I * LDH, sKl + 16 * I * LDH, LDH, sSh + 16 * nb * LDH, sSl + 16 * nb * LDH, LDH, 0, D);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = 16 * I + 4 * kq + j, col = 16 * nb + r;
+        put_split(sXh + col * LMH + t, sXl + col * LMH + t, acc[0][j]);
+        a.dDl[(sh * C + t) * D + c0 + col] = acc[0][j];
+      }
+    }
+    __syncthreads();
+    // dS = b_C dS + Qs^T dO - W^T dDelta (fp32 in registers; split copy refreshed)
+    if (owner) {
+      f32x4 acc[NBC], neg[NBC];
+#pragma unroll
+      for (int nb = 0; nb < NBC; ++nb) acc[nb] = neg[nb] = zero4f();
+      mm3<NBC>(acc, sQh + 16 * w * LMH, sQl + 16 * w * LMH, LMH, sOh, sOl, LMH, 0, C);
+      mm3<NBC>(neg, sWh + 16 * w * LMH, sWl + 16 * w * LMH, LMH, sXh, sXl, LMH, 0, C);
+#pragma unroll
+      for (int nb = 0; nb < NBC; ++nb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 16 * w + 4 * kq + j, col = 16 * nb + r;
+          ds[nb][j] = sG[i] * ds[nb][j] + acc[nb][j] - neg[nb][j];
+          put_split(sSh + col * LDH + i, sSl + col * LDH + i, ds[nb][j]);
+        }
+    }
+  }
+  if (a.d_init && owner) {
+#pragma unroll
+    for (int nb = 0; nb < NBC; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        a.d_init[uo + static_cast<size_t>(16 * w + 4 * kq + j) * D + c0 + 16 * nb + r] = ds[nb][j];
   }
 }
 
@@ -1667,6 +2032,14 @@ hipError_t set_lds_d() {
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_fscan<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(sizeof(float) * ScanL<D>::F_FLOATS));
   if (e != hipSuccess) return e;
+  if constexpr (split_scans<D, In>()) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_fscan3<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(ScanLS<D>::BYTES));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_rscan3<D>), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(ScanLR<D>::BYTES));
+    if (e != hipSuccess) return e;
+  }
   return hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_rscan<D>),
                              hipFuncAttributeMaxDynamicSharedMemorySize,
                              static_cast<int>(sizeof(float) * ScanL<D>::R_FLOATS));
@@ -1703,9 +2076,15 @@ hipError_t run_bwd(const BwdArgs& a, int64_t ns, hipStream_t stream) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (unit_blocks > 0) {
-    hipLaunchKernelGGL((bwd_fscan<D>), dim3(unit_blocks), dim3(NSC), sizeof(float) * ScanL<D>::F_FLOATS, stream, a);
+    if constexpr (split_scans<D, In>())
+      hipLaunchKernelGGL((bwd_fscan3<D>), dim3(unit_blocks), dim3(NSC), ScanLS<D>::BYTES, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_fscan<D>), dim3(unit_blocks), dim3(NSC), sizeof(float) * ScanL<D>::F_FLOATS, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_rscan<D>), dim3(unit_blocks), dim3(NSC), sizeof(float) * ScanL<D>::R_FLOATS, stream, a);
+    if constexpr (split_scans<D, In>())
+      hipLaunchKernelGGL((bwd_rscan3<D>), dim3(unit_blocks), dim3(NSC), ScanLR<D>::BYTES, stream, a);
+    else
+      hipLaunchKernelGGL((bwd_rscan<D>), dim3(unit_blocks), dim3(NSC), sizeof(float) * ScanL<D>::R_FLOATS, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (chunk_blocks > 0) {

@@ -171,7 +171,6 @@ __global__ void __launch_bounds__(NT, 1) chunk_kernel(ChunkArgs p) {
   }
   const int nch = (ntok + C - 1) / C;
   const size_t unit_state = (static_cast<size_t>(doc) * H + h) * D * D;
-  const size_t row_stride = static_cast<size_t>(H) * D;  // elements between tokens
 
   const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
