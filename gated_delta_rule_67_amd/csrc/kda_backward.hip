@@ -892,6 +892,50 @@ __device__ __forceinline__ void store_split(const Staged<ROWS, COLS, NTH>& s, ui
   }
 }
 
+// Row-major LDS operands of bwd_gstate, fp32 rows (SP = false) or split rows
+// (SP = true): a row of K values holds its K hi bf16 then its K lo bf16 in
+// the same row stride (K + 4 floats), so either layout fits the same region.
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+template <bool SP>
+__device__ __forceinline__ float ld_el(const float* base, int row, int ld, int K, int col) {
+  if constexpr (SP) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(base) + 2 * row * ld;
+    return bf2f(p[col]) + bf2f(p[K + col]);
+  } else {
+    return base[row * ld + col];
+  }
+}
+template <bool SP>
+__device__ __forceinline__ void st_el(float* base, int row, int ld, int K, int col, float v) {
+  if constexpr (SP) {
+    uint16_t* p = reinterpret_cast<uint16_t*>(base) + 2 * row * ld;
+    put_split(p + col, p + K + col, v);
+  } else {
+    base[row * ld + col] = v;
+  }
+}
+// acc[n] += A rows x Bt rows over k in [k_lo, k_hi) (rows of K values, strides in floats)
+template <bool SP, int NB>
+__device__ __forceinline__ void mm_any(f32x4 (&acc)[NB], const float* A, int lda, const float* Bt, int ldb, int K,
+                                       int k_lo, int k_hi) {
+  if constexpr (SP) {
+    const uint16_t* a16 = reinterpret_cast<const uint16_t*>(A);
+    const uint16_t* b16 = reinterpret_cast<const uint16_t*>(Bt);
+    mm3<NB>(acc, a16, a16 + K, 2 * lda, b16, b16 + K, 2 * ldb, k_lo, k_hi);
+  } else {
+    mm_kc<NB>(acc, A, lda, Bt, ldb, k_lo, k_hi);
+  }
+}
+template <bool SP, int ROWS, int COLS, int NTH>
+__device__ __forceinline__ void stage_store(const Staged<ROWS, COLS, NTH>& st, float* dst, int ld) {
+  if constexpr (SP) {
+    uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+    store_split(st, d16, d16 + COLS, 2 * ld);
+  } else {
+    st.store(dst, ld);
+  }
+}
 // bwd_fscan with split-bf16 products: entry state of every chunk, Delta = U - W S.
 template <int D>
 __global__ void __launch_bounds__(NSC) bwd_fscan3(BwdArgs a) {
@@ -1287,6 +1331,29 @@ __device__ __forceinline__ void load_mat_t(float* dst, const float* src) {
   }
 }
 
+// A dense ROWS x COLS fp32 matrix transposed into LDS rows of ROWS values
+// (dst row c = column c of src), fp32 or split.
+template <bool SP, int ROWS, int COLS, int LDT, int NTH>
+__device__ __forceinline__ void load_mat_t_any(float* dst, const float* src) {
+  if constexpr (SP) {
+    constexpr int G = COLS / 4, N = ROWS * G, IT = (N + NTH - 1) / NTH;
+    float4 x[IT];
+#pragma unroll
+    for (int it = 0; it < IT; ++it) x[it] = load4(src + min(it * NTH + static_cast<int>(threadIdx.x), N - 1) * 4);
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int idx = it * NTH + threadIdx.x, rr = idx / G, c = 4 * (idx - rr * G);
+      if (idx >= N) continue;
+      st_el<true>(dst, c + 0, LDT, ROWS, rr, x[it].x);
+      st_el<true>(dst, c + 1, LDT, ROWS, rr, x[it].y);
+      st_el<true>(dst, c + 2, LDT, ROWS, rr, x[it].z);
+      st_el<true>(dst, c + 3, LDT, ROWS, rr, x[it].w);
+    }
+  } else {
+    load_mat_t<ROWS, COLS, LDT, NTH>(dst, src);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // bwd_gstate: per (chunk, head).  Wave w owns rows [16w, 16w + 16) of every
 // C x D result.
@@ -1316,6 +1383,9 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
   constexpr int LD = P::LD, LM = P::LM, NCT = D / 16;
   // wave wv: token block w = wv & 3, channel tiles [ctb, ctb + NCTH)
   constexpr int NCTH = NCT >= 2 ? NCT / 2 : 1, NB = NCTH < 4 ? NCTH : 4;
+  // bf16 inputs: the product operands (T^T, dDelta^T, dR, S, dO, Delta, dS')
+  // are held split in LDS, rows of the same stride
+  constexpr bool SP = split_scans<D, In>();
   extern __shared__ __align__(16) float sm[];
   float* sS = sm + P::RS;
   float* sX = sm + P::RX;
@@ -1346,8 +1416,8 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
     sBeta[tid] = tid < L.count ? bv : 0.f;
   }
   if (tid < 2 * C) sDb[tid] = 0.f;
-  load_mat_t<C, C, LM, NTS>(sT, a.Tm + sh * C * C);   // T^T
-  load_mat_t<C, D, LM, NTS>(sX, a.dDl + sh * C * D);  // dDelta^T
+  load_mat_t_any<SP, C, C, LM, NTS>(sT, a.Tm + sh * C * C);   // T^T
+  load_mat_t_any<SP, C, D, LM, NTS>(sX, a.dDl + sh * C * D);  // dDelta^T
   load_rows<D, LD, float, NTS>(sR, a.log_g, L.tok0, L.count, H, h);  // log_g rows (0 past the end)
   __syncthreads();
   // the entry state and dO are loaded now and written to LDS after dR
@@ -1389,20 +1459,20 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
       f32x4 acc[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n) acc[n] = zero4f();
-      mm_kc<NB>(acc, sT + 16 * w * LM, LM, sX + 16 * (ctb + c0) * LM, LM, 16 * w, C);
+      mm_any<SP, NB>(acc, sT + 16 * w * LM, LM, sX + 16 * (ctb + c0) * LM, LM, C, SP ? 32 * (w >> 1) : 16 * w, C);
 #pragma unroll
       for (int n = 0; n < NB; ++n)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + c0 + n) + r;
-          sR[t * LD + i] = acc[n][j];
+          st_el<SP>(sR, t, LD, D, i, acc[n][j]);
           if (t < L.count) a.dv[row(t) * D + i] = sBeta[t] * acc[n][j];
         }
     }
   }
-  stS.store(sS, LD);
+  stage_store<SP>(stS, sS, LD);
   __syncthreads();  // dR and S in place; dDelta^T no longer needed
-  stO.store(sX, LD);  // dO
+  stage_store<SP>(stO, sX, LD);  // dO
   Staged<D, D, NTS> stD;  // dS', for the row sums against S
   stD.load_all(a.dSo + sh * D * D, D, 0);
   float dq_[NCTH][4], dk_[NCTH][4], dg_[NCTH][4];
@@ -1415,7 +1485,7 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
       f32x4 acc[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n) acc[n] = zero4f();
-      mm_kc<NB>(acc, sR + 16 * w * LD, LD, sS + 16 * (ctb + c0) * LD, LD, 0, D);
+      mm_any<SP, NB>(acc, sR + 16 * w * LD, LD, sS + 16 * (ctb + c0) * LD, LD, D, 0, D);
 #pragma unroll
       for (int n = 0; n < NB; ++n)
 #pragma unroll
@@ -1424,7 +1494,7 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
           const float kb = kv[c][j] * bb[c][j];
           const float vx = to_f32(v[row(min(t, L.count - 1)) * D + i]);
           const float vv = t < L.count ? vx : 0.f;
-          dbr[j] += sR[t * LD + i] * vv - kb * acc[n][j];
+          dbr[j] += ld_el<SP>(sR, t, LD, D, i) * vv - kb * acc[n][j];
           const float dkb = -sBeta[t] * acc[n][j];
           dk_[c][j] = dkb * bb[c][j];
           dg_[c][j] = dkb * kb;
@@ -1441,7 +1511,7 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
       f32x4 acc[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n) acc[n] = zero4f();
-      mm_kc<NB>(acc, sX + 16 * w * LD, LD, sS + 16 * (ctb + c0) * LD, LD, 0, D);
+      mm_any<SP, NB>(acc, sX + 16 * w * LD, LD, sS + 16 * (ctb + c0) * LD, LD, D, 0, D);
 #pragma unroll
       for (int n = 0; n < NB; ++n)
 #pragma unroll
@@ -1464,16 +1534,16 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
     for (int it = 0; it < IT; ++it) {
       const int idx = it * NTS + tid, i = idx / G, jj = 4 * (idx - i * G);
       if (idx >= N) continue;  // whole waves
-      const float* sr = sS + i * LD + jj;
       const float4 xd = stD.x[it];
-      float acc = xd.x * sr[0] + xd.y * sr[1] + xd.z * sr[2] + xd.w * sr[3];
+      float acc = xd.x * ld_el<SP>(sS, i, LD, D, jj) + xd.y * ld_el<SP>(sS, i, LD, D, jj + 1) +
+                  xd.z * ld_el<SP>(sS, i, LD, D, jj + 2) + xd.w * ld_el<SP>(sS, i, LD, D, jj + 3);
 #pragma unroll
       for (int o = 1; o < G; o <<= 1) acc += __shfl_xor(acc, o, 64);
       if ((tid & (G - 1)) == 0) sGam[i] = sEg[i] * acc;
     }
   }
   __syncthreads();  // done with S
-  stL.store(sS, LD);  // Delta, rows
+  stage_store<SP>(stL, sS, LD);  // Delta, rows
   __syncthreads();
   stD.load_all(a.dSo + sh * D * D, D, 0);  // dS' again (L2), for Z
   // dAqk = scale tril(dO Delta^T), dA = -tril(dR Delta^T, -1); this wave's
@@ -1487,8 +1557,8 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
       for (int j = 0; j < 4; ++j) akk[n][j] = a.Ab[sh * C * C + (16 * w + 4 * kq + j) * C + 16 * (2 * half + n) + r];
 #pragma unroll
     for (int n = 0; n < 2; ++n) aq[n] = aa[n] = zero4f();
-    mm_kc<2>(aq, sX + 16 * w * LD, LD, sS + 32 * half * LD, LD, 0, D);
-    mm_kc<2>(aa, sR + 16 * w * LD, LD, sS + 32 * half * LD, LD, 0, D);
+    mm_any<SP, 2>(aq, sX + 16 * w * LD, LD, sS + 32 * half * LD, LD, D, 0, D);
+    mm_any<SP, 2>(aa, sR + 16 * w * LD, LD, sS + 32 * half * LD, LD, D, 0, D);
 #pragma unroll
     for (int n = 0; n < 2; ++n)
 #pragma unroll
@@ -1513,7 +1583,7 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
   }
   __syncthreads();  // done with dO (sX) and dR (sR); Delta rows stay in sS
   static_assert(D * LD <= P::MID + C * LD, "dS' fits over the dO and dR regions");
-  stD.store(sX, LD);  // dS'
+  stage_store<SP>(stD, sX, LD);  // dS'
   __syncthreads();
   // Z = Delta dS'^T: dKd = Z
   float colp[NCTH];
@@ -1523,7 +1593,7 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
       f32x4 acc[NB];
 #pragma unroll
       for (int n = 0; n < NB; ++n) acc[n] = zero4f();
-      mm_kc<NB>(acc, sS + 16 * w * LD, LD, sX + 16 * (ctb + c0) * LD, LD, 0, D);
+      mm_any<SP, NB>(acc, sS + 16 * w * LD, LD, sX + 16 * (ctb + c0) * LD, LD, D, 0, D);
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         const int c = c0 + n;
