@@ -55,9 +55,12 @@ def check(tag, got, ref, tol):
     return worst
 
 
+# bf16 d >= 32 runs the scans and the state-side kernel on split-bf16
+# products, bf16 d = 16 and every fp32 case on fp32 products
 @pytest.mark.parametrize("dtype,d,B,T,H", [("f32", 32, 2, 150, 2), ("bf16", 128, 2, 200, 2),
                                             ("f32", 16, 1, 64, 3), ("f32", 64, 1, 129, 2),
-                                            ("f32", 128, 1, 70, 1)])
+                                            ("f32", 128, 1, 70, 1), ("bf16", 32, 1, 100, 2),
+                                            ("bf16", 16, 1, 70, 2)])
 def test_dense_ragged(dtype, d, B, T, H):
     inp = kda_inputs.make_inputs(B=B, T=T, H=H, dk=d, dv=d, dtype=dtype, seed=100 + d + T,
                                  init="normal", init_std=0.05)
@@ -84,12 +87,13 @@ def test_no_initial_state_and_no_final_gradient():
     check("zeros", gpu_bwd(inp, up, init=False), oracle_bwd(inp, up, init=False), TOL["f32"])
 
 
-@pytest.mark.parametrize("mode", ["uniform", "erase"])
-def test_extreme_gates(mode):
+@pytest.mark.parametrize("mode,dtype,d", [("uniform", "f32", 32), ("erase", "f32", 32), ("uniform", "bf16", 64),
+                                          ("erase", "bf16", 64)])
+def test_extreme_gates(mode, dtype, d):
     """Gates uniform in [-20, 0], and every fifth token erasing the state
     (log_g = -inf): no factor of the chunk form may overflow or lose the
-    gradient of the tokens it separates."""
-    inp = kda_inputs.make_inputs(B=1, T=160, H=2, dk=32, dv=32, dtype="f32", seed=130, init="normal",
+    gradient of the tokens it separates (bf16 d = 64: the split products)."""
+    inp = kda_inputs.make_inputs(B=1, T=160, H=2, dk=d, dv=d, dtype=dtype, seed=130, init="normal",
                                  init_std=0.1)
     rng = np.random.default_rng(131)
     g = rng.uniform(-20.0, 0.0, inp["log_g"].shape).astype(np.float32)
@@ -99,7 +103,7 @@ def test_extreme_gates(mode):
     inp["log_g"] = torch.from_numpy(g)
     up = kda_inputs.upstream_grads(inp, seed=230)
     got, ref = gpu_bwd(inp, up), oracle_bwd(inp, up)
-    check(f"gates {mode}", got, ref, TOL["f32"])
+    check(f"gates {mode} {dtype} d={d}", got, ref, TOL[dtype])
 
 
 def test_full_size_dense_workload_sampled_units():
