@@ -47,6 +47,7 @@
 //                 dq, dk and dG (staged in the dq, dk, dlog_g outputs)
 //   bwd_gpairs    per chunk: the pair terms, then dlog_g = reverse cumsum(dG)
 #include <algorithm>
+#include <type_traits>
 
 #include "kda_common.h"
 #include "kda_launch.h"
@@ -278,6 +279,8 @@ __device__ __forceinline__ bool at_level(int l, int t, int s) {
 }
 
 __device__ __forceinline__ f32x4 zero4f() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ float ld1f(const float* p) { return *p; }
+__device__ __forceinline__ float ld1f(const bf16_t* p) { return to_f32(*p); }
 
 // Split-bf16 operands (bf16 inputs).  An fp32 value x is held as hi + lo, two
 // bf16 values (round to nearest even twice: |x - hi - lo| <= 2^-16 |x|), and a
@@ -323,34 +326,68 @@ __device__ __forceinline__ void put_split4(uint16_t* hi, uint16_t* lo, float4 x)
 
 // ---------------------------------------------------------------------------
 // bwd_prep: per (chunk, head).
-template <int D>
+template <typename In>
+constexpr int prep_threads() {
+  return sizeof(In) == 2 ? 256 : 512;
+}
+
+template <int D, typename In>
 struct PrepL {
+  // bf16 inputs: K, Q and V^T stay bf16 in LDS and the regions overlap more
+  // ((K*b)^T over K and Q, V^T over Akk, T over Aqk): about 75 KB for d = 128,
+  // two 4-wave workgroups per CU, so one's load and store phases overlap the
+  // other's products.  fp32 inputs: fp32 rows, one 8-wave workgroup per CU.
+  static constexpr bool COMPACT = sizeof(In) == 2;
+  static constexpr int NTH = prep_threads<In>();
   static constexpr int LD = D + 4, LM = C + 4;
-  static constexpr int CD = C * LD, CM = C * LM, XT = (CD > D * LM ? CD : D * LM);
-  static constexpr int R0 = 0;                          // K rows, later V^T
-  static constexpr int R1 = R0 + XT;                    // Q rows, later (K*b)^T
-  static constexpr int R2 = R1 + XT;                    // F, later Akk | Aqk
-  static constexpr int R3 = R2 + (CD > 2 * CM ? CD : 2 * CM);  // T
-  static constexpr int R4 = R3 + CM;                    // 4 x 16 x 17 wave scratch
+  static constexpr int LDK = COMPACT ? D + 8 : D + 4;  // K, Q row stride (elements)
+  static constexpr int LMV = C + 4;                     // V^T row stride (elements)
+  static constexpr int CD = C * LD, CM = C * LM;
+  static constexpr int KQF = COMPACT ? C * LDK / 2 : (CD > D * LM ? CD : D * LM);  // floats per K or Q region
+  static constexpr int R0 = 0;                          // K rows (fp32 layout: later V^T)
+  static constexpr int R1 = R0 + KQF;                   // Q rows (fp32 layout: later (K*b)^T)
+  static constexpr int R2 = R1 + KQF;                   // F, later Akk | Aqk
+  static constexpr int R3 = R2 + (CD > 2 * CM ? CD : 2 * CM);  // T (fp32 layout)
+  static constexpr int R4 = R3 + (COMPACT ? 0 : CM);    // 4 x 16 x 17 wave scratch
   static constexpr int RB = R4 + 4 * 16 * 17;           // beta [C]
   static constexpr int RT = RB + C;                     // block totals [2][D]
   static constexpr int FLOATS = RT + 2 * D;
   static constexpr size_t BYTES = sizeof(float) * FLOATS;
+  static_assert(!COMPACT || 2 * KQF >= D * LM, "(K*b)^T fits over K and Q");
+  static_assert(!COMPACT || D * LMV / 2 <= CM, "V^T fits over Akk");
 };
 
-constexpr int NTP = 512;  // bwd_prep threads: 8 waves, two per 16-token block
+// C rows of a [tokens, H, D] bf16 tensor copied into LDS as bf16 (row stride
+// LDK), rows >= count zero.
+template <int D, int LDK, int NTH>
+__device__ __forceinline__ void load_rows_raw(bf16_t* dst, const bf16_t* src, int64_t tok0, int count, int H, int h) {
+  constexpr int G = D / 4, N = C * G, IT = (N + NTH - 1) / NTH;
+  uint2 x[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
+    const uint2 y = *reinterpret_cast<const uint2*>(src + ((tok0 + min(t, count - 1)) * H + h) * D + 4 * g4);
+    x[it] = t < count ? y : make_uint2(0u, 0u);
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int idx = it * NTH + threadIdx.x, t = idx / G, g4 = idx - t * G;
+    if (idx < N) *reinterpret_cast<uint2*>(dst + t * LDK + 4 * g4) = x[it];
+  }
+}
 
 template <int D, typename In>
-__global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
-  using P = PrepL<D>;
-  constexpr int LD = P::LD, LM = P::LM;
+__global__ void __launch_bounds__(prep_threads<In>()) bwd_prep(BwdArgs a) {
+  using P = PrepL<D, In>;
+  constexpr int LD = P::LD, LM = P::LM, LDK = P::LDK, NTH = P::NTH;
+  using KQ = std::conditional_t<P::COMPACT, In, float>;  // element type of K, Q, V^T in LDS
   extern __shared__ __align__(16) float sm[];
-  float* sK = sm + P::R0;
-  float* sQ = sm + P::R1;
+  KQ* sK = reinterpret_cast<KQ*>(sm + P::R0);
+  KQ* sQ = reinterpret_cast<KQ*>(sm + P::R1);
   float* sF = sm + P::R2;
   float* sAb = sm + P::R2;
   float* sAq = sm + P::R2 + P::CM;
-  float* sT = sm + P::R3;
+  float* sT = P::COMPACT ? sAq : sm + P::R3;
   float* sBeta = sm + P::RB;
   float* sTot = sm + P::RT;
 
@@ -360,15 +397,20 @@ __global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
   // wave wv: 16-token block w, and half hf of the channels (pair tiles) or of
   // the column tiles (W, U)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, w = wv & 3, hf = wv >> 2, r = lane & 15, kq = lane >> 4;
-  constexpr int KH = D >= 32 ? D / 2 : D;  // channels per half
+  constexpr int KH = (NTH == 512 && D >= 32) ? D / 2 : D;  // channels per half
   const bool khalf = hf * KH < D;
   const size_t sh = static_cast<size_t>(slot) * a.H + h;
   const In* q = static_cast<const In*>(a.q);
   const In* k = static_cast<const In*>(a.k);
   const In* v = static_cast<const In*>(a.v);
 
-  load_rows<D, LD, In, NTP>(sK, k, L.tok0, L.count, a.H, h);
-  load_rows<D, LD, In, NTP>(sQ, q, L.tok0, L.count, a.H, h);
+  if constexpr (P::COMPACT) {
+    load_rows_raw<D, LDK, NTH>(sK, k, L.tok0, L.count, a.H, h);
+    load_rows_raw<D, LDK, NTH>(sQ, q, L.tok0, L.count, a.H, h);
+  } else {
+    load_rows<D, LD, In, NTH>(sK, k, L.tok0, L.count, a.H, h);
+    load_rows<D, LD, In, NTH>(sQ, q, L.tok0, L.count, a.H, h);
+  }
   if (tid < C) {
     const float bv = a.beta[(L.tok0 + min(tid, L.count - 1)) * a.H + h];
     sBeta[tid] = tid < L.count ? bv : 0.f;
@@ -384,12 +426,13 @@ __global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
   // (k = k0 + 4 kq + m for the m-th MFMA, the same order on both sides)
   auto pair_tile = [&](int I, int J, f32x4& accK, f32x4& accQ) {
     const int tt = (16 * I + r) * LD + 4 * kq, ts = (16 * J + r) * LD + 4 * kq;
+    const int ttk = (16 * I + r) * LDK + 4 * kq, tsk = (16 * J + r) * LDK + 4 * kq;
     for (int k0 = hf * KH; k0 < hf * KH + KH; k0 += 16) {
       const float4 ft = *reinterpret_cast<const float4*>(sF + tt + k0);
-      const float4 kt = *reinterpret_cast<const float4*>(sK + tt + k0);
-      const float4 qt = *reinterpret_cast<const float4*>(sQ + tt + k0);
+      const float4 kt = load4(sK + ttk + k0);
+      const float4 qt = load4(sQ + ttk + k0);
       const float4 fs = *reinterpret_cast<const float4*>(sF + ts + k0);
-      const float4 ks = *reinterpret_cast<const float4*>(sK + ts + k0);
+      const float4 ks = load4(sK + tsk + k0);
       accK = mma(kt.x * ft.x, ks.x * fs.x, accK);
       accQ = mma(qt.x * ft.x, ks.x * fs.x, accQ);
       accK = mma(kt.y * ft.y, ks.y * fs.y, accK);
@@ -433,10 +476,10 @@ __global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
   // diagonal of Aqk: r(t, t) = 1
   if (khalf) {
     f32x4 tq = zero4f();
-    const int tt = (16 * w + r) * LD + 4 * kq;
+    const int tt = (16 * w + r) * LDK + 4 * kq;
     for (int k0 = hf * KH; k0 < hf * KH + KH; k0 += 16) {
-      const float4 qt = *reinterpret_cast<const float4*>(sQ + tt + k0);
-      const float4 kt = *reinterpret_cast<const float4*>(sK + tt + k0);
+      const float4 qt = load4(sQ + tt + k0);
+      const float4 kt = load4(sK + tt + k0);
       tq = mma(qt.x, kt.x, tq);
       tq = mma(qt.y, kt.y, tq);
       tq = mma(qt.z, kt.z, tq);
@@ -446,7 +489,7 @@ __global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
     for (int j = 0; j < 4; ++j) aq_d[j] += (4 * kq + j == r) ? tq[j] : 0.f;
   }
   __syncthreads();  // everyone done with sF
-  for (int idx = tid; idx < 2 * P::CM; idx += NTP) sAb[idx] = 0.f;
+  for (int idx = tid; idx < 2 * P::CM; idx += NTH) sAb[idx] = 0.f;
   __syncthreads();
   // the two channel halves of every tile: the first half's waves store, the
   // second half's add
@@ -475,7 +518,7 @@ __global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
   }
   __syncthreads();
   // Akk and (scale * Aqk)^T to the workspace
-  for (int idx = tid; idx < C * C; idx += NTP) {
+  for (int idx = tid; idx < C * C; idx += NTH) {
     const int t = idx / C, s = idx - t * C;
     a.Ab[sh * C * C + idx] = sAb[t * LM + s];
     a.AsT[sh * C * C + idx] = a.scale * sAq[s * LM + t];
@@ -492,10 +535,10 @@ __global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
     for (int u = 0; u < 32; ++u) {
       const int t = 32 * ph + u;
       b *= al[u];
-      const float qv = sQ[t * LD + ci];
+      const float qv = ld1f(sQ + t * LDK + ci);
       x4[u & 3] = a.scale * qv * b;
       if ((u & 3) == 3) *reinterpret_cast<float4*>(qst + u - 3) = make_float4(x4[0], x4[1], x4[2], x4[3]);
-      kb[u] = sK[t * LD + ci] * b;
+      kb[u] = ld1f(sK + t * LDK + ci) * b;
     }
     if (ph == 1) a.eg[sh * D + ci] = b;
     float rr = ph == 0 ? sTot[D + ci] : 1.f;
@@ -503,23 +546,37 @@ __global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
 #pragma unroll
     for (int u = 31; u >= 0; --u) {
       const int t = 32 * ph + u;
-      const float kd = sK[t * LD + ci] * rr;
+      const float kd = ld1f(sK + t * LDK + ci) * rr;
       x4[u & 3] = kd;
       a.Kd[(sh * C + t) * D + ci] = kd;
       if ((u & 3) == 0) *reinterpret_cast<float4*>(kdt + u) = make_float4(x4[0], x4[1], x4[2], x4[3]);
       rr *= al[u];
     }
   }
-  for (int idx = tid; idx < P::CM; idx += NTP) sT[idx] = 0.f;
+  if constexpr (P::COMPACT) __syncthreads();  // T lies over Aqk: the (scale Aqk)^T writes are done
+  for (int idx = tid; idx < P::CM; idx += NTH) sT[idx] = 0.f;
   __syncthreads();  // K and Q no longer needed; T zeroed
-  float* sKbT = sQ;  // (K*b)^T [i][t]
-  float* sVT = sK;   // V^T [i][t]
+  float* sKbT = P::COMPACT ? sm + P::R0 : reinterpret_cast<float*>(sQ);  // (K*b)^T [i][t]
+  KQ* sVT = P::COMPACT ? reinterpret_cast<KQ*>(sAb) : sK;                // V^T [i][t]
   if (chan) {
 #pragma unroll
     for (int u = 0; u < 32; u += 4)
       *reinterpret_cast<float4*>(sKbT + ci * LM + 32 * ph + u) = make_float4(kb[u], kb[u + 1], kb[u + 2], kb[u + 3]);
   }
-  load_rows_t<D, LM, In, NTP>(sVT, v, L.tok0, L.count, a.H, h);
+  // V^T: the fp32 layout stages it now; the compact one loads V into
+  // registers and writes it over Akk once the solve below is done with Akk
+  constexpr int VG = D / 4, VN = C * VG, VIT = (VN + NTH - 1) / NTH;
+  uint2 vx[P::COMPACT ? VIT : 1];
+  if constexpr (P::COMPACT) {
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int idx = it * NTH + tid, t = idx / VG, g4 = idx - t * VG;
+      const uint2 y = *reinterpret_cast<const uint2*>(v + ((L.tok0 + min(t, L.count - 1)) * a.H + h) * D + 4 * g4);
+      vx[it] = t < L.count ? y : make_uint2(0u, 0u);
+    }
+  } else {
+    load_rows_t<D, LM, In, NTH>(sVT, v, L.tok0, L.count, a.H, h);
+  }
   // T = (I + diag(beta) Akk)^-1: diagonal 16 x 16 blocks by forward substitution
   if (tid < 64) {
     const int I = tid >> 4, c = tid & 15;
@@ -566,13 +623,26 @@ __global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < C * C; idx += NTP) {
+  for (int idx = tid; idx < C * C; idx += NTH) {
     const int t = idx / C, s = idx - t * C;
     a.Tm[sh * C * C + idx] = sT[t * LM + s];
   }
+  if constexpr (P::COMPACT) {  // V^T over Akk (the solve is done with it)
+    uint16_t* vt = reinterpret_cast<uint16_t*>(sVT);
+#pragma unroll
+    for (int it = 0; it < VIT; ++it) {
+      const int idx = it * NTH + tid, t = idx / VG, c = 4 * (idx - t * VG);
+      if (idx >= VN) continue;
+      vt[(c + 0) * P::LMV + t] = static_cast<uint16_t>(vx[it].x);
+      vt[(c + 1) * P::LMV + t] = static_cast<uint16_t>(vx[it].x >> 16);
+      vt[(c + 2) * P::LMV + t] = static_cast<uint16_t>(vx[it].y);
+      vt[(c + 3) * P::LMV + t] = static_cast<uint16_t>(vx[it].y >> 16);
+    }
+    __syncthreads();
+  }
   // W = T diag(beta) (K*b), U = T diag(beta) V; T is lower triangular, so
   // rows [16w, 16w + 16) contract over s < 16 (w + 1)
-  constexpr int NCT = D / 16, NCTP = NCT >= 2 ? NCT / 2 : NCT, NB = NCTP < 4 ? NCTP : 4;
+  constexpr int NCT = D / 16, NCTP = (NTH == 512 && NCT >= 2) ? NCT / 2 : NCT, NB = NCTP < 4 ? NCTP : 4;
   const int kend = 16 * (w + 1);
 #pragma unroll
   for (int cc = 0; cc < NCTP; cc += NB) {
@@ -589,7 +659,7 @@ __global__ void __launch_bounds__(NTP) bwd_prep(BwdArgs a) {
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         bw[n] = *reinterpret_cast<const float4*>(sKbT + (16 * (c0 + n) + r) * LM + k0 + 4 * kq);
-        bu[n] = *reinterpret_cast<const float4*>(sVT + (16 * (c0 + n) + r) * LM + k0 + 4 * kq);
+        bu[n] = load4(sVT + (16 * (c0 + n) + r) * P::LMV + k0 + 4 * kq);
       }
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
@@ -1696,8 +1766,6 @@ __device__ __forceinline__ void load_cols_t(In* dst, const In* src, int64_t tok0
   }
 }
 
-__device__ __forceinline__ float ld1f(const float* p) { return *p; }
-__device__ __forceinline__ float ld1f(const bf16_t* p) { return to_f32(*p); }
 
 // Level-l factors of one channel for the 8 tokens [8 seg, 8 seg + 8): al are
 // their gates, segtot[s] the product of the gates of segment s (LDS, this
@@ -2091,7 +2159,7 @@ template <int D, typename In>
 hipError_t set_lds_d() {
   hipError_t e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_prep<D, In>), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          static_cast<int>(PrepL<D>::BYTES));
+                          static_cast<int>(PrepL<D, In>::BYTES));
   if (e != hipSuccess) return e;
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(bwd_gstate<D, In>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(GsL<D>::BYTES));
@@ -2142,7 +2210,8 @@ hipError_t run_bwd(const BwdArgs& a, int64_t ns, hipStream_t stream) {
   const unsigned unit_blocks = static_cast<unsigned>((static_cast<int64_t>(a.N) * a.H + 7) / 8 * 8) * ScanL<D>::NTILE;
   hipError_t e;
   if (chunk_blocks > 0) {
-    hipLaunchKernelGGL((bwd_prep<D, In>), dim3(chunk_blocks), dim3(NTP), PrepL<D>::BYTES, stream, a);
+    using PP = PrepL<D, In>;
+    hipLaunchKernelGGL((bwd_prep<D, In>), dim3(chunk_blocks), dim3(PP::NTH), PP::BYTES, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if (unit_blocks > 0) {
