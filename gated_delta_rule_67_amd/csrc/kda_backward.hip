@@ -88,9 +88,9 @@ struct BwdArgs {
   float* Kd;    // C x D
   float* QsT;   // D x C   (scale * q_t * b_t)^T
   float* Dl;    // C x D   Delta
-  float* dDl;   // C x D   dDelta
+  float* dDl;   // D x C   dDelta^T
   float* AsT;   // C x C   (scale * Aqk)^T
-  float* Tm;    // C x C
+  float* Tm;    // C x C   T^T
   float* Ab;    // C x C   Akk (strictly lower, beta not applied)
   float* dAq;   // C x C   dL/dAqk
   float* dAb;   // C x C   dL/dAkk
@@ -625,7 +625,7 @@ __global__ void __launch_bounds__(prep_threads<In>()) bwd_prep(BwdArgs a) {
   __syncthreads();
   for (int idx = tid; idx < C * C; idx += NTH) {
     const int t = idx / C, s = idx - t * C;
-    a.Tm[sh * C * C + idx] = sT[t * LM + s];
+    a.Tm[sh * C * C + idx] = sT[s * LM + t];  // T^T
   }
   if constexpr (P::COMPACT) {  // V^T over Akk (the solve is done with it)
     uint16_t* vt = reinterpret_cast<uint16_t*>(sVT);
@@ -1229,8 +1229,9 @@ __global__ void __launch_bounds__(NSC) bwd_rscan3(BwdArgs a) {
       for (int j = 0; j < 4; ++j) {
         const int t = 16 * I + 4 * kq + j, col = 16 * nb + r;
         put_split(sXh + col * LMH + t, sXl + col * LMH + t, acc[0][j]);
-        a.dDl[(sh * C + t) * D + c0 + col] = acc[0][j];
       }
+      *reinterpret_cast<float4*>(a.dDl + (sh * D + c0 + 16 * nb + r) * C + 16 * I + 4 * kq) =
+          make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);  // dDelta^T
     }
     __syncthreads();
     // dS = b_C dS + Qs^T dO - W^T dDelta (fp32 in registers; split copy refreshed)
@@ -1327,8 +1328,9 @@ __global__ void __launch_bounds__(NSC) bwd_rscan(BwdArgs a) {
       for (int j = 0; j < 4; ++j) {
         const int t = 16 * I + 4 * kq + j, col = 16 * nb + r;
         sXT[col * LM + t] = acc[0][j];
-        a.dDl[(sh * C + t) * D + c0 + col] = acc[0][j];
       }
+      *reinterpret_cast<float4*>(a.dDl + (sh * D + c0 + 16 * nb + r) * C + 16 * I + 4 * kq) =
+          make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);  // dDelta^T
     }
     __syncthreads();
     // dS = b_C dS + Qs^T dO - W^T dDelta
@@ -1401,26 +1403,16 @@ __device__ __forceinline__ void load_mat_t(float* dst, const float* src) {
   }
 }
 
-// A dense ROWS x COLS fp32 matrix transposed into LDS rows of ROWS values
-// (dst row c = column c of src), fp32 or split.
-template <bool SP, int ROWS, int COLS, int LDT, int NTH>
-__device__ __forceinline__ void load_mat_t_any(float* dst, const float* src) {
+// A dense ROWS x COLS fp32 matrix into LDS rows (stride LD floats), fp32 or split.
+template <bool SP, int ROWS, int COLS, int LD, int NTH>
+__device__ __forceinline__ void load_mat_any(float* dst, const float* src) {
   if constexpr (SP) {
-    constexpr int G = COLS / 4, N = ROWS * G, IT = (N + NTH - 1) / NTH;
-    float4 x[IT];
-#pragma unroll
-    for (int it = 0; it < IT; ++it) x[it] = load4(src + min(it * NTH + static_cast<int>(threadIdx.x), N - 1) * 4);
-#pragma unroll
-    for (int it = 0; it < IT; ++it) {
-      const int idx = it * NTH + threadIdx.x, rr = idx / G, c = 4 * (idx - rr * G);
-      if (idx >= N) continue;
-      st_el<true>(dst, c + 0, LDT, ROWS, rr, x[it].x);
-      st_el<true>(dst, c + 1, LDT, ROWS, rr, x[it].y);
-      st_el<true>(dst, c + 2, LDT, ROWS, rr, x[it].z);
-      st_el<true>(dst, c + 3, LDT, ROWS, rr, x[it].w);
-    }
+    Staged<ROWS, COLS, NTH> st;
+    st.load_all(src, COLS, 0);
+    uint16_t* d16 = reinterpret_cast<uint16_t*>(dst);
+    store_split(st, d16, d16 + COLS, 2 * LD);
   } else {
-    load_mat_t<ROWS, COLS, LDT, NTH>(dst, src);
+    load_mat<ROWS, COLS, LD, NTH>(dst, src);
   }
 }
 
@@ -1486,8 +1478,8 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
     sBeta[tid] = tid < L.count ? bv : 0.f;
   }
   if (tid < 2 * C) sDb[tid] = 0.f;
-  load_mat_t_any<SP, C, C, LM, NTS>(sT, a.Tm + sh * C * C);   // T^T
-  load_mat_t_any<SP, C, D, LM, NTS>(sX, a.dDl + sh * C * D);  // dDelta^T
+  load_mat_any<SP, C, C, LM, NTS>(sT, a.Tm + sh * C * C);   // T^T
+  load_mat_any<SP, D, C, LM, NTS>(sX, a.dDl + sh * D * C);  // dDelta^T
   load_rows<D, LD, float, NTS>(sR, a.log_g, L.tok0, L.count, H, h);  // log_g rows (0 past the end)
   __syncthreads();
   // the entry state and dO are loaded now and written to LDS after dR
@@ -1685,20 +1677,32 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
       for (int c = 0; c < NCTH; ++c) sCol[w * D + 16 * (ctb + c) + r] = colp[c];
   }
   __syncthreads();
-  // dgamma joins dG at the chunk's last token; write the staged parts
+  // dgamma joins dG at the chunk's last token; the staged parts go through
+  // LDS (the operand regions are free now) and out as whole rows
+  float* oq = sm + P::RS;
+  float* ok = sm + P::RX;
+  float* og = sm + P::RR;
   if (active) {
 #pragma unroll
     for (int c = 0; c < NCTH; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + c) + r;
-        if (t >= L.count) continue;
         float g = dg_[c][j];
         if (t == L.count - 1) g += sGam[i] + sCol[i] + sCol[D + i] + sCol[2 * D + i] + sCol[3 * D + i];
-        a.dq[row(t) * D + i] = dq_[c][j];
-        a.dk[row(t) * D + i] = dk_[c][j];
-        a.dlog_g[row(t) * D + i] = g;
+        oq[t * LD + i] = dq_[c][j];
+        ok[t * LD + i] = dk_[c][j];
+        og[t * LD + i] = g;
       }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < C * (D / 4); idx += NTS) {
+    const int t = idx / (D / 4), c4 = 4 * (idx - t * (D / 4));
+    if (t >= L.count) continue;
+    const int64_t o = row(t) * D + c4;
+    *reinterpret_cast<float4*>(a.dq + o) = *reinterpret_cast<const float4*>(oq + t * LD + c4);
+    *reinterpret_cast<float4*>(a.dk + o) = *reinterpret_cast<const float4*>(ok + t * LD + c4);
+    *reinterpret_cast<float4*>(a.dlog_g + o) = *reinterpret_cast<const float4*>(og + t * LD + c4);
   }
   if (tid < L.count) a.dbeta[row(tid)] = sDb[tid] + sDb[C + tid];
 }
