@@ -2027,47 +2027,62 @@ __global__ void __launch_bounds__(NTG, 2) bwd_gpairs(BwdArgs a) {
       dq_[ct][j] += d * ld1f(sKT + i * LM + t);
       dk_[ct][j] += d * ld1f(sQT + i * LM + t);
     }
-  __syncthreads();  // done with F^T and the dA tiles
-  // the in-group terms, by channel row, over the dA tiles (dq, dk) and F^T (dG)
+  __syncthreads();  // done with Q^T, K^T, F^T and the dA tiles
+  // Sums in [token][channel] rows (stride LO): dq over the dAqk tile, dk over
+  // the dAkk tile, dG over Q^T, K^T and F^T; first the in-group terms, then
+  // the MFMA lanes' terms, then the state-side parts staged by bwd_gstate,
+  // read and written as whole rows.
+  constexpr int LO = CW + 4;
+  float* oq = sdAq;
+  float* ok = sdAb;
+  float* og = reinterpret_cast<float*>(gsm + P::OQ);
+  static_assert(C * LO * sizeof(float) <= P::OA - P::OQ, "dG rows fit over Q^T, K^T and F^T");
   if (fthr) {
-    float* dq8 = sdAq + fi * LM + 8 * seg;
-    float* dk8 = sdAb + fi * LM + 8 * seg;
-    float* dg8 = sFT + fi * LM + 8 * seg;
-    *reinterpret_cast<float4*>(dq8) = make_float4(pq[0], pq[1], pq[2], pq[3]);
-    *reinterpret_cast<float4*>(dq8 + 4) = make_float4(pq[4], pq[5], pq[6], pq[7]);
-    *reinterpret_cast<float4*>(dk8) = make_float4(pk[0], pk[1], pk[2], pk[3]);
-    *reinterpret_cast<float4*>(dk8 + 4) = make_float4(pk[4], pk[5], pk[6], pk[7]);
-    *reinterpret_cast<float4*>(dg8) = make_float4(pg[0], pg[1], pg[2], pg[3]);
-    *reinterpret_cast<float4*>(dg8 + 4) = make_float4(pg[4], pg[5], pg[6], pg[7]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = 8 * seg + u;
+      oq[t * LO + fi] = pq[u];
+      ok[t * LO + fi] = pk[u];
+      og[t * LO + fi] = pg[u];
+    }
   }
   __syncthreads();
-  // add the state-side parts staged by bwd_gstate; dG^T into sFT for the cumsum
   if (active) {
 #pragma unroll
     for (int ct = 0; ct < NCTW; ++ct)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = 16 * w + 4 * kq + j, i = 16 * (ctb + ct) + r;
-        const int64_t o = row(min(t, L.count - 1)) * D + c0 + i;
-        const float xq = a.dq[o], xk = a.dk[o], xg = a.dlog_g[o];
-        float g = 0.f;
-        const float gin = sFT[i * LM + t];
-        if (t < L.count) {
-          a.dq[o] = xq + dq_[ct][j] + sdAq[i * LM + t];
-          a.dk[o] = xk + dk_[ct][j] + sdAb[i * LM + t];
-          g = xg + dg_[ct][j] + gin;
-        }
-        sFT[i * LM + t] = g;
+        oq[t * LO + i] += dq_[ct][j];
+        ok[t * LO + i] += dk_[ct][j];
+        og[t * LO + i] += dg_[ct][j];
       }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < C * (CW / 4); idx += NTG) {
+    const int t = idx / (CW / 4), c4 = 4 * (idx - t * (CW / 4));
+    const int64_t o = row(min(t, L.count - 1)) * D + c0 + c4;
+    const float4 xq = *reinterpret_cast<const float4*>(a.dq + o), xk = *reinterpret_cast<const float4*>(a.dk + o);
+    const float4 xg = *reinterpret_cast<const float4*>(a.dlog_g + o);
+    float4* pgq = reinterpret_cast<float4*>(og + t * LO + c4);
+    if (t < L.count) {
+      const float4 yq = *reinterpret_cast<const float4*>(oq + t * LO + c4);
+      const float4 yk = *reinterpret_cast<const float4*>(ok + t * LO + c4);
+      const float4 yg = *pgq;
+      *reinterpret_cast<float4*>(a.dq + o) = make_float4(xq.x + yq.x, xq.y + yq.y, xq.z + yq.z, xq.w + yq.w);
+      *reinterpret_cast<float4*>(a.dk + o) = make_float4(xk.x + yk.x, xk.y + yk.y, xk.z + yk.z, xk.w + yk.w);
+      *pgq = make_float4(xg.x + yg.x, xg.y + yg.y, xg.z + yg.z, xg.w + yg.w);
+    } else {
+      *pgq = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
   }
   __syncthreads();
   // dlog_g = reverse cumulative sum of dG over the chunk: each factor thread
   // sums its 8 tokens, then adds the totals of the segments after its own
   float g[8];
   if (fthr) {
-    const float* src = sFT + fi * LM + 8 * seg;
-    const float4 x0 = *reinterpret_cast<const float4*>(src), x1 = *reinterpret_cast<const float4*>(src + 4);
-    g[0] = x0.x; g[1] = x0.y; g[2] = x0.z; g[3] = x0.w; g[4] = x1.x; g[5] = x1.y; g[6] = x1.z; g[7] = x1.w;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) g[u] = og[(8 * seg + u) * LO + fi];
 #pragma unroll
     for (int u = 6; u >= 0; --u) g[u] += g[u + 1];
     sSeg[seg * CW + fi] = g[0];
