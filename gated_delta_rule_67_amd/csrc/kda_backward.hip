@@ -206,33 +206,6 @@ __device__ __forceinline__ void load_mat(float* dst, const float* src) {
   }
 }
 
-// Columns [c0, c0 + COLS) of a dense rows x LDG matrix into LDS (stride LD).
-template <int ROWS, int COLS, int LD>
-__device__ __forceinline__ void load_cols(float* dst, const float* src, int ldg, int c0) {
-  constexpr int G = COLS / 4, N = ROWS * G, IT = (N + NT - 1) / NT;
-  float4 x[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int idx = it * NT + threadIdx.x, t = idx / G, g4 = idx - t * G;
-    x[it] = load4(src + static_cast<int64_t>(min(t, ROWS - 1)) * ldg + c0 + 4 * g4);
-  }
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int idx = it * NT + threadIdx.x, t = idx / G, g4 = idx - t * G;
-    if (idx < N) *reinterpret_cast<float4*>(dst + t * LD + 4 * g4) = x[it];
-  }
-}
-
-template <int ROWS, int COLS, int LD>
-__device__ __forceinline__ void store_cols(float* dst, int ldg, int c0, const float* src) {
-  constexpr int G = COLS / 4;
-  for (int idx = threadIdx.x; idx < ROWS * G; idx += NT) {
-    const int t = idx / G, g4 = idx - t * G;
-    *reinterpret_cast<float4*>(dst + static_cast<int64_t>(t) * ldg + c0 + 4 * g4) =
-        *reinterpret_cast<const float4*>(src + t * LD + 4 * g4);
-  }
-}
-
 // Gates of one channel over 32 tokens [base, base + 32) of the chunk (1 past
 // the document end).
 template <int D>
@@ -1378,28 +1351,6 @@ __device__ __forceinline__ void mm_kc(f32x4 (&acc)[NB], const float* A, int lda,
     for (int n = 0; n < NB; ++n) acc[n] = mma(a.z, b[n].z, acc[n]);
 #pragma unroll
     for (int n = 0; n < NB; ++n) acc[n] = mma(a.w, b[n].w, acc[n]);
-  }
-}
-
-// A dense rows x cols fp32 matrix, transposed into LDS: dst[c * LDT + r] = src[r][c].
-template <int ROWS, int COLS, int LDT, int NTH = NT>
-__device__ __forceinline__ void load_mat_t(float* dst, const float* src) {
-  constexpr int G = COLS / 4, N = ROWS * G, IT = (N + NTH - 1) / NTH;
-  float4 x[IT];
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int idx = it * NTH + threadIdx.x;
-    x[it] = load4(src + min(idx, N - 1) * 4);
-  }
-#pragma unroll
-  for (int it = 0; it < IT; ++it) {
-    const int idx = it * NTH + threadIdx.x, rr = idx / G, c = 4 * (idx - rr * G);
-    if (idx < N) {
-      dst[(c + 0) * LDT + rr] = x[it].x;
-      dst[(c + 1) * LDT + rr] = x[it].y;
-      dst[(c + 2) * LDT + rr] = x[it].z;
-      dst[(c + 3) * LDT + rr] = x[it].w;
-    }
   }
 }
 
