@@ -615,17 +615,18 @@ __global__ void __launch_bounds__(prep_threads<In>()) bwd_prep(BwdArgs a) {
   }
   // W = T diag(beta) (K*b), U = T diag(beta) V; T is lower triangular, so
   // rows [16w, 16w + 16) contract over s < 16 (w + 1)
-  constexpr int NCT = D / 16, NCTP = (NTH == 512 && NCT >= 2) ? NCT / 2 : NCT, NB = NCTP < 4 ? NCTP : 4;
-  const int kend = 16 * (w + 1);
-#pragma unroll
-  for (int cc = 0; cc < NCTP; cc += NB) {
-    const int c0 = hf * NCTP + cc;
-    if (c0 >= NCT) break;  // (D = 16: one column tile, first half only)
+  constexpr int NCT = D / 16, NCTP = (NTH == 512 && NCT >= 2) ? NCT / 2 : NCT;
+  constexpr bool PAIRED = NTH == 256 && NCT >= 2;  // 4 waves: paired row blocks, half the column tiles each
+  constexpr int NCW = PAIRED ? NCT / 2 : NCTP;     // column tiles per wave
+  constexpr int NB = NCW < 4 ? NCW : 4;
+  // rows [16 rb, 16 rb + 16) of W and U, column tiles [c0, c0 + NB)
+  auto wu_block = [&](int rb, int c0) {
+    const int kend = 16 * (rb + 1);
     f32x4 accW[NB], accU[NB];
 #pragma unroll
     for (int n = 0; n < NB; ++n) accW[n] = accU[n] = zero4f();
     for (int k0 = 0; k0 < kend; k0 += 16) {
-      const float4 tv = *reinterpret_cast<const float4*>(sT + (16 * w + r) * LM + k0 + 4 * kq);
+      const float4 tv = *reinterpret_cast<const float4*>(sT + (16 * rb + r) * LM + k0 + 4 * kq);
       const float4 bs = *reinterpret_cast<const float4*>(sBeta + k0 + 4 * kq);
       const float4 av = make_float4(tv.x * bs.x, tv.y * bs.y, tv.z * bs.z, tv.w * bs.w);
       float4 bw[NB], bu[NB];
@@ -660,13 +661,29 @@ __global__ void __launch_bounds__(prep_threads<In>()) bwd_prep(BwdArgs a) {
       const int i = 16 * (c0 + n) + r;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int t = 16 * w + 4 * kq + j;
+        const int t = 16 * rb + 4 * kq + j;
         a.Wm[(sh * C + t) * D + i] = accW[n][j];
         a.Um[(sh * C + t) * D + i] = accU[n][j];
       }
-      *reinterpret_cast<float4*>(a.WT + (sh * D + i) * C + 16 * w + 4 * kq) =
+      *reinterpret_cast<float4*>(a.WT + (sh * D + i) * C + 16 * rb + 4 * kq) =
           make_float4(accW[n][0], accW[n][1], accW[n][2], accW[n][3]);
     }
+  };
+  if constexpr (!PAIRED) {
+    // 8 waves: block w, the column tiles of half hf (D = 16: one tile, first half)
+#pragma unroll
+    for (int cc = 0; cc < NCTP; cc += NB) {
+      const int c0 = hf * NCTP + cc;
+      if (c0 < NCT) wu_block(w, c0);
+    }
+  } else {
+    // 4 waves: block I costs I + 1 steps of 16, so waves pair blocks {0, 3}
+    // and {1, 2} and split the column tiles, 5 steps each
+    const int rb0 = w < 2 ? 0 : 1;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int cc = 0; cc < NCW; cc += NB) wu_block(e == 0 ? rb0 : 3 - rb0, (w & 1) * NCW + cc);
   }
 }
 
