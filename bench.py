@@ -2,7 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
     python bench.py --only {prefill,varlen,step,backward,conv,norm,copy}      (profiling runs)
-    python bench.py --traffic-from FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+    python bench.py [--traffic-kind {prefill,backward}] --traffic-from FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
 
 A step is one kda_chunk_fwd call (chunked prefill) over the dense workload
 B=4 x T=4096 tokens, H=16 heads, dk=dv=128, bf16 q/k/v, fp32 gates/beta/state,
@@ -34,9 +34,10 @@ Only one GPU is used; --gpus above 1 exits with a message.
 roofline.traffic is the HBM bytes of one prefill call measured with rocprofv3
 counters (FETCH_SIZE, WRITE_SIZE; one pass each), scaled by what the same
 counters read for a plain copy of known size (--only copy).  --traffic-from
-turns those four runs' CSV output into profiles/traffic_prefill_dense.txt,
-stamped with a hash of the kernel sources; the figure is reported only while
-the sources still hash the same (else null).
+turns those four runs' CSV output into profiles/traffic_prefill_dense.txt
+(--traffic-kind backward: profiles/traffic_backward_dense.txt, for the
+backward's roofline), stamped with a hash of the kernel sources; the figure is
+reported only while the sources still hash the same (else null).
 """
 from __future__ import annotations
 
@@ -62,29 +63,41 @@ MFMA_PEAK_TFLOPS = 2516.6      # MI355X dense fp16/bf16 MFMA, TFLOP/s
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 (matrix and vector), TFLOP/s
 CHUNK = 64
 COPY_BYTES = 512 << 20         # calibration copy: bytes read (= bytes written)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_prefill_dense.txt")
-# the files that define the two prefill kernels (their code, not the ABI around them)
-KERNEL_SOURCES = ["kda_twopass.hip", "kda_common.h", "kda_fallback.h"]
+# Counter-measured HBM traffic per call, one summary per measured path: the
+# file, the sources that define its kernels (their code, not the ABI around
+# them), the kernels summed, and the workload the counters were taken on.
+TRAFFIC = {
+    "prefill": dict(file=os.path.join(ROOT, "profiles", "traffic_prefill_dense.txt"),
+                    sources=["kda_twopass.hip", "kda_common.h", "kda_fallback.h"],
+                    kernels=("prep_kernel", "scan_kernel"),
+                    what="one kda_chunk_fwd call, dense 4 x 4096 tokens, 16 heads, d = 128, bf16"),
+    "backward": dict(file=os.path.join(ROOT, "profiles", "traffic_backward_dense.txt"),
+                     sources=["kda_backward.hip", "kda_common.h"],
+                     kernels=("bwd_prep", "bwd_fscan", "bwd_rscan", "bwd_gstate", "bwd_gpairs"),
+                     what="one kda_chunk_bwd call, dense 4 x 4096 tokens, 16 heads, d = 128, bf16"),
+}
+TRAFFIC_FILE = TRAFFIC["prefill"]["file"]
+KERNEL_SOURCES = TRAFFIC["prefill"]["sources"]
 
 
-def sources_hash() -> str:
+def sources_hash(kind: str = "prefill") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in TRAFFIC[kind]["sources"]:
         with open(os.path.join(ROOT, "gated_delta_rule_67_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per prefill call from the committed counter summary, or None
-    when it is missing or was taken on other kernel sources."""
+def read_traffic(kind: str = "prefill"):
+    """HBM bytes per call from the committed counter summary, or None when it
+    is missing or was taken on other kernel sources."""
     try:
         kv = {}
-        for line in open(TRAFFIC_FILE):
+        for line in open(TRAFFIC[kind]["file"]):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-        if kv.get("sources_sha256") != sources_hash():
+        if kv.get("sources_sha256") != sources_hash(kind):
             return None
         return int(kv["traffic_bytes_per_call"])
     except (OSError, KeyError, ValueError):
@@ -109,7 +122,7 @@ def _counter_sums(run_dir: str, counter: str):
     return {k: sum(v) / len(v) for k, v in out.items()}
 
 
-def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
+def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kind="prefill"):
     fe, wr = _counter_sums(fetch_dir, "FETCH_SIZE"), _counter_sums(write_dir, "WRITE_SIZE")
     cf, cw = _counter_sums(copy_fetch_dir, "FETCH_SIZE"), _counter_sums(copy_write_dir, "WRITE_SIZE")
     pick = lambda d, pat: sum(v for k, v in d.items() if pat in k)
@@ -117,11 +130,11 @@ def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir):
     copy_w = max(cw.values())
     k_fetch = COPY_BYTES / (copy_f * 1024.0)
     k_write = COPY_BYTES / (copy_w * 1024.0)
-    lines = [f"sources_sha256: {sources_hash()}",
+    lines = [f"sources_sha256: {sources_hash(kind)}",
              f"copy_fetch_kib: {copy_f:.1f}", f"copy_write_kib: {copy_w:.1f}",
              f"fetch_scale: {k_fetch:.4f}", f"write_scale: {k_write:.4f}"]
     total = 0.0
-    for pat in ("prep_kernel", "scan_kernel"):
+    for pat in TRAFFIC[kind]["kernels"]:
         f, w = pick(fe, pat), pick(wr, pat)
         b = f * 1024 * k_fetch + w * 1024 * k_write
         total += b
@@ -282,7 +295,7 @@ def bench_backward(kda, steps, warmup):
             "algorithmic_flops": fl, "algorithmic_bytes": nb,
             "hbm_gbs": round(nb / (avg * 1e-3) / 1e9, 1),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tf / FP32_PEAK_TFLOPS, 4), "traffic": None},
+                         "frac": round(tf / FP32_PEAK_TFLOPS, 4), "traffic": read_traffic("backward")},
             "workspace_bytes": int(ws.numel())}
 
 
@@ -528,16 +541,19 @@ def main():
                     default="all",
                     help="restrict the run (profiling); the JSON line needs 'all'")
     ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
-                    help="rocprofv3 csv dirs: prefill FETCH_SIZE, prefill WRITE_SIZE, copy FETCH_SIZE, "
-                         "copy WRITE_SIZE; writes " + os.path.relpath(TRAFFIC_FILE, ROOT))
+                    help="rocprofv3 csv dirs: FETCH_SIZE and WRITE_SIZE of the measured path, then FETCH_SIZE and "
+                         "WRITE_SIZE of the copy; writes the path's profiles/traffic_*.txt")
+    ap.add_argument("--traffic-kind", choices=sorted(TRAFFIC), default="prefill",
+                    help="which path --traffic-from summarises (bench.py --only <kind> made its runs)")
     args = ap.parse_args()
     if args.traffic_from:
-        lines = write_traffic(*args.traffic_from)
-        with open(TRAFFIC_FILE, "w") as fh:
-            fh.write("# HBM traffic of one kda_chunk_fwd call, dense 4 x 4096 tokens, 16 heads, d = 128, bf16\n")
-            fh.write("# made by: python bench.py --traffic-from " + " ".join(args.traffic_from) + "\n")
+        kind = args.traffic_kind
+        lines = write_traffic(*args.traffic_from, kind=kind)
+        with open(TRAFFIC[kind]["file"], "w") as fh:
+            fh.write(f"# HBM traffic of {TRAFFIC[kind]['what']}\n")
+            fh.write(f"# made by: python bench.py --traffic-kind {kind} --traffic-from " + " ".join(args.traffic_from) + "\n")
             fh.write("# from four counter runs (cd /tmp && export TMPDIR=/tmp first), one pass each:\n")
-            for ctr, what, d in (("FETCH_SIZE", "prefill", args.traffic_from[0]), ("WRITE_SIZE", "prefill", args.traffic_from[1]),
+            for ctr, what, d in (("FETCH_SIZE", kind, args.traffic_from[0]), ("WRITE_SIZE", kind, args.traffic_from[1]),
                                  ("FETCH_SIZE", "copy", args.traffic_from[2]), ("WRITE_SIZE", "copy", args.traffic_from[3])):
                 steps = "--steps 3 --warmup 1"
                 fh.write(f"#   rocprofv3 --pmc {ctr} -f csv -d {d} -o run -- python3 bench.py --only {what} {steps}\n")

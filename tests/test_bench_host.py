@@ -81,15 +81,32 @@ def test_traffic_is_scaled_by_the_copy_calibration(tmp_path):
     assert kv["sources_sha256"] == bench.sources_hash()
 
 
-def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch):
+@pytest.mark.parametrize("kind", ["prefill", "backward"])
+def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path, monkeypatch, kind):
     f = tmp_path / "traffic.txt"
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    f.write_text(f"# comment\nsources_sha256: {bench.sources_hash()}\ntraffic_bytes_per_call: 123456\n")
-    assert bench.read_traffic() == 123456
+    monkeypatch.setitem(bench.TRAFFIC[kind], "file", str(f))
+    f.write_text(f"# comment\nsources_sha256: {bench.sources_hash(kind)}\ntraffic_bytes_per_call: 123456\n")
+    assert bench.read_traffic(kind) == 123456
     f.write_text("sources_sha256: 0000000000000000\ntraffic_bytes_per_call: 123456\n")
-    assert bench.read_traffic() is None
+    assert bench.read_traffic(kind) is None
     f.unlink()
-    assert bench.read_traffic() is None
+    assert bench.read_traffic(kind) is None
+
+
+def test_backward_traffic_sums_the_five_backward_kernels(tmp_path):
+    kib = bench.COPY_BYTES / 1024.0
+    _write_counter_csv(tmp_path / "cf", "FETCH_SIZE", [("copy_kernel", 1, kib)])
+    _write_counter_csv(tmp_path / "cw", "WRITE_SIZE", [("copy_kernel", 1, kib)])
+    names = ["bwd_prep<128>", "bwd_fscan3<128>", "bwd_rscan3<128>", "bwd_gstate<128>", "bwd_gpairs<128>"]
+    _write_counter_csv(tmp_path / "bf", "FETCH_SIZE", [(n, i, 10.0 * (i + 1)) for i, n in enumerate(names)] +
+                       [("prep_kernel(x)", 9, 1000.0)])
+    _write_counter_csv(tmp_path / "bw", "WRITE_SIZE", [(n, i, 1.0) for i, n in enumerate(names)])
+    lines = bench.write_traffic(str(tmp_path / "bf"), str(tmp_path / "bw"), str(tmp_path / "cf"), str(tmp_path / "cw"),
+                                kind="backward")
+    kv = dict(l.split(": ", 1) for l in lines)
+    assert int(kv["traffic_bytes_per_call"]) == round((10 + 20 + 30 + 40 + 50 + 5) * 1024)
+    assert kv["sources_sha256"] == bench.sources_hash("backward")
+    assert bench.sources_hash("backward") != bench.sources_hash("prefill")
 
 
 def test_backward_bytes_and_flops_of_the_dense_workload():
