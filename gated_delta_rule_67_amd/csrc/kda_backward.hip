@@ -4,9 +4,9 @@
 // through the gated delta rule (NeMo glm5_next.layers: `_torch_recurrent_kda`
 // is the differentiable reference; the KDA parameters are trained under FSDP).
 // Arithmetic: fp32 operands, MFMA (v_mfma_f32_16x16x4_f32) and state; for bf16
-// inputs the two scans form their products from split-bf16 operands (three
-// bf16 MFMAs per product, about 16 bits of precision per term) with the state
-// kept in fp32.
+// inputs the two scans and bwd_gstate form their products from split-bf16
+// operands (three bf16 MFMAs per product, about 16 bits of precision per term)
+// with the state and every stored intermediate kept in fp32.
 //
 // Chunk form (64 tokens, one unit = (sequence or document, head)).  Inside a
 // chunk with entry state S, b_t = prod_{u<=t} alpha_u (alpha = exp(log_g), per
@@ -35,6 +35,8 @@
 // of t's half to t (upper half) or from t+1 to the last token of the half
 // (lower half).  Every factor is a product of gates <= 1, so the MFMA operands
 // x_t F_l(t) and y_s F_l(s) are bounded by the inputs.  Pairs t = s have r = 1.
+// bwd_gpairs sums levels 3-5 (pairs inside an aligned 8-token group) per
+// channel with r(t, s) as a running product of gates instead.
 //
 // Kernels, in launch order (slots are chunks, one workgroup per (slot, head)
 // or per (unit, value-column tile)):
@@ -45,7 +47,8 @@
 //                 (bwd_rscan3 with split-bf16 products)
 //   bwd_gstate    per chunk: dv, dbeta, dAqk, dA and the state-side parts of
 //                 dq, dk and dG (staged in the dq, dk, dlog_g outputs)
-//   bwd_gpairs    per chunk: the pair terms, then dlog_g = reverse cumsum(dG)
+//   bwd_gpairs    per (chunk, 64 channels): the pair terms, then
+//                 dlog_g = reverse cumsum(dG)
 #include <algorithm>
 #include <type_traits>
 
