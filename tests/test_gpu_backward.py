@@ -81,10 +81,31 @@ def test_packed_edge_lengths(dtype):
         np.testing.assert_array_equal(got["d_init_state"][n], up["d_final"][n].numpy())
 
 
-def test_no_initial_state_and_no_final_gradient():
-    inp = kda_inputs.make_inputs(B=2, T=100, H=2, dk=32, dv=32, dtype="f32", seed=120, init="zeros")
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 64)])
+def test_no_initial_state_and_no_final_gradient(dtype, d):
+    inp = kda_inputs.make_inputs(B=2, T=100, H=2, dk=d, dv=d, dtype=dtype, seed=120, init="zeros")
     up = kda_inputs.upstream_grads(inp, seed=220, final=False)
-    check("zeros", gpu_bwd(inp, up, init=False), oracle_bwd(inp, up, init=False), TOL["f32"])
+    check(f"zeros {dtype} d={d}", gpu_bwd(inp, up, init=False), oracle_bwd(inp, up, init=False), TOL[dtype])
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 32), ("bf16", 64)])
+def test_without_initial_state_gradient(dtype, d):
+    """d_init_state not requested: the other five gradients are unchanged."""
+    inp = kda_inputs.make_inputs(B=1, T=130, H=2, dk=d, dv=d, dtype=dtype, seed=125, init="normal", init_std=0.05)
+    up = kda_inputs.upstream_grads(inp, seed=225)
+    dv_ = to_dev(inp)
+    g = kda.chunk_bwd(dv_["q"], dv_["k"], dv_["v"], dv_["log_g"], dv_["beta"], up["d_out"].cuda(),
+                      init_state=dv_["init_state"], d_final=up["d_final"].cuda(), scale=inp["scale"],
+                      d_init_state=False)
+    torch.cuda.synchronize()
+    ref = oracle_bwd(inp, up)
+    assert "d_init_state" not in g or g["d_init_state"] is None
+    for n in NAMES:
+        if n == "d_init_state":
+            continue
+        e = err(g[n].cpu().numpy(), ref[n])
+        print(f"[no d_init {dtype} d={d}] {n} {e:.2e}", flush=True)
+        assert e <= TOL[dtype], (n, e)
 
 
 @pytest.mark.parametrize("mode,dtype,d", [("uniform", "f32", 32), ("erase", "f32", 32), ("uniform", "bf16", 64),
