@@ -273,32 +273,38 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ f32x4 mfma_bf(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ uint32_t rne_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Two fp32 values rounded to nearest even as packed bf16 (one
+// v_cvt_pk_bf16_f32), and back.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  bf16x2v r;
+  r[0] = static_cast<__bf16>(a);
+  r[1] = static_cast<__bf16>(b);
+  return __builtin_bit_cast(uint32_t, r);
 }
-// hi and lo halves of x, as bf16 bits
-__device__ __forceinline__ void split2(float x, uint32_t& hi, uint32_t& lo) {
-  hi = rne_bf16(x);
-  lo = rne_bf16(x - __uint_as_float(hi << 16));
+__device__ __forceinline__ float bf16_lo_f(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16_hi_f(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+
+// hi and lo halves of a pair of values, packed: hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16(x0, x1);
+  lo = pack_bf16(x0 - bf16_lo_f(hi), x1 - bf16_hi_f(hi));
 }
 __device__ __forceinline__ void put_split(uint16_t* hi, uint16_t* lo, float x) {
   uint32_t h, l;
-  split2(x, h, l);
+  split_pair(x, 0.f, h, l);
   *hi = static_cast<uint16_t>(h);
   *lo = static_cast<uint16_t>(l);
 }
 // four consecutive values
 __device__ __forceinline__ void put_split4(uint16_t* hi, uint16_t* lo, float4 x) {
-  uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-  split2(x.x, h0, l0);
-  split2(x.y, h1, l1);
-  split2(x.z, h2, l2);
-  split2(x.w, h3, l3);
-  *reinterpret_cast<uint2*>(hi) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-  *reinterpret_cast<uint2*>(lo) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+  uint32_t h01, l01, h23, l23;
+  split_pair(x.x, x.y, h01, l01);
+  split_pair(x.z, x.w, h23, l23);
+  *reinterpret_cast<uint2*>(hi) = make_uint2(h01, h23);
+  *reinterpret_cast<uint2*>(lo) = make_uint2(l01, l23);
 }
-
 
 // ---------------------------------------------------------------------------
 // bwd_prep: per (chunk, head).
