@@ -8,21 +8,22 @@
 //   T        = (I + A)^-1,  W = T Xk,  U = T Xv
 //   Delta    = U - W S                                  (per-token beta (v - S^T k))
 //   Aqk[i,j] = sum_c q_ic k_jc exp(G_ic - G_jc)            (j <= i)
-//   O        = scale (Q exp(G) S + Aqk Delta) = Q' S + Ou
-//              with B = scale Aqk T, Q' = scale Q exp(G) - B Xk, Ou = B Xv
+//   O        = scale (Q exp(G) S + Aqk Delta) = Qs S + As Delta
+//              with Qs = scale Q exp(G), As = scale Aqk
 //   S_next   = exp(gamma) S + (K exp(gamma - G))^T Delta
 // (the output reads the state after each token's update).
 //
 // Pass 1 (prep_kernel) depends on nothing but the chunk's own inputs, so it
-// runs over every (chunk, head) at once: it forms A, Aqk, T, B and writes the
-// fp16 operands W, Q', K exp(gamma - G), U, Ou plus exp(gamma) to a workspace
+// runs over every (chunk, head) at once: it forms A, Aqk, T and writes the
+// fp16 operands W, Qs, K exp(gamma - G), U, As plus exp(gamma) to a workspace
 // slot.  Pass 2 (scan_kernel) is the only serial part: per (unit, 32-column
 // value tile) it walks the unit's chunks with the fp32 state in MFMA
-// accumulators, three 64x128x32-class products per chunk (W S and Q' S share
-// the state operand; K^T Delta updates the state), with the slot operands of
-// the next two chunks in flight while one chunk is processed.  Its eight
-// waves split the roles: four form Delta (the serial chain), four form the
-// outputs, all eight update 16 state rows each.
+// accumulators, three 64x128x32-class products per chunk (W S and Qs S share
+// the state operand; K^T Delta updates the state) and As Delta, which reads
+// the Delta tile the state update reads, with the slot operands of the next
+// two chunks in flight while one chunk is processed.  Its eight waves split
+// the roles: four form Delta (the serial chain), four form the outputs, all
+// eight update 16 state rows each.
 //
 // Decay factors without overflow (pass 1).  The chunk is cut into four
 // 16-token blocks.  With R_I = G before block I's first token:
@@ -37,7 +38,7 @@
 // Fast-path guard.  A chunk is evaluated token by token in exact fp32 (in
 // pass 2) instead when its half-block decay exceeds the bound, its inputs
 // could overflow an fp16 operand, a diagonal block of A exceeds 1 in
-// magnitude, any fp16 intermediate (T, B, W, U, Q', Ou, Delta) would exceed
+// magnitude, any fp16 intermediate (T, W, U, Qs, As, Delta) would exceed
 // F16_SAFE, or the entry state exceeds S_MAX.
 //
 // Arithmetic: fp16 MFMA operands (formed in fp32 from the bf16 inputs and
@@ -74,26 +75,32 @@ constexpr float S_MAX = 2048.0f;                // |S| bound of the fast path
 constexpr float F16_SAFE = 16384.0f;            // bound of every fp16 intermediate
 
 // Workspace slot of one (chunk, head), bytes.
-// -W, Q' and (K exp(gamma - G))^T are stored in the order the scan's lanes
-// read them, so every scan load instruction covers 1 KiB of whole lines:
-//   NW, QP: [I 4][ks 4][lane 64][j 8] = X[16I+lc][32ks+8lg+j]
+// -W, Qs, As and (K exp(gamma - G))^T are stored in the order the scan's
+// lanes read them, so every scan load instruction covers 1 KiB of whole lines:
+//   NW, QS: [I 4][ks 4][lane 64][j 8] = X[16I+lc][32ks+8lg+j]
+//   AS:     [I 4][ks 2][lane 64][j 8] = As[16I+lc][32ks+8lg+j]  (zero above the diagonal)
 //   KDT:    [r 8][ks 2][lane 64][j 8] = Kd^T[16r+lc][32ks+8lg+j]
 constexpr size_t OFF_NW = 0;        // -W          64 x 128  fp16
-constexpr size_t OFF_QP = 16384;    // Q'          64 x 128  fp16
+constexpr size_t OFF_QS = 16384;    // Qs          64 x 128  fp16
 constexpr size_t OFF_KDT = 32768;   // Kd^T        128 x 64  fp16
 constexpr size_t OFF_UP = 49152;    // U  by scan lane: [I][tile][lane][b][e] = U[16I+lc][32tile+16b+4lg+e]
-constexpr size_t OFF_OP = 65536;    // Ou by scan lane: [I][tile][lane][b][e] = Ou[16I+lc][32tile+16b+4lg+e]
-constexpr size_t OFF_GAM = 81920;   // exp(gamma)  [128] fp32
-constexpr size_t OFF_FLAG = 82432;  // per prep wave "not on the fast path" [8] bytes
-constexpr size_t SLOT_BYTES = 82944;
+constexpr size_t OFF_AS = 65536;    // As          64 x 64   fp16
+constexpr size_t OFF_GAM = 73728;   // exp(gamma)  [128] fp32
+constexpr size_t OFF_FLAG = 74240;  // per prep wave "not on the fast path" [8] bytes
+constexpr size_t SLOT_BYTES = 74752;
+
+// position of fragA(X_IJ) (lane holds X[16I+lc][16J+4lg+e]) in a [I][ks][lane][j] field of
+// 64 x (16 nks) fp16: k-step J/2, lane (lg' = 2(J&1) + lg/2, lc), position 4(lg&1)
+__device__ __forceinline__ int frag_pos(int I, int J, int nks, int lane) {
+  const int lc = lane & 15, lg = lane >> 4;
+  return ((I * nks + (J >> 1)) * 64 + 16 * (2 * (J & 1) + (lg >> 1)) + lc) * 8 + 4 * (lg & 1);
+}
 
 // LDS fragment slots of pass 1 (one f16x4 per lane each).
 constexpr int S_TD = 0;    // fragA(T_II)               4
 constexpr int S_AO = 4;    // fragA(A_IJ), I > J        6
-constexpr int S_AQ = 10;   // fragA(Aqk_IJ), J <= I     10
-constexpr int S_TO = 20;   // fragA(T_IJ), I > J        6
-constexpr int S_BS = 26;   // fragA(-scale B_IJ), J <= I 10
-constexpr int NFRAG = 36;
+constexpr int S_TO = 10;   // fragA(T_IJ), I > J        6
+constexpr int NFRAG = 16;
 
 __device__ __forceinline__ constexpr int tile10(int I, int J) { return (I * (I + 1)) / 2 + J; }  // J <= I
 __device__ __forceinline__ constexpr int pair6(int I, int J) { return (I * (I - 1)) / 2 + J; }   // J < I
@@ -151,10 +158,10 @@ __device__ __forceinline__ f16x8 off_factor(const PrepSmem& sm, int I, int J, in
   return r;
 }
 
-// Column J of T below the diagonal and column J of -scale B = -scale Aqk T,
-// into the fragment slots.  tbJ = fragB(T_JJ).  Returns "an entry is too large".
+// Column J of T below the diagonal, into the fragment slots.  tbJ =
+// fragB(T_JJ).  Returns "an entry is too large".
 template <int J>
-__device__ __forceinline__ bool t_column(PrepSmem& sm, f16x4 tbJ, float nscale, int lane) {
+__device__ __forceinline__ bool t_column(PrepSmem& sm, f16x4 tbJ, int lane) {
   bool bad = false;
   f16x4 tb[4];  // fragB(T_KJ)
   tb[J] = tbJ;
@@ -176,20 +183,6 @@ __device__ __forceinline__ bool t_column(PrepSmem& sm, f16x4 tbJ, float nscale, 
     }
     sm.frag[S_TO + pair6(I, J)][lane] = sa;
     tb[I] = sb;
-  }
-#pragma unroll
-  for (int I = J; I < 4; ++I) {
-    f32x4 acc = zero4();  // fragA(sum_K Aqk_IK T_KJ)
-#pragma unroll
-    for (int K = J; K <= I; ++K) acc = mfma16(tb[K], sm.frag[S_AQ + tile10(I, K)][lane], acc);
-    f16x4 bs;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = nscale * acc[e];
-      bad |= !(fabsf(x) <= F16_SAFE);
-      bs[e] = (f16)x;
-    }
-    sm.frag[S_BS + tile10(I, J)][lane] = bs;
   }
   return bad;
 }
@@ -488,15 +481,22 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
 #pragma unroll
       for (int e = 0; e < 4; ++e) res[e] = (f16)(bA * acc[e]);
       sm.frag[S_AO + pair6(I, J)][lane] = res;
-    } else {
+    } else {  // As = scale Aqk, straight to the slot
+      float amax = 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) res[e] = (f16)((16 * J + 4 * lg + e) <= (16 * I + lc) ? acc[e] : 0.f);
-      sm.frag[S_AQ + tile10(I, J)][lane] = res;
+      for (int e = 0; e < 4; ++e) {
+        const float x = (16 * J + 4 * lg + e) <= (16 * I + lc) ? p.scale * acc[e] : 0.f;
+        amax = fmaxf(amax, fabsf(x));
+        res[e] = (f16)x;
+      }
+      bad |= !(amax <= F16_SAFE);
+      *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(slot + OFF_AS) + frag_pos(I, J, 2, lane)) = res;
     }
   }
   lds_barrier();
 
-  // ---------------- phase 3: Xk^T, Xv^T into LDS; waves 0-3: column w of T and of -scale B
+  // ---------------- phase 3: Xk^T, Xv^T into LDS; waves 0-3: column w of T;
+  // waves 0-5: one of the six zero tiles of As above the diagonal
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     f16x2 xk2, xv2;
@@ -505,24 +505,28 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
     *reinterpret_cast<f16x2*>(&sm.u.x.XkT[c8 + c][r0]) = xk2;
     *reinterpret_cast<f16x2*>(&sm.u.x.XvT[c8 + c][r0]) = xv2;
   }
-  {
-    const float nscale = -p.scale;
-    switch (w) {
-      case 0: bad |= t_column<0>(sm, tbd, nscale, lane); break;
-      case 1: bad |= t_column<1>(sm, tbd, nscale, lane); break;
-      case 2: bad |= t_column<2>(sm, tbd, nscale, lane); break;
-      case 3: bad |= t_column<3>(sm, tbd, nscale, lane); break;
-      default: break;
-    }
+  if (w < 6) {  // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+    const int zi = w < 3 ? 0 : w < 5 ? 1 : 2;
+    const int zj = zi + 1 + w - (zi == 0 ? 0 : zi == 1 ? 3 : 5);
+    f16x4 z;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = (f16)0.f;
+    *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(slot + OFF_AS) + frag_pos(zi, zj, 2, lane)) = z;
+  }
+  switch (w) {
+    case 0: bad |= t_column<0>(sm, tbd, lane); break;
+    case 1: bad |= t_column<1>(sm, tbd, lane); break;
+    case 2: bad |= t_column<2>(sm, tbd, lane); break;
+    case 3: bad |= t_column<3>(sm, tbd, lane); break;
+    default: break;
   }
   lds_barrier();
 
-  // ---------------- phase 4: W, U, Q', Ou for value / key columns 16w .. 16w+15
+  // ---------------- phase 4: W, U, Qs for value / key columns 16w .. 16w+15
   {
     f16* nw = reinterpret_cast<f16*>(slot + OFF_NW);
-    f16* qp = reinterpret_cast<f16*>(slot + OFF_QP);
+    f16* qs = reinterpret_cast<f16*>(slot + OFF_QS);
     f16* up = reinterpret_cast<f16*>(slot + OFF_UP);
-    f16* op = reinterpret_cast<f16*>(slot + OFF_OP);
     float omax = 0.f;
     const int n = w;
     f16x4 xk[4], xvv[4];
@@ -540,7 +544,7 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
     const float R3[4] = {R2[0] * e2.x, R2[1] * e2.y, R2[2] * e2.z, R2[3] * e2.w};
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      f32x4 aW = zero4(), aU = zero4(), aQ, aO = zero4();
+      f32x4 aW = zero4(), aU = zero4(), aQ;  // aQ: Qs^T [col 4lg+e][tok lc]
       const f16x4 ql = ld4(&sm.Ql[16 * I + lc][16 * n + 4 * lg]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -550,27 +554,22 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
 #pragma unroll
       for (int J = 0; J <= I; ++J) {
         const f16x4 tf = I == J ? sm.frag[S_TD + I][lane] : sm.frag[S_TO + pair6(I, J)][lane];
-        const f16x4 bf = sm.frag[S_BS + tile10(I, J)][lane];
         aW = mfma16(xk[J], tf, aW);   // W^T     [col 4lg+e][tok lc]
         aU = mfma16(xvv[J], tf, aU);  // U^T     [col 4lg+e][tok lc]
-        aQ = mfma16(xk[J], bf, aQ);   // Q'^T    [col 4lg+e][tok lc]
-        aO = mfma16(xvv[J], bf, aO);  // -Ou^T   [col 4lg+e][tok lc]
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        omax = fmaxf(omax, fmaxf(fmaxf(fabsf(aW[e]), fabsf(aU[e])), fmaxf(fabsf(aQ[e]), fabsf(aO[e]))));
+        omax = fmaxf(omax, fmaxf(fmaxf(fabsf(aW[e]), fabsf(aU[e])), fabsf(aQ[e])));
         aW[e] = -aW[e];
-        aO[e] = -aO[e];
       }
       // X[tok 16I+lc][col 16n+4lg+e]: block I, k-step n/2, lane
       // (lg' = 2(n&1) + lg/2, lc), position 4(lg&1)+e
       const int rowoff = ((I * 4 + (n >> 1)) * 64 + 16 * (2 * (n & 1) + (lg >> 1)) + lc) * 8 + 4 * (lg & 1);
       *reinterpret_cast<f16x4*>(nw + rowoff) = h4(aW);
-      *reinterpret_cast<f16x4*>(qp + rowoff) = h4(aQ);
-      // U and Ou in the order one scan lane consumes them (same lane here)
+      *reinterpret_cast<f16x4*>(qs + rowoff) = h4(aQ);
+      // U in the order one scan lane consumes it (same lane here)
       const int laneoff = ((I * NTILE + (n >> 1)) * 64 + lane) * 8 + 4 * (n & 1);
       *reinterpret_cast<f16x4*>(up + laneoff) = h4(aU);
-      *reinterpret_cast<f16x4*>(op + laneoff) = h4(aO);
     }
     bad |= !(omax <= F16_SAFE);
   }
@@ -615,14 +614,16 @@ struct __align__(16) ScanSmem {
 };
 
 // Slot operands of one chunk as one scan thread uses them.  Waves 0-3 form
-// Delta rows 16w.. (m = -W rows, uo = U); waves 4-7 form output rows
-// 16(w-4).. (m = Q' rows, uo = Ou); every wave updates key rows 16w.. .
-// Both kinds run the same instruction stream (transposed products
-// [col][token]); only their operands and the targets of their stores differ.
+// Delta rows 16w.. (m = -W rows); waves 4-7 form output rows 16(w-4)..
+// (m = Qs rows, then As rows against Delta); every wave updates key rows
+// 16w.. .  Both kinds run the same instruction stream (transposed products
+// [col][token]); only their operands and the targets of their stores differ,
+// and each kind skips the one load it has no use for (a wave-uniform branch).
 struct Pre {
-  f16x8 m[4];       // -W or Q' row 16I+lc, key cols 32ks+8lg ..
+  f16x8 m[4];       // -W or Qs row 16I+lc, key cols 32ks+8lg ..
+  f16x8 u;          // U of this lane, [b][e] (Delta waves)
   f16x8 kd[2];      // Kd^T row 16w+lc, tokens 32ks+8lg ..
-  f16x8 uo;         // U / Ou of this lane, [b][e]
+  f16x8 as[2];      // As row 16I+lc, tokens 32ks+8lg .. (output waves)
   float4 gam;       // exp(gamma) of key rows 16w+4lg ..
   int2 flag;        // the eight per-wave bytes of the prep kernel
 };
@@ -683,17 +684,24 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
   auto load_flag = [&](int k, Pre& r) { r.flag = *reinterpret_cast<const int2*>(slot_of(k) + OFF_FLAG); };
   auto load_a = [&](int k, Pre& r) {
     const unsigned char* sl = slot_of(k);
-    const f16* mp = reinterpret_cast<const f16*>(sl + (is_o ? OFF_QP : OFF_NW)) + (I * 4 * 64 + lane) * 8;
-    const f16* uo = reinterpret_cast<const f16*>(sl + (is_o ? OFF_OP : OFF_UP)) + ((I * NTILE + tile) * 64 + lane) * 8;
+    const f16* mp = reinterpret_cast<const f16*>(sl + (is_o ? OFF_QS : OFF_NW)) + (I * 4 * 64 + lane) * 8;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) r.m[ks] = ld8(mp + ks * 64 * 8);
-    r.uo = ld8(uo);
+    if (!is_o) r.u = ld8(reinterpret_cast<const f16*>(sl + OFF_UP) + ((I * NTILE + tile) * 64 + lane) * 8);
+    else r.u = f16x8{};
   };
   auto load_b = [&](int k, Pre& r) {
     const unsigned char* sl = slot_of(k);
     const f16* kd = reinterpret_cast<const f16*>(sl + OFF_KDT) + (w * 2 * 64 + lane) * 8;
+    const f16* as = reinterpret_cast<const f16*>(sl + OFF_AS) + (I * 2 * 64 + lane) * 8;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) r.kd[ks] = ld8(kd + ks * 64 * 8);
+    if (is_o) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) r.as[ks] = ld8(as + ks * 64 * 8);
+    } else {
+      r.as[0] = r.as[1] = f16x8{};
+    }
     r.gam = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl + OFF_GAM) + 16 * w + 4 * lg);
   };
   auto load = [&](int k, Pre& r) {
@@ -744,28 +752,24 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
     const bool sbig = (sm.sbp[0] | sm.sbp[1] | sm.sbp[2] | sm.sbp[3] | sm.sbp[4] | sm.sbp[5] | sm.sbp[6] |
                        sm.sbp[7]) != 0;
 
-    // ---- phase A: Delta^T = U^T + S^T (-W)^T (waves 0-3, into DT) and
-    // O^T = Ou^T + S^T Q'^T (waves 4-7, to out), one instruction stream
+    // ---- phase A: Delta^T = U^T + S^T (-W)^T (waves 0-3, into DT) and the
+    // first part of O^T, S^T Qs^T (waves 4-7, kept), one instruction stream
     f16x8 sf[4][2];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int b = 0; b < 2; ++b) sf[ks][b] = ld8(&sm.ST[16 * b + lc][32 * ks + 8 * lg]);
-    // output rows past the document's end fall outside the resource; the
-    // Delta waves' copy of the store gets an empty resource (dropped)
-    const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(
-        p.out + (tok0 * H + h) * D + col0, is_o ? static_cast<uint32_t>(((nv - 1) * H * D + DVT) * 4) : 0u);
-    const uint32_t ooff = static_cast<uint32_t>(((16 * I + lc) * H * D + 4 * lg) * 4);
     f16* dt = is_o ? &sm.DTX[0][0] : &sm.DT[0][0];
     bool dbig = false;
+    f32x4 oacc[2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       f32x4 acc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = (float)cur.uo[4 * b + e];
+      for (int e = 0; e < 4; ++e) acc[e] = is_o ? 0.f : (float)cur.u[4 * b + e];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) acc = mfma32(sf[ks][b], cur.m[ks], acc);  // [col 4lg+e][tok lc]
-      buffer_store16(acc, orsrc, ooff + 64 * b);
+      oacc[b] = acc;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         dbig |= !(fabsf(acc[e]) <= F16_SAFE);
@@ -781,7 +785,8 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
 
-    // ---- phase B: S = exp(gamma) S + Kd^T Delta (all waves, key rows 16w..)
+    // ---- phase B: S = exp(gamma) S + Kd^T Delta (all waves, key rows 16w..),
+    // then O^T += Delta^T As^T (waves 4-7, to out)
     const bool fbk = pflag != 0 || sbig || (sm.dbp[0] | sm.dbp[1] | sm.dbp[2] | sm.dbp[3]) != 0;
     if (!fbk) {  // workgroup-uniform
       f16x8 dB[2][2];
@@ -797,12 +802,23 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) s[0][b] = mfma32(cur.kd[ks], dB[ks][b], s[0][b]);
       }
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) oacc[b] = mfma32(dB[ks][b], cur.as[ks], oacc[b]);  // [col 4lg+e][tok lc]
       __builtin_amdgcn_sched_barrier(0);
       load_b(kn, cur);
       __builtin_amdgcn_sched_barrier(0);
       write_st(s);
+      // output rows past the document's end fall outside the resource; the
+      // Delta waves' copy of the store gets an empty resource (dropped)
+      const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(
+          p.out + (tok0 * H + h) * D + col0, is_o ? static_cast<uint32_t>(((nv - 1) * H * D + DVT) * 4) : 0u);
+      const uint32_t ooff = static_cast<uint32_t>(((16 * I + lc) * H * D + 4 * lg) * 4);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) buffer_store16(oacc[b], orsrc, ooff + 64 * b);
     } else {
-      // token by token from the entry state; rewrites this chunk's outputs
+      // token by token from the entry state; writes this chunk's outputs
       __syncthreads();
       const State2 r = scan_fallback(sm.fb, State2{s[0][0], s[0][1]}, fa, tok_begin, ntok, k, h, col0);
       s[0][0] = r.s0;

@@ -92,7 +92,7 @@ const char* kda_last_error(void);
 /* Device scratch bytes kda_chunk_fwd needs for this descriptor; packed != 0
  * for a call with cu_seqlens (desc->seq_len = total tokens, num_seqs =
  * documents), 0 for a dense batch.  For bf16 q/k/v with d = 128 the chunked
- * prefill stages fp16 per-chunk operands there: about 81 KiB per 64-token
+ * prefill stages fp16 per-chunk operands there: 73 KiB per 64-token
  * chunk and head (dense: B * ceil(T/64) chunks; packed: ceil(T/64) + N, an
  * upper bound), plus a few bytes per document when packed.  Other
  * configurations need at most a few bytes per document (0 for a dense

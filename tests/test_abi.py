@@ -168,7 +168,7 @@ def test_empty_problems_are_noops():
     assert chunk(desc(seq_len=0), q=None, k=None, v=None, g=None, b=None, out=None) == OK
 
 
-SLOT = 82944  # workspace bytes per (64-token chunk, head) of the bf16 d = 128 prefill
+SLOT = 74752  # workspace bytes per (64-token chunk, head) of the bf16 d = 128 prefill
 
 
 def test_workspace_bytes_dense_and_null():
