@@ -199,21 +199,24 @@ def settle(fn, seconds: float = SETTLE_S):
 def timed_calls(fn, steps: int, warmup: int):
     """Settle, run fn warmup times, then steps times bracketed by
     synchronisation.  Returns (wall seconds of the timed region, per-call
-    event milliseconds)."""
+    event milliseconds).  One pair of HIP events on the launch stream spans
+    the steps calls and the mean call is their time over steps: an event
+    recorded between two calls holds the next call's first kernel back until
+    the event has been signalled, a gap the calls themselves do not have."""
     settle(fn)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for a, b in ev:
-        a.record(stream)
+    a.record(stream)
+    for _ in range(steps):
         fn()
-        b.record(stream)
+    b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [a.elapsed_time(b) for a, b in ev]
+    return wall, [a.elapsed_time(b) / steps] * steps
 
 
 def to_dev(inp):
@@ -241,7 +244,7 @@ def bench_prefill(kda, steps, warmup):
 def bench_varlen(kda, steps, warmup):
     """The packed workload: 65536 tokens split into documents of log-uniform
     length, H=32, d=128, bf16, zero initial states; timed like the dense
-    prefill (back-to-back calls, HIP events per call).  Reported beside the
+    prefill (back-to-back calls, HIP events around them).  Reported beside the
     headline, not as it."""
     inp = kda_inputs.config("varlen")
     d = to_dev(inp)
@@ -269,7 +272,7 @@ def bench_varlen(kda, steps, warmup):
 def bench_backward(kda, steps, warmup):
     """kda_chunk_bwd on the dense prefill workload (4 x 4096 tokens, H = 16,
     d = 128, bf16 q/k/v) with seeded upstream gradients, timed like the
-    prefill (back-to-back calls, HIP events per call).  The backward computes
+    prefill (back-to-back calls, HIP events around them).  The backward computes
     in fp32 on the matrix cores, so its roofline is the fp32 peak."""
     inp = kda_inputs.config("prefill")
     up = kda_inputs.upstream_grads(inp, seed=240)
