@@ -4,8 +4,15 @@ Thin ctypes layer over the C ABI declared in ``include/kda.h``: it checks
 tensor shapes/dtypes/devices, allocates outputs with torch (device memory and
 streams are torch's job), and passes raw device pointers plus torch's current
 HIP stream.  Every step of the computation runs in the HIP kernels of
-``libkda.so``; there is no CPU or PyTorch fallback, and importing this package
-fails if the library has not been built (``python -m gated_delta_rule_67_amd.build``).
+``libkda.so``; there is no CPU or PyTorch fallback.  The library is loaded on
+first use, so the package (and its ``build`` module) imports before it is
+built; any call then raises ``ImportError`` until ``libkda.so`` exists
+(``python -m gated_delta_rule_67_amd.build``).
+
+Outputs and workspaces this module allocates are allocated on the stream the
+kernels run on (``stream``, else torch's current stream), so torch's caching
+allocator never hands their memory to another stream while the kernels still
+use it.
 
     out, final_state = chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None)
     out = step(q, k, v, log_g, beta, state)        # state updated in place
@@ -18,7 +25,9 @@ NeMo glm5_next.layers; q/k/v/g are [batch, seq, heads, head_dim], beta is
 from __future__ import annotations
 
 import ctypes
+import functools
 import os
+import threading
 
 import torch
 
@@ -81,16 +90,34 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
-lib = _load()
+_LIB = None
+_LIB_LOCK = threading.Lock()
+
+
+def _lib() -> ctypes.CDLL:
+    """The loaded libkda.so (loaded once, on first use)."""
+    global _LIB
+    if _LIB is None:
+        with _LIB_LOCK:
+            if _LIB is None:
+                _LIB = _load()
+    return _LIB
+
+
+def __getattr__(name):
+    # ``gated_delta_rule_67_amd.lib``: the ctypes handle, loaded on first access
+    if name == "lib":
+        return _lib()
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")
 
 
 def abi_version() -> int:
-    return lib.kda_abi_version()
+    return _lib().kda_abi_version()
 
 
 def _check(status: int):
     if status != 0:
-        raise KdaError(status, lib.kda_last_error().decode())
+        raise KdaError(status, _lib().kda_last_error().decode())
 
 
 def _ptr(t):
@@ -121,6 +148,21 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _allocates_on_launch_stream(fn):
+    """Run ``fn`` with ``stream`` (when one is given) as torch's current
+    stream, so the outputs and the workspace it allocates belong to the stream
+    its kernels are enqueued on.  A workspace dropped on return then goes back
+    to that stream's pool, where later allocations are ordered after the
+    kernels that still use it."""
+    @functools.wraps(fn)
+    def wrapper(*args, stream=None, **kwargs):
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, stream=stream, **kwargs)
+    return wrapper
+
+
 def make_desc(num_seqs, seq_len, H, dk, dv, qkv_dtype, scale=None, workspace=None) -> KdaDesc:
     d = KdaDesc()
     d.num_seqs, d.seq_len, d.num_heads, d.dk, d.dv = num_seqs, seq_len, H, dk, dv
@@ -135,9 +177,10 @@ def workspace_bytes(num_seqs: int, seq_len: int, H: int, d: int, packed: bool,
                     qkv_dtype: int = KDA_BF16) -> int:
     """Device scratch bytes of a chunk_fwd call (see kda_chunk_workspace_bytes)."""
     desc = make_desc(num_seqs, seq_len, H, d, d, qkv_dtype)
-    return lib.kda_chunk_workspace_bytes(ctypes.byref(desc), int(packed))
+    return _lib().kda_chunk_workspace_bytes(ctypes.byref(desc), int(packed))
 
 
+@_allocates_on_launch_stream
 def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None,
               out=None, final_state=None, workspace=None, stream=None):
     """Chunked prefill.  Returns (out [B,T,H,dv] fp32, final_state [N,H,dk,dv] fp32).
@@ -177,12 +220,12 @@ def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None
     else:
         _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
     desc = make_desc(N, L, H, dk, dv, code, scale)
-    need = lib.kda_chunk_workspace_bytes(ctypes.byref(desc), int(cu_seqlens is not None))
+    need = _lib().kda_chunk_workspace_bytes(ctypes.byref(desc), int(cu_seqlens is not None))
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         desc.workspace, desc.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(lib.kda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
+    _check(_lib().kda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
                              _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
                              _stream(stream)))
     return out, final_state
@@ -191,9 +234,10 @@ def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None
 def bwd_workspace_bytes(num_seqs: int, seq_len: int, H: int, d: int, packed: bool) -> int:
     """Device scratch bytes of a chunk_bwd call (see kda_chunk_bwd_workspace_bytes)."""
     desc = make_desc(num_seqs, seq_len, H, d, d, KDA_BF16)
-    return lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(desc), int(packed))
+    return _lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(desc), int(packed))
 
 
+@_allocates_on_launch_stream
 def chunk_bwd(q, k, v, log_g, beta, d_out, init_state=None, cu_seqlens=None, d_final=None, scale=None,
               grads=None, d_init_state=True, workspace=None, stream=None):
     """Reverse mode of ``chunk_fwd``: gradients of sum(d_out * out) +
@@ -237,18 +281,19 @@ def chunk_bwd(q, k, v, log_g, beta, d_out, init_state=None, cu_seqlens=None, d_f
         else:
             _need(g[name], name, shp, torch.float32, dev)
     desc = make_desc(N, L, H, dk, dv, code, scale)
-    need = lib.kda_chunk_bwd_workspace_bytes(ctypes.byref(desc), int(cu_seqlens is not None))
+    need = _lib().kda_chunk_bwd_workspace_bytes(ctypes.byref(desc), int(cu_seqlens is not None))
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
         desc.workspace, desc.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
-    _check(lib.kda_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
+    _check(_lib().kda_chunk_bwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
                              _ptr(init_state), _ptr(cu_seqlens), _ptr(d_out), _ptr(d_final), _ptr(g["dq"]),
                              _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dlog_g"]), _ptr(g["dbeta"]),
                              _ptr(g["d_init_state"]), _stream(stream)))
     return g
 
 
+@_allocates_on_launch_stream
 def short_conv(x, weight, cu_seqlens=None, init_cache=None, activation=0, out=None, final_cache=None,
                stream=None):
     """Short causal depthwise convolution of x [B, T, channels] (fp32 or bf16)
@@ -285,11 +330,12 @@ def short_conv(x, weight, cu_seqlens=None, init_cache=None, activation=0, out=No
     desc = make_desc(N, L, 1, 16, 16, code)
     fc = final_cache if (final_cache is not None and final_cache.numel() > 0) else None
     ic = init_cache if (init_cache is not None and init_cache.numel() > 0) else None
-    _check(lib.kda_short_conv(ctypes.byref(desc), Cn, K, int(activation), _ptr(x), _ptr(weight), _ptr(cu_seqlens),
+    _check(_lib().kda_short_conv(ctypes.byref(desc), Cn, K, int(activation), _ptr(x), _ptr(weight), _ptr(cu_seqlens),
                               _ptr(ic), _ptr(out), _ptr(fc), _stream(stream)))
     return out, final_cache
 
 
+@_allocates_on_launch_stream
 def gated_rmsnorm(o, gate, weight, eps, out=None, out_dtype=torch.bfloat16, stream=None):
     """Gated per-head RMSNorm of the mixer output o [B, T, H, D] (fp32) with
     ``gate`` like o (fp32 or bf16) and ``weight`` [D] (fp32):
@@ -308,11 +354,12 @@ def gated_rmsnorm(o, gate, weight, eps, out=None, out_dtype=torch.bfloat16, stre
         _need(out, "out", (B, T, H, D), out.dtype, dev)
     desc = make_desc(B, T, H, D, D, g_code)
     desc.out_dtype = _dtype_code(out)
-    _check(lib.kda_gated_rmsnorm(ctypes.byref(desc), _ptr(o), _ptr(gate), _ptr(weight), ctypes.c_float(eps),
+    _check(_lib().kda_gated_rmsnorm(ctypes.byref(desc), _ptr(o), _ptr(gate), _ptr(weight), ctypes.c_float(eps),
                                  _ptr(out), _stream(stream)))
     return out
 
 
+@_allocates_on_launch_stream
 def step(q, k, v, log_g, beta, state, scale=None, out=None, stream=None):
     """Decode (n_tok = 1) or multi-row verify: rows [N, n_tok, H, d] applied in
     order to ``state`` [N, H, dk, dv] (fp32), which is updated in place.
@@ -331,11 +378,12 @@ def step(q, k, v, log_g, beta, state, scale=None, out=None, stream=None):
     else:
         _need(out, "out", (N, n_tok, H, dv), torch.float32, dev)
     desc = make_desc(N, n_tok, H, dk, dv, code, scale)
-    _check(lib.kda_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
+    _check(_lib().kda_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
                         _ptr(state), ctypes.c_int32(n_tok), _ptr(out), _stream(stream)))
     return out
 
 
+@_allocates_on_launch_stream
 def step_rows(q, k, v, log_g, beta, state, scale=None, out=None, deltas=None, stream=None):
     """Speculative verify, first half: the outputs of rows [N, n_tok, H, d] as
     ``step`` would give them, with ``state`` left unchanged.  Returns (out,
@@ -358,7 +406,7 @@ def step_rows(q, k, v, log_g, beta, state, scale=None, out=None, deltas=None, st
     else:
         _need(deltas, "deltas", (N, n_tok, H, dv), torch.float32, dev)
     desc = make_desc(N, n_tok, H, dk, dv, code, scale)
-    _check(lib.kda_step_rows(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
+    _check(_lib().kda_step_rows(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
                              _ptr(state), ctypes.c_int32(n_tok), _ptr(out), _ptr(deltas), _stream(stream)))
     return out, deltas
 
@@ -376,5 +424,5 @@ def step_commit(k, log_g, deltas, state, accept, stream=None):
     _need(state, "state", (N, H, dk, dv), torch.float32, dev)
     _need(accept, "accept", (N,), torch.int32, dev)
     desc = make_desc(N, n_tok, H, dk, dv, code, None)
-    _check(lib.kda_step_commit(ctypes.byref(desc), _ptr(k), _ptr(log_g), _ptr(deltas), _ptr(accept),
+    _check(_lib().kda_step_commit(ctypes.byref(desc), _ptr(k), _ptr(log_g), _ptr(deltas), _ptr(accept),
                                _ptr(state), ctypes.c_int32(n_tok), _stream(stream)))

@@ -28,29 +28,22 @@ kda_status fail(kda_status st, const char* fmt, ...) {
   return st;
 }
 
-// Prefill path.  bf16 q/k/v with d = 128 run chunked on MFMA: by default in
-// two passes (parallel per-chunk preparation, then the serial state scan);
-// KDA_PREFILL_PATH=fused selects the single-pass fused kernel instead,
-// KDA_PREFILL_PATH=recurrent forces the token-recurrent kernel (any dtype / d),
-// and unset or =twopass keeps the default.
-enum class Path { Recurrent, Fused, TwoPass };
+// Prefill path.  bf16 q/k/v with d = 128 run chunked on MFMA in two passes
+// (parallel per-chunk preparation, then the serial state scan); everything
+// else runs the token-recurrent kernel.  KDA_PREFILL_PATH=recurrent forces the
+// token-recurrent kernel for any problem (a test and diagnosis switch).
+enum class Path { Recurrent, TwoPass };
 
 Path prefill_path(const kda::ChunkLaunch& a) {
   const char* e = std::getenv("KDA_PREFILL_PATH");
   if (e && std::strcmp(e, "recurrent") == 0) return Path::Recurrent;
-  if (e && std::strcmp(e, "fused") == 0 && kda::chunk_mfma_supported(a)) return Path::Fused;
   if (kda::twopass_supported(a)) return Path::TwoPass;
-  if (kda::chunk_mfma_supported(a)) return Path::Fused;
   return Path::Recurrent;
 }
 
 size_t workspace_need(Path path, const kda::ChunkLaunch& a) {
   const bool packed = a.cu_seqlens != nullptr;
-  switch (path) {
-    case Path::TwoPass: return kda::twopass_workspace_bytes(a.num_seqs, a.seq_len, a.num_heads, packed);
-    case Path::Fused: return kda::chunk_workspace_bytes(a.num_seqs, packed);
-    default: return 0;
-  }
+  return path == Path::TwoPass ? kda::twopass_workspace_bytes(a.num_seqs, a.seq_len, a.num_heads, packed) : 0;
 }
 
 // The launch record of a descriptor (pointers left empty; cu_seqlens only
@@ -194,9 +187,7 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
   a.workspace = ws_need > 0 ? d->workspace : nullptr;
   a.scale = resolve_scale(d);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = path == Path::TwoPass ? kda::launch_chunk_twopass(a, s)
-                       : path == Path::Fused ? kda::launch_chunk_mfma(a, s)
-                                             : kda::launch_chunk_recurrent(a, s);
+  const hipError_t e = path == Path::TwoPass ? kda::launch_chunk_twopass(a, s) : kda::launch_chunk_recurrent(a, s);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
   return KDA_OK;
 }

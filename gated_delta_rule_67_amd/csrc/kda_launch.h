@@ -64,12 +64,6 @@ hipError_t launch_commit(const CommitLaunch& a, hipStream_t stream);
 // Prefill through the token-recurrent kernel (any dtype / d).  No workspace.
 hipError_t launch_chunk_recurrent(const ChunkLaunch& a, hipStream_t stream);
 
-// Prefill through the fused single-pass chunked MFMA kernel (bf16 q/k/v, d = 128).
-hipError_t launch_chunk_mfma(const ChunkLaunch& a, hipStream_t stream);
-bool chunk_mfma_supported(const ChunkLaunch& a);
-// Its workspace: the longest-first document order of a packed problem.
-size_t chunk_workspace_bytes(int n_docs, bool packed);
-
 // Prefill in two passes: per-chunk preparation over all chunks at once, then
 // the serial state scan (bf16 q/k/v, d = 128).
 hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream);

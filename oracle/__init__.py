@@ -10,7 +10,8 @@ The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, libm ``exp``): the
 token loop of the gated delta rule as printed in the GLM-5.3-Flash model notes
 (Glm5NextTextLinearAttention snippet), with the output read from the updated
 state, and packed documents reset at their boundaries (NeMo glm5_next.layers,
-``_torch_recurrent_kda``); its reverse mode, the same loop differentiated
+``_torch_recurrent_kda``), optionally on L2-normalised query and key rows
+(``qk_l2norm``); its reverse mode, the same loop differentiated
 token by token (that page documents the recurrence as differentiable); and the
 short causal depthwise convolution that feeds q, k and v
 (``_TorchShortConvolution``); and the gated per-head RMSNorm on the output
@@ -56,6 +57,8 @@ def load(path: str = LIB_PATH):
     lib.kda_oracle_short_conv.argtypes = [i64, i64, i64, i64, dp, dp, ip, dp, ctypes.c_int, dp, dp, ctypes.c_int]
     lib.kda_oracle_gated_rmsnorm.restype = ctypes.c_int
     lib.kda_oracle_gated_rmsnorm.argtypes = [i64, i64, dp, dp, dp, ctypes.c_double, dp]
+    lib.kda_oracle_qk_l2norm.restype = ctypes.c_int
+    lib.kda_oracle_qk_l2norm.argtypes = [i64, i64, ctypes.c_double, dp, dp, dp, dp]
     lib.kda_oracle_threads.restype = ctypes.c_int
     lib.kda_oracle_threads.argtypes = [ctypes.c_int]
     return lib
@@ -82,18 +85,39 @@ def threads(n_threads: int = 0) -> int:
     return _get_lib().kda_oracle_threads(n_threads)
 
 
+QK_L2_EPS = 1e-6  # eps inside the root of the optional q / k L2 normalisation
+
+
+def qk_l2norm(q, k, eps: float = QK_L2_EPS, lib=None):
+    """Each (token, head) row of q and of k divided by sqrt(sum of squares +
+    eps).  q, k: [..., D].  Returns (qn, kn) in float64."""
+    lib = lib or _get_lib()
+    q, k = _f64(q), _f64(k)
+    assert q.shape == k.shape
+    D = q.shape[-1]
+    qn, kn = np.zeros(q.shape), np.zeros(k.shape)
+    rc = lib.kda_oracle_qk_l2norm(q.size // D, D, float(eps), _ptr(q), _ptr(k), _ptr(qn), _ptr(kn))
+    if rc != 0:
+        raise ValueError(f"kda_oracle_qk_l2norm failed with code {rc}")
+    return qn, kn
+
+
 def kda_forward(q, k, v, log_g, beta, init_state=None, cu_seqlens=None,
-                scale=None, n_threads: int = 0, lib=None):
+                scale=None, n_threads: int = 0, lib=None, qk_l2norm_eps=None):
     """Run the token-loop recurrence.
 
     q, k, log_g: [B, T, H, dk]; v: [B, T, H, dv]; beta: [B, T, H].
     Dense: B independent sequences.  Packed: B == 1 and ``cu_seqlens`` [N+1]
     splits the row into N documents, each starting from its own initial state.
     init_state: [N, H, dk, dv] or None (zeros).  scale defaults to dk**-0.5.
+    ``qk_l2norm_eps`` (a float) first L2-normalises every row of q and k
+    (:func:`qk_l2norm`); None leaves them as given.
     Returns (out [B, T, H, dv], final_state [N, H, dk, dv]) in float64.
     """
     lib = lib or _get_lib()
     q, k, v, log_g, beta = (_f64(x) for x in (q, k, v, log_g, beta))
+    if qk_l2norm_eps is not None:
+        q, k = qk_l2norm(q, k, qk_l2norm_eps, lib=lib)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     assert k.shape == q.shape and log_g.shape == q.shape
@@ -120,7 +144,7 @@ def kda_forward(q, k, v, log_g, beta, init_state=None, cu_seqlens=None,
     return out, fin
 
 
-def kda_step(q, k, v, log_g, beta, state, scale=None, n_threads: int = 0):
+def kda_step(q, k, v, log_g, beta, state, scale=None, n_threads: int = 0, qk_l2norm_eps=None):
     """Decode / verify: n_tok rows per sequence applied in order from ``state``.
 
     Rows are [N, n_tok, H, d]; row t of a sequence is applied after rows < t
@@ -128,7 +152,7 @@ def kda_step(q, k, v, log_g, beta, state, scale=None, n_threads: int = 0):
     (out [N, n_tok, H, dv], new_state [N, H, dk, dv]); ``state`` is not modified.
     """
     return kda_forward(q, k, v, log_g, beta, init_state=state, scale=scale,
-                       n_threads=n_threads)
+                       n_threads=n_threads, qk_l2norm_eps=qk_l2norm_eps)
 
 
 def kda_backward(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None,

@@ -348,6 +348,25 @@ int kda_oracle_gated_rmsnorm(int64_t rows, int64_t D, const double* o, const dou
   return 0;
 }
 
+/* One row divided by its L2 norm, eps inside the root. */
+static void l2norm_row(int64_t D, double eps, const double* x, double* y) {
+  double ss = 0.0;
+  for (int64_t i = 0; i < D; ++i) ss += x[i] * x[i];
+  const double inv = 1.0 / sqrt(ss + eps);
+  for (int64_t i = 0; i < D; ++i) y[i] = x[i] * inv;
+}
+
+int kda_oracle_qk_l2norm(int64_t rows, int64_t D, double eps, const double* q, const double* k,
+                         double* qn, double* kn) {
+  if (!q || !k || !qn || !kn) return -1;
+  if (rows < 0 || D <= 0 || !(eps >= 0.0)) return -2;
+  for (int64_t r = 0; r < rows; ++r) {
+    l2norm_row(D, eps, q + r * D, qn + r * D);
+    l2norm_row(D, eps, k + r * D, kn + r * D);
+  }
+  return 0;
+}
+
 int kda_oracle_threads(int n_threads) {
 #ifdef _OPENMP
   return n_threads > 0 ? n_threads : omp_get_max_threads();

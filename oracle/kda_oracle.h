@@ -108,6 +108,18 @@ int kda_oracle_gated_rmsnorm(int64_t rows, int64_t D, const double* o, const dou
                              const double* w, double eps, double* y);
 
 /* Number of OpenMP threads a call with n_threads would use. */
+/* L2 normalisation of the query and key rows, the optional first step of the
+ * mixer (the pages do not print it; the reading taken is the plain one: each
+ * row of head_dim D, one token of one head, divided by its Euclidean norm
+ * with eps inside the root):
+ *
+ *     qn[r, i] = q[r, i] / sqrt(sum_i q[r, :]^2 + eps),   kn likewise from k
+ *
+ * q, k, qn, kn: [rows, D].  The recurrence then runs on (qn, kn) unchanged.
+ * Returns 0, or -1 NULL pointer / -2 bad size. */
+int kda_oracle_qk_l2norm(int64_t rows, int64_t D, double eps, const double* q, const double* k,
+                         double* qn, double* kn);
+
 int kda_oracle_threads(int n_threads);
 
 #ifdef __cplusplus

@@ -149,16 +149,18 @@ def test_full_size_dense_workload_sampled_units():
 def test_full_size_packed_workload_sampled_units():
     """The packed 65536-token, 32-head workload (26 documents, log-uniform
     lengths 64..16384, zero initial states) at full size; the oracle checks
-    every gradient of sampled (document, head) units: the two shortest
-    documents, a mid-length one, and the first document at another head."""
+    every gradient of sampled (document, head) units: the longest document
+    (214 chunks of serial scan in each direction) at two heads, the two
+    shortest documents, a mid-length one, and the first document at another
+    head."""
     inp = kda_inputs.config("varlen")
     up = kda_inputs.upstream_grads(inp, seed=250)
     got = gpu_bwd(inp, up)
     cu = inp["cu_seqlens"].numpy().astype(np.int64)
     lens = np.diff(cu)
     order = np.argsort(lens)
-    docs = [int(order[0]), int(order[1]), int(order[len(order) // 2])]
-    for n, h in [(docs[0], 0), (docs[1], 17), (docs[2], 31), (0, 5)]:
+    docs = [int(order[0]), int(order[1]), int(order[len(order) // 2]), int(order[-1])]
+    for n, h in [(docs[3], 0), (docs[3], 29), (docs[0], 0), (docs[1], 17), (docs[2], 31), (0, 5)]:
         a, e = int(cu[n]), int(cu[n + 1])
         sl = lambda t: t[:, a:e, h:h + 1]
         unit = dict(q=sl(inp["q"]), k=sl(inp["k"]), v=sl(inp["v"]), log_g=sl(inp["log_g"]),

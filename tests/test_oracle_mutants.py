@@ -5,7 +5,8 @@ term, a wrong sign, a wrong index or axis, a transposed operand, a missing
 reset, a wrong step order), compiled to a temporary library and run against
 ``test_oracle_pins.py`` (forward mutants), ``test_oracle_bwd_pins.py``
 (reverse-mode mutants), ``test_oracle_conv_pins.py`` (convolution mutants) or
-``test_oracle_norm_pins.py`` (norm mutants) in a subprocess (a mutant may read out of bounds, so it
+``test_oracle_norm_pins.py`` (norm mutants) or ``test_oracle_l2_pins.py``
+(q / k normalisation mutants) in a subprocess (a mutant may read out of bounds, so it
 never runs in this process).  The committed oracle is never modified.
 """
 import os
@@ -102,6 +103,22 @@ NORM_MUTANTS = {
 }
 
 
+# planted mistakes in the q / k L2 normalisation
+L2_MUTANTS = {
+    "l2_eps_outside_sqrt": ("static void l2norm_row(", "const double inv = 1.0 / sqrt(ss + eps);",
+                            "const double inv = 1.0 / (sqrt(ss) + eps);"),
+    "l2_no_sqrt": ("static void l2norm_row(", "const double inv = 1.0 / sqrt(ss + eps);",
+                   "const double inv = 1.0 / (ss + eps);"),
+    "l2_abs_not_square": ("static void l2norm_row(", "ss += x[i] * x[i];", "ss += fabs(x[i]);"),
+    "l2_q_left_as_is": ("int kda_oracle_qk_l2norm(", "l2norm_row(D, eps, q + r * D, qn + r * D);",
+                        "for (int64_t i = 0; i < D; ++i) qn[r * D + i] = q[r * D + i];"),
+    "l2_k_from_q": ("int kda_oracle_qk_l2norm(", "l2norm_row(D, eps, k + r * D, kn + r * D);",
+                    "l2norm_row(D, eps, q + r * D, kn + r * D);"),
+    "l2_first_row_only": ("int kda_oracle_qk_l2norm(", "for (int64_t r = 0; r < rows; ++r) {",
+                          "for (int64_t r = 0; r < (rows > 0); ++r) {"),
+}
+
+
 def _mutate_in(src, func, old, new, name):
     """Replace `old` by `new` inside the body of the C function starting with
     `func` (up to the next top-level closing brace); `old` must occur exactly
@@ -159,7 +176,7 @@ def _build(workdir, name, src_text):
 def test_unmutated_copy_passes(workdir):
     lib = _build(workdir, "clean", open(SRC).read())
     for pins in ("test_oracle_pins.py", "test_oracle_bwd_pins.py", "test_oracle_conv_pins.py",
-                 "test_oracle_norm_pins.py"):
+                 "test_oracle_norm_pins.py", "test_oracle_l2_pins.py"):
         rc, out = _run_pins(lib, pins)
         assert rc == 0, out
 
@@ -205,3 +222,12 @@ def test_norm_mutant_is_caught(workdir, name):
     mutated = _mutate_in(src, "int kda_oracle_gated_rmsnorm(", old, new, name)
     rc, out = _run_pins(_build(workdir, name, mutated), "test_oracle_norm_pins.py")
     assert rc != 0, f"mutant {name} survived the norm pins:\n{out}"
+
+
+@pytest.mark.parametrize("name", sorted(L2_MUTANTS))
+def test_l2_mutant_is_caught(workdir, name):
+    src = open(SRC).read()
+    func, old, new = L2_MUTANTS[name]
+    mutated = _mutate_in(src, func, old, new, name)
+    rc, out = _run_pins(_build(workdir, name, mutated), "test_oracle_l2_pins.py")
+    assert rc != 0, f"mutant {name} survived the L2 normalisation pins:\n{out}"
