@@ -1,43 +1,46 @@
 """Benchmark of libkda on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-    python bench.py --only {prefill,varlen,step,backward,conv,norm,copy}      (profiling runs)
-    python bench.py [--traffic-kind {prefill,backward}] --traffic-from FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+    python bench.py --only {prefill,varlen,step,backward,conv,norm,strong,copy,peak}   (profiling runs)
+    python bench.py [--traffic-kind KIND] --traffic-from FETCH_DIR WRITE_DIR COPY_FETCH_DIR COPY_WRITE_DIR
+    python bench.py --mfma-from SQ_DIR                                      (MFMA counter summary)
 
-A step is one kda_chunk_fwd call (chunked prefill) over the dense workload
-B=4 x T=4096 tokens, H=16 heads, dk=dv=128, bf16 q/k/v, fp32 gates/beta/state,
-fp32 out, with inputs resident in HBM.  ``value`` is prefill tokens/s
-(tokens of the 16-head mixer per second).  The same JSON line carries:
-  roofline      prefill kernel: algorithmic bytes per launch / mean launch time
-                (HIP events on the launch stream) against 8 TB/s HBM
-  mfma          algorithmic prefill FLOP/s against the 2516.6 TFLOP/s dense
-                16-bit MFMA peak
-  varlen        the packed 65536-token, 32-head prefill: tokens/s and its own
-                HBM roofline (beside the headline, not part of it)
-  gated_rmsnorm kda_gated_rmsnorm on the dense workload's output (fp32 o,
-                bf16 gate and out): its own HBM roofline
-  short_conv    kda_short_conv over q, k, v of the dense workload (6144
-                channels, width 4, bf16): its own HBM roofline
-  backward      kda_chunk_bwd on the dense workload: tokens/s and its roofline
-                against the 157.3 TFLOP/s fp32 peak (it computes in fp32)
-  verify_rollback  the 64 x 4-row verify split into kda_step_rows (state read
-                only) and kda_step_commit, each with its own HBM roofline
-  decode/verify kda_step GB/s on 256 x 1 and 64 x 4 rows, H=32, d=128, each
-                with its own roofline (state read + write + row traffic)
-  cpu_baseline  the fp64 oracle timed on the host on a bounded sample of the
-                same prefill workload
+A step is one kda_chunk_fwd call (chunked prefill) over the packed workload:
+one row of 65536 tokens split into 26 documents of log-uniform length
+(64..16384), H=32 heads, dk=dv=128, bf16 q/k/v, fp32 gates/beta, zero initial
+states, fp32 out and final states, inputs resident in HBM.  ``value`` is its
+tokens/s over exactly K back-to-back calls (wall clock between two
+synchronisations).  The same JSON line carries:
+  roofline      that call: algorithmic bytes per call / mean call time (one
+                HIP event pair on the launch stream around the K calls)
+                against 8 TB/s HBM, with the counter-measured traffic
+  flushed       the same call timed one by one after a 1 GiB read that evicts
+                the last-level cache: median / p10 / p90 over 100 calls
+  mfma          algorithmic FLOP/s against the 2516.6 TFLOP/s dense 16-bit
+                MFMA peak, and the counter-measured MFMA busy fraction
+  dense_prefill the dense 4 x 4096-token, 16-head prefill, timed the same ways
+  strong_gates  the dense workload with stronger gates (log_g scale 1.0 and
+                log_g ~ U[-5, 0]): tokens/s and the fraction of chunks that
+                take the exact per-token fallback instead of the MFMA path
+  decode/verify kda_step on 256 x 1 and 64 x 4 rows, H=32, d=128, each with
+                its own HBM roofline (state read + write + row traffic)
+  verify_rollback  the 64 x 4-row verify split into kda_step_rows and
+                kda_step_commit, each with its own HBM roofline
+  backward      kda_chunk_bwd on the dense workload (fp32 matrix-core roofline)
+  short_conv, gated_rmsnorm   the two elementwise kernels' HBM rooflines
+  peaks         this GPU's re-measured peaks: a plain 1 GiB device copy (GB/s)
+                and a dense fp16 MFMA loop (TFLOP/s), against which the
+                rooflines above can also be read
+  cpu_baseline  the fp64 oracle timed on the host on a bounded sample
 Every timed region follows SETTLE_S seconds of the same workload run back to
 back (untimed), then the W warm-up steps: the GPU's clocks need some 30 ms
 of sustained load to reach their steady state.
 Only one GPU is used; --gpus above 1 exits with a message.
 
-roofline.traffic is the HBM bytes of one prefill call measured with rocprofv3
-counters (FETCH_SIZE, WRITE_SIZE; one pass each), scaled by what the same
-counters read for a plain copy of known size (--only copy).  --traffic-from
-turns those four runs' CSV output into profiles/traffic_prefill_dense.txt
-(--traffic-kind backward: profiles/traffic_backward_dense.txt, for the
-backward's roofline), stamped with a hash of the kernel sources; the figure is
-reported only while the sources still hash the same (else null).
+Counter summaries under profiles/ (HBM traffic from FETCH_SIZE / WRITE_SIZE,
+scaled by what the same counters read for a plain copy of known size; MFMA
+busy cycles) are stamped with a hash of the kernel sources and reported only
+while the sources still hash the same (else null).
 """
 from __future__ import annotations
 
@@ -67,6 +70,10 @@ COPY_BYTES = 512 << 20         # calibration copy: bytes read (= bytes written)
 # file, the sources that define its kernels (their code, not the ABI around
 # them), the kernels summed, and the workload the counters were taken on.
 TRAFFIC = {
+    "varlen": dict(file=os.path.join(ROOT, "profiles", "traffic_prefill_packed.txt"),
+                   sources=["kda_twopass.hip", "kda_common.h", "kda_fallback.h"],
+                   kernels=("prep_kernel", "scan_kernel"),
+                   what="one kda_chunk_fwd call, packed 65536 tokens in 26 documents, 32 heads, d = 128, bf16"),
     "prefill": dict(file=os.path.join(ROOT, "profiles", "traffic_prefill_dense.txt"),
                     sources=["kda_twopass.hip", "kda_common.h", "kda_fallback.h"],
                     kernels=("prep_kernel", "scan_kernel"),
@@ -76,8 +83,7 @@ TRAFFIC = {
                      kernels=("bwd_prep", "bwd_fscan", "bwd_rscan", "bwd_gstate", "bwd_gpairs"),
                      what="one kda_chunk_bwd call, dense 4 x 4096 tokens, 16 heads, d = 128, bf16"),
 }
-TRAFFIC_FILE = TRAFFIC["prefill"]["file"]
-KERNEL_SOURCES = TRAFFIC["prefill"]["sources"]
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_prefill_packed.txt")
 
 
 def sources_hash(kind: str = "prefill") -> str:
@@ -198,11 +204,11 @@ def settle(fn, seconds: float = SETTLE_S):
 
 def timed_calls(fn, steps: int, warmup: int):
     """Settle, run fn warmup times, then steps times bracketed by
-    synchronisation.  Returns (wall seconds of the timed region, per-call
-    event milliseconds).  One pair of HIP events on the launch stream spans
-    the steps calls and the mean call is their time over steps: an event
-    recorded between two calls holds the next call's first kernel back until
-    the event has been signalled, a gap the calls themselves do not have."""
+    synchronisation.  Returns (wall seconds of the timed region, mean event
+    milliseconds per call).  One pair of HIP events on the launch stream spans
+    the steps calls: an event recorded between two calls holds the next
+    call's first kernel back until the event has been signalled, a gap the
+    calls themselves do not have."""
     settle(fn)
     for _ in range(warmup):
         fn()
@@ -216,7 +222,50 @@ def timed_calls(fn, steps: int, warmup: int):
     b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return wall, [a.elapsed_time(b) / steps] * steps
+    return wall, a.elapsed_time(b) / steps
+
+
+class CacheFlush:
+    """Reads a 1 GiB buffer: the lines it leaves in the 256 MB last-level
+    cache are clean, so the next call neither hits on its own inputs nor pays
+    a write-back."""
+
+    def __init__(self):
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        torch.sum(self.buf, dim=0, out=self.sink)
+
+
+def flushed_calls(fn, n: int, flush: CacheFlush):
+    """fn timed n times one by one with HIP events on the launch stream, the
+    cache flushed before each call.  Returns the per-call milliseconds."""
+    def one():
+        flush()
+        fn()
+    settle(one)
+    stream = torch.cuda.current_stream()
+    ms = []
+    for _ in range(n):
+        flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        ms.append(a.elapsed_time(b))
+    return ms
+
+
+def spread(ms, back_to_back_ms=None):
+    """median / p10 / p90 of per-call milliseconds, in microseconds."""
+    x = np.asarray(ms, dtype=np.float64) * 1e3
+    r = {"n": int(x.size), "median_us": round(float(np.median(x)), 2),
+         "p10_us": round(float(np.percentile(x, 10)), 2), "p90_us": round(float(np.percentile(x, 90)), 2)}
+    if back_to_back_ms is not None:
+        r["back_to_back_mean_us"] = round(back_to_back_ms * 1e3, 2)
+    return r
 
 
 def to_dev(inp):
@@ -224,49 +273,89 @@ def to_dev(inp):
             for k in ("q", "k", "v", "log_g", "beta", "init_state", "cu_seqlens")}
 
 
-def bench_prefill(kda, steps, warmup):
-    inp = kda_inputs.config("prefill")
+def hbm_roofline(nbytes: int, ms: float, traffic=None, **extra):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    r.update(extra)
+    return r
+
+
+def bench_prefill_workload(kda, name, steps, warmup, flush, n_flushed=100, **overrides):
+    """One prefill workload (dense or packed, kda_inputs config ``name``): K
+    back-to-back calls (wall clock and one event pair), then ``n_flushed``
+    calls one by one after a cache flush."""
+    inp = kda_inputs.config(name, **overrides)
     d = to_dev(inp)
     B, T, H, D = inp["q"].shape
+    packed = d["cu_seqlens"] is not None
+    N = d["cu_seqlens"].numel() - 1 if packed else B
     out = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
-    fin = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    fin = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+    ws = torch.empty(kda.workspace_bytes(N, T, H, D, packed=packed), dtype=torch.uint8, device="cuda")
 
     def call():
         kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_g"], d["beta"], init_state=d["init_state"],
-                      out=out, final_state=fin)
+                      cu_seqlens=d["cu_seqlens"], out=out, final_state=fin, workspace=ws)
 
-    wall, ms = timed_calls(call, steps, warmup)
+    wall, mean_ms = timed_calls(call, steps, warmup)
+    flushed = flushed_calls(call, n_flushed, flush) if n_flushed else None
     tokens = B * T
-    return dict(inp=inp, wall=wall, ms=ms, tokens=tokens, H=H, D=D,
-                bytes=prefill_bytes(tokens, H, D, n_states=B), flops=prefill_flops(tokens, H, D))
+    n_states = N if inp["init_state"] is not None else 0
+    nbytes = prefill_bytes(tokens, H, D, n_states=n_states) + N * H * D * D * 4 * (n_states == 0)
+    return dict(inp=inp, wall=wall, mean_ms=mean_ms, flushed=flushed, tokens=tokens, N=N, H=H, D=D,
+                packed=packed, bytes=nbytes, flops=prefill_flops(tokens, H, D), ws_bytes=int(ws.numel()),
+                call=call, d=d)
 
 
-def bench_varlen(kda, steps, warmup):
-    """The packed workload: 65536 tokens split into documents of log-uniform
-    length, H=32, d=128, bf16, zero initial states; timed like the dense
-    prefill (back-to-back calls, HIP events around them).  Reported beside the
-    headline, not as it."""
-    inp = kda_inputs.config("varlen")
-    d = to_dev(inp)
-    B, T, H, D = inp["q"].shape
-    N = d["cu_seqlens"].numel() - 1
-    out = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
-    fin = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+def prefill_summary(p, steps, traffic=None, kernel=None):
+    """The reported object of one prefill workload."""
+    tf = p["flops"] / (p["mean_ms"] * 1e-3) / 1e12
+    r = {"tokens_per_s": round(p["tokens"] / (p["wall"] / steps), 1),
+         "token_heads_per_s": round(p["tokens"] * p["H"] / (p["wall"] / steps), 1),
+         "us_per_call": round(p["mean_ms"] * 1e3, 2),
+         "algorithmic_bytes": p["bytes"], "algorithmic_flops": p["flops"],
+         "roofline": hbm_roofline(p["bytes"], p["mean_ms"], traffic,
+                                  **({"kernel": kernel} if kernel else {})),
+         "mfma": {"achieved_TFLOPs": round(tf, 2), "peak_TFLOPs": MFMA_PEAK_TFLOPS,
+                  "frac": round(tf / MFMA_PEAK_TFLOPS, 4)},
+         "workspace_bytes": p["ws_bytes"]}
+    if p["flushed"]:
+        r["flushed"] = spread(p["flushed"], p["mean_ms"])
+    return r
 
-    def call():
-        kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_g"], d["beta"], cu_seqlens=d["cu_seqlens"],
-                      out=out, final_state=fin)
 
-    wall, ms = timed_calls(call, steps, warmup)
-    avg = float(np.mean(ms))
-    nbytes = prefill_bytes(T, H, D, n_states=0) + N * H * D * D * 4  # final states only (zero initial)
-    gbs = nbytes / (avg * 1e-3) / 1e9
-    return {"workload": f"packed varlen prefill, 1 x {T} tokens in {N} documents (log-uniform 64..16384), "
-                        f"H={H}, dk=dv={D}, bf16 q/k/v, zero initial states",
-            "tokens_per_s": round(T / (wall / steps), 1), "us_per_call": round(avg * 1e3, 2),
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
-            "algorithmic_bytes": nbytes}
+def fallback_fraction(inp) -> float:
+    """Fraction of (chunk, head) pairs whose 64-token chunk fails the MFMA
+    path's decay guard (decay beyond e^-6 over the first or the second half of
+    any 16-token block, in any channel), computed on the host from log_g.
+    The guard's other triggers (input and intermediate magnitudes) do not
+    fire on these inputs' distributions."""
+    g = inp["log_g"].double().numpy()
+    B, T, H, D = g.shape
+    nch = (T + CHUNK - 1) // CHUNK
+    pad = nch * CHUNK - T
+    if pad:
+        g = np.concatenate([g, np.zeros((B, pad, H, D))], axis=1)
+    # [B, chunk, block, half, 8 tokens, H, D] -> decay of each half block
+    half = g.reshape(B, nch, 4, 2, 8, H, D).sum(axis=4)
+    bad = (half < -6.0).any(axis=(2, 3, 5))  # [B, chunk, H]
+    return float(bad.mean())
+
+
+def bench_strong_gates(kda, steps, warmup, flush):
+    """The dense workload with stronger gates than its 0.05 scale: log_g =
+    -softplus(N(0,1)) at scale 1.0, and log_g ~ U[-5, 0].  Reports tokens/s
+    and the fraction of (chunk, head) pairs on the exact per-token fallback."""
+    res = {}
+    for tag, over in (("gate_scale_1.0", dict(gate_scale=1.0)), ("uniform_-5_0", dict(gate_uniform=5.0))):
+        p = bench_prefill_workload(kda, "prefill", steps, warmup, flush, n_flushed=0, **over)
+        res[tag] = {"tokens_per_s": round(p["tokens"] / (p["wall"] / steps), 1),
+                    "us_per_call": round(p["mean_ms"] * 1e3, 2),
+                    "fallback_chunk_fraction": round(fallback_fraction(p["inp"]), 4)}
+        del p
+        torch.cuda.empty_cache()
+    return res
 
 
 def bench_backward(kda, steps, warmup):
@@ -287,8 +376,7 @@ def bench_backward(kda, steps, warmup):
         kda.chunk_bwd(d["q"], d["k"], d["v"], d["log_g"], d["beta"], do, init_state=d["init_state"], d_final=dfin,
                       grads=grads, workspace=ws)
 
-    wall, ms = timed_calls(call, steps, warmup)
-    avg = float(np.mean(ms))
+    wall, avg = timed_calls(call, steps, warmup)
     tokens = B * T
     fl, nb = backward_flops(tokens, H, D), backward_bytes(tokens, H, D, n_states=B)
     tf = fl / (avg * 1e-3) / 1e12
@@ -323,8 +411,7 @@ def bench_conv(kda, steps, warmup):
     def call():
         kda.short_conv(x, w, out=out, final_cache=fin)
 
-    wall, ms = timed_calls(call, steps, warmup)
-    avg = float(np.mean(ms))
+    wall, avg = timed_calls(call, steps, warmup)
     nb = conv_bytes(B * T, Cn, K, B)
     gbs = nb / (avg * 1e-3) / 1e9
     return {"workload": f"short causal depthwise conv, {B} x {T} tokens, {Cn} channels (q, k, v of 16 heads x 128), "
@@ -355,8 +442,7 @@ def bench_norm(kda, steps, warmup):
     def call():
         kda.gated_rmsnorm(o, g, w, 1e-6, out=out)
 
-    wall, ms = timed_calls(call, steps, warmup)
-    avg = float(np.mean(ms))
+    wall, avg = timed_calls(call, steps, warmup)
     nb = norm_bytes(B * T * H, D)
     gbs = nb / (avg * 1e-3) / 1e9
     return {"workload": f"gated per-head RMSNorm, {B} x {T} tokens x {H} heads x {D}, fp32 o, bf16 gate, bf16 out",
@@ -366,47 +452,30 @@ def bench_norm(kda, steps, warmup):
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
 
 
-def bench_step(kda, name, steps, warmup):
+def bench_step(kda, name, steps, warmup, flush):
     """kda_step timed per call with HIP events; before every call a 1 GiB
     buffer is read (clean lines, nothing to write back) so the state (128 MiB
     for verify) is not served from the 256 MB last-level cache left warm by
-    the previous call."""
+    the previous call.  Reports the mean and the median / p10 / p90."""
     inp = kda_inputs.config(name)
     d = to_dev(inp)
     N, n_tok, H, D = inp["q"].shape
     state = d["init_state"].clone()
     out = torch.empty((N, n_tok, H, D), dtype=torch.float32, device="cuda")
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    sink = torch.empty((), dtype=torch.float32, device="cuda")
 
     def call():
         kda.step(d["q"], d["k"], d["v"], d["log_g"], d["beta"], state, out=out)
 
-    def flushed_call():
-        torch.sum(flush, dim=0, out=sink)
-        call()
-
-    settle(flushed_call)
     for _ in range(warmup):
         call()
-    stream = torch.cuda.current_stream()
-    ms = []
-    for _ in range(steps):
-        torch.sum(flush, dim=0, out=sink)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        call()
-        b.record(stream)
-        b.synchronize()
-        ms.append(a.elapsed_time(b))
+    ms = flushed_calls(call, max(steps, 100), flush)
     nbytes = step_bytes(N, n_tok, H, D)
     avg = float(np.mean(ms))
-    gbs = nbytes / (avg * 1e-3) / 1e9
     return {"workload": f"{N} sequences x {n_tok} rows, H={H}, dk=dv={D}, bf16 q/k/v, fp32 state in place "
                         "(caches flushed before each call)",
-            "us_per_call": round(avg * 1e3, 2), "achieved_GBs": round(gbs, 1),
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+            "us_per_call": round(avg * 1e3, 2), "achieved_GBs": round(nbytes / (avg * 1e-3) / 1e9, 1),
+            "per_call": spread(ms),
+            "roofline": hbm_roofline(nbytes, avg),
             "algorithmic_bytes": nbytes}
 
 
@@ -423,7 +492,7 @@ def commit_bytes(N: int, n_tok: int, H: int, d: int, qkv_bytes=2) -> int:
     return N * H * 2 * d * d * 4 + N * n_tok * H * (d * qkv_bytes + d * 4 + d * 4) + N * 4
 
 
-def bench_verify_commit(kda, steps, warmup):
+def bench_verify_commit(kda, steps, warmup, flush):
     """Speculative verify on the verify workload: kda_step_rows (state read
     only) then kda_step_commit of all rows, each timed with HIP events after a
     1 GiB read, like bench_step."""
@@ -434,8 +503,6 @@ def bench_verify_commit(kda, steps, warmup):
     out = torch.empty((N, n_tok, H, D), dtype=torch.float32, device="cuda")
     deltas = torch.empty((N, n_tok, H, D), dtype=torch.float32, device="cuda")
     accept = torch.full((N,), n_tok, dtype=torch.int32, device="cuda")
-    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-    sink = torch.empty((), dtype=torch.float32, device="cuda")
 
     def rows():
         kda.step_rows(d["q"], d["k"], d["v"], d["log_g"], d["beta"], state, out=out, deltas=deltas)
@@ -443,59 +510,83 @@ def bench_verify_commit(kda, steps, warmup):
     def commit():
         kda.step_commit(d["k"], d["log_g"], deltas, state, accept)
 
-    def both():
-        torch.sum(flush, dim=0, out=sink)
-        rows()
-        torch.sum(flush, dim=0, out=sink)
-        commit()
-
-    settle(both)
     for _ in range(warmup):
-        both()
-    stream = torch.cuda.current_stream()
-    t_rows, t_commit = [], []
-    for _ in range(steps):
-        for fn, acc in ((rows, t_rows), (commit, t_commit)):
-            torch.sum(flush, dim=0, out=sink)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            fn()
-            b.record(stream)
-            b.synchronize()
-            acc.append(a.elapsed_time(b))
-    r_us, c_us = float(np.mean(t_rows)) * 1e3, float(np.mean(t_commit)) * 1e3
+        rows()
+        commit()
+    n = max(steps, 100)
+    t_rows = flushed_calls(rows, n, flush)
+    t_commit = flushed_calls(commit, n, flush)
+    r_ms, c_ms = float(np.mean(t_rows)), float(np.mean(t_commit))
     rb, cb = rows_bytes(N, n_tok, H, D), commit_bytes(N, n_tok, H, D)
-    r_gbs, c_gbs = rb / (r_us * 1e-6) / 1e9, cb / (c_us * 1e-6) / 1e9
-    roof = lambda g: {"bound": "hbm", "achieved": round(g, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": round(g / HBM_PEAK_GBS, 4), "traffic": None}
     return {"workload": f"{N} sequences x {n_tok} draft rows, H={H}, dk=dv={D}, bf16 q/k/v: rows scored with the "
                         "state read only, then every row committed (caches flushed before each call)",
-            "rows": {"us_per_call": round(r_us, 2), "algorithmic_bytes": rb, "roofline": roof(r_gbs)},
-            "commit": {"us_per_call": round(c_us, 2), "algorithmic_bytes": cb, "roofline": roof(c_gbs)}}
+            "rows": {"us_per_call": round(r_ms * 1e3, 2), "per_call": spread(t_rows), "algorithmic_bytes": rb,
+                     "roofline": hbm_roofline(rb, r_ms)},
+            "commit": {"us_per_call": round(c_ms * 1e3, 2), "per_call": spread(t_commit), "algorithmic_bytes": cb,
+                       "roofline": hbm_roofline(cb, c_ms)}}
+
+
+def host_cores():
+    """(threads the oracle runs on, logical CPUs this process may use, nproc).
+    The oracle uses the CPUs this process may run on, capped by
+    OMP_NUM_THREADS when the environment sets it (a GPU host grants each GPU
+    a share of its cores and says so there)."""
+    nproc = os.cpu_count() or 1
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = nproc
+    threads = allowed
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        threads = min(threads, int(omp))
+    return max(1, threads), allowed, nproc
+
+
+def host_cpu_model() -> str:
+    """lscpu's model name (else /proc/cpuinfo's)."""
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=20).stdout
+        for line in out.splitlines():
+            if line.strip().startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, ValueError, Exception):  # noqa: BLE001 - best effort description
+        pass
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(inp, target_s=10.0):
-    """Time the fp64 oracle on a bounded sample of the prefill workload: the
-    whole workload (all sequences and heads, OpenMP over the units), repeated
-    until about target_s of wall time has passed."""
+    """Time the fp64 oracle on a bounded sample of the headline workload: the
+    whole packed workload (all documents and heads, OpenMP over the units,
+    longest first), repeated until about target_s of wall time has passed."""
     import oracle
     from kda_inputs import to_f64
-    threads = max(1, min(16, os.cpu_count() or 1))
+    threads, allowed, nproc = host_cores()
     B, T, H, D = inp["q"].shape
     args = (to_f64(inp["q"]), to_f64(inp["k"]), to_f64(inp["v"]), to_f64(inp["log_g"]), to_f64(inp["beta"]))
+    cu = inp["cu_seqlens"].numpy().astype(np.int64) if inp["cu_seqlens"] is not None else None
     s0 = to_f64(inp["init_state"])
     reps, elapsed = 0, 0.0
     while elapsed < target_s:
         t0 = time.perf_counter()
-        oracle.kda_forward(*args, init_state=s0, scale=inp["scale"], n_threads=threads)
+        oracle.kda_forward(*args, init_state=s0, cu_seqlens=cu, scale=inp["scale"], n_threads=threads)
         elapsed += time.perf_counter() - t0
         reps += 1
     token_heads = reps * B * T * H
     res = {"value": round(reps * B * T / elapsed, 1), "unit": "tokens/s", "cores": threads,
            "kind": "oracle",
-           "sample": f"the whole workload ({B} x {T} tokens x {H} heads, fp64 token loop) run {reps} times "
+           "sample": f"the whole packed workload ({B} x {T} tokens, {H} heads, fp64 token loop) run {reps} times "
                      f"back to back, {token_heads} token-heads in {elapsed:.1f} s on {threads} threads",
-           "host_cpu": host_cpu_model()}
+           "host_cpu": host_cpu_model(), "nproc": nproc, "cpus_allowed": allowed,
+           "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+    del args
     # single-thread oracle on the small workloads (the whole of each, once)
     single = {}
     for name in ("tiny", "decode", "verify"):
@@ -514,24 +605,89 @@ def cpu_baseline(inp, target_s=10.0):
     return res
 
 
-def host_cpu_model() -> str:
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
-    except OSError:
-        pass
-    return "unknown"
+PEAK_LIB = os.path.join(ROOT, "gated_delta_rule_67_amd", "libkda_peak.so")
+
+
+def bench_peaks(steps, warmup):
+    """This GPU's re-measured peaks: a 1 GiB device-to-device copy (bytes read
+    plus written per second) and the dense fp16 MFMA loop of libkda_peak.so."""
+    import ctypes
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").uniform_()
+    dst = torch.empty_like(src)
+    _, ms = timed_calls(lambda: dst.copy_(src), steps, warmup)
+    copy_gbs = 2 * src.numel() * 4 / (ms * 1e-3) / 1e9
+    del src, dst
+    lib = ctypes.CDLL(PEAK_LIB)
+    lib.kda_peak_mfma_f16.restype = ctypes.c_int
+    lib.kda_peak_mfma_f16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    blocks, iters = 2048, 4000
+    sink = torch.zeros(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def mfma():
+        rc = lib.kda_peak_mfma_f16(blocks, iters, ctypes.c_void_p(sink.data_ptr()),
+                                   ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"kda_peak_mfma_f16 failed ({rc})")
+
+    _, ms = timed_calls(mfma, max(3, steps // 4), 1)
+    flop = blocks * 4 * iters * 8 * 16384
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"copy_GBs": round(copy_gbs, 1), "copy_frac_of_8TBs": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "mfma_f16_TFLOPs": round(tf, 1), "mfma_frac_of_2516TF": round(tf / MFMA_PEAK_TFLOPS, 4),
+            "how": "copy: torch copy_ of 1 GiB fp32 (read + write); mfma: 2048 workgroups x 4 waves x 4000 "
+                   "rounds of 8 independent v_mfma_f32_16x16x32_f16"}
 
 
 def bench_copy(steps, warmup):
     """A plain device copy of COPY_BYTES (the counter calibration kernel)."""
     src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").uniform_()
     dst = torch.empty_like(src)
-    wall, ms = timed_calls(lambda: dst.copy_(src), steps, warmup)
-    avg = float(np.mean(ms))
-    print(f"copy: {COPY_BYTES >> 20} MiB in {avg * 1e3:.1f} us = {2 * COPY_BYTES / (avg * 1e-3) / 1e9:.0f} GB/s",
+    _, ms = timed_calls(lambda: dst.copy_(src), steps, warmup)
+    print(f"copy: {COPY_BYTES >> 20} MiB in {ms * 1e3:.1f} us = {2 * COPY_BYTES / (ms * 1e-3) / 1e9:.0f} GB/s",
           file=sys.stderr, flush=True)
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES")
+
+
+def write_mfma(run_dir, n_cu=256):
+    """Per-kernel MFMA counters of one rocprofv3 --pmc run (mean per
+    dispatch), and the two fractions they give: counted MFMA FLOP (512 per
+    F16 MOP) and MFMA-busy cycles over the kernel's active cycles on all
+    n_cu * 4 SIMDs."""
+    lines = [f"sources_sha256: {sources_hash('varlen')}"]
+    per = {c: {} for c in MFMA_COUNTERS}
+    for c in MFMA_COUNTERS:
+        try:
+            per[c] = _counter_sums(run_dir, c)
+        except SystemExit:
+            per[c] = {}
+    for pat in TRAFFIC["varlen"]["kernels"]:
+        vals = {c: sum(v for k, v in per[c].items() if pat in k) for c in MFMA_COUNTERS}
+        for c, v in vals.items():
+            lines.append(f"{pat}_{c}: {v:.0f}")
+        if vals["GRBM_GUI_ACTIVE"] > 0:
+            busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (vals["GRBM_GUI_ACTIVE"] * n_cu * 4)
+            lines.append(f"{pat}_mfma_busy_frac: {busy:.4f}")
+        lines.append(f"{pat}_counted_mfma_flop: {512 * vals['SQ_INSTS_VALU_MFMA_MOPS_F16']:.0f}")
+    return lines
+
+
+def read_mfma():
+    """The committed MFMA counter summary as a dict, or None when it is
+    missing or was taken on other kernel sources."""
+    try:
+        kv = {}
+        for line in open(MFMA_FILE):
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.pop("sources_sha256", None) != sources_hash("varlen"):
+            return None
+        return {k: float(v) for k, v in kv.items()}
+    except (OSError, ValueError):
+        return None
 
 
 def main():
@@ -540,14 +696,17 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["all", "prefill", "varlen", "step", "backward", "conv", "norm", "copy"],
-                    default="all",
-                    help="restrict the run (profiling); the JSON line needs 'all'")
+    ap.add_argument("--only", choices=["all", "prefill", "varlen", "step", "backward", "conv", "norm", "strong",
+                                       "copy", "peak"],
+                    default="all", help="restrict the run (profiling); the JSON line needs 'all'")
     ap.add_argument("--traffic-from", nargs=4, metavar="DIR",
                     help="rocprofv3 csv dirs: FETCH_SIZE and WRITE_SIZE of the measured path, then FETCH_SIZE and "
                          "WRITE_SIZE of the copy; writes the path's profiles/traffic_*.txt")
-    ap.add_argument("--traffic-kind", choices=sorted(TRAFFIC), default="prefill",
+    ap.add_argument("--traffic-kind", choices=sorted(TRAFFIC), default="varlen",
                     help="which path --traffic-from summarises (bench.py --only <kind> made its runs)")
+    ap.add_argument("--mfma-from", metavar="DIR",
+                    help="rocprofv3 csv dir of one --pmc run of the MFMA counters over --only varlen; writes "
+                         "profiles/mfma_prefill_packed.txt")
     args = ap.parse_args()
     if args.traffic_from:
         kind = args.traffic_kind
@@ -564,6 +723,20 @@ def main():
             fh.write("\n".join(lines) + "\n")
         print("\n".join(lines))
         return
+    if args.mfma_from:
+        lines = write_mfma(args.mfma_from)
+        with open(MFMA_FILE, "w") as fh:
+            fh.write("# MFMA counters of one kda_chunk_fwd call, packed 65536 tokens in 26 documents, 32 heads, "
+                     "d = 128, bf16\n")
+            fh.write(f"# made by: python bench.py --mfma-from {args.mfma_from}\n")
+            fh.write(f"# from: rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -f csv -d {args.mfma_from} -o run -- "
+                     "python3 bench.py --only varlen --steps 3 --warmup 1\n")
+            fh.write("# values are per dispatch (mean over the run's dispatches); mfma_busy_frac = "
+                     "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * 256 CUs * 4 SIMDs); counted_mfma_flop = "
+                     "512 * SQ_INSTS_VALU_MFMA_MOPS_F16\n")
+            fh.write("\n".join(lines) + "\n")
+        print("\n".join(lines))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build runs on a single MI355X)", file=sys.stderr)
@@ -576,13 +749,19 @@ def main():
     if args.only == "copy":
         bench_copy(args.steps, args.warmup)
         return
+    flush = CacheFlush()
     res = {}
-    if args.only in ("all", "prefill"):
-        res["prefill"] = bench_prefill(kda, args.steps, args.warmup)
-        print(f"prefill: mean {np.mean(res['prefill']['ms']) * 1e3:.1f} us/call", file=sys.stderr, flush=True)
     if args.only in ("all", "varlen"):
-        res["varlen"] = bench_varlen(kda, args.steps, args.warmup)
-        print(f"varlen prefill: {res['varlen']['us_per_call']} us/call", file=sys.stderr, flush=True)
+        res["varlen"] = bench_prefill_workload(kda, "varlen", args.steps, args.warmup, flush,
+                                               n_flushed=100 if args.only == "all" else 0)
+        print(f"packed prefill: {res['varlen']['mean_ms'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+    if args.only in ("all", "prefill"):
+        res["prefill"] = bench_prefill_workload(kda, "prefill", args.steps, args.warmup, flush,
+                                                n_flushed=100 if args.only == "all" else 0)
+        print(f"dense prefill: {res['prefill']['mean_ms'] * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+    if args.only in ("all", "strong"):
+        res["strong_gates"] = bench_strong_gates(kda, args.steps, args.warmup, flush)
+        print(f"strong gates: {res['strong_gates']}", file=sys.stderr, flush=True)
     if args.only in ("all", "backward"):
         res["backward"] = bench_backward(kda, args.steps, args.warmup)
         print(f"backward {res['backward']['us_per_call']} us per call", file=sys.stderr, flush=True)
@@ -593,22 +772,34 @@ def main():
         res["gated_rmsnorm"] = bench_norm(kda, args.steps, args.warmup)
         print(f"gated rmsnorm {res['gated_rmsnorm']['us_per_call']} us per call", file=sys.stderr, flush=True)
     if args.only in ("all", "step"):
-        res["decode"] = bench_step(kda, "decode", args.steps, args.warmup)
-        res["verify"] = bench_step(kda, "verify", args.steps, args.warmup)
-        res["verify_rollback"] = bench_verify_commit(kda, args.steps, args.warmup)
+        res["decode"] = bench_step(kda, "decode", args.steps, args.warmup, flush)
+        res["verify"] = bench_step(kda, "verify", args.steps, args.warmup, flush)
+        res["verify_rollback"] = bench_verify_commit(kda, args.steps, args.warmup, flush)
         vr = res["verify_rollback"]
         print(f"decode {res['decode']['us_per_call']} us, verify {res['verify']['us_per_call']} us, "
               f"verify rows {vr['rows']['us_per_call']} us + commit {vr['commit']['us_per_call']} us",
               file=sys.stderr, flush=True)
+    if args.only in ("all", "peak"):
+        res["peaks"] = bench_peaks(args.steps, args.warmup)
+        print(f"peaks {res['peaks']}", file=sys.stderr, flush=True)
     if args.only != "all":
         return
 
-    p = res["prefill"]
+    p = res["varlen"]
     ms_per_step = p["wall"] / args.steps * 1e3
     value = p["tokens"] / (ms_per_step * 1e-3)
-    k_ms = float(np.mean(p["ms"]))
-    gbs = p["bytes"] / (k_ms * 1e-3) / 1e9
-    tflops = p["flops"] / (k_ms * 1e-3) / 1e12
+    head = prefill_summary(p, args.steps, read_traffic("varlen"),
+                           kernel="kda_chunk_fwd = prep_kernel + scan_kernel back to back (one call)")
+    mf = read_mfma()
+    if mf is not None:
+        counted = mf.get("prep_kernel_counted_mfma_flop", 0.0) + mf.get("scan_kernel_counted_mfma_flop", 0.0)
+        head["mfma"]["counted_mfma_flop_per_call"] = counted
+        head["mfma"]["counted_TFLOPs"] = round(counted / (p["mean_ms"] * 1e-3) / 1e12, 2)
+        head["mfma"]["counted_frac"] = round(counted / (p["mean_ms"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)
+        head["mfma"]["busy_frac"] = {k: mf.get(f"{k}_mfma_busy_frac") for k in ("prep_kernel", "scan_kernel")}
+    dense = prefill_summary(res["prefill"], args.steps, read_traffic("prefill"))
+    dense["workload"] = ("chunked prefill, dense B=4 x T=4096, H=16, dk=dv=128, bf16 q/k/v, fp32 log_g/beta/"
+                         "state, fp32 out, chunk 64")
     line = {
         "metric": "KDA prefill tokens/s (+MFMA %) and decode state-update HBM GB/s, dk=dv=128",
         "value": round(value, 1),
@@ -620,28 +811,35 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 MFMA operands, f32 accumulation and state (bf16 inputs)",
+        "dtype": "bf16 in; f16 MFMA operands, f32 accumulation, state and out",
         "data": "synthetic (seeded; q,v~N(0,1), k L2-normalised, log_g=-softplus(N)*0.05, beta=sigmoid(N))",
-        "config": {"workload": "chunked prefill, dense B=4 x T=4096, H=16, dk=dv=128, bf16 q/k/v, "
-                               "fp32 log_g/beta/state, fp32 out, chunk 64",
-                   "global_batch": 4, "seq_len": 4096, "heads": 16, "head_dim": 128},
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": read_traffic(),
-                     "kernel": "kda_chunk_fwd = prep_kernel + scan_kernel back to back (one call)"},
-        "prefill_kernel_us": round(k_ms * 1e3, 2),
+        "config": {"workload": f"packed varlen chunked prefill: 1 x {p['tokens']} tokens in {p['N']} documents "
+                               "(log-uniform 64..16384), H=32, dk=dv=128, bf16 q/k/v, fp32 log_g/beta, zero initial "
+                               "states, fp32 out and final states, chunk 64",
+                   "global_batch": 1, "seq_len": p["tokens"], "documents": p["N"], "heads": 32, "head_dim": 128},
+        "roofline": head["roofline"],
+        "flushed": head["flushed"],
+        "prefill_kernel_us": head["us_per_call"],
         "algorithmic_bytes_per_launch": p["bytes"],
-        "mfma": {"achieved_TFLOPs": round(tflops, 2), "peak_TFLOPs": MFMA_PEAK_TFLOPS,
-                 "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "algorithmic_flop_per_launch": p["flops"]},
-        "varlen": res["varlen"],
+        "mfma": dict(head["mfma"], algorithmic_flop_per_launch=p["flops"]),
+        "token_heads_per_s": head["token_heads_per_s"],
+        "dense_prefill": dense,
+        "strong_gates": res["strong_gates"],
         "decode": res["decode"],
         "verify": res["verify"],
         "verify_rollback": res["verify_rollback"],
         "backward": res["backward"],
         "short_conv": res["short_conv"],
         "gated_rmsnorm": res["gated_rmsnorm"],
+        "peaks": res["peaks"],
     }
+    inp = p["inp"]
+    for k in list(res):
+        res[k] = None
+    del p
+    torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(p["inp"])
+        line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)
 
 

@@ -19,6 +19,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libkda.so")
+# the benchmark's peak probe, a library of its own (not part of libkda)
+PEAK_SRC = "kda_peak.hip"
+PEAK_OUT = os.path.join(PKG, "libkda_peak.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
@@ -49,18 +52,23 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
+        raise RuntimeError(f"link of {os.path.basename(out)} failed:\n{r.stderr}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES + [PEAK_SRC]))
+    _link(objs[:-1], OUT)
+    _link(objs[-1:], PEAK_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {PEAK_OUT}")
     return OUT
 
 

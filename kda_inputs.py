@@ -78,7 +78,7 @@ def _cast(x: np.ndarray, dtype: str) -> torch.Tensor:
 def make_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
                 seed: int = 0, gate_scale: float = 0.05, init: str = "normal",
                 lengths=None, doc_lo: int | None = None, doc_hi: int | None = None,
-                init_std: float = 0.02) -> dict:
+                init_std: float = 0.02, gate_uniform: float | None = None) -> dict:
     """Draw one seeded workload.
 
     Dense when neither ``lengths`` nor ``doc_lo`` is given (B sequences of T
@@ -86,6 +86,9 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
     or ``doc_lo``/``doc_hi`` (drawn log-uniform) is given; then B must be 1.
     Returns CPU tensors: q, k, v (``dtype``), log_g, beta (float32),
     init_state (float32 or None), cu_seqlens (int32 or None), and ``scale``.
+    ``gate_uniform`` = a replaces the gate recipe by log_g ~ U[-a, 0], taken
+    from the same normal draws through the normal CDF (so every other tensor
+    of the workload is unchanged).
     """
     rng = np.random.default_rng(seed)
     cu = None
@@ -102,7 +105,11 @@ def make_inputs(B: int, T: int, H: int, dk: int, dv: int, dtype: str = "bf16",
     k /= np.sqrt(np.sum(np.square(k, dtype=np.float64), axis=-1, keepdims=True)).astype(np.float32)
     v = rng.standard_normal((B, T, H, dv), dtype=np.float32)
     g = rng.standard_normal((B, T, H, dk), dtype=np.float32)
-    log_g = (-np.logaddexp(np.float32(0.0), g) * np.float32(gate_scale)).astype(np.float32)
+    if gate_uniform is None:
+        log_g = (-np.logaddexp(np.float32(0.0), g) * np.float32(gate_scale)).astype(np.float32)
+    else:
+        from scipy.special import ndtr
+        log_g = (-float(gate_uniform) * ndtr(g.astype(np.float64))).astype(np.float32)
     del g
     b = rng.standard_normal((B, T, H), dtype=np.float32)
     beta = (1.0 / (1.0 + np.exp(-b.astype(np.float64)))).astype(np.float32)
