@@ -648,29 +648,29 @@ def bench_copy(steps, warmup):
           file=sys.stderr, flush=True)
 
 
-MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", "SQ_BUSY_CU_CYCLES")
+# rocprofv3's derived MFMA metrics (it applies their reductions over SIMDs and
+# XCDs): MfmaUtil = 100 * sum SQ_VALU_MFMA_BUSY_CYCLES / (max GRBM_GUI_ACTIVE *
+# SIMD_NUM); MfmaFlopsF16 = 512 * SQ_INSTS_VALU_MFMA_MOPS_F16.  One pass.
+MFMA_COUNTERS = ("MfmaUtil", "MfmaFlopsF16")
 
 
-def write_mfma(run_dir, n_cu=256):
-    """Per-kernel MFMA counters of one rocprofv3 --pmc run (mean per
-    dispatch), and the two fractions they give: counted MFMA FLOP (512 per
-    F16 MOP) and MFMA-busy cycles over the kernel's active cycles on all
-    n_cu * 4 SIMDs."""
+def write_mfma(run_dir):
+    """Per-kernel MFMA metrics of one rocprofv3 --pmc run (mean per dispatch):
+    the busy fraction of the matrix cores while the kernel runs, and the fp16
+    MFMA FLOP it executed (algorithmic plus any redundant work)."""
     lines = [f"sources_sha256: {sources_hash('varlen')}"]
-    per = {c: {} for c in MFMA_COUNTERS}
+    per = {}
     for c in MFMA_COUNTERS:
         try:
             per[c] = _counter_sums(run_dir, c)
         except SystemExit:
             per[c] = {}
     for pat in TRAFFIC["varlen"]["kernels"]:
-        vals = {c: sum(v for k, v in per[c].items() if pat in k) for c in MFMA_COUNTERS}
-        for c, v in vals.items():
-            lines.append(f"{pat}_{c}: {v:.0f}")
-        if vals["GRBM_GUI_ACTIVE"] > 0:
-            busy = vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (vals["GRBM_GUI_ACTIVE"] * n_cu * 4)
-            lines.append(f"{pat}_mfma_busy_frac: {busy:.4f}")
-        lines.append(f"{pat}_counted_mfma_flop: {512 * vals['SQ_INSTS_VALU_MFMA_MOPS_F16']:.0f}")
+        util = [v for k, v in per["MfmaUtil"].items() if pat in k]
+        flop = sum(v for k, v in per["MfmaFlopsF16"].items() if pat in k)
+        if util:
+            lines.append(f"{pat}_mfma_busy_frac: {util[0] / 100.0:.4f}")
+        lines.append(f"{pat}_counted_mfma_flop: {flop:.0f}")
     return lines
 
 
@@ -731,9 +731,9 @@ def main():
             fh.write(f"# made by: python bench.py --mfma-from {args.mfma_from}\n")
             fh.write(f"# from: rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -f csv -d {args.mfma_from} -o run -- "
                      "python3 bench.py --only varlen --steps 3 --warmup 1\n")
-            fh.write("# values are per dispatch (mean over the run's dispatches); mfma_busy_frac = "
-                     "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE * 256 CUs * 4 SIMDs); counted_mfma_flop = "
-                     "512 * SQ_INSTS_VALU_MFMA_MOPS_F16\n")
+            fh.write("# values are per dispatch (mean over the run's dispatches); mfma_busy_frac = MfmaUtil / 100 "
+                     "(busy cycles of the matrix cores over the kernel's active cycles on all SIMDs); "
+                     "counted_mfma_flop = MfmaFlopsF16\n")
             fh.write("\n".join(lines) + "\n")
         print("\n".join(lines))
         return

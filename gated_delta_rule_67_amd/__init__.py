@@ -32,12 +32,13 @@ import threading
 import torch
 
 __all__ = ["chunk_fwd", "chunk_bwd", "step", "step_rows", "step_commit", "short_conv", "gated_rmsnorm",
-           "workspace_bytes",
-           "bwd_workspace_bytes",
-           "abi_version", "KdaError", "LIB_PATH", "KDA_F32", "KDA_BF16"]
+           "workspace_bytes", "bwd_workspace_bytes", "abi_version", "KdaError", "LIB_PATH", "KDA_F32",
+           "KDA_BF16", "KDA_FLAG_QK_L2NORM", "QK_L2NORM_EPS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 KDA_F32, KDA_BF16 = 0, 1
+KDA_FLAG_QK_L2NORM = 1
+QK_L2NORM_EPS = 1e-6  # eps inside the root of the in-kernel q / k L2 normalisation
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
            4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_HIP"}
 
@@ -48,7 +49,8 @@ class KdaDesc(ctypes.Structure):
                 ("num_heads", ctypes.c_int32), ("dk", ctypes.c_int32), ("dv", ctypes.c_int32),
                 ("qkv_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("workspace", ctypes.c_void_p),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("flags", ctypes.c_uint32),
+                ("reserved", ctypes.c_uint32)]
 
 
 class KdaError(RuntimeError):
@@ -163,10 +165,19 @@ def _allocates_on_launch_stream(fn):
     return wrapper
 
 
-def make_desc(num_seqs, seq_len, H, dk, dv, qkv_dtype, scale=None, workspace=None) -> KdaDesc:
+def _out_code(dtype) -> int:
+    if dtype == torch.float32:
+        return KDA_F32
+    if dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"out must be float32 or bfloat16, got {dtype}")
+
+
+def make_desc(num_seqs, seq_len, H, dk, dv, qkv_dtype, scale=None, workspace=None, out_dtype=KDA_F32,
+              flags=0) -> KdaDesc:
     d = KdaDesc()
     d.num_seqs, d.seq_len, d.num_heads, d.dk, d.dv = num_seqs, seq_len, H, dk, dv
-    d.qkv_dtype, d.out_dtype = qkv_dtype, KDA_F32
+    d.qkv_dtype, d.out_dtype, d.flags = qkv_dtype, out_dtype, flags
     d.scale = 0.0 if scale is None else float(scale)
     if workspace is not None:
         d.workspace, d.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
@@ -182,14 +193,17 @@ def workspace_bytes(num_seqs: int, seq_len: int, H: int, d: int, packed: bool,
 
 @_allocates_on_launch_stream
 def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None,
-              out=None, final_state=None, workspace=None, stream=None):
-    """Chunked prefill.  Returns (out [B,T,H,dv] fp32, final_state [N,H,dk,dv] fp32).
+              out=None, final_state=None, workspace=None, stream=None, out_dtype=torch.float32,
+              qk_l2norm=False):
+    """Chunked prefill.  Returns (out [B,T,H,dv], final_state [N,H,dk,dv] fp32).
 
     Dense: B sequences.  Packed: B == 1 and int32 ``cu_seqlens`` [N+1] on the
     device splits the row into N documents.  ``init_state`` [N,H,dk,dv] or None
     (zeros).  ``final_state`` may be passed (and may be ``init_state`` itself
     for an in-place resume); pass ``final_state=False`` to skip it.
     ``workspace`` (uint8 device tensor) is allocated when absent or too small.
+    ``out_dtype`` float32 or bfloat16 (the dtype of ``out`` when passed);
+    ``qk_l2norm`` L2-normalises every q and k row inside the kernels.
     """
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -210,16 +224,17 @@ def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None
     if init_state is not None:
         _need(init_state, "init_state", (N, H, dk, dv), torch.float32, dev)
     if out is None:
-        out = torch.empty((B, T, H, dv), dtype=torch.float32, device=dev)
+        out = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
     else:
-        _need(out, "out", (B, T, H, dv), torch.float32, dev)
+        _need(out, "out", (B, T, H, dv), out.dtype, dev)
     if final_state is None:
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     elif final_state is False:
         final_state = None
     else:
         _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
-    desc = make_desc(N, L, H, dk, dv, code, scale)
+    desc = make_desc(N, L, H, dk, dv, code, scale, out_dtype=_out_code(out.dtype),
+                     flags=KDA_FLAG_QK_L2NORM if qk_l2norm else 0)
     need = _lib().kda_chunk_workspace_bytes(ctypes.byref(desc), int(cu_seqlens is not None))
     if need > 0:
         if workspace is None or workspace.numel() * workspace.element_size() < need:
@@ -360,10 +375,11 @@ def gated_rmsnorm(o, gate, weight, eps, out=None, out_dtype=torch.bfloat16, stre
 
 
 @_allocates_on_launch_stream
-def step(q, k, v, log_g, beta, state, scale=None, out=None, stream=None):
+def step(q, k, v, log_g, beta, state, scale=None, out=None, stream=None, out_dtype=torch.float32,
+         qk_l2norm=False):
     """Decode (n_tok = 1) or multi-row verify: rows [N, n_tok, H, d] applied in
     order to ``state`` [N, H, dk, dv] (fp32), which is updated in place.
-    Returns out [N, n_tok, H, dv] fp32."""
+    Returns out [N, n_tok, H, dv] (``out_dtype``: float32 or bfloat16)."""
     N, n_tok, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -374,20 +390,23 @@ def step(q, k, v, log_g, beta, state, scale=None, out=None, stream=None):
     _need(beta, "beta", (N, n_tok, H), torch.float32, dev)
     _need(state, "state", (N, H, dk, dv), torch.float32, dev)
     if out is None:
-        out = torch.empty((N, n_tok, H, dv), dtype=torch.float32, device=dev)
+        out = torch.empty((N, n_tok, H, dv), dtype=out_dtype, device=dev)
     else:
-        _need(out, "out", (N, n_tok, H, dv), torch.float32, dev)
-    desc = make_desc(N, n_tok, H, dk, dv, code, scale)
+        _need(out, "out", (N, n_tok, H, dv), out.dtype, dev)
+    desc = make_desc(N, n_tok, H, dk, dv, code, scale, out_dtype=_out_code(out.dtype),
+                     flags=KDA_FLAG_QK_L2NORM if qk_l2norm else 0)
     _check(_lib().kda_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
                         _ptr(state), ctypes.c_int32(n_tok), _ptr(out), _stream(stream)))
     return out
 
 
 @_allocates_on_launch_stream
-def step_rows(q, k, v, log_g, beta, state, scale=None, out=None, deltas=None, stream=None):
+def step_rows(q, k, v, log_g, beta, state, scale=None, out=None, deltas=None, stream=None,
+              out_dtype=torch.float32, qk_l2norm=False):
     """Speculative verify, first half: the outputs of rows [N, n_tok, H, d] as
     ``step`` would give them, with ``state`` left unchanged.  Returns (out,
-    deltas), both [N, n_tok, H, dv] fp32; ``deltas`` feeds ``step_commit``."""
+    deltas), both [N, n_tok, H, dv] (out in ``out_dtype``, deltas fp32);
+    ``deltas`` feeds ``step_commit``."""
     N, n_tok, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype
@@ -398,23 +417,25 @@ def step_rows(q, k, v, log_g, beta, state, scale=None, out=None, deltas=None, st
     _need(beta, "beta", (N, n_tok, H), torch.float32, dev)
     _need(state, "state", (N, H, dk, dv), torch.float32, dev)
     if out is None:
-        out = torch.empty((N, n_tok, H, dv), dtype=torch.float32, device=dev)
+        out = torch.empty((N, n_tok, H, dv), dtype=out_dtype, device=dev)
     else:
-        _need(out, "out", (N, n_tok, H, dv), torch.float32, dev)
+        _need(out, "out", (N, n_tok, H, dv), out.dtype, dev)
     if deltas is None:
         deltas = torch.empty((N, n_tok, H, dv), dtype=torch.float32, device=dev)
     else:
         _need(deltas, "deltas", (N, n_tok, H, dv), torch.float32, dev)
-    desc = make_desc(N, n_tok, H, dk, dv, code, scale)
+    desc = make_desc(N, n_tok, H, dk, dv, code, scale, out_dtype=_out_code(out.dtype),
+                     flags=KDA_FLAG_QK_L2NORM if qk_l2norm else 0)
     _check(_lib().kda_step_rows(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
                              _ptr(state), ctypes.c_int32(n_tok), _ptr(out), _ptr(deltas), _stream(stream)))
     return out, deltas
 
 
-def step_commit(k, log_g, deltas, state, accept, stream=None):
+def step_commit(k, log_g, deltas, state, accept, stream=None, qk_l2norm=False):
     """Speculative verify, second half: advance each sequence n of ``state``
     (in place) by its first ``accept[n]`` rows (int32 [N] on the device), from
-    the ``deltas`` that ``step_rows`` returned for the same rows and state."""
+    the ``deltas`` that ``step_rows`` returned for the same rows and state
+    (``qk_l2norm`` as given to ``step_rows``)."""
     N, n_tok, H, dk = k.shape
     dv = deltas.shape[-1]
     dev = k.device
@@ -423,6 +444,6 @@ def step_commit(k, log_g, deltas, state, accept, stream=None):
     _need(deltas, "deltas", (N, n_tok, H, dv), torch.float32, dev)
     _need(state, "state", (N, H, dk, dv), torch.float32, dev)
     _need(accept, "accept", (N,), torch.int32, dev)
-    desc = make_desc(N, n_tok, H, dk, dv, code, None)
+    desc = make_desc(N, n_tok, H, dk, dv, code, None, flags=KDA_FLAG_QK_L2NORM if qk_l2norm else 0)
     _check(_lib().kda_step_commit(ctypes.byref(desc), _ptr(k), _ptr(log_g), _ptr(deltas), _ptr(accept),
                                _ptr(state), ctypes.c_int32(n_tok), _stream(stream)))

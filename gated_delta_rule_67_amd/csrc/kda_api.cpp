@@ -56,6 +56,8 @@ kda::ChunkLaunch launch_of(const kda_desc* d, bool packed) {
   a.num_heads = d->num_heads;
   a.d = d->dk;
   a.bf16 = d->qkv_dtype == KDA_BF16;
+  a.out_bf16 = d->out_dtype == KDA_BF16;
+  a.l2 = (d->flags & KDA_FLAG_QK_L2NORM) != 0;
   return a;
 }
 
@@ -77,8 +79,8 @@ kda_status check_desc(const kda_desc* d, const char* fn) {
     return fail(KDA_ERR_UNSUPPORTED, "%s: dk != dv (%d vs %d) is not supported", fn, d->dk, d->dv);
   if (d->dk != 16 && d->dk != 32 && d->dk != 64 && d->dk != 128)
     return fail(KDA_ERR_UNSUPPORTED, "%s: head dim %d not in {16, 32, 64, 128}", fn, d->dk);
-  if (d->out_dtype != KDA_F32)
-    return fail(KDA_ERR_UNSUPPORTED, "%s: only fp32 out is supported", fn);
+  if ((d->flags & ~KDA_FLAG_QK_L2NORM) != 0 || d->reserved != 0)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: unknown flags 0x%x (reserved %u)", fn, d->flags, d->reserved);
   if (static_cast<int64_t>(d->num_seqs) * d->num_heads > (1 << 26))
     return fail(KDA_ERR_SHAPE, "%s: num_seqs * num_heads too large", fn);
   return KDA_OK;
@@ -212,6 +214,7 @@ kda_status kda_step_rows(const kda_desc* d, const void* q, const void* k, const 
   a.out = out; a.deltas = deltas;
   a.num_seqs = d->num_seqs; a.n_tok = n_tok; a.num_heads = d->num_heads;
   a.d = d->dk; a.bf16 = d->qkv_dtype == KDA_BF16; a.scale = resolve_scale(d);
+  a.out_bf16 = d->out_dtype == KDA_BF16; a.l2 = (d->flags & KDA_FLAG_QK_L2NORM) != 0;
   const hipError_t e = kda::launch_step(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
   return KDA_OK;
@@ -238,7 +241,7 @@ kda_status kda_step_commit(const kda_desc* d, const void* k, const float* log_g,
   kda::CommitLaunch a{};
   a.k = k; a.log_g = log_g; a.deltas = deltas; a.accept = accept; a.state = state_inout;
   a.num_seqs = d->num_seqs; a.n_tok = n_tok; a.num_heads = d->num_heads;
-  a.d = d->dk; a.bf16 = d->qkv_dtype == KDA_BF16;
+  a.d = d->dk; a.bf16 = d->qkv_dtype == KDA_BF16; a.l2 = (d->flags & KDA_FLAG_QK_L2NORM) != 0;
   const hipError_t e = kda::launch_commit(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
   return KDA_OK;
@@ -257,6 +260,7 @@ kda_status kda_step(const kda_desc* d, const void* q, const void* k, const void*
   a.state = state_inout; a.out = out;
   a.num_seqs = d->num_seqs; a.n_tok = n_tok; a.num_heads = d->num_heads;
   a.d = d->dk; a.bf16 = d->qkv_dtype == KDA_BF16; a.scale = resolve_scale(d);
+  a.out_bf16 = d->out_dtype == KDA_BF16; a.l2 = (d->flags & KDA_FLAG_QK_L2NORM) != 0;
   const hipError_t e = kda::launch_step(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
   return KDA_OK;
@@ -276,6 +280,8 @@ kda_status kda_chunk_bwd(const kda_desc* d, const void* q, const void* k, const 
   static const char* fn = "kda_chunk_bwd";
   kda_status st = check_desc(d, fn);
   if (st != KDA_OK) return st;
+  if (d->flags != 0)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: flags 0x%x are not supported by the backward", fn, d->flags);
   if (d->seq_len < 0) return fail(KDA_ERR_SHAPE, "%s: seq_len < 0", fn);
   const bool packed = cu_seqlens != nullptr;
   const int64_t tokens = packed ? d->seq_len : static_cast<int64_t>(d->num_seqs) * d->seq_len;

@@ -23,6 +23,23 @@ __device__ __forceinline__ float to_f32(bf16_t x) {
 __device__ __forceinline__ float bf16_lo(uint32_t packed) { return __uint_as_float(packed << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
 
+// Two fp32 values rounded to nearest even as packed bf16 (one
+// v_cvt_pk_bf16_f32); the first value in the low half.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16_pack2(float a, float b) {
+  bf16x2_t r;
+  r[0] = static_cast<__bf16>(a);
+  r[1] = static_cast<__bf16>(b);
+  return __builtin_bit_cast(uint32_t, r);
+}
+// Four consecutive outputs (8-byte aligned) as fp32 or rounded bf16.
+__device__ __forceinline__ void store_out4(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+__device__ __forceinline__ void store_out4(bf16_t* p, float a, float b, float c, float d) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(bf16_pack2(a, b), bf16_pack2(c, d));
+}
+
 // exp(x) through the hardware base-2 exponential; exp(-inf) = 0.
 __device__ __forceinline__ float exp_fast(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
@@ -78,6 +95,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void buffer_store16(f32x4 x, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, x), r, static_cast<int>(byte_off), 0, 0);
+}
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+// four fp32 values rounded to bf16, one 8-byte range-checked store
+__device__ __forceinline__ void buffer_store8_bf16(f32x4 x, __amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  const i32x2 v = {static_cast<int>(bf16_pack2(x[0], x[1])), static_cast<int>(bf16_pack2(x[2], x[3]))};
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, static_cast<int>(byte_off), 0, 0);
 }
 // Range-checked loads through the same descriptor: a lane whose access falls
 // outside the range reads zeros.

@@ -8,6 +8,9 @@
 // Glm5NextTextLinearAttention snippet): decay the key rows, read back S^T k,
 // form delta = beta (v - S^T k), add k delta^T; the output is read from the
 // updated state through S_new^T q = S_decayed^T q + delta (k . q).
+// With the q / k L2 normalisation the staged k and q rows are divided by
+// sqrt(sum of squares + eps) before the walk.  Outputs are fp32, or rounded
+// once to bf16.
 #pragma once
 
 #include "kda_common.h"
@@ -28,6 +31,8 @@ struct Stage {
   float v[TG][DVT];
   float beta[TG];
   float kq[TG];
+  float ik[TG];   // 1/|k| and 1/|q| of the staged rows (L2 normalisation)
+  float iq[TG];
   float red[2][NWAVE][DVT][2];
 };
 
@@ -37,9 +42,11 @@ struct Args {
   const bf16_t* v;
   const float* log_g;
   const float* beta;
-  float* out;
+  void* out;       // fp32, or bf16 when out_bf16
   int H;
   float scale;
+  bool out_bf16;
+  bool l2;         // L2-normalise the q and k rows
 };
 
 // Chunk ck of the document whose tokens start at tok_begin (ntok tokens), head
@@ -93,18 +100,42 @@ __device__ __forceinline__ void eval_chunk(Stage<NWAVE>& st, f32x4 (&s)[8 / NWAV
       if (tid < TG) st.beta[tid] = bb;
     }
     lds_barrier();
-    {  // kq[r] = k_r . q_r : 16 lanes per token, 8 channels each
+    {  // kq[r] = k_r . q_r (and k.k, q.q): 16 lanes per token, 8 channels each
       if (tid < 16 * TG) {
         const int r = tid >> 4, cc = (tid & 15) * 8;
-        float acc = 0.f;
+        float acc = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) acc += st.k[r][cc + c] * st.q[r][cc + c];
+        for (int c = 0; c < 8; ++c) {
+          acc += st.k[r][cc + c] * st.q[r][cc + c];
+          kk += st.k[r][cc + c] * st.k[r][cc + c];
+          qq += st.q[r][cc + c] * st.q[r][cc + c];
+        }
 #pragma unroll
-        for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
-        if ((tid & 15) == 0) st.kq[r] = acc;
+        for (int o = 1; o < 16; o <<= 1) {
+          acc += __shfl_xor(acc, o);
+          kk += __shfl_xor(kk, o);
+          qq += __shfl_xor(qq, o);
+        }
+        const float ik = p.l2 ? __frsqrt_rn(kk + 1e-6f) : 1.f;
+        const float iq = p.l2 ? __frsqrt_rn(qq + 1e-6f) : 1.f;
+        if ((tid & 15) == 0) {
+          st.kq[r] = acc * ik * iq;
+          st.ik[r] = ik;
+          st.iq[r] = iq;
+        }
       }
     }
     lds_barrier();
+    if (p.l2) {  // the staged rows normalised in place
+      constexpr int PER = TG * D / NT;
+#pragma unroll
+      for (int x = 0; x < PER; ++x) {
+        const int idx = tid + x * NT, r = idx / D, c = idx % D;
+        st.k[r][c] *= st.ik[r];
+        st.q[r][c] *= st.iq[r];
+      }
+      lds_barrier();
+    }
     for (int r = 0; r < tg; ++r) {
       const int par = (t0 + r) & 1;
       {
@@ -151,8 +182,14 @@ __device__ __forceinline__ void eval_chunk(Stage<NWAVE>& st, f32x4 (&s)[8 / NWAV
             B += st.red[par][x][n][1];
           }
           dl[b] = bt * (st.v[r][n] - A);
-          if (cw == 0 && lg == 0)
-            p.out[((tok0 + t0 + r) * H + h) * D + col0 + n] = p.scale * (B + dl[b] * kq);
+          if (cw == 0 && lg == 0) {
+            const size_t oi = ((tok0 + t0 + r) * H + h) * D + col0 + n;
+            const float o = p.scale * (B + dl[b] * kq);
+            if (p.out_bf16)
+              reinterpret_cast<__bf16*>(p.out)[oi] = static_cast<__bf16>(o);
+            else
+              static_cast<float*>(p.out)[oi] = o;
+          }
         }
 #pragma unroll
         for (int a = 0; a < NA; ++a)

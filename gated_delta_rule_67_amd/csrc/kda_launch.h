@@ -22,6 +22,8 @@ struct StepLaunch {
   int num_heads;
   int d;        // dk == dv
   bool bf16;    // q/k/v element type
+  bool out_bf16;  // out element type (else fp32)
+  bool l2;      // L2-normalise the q and k rows first
   float scale;
 };
 
@@ -37,6 +39,7 @@ struct CommitLaunch {
   int num_heads;
   int d;
   bool bf16;
+  bool l2;      // L2-normalise the k rows first
 };
 
 // Arguments of one chunked prefill launch; shapes already validated.
@@ -56,6 +59,8 @@ struct ChunkLaunch {
   int num_heads;
   int d;
   bool bf16;
+  bool out_bf16;              // out element type (else fp32)
+  bool l2;                    // L2-normalise the q and k rows first
   float scale;
 };
 

@@ -121,6 +121,8 @@ struct PrepArgs {
   float scale;
 };
 
+constexpr float L2_EPS = 1e-6f;  // eps inside the root of the q / k L2 normalisation
+
 struct __align__(16) PrepSmem {
   union {
     struct {
@@ -137,6 +139,7 @@ struct __align__(16) PrepSmem {
   f16 fDl[4][D];           // exp(R_I - M_I)
   f16 fDr[4][D];           // exp(M_I - R_{I+1})
   float beta[C];
+  float2 nrm[2][C];        // per channel half: (k.k, q.q) of each row (L2 normalisation)
   f16x4 frag[NFRAG][64];
 };
 
@@ -187,6 +190,7 @@ __device__ __forceinline__ bool t_column(PrepSmem& sm, f16x4 tbJ, int lane) {
   return bad;
 }
 
+template <bool L2>
 __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) prep_kernel(PrepArgs p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   PrepSmem& sm = *reinterpret_cast<PrepSmem*>(smem_raw);
@@ -267,7 +271,46 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
       }
       bad |= !(fabsf(bt[j]) <= BETA_MAX);
     }
-    bad |= mk[0] > QK_MAX_BITS || mk[1] > QK_MAX_BITS || mv[0] > V_MAX_BITS || mv[1] > V_MAX_BITS;
+    // normalised q and k rows are at most 1 in magnitude: only v is bounded then
+    if (!L2) bad |= mk[0] > QK_MAX_BITS || mk[1] > QK_MAX_BITS;
+    bad |= mv[0] > V_MAX_BITS || mv[1] > V_MAX_BITS;
+  }
+  // L2 normalisation: 1/|k| and 1/|q| of rows r0, r0+1.  A row's channels sit
+  // in the eight oct lanes of this wave and of its partner wave w^1 (the other
+  // channel half): a shuffle reduction, then one exchange through LDS.
+  float ikr[2] = {1.f, 1.f}, iqr[2] = {1.f, 1.f};
+  if (L2) {
+    float kk[2], qq[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t kw[4] = {kr[j].x, kr[j].y, kr[j].z, kr[j].w};
+      const uint32_t qw[4] = {qr[j].x, qr[j].y, qr[j].z, qr[j].w};
+      float a = 0.f, b = 0.f;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float k0 = bf16_lo(kw[x]), k1 = bf16_hi(kw[x]), q0 = bf16_lo(qw[x]), q1 = bf16_hi(qw[x]);
+        a += k0 * k0 + k1 * k1;
+        b += q0 * q0 + q1 * q1;
+      }
+#pragma unroll
+      for (int o = 1; o < 8; o <<= 1) {
+        a += __shfl_xor(a, o, 64);
+        b += __shfl_xor(b, o, 64);
+      }
+      kk[j] = a;
+      qq[j] = b;
+    }
+    if (oct == 0) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) sm.nrm[w & 1][r0 + j] = make_float2(kk[j], qq[j]);
+    }
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float2 o = sm.nrm[(w & 1) ^ 1][r0 + j];
+      ikr[j] = __frsqrt_rn(kk[j] + o.x + L2_EPS);
+      iqr[j] = __frsqrt_rn(qq[j] + o.y + L2_EPS);
+    }
   }
   f16x8 hl[2], hr[2], xv[2];  // k exp(G - R), k exp(R' - G), beta v of rows r0, r0+1
   {
@@ -305,8 +348,8 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
           const uint32_t kw = c < 2 ? kr[j].x : c < 4 ? kr[j].y : c < 6 ? kr[j].z : kr[j].w;
           const uint32_t qw = c < 2 ? qr[j].x : c < 4 ? qr[j].y : c < 6 ? qr[j].z : qr[j].w;
           const uint32_t vw = c < 2 ? vr[j].x : c < 4 ? vr[j].y : c < 6 ? vr[j].z : vr[j].w;
-          const float kv = (c & 1) ? bf16_hi(kw) : bf16_lo(kw);
-          const float qv = (c & 1) ? bf16_hi(qw) : bf16_lo(qw);
+          const float kv = ((c & 1) ? bf16_hi(kw) : bf16_lo(kw)) * ikr[j];
+          const float qv = ((c & 1) ? bf16_hi(qw) : bf16_lo(qw)) * iqr[j];
           const float vv = (c & 1) ? bf16_hi(vw) : bf16_lo(vw);
           hl[j][c] = (f16)(kv * Pv[j]);
           hq4[j][cc] = (f16)(qv * Pv[j]);
@@ -593,7 +636,9 @@ struct ScanArgs {
   const int32_t* cstart;      // packed: first chunk slot of each document
   const int32_t* order;       // null: identity document order
   const unsigned char* ws;    // chunk slots
-  float* out;
+  void* out;                  // fp32, or bf16 when out_bf16
+  bool out_bf16;
+  bool l2;                    // q / k rows L2-normalised (the fallback normalises its own)
   int num_docs;
   int T;
   int H;
@@ -731,7 +776,7 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
     for (int e = 0; e < 4; ++e)
       s[0][b][e] = p.init_state ? p.init_state[unit_state + (16 * w + 4 * lg + e) * D + col0 + 16 * b + lc] : 0.f;
   write_st(s);
-  const fb::Args fa{p.q, p.k, p.v, p.log_g, p.beta, p.out, H, p.scale};
+  const fb::Args fa{p.q, p.k, p.v, p.log_g, p.beta, p.out, H, p.scale, p.out_bf16, p.l2};
 
   // One chunk: consume cur (chunk k); each group of cur's registers is
   // refilled with chunk k+2 right after its last use (clamped to the last
@@ -812,11 +857,18 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
       write_st(s);
       // output rows past the document's end fall outside the resource; the
       // Delta waves' copy of the store gets an empty resource (dropped)
+      const uint32_t osz = p.out_bf16 ? 2u : 4u;
       const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(
-          p.out + (tok0 * H + h) * D + col0, is_o ? static_cast<uint32_t>(((nv - 1) * H * D + DVT) * 4) : 0u);
-      const uint32_t ooff = static_cast<uint32_t>(((16 * I + lc) * H * D + 4 * lg) * 4);
+          static_cast<unsigned char*>(p.out) + ((tok0 * H + h) * D + col0) * osz,
+          is_o ? static_cast<uint32_t>(((nv - 1) * H * D + DVT)) * osz : 0u);
+      const uint32_t ooff = static_cast<uint32_t>((16 * I + lc) * H * D + 4 * lg) * osz;
+      if (p.out_bf16) {  // kernel-argument branch: uniform
 #pragma unroll
-      for (int b = 0; b < 2; ++b) buffer_store16(oacc[b], orsrc, ooff + 64 * b);
+        for (int b = 0; b < 2; ++b) buffer_store8_bf16(oacc[b], orsrc, ooff + 32 * b);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) buffer_store16(oacc[b], orsrc, ooff + 64 * b);
+      }
     } else {
       // token by token from the entry state; writes this chunk's outputs
       __syncthreads();
@@ -972,8 +1024,11 @@ static hipError_t prepare_device() {
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= MAX_DEV) return hipErrorInvalidDevice;
   if (!ready[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(sizeof(PrepSmem)));
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sizeof(PrepSmem)));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(prep_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sizeof(PrepSmem)));
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(sizeof(ScanSmem)));
@@ -1017,8 +1072,12 @@ hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream) {
     pp.H = a.num_heads;
     pp.nchd = nchd;
     pp.scale = a.scale;
-    hipLaunchKernelGGL(prep_kernel, dim3(static_cast<unsigned>(ns * a.num_heads)), dim3(NTP), sizeof(PrepSmem),
-                       stream, pp);
+    if (a.l2)
+      hipLaunchKernelGGL(prep_kernel<true>, dim3(static_cast<unsigned>(ns * a.num_heads)), dim3(NTP),
+                         sizeof(PrepSmem), stream, pp);
+    else
+      hipLaunchKernelGGL(prep_kernel<false>, dim3(static_cast<unsigned>(ns * a.num_heads)), dim3(NTP),
+                         sizeof(PrepSmem), stream, pp);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1034,7 +1093,9 @@ hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream) {
   sp.cstart = packed ? l.cstart : nullptr;
   sp.order = (packed && a.num_seqs > 1 && a.num_seqs <= 4096) ? l.order : nullptr;
   sp.ws = l.slots;
-  sp.out = static_cast<float*>(a.out);
+  sp.out = a.out;
+  sp.out_bf16 = a.out_bf16;
+  sp.l2 = a.l2;
   sp.num_docs = a.num_seqs;
   sp.T = a.seq_len;
   sp.H = a.num_heads;

@@ -16,14 +16,6 @@ __device__ __forceinline__ void load8f(const bf16_t* p, float (&o)[8]) {
   o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x); o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
   o[4] = bf16_lo(u.z); o[5] = bf16_hi(u.z); o[6] = bf16_lo(u.w); o[7] = bf16_hi(u.w);
 }
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-// two values rounded to nearest even as packed bf16 (one v_cvt_pk_bf16_f32)
-__device__ __forceinline__ uint32_t bf16_pack2(float a, float b) {
-  bf16x2_t r;
-  r[0] = static_cast<__bf16>(a);
-  r[1] = static_cast<__bf16>(b);
-  return __builtin_bit_cast(uint32_t, r);
-}
 __device__ __forceinline__ void store8f(float* p, const float (&v)[8]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);

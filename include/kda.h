@@ -22,7 +22,9 @@
  *      beta        : [batch, seq, heads]         states : [N, heads, dk, dv]
  *    (the [batch, sequence, heads, head_dim] layout of `_torch_recurrent_kda`).
  *  - q, k, v have element type desc->qkv_dtype (fp32 or bf16); log_g, beta and
- *    states are fp32; out has element type desc->out_dtype (fp32 only in v1).
+ *    states are fp32; out has element type desc->out_dtype: fp32, or bf16
+ *    (the fp32 result rounded once to nearest even) for kda_chunk_fwd,
+ *    kda_step and kda_step_rows.
  *  - Every data pointer is a DEVICE pointer owned by the caller and must be
  *    16-byte aligned.  The library never allocates, frees or caches device
  *    memory; scratch comes from desc->workspace.  The descriptor itself is host
@@ -36,8 +38,13 @@
  *    across the ABI.
  *  - Preconditions the library does not check (they live in device memory):
  *    log_g <= 0 (log_g = -inf allowed), cu_seqlens well formed.
- *  - Supported in v1: dk == dv in {16, 32, 64, 128}; qkv_dtype fp32 or bf16;
- *    out_dtype fp32.  Anything else returns KDA_ERR_UNSUPPORTED.
+ *  - Supported: dk == dv in {16, 32, 64, 128}; qkv_dtype fp32 or bf16;
+ *    out_dtype as above.  Anything else returns KDA_ERR_UNSUPPORTED.
+ *  - desc->flags selects options (KDA_FLAG_*); unknown bits return
+ *    KDA_ERR_UNSUPPORTED.
+ *  - Environment: KDA_VALIDATE=1 makes kda_chunk_fwd and kda_step check their
+ *    device-resident preconditions and results (see below); it synchronises
+ *    the stream and is meant for debugging only.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -49,7 +56,18 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
+
+/* desc->flags bits.
+ * KDA_FLAG_QK_L2NORM: every (token, head) row of q and of k is divided by
+ *   sqrt(sum of its squares + 1e-6) inside the kernels before the recurrence
+ *   uses it (the optional normalisation step in front of the mixer; the pages
+ *   do not print it, and this plain L2 form with eps inside the root is the
+ *   reading taken).  Honoured by kda_chunk_fwd, kda_step, kda_step_rows and
+ *   kda_step_commit (which normalises the k rows it replays); kda_chunk_bwd
+ *   returns KDA_ERR_UNSUPPORTED with it. */
+#define KDA_FLAG_QK_L2NORM 1u
+#define KDA_QK_L2NORM_EPS 1e-6f
 
 typedef enum {
   KDA_OK = 0,
@@ -73,11 +91,13 @@ typedef struct kda_desc {
   int32_t dk;        /* key / query head dim  (rows of S)                        */
   int32_t dv;        /* value head dim        (columns of S)                     */
   int32_t qkv_dtype; /* kda_dtype of q, k, v                                     */
-  int32_t out_dtype; /* kda_dtype of out (KDA_F32)                               */
+  int32_t out_dtype; /* kda_dtype of out                                        */
   float scale;       /* output scale; 0 selects dk^-0.5                          */
   void* workspace;   /* device scratch of kda_chunk_fwd, at least
                         kda_chunk_workspace_bytes(desc, packed) bytes          */
   size_t workspace_bytes;
+  uint32_t flags;    /* KDA_FLAG_* bits; 0 = none                                */
+  uint32_t reserved; /* must be 0                                                */
 } kda_desc;
 
 /* ABI version of the loaded library (KDA_ABI_VERSION it was built with). */
@@ -91,7 +111,9 @@ const char* kda_last_error(void);
 
 /* Device scratch bytes kda_chunk_fwd needs for this descriptor; packed != 0
  * for a call with cu_seqlens (desc->seq_len = total tokens, num_seqs =
- * documents), 0 for a dense batch.  For bf16 q/k/v with d = 128 the chunked
+ * documents), 0 for a dense batch.  The descriptor alone cannot tell the two
+ * apart (num_seqs and seq_len mean different things in each), and the slot
+ * count differs: dense B * ceil(T/64), packed ceil(T/64) + N.  For bf16 q/k/v with d = 128 the chunked
  * prefill stages fp16 per-chunk operands there: 73 KiB per 64-token
  * chunk and head (dense: B * ceil(T/64) chunks; packed: ceil(T/64) + N, an
  * upper bound), plus a few bytes per document when packed.  Other
@@ -121,10 +143,16 @@ size_t kda_chunk_workspace_bytes(const kda_desc* desc, int packed);
  * Evaluation path: bf16 q/k/v with d = 128 take the two-pass chunked kernels
  * (per-chunk operands staged in the workspace); other inputs take the
  * token-recurrent kernel.  The environment variable KDA_PREFILL_PATH, read at
- * every call, overrides this for testing: "fused" selects the single-pass
- * chunked kernel (bf16, d = 128; a few workspace bytes per document), and
- * "recurrent" the token-recurrent kernel.  A workspace smaller than the
- * selected path needs returns KDA_ERR_WORKSPACE before anything is enqueued.
+ * every call, set to "recurrent" forces the token-recurrent kernel (a test
+ * and diagnosis switch).  A workspace smaller than the selected path needs
+ * returns KDA_ERR_WORKSPACE before anything is enqueued.
+ *
+ * KDA_VALIDATE=1 (read at every call): before the launch, the call copies
+ * cu_seqlens and log_g to the host and returns KDA_ERR_SHAPE if cu_seqlens
+ * is not [0, ..., seq_len] non-decreasing or any log_g is NaN or positive;
+ * it fills out and final_state with NaN first, and after the kernels (a
+ * stream synchronisation) returns KDA_ERR_HIP if any element of out or
+ * final_state was left unwritten or is not finite.
  */
 kda_status kda_chunk_fwd(const kda_desc* desc, const void* q, const void* k,
                          const void* v, const float* log_g, const float* beta,
@@ -142,6 +170,8 @@ kda_status kda_chunk_fwd(const kda_desc* desc, const void* q, const void* k,
  * Rows of one sequence are applied in order t = 0 .. n_tok-1 (metrale
  * glm5next_layer invariants: verify row t uses slot t; decode is n_tok = 1).
  * N = desc->num_seqs; desc->seq_len is ignored; no workspace is used.
+ * KDA_VALIDATE=1 checks log_g on the host first and the finiteness of out
+ * and of the updated state after the kernel, as for kda_chunk_fwd.
  */
 kda_status kda_step(const kda_desc* desc, const void* q, const void* k,
                     const void* v, const float* log_g, const float* beta,
@@ -203,7 +233,8 @@ kda_status kda_step_commit(const kda_desc* desc, const void* k,
  *                  pass d_final_state through unchanged)
  * No output may alias an input or another output.  Everything is computed
  * in fp32 (fp32 matrix-core products, fp32 state); the forward is recomputed
- * inside the call, so out and final_state are not inputs.
+ * inside the call, so out and final_state are not inputs.  desc->out_dtype
+ * is ignored; desc->flags must be 0 (KDA_FLAG_QK_L2NORM: unsupported).
  *
  * desc->workspace must hold kda_chunk_bwd_workspace_bytes(desc, packed)
  * bytes whenever there are tokens or the problem is packed: about 465 KiB

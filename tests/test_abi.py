@@ -38,7 +38,7 @@ def test_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert kda.abi_version() == 6
+    assert kda.abi_version() == 7
     seen = set()
     for code in range(8):
         s = lib.kda_status_string(code).decode()
@@ -52,7 +52,7 @@ def desc(**kw):
     base.update(kw)
     d = kda.make_desc(base["num_seqs"], base["seq_len"], base["H"], base["dk"], base["dv"],
                       base["qkv_dtype"], base.get("scale"))
-    for f in ("out_dtype", "workspace", "workspace_bytes"):
+    for f in ("out_dtype", "workspace", "workspace_bytes", "flags", "reserved"):
         if f in kw:
             setattr(d, f, kw[f])
     return d
@@ -102,8 +102,30 @@ def test_unsupported_dims(dk, dv):
     assert "kda_" in last()
 
 
-def test_bf16_out_unsupported():
-    assert chunk(desc(out_dtype=kda.KDA_BF16)) == UNSUPPORTED
+def test_bf16_out_passes_validation():
+    # accepted: the call gets as far as the missing workspace (chunked) or a no-op (no sequences)
+    assert chunk(desc(out_dtype=kda.KDA_BF16)) == WORKSPACE
+    assert step(desc(num_seqs=0, out_dtype=kda.KDA_BF16), q=None, k=None, v=None, g=None, b=None, s=None,
+                out=None) == OK
+
+
+def test_flags():
+    assert chunk(desc(flags=kda.KDA_FLAG_QK_L2NORM)) == WORKSPACE      # known flag: validation goes on
+    for bad in (2, 0x80000000):
+        assert chunk(desc(flags=bad)) == UNSUPPORTED
+        assert "flags" in last()
+        assert step(desc(flags=bad)) == UNSUPPORTED
+    assert chunk(desc(reserved=1)) == UNSUPPORTED
+    # the backward takes no flags
+    d = desc(flags=kda.KDA_FLAG_QK_L2NORM)
+    assert lib.kda_chunk_bwd(ctypes.byref(d), *([P(0)] * 15), None) == UNSUPPORTED
+    assert "backward" in last()
+
+
+def test_descriptor_layout_matches_the_header():
+    # kda_desc: 8 int32/float fields, a pointer, a size_t, then flags and reserved (56 bytes on LP64)
+    assert ctypes.sizeof(kda.KdaDesc) == 56
+    assert kda.KdaDesc.flags.offset == 48 and kda.KdaDesc.reserved.offset == 52
 
 
 def test_non_finite_scale():
