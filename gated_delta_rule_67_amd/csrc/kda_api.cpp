@@ -14,7 +14,10 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <vector>
+
 #include "kda_launch.h"
+#include "kda_validate.h"
 
 namespace {
 
@@ -90,6 +93,60 @@ float resolve_scale(const kda_desc* d) {
   return d->scale != 0.0f ? d->scale : 1.0f / std::sqrt(static_cast<float>(d->dk));
 }
 
+bool validate_mode() {
+  const char* e = std::getenv("KDA_VALIDATE");
+  return e && std::strcmp(e, "1") == 0;
+}
+
+// KDA_VALIDATE=1, before a launch: cu_seqlens and log_g copied to the host
+// and checked (the preconditions that live in device memory).
+kda_status validate_inputs(const int32_t* cu_seqlens, int num_docs, int64_t tokens, const float* log_g,
+                           size_t n_log_g, hipStream_t s, const char* fn) {
+  int64_t where = 0;
+  if (cu_seqlens) {
+    std::vector<int32_t> cu(static_cast<size_t>(num_docs) + 1);
+    if (hipMemcpyAsync(cu.data(), cu_seqlens, cu.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return fail(KDA_ERR_HIP, "%s (KDA_VALIDATE): copying cu_seqlens failed", fn);
+    if (const char* m = kda::validate::cu_seqlens(cu.data(), num_docs, tokens, &where))
+      return fail(KDA_ERR_SHAPE, "%s (KDA_VALIDATE): %s (entry %lld)", fn, m, (long long)where);
+  }
+  if (n_log_g > 0) {
+    std::vector<float> g(n_log_g);
+    if (hipMemcpyAsync(g.data(), log_g, n_log_g * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return fail(KDA_ERR_HIP, "%s (KDA_VALIDATE): copying log_g failed", fn);
+    if (const char* m = kda::validate::log_gates(g.data(), n_log_g, &where))
+      return fail(KDA_ERR_SHAPE, "%s (KDA_VALIDATE): %s (element %lld)", fn, m, (long long)where);
+  }
+  return KDA_OK;
+}
+
+// KDA_VALIDATE=1, after a launch: every element of an output finite (the
+// outputs were filled with NaN before the launch, so an unwritten element
+// shows up too).
+kda_status validate_output(const void* p, size_t count, bool bf16, const char* name, hipStream_t s,
+                           const char* fn) {
+  if (!p || count == 0) return KDA_OK;
+  int64_t where = 0;
+  const char* m = nullptr;
+  if (bf16) {
+    std::vector<uint16_t> h(count);
+    if (hipMemcpyAsync(h.data(), p, count * 2, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return fail(KDA_ERR_HIP, "%s (KDA_VALIDATE): copying %s failed", fn, name);
+    m = kda::validate::finite_bf16(h.data(), count, &where);
+  } else {
+    std::vector<float> h(count);
+    if (hipMemcpyAsync(h.data(), p, count * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return fail(KDA_ERR_HIP, "%s (KDA_VALIDATE): copying %s failed", fn, name);
+    m = kda::validate::finite_f32(h.data(), count, &where);
+  }
+  if (m) return fail(KDA_ERR_HIP, "%s (KDA_VALIDATE): element %lld of %s %s", fn, (long long)where, name, m);
+  return KDA_OK;
+}
+
 kda_status check_ptr(const void* p, const char* name, const char* fn, bool required) {
   if (!p) return required ? fail(KDA_ERR_NULL, "%s: %s is NULL", fn, name) : KDA_OK;
   if (misaligned(p)) return fail(KDA_ERR_ALIGN, "%s: %s is not 16-byte aligned", fn, name);
@@ -150,48 +207,8 @@ size_t kda_chunk_workspace_bytes(const kda_desc* d, int packed) {
 kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const void* v,
                          const float* log_g, const float* beta, const float* init_state,
                          const int32_t* cu_seqlens, void* out, float* final_state, void* stream) {
-  static const char* fn = "kda_chunk_fwd";
-  kda_status st = check_desc(d, fn);
-  if (st != KDA_OK) return st;
-  if (d->seq_len < 0) return fail(KDA_ERR_SHAPE, "%s: seq_len < 0", fn);
-  const bool packed = cu_seqlens != nullptr;
-  const int64_t tokens = packed ? d->seq_len : static_cast<int64_t>(d->num_seqs) * d->seq_len;
-  if (tokens > INT32_MAX / 2) return fail(KDA_ERR_SHAPE, "%s: too many tokens (%lld)", fn, (long long)tokens);
-  if (packed && d->num_seqs == 0 && d->seq_len != 0)
-    return fail(KDA_ERR_SHAPE, "%s: packed problem with tokens but no documents", fn);
-  const bool has_tok = tokens > 0;
-  const bool has_units = d->num_seqs > 0;
-  if ((st = check_ptr(q, "q", fn, has_tok)) != KDA_OK) return st;
-  if ((st = check_ptr(k, "k", fn, has_tok)) != KDA_OK) return st;
-  if ((st = check_ptr(v, "v", fn, has_tok)) != KDA_OK) return st;
-  if ((st = check_ptr(log_g, "log_g", fn, has_tok)) != KDA_OK) return st;
-  if ((st = check_ptr(beta, "beta", fn, has_tok)) != KDA_OK) return st;
-  if ((st = check_ptr(out, "out", fn, has_tok)) != KDA_OK) return st;
-  if ((st = check_ptr(init_state, "init_state", fn, false)) != KDA_OK) return st;
-  if ((st = check_ptr(final_state, "final_state", fn, false)) != KDA_OK) return st;
-  if ((st = check_ptr(cu_seqlens, "cu_seqlens", fn, false)) != KDA_OK) return st;
-  if (out && (out == q || out == k || out == v || out == log_g || out == beta || out == init_state))
-    return fail(KDA_ERR_SHAPE, "%s: out aliases an input", fn);
-  kda::ChunkLaunch a = launch_of(d, packed);
-  const Path path = prefill_path(a);
-  const size_t ws_need = workspace_need(path, a);
-  if (ws_need > 0) {
-    if (!d->workspace || d->workspace_bytes < ws_need)
-      return fail(KDA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, ws_need,
-                  d->workspace ? d->workspace_bytes : size_t(0));
-    if (misaligned(d->workspace)) return fail(KDA_ERR_ALIGN, "%s: workspace is not 16-byte aligned", fn);
-  }
-  if (!has_units || (!has_tok && !final_state)) return KDA_OK;
-
-  a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
-  a.init_state = init_state; a.cu_seqlens = cu_seqlens;
-  a.out = out; a.final_state = final_state;
-  a.workspace = ws_need > 0 ? d->workspace : nullptr;
-  a.scale = resolve_scale(d);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = path == Path::TwoPass ? kda::launch_chunk_twopass(a, s) : kda::launch_chunk_recurrent(a, s);
-  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
-  return KDA_OK;
+  return kda::chunk_fwd_checked(d, q, k, v, log_g, beta, init_state, cu_seqlens, out, final_state, stream,
+                                d ? d->workspace : nullptr, d ? d->workspace_bytes : 0, false, "kda_chunk_fwd");
 }
 
 kda_status kda_step_rows(const kda_desc* d, const void* q, const void* k, const void* v,
@@ -261,8 +278,25 @@ kda_status kda_step(const kda_desc* d, const void* q, const void* k, const void*
   a.num_seqs = d->num_seqs; a.n_tok = n_tok; a.num_heads = d->num_heads;
   a.d = d->dk; a.bf16 = d->qkv_dtype == KDA_BF16; a.scale = resolve_scale(d);
   a.out_bf16 = d->out_dtype == KDA_BF16; a.l2 = (d->flags & KDA_FLAG_QK_L2NORM) != 0;
-  const hipError_t e = kda::launch_step(a, static_cast<hipStream_t>(stream));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t n_out = static_cast<size_t>(d->num_seqs) * n_tok * d->num_heads * d->dv;
+  const bool check = validate_mode();
+  if (check) {
+    const kda_status vs = validate_inputs(nullptr, 0, 0, log_g, n_out / d->dv * d->dk, s, fn);
+    if (vs != KDA_OK) return vs;
+    if (hipMemsetAsync(out, 0xff, n_out * (a.out_bf16 ? 2 : 4), s) != hipSuccess)
+      return fail(KDA_ERR_HIP, "%s (KDA_VALIDATE): NaN fill failed", fn);
+  }
+  const hipError_t e = kda::launch_step(a, s);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  if (check) {
+    if (hipStreamSynchronize(s) != hipSuccess) return fail(KDA_ERR_HIP, "%s (KDA_VALIDATE): kernel failed", fn);
+    kda_status vs = validate_output(out, n_out, a.out_bf16, "out", s, fn);
+    if (vs != KDA_OK) return vs;
+    vs = validate_output(state_inout, static_cast<size_t>(d->num_seqs) * d->num_heads * d->dk * d->dv, false,
+                         "state_inout", s, fn);
+    if (vs != KDA_OK) return vs;
+  }
   return KDA_OK;
 }
 
@@ -418,3 +452,73 @@ kda_status kda_gated_rmsnorm(const kda_desc* d, const float* o, const void* gate
 }
 
 }  // extern "C"
+
+namespace kda {
+
+kda_status chunk_fwd_checked(const kda_desc* d, const void* q, const void* k, const void* v, const float* log_g,
+                             const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
+                             float* final_state, void* stream, void* ws, size_t ws_bytes, bool fixed_ws,
+                             const char* fn) {
+  kda_status st = check_desc(d, fn);
+  if (st != KDA_OK) return st;
+  if (d->seq_len < 0) return fail(KDA_ERR_SHAPE, "%s: seq_len < 0", fn);
+  const bool packed = cu_seqlens != nullptr;
+  const int64_t tokens = packed ? d->seq_len : static_cast<int64_t>(d->num_seqs) * d->seq_len;
+  if (tokens > INT32_MAX / 2) return fail(KDA_ERR_SHAPE, "%s: too many tokens (%lld)", fn, (long long)tokens);
+  if (packed && d->num_seqs == 0 && d->seq_len != 0)
+    return fail(KDA_ERR_SHAPE, "%s: packed problem with tokens but no documents", fn);
+  const bool has_tok = tokens > 0;
+  const bool has_units = d->num_seqs > 0;
+  if ((st = check_ptr(q, "q", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(k, "k", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(v, "v", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(log_g, "log_g", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(beta, "beta", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(out, "out", fn, has_tok)) != KDA_OK) return st;
+  if ((st = check_ptr(init_state, "init_state", fn, false)) != KDA_OK) return st;
+  if ((st = check_ptr(final_state, "final_state", fn, false)) != KDA_OK) return st;
+  if ((st = check_ptr(cu_seqlens, "cu_seqlens", fn, false)) != KDA_OK) return st;
+  if (out && (out == q || out == k || out == v || out == log_g || out == beta || out == init_state))
+    return fail(KDA_ERR_SHAPE, "%s: out aliases an input", fn);
+  kda::ChunkLaunch a = launch_of(d, packed);
+  const Path path = prefill_path(a);
+  const size_t ws_need = workspace_need(path, a);
+  if (ws_need > 0) {
+    if (fixed_ws && ws_bytes < ws_need)
+      return fail(KDA_ERR_WORKSPACE, "%s: the problem needs %zu bytes of scratch; the fixed scratch holds %zu", fn,
+                  ws_need, ws_bytes);
+    if (!ws || ws_bytes < ws_need)
+      return fail(KDA_ERR_WORKSPACE, "%s: workspace needs %zu bytes (got %zu)", fn, ws_need, ws ? ws_bytes : size_t(0));
+    if (misaligned(ws)) return fail(KDA_ERR_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+  }
+  if (!has_units || (!has_tok && !final_state)) return KDA_OK;
+
+  a.q = q; a.k = k; a.v = v; a.log_g = log_g; a.beta = beta;
+  a.init_state = init_state; a.cu_seqlens = cu_seqlens;
+  a.out = out; a.final_state = final_state;
+  a.workspace = ws_need > 0 ? ws : nullptr;
+  a.scale = resolve_scale(d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t n_out = static_cast<size_t>(tokens) * d->num_heads * d->dv;
+  const size_t n_fin = static_cast<size_t>(d->num_seqs) * d->num_heads * d->dk * d->dv;
+  const bool check = validate_mode();
+  if (check) {
+    st = validate_inputs(cu_seqlens, d->num_seqs, d->seq_len, log_g, static_cast<size_t>(tokens) * d->num_heads * d->dk,
+                         s, fn);
+    if (st != KDA_OK) return st;
+    // NaN fill (all-ones bits are a NaN in fp32 and in bf16): unwritten elements stay NaN
+    if (hipMemsetAsync(out, 0xff, n_out * (a.out_bf16 ? 2 : 4), s) != hipSuccess ||
+        (final_state && final_state != init_state && hipMemsetAsync(final_state, 0xff, n_fin * 4, s) != hipSuccess))
+      return fail(KDA_ERR_HIP, "%s (KDA_VALIDATE): NaN fill failed", fn);
+  }
+  const hipError_t e = path == Path::TwoPass ? kda::launch_chunk_twopass(a, s) : kda::launch_chunk_recurrent(a, s);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  if (check) {
+    if (hipStreamSynchronize(s) != hipSuccess) return fail(KDA_ERR_HIP, "%s (KDA_VALIDATE): kernel failed", fn);
+    if ((st = validate_output(out, n_out, a.out_bf16, "out", s, fn)) != KDA_OK) return st;
+    if ((st = validate_output(final_state, n_fin, false, "final_state", s, fn)) != KDA_OK) return st;
+  }
+  return KDA_OK;
+}
+
+}  // namespace kda

@@ -4,7 +4,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/kda.h"
+
 namespace kda {
+
+// kda_chunk_fwd's validation and launch with the workspace given explicitly:
+// the caller's (desc->workspace) or the library's fixed scratch (fixed_ws,
+// ws_bytes = its capacity).  fn names the entry point in error messages.
+kda_status chunk_fwd_checked(const kda_desc* d, const void* q, const void* k, const void* v, const float* log_g,
+                             const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
+                             float* final_state, void* stream, void* ws, size_t ws_bytes, bool fixed_ws,
+                             const char* fn);
 
 // Arguments of one decode / verify launch; shapes already validated.
 struct StepLaunch {

@@ -206,3 +206,47 @@ def test_packed_workload_qk_l2norm_and_bf16_out():
     e_f = err(fin.cpu().numpy(), ref_f)
     print(f"[varlen L2 + bf16 out] {bar:.3f} of the bar, err_final={e_f:.3e}", flush=True)
     assert bar <= 1.0 and e_f <= TOL["bf16"]
+
+
+# ---------------------------------------------------------------- KDA_VALIDATE=1
+def test_validate_mode_passes_good_calls(monkeypatch):
+    monkeypatch.setenv("KDA_VALIDATE", "1")
+    inp = kda_inputs.make_inputs(B=1, T=300, H=2, dk=128, dv=128, dtype="bf16", seed=330,
+                                 lengths=[0, 100, 200], init="normal", init_std=0.05)
+    out, fin = chunk(inp)
+    ref_o, ref_f = oracle_full(inp)
+    assert err(out.cpu().numpy(), ref_o) <= TOL["bf16"] and err(fin.cpu().numpy(), ref_f) <= TOL["bf16"]
+    d = to_dev(kda_inputs.make_inputs(B=4, T=2, H=2, dk=64, dv=64, dtype="f32", seed=331))
+    kda.step(d["q"], d["k"], d["v"], d["log_g"], d["beta"], d["init_state"].clone(), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+
+
+def test_validate_mode_rejects_bad_device_inputs(monkeypatch):
+    monkeypatch.setenv("KDA_VALIDATE", "1")
+    inp = kda_inputs.make_inputs(B=1, T=300, H=2, dk=128, dv=128, dtype="bf16", seed=332,
+                                 lengths=[100, 200], init="normal", init_std=0.05)
+    d = to_dev(inp)
+    call = lambda cu, g: kda.chunk_fwd(d["q"], d["k"], d["v"], g, d["beta"], init_state=d["init_state"],
+                                       cu_seqlens=cu)
+    for bad in ([0, 200, 100], [0, 100, 299], [5, 100, 300]):   # decreasing, short total, bad start
+        with pytest.raises(kda.KdaError) as ei:
+            call(torch.tensor(bad, dtype=torch.int32, device="cuda"), d["log_g"])
+        assert ei.value.status == 2 and "KDA_VALIDATE" in str(ei.value)
+    g = d["log_g"].clone()
+    g[0, 150, 1, 3] = 0.5                                          # not a decay
+    with pytest.raises(kda.KdaError) as ei:
+        call(d["cu_seqlens"], g)
+    assert ei.value.status == 2 and "positive" in str(ei.value)
+    g[0, 150, 1, 3] = float("nan")
+    with pytest.raises(kda.KdaError):
+        call(d["cu_seqlens"], g)
+
+
+def test_validate_mode_reports_non_finite_outputs(monkeypatch):
+    """Unnormalised keys (|k|^2 ~ 1000) make the recurrence itself diverge: the
+    call runs, and the mode reports the non-finite output."""
+    monkeypatch.setenv("KDA_VALIDATE", "1")
+    inp = unnormalised(kda_inputs.make_inputs(B=1, T=200, H=2, dk=128, dv=128, dtype="bf16", seed=333), seed=334)
+    with pytest.raises(kda.KdaError) as ei:
+        chunk(inp)
+    assert ei.value.status == 7 and "not finite" in str(ei.value)
