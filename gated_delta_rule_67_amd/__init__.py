@@ -31,13 +31,14 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_bwd", "step", "step_rows", "step_commit", "short_conv", "gated_rmsnorm",
+__all__ = ["chunk_fwd", "chunk_fwd_static", "chunk_bwd", "step", "step_rows", "step_commit", "short_conv", "gated_rmsnorm",
            "workspace_bytes", "bwd_workspace_bytes", "abi_version", "KdaError", "LIB_PATH", "KDA_F32",
            "KDA_BF16", "KDA_FLAG_QK_L2NORM", "QK_L2NORM_EPS"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkda.so")
 KDA_F32, KDA_BF16 = 0, 1
 KDA_FLAG_QK_L2NORM = 1
+STATIC_SCRATCH_BYTES = 64 << 20  # KDA_STATIC_SCRATCH_BYTES: the fixed scratch of chunk_fwd_static
 QK_L2NORM_EPS = 1e-6  # eps inside the root of the in-kernel q / k L2 normalisation
 _STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
            4: "KDA_ERR_ALIGN", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_UNSUPPORTED", 7: "KDA_ERR_HIP"}
@@ -75,6 +76,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_workspace_bytes.argtypes = [D, ctypes.c_int]
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+    lib.kda_chunk_fwd_static.restype = ctypes.c_int
+    lib.kda_chunk_fwd_static.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.kda_chunk_bwd_workspace_bytes.argtypes = [D, ctypes.c_int]
     lib.kda_chunk_bwd.restype = ctypes.c_int
@@ -243,6 +246,41 @@ def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None
     _check(_lib().kda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
                              _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
                              _stream(stream)))
+    return out, final_state
+
+
+def chunk_fwd_static(q, k, v, log_g, beta, out, final_state=None, init_state=None, cu_seqlens=None, scale=None,
+                     stream=None, qk_l2norm=False):
+    """``chunk_fwd`` through kda_chunk_fwd_static: the library's fixed scratch
+    (STATIC_SCRATCH_BYTES per device) instead of a workspace, and no
+    allocation here either: ``out`` [B,T,H,dv] (fp32 or bf16) and
+    ``final_state`` [N,H,dk,dv] fp32 (or None) are the caller's.  Calls that
+    overlap on one device share that scratch and must be ordered by the caller."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    for t, name, shp in ((k, "k", (B, T, H, dk)), (v, "v", (B, T, H, dv))):
+        _need(t, name, shp, dt, dev)
+    _need(log_g, "log_g", (B, T, H, dk), torch.float32, dev)
+    _need(beta, "beta", (B, T, H), torch.float32, dev)
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed mode takes a single row (B == 1)")
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
+        N, L = cu_seqlens.shape[0] - 1, T
+    else:
+        N, L = B, T
+    if init_state is not None:
+        _need(init_state, "init_state", (N, H, dk, dv), torch.float32, dev)
+    _need(out, "out", (B, T, H, dv), out.dtype, dev)
+    if final_state is not None:
+        _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
+    desc = make_desc(N, L, H, dk, dv, code, scale, out_dtype=_out_code(out.dtype),
+                     flags=KDA_FLAG_QK_L2NORM if qk_l2norm else 0)
+    _check(_lib().kda_chunk_fwd_static(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
+                                       _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
+                                       _stream(stream)))
     return out, final_state
 
 

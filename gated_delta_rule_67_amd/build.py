@@ -25,7 +25,7 @@ PEAK_OUT = os.path.join(PKG, "libkda_peak.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_twopass.hip", "kda_backward.hip", "kda_conv.hip", "kda_norm.hip"]
+SOURCES = ["kda_api.cpp", "kda_recurrent.hip", "kda_twopass.hip", "kda_backward.hip", "kda_conv.hip", "kda_norm.hip", "kda_static.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]

@@ -455,6 +455,10 @@ kda_status kda_gated_rmsnorm(const kda_desc* d, const float* o, const void* gate
 
 namespace kda {
 
+kda_status fail_hip(const char* fn, const char* what, hipError_t e) {
+  return fail(KDA_ERR_HIP, "%s: %s: %s", fn, what, hipGetErrorString(e));
+}
+
 kda_status chunk_fwd_checked(const kda_desc* d, const void* q, const void* k, const void* v, const float* log_g,
                              const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
                              float* final_state, void* stream, void* ws, size_t ws_bytes, bool fixed_ws,

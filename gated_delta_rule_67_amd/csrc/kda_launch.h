@@ -15,6 +15,8 @@ kda_status chunk_fwd_checked(const kda_desc* d, const void* q, const void* k, co
                              const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
                              float* final_state, void* stream, void* ws, size_t ws_bytes, bool fixed_ws,
                              const char* fn);
+// Records "fn: what: <HIP error>" as the thread's last error; returns KDA_ERR_HIP.
+kda_status fail_hip(const char* fn, const char* what, hipError_t e);
 
 // Arguments of one decode / verify launch; shapes already validated.
 struct StepLaunch {

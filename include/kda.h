@@ -160,6 +160,26 @@ kda_status kda_chunk_fwd(const kda_desc* desc, const void* q, const void* k,
                          void* out, float* final_state, void* stream);
 
 /*
+ * kda_chunk_fwd without a workspace, for callers that cannot allocate (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, results and errors as kda_chunk_fwd, except
+ * that desc->workspace and desc->workspace_bytes are ignored: the scratch is
+ * a fixed array of KDA_STATIC_SCRATCH_BYTES inside the library, one per
+ * device, held until the process ends.  A problem needing more scratch than
+ * that (kda_chunk_workspace_bytes) returns KDA_ERR_WORKSPACE before
+ * anything is enqueued.  Calls allocate nothing (no hipMalloc, no hipFree).
+ * Every call on a device shares that device's array: calls that may overlap
+ * on one device (different streams, different host threads) race on it and
+ * must be ordered by the caller.  The array's contents on entry do not
+ * matter (every byte a call reads it wrote first).
+ */
+#define KDA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_chunk_fwd_static(const kda_desc* desc, const void* q, const void* k,
+                                const void* v, const float* log_g, const float* beta,
+                                const float* init_state, const int32_t* cu_seqlens,
+                                void* out, float* final_state, void* stream);
+
+/*
  * Decode / multi-row verify, updating the state in place.
  *
  *   q, k, log_g [N, n_tok, H, dk];  v [N, n_tok, H, dv];  beta [N, n_tok, H]
