@@ -305,7 +305,7 @@ def bench_prefill_workload(kda, name, steps, warmup, flush, n_flushed=100, **ove
     nbytes = prefill_bytes(tokens, H, D, n_states=n_states) + N * H * D * D * 4 * (n_states == 0)
     return dict(inp=inp, wall=wall, mean_ms=mean_ms, flushed=flushed, tokens=tokens, N=N, H=H, D=D,
                 packed=packed, bytes=nbytes, flops=prefill_flops(tokens, H, D), ws_bytes=int(ws.numel()),
-                call=call, d=d)
+                call=call, d=d, ws=ws)
 
 
 def prefill_summary(p, steps, traffic=None, kernel=None):
@@ -325,34 +325,47 @@ def prefill_summary(p, steps, traffic=None, kernel=None):
     return r
 
 
-def fallback_fraction(inp) -> float:
-    """Fraction of (chunk, head) pairs whose 64-token chunk fails the MFMA
-    path's decay guard (decay beyond e^-6 over the first or the second half of
-    any 16-token block, in any channel), computed on the host from log_g.
-    The guard's other triggers (input and intermediate magnitudes) do not
-    fire on these inputs' distributions."""
+SLOT_BYTES, SLOT_FLAG_OFF = 74752, 74240  # workspace slot of one (chunk, head); its per-wave fallback bytes
+
+
+def tree_fraction(inp) -> float:
+    """Fraction of (chunk, head) pairs whose diagonal tiles the prep kernel
+    builds from the binary pair tree (decay beyond e^-6 over the first or the
+    second half of any 16-token block, in any channel), computed on the host
+    from log_g."""
     g = inp["log_g"].double().numpy()
     B, T, H, D = g.shape
     nch = (T + CHUNK - 1) // CHUNK
     pad = nch * CHUNK - T
     if pad:
         g = np.concatenate([g, np.zeros((B, pad, H, D))], axis=1)
-    # [B, chunk, block, half, 8 tokens, H, D] -> decay of each half block
-    half = g.reshape(B, nch, 4, 2, 8, H, D).sum(axis=4)
-    bad = (half < -6.0).any(axis=(2, 3, 5))  # [B, chunk, H]
-    return float(bad.mean())
+    half = g.reshape(B, nch, 4, 2, 8, H, D).sum(axis=4)  # [B, chunk, block, half, H, D]
+    return float((half < -6.0).any(axis=(2, 3, 5)).mean())
+
+
+def fallback_fraction(ws, n_slots: int) -> float:
+    """Fraction of (chunk, head) slots the prep kernel flagged for the exact
+    per-token fallback, read from the flags it wrote into a dense problem's
+    workspace (the scan's own state and Delta bounds are not included)."""
+    flags = ws[: n_slots * SLOT_BYTES].view(n_slots, SLOT_BYTES)[:, SLOT_FLAG_OFF:SLOT_FLAG_OFF + 8]
+    return float((flags != 0).any(dim=1).float().mean())
 
 
 def bench_strong_gates(kda, steps, warmup, flush):
     """The dense workload with stronger gates than its 0.05 scale: log_g =
-    -softplus(N(0,1)) at scale 1.0, and log_g ~ U[-5, 0].  Reports tokens/s
-    and the fraction of (chunk, head) pairs on the exact per-token fallback."""
+    -softplus(N(0,1)) at scale 1.0, and log_g ~ U[-5, 0].  Reports tokens/s,
+    the fraction of (chunk, head) pairs whose diagonal tiles come from the
+    pair tree, and the fraction the prep kernel sent to the exact per-token
+    fallback."""
     res = {}
     for tag, over in (("gate_scale_1.0", dict(gate_scale=1.0)), ("uniform_-5_0", dict(gate_uniform=5.0))):
         p = bench_prefill_workload(kda, "prefill", steps, warmup, flush, n_flushed=0, **over)
+        B, T, H = p["inp"]["q"].shape[:3]
         res[tag] = {"tokens_per_s": round(p["tokens"] / (p["wall"] / steps), 1),
                     "us_per_call": round(p["mean_ms"] * 1e3, 2),
-                    "fallback_chunk_fraction": round(fallback_fraction(p["inp"]), 4)}
+                    "tree_chunk_fraction": round(tree_fraction(p["inp"]), 4),
+                    "fallback_chunk_fraction": round(fallback_fraction(p["ws"], B * ((T + CHUNK - 1) // CHUNK) * H),
+                                                     4)}
         del p
         torch.cuda.empty_cache()
     return res

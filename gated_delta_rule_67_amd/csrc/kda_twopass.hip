@@ -35,11 +35,16 @@
 // exp(HALF_SPAN_MAX).  exp(G) = Kl-side factor times exp(R_I) <= 1 and
 // exp(gamma - G) = Kr-side factor times exp(gamma - R_{I+1}) <= 1.
 //
+// Strong decays.  The midpoint factors of the diagonal tiles grow like the
+// decay over half a block; beyond HALF_SPAN_MAX in any channel the chunk's
+// diagonal tiles are built instead by a binary tree of token pairs whose
+// factors are all <= 1 (diag_tree below), so no gate, however strong, leaves
+// the MFMA path.
+//
 // Fast-path guard.  A chunk is evaluated token by token in exact fp32 (in
-// pass 2) instead when its half-block decay exceeds the bound, its inputs
-// could overflow an fp16 operand, a diagonal block of A exceeds 1 in
-// magnitude, any fp16 intermediate (T, W, U, Qs, As, Delta) would exceed
-// F16_SAFE, or the entry state exceeds S_MAX.
+// pass 2) instead when its inputs could overflow an fp16 operand, a diagonal
+// block of A exceeds 1 in magnitude, any fp16 intermediate (T, W, U, Qs, As,
+// Delta) would exceed F16_SAFE, or the entry state exceeds S_MAX.
 //
 // Arithmetic: fp16 MFMA operands (formed in fp32 from the bf16 inputs and
 // rounded once; the guard keeps them inside fp16's range), fp32
@@ -140,6 +145,7 @@ struct __align__(16) PrepSmem {
   f16 fDr[4][D];           // exp(M_I - R_{I+1})
   float beta[C];
   float2 nrm[2][C];        // per channel half: (k.k, q.q) of each row (L2 normalisation)
+  int strong[8];           // per stage-A wave: a half block decays beyond HALF_SPAN_MAX
   f16x4 frag[NFRAG][64];
 };
 
@@ -190,6 +196,134 @@ __device__ __forceinline__ bool t_column(PrepSmem& sm, f16x4 tbJ, int lane) {
   return bad;
 }
 
+// x from lane (lane - SH) / (lane + SH) of the same 16-lane row (DPP row
+// shift); lanes whose source lies outside the row keep `fill`.  A DPP read
+// from a lane outside EXEC also returns `fill`, so the shift must run in every
+// lane: the empty asm pins it ahead of the caller's select, which the compiler
+// would otherwise turn into an EXEC-masked branch around the shift.
+template <int SH>
+__device__ __forceinline__ float row_shr(float x, float fill) {
+  float y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                                                  __builtin_bit_cast(int, x), 0x110 + SH, 0xf, 0xf,
+                                                                  false));
+  asm volatile("" : "+v"(y));
+  return y;
+}
+template <int SH>
+__device__ __forceinline__ float row_shl(float x, float fill) {
+  float y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, fill),
+                                                                  __builtin_bit_cast(int, x), 0x100 + SH, 0xf, 0xf,
+                                                                  false));
+  asm volatile("" : "+v"(y));
+  return y;
+}
+
+struct DiagTiles {
+  f32x4 a;  // fragA of sum_c k_t k_s exp(G_t - G_s), s < t (rows t = lc)
+  f32x4 b;  // the same in fragB (rows t = 4lg+e)
+  f32x4 q;  // fragA of sum_c q_t k_s exp(G_t - G_s), s <= t
+};
+
+// One level of the pair tree: tiles of 2HF tokens, t in the upper and s in
+// the lower half of one tile.  P(t) = gates from the start of t's half through
+// t, S(s) = gates after s to the end of s's half; exp(G_t - G_s) = P(t) S(s).
+// Products along the tokens are segmented scans across the 16 lanes of the
+// row (lane lc = token).
+template <int HF>
+__device__ __forceinline__ void tree_level(const float (&a)[8], const float (&kf)[8], const float (&qf)[8], int lc,
+                                           int lg, DiagTiles& r) {
+  const int pos = lc & (HF - 1);
+  const bool upper = ((lc / HF) & 1) != 0;
+  f16x8 L, Lq, R;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    // every shift is taken in all lanes first (see row_shr), then selected
+    float P = a[c], Si = a[c];
+    if (HF >= 2) {
+      const float up = row_shr<1>(P, 1.f), dn = row_shl<1>(Si, 1.f);
+      P *= pos >= 1 ? up : 1.f;
+      Si *= pos + 1 < HF ? dn : 1.f;
+    }
+    if (HF >= 4) {
+      const float up = row_shr<2>(P, 1.f), dn = row_shl<2>(Si, 1.f);
+      P *= pos >= 2 ? up : 1.f;
+      Si *= pos + 2 < HF ? dn : 1.f;
+    }
+    if (HF >= 8) {
+      const float up = row_shr<4>(P, 1.f), dn = row_shl<4>(Si, 1.f);
+      P *= pos >= 4 ? up : 1.f;
+      Si *= pos + 4 < HF ? dn : 1.f;
+    }
+    float S = 1.f;  // exclusive of s
+    if (HF >= 2) {
+      const float nx = row_shl<1>(Si, 1.f);
+      S = pos + 1 < HF ? nx : 1.f;
+    }
+    L[c] = (f16)(upper ? kf[c] * P : 0.f);
+    Lq[c] = (f16)(upper ? qf[c] * P : 0.f);
+    R[c] = (f16)(upper ? 0.f : kf[c] * S);
+  }
+  const f32x4 ta = mfma32(R, L, zero4());   // (t = lc, s = 4lg+e)
+  const f32x4 tb = mfma32(L, R, zero4());   // (t = 4lg+e, s = lc)
+  const f32x4 tq = mfma32(R, Lq, zero4());  // (t = lc, s = 4lg+e)
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if ((lc ^ (4 * lg + e)) < 2 * HF) {  // t and s in one tile of this level
+      r.a[e] += ta[e];
+      r.b[e] += tb[e];
+      r.q[e] += tq[e];
+    }
+  }
+}
+
+// The diagonal tiles of block I (tokens 16I .. 16I+15 of the chunk starting at
+// token tok0, nv of them valid) for chunks with strong decays: every pair
+// s < t of the block belongs to exactly one level (the tile of 2HF tokens, HF
+// = 8, 4, 2, 1, that has t in its upper and s in its lower half), and every
+// operand is an input times products of gates <= 1, so nothing overflows for
+// any gate (-inf included) and small values only lose what is negligible.
+// k, q and log_g are read again here (rows past nv read zeros: identity
+// tokens); ik, iq scale k and q (the L2 normalisation, else 1).
+__device__ __noinline__ DiagTiles diag_tree(const bf16_t* qg, const bf16_t* kg, const float* lgg, size_t tok0,
+                                            int nv, int H, int h, int I, float ik, float iq) {
+  const int lane = threadIdx.x & 63, lc = lane & 15, lg = lane >> 4;
+  const uint32_t rs = static_cast<uint32_t>(H * D);
+  const size_t base = (tok0 * H + h) * D;
+  const uint32_t nrow = static_cast<uint32_t>(nv);
+  const __amdgpu_buffer_rsrc_t rg = buffer_rsrc(lgg + base, nrow * rs * 4u);
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(kg + base, nrow * rs * 2u);
+  const __amdgpu_buffer_rsrc_t rq = buffer_rsrc(qg + base, nrow * rs * 2u);
+  DiagTiles r{zero4(), zero4(), zero4()};
+  float qk = 0.f;
+#pragma unroll 1
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t off = static_cast<uint32_t>(16 * I + lc) * rs + static_cast<uint32_t>(32 * ks + 8 * lg);
+    const float4 g0 = __builtin_bit_cast(float4, buffer_load16(rg, off * 4u));
+    const float4 g1 = __builtin_bit_cast(float4, buffer_load16(rg, off * 4u + 16u));
+    const uint4 kw = buffer_load16(rk, off * 2u), qw = buffer_load16(rq, off * 2u);
+    const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const uint32_t kk[4] = {kw.x, kw.y, kw.z, kw.w}, qq[4] = {qw.x, qw.y, qw.z, qw.w};
+    float a[8], kf[8], qf[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      a[c] = exp_fast(gv[c]);
+      kf[c] = ((c & 1) ? bf16_hi(kk[c >> 1]) : bf16_lo(kk[c >> 1])) * ik;
+      qf[c] = ((c & 1) ? bf16_hi(qq[c >> 1]) : bf16_lo(qq[c >> 1])) * iq;
+      qk += qf[c] * kf[c];
+    }
+    tree_level<8>(a, kf, qf, lc, lg, r);
+    tree_level<4>(a, kf, qf, lc, lg, r);
+    tree_level<2>(a, kf, qf, lc, lg, r);
+    tree_level<1>(a, kf, qf, lc, lg, r);
+  }
+  // the pairs t = s of Aqk: q_t . k_t, summed over the four channel groups
+  qk += __shfl_xor(qk, 16, 64);
+  qk += __shfl_xor(qk, 32, 64);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r.q[e] += (4 * lg + e) == lc ? qk : 0.f;
+  return r;
+}
+
 template <bool L2>
 __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) prep_kernel(PrepArgs p) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -228,6 +362,7 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
   const int r0 = 16 * IA + 2 * qt;
   const float lim_lo = __expf(-HALF_SPAN_MAX);
   bool bad = false;
+  bool strong = false;  // a half block of this thread's channels decays beyond HALF_SPAN_MAX
 
   // ---------------- phase 1: loads and stage A (this thread: 2 rows x 8 channels)
   float4 g[2][2];
@@ -356,7 +491,8 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
           hr[j][c] = (f16)(kv * Sv[j]);
           xv[j][c] = (f16)(bt[j] * vv);
         }
-        bad |= (dl < lim_lo) | (dr < lim_lo) | (dl != dl) | (dr != dr);
+        strong |= (dl < lim_lo) | (dr < lim_lo);
+        bad |= (dl != dl) | (dr != dr);
         tot4[cc] = dl * dr;
         // the reciprocals only feed fp16 factors: the hardware estimate is enough
         fdl4[cc] = (f16)__builtin_amdgcn_rcpf(fmaxf(dl, lim_lo));
@@ -377,8 +513,13 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
       *reinterpret_cast<f16x8*>(&sm.u.a.Kr[r0 + j][c8]) = hr[j];
     }
     if ((w & 1) == 0 && oct == 0) *reinterpret_cast<float2*>(&sm.beta[r0]) = make_float2(bt[0], bt[1]);
+    const bool any_strong = __builtin_amdgcn_ballot_w64(strong) != 0;
+    if (lane == 0) sm.strong[w] = any_strong;
   }
   lds_barrier();
+  // workgroup-uniform: the diagonal tiles of this chunk come from the pair tree
+  const bool tree = (sm.strong[0] | sm.strong[1] | sm.strong[2] | sm.strong[3] | sm.strong[4] | sm.strong[5] |
+                     sm.strong[6] | sm.strong[7]) != 0;
 
   // ---------------- phase 2: K exp(gamma - G) out, Xk, products
   {
@@ -428,13 +569,36 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
     // diagonal block I = w of A in both layouts, and its inverse
     const int I = w;
     f32x4 accA = zero4(), accB = zero4();
+    if (tree) {
+      float ik = 1.f, iq = 1.f;
+      if (L2) {
+        const float2 n0 = sm.nrm[0][16 * I + lc], n1 = sm.nrm[1][16 * I + lc];
+        ik = __frsqrt_rn(n0.x + n1.x + L2_EPS);
+        iq = __frsqrt_rn(n0.y + n1.y + L2_EPS);
+      }
+      const DiagTiles dt = diag_tree(p.q, p.k, p.log_g, tok0, nv, H, h, I, ik, iq);
+      accA = dt.a;
+      accB = dt.b;
+      // Aqk_II (the item list skips it on this path)
+      float amax = 0.f;
+      f16x4 res;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kc = 32 * ks + 8 * lg;
-      const f16x8 ls = ld8(&sm.u.a.Kl[16 * I + lc][kc]) * ld8(&sm.fDl[I][kc]);
-      const f16x8 rs = ld8(&sm.u.a.Kr[16 * I + lc][kc]) * ld8(&sm.fDr[I][kc]);
-      accA = mfma32(rs, ls, accA);  // fragA: rows 16I+lc, cols 16I+4lg+e
-      accB = mfma32(ls, rs, accB);  // fragB: rows 16I+4lg+e, cols 16I+lc
+      for (int e = 0; e < 4; ++e) {
+        const float x = (4 * lg + e) <= lc ? p.scale * dt.q[e] : 0.f;
+        amax = fmaxf(amax, fabsf(x));
+        res[e] = (f16)x;
+      }
+      bad |= !(amax <= F16_SAFE);
+      *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(slot + OFF_AS) + frag_pos(I, I, 2, lane)) = res;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int kc = 32 * ks + 8 * lg;
+        const f16x8 ls = ld8(&sm.u.a.Kl[16 * I + lc][kc]) * ld8(&sm.fDl[I][kc]);
+        const f16x8 rs = ld8(&sm.u.a.Kr[16 * I + lc][kc]) * ld8(&sm.fDr[I][kc]);
+        accA = mfma32(rs, ls, accA);  // fragA: rows 16I+lc, cols 16I+4lg+e
+        accB = mfma32(ls, rs, accB);  // fragB: rows 16I+4lg+e, cols 16I+lc
+      }
     }
     f16x4 a, b;
     const float bA = sm.beta[16 * I + lc];
@@ -495,6 +659,7 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
       const int t = item - 6;
       I = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
       J = t - tile10(I, 0);
+      if (tree && I == J) continue;  // the diagonal waves wrote it (wave-uniform)
     }
     const f16(*L)[LDK] = isq ? sm.Ql : sm.u.a.Kl;
     f32x4 acc = zero4();

@@ -258,3 +258,33 @@ def test_workspace_reused_and_contents_ignored():
         e_o, e_f = err(out.cpu().numpy(), ref_o), err(fin.cpu().numpy(), ref_f)
         print(f"[{tag}] err_out={e_o:.3e} err_final={e_f:.3e}", flush=True)
         assert e_o <= TOL["bf16"] and e_f <= TOL["bf16"]
+
+
+SLOT_BYTES, FLAG_OFF = 74752, 74240  # workspace slot of one (chunk, head); its eight per-wave fallback bytes
+
+
+@pytest.mark.parametrize("gates", ["gate_scale 1.0", "uniform -5..0", "uniform -20..0 with resets"])
+def test_strong_gates_stay_on_the_mfma_path(gates):
+    """Gates far stronger than the workloads' 0.05 scale: every chunk must still
+    take the MFMA path (its diagonal tiles from the pair tree; no prep
+    fallback flag set) and match the oracle."""
+    B, T, H = 2, 640, 4
+    over = {"gate_scale 1.0": dict(gate_scale=1.0), "uniform -5..0": dict(gate_uniform=5.0),
+            "uniform -20..0 with resets": dict(gate_uniform=20.0)}[gates]
+    inp = kda_inputs.make_inputs(B=B, T=T, H=H, dk=128, dv=128, dtype="bf16", seed=95, init="normal",
+                                 init_std=0.05, **over)
+    if "resets" in gates:
+        g = inp["log_g"].numpy().copy()
+        g[:, 70] = -np.inf
+        g[0, 300:305, 1, :40] = -np.inf
+        inp["log_g"] = torch.from_numpy(g)
+    ws = torch.empty(kda.workspace_bytes(B, T, H, 128, packed=False), dtype=torch.uint8, device="cuda")
+    out, fin = run_chunk(inp, workspace=ws)
+    n_slots = B * (T // 64) * H
+    flags = ws[: n_slots * SLOT_BYTES].view(n_slots, SLOT_BYTES)[:, FLAG_OFF:FLAG_OFF + 8]
+    frac = float((flags != 0).any(dim=1).float().mean())
+    ref_o, ref_f = oracle_full(inp)
+    e_o, e_f = err(out.cpu().numpy(), ref_o), err(fin.cpu().numpy(), ref_f)
+    print(f"[strong gates {gates}] fallback fraction {frac:.3f} err_out={e_o:.3e} err_final={e_f:.3e}", flush=True)
+    assert frac == 0.0
+    assert e_o <= TOL["bf16"] and e_f <= TOL["bf16"]
