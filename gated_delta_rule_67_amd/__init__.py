@@ -31,7 +31,7 @@ import threading
 
 import torch
 
-__all__ = ["chunk_fwd", "chunk_fwd_static", "chunk_bwd", "step", "step_rows", "step_commit", "short_conv", "gated_rmsnorm",
+__all__ = ["chunk_fwd", "chunk_fwd_gated_norm", "chunk_fwd_static", "chunk_bwd", "step", "step_rows", "step_commit", "short_conv", "gated_rmsnorm",
            "workspace_bytes", "bwd_workspace_bytes", "abi_version", "KdaError", "LIB_PATH", "KDA_F32",
            "KDA_BF16", "KDA_FLAG_QK_L2NORM", "QK_L2NORM_EPS"]
 
@@ -76,6 +76,8 @@ def _load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_workspace_bytes.argtypes = [D, ctypes.c_int]
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_chunk_fwd.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
+    lib.kda_chunk_fwd_gated_norm.restype = ctypes.c_int
+    lib.kda_chunk_fwd_gated_norm.argtypes = [D, P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P]
     lib.kda_chunk_fwd_static.restype = ctypes.c_int
     lib.kda_chunk_fwd_static.argtypes = [D, P, P, P, P, P, P, P, P, P, P]
     lib.kda_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
@@ -246,6 +248,57 @@ def chunk_fwd(q, k, v, log_g, beta, init_state=None, cu_seqlens=None, scale=None
     _check(_lib().kda_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
                              _ptr(init_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
                              _stream(stream)))
+    return out, final_state
+
+
+@_allocates_on_launch_stream
+def chunk_fwd_gated_norm(q, k, v, log_g, beta, gate, norm_weight, eps, init_state=None, cu_seqlens=None, scale=None,
+                         out=None, final_state=None, workspace=None, stream=None, out_dtype=torch.bfloat16,
+                         qk_l2norm=False):
+    """``chunk_fwd`` whose output passes the gated per-head RMSNorm in the same
+    kernels: out = o / sqrt(mean(o^2) + eps) * norm_weight * sigmoid(gate) per
+    (token, head), o never stored.  ``gate`` is shaped like the output with
+    q's dtype, ``norm_weight`` [dv] fp32.  Returns (out [B,T,H,dv] in
+    ``out_dtype``, final_state)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev, dt = q.device, q.dtype
+    code = _dtype_code(q)
+    _need(k, "k", (B, T, H, dk), dt, dev)
+    _need(v, "v", (B, T, H, dv), dt, dev)
+    _need(log_g, "log_g", (B, T, H, dk), torch.float32, dev)
+    _need(beta, "beta", (B, T, H), torch.float32, dev)
+    _need(gate, "gate", (B, T, H, dv), dt, dev)
+    _need(norm_weight, "norm_weight", (dv,), torch.float32, dev)
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("packed mode takes a single row (B == 1)")
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
+        N, L = cu_seqlens.shape[0] - 1, T
+    else:
+        N, L = B, T
+    if init_state is not None:
+        _need(init_state, "init_state", (N, H, dk, dv), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    else:
+        _need(out, "out", (B, T, H, dv), out.dtype, dev)
+    if final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    else:
+        _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
+    desc = make_desc(N, L, H, dk, dv, code, scale, out_dtype=_out_code(out.dtype),
+                     flags=KDA_FLAG_QK_L2NORM if qk_l2norm else 0)
+    need = _lib().kda_chunk_workspace_bytes(ctypes.byref(desc), int(cu_seqlens is not None))
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        desc.workspace, desc.workspace_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    _check(_lib().kda_chunk_fwd_gated_norm(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(log_g), _ptr(beta),
+                                           _ptr(init_state), _ptr(cu_seqlens), _ptr(gate), _ptr(norm_weight),
+                                           ctypes.c_float(eps), _ptr(out), _ptr(final_state), _stream(stream)))
     return out, final_state
 
 

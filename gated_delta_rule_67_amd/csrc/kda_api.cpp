@@ -211,6 +211,16 @@ kda_status kda_chunk_fwd(const kda_desc* d, const void* q, const void* k, const 
                                 d ? d->workspace : nullptr, d ? d->workspace_bytes : 0, false, "kda_chunk_fwd");
 }
 
+kda_status kda_chunk_fwd_gated_norm(const kda_desc* d, const void* q, const void* k, const void* v,
+                                    const float* log_g, const float* beta, const float* init_state,
+                                    const int32_t* cu_seqlens, const void* gate, const float* norm_weight, float eps,
+                                    void* out, float* final_state, void* stream) {
+  const kda::OutNorm norm{gate, norm_weight, eps};
+  return kda::chunk_fwd_checked(d, q, k, v, log_g, beta, init_state, cu_seqlens, out, final_state, stream,
+                                d ? d->workspace : nullptr, d ? d->workspace_bytes : 0, false,
+                                "kda_chunk_fwd_gated_norm", &norm);
+}
+
 kda_status kda_step_rows(const kda_desc* d, const void* q, const void* k, const void* v,
                          const float* log_g, const float* beta, const float* state, int32_t n_tok,
                          void* out, float* deltas, void* stream) {
@@ -462,7 +472,7 @@ kda_status fail_hip(const char* fn, const char* what, hipError_t e) {
 kda_status chunk_fwd_checked(const kda_desc* d, const void* q, const void* k, const void* v, const float* log_g,
                              const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
                              float* final_state, void* stream, void* ws, size_t ws_bytes, bool fixed_ws,
-                             const char* fn) {
+                             const char* fn, const OutNorm* norm) {
   kda_status st = check_desc(d, fn);
   if (st != KDA_OK) return st;
   if (d->seq_len < 0) return fail(KDA_ERR_SHAPE, "%s: seq_len < 0", fn);
@@ -486,6 +496,20 @@ kda_status chunk_fwd_checked(const kda_desc* d, const void* q, const void* k, co
     return fail(KDA_ERR_SHAPE, "%s: out aliases an input", fn);
   kda::ChunkLaunch a = launch_of(d, packed);
   const Path path = prefill_path(a);
+  if (norm) {
+    if ((st = check_ptr(norm->gate, "gate", fn, has_tok)) != KDA_OK) return st;
+    if ((st = check_ptr(norm->weight, "norm_weight", fn, has_tok)) != KDA_OK) return st;
+    if (!std::isfinite(norm->eps) || norm->eps < 0.f) return fail(KDA_ERR_SHAPE, "%s: eps must be finite and >= 0", fn);
+    if (out && (out == norm->gate || out == static_cast<const void*>(norm->weight)))
+      return fail(KDA_ERR_SHAPE, "%s: out aliases gate or norm_weight", fn);
+    if (path != Path::TwoPass)
+      return fail(KDA_ERR_UNSUPPORTED, "%s: the fused norm needs the chunked path (bf16 q/k/v, d = 128); use "
+                  "kda_chunk_fwd then kda_gated_rmsnorm", fn);
+    a.gate = norm->gate;
+    a.norm_w = norm->weight;
+    a.eps = norm->eps;
+    a.gate_bf16 = d->qkv_dtype == KDA_BF16;
+  }
   const size_t ws_need = workspace_need(path, a);
   if (ws_need > 0) {
     if (fixed_ws && ws_bytes < ws_need)

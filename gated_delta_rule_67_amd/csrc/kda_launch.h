@@ -8,13 +8,21 @@
 
 namespace kda {
 
+// The gated RMSNorm fused behind a prefill (kda_chunk_fwd_gated_norm).
+struct OutNorm {
+  const void* gate;      // like out, element type qkv_dtype
+  const float* weight;   // [dv]
+  float eps;
+};
+
 // kda_chunk_fwd's validation and launch with the workspace given explicitly:
 // the caller's (desc->workspace) or the library's fixed scratch (fixed_ws,
-// ws_bytes = its capacity).  fn names the entry point in error messages.
+// ws_bytes = its capacity).  norm (or null) fuses the gated RMSNorm into the
+// output.  fn names the entry point in error messages.
 kda_status chunk_fwd_checked(const kda_desc* d, const void* q, const void* k, const void* v, const float* log_g,
                              const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
                              float* final_state, void* stream, void* ws, size_t ws_bytes, bool fixed_ws,
-                             const char* fn);
+                             const char* fn, const OutNorm* norm = nullptr);
 // Records "fn: what: <HIP error>" as the thread's last error; returns KDA_ERR_HIP.
 kda_status fail_hip(const char* fn, const char* what, hipError_t e);
 
@@ -74,6 +82,11 @@ struct ChunkLaunch {
   bool out_bf16;              // out element type (else fp32)
   bool l2;                    // L2-normalise the q and k rows first
   float scale;
+  // gated RMSNorm of the output (two-pass path only): gate null = none
+  const void* gate;           // like out, bf16 when gate_bf16 else fp32
+  const float* norm_w;        // [d]
+  float eps;
+  bool gate_bf16;
 };
 
 hipError_t launch_step(const StepLaunch& a, hipStream_t stream);

@@ -142,9 +142,11 @@ size_t kda_chunk_workspace_bytes(const kda_desc* desc, int packed);
  *
  * Evaluation path: bf16 q/k/v with d = 128 take the two-pass chunked kernels
  * (per-chunk operands staged in the workspace); other inputs take the
- * token-recurrent kernel.  The environment variable KDA_PREFILL_PATH, read at
- * every call, set to "recurrent" forces the token-recurrent kernel (a test
- * and diagnosis switch).  A workspace smaller than the selected path needs
+ * token-recurrent kernel.  The chunked path's serial pass runs four 32-column
+ * workgroups per (sequence or document, head) (kda_chunk_fwd_gated_norm: one
+ * 16-wave workgroup per unit).  The environment variable KDA_PREFILL_PATH,
+ * read at every call, is a test and diagnosis switch: "recurrent" forces the
+ * token-recurrent kernel, "unit" the whole-unit form of the serial pass.  A workspace smaller than the selected path needs
  * returns KDA_ERR_WORKSPACE before anything is enqueued.
  *
  * KDA_VALIDATE=1 (read at every call): before the launch, the call copies
@@ -158,6 +160,30 @@ kda_status kda_chunk_fwd(const kda_desc* desc, const void* q, const void* k,
                          const void* v, const float* log_g, const float* beta,
                          const float* init_state, const int32_t* cu_seqlens,
                          void* out, float* final_state, void* stream);
+
+/*
+ * kda_chunk_fwd with the gated per-head RMSNorm of its output fused into the
+ * scan's epilogue (NeMo glm5_next.layers: the mixer output passes
+ * `_TorchRMSNormGated` before the output projection; kda_gated_rmsnorm below
+ * is the same norm as a pass of its own).  out receives, per token t and
+ * head h, with o[t,h,:] what kda_chunk_fwd would write (never stored here):
+ *
+ *     out[t,h,i] = o[t,h,i] / sqrt(mean(o[t,h,:]^2) + eps) * norm_weight[i] * sigmoid(gate[t,h,i])
+ *
+ *   gate         [B, T, H, dv], element type desc->qkv_dtype
+ *   norm_weight  [dv] fp32 (shared by the heads);  eps >= 0
+ *   out          [B, T, H, dv], out_dtype (bf16 rounds the normalised value once)
+ * Everything else (arguments, workspace, final_state, errors, KDA_VALIDATE)
+ * is as for kda_chunk_fwd.  Supported where kda_chunk_fwd takes the chunked
+ * two-pass path (bf16 q/k/v, d = 128); other configurations return
+ * KDA_ERR_UNSUPPORTED (run kda_chunk_fwd, then kda_gated_rmsnorm).  out
+ * must not alias gate or norm_weight.
+ */
+kda_status kda_chunk_fwd_gated_norm(const kda_desc* desc, const void* q, const void* k,
+                                    const void* v, const float* log_g, const float* beta,
+                                    const float* init_state, const int32_t* cu_seqlens,
+                                    const void* gate, const float* norm_weight, float eps,
+                                    void* out, float* final_state, void* stream);
 
 /*
  * kda_chunk_fwd without a workspace, for callers that cannot allocate (code

@@ -250,3 +250,102 @@ def test_validate_mode_reports_non_finite_outputs(monkeypatch):
     with pytest.raises(kda.KdaError) as ei:
         chunk(inp)
     assert ei.value.status == 7 and "not finite" in str(ei.value)
+
+
+
+# ---------------------------------------------------------------- fused gated RMSNorm
+def norm_inputs(inp, seed):
+    rng = np.random.default_rng(seed)
+    B, T, H, D = inp["v"].shape
+    gate = torch.from_numpy(rng.standard_normal((B, T, H, D), dtype=np.float32)).to(torch.bfloat16)
+    w = torch.from_numpy(rng.standard_normal(D).astype(np.float32))
+    return gate, w
+
+
+def norm_bar(y, y_ref, o_ref, gate, w, eps, tol, bf16_out):
+    """max |y - y_ref| / bar, per element, for y = norm(o): the prefill's own
+    bar (|do| <= tol * rms of the whole output) carried through the norm.
+    With r = sqrt(mean(o^2) + eps) of the row, d(o_i / r) = do_i / r -
+    o_i dr / r^2 and |dr| <= max|do|, so |dy_i| <= |w_i sigmoid(g_i)| (1 +
+    |o_i| / r) max|do| / r; bf16 out adds one rounding, 2^-8 |y_i|.  A row whose
+    own RMS is far below the tensor's (a first token whose q.k nearly cancels)
+    is amplified by the norm, and the bar grows with it."""
+    y = np.asarray(y, dtype=np.float64)
+    assert np.all(np.isfinite(y))
+    do = tol * np.sqrt(np.mean(o_ref ** 2))
+    r = np.sqrt(np.mean(o_ref ** 2, axis=-1, keepdims=True) + eps)
+    gain = np.abs(to_f64(w)) / (1.0 + np.exp(-to_f64(gate)))
+    bar = gain * (1.0 + np.abs(o_ref) / r) * do / r + 1e-6 * np.sqrt(np.mean(y_ref ** 2))
+    if bf16_out:
+        bar = bar + 2.0 ** -8 * np.abs(y_ref)
+    return float(np.max(np.abs(y - y_ref) / bar))
+
+
+def fused(inp, gate, w, eps, **kw):
+    d = to_dev(inp)
+    out, fin = kda.chunk_fwd_gated_norm(d["q"], d["k"], d["v"], d["log_g"], d["beta"], gate.cuda(), w.cuda(), eps,
+                                        init_state=d["init_state"], cu_seqlens=d["cu_seqlens"], scale=inp["scale"],
+                                        **kw)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+NORM_CASES = {
+    "dense ragged": dict(B=2, T=200, H=3, dk=128, dv=128, dtype="bf16", seed=341, init="normal", init_std=0.1),
+    "packed edges": dict(B=1, T=590, H=2, dk=128, dv=128, dtype="bf16", seed=342,
+                         lengths=[0, 1, 63, 64, 65, 0, 130, 7, 260], init="normal", init_std=0.1),
+}
+
+
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("name", sorted(NORM_CASES))
+def test_chunk_fwd_gated_norm(name, out_dtype):
+    inp = kda_inputs.make_inputs(**NORM_CASES[name])
+    gate, w = norm_inputs(inp, 343)
+    out, fin = fused(inp, gate, w, 1e-6, out_dtype=out_dtype)
+    ref_o, ref_f = oracle_full(inp)
+    ref = oracle.gated_rmsnorm(ref_o, to_f64(gate), to_f64(w), 1e-6)
+    bar = norm_bar(out.float().cpu().numpy(), ref, ref_o, gate, w, 1e-6, TOL["bf16"], out_dtype == torch.bfloat16)
+    print(f"[norm {name} {out_dtype}] {bar:.3f} of the bar", flush=True)
+    assert bar <= 1.0
+    assert err(fin.cpu().numpy(), ref_f) <= TOL["bf16"]
+
+
+def test_chunk_fwd_gated_norm_on_fallback_chunks():
+    """Chunks on the exact per-token fallback (|beta| > 1 sends a chunk there)
+    through the norm epilogue.  The trigger keeps every row's magnitude like the
+    others': the norm rescales each row to unit RMS, so rows far below the
+    tensor's RMS would turn the prefill's own rounding into large relative errors."""
+    inp = kda_inputs.make_inputs(B=2, T=64 * 4 + 9, H=2, dk=128, dv=128, dtype="bf16", seed=344,
+                                 init="normal", init_std=0.05)
+    b = inp["beta"].numpy().copy()
+    b[0, 70:72] = 1.5                           # chunk 1 of sequence 0
+    b[1, 200] = -1.2                            # chunk 3 of sequence 1
+    inp["beta"] = torch.from_numpy(b)
+    gate, w = norm_inputs(inp, 345)
+    out, _ = fused(inp, gate, w, 1e-5, out_dtype=torch.float32)
+    ref_o, _ = oracle_full(inp)
+    ref = oracle.gated_rmsnorm(ref_o, to_f64(gate), to_f64(w), 1e-5)
+    assert norm_bar(out.cpu().numpy(), ref, ref_o, gate, w, 1e-5, TOL["bf16"], False) <= 1.0
+
+
+def test_packed_workload_gated_norm_bf16_out():
+    """The packed 65536-token, 32-head workload through the fused norm with bf16
+    out (the mixer's output as the next projection takes it), whole tensor."""
+    inp = kda_inputs.config("varlen")
+    gate, w = norm_inputs(inp, 346)
+    out, fin = fused(inp, gate, w, 1e-6)
+    ref_o, ref_f = oracle_full(inp)
+    ref = oracle.gated_rmsnorm(ref_o, to_f64(gate), to_f64(w), 1e-6)
+    bar = norm_bar(out.float().cpu().numpy(), ref, ref_o, gate, w, 1e-6, TOL["bf16"], True)
+    e_f = err(fin.cpu().numpy(), ref_f)
+    print(f"[varlen fused norm bf16 out] {bar:.3f} of the bar, err_final={e_f:.3e}", flush=True)
+    assert bar <= 1.0 and e_f <= TOL["bf16"]
+
+
+def test_gated_norm_needs_the_chunked_path():
+    inp = kda_inputs.make_inputs(B=1, T=40, H=2, dk=64, dv=64, dtype="bf16", seed=347)
+    gate, w = norm_inputs(inp, 348)
+    with pytest.raises(kda.KdaError) as ei:
+        fused(inp, gate, w, 1e-6)
+    assert ei.value.status == 6

@@ -21,6 +21,17 @@ if not torch.cuda.is_available():  # collected on CPU, skipped there
 
 import gated_delta_rule_67_amd as kda  # noqa: E402
 
+# The chunked path's serial pass has two forms: four 32-column workgroups per
+# (sequence or document, head), or one 16-wave workgroup per unit.  Every
+# test runs under both (the switch only affects bf16 d = 128 prefill).
+SCAN_FORMS = ["tile", "unit"]
+
+
+@pytest.fixture(params=SCAN_FORMS, autouse=True)
+def scan_form(request, monkeypatch):
+    monkeypatch.setenv("KDA_PREFILL_PATH", request.param)
+    return request.param
+
 def run_chunk(inp, **kw):
     d = to_dev(inp)
     out, fin = kda.chunk_fwd(d["q"], d["k"], d["v"], d["log_g"], d["beta"], init_state=d["init_state"],
@@ -227,13 +238,13 @@ def test_mixed_fast_and_fallback_chunks():
     check_full(inp, "mixed fast/fallback chunks")
 
 
-def test_mfma_path_matches_recurrent_path(monkeypatch):
+def test_mfma_path_matches_recurrent_path(monkeypatch, scan_form):
     """The chunked kernel agrees with the token-recurrent one (and with the oracle)."""
     inp = kda_inputs.make_inputs(B=2, T=333, H=4, dk=128, dv=128, dtype="bf16", seed=91)
     out_c, fin_c = run_chunk(inp)
     monkeypatch.setenv("KDA_PREFILL_PATH", "recurrent")
     out_r, fin_r = run_chunk(inp)
-    monkeypatch.delenv("KDA_PREFILL_PATH")
+    monkeypatch.setenv("KDA_PREFILL_PATH", scan_form)
     ref_o, ref_f = oracle_full(inp)
     e_c = err(out_c.cpu().numpy(), ref_o)
     e_r = err(out_r.cpu().numpy(), ref_o)
@@ -288,3 +299,17 @@ def test_strong_gates_stay_on_the_mfma_path(gates):
     print(f"[strong gates {gates}] fallback fraction {frac:.3f} err_out={e_o:.3e} err_final={e_f:.3e}", flush=True)
     assert frac == 0.0
     assert e_o <= TOL["bf16"] and e_f <= TOL["bf16"]
+
+
+def test_scan_forms_agree(monkeypatch):
+    """The two forms of the serial pass give the same results on a packed batch."""
+    inp = kda_inputs.make_inputs(B=1, T=1500, H=4, dk=128, dv=128, dtype="bf16", seed=96,
+                                 lengths=[1, 700, 63, 0, 736], init="normal", init_std=0.05)
+    res = {}
+    for form in SCAN_FORMS:
+        monkeypatch.setenv("KDA_PREFILL_PATH", form)
+        res[form] = run_chunk(inp)
+    (o1, f1), (o2, f2) = res["tile"], res["unit"]
+    e_o, e_f = err(o2.cpu().numpy(), o1.cpu().numpy()), err(f2.cpu().numpy(), f1.cpu().numpy())
+    print(f"[tile vs unit] out={e_o:.3e} final={e_f:.3e}", flush=True)
+    assert e_o <= 1e-5 and e_f <= 1e-5
