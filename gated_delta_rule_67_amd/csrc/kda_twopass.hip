@@ -1418,17 +1418,39 @@ __global__ void __launch_bounds__(1024) chunk_map_kernel(const int32_t* __restri
   for (int c = max(carry, 0) + tid; c < n_slots; c += 1024) table[c] = -1;
 }
 
-__global__ void __launch_bounds__(256) doc_order_kernel(const int32_t* __restrict__ cu, int n,
-                                                        int32_t* __restrict__ order) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  const int li = cu[i + 1] - cu[i];
-  int rank = 0;
-  for (int j = 0; j < n; ++j) {
-    const int lj = cu[j + 1] - cu[j];
-    rank += (lj > li) || (lj == li && j < i);
+// Longest-first order of the documents: one workgroup sorts (length
+// descending, index ascending) keys in LDS with a bitonic network over the
+// next power of two >= n (n <= MAX_ORDER_DOCS), then writes order[rank] = index.
+constexpr int MAX_ORDER_DOCS = 16384;
+
+__global__ void __launch_bounds__(1024) doc_order_kernel(const int32_t* __restrict__ cu, int n,
+                                                         int32_t* __restrict__ order) {
+  __shared__ uint64_t key[MAX_ORDER_DOCS];
+  int m = 1;
+  while (m < n) m <<= 1;
+  for (int i = threadIdx.x; i < m; i += 1024) {
+    // ascending keys = longest first, then lower index; padding sorts last
+    const uint32_t len = i < n ? static_cast<uint32_t>(max(cu[i + 1] - cu[i], 0)) : 0u;
+    key[i] = i < n ? (static_cast<uint64_t>(0x7fffffffu - len) << 32) | static_cast<uint32_t>(i) : ~uint64_t(0);
   }
-  order[rank] = i;
+  __syncthreads();
+  for (int size = 2; size <= m; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < m; i += 1024) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = (i & size) == 0;
+          const uint64_t a = key[i], b = key[j];
+          if ((a > b) == up) {
+            key[i] = b;
+            key[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = threadIdx.x; r < n; r += 1024) order[r] = static_cast<int32_t>(key[r] & 0xffffffffu);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -1470,7 +1492,8 @@ WsLayout ws_layout(void* base, int num_seqs, int seq_len, int H, bool packed) {
 }  // namespace
 
 hipError_t launch_doc_order(const int32_t* cu_seqlens, int n, int32_t* order, hipStream_t stream) {
-  hipLaunchKernelGGL(doc_order_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, cu_seqlens, n, order);
+  if (n < 1 || n > MAX_ORDER_DOCS) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(doc_order_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, n, order);
   return hipGetLastError();
 }
 
@@ -1541,7 +1564,7 @@ hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream) {
                        static_cast<int>(ns), l.cstart, l.table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.num_seqs > 1 && a.num_seqs <= 4096) {
+    if (a.num_seqs > 1 && a.num_seqs <= MAX_ORDER_DOCS) {
       e = launch_doc_order(a.cu_seqlens, a.num_seqs, l.order, stream);
       if (e != hipSuccess) return e;
     }
@@ -1580,7 +1603,7 @@ hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream) {
   sp.final_state = a.final_state;
   sp.cu_seqlens = a.cu_seqlens;
   sp.cstart = packed ? l.cstart : nullptr;
-  sp.order = (packed && a.num_seqs > 1 && a.num_seqs <= 4096) ? l.order : nullptr;
+  sp.order = (packed && a.num_seqs > 1 && a.num_seqs <= MAX_ORDER_DOCS) ? l.order : nullptr;
   sp.ws = l.slots;
   sp.out = a.out;
   sp.out_bf16 = a.out_bf16;

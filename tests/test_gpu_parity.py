@@ -116,16 +116,18 @@ def test_long_single_document():
     check_full(inp, "packed one long document")
 
 
-def test_more_documents_than_the_ordering_covers():
-    """5000 short documents (0 to 40 tokens): packed problems past 4096 documents are
-    scanned in their given order, and the chunk map walks the documents in
-    several blocks of 1024."""
+@pytest.mark.parametrize("n_docs", [5000, 17000])
+def test_many_documents(n_docs):
+    """Thousands of short documents (0 to 40 tokens): the longest-first sort
+    covers up to 16384 documents (a bitonic network over the next power of
+    two), problems with more are scanned in their given order, and the chunk
+    map walks the documents in several blocks of 1024."""
     rng = np.random.default_rng(23)
-    lens = [int(x) for x in rng.integers(0, 41, size=5000)]
+    lens = [int(x) for x in rng.integers(0, 41, size=n_docs)]
     lens[0], lens[1] = 0, 1
     inp = kda_inputs.make_inputs(B=1, T=sum(lens), H=2, dk=128, dv=128, dtype="bf16", seed=24,
                                  lengths=lens, init="normal", init_std=0.05)
-    check_full(inp, "packed 5000 short documents")
+    check_full(inp, f"packed {n_docs} short documents")
 
 
 def test_packed_zero_initial_state():
