@@ -164,7 +164,5 @@ struct NormLaunch {
 
 hipError_t launch_gated_rmsnorm(const NormLaunch& a, hipStream_t stream);
 
-// Longest-first order of the documents of a packed problem (1 <= n <= 16384).
-hipError_t launch_doc_order(const int32_t* cu_seqlens, int n, int32_t* order, hipStream_t stream);
 
 }  // namespace kda

@@ -1379,12 +1379,20 @@ __global__ void __launch_bounds__(NTU, 1) scan_unit_kernel(ScanArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Packed problems: chunk slots of the documents (one workgroup).
-// cstart[d] = sum over earlier documents of ceil(len / 64); cstart[n] = total;
-// table[slot] = document owning the slot, -1 for unused slots up to n_slots.
-__global__ void __launch_bounds__(1024) chunk_map_kernel(const int32_t* __restrict__ cu, int n, int n_slots,
-                                                         int32_t* __restrict__ cstart, int32_t* __restrict__ table) {
+// Packed problems: the document map, one workgroup.
+//  - cstart[d] = sum over earlier documents of ceil(len / 64); cstart[n] = total;
+//  - table[slot] = document owning the slot (a binary search of cstart per
+//    slot), -1 for unused slots up to n_slots;
+//  - with do_order (n <= MAX_ORDER_DOCS): order[rank] = document, longest
+//    first (ties by index), from a bitonic sort of (length descending, index)
+//    keys in LDS over the next power of two >= n.
+constexpr int MAX_ORDER_DOCS = 16384;
+
+__global__ void __launch_bounds__(1024) doc_map_kernel(const int32_t* __restrict__ cu, int n, int n_slots,
+                                                       int32_t* __restrict__ cstart, int32_t* __restrict__ table,
+                                                       int32_t* __restrict__ order, int do_order) {
   __shared__ int wsum[16];
+  __shared__ uint64_t key[MAX_ORDER_DOCS];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int carry = 0;
   for (int base = 0; base < n; base += 1024) {
@@ -1410,25 +1418,23 @@ __global__ void __launch_bounds__(1024) chunk_map_kernel(const int32_t* __restri
     __syncthreads();
   }
   if (tid == 0) cstart[n] = carry;
-  __syncthreads();
-  for (int d = tid; d < n; d += 1024) {
-    const int b = cstart[d], e = min(cstart[d + 1], n_slots);
-    for (int c = b; c < e; ++c) table[c] = d;
+  __syncthreads();  // cstart complete (global writes of this workgroup)
+  for (int c = tid; c < n_slots; c += 1024) {
+    int doc = -1;
+    if (c < carry) {  // the last document whose first slot is <= c (empty documents own none)
+      int lo = 0, hi = n;  // cstart[lo] <= c < cstart[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cstart[mid] <= c) lo = mid; else hi = mid;
+      }
+      doc = lo;
+    }
+    table[c] = doc;
   }
-  for (int c = max(carry, 0) + tid; c < n_slots; c += 1024) table[c] = -1;
-}
-
-// Longest-first order of the documents: one workgroup sorts (length
-// descending, index ascending) keys in LDS with a bitonic network over the
-// next power of two >= n (n <= MAX_ORDER_DOCS), then writes order[rank] = index.
-constexpr int MAX_ORDER_DOCS = 16384;
-
-__global__ void __launch_bounds__(1024) doc_order_kernel(const int32_t* __restrict__ cu, int n,
-                                                         int32_t* __restrict__ order) {
-  __shared__ uint64_t key[MAX_ORDER_DOCS];
+  if (!do_order) return;  // kernel argument: uniform
   int m = 1;
   while (m < n) m <<= 1;
-  for (int i = threadIdx.x; i < m; i += 1024) {
+  for (int i = tid; i < m; i += 1024) {
     // ascending keys = longest first, then lower index; padding sorts last
     const uint32_t len = i < n ? static_cast<uint32_t>(max(cu[i + 1] - cu[i], 0)) : 0u;
     key[i] = i < n ? (static_cast<uint64_t>(0x7fffffffu - len) << 32) | static_cast<uint32_t>(i) : ~uint64_t(0);
@@ -1436,21 +1442,21 @@ __global__ void __launch_bounds__(1024) doc_order_kernel(const int32_t* __restri
   __syncthreads();
   for (int size = 2; size <= m; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int i = threadIdx.x; i < m; i += 1024) {
+      for (int i = tid; i < m; i += 1024) {
         const int j = i ^ stride;
         if (j > i) {
           const bool up = (i & size) == 0;
-          const uint64_t a = key[i], b = key[j];
-          if ((a > b) == up) {
-            key[i] = b;
-            key[j] = a;
+          const uint64_t x = key[i], y = key[j];
+          if ((x > y) == up) {
+            key[i] = y;
+            key[j] = x;
           }
         }
       }
       __syncthreads();
     }
   }
-  for (int r = threadIdx.x; r < n; r += 1024) order[r] = static_cast<int32_t>(key[r] & 0xffffffffu);
+  for (int r = tid; r < n; r += 1024) order[r] = static_cast<int32_t>(key[r] & 0xffffffffu);
 }
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -1490,12 +1496,6 @@ WsLayout ws_layout(void* base, int num_seqs, int seq_len, int H, bool packed) {
 }
 
 }  // namespace
-
-hipError_t launch_doc_order(const int32_t* cu_seqlens, int n, int32_t* order, hipStream_t stream) {
-  if (n < 1 || n > MAX_ORDER_DOCS) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(doc_order_kernel, dim3(1), dim3(1024), 0, stream, cu_seqlens, n, order);
-  return hipGetLastError();
-}
 
 size_t twopass_workspace_bytes(int num_seqs, int seq_len, int num_heads, bool packed) {
   return ws_layout(nullptr, num_seqs, seq_len, num_heads, packed).bytes;
@@ -1560,14 +1560,11 @@ hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream) {
   const int64_t ns = n_slots_of(a.num_seqs, a.seq_len, packed);
   const int nchd = (a.seq_len + C - 1) / C;
   if (packed) {
-    hipLaunchKernelGGL(chunk_map_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.num_seqs,
-                       static_cast<int>(ns), l.cstart, l.table);
-    hipError_t e = hipGetLastError();
+    const int do_order = a.num_seqs > 1 && a.num_seqs <= MAX_ORDER_DOCS;
+    hipLaunchKernelGGL(doc_map_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, a.num_seqs,
+                       static_cast<int>(ns), l.cstart, l.table, l.order, do_order);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.num_seqs > 1 && a.num_seqs <= MAX_ORDER_DOCS) {
-      e = launch_doc_order(a.cu_seqlens, a.num_seqs, l.order, stream);
-      if (e != hipSuccess) return e;
-    }
   }
   if (ns > 0) {
     PrepArgs pp{};
