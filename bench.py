@@ -465,6 +465,50 @@ def bench_norm(kda, steps, warmup):
                          "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
 
 
+def bench_fused_norm(kda, steps, warmup):
+    """The mixer's output path on the dense and packed workloads, bf16 out,
+    three ways, timed like the prefill: kda_chunk_fwd_gated_norm (the norm in
+    the scan's epilogue, one call); kda_chunk_fwd with fp32 out followed by
+    kda_gated_rmsnorm (the two calls it replaces); kda_chunk_fwd with bf16 out
+    and no norm (the floor of the pair)."""
+    res = {}
+    for name in ("prefill", "varlen"):
+        inp = kda_inputs.config(name)
+        d = to_dev(inp)
+        B, T, H, D = inp["q"].shape
+        packed = d["cu_seqlens"] is not None
+        N = d["cu_seqlens"].numel() - 1 if packed else B
+        rng = np.random.default_rng(421)
+        g = torch.from_numpy(rng.standard_normal((B, T, H, D), dtype=np.float32)).to(torch.bfloat16).cuda()
+        w = torch.from_numpy(rng.standard_normal(D).astype(np.float32)).cuda()
+        o32 = torch.empty((B, T, H, D), dtype=torch.float32, device="cuda")
+        o16 = torch.empty((B, T, H, D), dtype=torch.bfloat16, device="cuda")
+        fin = torch.empty((N, H, D, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(kda.workspace_bytes(N, T, H, D, packed=packed), dtype=torch.uint8, device="cuda")
+        kw = dict(init_state=d["init_state"], cu_seqlens=d["cu_seqlens"], final_state=fin, workspace=ws)
+        args = (d["q"], d["k"], d["v"], d["log_g"], d["beta"])
+
+        def fused():
+            kda.chunk_fwd_gated_norm(*args, g, w, 1e-6, out=o16, **kw)
+
+        def two_calls():
+            kda.chunk_fwd(*args, out=o32, **kw)
+            kda.gated_rmsnorm(o32, g, w, 1e-6, out=o16)
+
+        def plain_bf16():
+            kda.chunk_fwd(*args, out=o16, out_dtype=torch.bfloat16, **kw)
+
+        r = {}
+        for tag, fn in (("fused_gated_norm", fused), ("chunk_fwd_then_norm", two_calls),
+                        ("chunk_fwd_bf16_no_norm", plain_bf16)):
+            _, ms = timed_calls(fn, steps, warmup)
+            r[tag + "_us"] = round(ms * 1e3, 2)
+        res[name] = r
+        del d, g, o32, o16, fin, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def bench_step(kda, name, steps, warmup, flush):
     """kda_step timed per call with HIP events; before every call a 1 GiB
     buffer is read (clean lines, nothing to write back) so the state (128 MiB
@@ -784,6 +828,8 @@ def main():
     if args.only in ("all", "norm"):
         res["gated_rmsnorm"] = bench_norm(kda, args.steps, args.warmup)
         print(f"gated rmsnorm {res['gated_rmsnorm']['us_per_call']} us per call", file=sys.stderr, flush=True)
+        res["fused_gated_norm"] = bench_fused_norm(kda, args.steps, args.warmup)
+        print(f"fused gated norm {res['fused_gated_norm']}", file=sys.stderr, flush=True)
     if args.only in ("all", "step"):
         res["decode"] = bench_step(kda, "decode", args.steps, args.warmup, flush)
         res["verify"] = bench_step(kda, "verify", args.steps, args.warmup, flush)
@@ -844,6 +890,7 @@ def main():
         "backward": res["backward"],
         "short_conv": res["short_conv"],
         "gated_rmsnorm": res["gated_rmsnorm"],
+        "fused_gated_norm": res["fused_gated_norm"],
         "peaks": res["peaks"],
     }
     inp = p["inp"]
