@@ -528,12 +528,28 @@ def bench_step(kda, name, steps, warmup, flush):
     ms = flushed_calls(call, max(steps, 100), flush)
     nbytes = step_bytes(N, n_tok, H, D)
     avg = float(np.mean(ms))
-    return {"workload": f"{N} sequences x {n_tok} rows, H={H}, dk=dv={D}, bf16 q/k/v, fp32 state in place "
-                        "(caches flushed before each call)",
-            "us_per_call": round(avg * 1e3, 2), "achieved_GBs": round(nbytes / (avg * 1e-3) / 1e9, 1),
-            "per_call": spread(ms),
-            "roofline": hbm_roofline(nbytes, avg),
-            "algorithmic_bytes": nbytes}
+    r = {"workload": f"{N} sequences x {n_tok} rows, H={H}, dk=dv={D}, bf16 q/k/v, fp32 state in place "
+                     "(caches flushed before each call)",
+         "us_per_call": round(avg * 1e3, 2), "achieved_GBs": round(nbytes / (avg * 1e-3) / 1e9, 1),
+         "per_call": spread(ms),
+         "roofline": hbm_roofline(nbytes, avg),
+         "algorithmic_bytes": nbytes}
+    if n_tok > 1:
+        # the same states streamed by a one-row step: what the state traffic
+        # alone reaches at this many units
+        q1 = {k: d[k][:, :1].contiguous() for k in ("q", "k", "v", "log_g", "beta")}
+        out1 = torch.empty((N, 1, H, D), dtype=torch.float32, device="cuda")
+
+        def call1():
+            kda.step(q1["q"], q1["k"], q1["v"], q1["log_g"], q1["beta"], state, out=out1)
+
+        ms1 = flushed_calls(call1, max(steps, 100), flush)
+        nb1 = step_bytes(N, 1, H, D)
+        a1 = float(np.mean(ms1))
+        r["one_row_same_states"] = {"us_per_call": round(a1 * 1e3, 2),
+                                    "achieved_GBs": round(nb1 / (a1 * 1e-3) / 1e9, 1),
+                                    "algorithmic_bytes": nb1}
+    return r
 
 
 def rows_bytes(N: int, n_tok: int, H: int, d: int, qkv_bytes=2) -> int:
