@@ -357,11 +357,12 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
   const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index 0..7, uniform (SGPR)
   // stage A: wave w covers block IA = w/2 (rows 16IA .. 16IA+15) and channel
-  // half w%2; lane (oct, qt) = (lane%8, lane/8) owns rows r0 = 16IA+2qt, r0+1
-  // and channels c8 .. c8+7.  The eight lanes of one channel octet sit 8 apart.
+  // half w%2; lane (qt, oct) = (lane%8, lane/8) owns rows r0 = 16IA+2qt, r0+1
+  // and channels c8 .. c8+7.  The eight row pairs of a channel octet are eight
+  // adjacent lanes, so products over them are DPP row shifts.
   const int IA = w >> 1;
-  const int oct = lane & 7;
-  const int qt = lane >> 3;
+  const int qt = lane & 7;
+  const int oct = lane >> 3;
   const int c8 = 64 * (w & 1) + 8 * oct;
   const int r0 = 16 * IA + 2 * qt;
   const float lim_lo = __expf(-HALF_SPAN_MAX);
@@ -432,7 +433,7 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
         b += q0 * q0 + q1 * q1;
       }
 #pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
+      for (int o = 8; o < 64; o <<= 1) {  // over the eight channel octets
         a += __shfl_xor(a, o, 64);
         b += __shfl_xor(b, o, 64);
       }
@@ -453,8 +454,7 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
   }
   f16x8 hl[2], hr[2], xv[2];  // k exp(G - R), k exp(R' - G), beta v of rows r0, r0+1
   {
-    const int ldn8 = (lane - 8) & 63, ldn16 = (lane - 16) & 63, ldn32 = (lane - 32) & 63;
-    const int lup8 = (lane + 8) & 63, lup16 = (lane + 16) & 63, lup32 = (lane + 32) & 63;
+    const int l3 = (lane & ~7) | 3, l4 = (lane & ~7) | 4;  // row pairs 3 and 4 of this octet
     // two passes of four channels keep the live registers down
 #pragma unroll
     for (int hc = 0; hc < 2; ++hc) {
@@ -467,19 +467,21 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
         const float a0 = exp_fast(cc == 0 ? ga.x : cc == 1 ? ga.y : cc == 2 ? ga.z : ga.w);
         const float a1 = exp_fast(cc == 0 ? gb4.x : cc == 1 ? gb4.y : cc == 2 ? gb4.z : gb4.w);
         const float pr = a0 * a1;
-        // inclusive prefix (x) and suffix (y) products over the block's eight row pairs
+        // inclusive prefix (x) and suffix (y) products over the block's eight
+        // row pairs (lanes qt = 0..7 of this octet; every shift is taken in
+        // all lanes first, then selected)
         float x = pr, y = pr, t;
-        t = __shfl(x, ldn8, 64);  x = qt >= 1 ? x * t : x;
-        t = __shfl(x, ldn16, 64); x = qt >= 2 ? x * t : x;
-        t = __shfl(x, ldn32, 64); x = qt >= 4 ? x * t : x;
-        t = __shfl(y, lup8, 64);  y = qt <= 6 ? y * t : y;
-        t = __shfl(y, lup16, 64); y = qt <= 5 ? y * t : y;
-        t = __shfl(y, lup32, 64); y = qt <= 3 ? y * t : y;
-        const float xe = __shfl(x, ldn8, 64), ye = __shfl(y, lup8, 64);
+        t = row_shr<1>(x, 1.f); x = qt >= 1 ? x * t : x;
+        t = row_shr<2>(x, 1.f); x = qt >= 2 ? x * t : x;
+        t = row_shr<4>(x, 1.f); x = qt >= 4 ? x * t : x;
+        t = row_shl<1>(y, 1.f); y = qt <= 6 ? y * t : y;
+        t = row_shl<2>(y, 1.f); y = qt <= 5 ? y * t : y;
+        t = row_shl<4>(y, 1.f); y = qt <= 3 ? y * t : y;
+        const float xe = row_shr<1>(x, 1.f), ye = row_shl<1>(y, 1.f);
         const float E = qt >= 1 ? xe : 1.f;  // over the row pairs before this lane's
         const float F = qt <= 6 ? ye : 1.f;  // over the row pairs after it
-        const float dl = __shfl(x, oct + 24, 64);  // over the first half of the block
-        const float dr = __shfl(y, oct + 32, 64);  // over the second half
+        const float dl = __shfl(x, l3, 64);  // over the first half of the block
+        const float dr = __shfl(y, l4, 64);  // over the second half
         const float Pv[2] = {E * a0, E * pr};
         const float Sv[2] = {a1 * F, F};
 #pragma unroll
