@@ -1083,6 +1083,271 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
 }
 
 // ---------------------------------------------------------------------------
+// Pass 2, four-wave form: the same 32-column tiles as scan_kernel, with each
+// wave forming both Delta and the outputs of token block I = w (one read of
+// the staged state serves both products) and updating key rows 32w .. 32w+31.
+// At about half of scan_kernel's registers per lane, two workgroups share a
+// CU, so when there are more tiles than CUs two units' serial chains
+// interleave on every CU and hide each other's waits.
+constexpr int NT4 = 256;  // four-wave scan threads
+
+struct __align__(16) Scan4Smem {
+  f16 ST[DVT][LDK];   // S^T (fp16) [value col][key row]
+  f16 DT[DVT][LDT];   // Delta^T    [value col][token]
+  fb::Stage<4> fb;
+  int sbp[4];         // per wave: state beyond the fast-path bound
+  int dbp[4];         // per wave: Delta beyond the fp16 bound
+};
+
+// Slot operands of one chunk as one four-wave scan thread uses them.
+struct Pre4 {
+  f16x8 mw[4];      // -W row 16w+lc, key cols 32ks+8lg ..
+  f16x8 mq[4];      // Qs row 16w+lc, key cols 32ks+8lg ..
+  f16x8 u;          // U of this lane, [b][e]
+  f16x8 kd[2][2];   // Kd^T rows 32w+16a+lc, tokens 32ks+8lg ..
+  f16x8 as[2];      // As row 16w+lc, tokens 32ks+8lg ..
+  float4 gam[2];    // exp(gamma) of key rows 32w+16a+4lg ..
+  int2 flag;
+};
+
+struct WaveState4 {
+  f32x4 s[2][2];
+};
+
+// The token-by-token evaluation of one chunk, out of line (see scan_fallback).
+__device__ __noinline__ WaveState4 scan4_fallback(fb::Stage<4>& st, WaveState4 in, const fb::Args fa,
+                                                  size_t tok_begin, int ntok, int k, int h, int col0) {
+  fb::eval_chunk<4>(st, in.s, fa, tok_begin, ntok, k, h, col0);
+  return in;
+}
+
+__global__ void __launch_bounds__(NT4, 2) scan4_kernel(ScanArgs p) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  Scan4Smem& sm = *reinterpret_cast<Scan4Smem*>(smem_raw);
+
+  const int num_units = p.num_docs * p.H;
+  const int grp = blockIdx.x / (8 * NTILE);
+  const int rem = blockIdx.x - grp * 8 * NTILE;
+  const int tile = rem / 8;
+  const int u = grp * 8 + (rem & 7);  // rank of the unit (longest documents first)
+  if (u >= num_units) return;
+  const int H = p.H;
+  const int rank = u / H;
+  const int h = u - rank * H;
+  const int doc = p.order ? p.order[rank] : rank;
+  const int col0 = tile * DVT;
+  size_t tok_begin;
+  int ntok, cbase;
+  if (p.cu_seqlens) {
+    tok_begin = p.cu_seqlens[doc];
+    ntok = p.cu_seqlens[doc + 1] - p.cu_seqlens[doc];
+    cbase = p.cstart[doc];
+  } else {
+    tok_begin = static_cast<size_t>(doc) * p.T;
+    ntok = p.T;
+    cbase = doc * p.nchd;
+  }
+  const int nch = (ntok + C - 1) / C;
+  if (cbase + nch > p.n_slots) return;  // malformed cu_seqlens: never read past the workspace
+  const size_t unit_state = (static_cast<size_t>(doc) * H + h) * D * D;
+  const unsigned char* slot0 = p.ws + (static_cast<size_t>(cbase) * H + h) * SLOT_BYTES;
+  const size_t slot_stride = static_cast<size_t>(H) * SLOT_BYTES;
+
+  const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index = token block, uniform (SGPR)
+
+  auto slot_of = [&](int k) { return slot0 + static_cast<size_t>(k) * slot_stride; };
+  auto load_flag = [&](int k, Pre4& r) { r.flag = *reinterpret_cast<const int2*>(slot_of(k) + OFF_FLAG); };
+  auto load_a = [&](int k, Pre4& r) {
+    const unsigned char* sl = slot_of(k);
+    const f16* nw = reinterpret_cast<const f16*>(sl + OFF_NW) + (w * 4 * 64 + lane) * 8;
+    const f16* qs = reinterpret_cast<const f16*>(sl + OFF_QS) + (w * 4 * 64 + lane) * 8;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      r.mw[ks] = ld8(nw + ks * 64 * 8);
+      r.mq[ks] = ld8(qs + ks * 64 * 8);
+    }
+    r.u = ld8(reinterpret_cast<const f16*>(sl + OFF_UP) + ((w * NTILE + tile) * 64 + lane) * 8);
+  };
+  auto load_b = [&](int k, Pre4& r) {
+    const unsigned char* sl = slot_of(k);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const f16* kd = reinterpret_cast<const f16*>(sl + OFF_KDT) + ((2 * w + a) * 2 * 64 + lane) * 8;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) r.kd[a][ks] = ld8(kd + ks * 64 * 8);
+      r.gam[a] = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl + OFF_GAM) + 32 * w + 16 * a +
+                                                  4 * lg);
+    }
+    const f16* as = reinterpret_cast<const f16*>(sl + OFF_AS) + (w * 2 * 64 + lane) * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) r.as[ks] = ld8(as + ks * 64 * 8);
+  };
+  auto load = [&](int k, Pre4& r) {
+    load_flag(k, r);
+    load_a(k, r);
+    load_b(k, r);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // s[a][b][e] = S[32w+16a+4lg+e][col0+16b+lc]
+  auto write_st = [&](f32x4 (&s)[2][2]) {
+    bool big = false;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) big |= !(fabsf(s[a][b][e]) <= S_MAX);
+        *reinterpret_cast<f16x4*>(&sm.ST[16 * b + lc][32 * w + 16 * a + 4 * lg]) = h4(s[a][b]);
+      }
+    const bool any = __builtin_amdgcn_ballot_w64(big) != 0;
+    if (lane == 0) sm.sbp[w] = any;
+  };
+
+  f32x4 s[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        s[a][b][e] = p.init_state
+                         ? p.init_state[unit_state + (32 * w + 16 * a + 4 * lg + e) * D + col0 + 16 * b + lc]
+                         : 0.f;
+  write_st(s);
+  const fb::Args fa{p.q, p.k, p.v, p.log_g, p.beta, p.out, H, p.scale, p.out_bf16, p.l2};
+
+  // One chunk, as in scan_kernel: cur holds chunk k; each group of its
+  // registers is refilled with chunk k+1 right after its last use (one
+  // buffer: the other workgroup on the CU covers the wait).
+  auto step = [&](int k, Pre4& cur) {
+    const int kn = min(k + 1, nch - 1);
+    const size_t tok0 = tok_begin + static_cast<size_t>(k) * C;
+    const int nv = min(C, ntok - k * C);
+    lds_barrier();  // ST of the entry state is complete
+    const int pflag = __builtin_amdgcn_readfirstlane(cur.flag.x | cur.flag.y);
+    __builtin_amdgcn_sched_barrier(0);
+    load_flag(kn, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    const bool sbig = (sm.sbp[0] | sm.sbp[1] | sm.sbp[2] | sm.sbp[3]) != 0;
+
+    // ---- phase A: Delta^T = U^T + S^T (-W)^T (into DT) and the first part of
+    // O^T, S^T Qs^T, for token block w, from one read of the staged state
+    f16x8 sf[4][2];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) sf[ks][b] = ld8(&sm.ST[16 * b + lc][32 * ks + 8 * lg]);
+    bool dbig = false;
+    f32x4 oacc[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      f32x4 acc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = (float)cur.u[4 * b + e];
+      f32x4 o = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        acc = mfma32(sf[ks][b], cur.mw[ks], acc);  // [col 4lg+e][tok lc]
+        o = mfma32(sf[ks][b], cur.mq[ks], o);
+      }
+      oacc[b] = o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dbig |= !(fabsf(acc[e]) <= F16_SAFE);
+        sm.DT[16 * b + 4 * lg + e][16 * w + lc] = (f16)acc[e];
+      }
+    }
+    {
+      const bool any = __builtin_amdgcn_ballot_w64(dbig) != 0;
+      if (lane == 0) sm.dbp[w] = any;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(kn, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+
+    // ---- phase B: S = exp(gamma) S + Kd^T Delta (key rows 32w..), then
+    // O^T += Delta^T As^T (to out)
+    const bool fbk = pflag != 0 || sbig || (sm.dbp[0] | sm.dbp[1] | sm.dbp[2] | sm.dbp[3]) != 0;
+    if (!fbk) {  // workgroup-uniform
+      f16x8 dB[2][2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) dB[ks][b] = ld8(&sm.DT[16 * b + lc][32 * ks + 8 * lg]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const float gg[4] = {cur.gam[a].x, cur.gam[a].y, cur.gam[a].z, cur.gam[a].w};
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[a][b][e] *= gg[e];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) s[a][b] = mfma32(cur.kd[a][ks], dB[ks][b], s[a][b]);
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) oacc[b] = mfma32(dB[ks][b], cur.as[ks], oacc[b]);  // [col 4lg+e][tok lc]
+      __builtin_amdgcn_sched_barrier(0);
+      load_b(kn, cur);
+      __builtin_amdgcn_sched_barrier(0);
+      write_st(s);
+      // output rows past the document's end fall outside the resource
+      const uint32_t osz = p.out_bf16 ? 2u : 4u;
+      const __amdgpu_buffer_rsrc_t orsrc =
+          buffer_rsrc(static_cast<unsigned char*>(p.out) + ((tok0 * H + h) * D + col0) * osz,
+                      static_cast<uint32_t>(((nv - 1) * H * D + DVT)) * osz);
+      const uint32_t ooff = static_cast<uint32_t>((16 * w + lc) * H * D + 4 * lg) * osz;
+      if (p.out_bf16) {  // kernel-argument branch: uniform
+#pragma unroll
+        for (int b = 0; b < 2; ++b) buffer_store8_bf16(oacc[b], orsrc, ooff + 32 * b);
+      } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) buffer_store16(oacc[b], orsrc, ooff + 64 * b);
+      }
+    } else {
+      // token by token from the entry state; writes this chunk's outputs
+      __syncthreads();
+      WaveState4 r;
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) r.s[a][b] = s[a][b];
+      r = scan4_fallback(sm.fb, r, fa, tok_begin, ntok, k, h, col0);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) s[a][b] = r.s[a][b];
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      load_b(kn, cur);
+      __builtin_amdgcn_sched_barrier(0);
+      write_st(s);
+    }
+  };
+
+  if (nch > 0) {  // workgroup-uniform
+    Pre4 b0;
+    load(0, b0);
+    for (int k = 0; k < nch; ++k) step(k, b0);
+  }
+
+  if (p.final_state) {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p.final_state[unit_state + (32 * w + 16 * a + 4 * lg + e) * D + col0 + 16 * b + lc] = s[a][b][e];
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Pass 2, whole-unit form: one 16-wave workgroup per unit owns all 128 value
 // columns, as two halves of 64 columns (waves 8h .. 8h+7).  Within a half the
 // roles are those of scan_kernel with four 16-column blocks instead of two:
@@ -1530,6 +1795,7 @@ static hipError_t prepare_device() {
     } k[] = {{reinterpret_cast<const void*>(prep_kernel<false>), sizeof(PrepSmem)},
              {reinterpret_cast<const void*>(prep_kernel<true>), sizeof(PrepSmem)},
              {reinterpret_cast<const void*>(scan_kernel), sizeof(ScanSmem)},
+             {reinterpret_cast<const void*>(scan4_kernel), sizeof(Scan4Smem)},
              {reinterpret_cast<const void*>(scan_unit_kernel), sizeof(UnitSmem)}};
     for (const auto& x : k) {
       e = hipFuncSetAttribute(x.fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(x.bytes));
@@ -1544,12 +1810,21 @@ static hipError_t prepare_device() {
 // epilogue, which needs a token's 128 columns in one workgroup; else four
 // 32-column tiles per unit, which is faster for a plain output (its steps read
 // a quarter of the staged state per workgroup, and a unit's four workgroups
-// run in parallel).  KDA_PREFILL_PATH=unit forces the whole-unit form for a
-// plain output too (a test and diagnosis switch).
-bool use_unit_scan(const ChunkLaunch& a) {
-  if (a.gate) return true;
+// run in parallel).  The tiles take the four-wave form, two workgroups per CU,
+// when there are more of them than CUs, else the eight-wave form, whose steps
+// are shorter.  KDA_PREFILL_PATH=unit, =tile8 or =tile4 forces a form for a
+// plain output (a test and diagnosis switch).
+enum class ScanForm { Unit, Tile8, Tile4 };
+constexpr int64_t TILE4_MIN_TILES = 257;
+
+ScanForm scan_form(const ChunkLaunch& a) {
+  if (a.gate) return ScanForm::Unit;
   const char* e = std::getenv("KDA_PREFILL_PATH");
-  return e && std::strcmp(e, "unit") == 0;
+  if (e && std::strcmp(e, "unit") == 0) return ScanForm::Unit;
+  if (e && std::strcmp(e, "tile8") == 0) return ScanForm::Tile8;
+  if (e && std::strcmp(e, "tile4") == 0) return ScanForm::Tile4;
+  const int64_t tiles = static_cast<int64_t>(a.num_seqs) * a.num_heads * NTILE;
+  return tiles >= TILE4_MIN_TILES ? ScanForm::Tile4 : ScanForm::Tile8;
 }
 
 hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream) {
@@ -1618,12 +1893,14 @@ hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream) {
   sp.eps = a.eps;
   sp.gate_bf16 = a.gate_bf16;
   const unsigned units = static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads);
-  if (use_unit_scan(a)) {
+  const ScanForm form = scan_form(a);
+  const unsigned blocks = ((units + 7) / 8) * 8 * NTILE;
+  if (form == ScanForm::Unit)
     hipLaunchKernelGGL(scan_unit_kernel, dim3(units), dim3(NTU), sizeof(UnitSmem), stream, sp);
-  } else {
-    const unsigned blocks = ((units + 7) / 8) * 8 * NTILE;
+  else if (form == ScanForm::Tile4)
+    hipLaunchKernelGGL(scan4_kernel, dim3(blocks), dim3(NT4), sizeof(Scan4Smem), stream, sp);
+  else
     hipLaunchKernelGGL(scan_kernel, dim3(blocks), dim3(NTS), sizeof(ScanSmem), stream, sp);
-  }
   return hipGetLastError();
 }
 

@@ -21,10 +21,11 @@ if not torch.cuda.is_available():  # collected on CPU, skipped there
 
 import gated_delta_rule_67_amd as kda  # noqa: E402
 
-# The chunked path's serial pass has two forms: four 32-column workgroups per
-# (sequence or document, head), or one 16-wave workgroup per unit.  Every
-# test runs under both (the switch only affects bf16 d = 128 prefill).
-SCAN_FORMS = ["tile", "unit"]
+# The chunked path's serial pass has three forms: four 32-column workgroups
+# per (sequence or document, head) of eight waves ("tile8") or of four waves,
+# two per CU ("tile4"), or one 16-wave workgroup per unit ("unit").  Every
+# test runs under each (the switch only affects bf16 d = 128 prefill).
+SCAN_FORMS = ["tile8", "tile4", "unit"]
 
 
 @pytest.fixture(params=SCAN_FORMS, autouse=True)
@@ -311,7 +312,9 @@ def test_scan_forms_agree(monkeypatch):
     for form in SCAN_FORMS:
         monkeypatch.setenv("KDA_PREFILL_PATH", form)
         res[form] = run_chunk(inp)
-    (o1, f1), (o2, f2) = res["tile"], res["unit"]
-    e_o, e_f = err(o2.cpu().numpy(), o1.cpu().numpy()), err(f2.cpu().numpy(), f1.cpu().numpy())
-    print(f"[tile vs unit] out={e_o:.3e} final={e_f:.3e}", flush=True)
-    assert e_o <= 1e-5 and e_f <= 1e-5
+    o1, f1 = res["tile8"]
+    for form in SCAN_FORMS[1:]:
+        o2, f2 = res[form]
+        e_o, e_f = err(o2.cpu().numpy(), o1.cpu().numpy()), err(f2.cpu().numpy(), f1.cpu().numpy())
+        print(f"[tile8 vs {form}] out={e_o:.3e} final={e_f:.3e}", flush=True)
+        assert e_o <= 1e-5 and e_f <= 1e-5
