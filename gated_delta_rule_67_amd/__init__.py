@@ -256,10 +256,10 @@ def chunk_fwd_gated_norm(q, k, v, log_g, beta, gate, norm_weight, eps, init_stat
                          out=None, final_state=None, workspace=None, stream=None, out_dtype=torch.bfloat16,
                          qk_l2norm=False):
     """``chunk_fwd`` whose output passes the gated per-head RMSNorm in the same
-    kernels: out = o / sqrt(mean(o^2) + eps) * norm_weight * sigmoid(gate) per
-    (token, head), o never stored.  ``gate`` is shaped like the output with
-    q's dtype, ``norm_weight`` [dv] fp32.  Returns (out [B,T,H,dv] in
-    ``out_dtype``, final_state)."""
+    call: out = o / sqrt(mean(o^2) + eps) * norm_weight * sigmoid(gate) per
+    (token, head), o written to ``out`` in its dtype and normalised there in
+    place.  ``gate`` is shaped like the output with q's dtype, ``norm_weight``
+    [dv] fp32.  Returns (out [B,T,H,dv] in ``out_dtype``, final_state)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     dev, dt = q.device, q.dtype

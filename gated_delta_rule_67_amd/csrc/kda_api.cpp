@@ -502,13 +502,6 @@ kda_status chunk_fwd_checked(const kda_desc* d, const void* q, const void* k, co
     if (!std::isfinite(norm->eps) || norm->eps < 0.f) return fail(KDA_ERR_SHAPE, "%s: eps must be finite and >= 0", fn);
     if (out && (out == norm->gate || out == static_cast<const void*>(norm->weight)))
       return fail(KDA_ERR_SHAPE, "%s: out aliases gate or norm_weight", fn);
-    if (path != Path::TwoPass)
-      return fail(KDA_ERR_UNSUPPORTED, "%s: the fused norm needs the chunked path (bf16 q/k/v, d = 128); use "
-                  "kda_chunk_fwd then kda_gated_rmsnorm", fn);
-    a.gate = norm->gate;
-    a.norm_w = norm->weight;
-    a.eps = norm->eps;
-    a.gate_bf16 = d->qkv_dtype == KDA_BF16;
   }
   const size_t ws_need = workspace_need(path, a);
   if (ws_need > 0) {
@@ -539,8 +532,24 @@ kda_status chunk_fwd_checked(const kda_desc* d, const void* q, const void* k, co
         (final_state && final_state != init_state && hipMemsetAsync(final_state, 0xff, n_fin * 4, s) != hipSuccess))
       return fail(KDA_ERR_HIP, "%s (KDA_VALIDATE): NaN fill failed", fn);
   }
-  const hipError_t e = path == Path::TwoPass ? kda::launch_chunk_twopass(a, s) : kda::launch_chunk_recurrent(a, s);
+  hipError_t e = path == Path::TwoPass ? kda::launch_chunk_twopass(a, s) : kda::launch_chunk_recurrent(a, s);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  if (norm && has_tok) {
+    // the output, as just stored in its own dtype, normalised in place
+    kda::NormLaunch nl{};
+    nl.o = out;
+    nl.gate = norm->gate;
+    nl.weight = norm->weight;
+    nl.out = out;
+    nl.rows = tokens * d->num_heads;
+    nl.d = d->dv;
+    nl.eps = norm->eps;
+    nl.gate_bf16 = d->qkv_dtype == KDA_BF16;
+    nl.out_bf16 = a.out_bf16;
+    nl.o_bf16 = a.out_bf16;
+    e = kda::launch_gated_rmsnorm(nl, s);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: %s", fn, hipGetErrorString(e));
+  }
   if (check) {
     if (hipStreamSynchronize(s) != hipSuccess) return fail(KDA_ERR_HIP, "%s (KDA_VALIDATE): kernel failed", fn);
     if ((st = validate_output(out, n_out, a.out_bf16, "out", s, fn)) != KDA_OK) return st;

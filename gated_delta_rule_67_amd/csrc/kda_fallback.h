@@ -50,18 +50,16 @@ struct Args {
 };
 
 // Chunk ck of the document whose tokens start at tok_begin (ntok tokens), head
-// h, state columns col0 .. col0+31.  Writes the chunk's outputs and advances s.
-// The NWAVE waves from thread tbase on run it together (it synchronises
-// the whole workgroup internally, so every thread of the workgroup must call
-// it the same number of times).  Outputs go to p.out, or, when obuf is not
-// null, as fp32 to obuf[token in chunk * obs + col0 + column] (LDS staging).
+// h, state columns col0 .. col0+31.  Writes the chunk's outputs to p.out and
+// advances s.  The NWAVE waves of the workgroup run it together (it
+// synchronises the whole workgroup internally, so every thread of the
+// workgroup must call it the same number of times).
 template <int NWAVE>
 __device__ __forceinline__ void eval_chunk(Stage<NWAVE>& st, f32x4 (&s)[8 / NWAVE][2], const Args& p,
-                                           size_t tok_begin, int ntok, int ck, int h, int col0, int tbase = 0,
-                                           float* obuf = nullptr, int obs = 0) {
+                                           size_t tok_begin, int ntok, int ck, int h, int col0) {
   constexpr int NT = 64 * NWAVE;
   constexpr int NA = 8 / NWAVE;
-  const int tid = static_cast<int>(threadIdx.x) - tbase, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
+  const int tid = static_cast<int>(threadIdx.x), lane = tid & 63, lc = lane & 15, lg = lane >> 4;
   const int cw = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform (SGPR)
   const int H = p.H;
   const int nv = min(C, ntok - ck * C);
@@ -188,15 +186,11 @@ __device__ __forceinline__ void eval_chunk(Stage<NWAVE>& st, f32x4 (&s)[8 / NWAV
           dl[b] = bt * (st.v[r][n] - A);
           if (cw == 0 && lg == 0) {
             const float o = p.scale * (B + dl[b] * kq);
-            if (obuf) {
-              obuf[(t0 + r) * obs + col0 + n] = o;
-            } else {
-              const size_t oi = ((tok0 + t0 + r) * H + h) * D + col0 + n;
-              if (p.out_bf16)
-                reinterpret_cast<__bf16*>(p.out)[oi] = static_cast<__bf16>(o);
-              else
-                static_cast<float*>(p.out)[oi] = o;
-            }
+            const size_t oi = ((tok0 + t0 + r) * H + h) * D + col0 + n;
+            if (p.out_bf16)
+              reinterpret_cast<__bf16*>(p.out)[oi] = static_cast<__bf16>(o);
+            else
+              static_cast<float*>(p.out)[oi] = o;
           }
         }
 #pragma unroll

@@ -8,7 +8,7 @@
 
 namespace kda {
 
-// The gated RMSNorm fused behind a prefill (kda_chunk_fwd_gated_norm).
+// The gated RMSNorm applied to a prefill's output (kda_chunk_fwd_gated_norm).
 struct OutNorm {
   const void* gate;      // like out, element type qkv_dtype
   const float* weight;   // [dv]
@@ -17,8 +17,9 @@ struct OutNorm {
 
 // kda_chunk_fwd's validation and launch with the workspace given explicitly:
 // the caller's (desc->workspace) or the library's fixed scratch (fixed_ws,
-// ws_bytes = its capacity).  norm (or null) fuses the gated RMSNorm into the
-// output.  fn names the entry point in error messages.
+// ws_bytes = its capacity).  norm (or null): the output is normalised in
+// place by the gated RMSNorm after the prefill.  fn names the entry point in
+// error messages.
 kda_status chunk_fwd_checked(const kda_desc* d, const void* q, const void* k, const void* v, const float* log_g,
                              const float* beta, const float* init_state, const int32_t* cu_seqlens, void* out,
                              float* final_state, void* stream, void* ws, size_t ws_bytes, bool fixed_ws,
@@ -82,11 +83,6 @@ struct ChunkLaunch {
   bool out_bf16;              // out element type (else fp32)
   bool l2;                    // L2-normalise the q and k rows first
   float scale;
-  // gated RMSNorm of the output (two-pass path only): gate null = none
-  const void* gate;           // like out, bf16 when gate_bf16 else fp32
-  const float* norm_w;        // [d]
-  float eps;
-  bool gate_bf16;
 };
 
 hipError_t launch_step(const StepLaunch& a, hipStream_t stream);
@@ -151,7 +147,7 @@ hipError_t launch_short_conv(const ConvLaunch& a, hipStream_t stream);
 
 // Arguments of one gated per-head RMSNorm; shapes already validated.
 struct NormLaunch {
-  const float* o;       // [rows, d]
+  const void* o;        // [rows, d], fp32, or bf16 when o_bf16; may be out
   const void* gate;     // [rows, d]
   const float* weight;  // [d]
   void* out;            // [rows, d]
@@ -160,6 +156,7 @@ struct NormLaunch {
   float eps;
   bool gate_bf16;
   bool out_bf16;
+  bool o_bf16;
 };
 
 hipError_t launch_gated_rmsnorm(const NormLaunch& a, hipStream_t stream);

@@ -9,7 +9,8 @@
 //
 // HBM-bound (o read, gate read, y written once).  A group of D / 8 lanes owns
 // one row, 8 channels per lane; the sum of squares is reduced with shuffles
-// inside the group.
+// inside the group.  o is fp32, or bf16 like out; out may be o itself (every
+// element is read and written by the same lane).
 #include "kda_common.h"
 #include "kda_launch.h"
 #include "kda_vec8.h"
@@ -20,7 +21,7 @@ namespace {
 constexpr int NTN = 256;
 
 struct NormArgs {
-  const float* o;
+  const void* o;
   const void* g;
   const float* w;
   void* out;
@@ -28,7 +29,7 @@ struct NormArgs {
   float eps;
 };
 
-template <int D, typename G, typename O>
+template <int D, typename G, typename O, typename OIn>
 __global__ void __launch_bounds__(NTN) gated_rmsnorm_kernel(NormArgs a) {
   constexpr int L = D / 8;  // lanes per row (divides 64)
   const int64_t gid = static_cast<int64_t>(blockIdx.x) * NTN + threadIdx.x;
@@ -37,7 +38,7 @@ __global__ void __launch_bounds__(NTN) gated_rmsnorm_kernel(NormArgs a) {
   if (row >= a.rows) return;  // the lanes of one row leave together
   const int64_t off = row * D + 8 * part;
   float o[8], g[8], w[8];
-  load8f(a.o + off, o);
+  load8f(static_cast<const OIn*>(a.o) + off, o);
   load8f(static_cast<const G*>(a.g) + off, g);
   load8f(a.w + 8 * part, w);
   float ss = 0.f;
@@ -52,18 +53,23 @@ __global__ void __launch_bounds__(NTN) gated_rmsnorm_kernel(NormArgs a) {
   store8f(static_cast<O*>(a.out) + off, y);
 }
 
-template <int D>
+template <int D, typename OIn>
 hipError_t launch_d(const NormLaunch& s, const NormArgs& a, hipStream_t stream) {
   const int64_t threads = a.rows * (D / 8);
   const unsigned blocks = static_cast<unsigned>((threads + NTN - 1) / NTN);
   if (s.gate_bf16) {
-    if (s.out_bf16) hipLaunchKernelGGL((gated_rmsnorm_kernel<D, bf16_t, bf16_t>), dim3(blocks), dim3(NTN), 0, stream, a);
-    else hipLaunchKernelGGL((gated_rmsnorm_kernel<D, bf16_t, float>), dim3(blocks), dim3(NTN), 0, stream, a);
+    if (s.out_bf16) hipLaunchKernelGGL((gated_rmsnorm_kernel<D, bf16_t, bf16_t, OIn>), dim3(blocks), dim3(NTN), 0, stream, a);
+    else hipLaunchKernelGGL((gated_rmsnorm_kernel<D, bf16_t, float, OIn>), dim3(blocks), dim3(NTN), 0, stream, a);
   } else {
-    if (s.out_bf16) hipLaunchKernelGGL((gated_rmsnorm_kernel<D, float, bf16_t>), dim3(blocks), dim3(NTN), 0, stream, a);
-    else hipLaunchKernelGGL((gated_rmsnorm_kernel<D, float, float>), dim3(blocks), dim3(NTN), 0, stream, a);
+    if (s.out_bf16) hipLaunchKernelGGL((gated_rmsnorm_kernel<D, float, bf16_t, OIn>), dim3(blocks), dim3(NTN), 0, stream, a);
+    else hipLaunchKernelGGL((gated_rmsnorm_kernel<D, float, float, OIn>), dim3(blocks), dim3(NTN), 0, stream, a);
   }
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_o(const NormLaunch& s, const NormArgs& a, hipStream_t stream) {
+  return s.o_bf16 ? launch_d<D, bf16_t>(s, a, stream) : launch_d<D, float>(s, a, stream);
 }
 
 }  // namespace
@@ -72,10 +78,10 @@ hipError_t launch_gated_rmsnorm(const NormLaunch& s, hipStream_t stream) {
   if (s.rows == 0) return hipSuccess;
   NormArgs a{s.o, s.gate, s.weight, s.out, s.rows, s.eps};
   switch (s.d) {
-    case 16: return launch_d<16>(s, a, stream);
-    case 32: return launch_d<32>(s, a, stream);
-    case 64: return launch_d<64>(s, a, stream);
-    case 128: return launch_d<128>(s, a, stream);
+    case 16: return launch_o<16>(s, a, stream);
+    case 32: return launch_o<32>(s, a, stream);
+    case 64: return launch_o<64>(s, a, stream);
+    case 128: return launch_o<128>(s, a, stream);
     default: return hipErrorInvalidValue;
   }
 }

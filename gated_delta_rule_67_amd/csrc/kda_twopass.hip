@@ -816,11 +816,6 @@ struct ScanArgs {
   int nchd;
   int n_slots;                // chunk slots per head in the workspace
   float scale;
-  // gated RMSNorm epilogue (whole-unit scan only): gate null = plain output
-  const void* gate;           // [.., H, D], bf16 when gate_bf16 else fp32
-  const float* norm_w;        // [D]
-  float eps;
-  bool gate_bf16;
 };
 
 constexpr int NTS = 512;  // scan threads: 8 waves
@@ -1348,304 +1343,6 @@ __global__ void __launch_bounds__(NT4, 2) scan4_kernel(ScanArgs p) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2, whole-unit form: one 16-wave workgroup per unit owns all 128 value
-// columns, as two halves of 64 columns (waves 8h .. 8h+7).  Within a half the
-// roles are those of scan_kernel with four 16-column blocks instead of two:
-// waves 0-3 of the half form Delta rows 16I.., waves 4-7 output rows 16I..,
-// and every wave updates key rows 16w'.. (w' = wave in the half) of its
-// half's columns.  The halves share nothing but the staged operands, the
-// workgroup barriers and the output staging: the outputs of a chunk land in
-// an fp32 LDS tile of whole token rows, from which every thread stores
-// 8-column pieces of rows, optionally through the gated RMSNorm
-// o / sqrt(mean(o^2) + eps) * w * sigmoid(gate) (NeMo glm5_next.layers,
-// `_TorchRMSNormGated`), which needs a token's 128 columns together.  Every
-// wave still reads its half's whole staged state each step, so a unit-step
-// moves as many LDS bytes as scan_kernel's four tile-steps, with a quarter of
-// the workgroups: a plain output takes scan_kernel.
-constexpr int NTU = 1024;     // whole-unit scan threads: 16 waves
-constexpr int LDO = D + 4;    // fp32 row stride of the output staging
-
-struct __align__(16) UnitSmem {
-  f16 ST[D][LDK];     // S^T (fp16) [value col][key row], both halves
-  f16 DT[D][LDT];     // Delta^T    [value col][token]
-  float OS[C][LDO];   // the chunk's outputs, fp32 [token][value col]
-  fb::Stage<8> fb[2]; // exact per-token fallback, one per half
-  float nw[D];        // norm weight
-  int sbp[16];        // per wave: state beyond the fast-path bound
-  int dbp[16];        // per wave: Delta beyond the fp16 bound (output waves: unused)
-};
-
-struct UPre {
-  f16x8 m[4];   // -W or Qs row 16I+lc, key cols 32ks+8lg ..
-  f16x8 u[2];   // U of this lane for the half's two 32-column tiles (Delta waves)
-  f16x8 kd[2];  // Kd^T row 16w'+lc, tokens 32ks+8lg ..
-  f16x8 as[2];  // As row 16I+lc, tokens 32ks+8lg .. (output waves)
-  float4 gam;   // exp(gamma) of key rows 16w'+4lg ..
-  int2 flag;
-};
-
-struct State4 {
-  f32x4 s[4];
-};
-
-// The exact per-token evaluation of one chunk for this half's 64 columns (two
-// 32-column tiles, one after the other), outputs into the staging tile.
-__device__ __noinline__ State4 unit_fallback(fb::Stage<8>& st, State4 in, const fb::Args fa, size_t tok_begin,
-                                             int ntok, int k, int h, int half, float* os) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    f32x4 s[1][2] = {{in.s[2 * t], in.s[2 * t + 1]}};
-    fb::eval_chunk<8>(st, s, fa, tok_begin, ntok, k, h, 64 * half + 32 * t, 512 * half, os, LDO);
-    in.s[2 * t] = s[0][0];
-    in.s[2 * t + 1] = s[0][1];
-  }
-  return in;
-}
-
-__global__ void __launch_bounds__(NTU, 1) scan_unit_kernel(ScanArgs p) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  UnitSmem& sm = *reinterpret_cast<UnitSmem*>(smem_raw);
-
-  const int num_units = p.num_docs * p.H;
-  const int u = blockIdx.x;  // rank of the unit (longest documents first)
-  if (u >= num_units) return;
-  const int H = p.H;
-  const int rank = u / H;
-  const int h = u - rank * H;
-  const int doc = p.order ? p.order[rank] : rank;
-  size_t tok_begin;
-  int ntok, cbase;
-  if (p.cu_seqlens) {
-    tok_begin = p.cu_seqlens[doc];
-    ntok = p.cu_seqlens[doc + 1] - p.cu_seqlens[doc];
-    cbase = p.cstart[doc];
-  } else {
-    tok_begin = static_cast<size_t>(doc) * p.T;
-    ntok = p.T;
-    cbase = doc * p.nchd;
-  }
-  const int nch = (ntok + C - 1) / C;
-  if (cbase + nch > p.n_slots) return;  // malformed cu_seqlens: never read past the workspace
-  const size_t unit_state = (static_cast<size_t>(doc) * H + h) * D * D;
-  const unsigned char* slot0 = p.ws + (static_cast<size_t>(cbase) * H + h) * SLOT_BYTES;
-  const size_t slot_stride = static_cast<size_t>(H) * SLOT_BYTES;
-
-  const int tid = threadIdx.x, lane = tid & 63, lc = lane & 15, lg = lane >> 4;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index 0..15, uniform (SGPR)
-  const int half = wv >> 3;     // value columns 64 half ..
-  const int w = wv & 7;         // wave within the half
-  const bool is_o = w >= 4;     // output wave (else Delta wave)
-  const int I = w & 3;          // token block of the Delta / output rows
-  const int c0 = 64 * half;     // first value column of the half
-
-  if (p.gate && tid < D) sm.nw[tid] = p.norm_w[tid];
-
-  auto slot_of = [&](int k) { return slot0 + static_cast<size_t>(k) * slot_stride; };
-  auto load_flag = [&](int k, UPre& r) { r.flag = *reinterpret_cast<const int2*>(slot_of(k) + OFF_FLAG); };
-  auto load_a = [&](int k, UPre& r) {
-    const unsigned char* sl = slot_of(k);
-    const f16* mp = reinterpret_cast<const f16*>(sl + (is_o ? OFF_QS : OFF_NW)) + (I * 4 * 64 + lane) * 8;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) r.m[ks] = ld8(mp + ks * 64 * 8);
-    if (!is_o) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        r.u[t] = ld8(reinterpret_cast<const f16*>(sl + OFF_UP) + ((I * NTILE + 2 * half + t) * 64 + lane) * 8);
-    } else {
-      r.u[0] = r.u[1] = f16x8{};
-    }
-  };
-  auto load_b = [&](int k, UPre& r) {
-    const unsigned char* sl = slot_of(k);
-    const f16* kd = reinterpret_cast<const f16*>(sl + OFF_KDT) + (w * 2 * 64 + lane) * 8;
-    const f16* as = reinterpret_cast<const f16*>(sl + OFF_AS) + (I * 2 * 64 + lane) * 8;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) r.kd[ks] = ld8(kd + ks * 64 * 8);
-    if (is_o) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) r.as[ks] = ld8(as + ks * 64 * 8);
-    } else {
-      r.as[0] = r.as[1] = f16x8{};
-    }
-    r.gam = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(sl + OFF_GAM) + 16 * w + 4 * lg);
-  };
-
-  // s.s[b][e] = S[16w+4lg+e][c0+16b+lc]
-  auto write_st = [&](const State4& s) {
-    bool big = false;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) big |= !(fabsf(s.s[b][e]) <= S_MAX);
-      *reinterpret_cast<f16x4*>(&sm.ST[c0 + 16 * b + lc][16 * w + 4 * lg]) = h4(s.s[b]);
-    }
-    const bool any = __builtin_amdgcn_ballot_w64(big) != 0;
-    if (lane == 0) sm.sbp[wv] = any;
-  };
-
-  State4 st;
-#pragma unroll
-  for (int b = 0; b < 4; ++b)
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      st.s[b][e] = p.init_state ? p.init_state[unit_state + (16 * w + 4 * lg + e) * D + c0 + 16 * b + lc] : 0.f;
-  write_st(st);
-  const fb::Args fa{p.q, p.k, p.v, p.log_g, p.beta, p.out, H, p.scale, p.out_bf16, p.l2};
-
-  // Output rows of chunk k from the staging tile: 16 threads per token row,
-  // 8 columns each (64 rows per pass of the 1024 threads); rows past the
-  // document's end are not stored.
-  auto emit = [&](int k) {
-    const int row = tid >> 4, cc = (tid & 15) * 8;
-    const int nv = min(C, ntok - k * C);
-    float o[8];
-    const float4 a0 = *reinterpret_cast<const float4*>(&sm.OS[row][cc]);
-    const float4 a1 = *reinterpret_cast<const float4*>(&sm.OS[row][cc + 4]);
-    o[0] = a0.x; o[1] = a0.y; o[2] = a0.z; o[3] = a0.w; o[4] = a1.x; o[5] = a1.y; o[6] = a1.z; o[7] = a1.w;
-    const size_t oi = ((tok_begin + static_cast<size_t>(k) * C + row) * H + h) * D + cc;
-    if (p.gate) {  // kernel argument: uniform
-      float ss = 0.f;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) ss += o[c] * o[c];
-#pragma unroll
-      for (int x = 1; x < 16; x <<= 1) ss += __shfl_xor(ss, x, 64);
-      const float inv = __frsqrt_rn(ss * (1.f / D) + p.eps);
-      float g[8];
-      if (row < nv) {
-        if (p.gate_bf16) {
-          const uint4 gw = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(p.gate) + oi);
-          g[0] = bf16_lo(gw.x); g[1] = bf16_hi(gw.x); g[2] = bf16_lo(gw.y); g[3] = bf16_hi(gw.y);
-          g[4] = bf16_lo(gw.z); g[5] = bf16_hi(gw.z); g[6] = bf16_lo(gw.w); g[7] = bf16_hi(gw.w);
-        } else {
-          const float4 g0 = *reinterpret_cast<const float4*>(static_cast<const float*>(p.gate) + oi);
-          const float4 g1 = *reinterpret_cast<const float4*>(static_cast<const float*>(p.gate) + oi + 4);
-          g[0] = g0.x; g[1] = g0.y; g[2] = g0.z; g[3] = g0.w; g[4] = g1.x; g[5] = g1.y; g[6] = g1.z; g[7] = g1.w;
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) o[c] = o[c] * inv * sm.nw[cc + c] / (1.f + exp_fast(-g[c]));
-      }
-    }
-    if (row < nv) {
-      if (p.out_bf16) {
-        store_out4(static_cast<bf16_t*>(p.out) + oi, o[0], o[1], o[2], o[3]);
-        store_out4(static_cast<bf16_t*>(p.out) + oi + 4, o[4], o[5], o[6], o[7]);
-      } else {
-        store_out4(static_cast<float*>(p.out) + oi, o[0], o[1], o[2], o[3]);
-        store_out4(static_cast<float*>(p.out) + oi + 4, o[4], o[5], o[6], o[7]);
-      }
-    }
-  };
-
-  // One chunk: consume cur (chunk k), refilling each group of its registers
-  // with chunk k+1 right after the group's last use.
-  auto step = [&](int k, UPre& cur) {
-    const int kn = min(k + 1, nch - 1);
-    lds_barrier();  // ST of the entry state is complete; the previous chunk's outputs are stored
-    const int pflag = __builtin_amdgcn_readfirstlane(cur.flag.x | cur.flag.y);
-    __builtin_amdgcn_sched_barrier(0);
-    load_flag(kn, cur);
-    __builtin_amdgcn_sched_barrier(0);
-    int sb = 0;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) sb |= sm.sbp[x];
-    const bool sbig = sb != 0;
-
-    // ---- phase A: Delta^T = U^T + S^T (-W)^T (Delta waves, into DT) and
-    // O^T = S^T Qs^T (output waves, kept), column block by column block
-    bool dbig = false;
-    f32x4 oacc[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      f16x8 sf[4];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sf[ks] = ld8(&sm.ST[c0 + 16 * b + lc][32 * ks + 8 * lg]);
-      f32x4 acc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = is_o ? 0.f : (float)cur.u[b >> 1][4 * (b & 1) + e];
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mfma32(sf[ks], cur.m[ks], acc);  // [col 4lg+e][tok lc]
-      oacc[b] = acc;
-      if (!is_o) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          dbig |= !(fabsf(acc[e]) <= F16_SAFE);
-          sm.DT[c0 + 16 * b + 4 * lg + e][16 * I + lc] = (f16)acc[e];
-        }
-      }
-    }
-    {
-      const bool any = __builtin_amdgcn_ballot_w64(dbig) != 0;
-      if (lane == 0) sm.dbp[wv] = any;
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    load_a(kn, cur);
-    __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();
-
-    // ---- phase B: S = exp(gamma) S + Kd^T Delta (all waves), O^T += Delta^T As^T
-    // (output waves), outputs to the staging tile
-    int db = 0;
-#pragma unroll
-    for (int x = 0; x < 16; ++x) db |= (x & 7) < 4 ? sm.dbp[x] : 0;
-    const bool fbk = pflag != 0 || sbig || db != 0;
-    if (!fbk) {  // workgroup-uniform
-      const float gg[4] = {cur.gam.x, cur.gam.y, cur.gam.z, cur.gam.w};
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        f16x8 dB[2];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) dB[ks] = ld8(&sm.DT[c0 + 16 * b + lc][32 * ks + 8 * lg]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st.s[b][e] *= gg[e];
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) st.s[b] = mfma32(cur.kd[ks], dB[ks], st.s[b]);
-        if (is_o) {
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks) oacc[b] = mfma32(dB[ks], cur.as[ks], oacc[b]);  // [col 4lg+e][tok lc]
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      load_b(kn, cur);
-      __builtin_amdgcn_sched_barrier(0);
-      write_st(st);
-      if (is_o) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sm.OS[16 * I + lc][c0 + 16 * b + 4 * lg + e] = oacc[b][e];
-      }
-    } else {
-      // token by token from the entry state, outputs into the staging tile
-      __syncthreads();
-      st = unit_fallback(sm.fb[half], st, fa, tok_begin, ntok, k, h, half, &sm.OS[0][0]);
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      load_b(kn, cur);
-      __builtin_amdgcn_sched_barrier(0);
-      write_st(st);
-    }
-    lds_barrier();  // the staging tile is complete
-    emit(k);
-  };
-
-  if (nch > 0) {  // workgroup-uniform
-    UPre cur;
-    load_flag(0, cur);
-    load_a(0, cur);
-    load_b(0, cur);
-    for (int k = 0; k < nch; ++k) step(k, cur);
-  }
-
-  if (p.final_state) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        p.final_state[unit_state + (16 * w + 4 * lg + e) * D + c0 + 16 * b + lc] = st.s[b][e];
-  }
-}
-
-// ---------------------------------------------------------------------------
 // Packed problems: the document map, one workgroup.
 //  - cstart[d] = sum over earlier documents of ceil(len / 64); cstart[n] = total;
 //  - table[slot] = document owning the slot (a binary search of cstart per
@@ -1795,8 +1492,7 @@ static hipError_t prepare_device() {
     } k[] = {{reinterpret_cast<const void*>(prep_kernel<false>), sizeof(PrepSmem)},
              {reinterpret_cast<const void*>(prep_kernel<true>), sizeof(PrepSmem)},
              {reinterpret_cast<const void*>(scan_kernel), sizeof(ScanSmem)},
-             {reinterpret_cast<const void*>(scan4_kernel), sizeof(Scan4Smem)},
-             {reinterpret_cast<const void*>(scan_unit_kernel), sizeof(UnitSmem)}};
+             {reinterpret_cast<const void*>(scan4_kernel), sizeof(Scan4Smem)}};
     for (const auto& x : k) {
       e = hipFuncSetAttribute(x.fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(x.bytes));
       if (e != hipSuccess) return e;
@@ -1806,21 +1502,15 @@ static hipError_t prepare_device() {
   return hipSuccess;
 }
 
-// Scan form: whole units (one 16-wave workgroup per unit) for the gated-norm
-// epilogue, which needs a token's 128 columns in one workgroup; else four
-// 32-column tiles per unit, which is faster for a plain output (its steps read
-// a quarter of the staged state per workgroup, and a unit's four workgroups
-// run in parallel).  The tiles take the four-wave form, two workgroups per CU,
-// when there are more of them than CUs, else the eight-wave form, whose steps
-// are shorter.  KDA_PREFILL_PATH=unit, =tile8 or =tile4 forces a form for a
-// plain output (a test and diagnosis switch).
-enum class ScanForm { Unit, Tile8, Tile4 };
+// Scan form: four 32-column tiles per (sequence or document, head); the
+// four-wave form, two workgroups per CU, when there are more tiles than CUs,
+// else the eight-wave form, whose steps are shorter.  KDA_PREFILL_PATH=tile8
+// or =tile4 forces a form (a test and diagnosis switch).
+enum class ScanForm { Tile8, Tile4 };
 constexpr int64_t TILE4_MIN_TILES = 257;
 
 ScanForm scan_form(const ChunkLaunch& a) {
-  if (a.gate) return ScanForm::Unit;
   const char* e = std::getenv("KDA_PREFILL_PATH");
-  if (e && std::strcmp(e, "unit") == 0) return ScanForm::Unit;
   if (e && std::strcmp(e, "tile8") == 0) return ScanForm::Tile8;
   if (e && std::strcmp(e, "tile4") == 0) return ScanForm::Tile4;
   const int64_t tiles = static_cast<int64_t>(a.num_seqs) * a.num_heads * NTILE;
@@ -1888,16 +1578,10 @@ hipError_t launch_chunk_twopass(const ChunkLaunch& a, hipStream_t stream) {
   sp.nchd = nchd;
   sp.n_slots = static_cast<int>(ns);
   sp.scale = a.scale;
-  sp.gate = a.gate;
-  sp.norm_w = a.norm_w;
-  sp.eps = a.eps;
-  sp.gate_bf16 = a.gate_bf16;
   const unsigned units = static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads);
   const ScanForm form = scan_form(a);
   const unsigned blocks = ((units + 7) / 8) * 8 * NTILE;
-  if (form == ScanForm::Unit)
-    hipLaunchKernelGGL(scan_unit_kernel, dim3(units), dim3(NTU), sizeof(UnitSmem), stream, sp);
-  else if (form == ScanForm::Tile4)
+  if (form == ScanForm::Tile4)
     hipLaunchKernelGGL(scan4_kernel, dim3(blocks), dim3(NT4), sizeof(Scan4Smem), stream, sp);
   else
     hipLaunchKernelGGL(scan_kernel, dim3(blocks), dim3(NTS), sizeof(ScanSmem), stream, sp);

@@ -164,22 +164,23 @@ kda_status kda_chunk_fwd(const kda_desc* desc, const void* q, const void* k,
                          void* out, float* final_state, void* stream);
 
 /*
- * kda_chunk_fwd with the gated per-head RMSNorm of its output fused into the
- * scan's epilogue (NeMo glm5_next.layers: the mixer output passes
+ * kda_chunk_fwd with the gated per-head RMSNorm applied to its output in the
+ * same call (NeMo glm5_next.layers: the mixer output passes
  * `_TorchRMSNormGated` before the output projection; kda_gated_rmsnorm below
- * is the same norm as a pass of its own).  out receives, per token t and
- * head h, with o[t,h,:] what kda_chunk_fwd would write (never stored here):
+ * is the same norm as a call of its own).  out receives, per token t and
+ * head h, with o[t,h,:] what kda_chunk_fwd would write:
  *
  *     out[t,h,i] = o[t,h,i] / sqrt(mean(o[t,h,:]^2) + eps) * norm_weight[i] * sigmoid(gate[t,h,i])
  *
  *   gate         [B, T, H, dv], element type desc->qkv_dtype
  *   norm_weight  [dv] fp32 (shared by the heads);  eps >= 0
- *   out          [B, T, H, dv], out_dtype (bf16 rounds the normalised value once)
- * Everything else (arguments, workspace, final_state, errors, KDA_VALIDATE)
- * is as for kda_chunk_fwd.  Supported where kda_chunk_fwd takes the chunked
- * two-pass path (bf16 q/k/v, d = 128); other configurations return
- * KDA_ERR_UNSUPPORTED (run kda_chunk_fwd, then kda_gated_rmsnorm).  out
- * must not alias gate or norm_weight.
+ *   out          [B, T, H, dv], out_dtype
+ * o is first stored into out in out_dtype and then normalised there in place
+ * by a second pass on the same stream (with bf16 out: o rounded once to bf16,
+ * the normalised value rounded once more).  Every kda_chunk_fwd configuration
+ * is supported.  Everything else (arguments, workspace, final_state, errors,
+ * KDA_VALIDATE on the prefill) is as for kda_chunk_fwd.  out must not alias
+ * gate or norm_weight.
  */
 kda_status kda_chunk_fwd_gated_norm(const kda_desc* desc, const void* q, const void* k,
                                     const void* v, const float* log_g, const float* beta,

@@ -267,9 +267,11 @@ def norm_bar(y, y_ref, o_ref, gate, w, eps, tol, bf16_out):
     bar (|do| <= tol * rms of the whole output) carried through the norm.
     With r = sqrt(mean(o^2) + eps) of the row, d(o_i / r) = do_i / r -
     o_i dr / r^2 and |dr| <= max|do|, so |dy_i| <= |w_i sigmoid(g_i)| (1 +
-    |o_i| / r) max|do| / r; bf16 out adds one rounding, 2^-8 |y_i|.  A row whose
-    own RMS is far below the tensor's (a first token whose q.k nearly cancels)
-    is amplified by the norm, and the bar grows with it."""
+    |o_i| / r) max|do| / r.  bf16 out adds two roundings of at most 2^-9 |y_i|
+    each: o is stored in the output's dtype before the norm reads it back, and
+    y is rounded once.  A row whose own RMS is far below the tensor's (a first
+    token whose q.k nearly cancels) is amplified by the norm, and the bar grows
+    with it."""
     y = np.asarray(y, dtype=np.float64)
     assert np.all(np.isfinite(y))
     do = tol * np.sqrt(np.mean(o_ref ** 2))
@@ -343,9 +345,21 @@ def test_packed_workload_gated_norm_bf16_out():
     assert bar <= 1.0 and e_f <= TOL["bf16"]
 
 
-def test_gated_norm_needs_the_chunked_path():
-    inp = kda_inputs.make_inputs(B=1, T=40, H=2, dk=64, dv=64, dtype="bf16", seed=347)
-    gate, w = norm_inputs(inp, 348)
-    with pytest.raises(kda.KdaError) as ei:
-        fused(inp, gate, w, 1e-6)
-    assert ei.value.status == 6
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("f32", 128)])
+def test_gated_norm_on_the_recurrent_path(dtype, d):
+    """Configurations outside the chunked MFMA path (d < 128, fp32 q/k/v) take
+    the token-recurrent prefill, then the same in-place norm."""
+    inp = kda_inputs.make_inputs(B=2, T=75, H=2, dk=d, dv=d, dtype=dtype, seed=347, init="normal", init_std=0.1)
+    B, T, H, D = inp["v"].shape
+    rng = np.random.default_rng(348)
+    g32 = rng.standard_normal((B, T, H, D), dtype=np.float32)
+    gate = torch.from_numpy(g32).to(torch.bfloat16) if dtype == "bf16" else torch.from_numpy(g32)
+    w = torch.from_numpy(rng.standard_normal(D).astype(np.float32))
+    out, fin = fused(inp, gate, w, 1e-6, out_dtype=torch.float32)
+    ref_o, ref_f = oracle_full(inp)
+    ref = oracle.gated_rmsnorm(ref_o, to_f64(gate), to_f64(w), 1e-6)
+    tol = TOL["bf16"] if dtype == "bf16" else TOL["f32"]
+    bar = norm_bar(out.cpu().numpy(), ref, ref_o, gate, w, 1e-6, tol, False)
+    print(f"[norm recurrent {dtype} d={d}] {bar:.3f} of the bar", flush=True)
+    assert bar <= 1.0
+    assert err(fin.cpu().numpy(), ref_f) <= tol
