@@ -72,11 +72,11 @@ COPY_BYTES = 512 << 20         # calibration copy: bytes read (= bytes written)
 TRAFFIC = {
     "varlen": dict(file=os.path.join(ROOT, "profiles", "traffic_prefill_packed.txt"),
                    sources=["kda_twopass.hip", "kda_common.h", "kda_fallback.h"],
-                   kernels=("prep_kernel", "scan_kernel"),
+                   kernels=("prep_kernel", "scan_kernel", "scan4_kernel"),
                    what="one kda_chunk_fwd call, packed 65536 tokens in 26 documents, 32 heads, d = 128, bf16"),
     "prefill": dict(file=os.path.join(ROOT, "profiles", "traffic_prefill_dense.txt"),
                     sources=["kda_twopass.hip", "kda_common.h", "kda_fallback.h"],
-                    kernels=("prep_kernel", "scan_kernel"),
+                    kernels=("prep_kernel", "scan_kernel", "scan4_kernel"),
                     what="one kda_chunk_fwd call, dense 4 x 4096 tokens, 16 heads, d = 128, bf16"),
     "backward": dict(file=os.path.join(ROOT, "profiles", "traffic_backward_dense.txt"),
                      sources=["kda_backward.hip", "kda_common.h"],
@@ -864,14 +864,15 @@ def main():
     ms_per_step = p["wall"] / args.steps * 1e3
     value = p["tokens"] / (ms_per_step * 1e-3)
     head = prefill_summary(p, args.steps, read_traffic("varlen"),
-                           kernel="kda_chunk_fwd = prep_kernel + scan_kernel back to back (one call)")
+                           kernel="kda_chunk_fwd = prep_kernel + scan4_kernel back to back (one call)")
     mf = read_mfma()
     if mf is not None:
-        counted = mf.get("prep_kernel_counted_mfma_flop", 0.0) + mf.get("scan_kernel_counted_mfma_flop", 0.0)
+        counted = sum(mf.get(f"{k}_counted_mfma_flop", 0.0) for k in TRAFFIC["varlen"]["kernels"])
         head["mfma"]["counted_mfma_flop_per_call"] = counted
         head["mfma"]["counted_TFLOPs"] = round(counted / (p["mean_ms"] * 1e-3) / 1e12, 2)
         head["mfma"]["counted_frac"] = round(counted / (p["mean_ms"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)
-        head["mfma"]["busy_frac"] = {k: mf.get(f"{k}_mfma_busy_frac") for k in ("prep_kernel", "scan_kernel")}
+        head["mfma"]["busy_frac"] = {k: mf[f"{k}_mfma_busy_frac"] for k in TRAFFIC["varlen"]["kernels"]
+                                     if f"{k}_mfma_busy_frac" in mf}
     dense = prefill_summary(res["prefill"], args.steps, read_traffic("prefill"))
     dense["workload"] = ("chunked prefill, dense B=4 x T=4096, H=16, dk=dv=128, bf16 q/k/v, fp32 log_g/beta/"
                          "state, fp32 out, chunk 64")

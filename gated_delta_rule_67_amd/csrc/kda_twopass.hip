@@ -454,7 +454,6 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
   }
   f16x8 hl[2], hr[2], xv[2];  // k exp(G - R), k exp(R' - G), beta v of rows r0, r0+1
   {
-    const int l3 = (lane & ~7) | 3, l4 = (lane & ~7) | 4;  // row pairs 3 and 4 of this octet
     // two passes of four channels keep the live registers down
 #pragma unroll
     for (int hc = 0; hc < 2; ++hc) {
@@ -480,8 +479,10 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
         const float xe = row_shr<1>(x, 1.f), ye = row_shl<1>(y, 1.f);
         const float E = qt >= 1 ? xe : 1.f;  // over the row pairs before this lane's
         const float F = qt <= 6 ? ye : 1.f;  // over the row pairs after it
-        const float dl = __shfl(x, l3, 64);  // over the first half of the block
-        const float dr = __shfl(y, l4, 64);  // over the second half
+        // broadcasts from row pairs 3 and 4 of this octet: swizzle bit masks
+        // (lane & 0x18) | 3 and | 4, immediates instead of address registers
+        const float dl = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x78));
+        const float dr = __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, y), 0x98));
         const float Pv[2] = {E * a0, E * pr};
         const float Sv[2] = {a1 * F, F};
 #pragma unroll
@@ -522,6 +523,11 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
     const bool any_strong = __builtin_amdgcn_ballot_w64(strong) != 0;
     if (lane == 0) sm.strong[w] = any_strong;
   }
+  // the checks so far as a wave mask now: a per-lane flag evaluated at the
+  // end would keep their inputs live through the products
+  const uint64_t bad_a = __builtin_amdgcn_ballot_w64(bad);
+  asm volatile("" ::"s"(bad_a));
+  bad = false;
   lds_barrier();
   // workgroup-uniform: the diagonal tiles of this chunk come from the pair tree
   const bool tree = (sm.strong[0] | sm.strong[1] | sm.strong[2] | sm.strong[3] | sm.strong[4] | sm.strong[5] |
@@ -788,7 +794,7 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
     bad |= !(omax <= F16_SAFE);
   }
   // one "not on the fast path" byte per wave
-  const bool any = __builtin_amdgcn_ballot_w64(bad) != 0;
+  const bool any = (__builtin_amdgcn_ballot_w64(bad) | bad_a) != 0;
   if (lane == 0) slot[OFF_FLAG + w] = any ? 1 : 0;
 }
 
