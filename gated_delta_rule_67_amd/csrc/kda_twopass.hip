@@ -87,7 +87,8 @@ constexpr float F16_SAFE = 16384.0f;            // bound of every fp16 intermedi
 // -W, Qs, As and (K exp(gamma - G))^T are stored in the order the scan's
 // lanes read them, so every scan load instruction covers 1 KiB of whole lines:
 //   NW, QS: [I 4][ks 4][lane 64][j 8] = X[16I+lc][32ks+8lg+j]
-//   AS:     [I 4][ks 2][lane 64][j 8] = As[16I+lc][32ks+8lg+j]  (zero above the diagonal)
+//   AS:     [I 4][ks 2][lane 64][j 8] = As[16I+lc][32ks+8lg+j]  (zero above the diagonal;
+//           the all-zero pieces (I 0|1, ks 1) are left unwritten)
 //   KDT:    [r 8][ks 2][lane 64][j 8] = Kd^T[16r+lc][32ks+8lg+j]
 constexpr size_t OFF_NW = 0;        // -W          64 x 128  fp16
 constexpr size_t OFF_QS = 16384;    // Qs          64 x 128  fp16
@@ -725,9 +726,12 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
     *reinterpret_cast<f16x2*>(&sm.u.x.XkT[c8 + c][r0]) = xk2;
     *reinterpret_cast<f16x2*>(&sm.u.x.XvT[c8 + c][r0]) = xv2;
   }
-  if (w < 6) {  // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-    const int zi = w < 3 ? 0 : w < 5 ? 1 : 2;
-    const int zj = zi + 1 + w - (zi == 0 ? 0 : zi == 1 ? 3 : 5);
+  // As above its diagonal: tiles (0,1) and (2,3) share their 32-token
+  // fragments with nonzero tiles and are written as zeros; the fragments of
+  // row blocks 0 and 1 over tokens 32..63 are all zero, never written, and
+  // never read by the scans
+  if (w < 2) {
+    const int zi = 2 * w, zj = zi + 1;
     f16x4 z;
 #pragma unroll
     for (int e = 0; e < 4; ++e) z[e] = (f16)0.f;
@@ -919,8 +923,8 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) r.kd[ks] = ld8(kd + ks * 64 * 8);
     if (is_o) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) r.as[ks] = ld8(as + ks * 64 * 8);
+      r.as[0] = ld8(as);
+      r.as[1] = I >= 2 ? ld8(as + 64 * 8) : f16x8{};  // row blocks 0, 1: zero past token 31
     } else {
       r.as[0] = r.as[1] = f16x8{};
     }
@@ -1181,8 +1185,8 @@ __global__ void __launch_bounds__(NT4, 2) scan4_kernel(ScanArgs p) {
                                                   4 * lg);
     }
     const f16* as = reinterpret_cast<const f16*>(sl + OFF_AS) + (w * 2 * 64 + lane) * 8;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) r.as[ks] = ld8(as + ks * 64 * 8);
+    r.as[0] = ld8(as);
+    r.as[1] = w >= 2 ? ld8(as + 64 * 8) : f16x8{};  // row blocks 0, 1: zero past token 31
   };
   auto load = [&](int k, Pre4& r) {
     load_flag(k, r);
