@@ -223,6 +223,40 @@ __device__ __forceinline__ float row_shl(float x, float fill) {
   return y;
 }
 
+// x from lane lane ^ 8 of the same 16-lane row (DPP row rotation by 8).  The
+// value is taken as a scalar: a bit cast of a vector element in place can
+// read the vector's first element instead.
+__device__ __forceinline__ float row_ror8(float x) {
+  float y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf,
+                                                                  false));
+  asm volatile("" : "+v"(y));
+  return y;
+}
+
+// The fp32 outputs of a 16-token x 32-column block stored as whole 128-byte
+// rows.  Lane (lc, lg) holds o[b][e] = O[row lc][col 16b + 4lg + e]; lanes lc
+// and lc ^ 8 swap one half (a DPP rotation by 8 within the 16-lane row), so the
+// first store writes rows 0..7 and the second rows 8..15, each instruction
+// eight whole rows.  off0: byte offset of the block's row 0, column 0; rs: row
+// stride in bytes.  Every lane of the wave must take part (DPP).
+// Cache policy of the output stores: nontemporal (the NT bit of the buffer
+// instruction's aux field).  The outputs are never read back, and whole-line
+// streaming stores leave L2 to the slot lines the other tiles of a unit
+// still read.
+constexpr int OUT_AUX = 2;
+__device__ __forceinline__ void store_rows_f32(const f32x4 (&o)[2], __amdgpu_buffer_rsrc_t r, uint32_t off0,
+                                               uint32_t rs, int lc, int lg) {
+  const bool lo = lc < 8;
+  const f32x4 x = lo ? o[1] : o[0];
+  f32x4 y;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) y[e] = row_ror8(x[e]);
+  const f32x4 pa = lo ? o[0] : y, pb = lo ? y : o[1];
+  const uint32_t off = off0 + static_cast<uint32_t>(lc & 7) * rs + static_cast<uint32_t>(16 * (lc >> 3) + 4 * lg) * 4u;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, pa), r, static_cast<int>(off), 0, OUT_AUX);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, pb), r, static_cast<int>(off + 8 * rs), 0, OUT_AUX);
+}
+
 struct DiagTiles {
   f32x4 a;  // fragA of sum_c k_t k_s exp(G_t - G_s), s < t (rows t = lc)
   f32x4 b;  // the same in fragB (rows t = 4lg+e)
@@ -1042,13 +1076,12 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
       const __amdgpu_buffer_rsrc_t orsrc = buffer_rsrc(
           static_cast<unsigned char*>(p.out) + ((tok0 * H + h) * D + col0) * osz,
           is_o ? static_cast<uint32_t>(((nv - 1) * H * D + DVT)) * osz : 0u);
-      const uint32_t ooff = static_cast<uint32_t>((16 * I + lc) * H * D + 4 * lg) * osz;
       if (p.out_bf16) {  // kernel-argument branch: uniform
+        const uint32_t ooff = static_cast<uint32_t>((16 * I + lc) * H * D + 4 * lg) * osz;
 #pragma unroll
         for (int b = 0; b < 2; ++b) buffer_store8_bf16(oacc[b], orsrc, ooff + 32 * b);
       } else {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) buffer_store16(oacc[b], orsrc, ooff + 64 * b);
+        store_rows_f32(oacc, orsrc, static_cast<uint32_t>(16 * I * H * D) * 4u, static_cast<uint32_t>(H * D) * 4u, lc, lg);
       }
     } else {
       // token by token from the entry state; writes this chunk's outputs
@@ -1306,13 +1339,12 @@ __global__ void __launch_bounds__(NT4, 2) scan4_kernel(ScanArgs p) {
       const __amdgpu_buffer_rsrc_t orsrc =
           buffer_rsrc(static_cast<unsigned char*>(p.out) + ((tok0 * H + h) * D + col0) * osz,
                       static_cast<uint32_t>(((nv - 1) * H * D + DVT)) * osz);
-      const uint32_t ooff = static_cast<uint32_t>((16 * w + lc) * H * D + 4 * lg) * osz;
       if (p.out_bf16) {  // kernel-argument branch: uniform
+        const uint32_t ooff = static_cast<uint32_t>((16 * w + lc) * H * D + 4 * lg) * osz;
 #pragma unroll
         for (int b = 0; b < 2; ++b) buffer_store8_bf16(oacc[b], orsrc, ooff + 32 * b);
       } else {
-#pragma unroll
-        for (int b = 0; b < 2; ++b) buffer_store16(oacc[b], orsrc, ooff + 64 * b);
+        store_rows_f32(oacc, orsrc, static_cast<uint32_t>(16 * w * H * D) * 4u, static_cast<uint32_t>(H * D) * 4u, lc, lg);
       }
     } else {
       // token by token from the entry state; writes this chunk's outputs
