@@ -144,12 +144,11 @@ size_t kda_chunk_workspace_bytes(const kda_desc* desc, int packed);
  * (per-chunk operands staged in the workspace); other inputs take the
  * token-recurrent kernel.  The chunked path's serial pass runs four 32-column
  * workgroups per (sequence or document, head): eight-wave ones, or four-wave
- * ones two to a CU when there are more such tiles than 256
- * (kda_chunk_fwd_gated_norm: one 16-wave workgroup per unit).  The
- * environment variable KDA_PREFILL_PATH, read at every call, is a test and
- * diagnosis switch: "recurrent" forces the token-recurrent kernel, "tile8",
- * "tile4" or "unit" a form of the serial pass.  A workspace smaller than the
- * selected path needs returns KDA_ERR_WORKSPACE before anything is enqueued.
+ * ones two to a CU when there are more such tiles than 256.  The environment
+ * variable KDA_PREFILL_PATH, read at every call, is a test and diagnosis
+ * switch: "recurrent" forces the token-recurrent kernel, "tile8" or "tile4" a
+ * form of the serial pass.  A workspace smaller than the selected path needs
+ * returns KDA_ERR_WORKSPACE before anything is enqueued.
  *
  * KDA_VALIDATE=1 (read at every call): before the launch, the call copies
  * cu_seqlens and log_g to the host and returns KDA_ERR_SHAPE if cu_seqlens
