@@ -93,7 +93,7 @@ constexpr float F16_SAFE = 16384.0f;            // bound of every fp16 intermedi
 constexpr size_t OFF_NW = 0;        // -W          64 x 128  fp16
 constexpr size_t OFF_QS = 16384;    // Qs          64 x 128  fp16
 constexpr size_t OFF_KDT = 32768;   // Kd^T        128 x 64  fp16
-constexpr size_t OFF_UP = 49152;    // U  by scan lane: [I][tile][lane][b][e] = U[16I+lc][32tile+16b+4lg+e]
+constexpr size_t OFF_UP = 49152;    // U  by scan lane: [I][tile][b][lane][e] = U[16I+lc][32tile+16b+4lg+e]
 constexpr size_t OFF_AS = 65536;    // As          64 x 64   fp16
 constexpr size_t OFF_GAM = 73728;   // exp(gamma)  [128] fp32
 constexpr size_t OFF_FLAG = 74240;  // per prep wave "not on the fast path" [8] bytes
@@ -636,7 +636,8 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
         res[e] = (f16)x;
       }
       bad |= !(amax <= F16_SAFE);
-      *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(slot + OFF_AS) + frag_pos(I, I, 2, lane)) = res;
+      __builtin_nontemporal_store(res, reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(slot + OFF_AS) +
+                                                                frag_pos(I, I, 2, lane)));
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
@@ -745,7 +746,8 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
         res[e] = (f16)x;
       }
       bad |= !(amax <= F16_SAFE);
-      *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(slot + OFF_AS) + frag_pos(I, J, 2, lane)) = res;
+      __builtin_nontemporal_store(res, reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(slot + OFF_AS) +
+                                                                frag_pos(I, J, 2, lane)));
     }
   }
   lds_barrier();
@@ -769,7 +771,8 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
     f16x4 z;
 #pragma unroll
     for (int e = 0; e < 4; ++e) z[e] = (f16)0.f;
-    *reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(slot + OFF_AS) + frag_pos(zi, zj, 2, lane)) = z;
+    __builtin_nontemporal_store(z, reinterpret_cast<f16x4*>(reinterpret_cast<f16*>(slot + OFF_AS) +
+                                                          frag_pos(zi, zj, 2, lane)));
   }
   switch (w) {
     case 0: bad |= t_column<0>(sm, tbd, lane); break;
@@ -823,11 +826,15 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
       // X[tok 16I+lc][col 16n+4lg+e]: block I, k-step n/2, lane
       // (lg' = 2(n&1) + lg/2, lc), position 4(lg&1)+e
       const int rowoff = ((I * 4 + (n >> 1)) * 64 + 16 * (2 * (n & 1) + (lg >> 1)) + lc) * 8 + 4 * (lg & 1);
-      *reinterpret_cast<f16x4*>(nw + rowoff) = h4(aW);
-      *reinterpret_cast<f16x4*>(qs + rowoff) = h4(aQ);
-      // U in the order one scan lane consumes it (same lane here)
-      const int laneoff = ((I * NTILE + (n >> 1)) * 64 + lane) * 8 + 4 * (n & 1);
-      *reinterpret_cast<f16x4*>(up + laneoff) = h4(aU);
+      // whole 128-byte lines per instruction (512 contiguous bytes), stored
+      // nontemporally: the scan reads them long after this kernel
+      __builtin_nontemporal_store(h4(aW), reinterpret_cast<f16x4*>(nw + rowoff));
+      __builtin_nontemporal_store(h4(aQ), reinterpret_cast<f16x4*>(qs + rowoff));
+      // U in the order one scan lane consumes it (same lane here): this
+      // wave's 16 columns are half b = n & 1 of tile n / 2, 512 contiguous
+      // bytes, stored like W and Qs
+      const int laneoff = (((I * NTILE + (n >> 1)) * 2 + (n & 1)) * 64 + lane) * 4;
+      __builtin_nontemporal_store(h4(aU), reinterpret_cast<f16x4*>(up + laneoff));
     }
     bad |= !(omax <= F16_SAFE);
   }
@@ -838,6 +845,14 @@ __global__ void __launch_bounds__(NTP) __attribute__((amdgpu_waves_per_eu(4))) p
 
 // ---------------------------------------------------------------------------
 // Pass 2: the serial state scan.
+
+// U of token block I, column tile `tile`, as one scan lane holds it: [b][e] =
+// U[16I+lc][32tile+16b+4lg+e], its two halves 512 bytes apart in the slot.
+__device__ __forceinline__ f16x8 ld_up(const unsigned char* sl, int I, int tile, int lane) {
+  const f16* up = reinterpret_cast<const f16*>(sl + OFF_UP) + ((I * NTILE + tile) * 2 * 64 + lane) * 4;
+  const f16x4 lo = *reinterpret_cast<const f16x4*>(up), hi = *reinterpret_cast<const f16x4*>(up + 64 * 4);
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 
 struct ScanArgs {
   const bf16_t* q;
@@ -947,7 +962,7 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
     const f16* mp = reinterpret_cast<const f16*>(sl + (is_o ? OFF_QS : OFF_NW)) + (I * 4 * 64 + lane) * 8;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) r.m[ks] = ld8(mp + ks * 64 * 8);
-    if (!is_o) r.u = ld8(reinterpret_cast<const f16*>(sl + OFF_UP) + ((I * NTILE + tile) * 64 + lane) * 8);
+    if (!is_o) r.u = ld_up(sl, I, tile, lane);
     else r.u = f16x8{};
   };
   auto load_b = [&](int k, Pre& r) {
@@ -1205,7 +1220,7 @@ __global__ void __launch_bounds__(NT4, 2) scan4_kernel(ScanArgs p) {
       r.mw[ks] = ld8(nw + ks * 64 * 8);
       r.mq[ks] = ld8(qs + ks * 64 * 8);
     }
-    r.u = ld8(reinterpret_cast<const f16*>(sl + OFF_UP) + ((w * NTILE + tile) * 64 + lane) * 8);
+    r.u = ld_up(sl, w, tile, lane);
   };
   auto load_b = [&](int k, Pre4& r) {
     const unsigned char* sl = slot_of(k);
