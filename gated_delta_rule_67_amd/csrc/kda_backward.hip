@@ -502,8 +502,9 @@ __global__ void __launch_bounds__(prep_threads<In>()) bwd_prep(BwdArgs a) {
   // Akk and (scale * Aqk)^T to the workspace
   for (int idx = tid; idx < C * C; idx += NTH) {
     const int t = idx / C, s = idx - t * C;
-    a.Ab[sh * C * C + idx] = sAb[t * LM + s];
-    a.AsT[sh * C * C + idx] = a.scale * sAq[s * LM + t];
+    // whole lines per instruction, read only by later kernels: nontemporal
+    __builtin_nontemporal_store(sAb[t * LM + s], a.Ab + sh * C * C + idx);
+    __builtin_nontemporal_store(a.scale * sAq[s * LM + t], a.AsT + sh * C * C + idx);
   }
   // per channel: b_t (prefix), Qs = scale q b, K*b (kept), Kd = k r(C-1, t), b_C
   // (the transposed rows QsT and KdT of channel ci are 32 consecutive floats
@@ -530,7 +531,7 @@ __global__ void __launch_bounds__(prep_threads<In>()) bwd_prep(BwdArgs a) {
       const int t = 32 * ph + u;
       const float kd = ld1f(sK + t * LDK + ci) * rr;
       x4[u & 3] = kd;
-      a.Kd[(sh * C + t) * D + ci] = kd;
+      __builtin_nontemporal_store(kd, a.Kd + (sh * C + t) * D + ci);
       if ((u & 3) == 0) *reinterpret_cast<float4*>(kdt + u) = make_float4(x4[0], x4[1], x4[2], x4[3]);
       rr *= al[u];
     }
@@ -607,7 +608,7 @@ __global__ void __launch_bounds__(prep_threads<In>()) bwd_prep(BwdArgs a) {
   __syncthreads();
   for (int idx = tid; idx < C * C; idx += NTH) {
     const int t = idx / C, s = idx - t * C;
-    a.Tm[sh * C * C + idx] = sT[s * LM + t];  // T^T
+    __builtin_nontemporal_store(sT[s * LM + t], a.Tm + sh * C * C + idx);  // T^T
   }
   if constexpr (P::COMPACT) {  // V^T over Akk (the solve is done with it)
     uint16_t* vt = reinterpret_cast<uint16_t*>(sVT);
@@ -1677,9 +1678,11 @@ __global__ void __launch_bounds__(NTS) bwd_gstate(BwdArgs a) {
     const int t = idx / (D / 4), c4 = 4 * (idx - t * (D / 4));
     if (t >= L.count) continue;
     const int64_t o = row(t) * D + c4;
-    *reinterpret_cast<float4*>(a.dq + o) = *reinterpret_cast<const float4*>(oq + t * LD + c4);
-    *reinterpret_cast<float4*>(a.dk + o) = *reinterpret_cast<const float4*>(ok + t * LD + c4);
-    *reinterpret_cast<float4*>(a.dlog_g + o) = *reinterpret_cast<const float4*>(og + t * LD + c4);
+    // whole rows, read back only by bwd_gpairs: nontemporal
+    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(oq + t * LD + c4), reinterpret_cast<f32x4*>(a.dq + o));
+    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(ok + t * LD + c4), reinterpret_cast<f32x4*>(a.dk + o));
+    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(og + t * LD + c4),
+                                reinterpret_cast<f32x4*>(a.dlog_g + o));
   }
   if (tid < L.count) a.dbeta[row(tid)] = sDb[tid] + sDb[C + tid];
 }
@@ -2046,8 +2049,11 @@ __global__ void __launch_bounds__(NTG, 2) bwd_gpairs(BwdArgs a) {
       const float4 yq = *reinterpret_cast<const float4*>(oq + t * LO + c4);
       const float4 yk = *reinterpret_cast<const float4*>(ok + t * LO + c4);
       const float4 yg = *pgq;
-      *reinterpret_cast<float4*>(a.dq + o) = make_float4(xq.x + yq.x, xq.y + yq.y, xq.z + yq.z, xq.w + yq.w);
-      *reinterpret_cast<float4*>(a.dk + o) = make_float4(xk.x + yk.x, xk.y + yk.y, xk.z + yk.z, xk.w + yk.w);
+      // the final gradients, whole rows: nontemporal
+      __builtin_nontemporal_store(f32x4{xq.x + yq.x, xq.y + yq.y, xq.z + yq.z, xq.w + yq.w},
+                                  reinterpret_cast<f32x4*>(a.dq + o));
+      __builtin_nontemporal_store(f32x4{xk.x + yk.x, xk.y + yk.y, xk.z + yk.z, xk.w + yk.w},
+                                  reinterpret_cast<f32x4*>(a.dk + o));
       *pgq = make_float4(xg.x + yg.x, xg.y + yg.y, xg.z + yg.z, xg.w + yg.w);
     } else {
       *pgq = make_float4(0.f, 0.f, 0.f, 0.f);

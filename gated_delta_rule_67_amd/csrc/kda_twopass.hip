@@ -1096,7 +1096,8 @@ __global__ void __launch_bounds__(NTS, 1) scan_kernel(ScanArgs p) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) buffer_store8_bf16(oacc[b], orsrc, ooff + 32 * b);
       } else {
-        store_rows_f32(oacc, orsrc, static_cast<uint32_t>(16 * I * H * D) * 4u, static_cast<uint32_t>(H * D) * 4u, lc, lg);
+        store_rows_f32(oacc, orsrc, static_cast<uint32_t>(16 * I * H * D) * 4u, static_cast<uint32_t>(H * D) * 4u,
+                       lc, lg);
       }
     } else {
       // token by token from the entry state; writes this chunk's outputs
@@ -1359,7 +1360,8 @@ __global__ void __launch_bounds__(NT4, 2) scan4_kernel(ScanArgs p) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) buffer_store8_bf16(oacc[b], orsrc, ooff + 32 * b);
       } else {
-        store_rows_f32(oacc, orsrc, static_cast<uint32_t>(16 * w * H * D) * 4u, static_cast<uint32_t>(H * D) * 4u, lc, lg);
+        store_rows_f32(oacc, orsrc, static_cast<uint32_t>(16 * w * H * D) * 4u, static_cast<uint32_t>(H * D) * 4u,
+                       lc, lg);
       }
     } else {
       // token by token from the entry state; writes this chunk's outputs
