@@ -1,6 +1,8 @@
 // kda_vec8.h -- 8 consecutive elements as fp32 registers, from and to fp32 or
 // bf16 memory (bf16: one 16-byte access; stores round fp32 to nearest even in
-// hardware, two values per instruction).  Used by the elementwise kernels.
+// hardware, two values per instruction).  Used by the elementwise kernels,
+// whose outputs are written once and not read again by the kernel: the stores
+// are nontemporal (the kernels' lanes cover whole lines per instruction).
 #pragma once
 
 #include "kda_common.h"
@@ -17,16 +19,13 @@ __device__ __forceinline__ void load8f(const bf16_t* p, float (&o)[8]) {
   o[4] = bf16_lo(u.z); o[5] = bf16_hi(u.z); o[6] = bf16_lo(u.w); o[7] = bf16_hi(u.w);
 }
 __device__ __forceinline__ void store8f(float* p, const float (&v)[8]) {
-  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
-  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+  __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4*>(p));
+  __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4*>(p + 4));
 }
 __device__ __forceinline__ void store8f(bf16_t* p, const float (&v)[8]) {
-  uint4 u;
-  u.x = bf16_pack2(v[0], v[1]);
-  u.y = bf16_pack2(v[2], v[3]);
-  u.z = bf16_pack2(v[4], v[5]);
-  u.w = bf16_pack2(v[6], v[7]);
-  *reinterpret_cast<uint4*>(p) = u;
+  const i32x4 u = {static_cast<int>(bf16_pack2(v[0], v[1])), static_cast<int>(bf16_pack2(v[2], v[3])),
+                   static_cast<int>(bf16_pack2(v[4], v[5])), static_cast<int>(bf16_pack2(v[6], v[7]))};
+  __builtin_nontemporal_store(u, reinterpret_cast<i32x4*>(p));
 }
 
 }  // namespace kda
