@@ -50,6 +50,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -86,11 +87,22 @@ TRAFFIC = {
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_prefill_packed.txt")
 
 
+def code_only(text: str) -> str:
+    """C++ source with comments and blank lines removed and line ends
+    trimmed: the part of a kernel source that decides what the counters
+    measure (string literals in these sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def sources_hash(kind: str = "prefill") -> str:
+    """Hash of the code (comments aside) of the sources that define a measured
+    path's kernels; a counter summary is used only while it matches."""
     h = hashlib.sha256()
     for f in TRAFFIC[kind]["sources"]:
-        with open(os.path.join(ROOT, "gated_delta_rule_67_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "gated_delta_rule_67_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

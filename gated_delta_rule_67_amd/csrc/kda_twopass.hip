@@ -223,9 +223,9 @@ __device__ __forceinline__ float row_shl(float x, float fill) {
   return y;
 }
 
-// x from lane lane ^ 8 of the same 16-lane row (DPP row rotation by 8).  The
-// value is taken as a scalar: a bit cast of a vector element in place can
-// read the vector's first element instead.
+// The value of x in lane (lane ^ 8), within the same 16-lane row (a DPP row
+// rotation by 8).  x is taken as a scalar: a bit cast of a vector element in
+// place can read the vector's first element instead.
 __device__ __forceinline__ float row_ror8(float x) {
   float y = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf,
                                                                   false));
@@ -233,17 +233,18 @@ __device__ __forceinline__ float row_ror8(float x) {
   return y;
 }
 
+// Cache policy of the scans' output stores: nontemporal (the NT bit of the
+// buffer instruction's aux field).  The outputs are never read back, and
+// whole-line streaming stores leave L2 to the slot lines the other tiles of a
+// unit still read.
+constexpr int OUT_AUX = 2;
+
 // The fp32 outputs of a 16-token x 32-column block stored as whole 128-byte
 // rows.  Lane (lc, lg) holds o[b][e] = O[row lc][col 16b + 4lg + e]; lanes lc
 // and lc ^ 8 swap one half (a DPP rotation by 8 within the 16-lane row), so the
 // first store writes rows 0..7 and the second rows 8..15, each instruction
 // eight whole rows.  off0: byte offset of the block's row 0, column 0; rs: row
 // stride in bytes.  Every lane of the wave must take part (DPP).
-// Cache policy of the output stores: nontemporal (the NT bit of the buffer
-// instruction's aux field).  The outputs are never read back, and whole-line
-// streaming stores leave L2 to the slot lines the other tiles of a unit
-// still read.
-constexpr int OUT_AUX = 2;
 __device__ __forceinline__ void store_rows_f32(const f32x4 (&o)[2], __amdgpu_buffer_rsrc_t r, uint32_t off0,
                                                uint32_t rs, int lc, int lg) {
   const bool lo = lc < 8;

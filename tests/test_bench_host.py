@@ -93,6 +93,16 @@ def test_traffic_is_reported_only_for_the_sources_it_was_taken_on(tmp_path, monk
     assert bench.read_traffic(kind) is None
 
 
+def test_source_stamp_ignores_comments_but_not_code():
+    """A traffic or MFMA summary stays valid across comment edits of the
+    kernel sources and lapses with any change to their code."""
+    code = "int f(int x) {  // doubled\n  return 2 * x;\n}\n"
+    assert bench.code_only(code) == bench.code_only("/* header\n over two lines */\n" + code.replace("doubled", "x2"))
+    assert bench.code_only(code) == bench.code_only(code.replace("\n", "\n\n"))
+    assert bench.code_only(code) != bench.code_only(code.replace("2 * x", "3 * x"))
+    assert bench.code_only(code) != bench.code_only(code.replace("return", "return -"))
+
+
 def test_backward_traffic_sums_the_five_backward_kernels(tmp_path):
     kib = bench.COPY_BYTES / 1024.0
     _write_counter_csv(tmp_path / "cf", "FETCH_SIZE", [("copy_kernel", 1, kib)])
