@@ -83,6 +83,15 @@ TRAFFIC = {
                      sources=["kda_backward.hip", "kda_common.h"],
                      kernels=("bwd_prep", "bwd_fscan", "bwd_rscan", "bwd_gstate", "bwd_gpairs"),
                      what="one kda_chunk_bwd call, dense 4 x 4096 tokens, 16 heads, d = 128, bf16"),
+    # the decode dispatches only: the whole-tile instantiation at 256 x 32
+    # units of 512 threads (verify's one-row reference uses it at 64 x 32
+    # units; verify and the speculative rows use the half-width one); its
+    # counter runs are bench.py --only step
+    "decode": dict(file=os.path.join(ROOT, "profiles", "traffic_decode.txt"),
+                   sources=["kda_recurrent.hip", "kda_common.h"],
+                   kernels=("recurrent_kernel<128, 128",), only="step", grid=256 * 32 * 512,
+                   what="one kda_step decode call, 256 sequences x 1 row, 32 heads, d = 128, bf16 q/k/v, "
+                        "fp32 state in place, caches flushed before each call"),
 }
 MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_prefill_packed.txt")
 
@@ -122,8 +131,9 @@ def read_traffic(kind: str = "prefill"):
         return None
 
 
-def _counter_sums(run_dir: str, counter: str):
-    """{kernel name: mean per-dispatch value} of one rocprofv3 --pmc csv run."""
+def _counter_sums(run_dir: str, counter: str, grid=None):
+    """{kernel name: mean per-dispatch value} of one rocprofv3 --pmc csv run;
+    with grid, only the dispatches of that many threads."""
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
         raise SystemExit(f"no counter_collection.csv under {run_dir}")
@@ -131,6 +141,8 @@ def _counter_sums(run_dir: str, counter: str):
     for f in files:
         for r in csv.DictReader(open(f)):
             if r.get("Counter_Name") != counter:
+                continue
+            if grid is not None and int(r["Grid_Size"]) != grid:
                 continue
             key = (r["Kernel_Name"], r["Dispatch_Id"])
             per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
@@ -141,7 +153,8 @@ def _counter_sums(run_dir: str, counter: str):
 
 
 def write_traffic(fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, kind="prefill"):
-    fe, wr = _counter_sums(fetch_dir, "FETCH_SIZE"), _counter_sums(write_dir, "WRITE_SIZE")
+    grid = TRAFFIC[kind].get("grid")
+    fe, wr = _counter_sums(fetch_dir, "FETCH_SIZE", grid), _counter_sums(write_dir, "WRITE_SIZE", grid)
     cf, cw = _counter_sums(copy_fetch_dir, "FETCH_SIZE"), _counter_sums(copy_write_dir, "WRITE_SIZE")
     pick = lambda d, pat: sum(v for k, v in d.items() if pat in k)
     copy_f = max(cf.values())   # the copy is the largest dispatch of its run
@@ -544,7 +557,7 @@ def bench_step(kda, name, steps, warmup, flush):
                      "(caches flushed before each call)",
          "us_per_call": round(avg * 1e3, 2), "achieved_GBs": round(nbytes / (avg * 1e-3) / 1e9, 1),
          "per_call": spread(ms),
-         "roofline": hbm_roofline(nbytes, avg),
+         "roofline": hbm_roofline(nbytes, avg, traffic=read_traffic("decode") if name == "decode" else None),
          "algorithmic_bytes": nbytes}
     if n_tok > 1:
         # the same states streamed by a one-row step: what the state traffic
@@ -800,11 +813,14 @@ def main():
             fh.write(f"# HBM traffic of {TRAFFIC[kind]['what']}\n")
             fh.write(f"# made by: python bench.py --traffic-kind {kind} --traffic-from " + " ".join(args.traffic_from) + "\n")
             fh.write("# from four counter runs (cd /tmp && export TMPDIR=/tmp first), one pass each:\n")
-            for ctr, what, d in (("FETCH_SIZE", kind, args.traffic_from[0]), ("WRITE_SIZE", kind, args.traffic_from[1]),
+            only = TRAFFIC[kind].get("only", kind)
+            for ctr, what, d in (("FETCH_SIZE", only, args.traffic_from[0]), ("WRITE_SIZE", only, args.traffic_from[1]),
                                  ("FETCH_SIZE", "copy", args.traffic_from[2]), ("WRITE_SIZE", "copy", args.traffic_from[3])):
                 steps = "--steps 3 --warmup 1"
                 fh.write(f"#   rocprofv3 --pmc {ctr} -f csv -d {d} -o run -- python3 bench.py --only {what} {steps}\n")
-            fh.write("# values are KiB per dispatch (mean over the run's dispatches); scale = copy bytes / counter bytes\n")
+            grid = TRAFFIC[kind].get("grid")
+            fh.write("# values are KiB per dispatch (mean over the run's dispatches"
+                     + (f" of {grid} threads" if grid else "") + "); scale = copy bytes / counter bytes\n")
             fh.write("\n".join(lines) + "\n")
         print("\n".join(lines))
         return

@@ -50,13 +50,16 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout.strip() == ""  # no JSON line
 
 
-def _write_counter_csv(dirname, counter, rows):
+def _write_counter_csv(dirname, counter, rows, grid=1024):
+    """rows: (kernel name, dispatch id, value) or (..., grid size in threads)."""
     os.makedirs(dirname, exist_ok=True)
     with open(os.path.join(dirname, "run_counter_collection.csv"), "w", newline="") as fh:
-        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Dispatch_Id", "Counter_Name", "Counter_Value"])
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Dispatch_Id", "Grid_Size", "Counter_Name", "Counter_Value"])
         w.writeheader()
-        for name, disp, val in rows:
-            w.writerow({"Kernel_Name": name, "Dispatch_Id": disp, "Counter_Name": counter, "Counter_Value": val})
+        for row in rows:
+            name, disp, val = row[:3]
+            w.writerow({"Kernel_Name": name, "Dispatch_Id": disp, "Grid_Size": row[3] if len(row) > 3 else grid,
+                        "Counter_Name": counter, "Counter_Value": val})
 
 
 def test_traffic_is_scaled_by_the_copy_calibration(tmp_path):
@@ -101,6 +104,24 @@ def test_source_stamp_ignores_comments_but_not_code():
     assert bench.code_only(code) == bench.code_only(code.replace("\n", "\n\n"))
     assert bench.code_only(code) != bench.code_only(code.replace("2 * x", "3 * x"))
     assert bench.code_only(code) != bench.code_only(code.replace("return", "return -"))
+
+
+def test_decode_traffic_counts_only_the_decode_dispatches(tmp_path):
+    """The decode instantiation also serves verify's one-row reference at a
+    quarter of the units: only dispatches of the decode grid are averaged."""
+    kib = bench.COPY_BYTES / 1024.0
+    _write_counter_csv(tmp_path / "cf", "FETCH_SIZE", [("copy_kernel", 1, kib / 2)])
+    _write_counter_csv(tmp_path / "cw", "WRITE_SIZE", [("copy_kernel", 1, kib)])
+    dec, ref = "void recurrent_kernel<128, 128, bf16_t, false>(RecArgs)", 256 * 32 * 512
+    other = "void recurrent_kernel<128, 64, bf16_t, false>(RecArgs)"
+    _write_counter_csv(tmp_path / "sf", "FETCH_SIZE", [(dec, 1, 100.0, ref), (dec, 2, 25.0, ref // 4),
+                                                       (dec, 3, 100.0, ref), (other, 4, 7.0, ref // 2)])
+    _write_counter_csv(tmp_path / "sw", "WRITE_SIZE", [(dec, 1, 200.0, ref), (dec, 2, 50.0, ref // 4),
+                                                       (dec, 3, 200.0, ref)])
+    lines = bench.write_traffic(str(tmp_path / "sf"), str(tmp_path / "sw"), str(tmp_path / "cf"), str(tmp_path / "cw"),
+                                kind="decode")
+    kv = dict(l.split(": ", 1) for l in lines)
+    assert int(kv["traffic_bytes_per_call"]) == round((100.0 * 2.0 + 200.0) * 1024)
 
 
 def test_backward_traffic_sums_the_five_backward_kernels(tmp_path):
