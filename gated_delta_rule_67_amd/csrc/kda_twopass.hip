@@ -23,7 +23,11 @@
 // the Delta tile the state update reads, with the slot operands of the next
 // two chunks in flight while one chunk is processed.  Its eight waves split
 // the roles: four form Delta (the serial chain), four form the outputs, all
-// eight update 16 state rows each.
+// eight update 16 state rows each.  scan4_kernel is the four-wave form (each
+// wave both roles for one 16-token block, two workgroups per CU), taken when
+// there are more tiles than CUs.  Outputs leave as whole 128-byte rows (fp32)
+// with the nontemporal policy; the slot is written likewise where its pieces
+// form whole lines per instruction.
 //
 // Decay factors without overflow (pass 1).  The chunk is cut into four
 // 16-token blocks.  With R_I = G before block I's first token:
@@ -48,7 +52,7 @@
 //
 // Arithmetic: fp16 MFMA operands (formed in fp32 from the bf16 inputs and
 // rounded once; the guard keeps them inside fp16's range), fp32
-// accumulation, state and outputs.  With L a strictly lower 16x16 diagonal
+// accumulation and state; outputs fp32, or rounded once to bf16.  With L a strictly lower 16x16 diagonal
 // block of A (L^16 = 0), (I + L)^-1 = (I - L)(I + L^2)(I + L^4)(I + L^8); the
 // off-diagonal blocks of T follow by block forward substitution,
 // T_IJ = -T_II sum_{J<=K<I} A_IK T_KJ.
