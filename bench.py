@@ -93,7 +93,14 @@ TRAFFIC = {
                    what="one kda_step decode call, 256 sequences x 1 row, 32 heads, d = 128, bf16 q/k/v, "
                         "fp32 state in place, caches flushed before each call"),
 }
-MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_prefill_packed.txt")
+# MFMA counter summaries, one per prefill workload (the counter run is
+# bench.py --only <kind>)
+MFMA = {
+    "varlen": dict(file=os.path.join(ROOT, "profiles", "mfma_prefill_packed.txt"),
+                   what="one kda_chunk_fwd call, packed 65536 tokens in 26 documents, 32 heads, d = 128, bf16"),
+    "prefill": dict(file=os.path.join(ROOT, "profiles", "mfma_prefill_dense.txt"),
+                    what="one kda_chunk_fwd call, dense 4 x 4096 tokens, 16 heads, d = 128, bf16"),
+}
 
 
 def code_only(text: str) -> str:
@@ -752,18 +759,18 @@ def bench_copy(steps, warmup):
 MFMA_COUNTERS = ("MfmaUtil", "MfmaFlopsF16")
 
 
-def write_mfma(run_dir):
+def write_mfma(run_dir, kind="varlen"):
     """Per-kernel MFMA metrics of one rocprofv3 --pmc run (mean per dispatch):
     the busy fraction of the matrix cores while the kernel runs, and the fp16
     MFMA FLOP it executed (algorithmic plus any redundant work)."""
-    lines = [f"sources_sha256: {sources_hash('varlen')}"]
+    lines = [f"sources_sha256: {sources_hash(kind)}"]
     per = {}
     for c in MFMA_COUNTERS:
         try:
             per[c] = _counter_sums(run_dir, c)
         except SystemExit:
             per[c] = {}
-    for pat in TRAFFIC["varlen"]["kernels"]:
+    for pat in TRAFFIC[kind]["kernels"]:
         util = [v for k, v in per["MfmaUtil"].items() if pat in k]
         flop = sum(v for k, v in per["MfmaFlopsF16"].items() if pat in k)
         if util:
@@ -772,20 +779,34 @@ def write_mfma(run_dir):
     return lines
 
 
-def read_mfma():
-    """The committed MFMA counter summary as a dict, or None when it is
-    missing or was taken on other kernel sources."""
+def read_mfma(kind="varlen"):
+    """The committed MFMA counter summary of a prefill workload as a dict, or
+    None when it is missing or was taken on other kernel sources."""
     try:
         kv = {}
-        for line in open(MFMA_FILE):
+        for line in open(MFMA[kind]["file"]):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
-        if kv.pop("sources_sha256", None) != sources_hash("varlen"):
+        if kv.pop("sources_sha256", None) != sources_hash(kind):
             return None
         return {k: float(v) for k, v in kv.items()}
     except (OSError, ValueError):
         return None
+
+
+def add_mfma_counters(summary, p, kind):
+    """Counted MFMA FLOP per call, their rate against the fp16 peak, and each
+    kernel's busy fraction, from the committed summary of this workload."""
+    mf = read_mfma(kind)
+    if mf is None:
+        return
+    counted = sum(mf.get(f"{k}_counted_mfma_flop", 0.0) for k in TRAFFIC[kind]["kernels"])
+    summary["mfma"]["counted_mfma_flop_per_call"] = counted
+    summary["mfma"]["counted_TFLOPs"] = round(counted / (p["mean_ms"] * 1e-3) / 1e12, 2)
+    summary["mfma"]["counted_frac"] = round(counted / (p["mean_ms"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)
+    summary["mfma"]["busy_frac"] = {k: mf[f"{k}_mfma_busy_frac"] for k in TRAFFIC[kind]["kernels"]
+                                    if f"{k}_mfma_busy_frac" in mf}
 
 
 def main():
@@ -803,8 +824,9 @@ def main():
     ap.add_argument("--traffic-kind", choices=sorted(TRAFFIC), default="varlen",
                     help="which path --traffic-from summarises (bench.py --only <kind> made its runs)")
     ap.add_argument("--mfma-from", metavar="DIR",
-                    help="rocprofv3 csv dir of one --pmc run of the MFMA counters over --only varlen; writes "
-                         "profiles/mfma_prefill_packed.txt")
+                    help="rocprofv3 csv dir of one --pmc run of the MFMA counters over --only <--mfma-kind>; "
+                         "writes that workload's profiles/mfma_prefill_*.txt")
+    ap.add_argument("--mfma-kind", choices=sorted(MFMA), default="varlen")
     args = ap.parse_args()
     if args.traffic_from:
         kind = args.traffic_kind
@@ -825,13 +847,13 @@ def main():
         print("\n".join(lines))
         return
     if args.mfma_from:
-        lines = write_mfma(args.mfma_from)
-        with open(MFMA_FILE, "w") as fh:
-            fh.write("# MFMA counters of one kda_chunk_fwd call, packed 65536 tokens in 26 documents, 32 heads, "
-                     "d = 128, bf16\n")
-            fh.write(f"# made by: python bench.py --mfma-from {args.mfma_from}\n")
+        kind = args.mfma_kind
+        lines = write_mfma(args.mfma_from, kind)
+        with open(MFMA[kind]["file"], "w") as fh:
+            fh.write(f"# MFMA counters of {MFMA[kind]['what']}\n")
+            fh.write(f"# made by: python bench.py --mfma-kind {kind} --mfma-from {args.mfma_from}\n")
             fh.write(f"# from: rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} -f csv -d {args.mfma_from} -o run -- "
-                     "python3 bench.py --only varlen --steps 3 --warmup 1\n")
+                     f"python3 bench.py --only {kind} --steps 3 --warmup 1\n")
             fh.write("# values are per dispatch (mean over the run's dispatches); mfma_busy_frac = MfmaUtil / 100 "
                      "(busy cycles of the matrix cores over the kernel's active cycles on all SIMDs); "
                      "counted_mfma_flop = MfmaFlopsF16\n")
@@ -893,15 +915,9 @@ def main():
     value = p["tokens"] / (ms_per_step * 1e-3)
     head = prefill_summary(p, args.steps, read_traffic("varlen"),
                            kernel="kda_chunk_fwd = prep_kernel + scan4_kernel back to back (one call)")
-    mf = read_mfma()
-    if mf is not None:
-        counted = sum(mf.get(f"{k}_counted_mfma_flop", 0.0) for k in TRAFFIC["varlen"]["kernels"])
-        head["mfma"]["counted_mfma_flop_per_call"] = counted
-        head["mfma"]["counted_TFLOPs"] = round(counted / (p["mean_ms"] * 1e-3) / 1e12, 2)
-        head["mfma"]["counted_frac"] = round(counted / (p["mean_ms"] * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)
-        head["mfma"]["busy_frac"] = {k: mf[f"{k}_mfma_busy_frac"] for k in TRAFFIC["varlen"]["kernels"]
-                                     if f"{k}_mfma_busy_frac" in mf}
+    add_mfma_counters(head, p, "varlen")
     dense = prefill_summary(res["prefill"], args.steps, read_traffic("prefill"))
+    add_mfma_counters(dense, res["prefill"], "prefill")
     dense["workload"] = ("chunked prefill, dense B=4 x T=4096, H=16, dk=dv=128, bf16 q/k/v, fp32 log_g/beta/"
                          "state, fp32 out, chunk 64")
     line = {
